@@ -1,0 +1,95 @@
+"""Field-level packers used only by the tests.
+
+They build block bytes from explicit fields (d, dmin, scales, mins, codes),
+in the forward direction, so that the oracle's unpacking can be checked
+against fields that were never derived from the oracle itself.  The
+arrangement is the GGUF block layout the pages name ("PESTI - Portable
+Execution Substrate for Transformer Inference", section "What This Is").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f16_bits(value: float) -> int:
+    """binary16 bit pattern of a value (round to nearest-even)."""
+    return int(np.array([value], dtype=np.float16).view(np.uint16)[0])
+
+
+def _put_u16(buf: bytearray, off: int, bits: int) -> None:
+    buf[off] = bits & 0xFF
+    buf[off + 1] = (bits >> 8) & 0xFF
+
+
+def pack_q8_0_block(d_bits: int, q) -> bytes:
+    """34 bytes: binary16 d then 32 int8 codes."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and all(-128 <= v <= 127 for v in q)
+    buf = bytearray(34)
+    _put_u16(buf, 0, d_bits)
+    for i, v in enumerate(q):
+        buf[2 + i] = v & 0xFF
+    return bytes(buf)
+
+
+def pack_q4_k_scales(sc, m) -> bytes:
+    """Twelve bytes holding eight 6-bit scales and eight 6-bit mins.
+    Bytes 0-3: scale j (j < 4) in bits 0-5, and bits 4-5 of scale j+4 in
+    bits 6-7.  Bytes 4-7: the same for the mins.  Bytes 8-11: bits 0-3 of
+    scale j+4 in the low nibble, bits 0-3 of min j+4 in the high nibble."""
+    assert len(sc) == 8 and len(m) == 8
+    assert all(0 <= v < 64 for v in list(sc) + list(m))
+    out = bytearray(12)
+    for j in range(4):
+        hi_sc = (sc[j + 4] >> 4) & 3
+        hi_m = (m[j + 4] >> 4) & 3
+        out[j] = sc[j] | (hi_sc << 6)
+        out[4 + j] = m[j] | (hi_m << 6)
+        out[8 + j] = (sc[j + 4] & 0xF) | ((m[j + 4] & 0xF) << 4)
+    return bytes(out)
+
+
+def pack_q4_k_block(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
+    """144 bytes: d, dmin, packed scales/mins, 128 code bytes.  Codes come in
+    runs of 64 weights; run r lives in bytes 32r..32r+31, its first half in
+    the low nibbles and its second half in the high nibbles."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 16 for v in q)
+    buf = bytearray(144)
+    _put_u16(buf, 0, d_bits)
+    _put_u16(buf, 2, dmin_bits)
+    buf[4:16] = pack_q4_k_scales(sc, m)
+    for r in range(4):
+        for l in range(32):
+            buf[16 + 32 * r + l] = q[64 * r + l] | (q[64 * r + 32 + l] << 4)
+    return bytes(buf)
+
+
+def pack_q6_k_block(d_bits: int, sc, q) -> bytes:
+    """210 bytes: 128 low-part bytes, 64 high-part bytes, 16 int8 scales, d.
+    Weight i = 128h + 32g + l keeps its low four bits in the low (g < 2) or
+    high (g >= 2) nibble of low-part byte 64h + 32(g % 2) + l, and its top two
+    bits at bit 2g of high-part byte 32h + l."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 64 for v in q)
+    assert len(sc) == 16 and all(-128 <= v <= 127 for v in sc)
+    ql = [0] * 128
+    qh = [0] * 64
+    for h in range(2):
+        for g in range(4):
+            for l in range(32):
+                v = q[128 * h + 32 * g + l]
+                shift = 4 if g >= 2 else 0
+                ql[64 * h + 32 * (g % 2) + l] |= (v & 0xF) << shift
+                qh[32 * h + l] |= (v >> 4) << (2 * g)
+    buf = bytearray(210)
+    buf[0:128] = bytes(ql)
+    buf[128:192] = bytes(qh)
+    buf[192:208] = bytes(int(v) & 0xFF for v in sc)
+    _put_u16(buf, 208, d_bits)
+    return bytes(buf)
+
+
+def rows_to_array(rows_of_blocks) -> np.ndarray:
+    """[[block bytes, ...] per row] -> uint8 [rows, row_bytes]."""
+    return np.array([np.frombuffer(b"".join(r), dtype=np.uint8) for r in rows_of_blocks])

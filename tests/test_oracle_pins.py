@@ -1,0 +1,506 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+* hand-worked fixtures under tests/golden/ (values derived by hand from the
+  block definitions, with the derivation in each file);
+* fields packed by an independent forward packer (tests/packing.py) and the
+  closed forms w = d*sc*q - dmin*m (Q4_K), d*sc*(q-32) (Q6_K), d*q (Q8_0),
+  scale*q (int8) evaluated in exact rationals;
+* one-hot codes, which pin each weight's position;
+* exact rational mat-vec (brute force) on 4x32 .. 8x256 matrices;
+* special cases (zero codes, zero scales, q = 32, zero d, subnormal d);
+* reductions to textbook operations (integer matrix product, identity).
+A set of planted mistakes checks that the pins catch plausible bugs.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import golden_io
+import packing
+import oracle
+
+GEMV_REL = 1e-4
+GEMM_REL = 2e-3
+
+
+# ---------------------------------------------------------------------------
+# helpers: exact values from explicit fields
+# ---------------------------------------------------------------------------
+def f16_value(bits: int) -> Fraction:
+    return Fraction(float(np.array([bits], dtype=np.uint16).view(np.float16)[0]))
+
+
+def random_f16_bits(rng, n):
+    """binary16 patterns spanning zero, subnormals, normals and the maximum."""
+    special = [0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x1234]
+    out = []
+    for _ in range(n):
+        if rng.random() < 0.3:
+            out.append(int(rng.choice(special)))
+        else:
+            out.append(int(rng.integers(0, 0x7C00)))   # finite, non-negative
+    return out
+
+
+def q4_k_exact(d_bits, dmin_bits, sc, m, q):
+    d, dmin = f16_value(d_bits), f16_value(dmin_bits)
+    return [d * sc[i // 32] * q[i] - dmin * m[i // 32] for i in range(256)]
+
+
+def q6_k_exact(d_bits, sc, q):
+    d = f16_value(d_bits)
+    return [d * sc[i // 16] * (q[i] - 32) for i in range(256)]
+
+
+def q8_0_exact(d_bits, q):
+    d = f16_value(d_bits)
+    return [d * v for v in q]
+
+
+def random_q4_k_fields(rng):
+    return (random_f16_bits(rng, 1)[0], random_f16_bits(rng, 1)[0],
+            [int(v) for v in rng.integers(0, 64, 8)], [int(v) for v in rng.integers(0, 64, 8)],
+            [int(v) for v in rng.integers(0, 16, 256)])
+
+
+def random_q6_k_fields(rng):
+    return (random_f16_bits(rng, 1)[0], [int(v) for v in rng.integers(-128, 128, 16)],
+            [int(v) for v in rng.integers(0, 64, 256)])
+
+
+def random_q8_0_fields(rng):
+    return random_f16_bits(rng, 1)[0], [int(v) for v in rng.integers(-128, 128, 32)]
+
+
+def as_fraction_array(w):
+    return [Fraction(float(v)) for v in np.asarray(w).reshape(-1)]
+
+
+# ---------------------------------------------------------------------------
+# 1. hand-worked fixtures
+# ---------------------------------------------------------------------------
+def check_dequant_fixture(name: str) -> bool:
+    fx = golden_io.load(name)
+    if "f64" not in fx:
+        return True
+    data, scales = golden_io.packed(fx)
+    w = oracle.dequantize(fx["format"], data, fx["rows"], fx["in_features"], scales)
+    ok = w.shape == (fx["rows"], fx["in_features"])
+    ok = ok and np.array_equal(w.reshape(-1), fx["f64"])
+    f32_expect = fx.get("f32", fx["f64"]).astype(np.float32)
+    w32 = oracle.dequantize_f32(fx["format"], data, fx["rows"], fx["in_features"], scales)
+    return bool(ok and np.array_equal(w32.reshape(-1), f32_expect))
+
+
+def check_gemv_fixture(name: str) -> bool:
+    fx = golden_io.load(name)
+    if "y" not in fx:
+        return True
+    data, scales = golden_io.packed(fx)
+    y, s = oracle.gemv_packed(fx["format"], data, fx["rows"], fx["in_features"],
+                              fx["x"].astype(np.float32), fx["bias"].astype(np.float32), scales)
+    return bool(np.array_equal(y.reshape(-1), fx["y"]))
+
+
+@pytest.mark.parametrize("name", golden_io.all_fixtures())
+def test_golden_fixture(name):
+    assert check_dequant_fixture(name), name
+    assert check_gemv_fixture(name), name
+
+
+def test_fixture_set_covers_every_format():
+    fmts = {golden_io.load(n)["format"] for n in golden_io.all_fixtures()}
+    assert fmts == {"q8_0", "q4_k", "q6_k", "i8row"}
+
+
+# ---------------------------------------------------------------------------
+# 2. independent packer -> oracle unpack == fields; closed forms, exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_q4_k_fields_and_closed_form(seed):
+    rng = np.random.default_rng([1, seed])
+    blocks, exact = [], []
+    for _ in range(8):
+        d, dmin, sc, m, q = random_q4_k_fields(rng)
+        blocks.append(packing.pack_q4_k_block(d, dmin, sc, m, q))
+        exact.extend(q4_k_exact(d, dmin, sc, m, q))
+        # field-level round trip through the oracle's unpackers
+        raw = np.frombuffer(blocks[-1], dtype=np.uint8)
+        sc_o, m_o = oracle.q4_k_scales_mins(raw[4:16])
+        assert list(sc_o) == sc and list(m_o) == m
+        assert list(oracle.q4_k_codes(raw[16:144])) == q
+    data = packing.rows_to_array([blocks[:4], blocks[4:]])
+    w = oracle.dequant_q4_k(data, 2, 1024)
+    assert as_fraction_array(w) == exact
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_q6_k_fields_and_closed_form(seed):
+    rng = np.random.default_rng([2, seed])
+    blocks, exact = [], []
+    for _ in range(6):
+        d, sc, q = random_q6_k_fields(rng)
+        blocks.append(packing.pack_q6_k_block(d, sc, q))
+        exact.extend(q6_k_exact(d, sc, q))
+        raw = np.frombuffer(blocks[-1], dtype=np.uint8)
+        assert list(oracle.q6_k_codes(raw[0:128], raw[128:192])) == q
+    data = packing.rows_to_array([blocks[:3], blocks[3:]])
+    w = oracle.dequant_q6_k(data, 2, 768)
+    assert as_fraction_array(w) == exact
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_q8_0_closed_form(seed):
+    rng = np.random.default_rng([3, seed])
+    blocks, exact = [], []
+    for _ in range(12):
+        d, q = random_q8_0_fields(rng)
+        blocks.append(packing.pack_q8_0_block(d, q))
+        exact.extend(q8_0_exact(d, q))
+    data = packing.rows_to_array([blocks[:4], blocks[4:8], blocks[8:]])
+    w = oracle.dequant_q8_0(data, 3, 128)
+    assert as_fraction_array(w) == exact
+
+
+def test_field_extremes_round_trip():
+    """All-zero and all-maximal fields, and each scale/min alone at 63."""
+    for val in (0, 63):
+        raw = np.frombuffer(packing.pack_q4_k_scales([val] * 8, [63 - val] * 8), dtype=np.uint8)
+        sc, m = oracle.q4_k_scales_mins(raw)
+        assert list(sc) == [val] * 8 and list(m) == [63 - val] * 8
+    for j in range(8):
+        sc_in = [63 if k == j else 0 for k in range(8)]
+        m_in = [0 if k == j else 63 for k in range(8)]
+        raw = np.frombuffer(packing.pack_q4_k_scales(sc_in, m_in), dtype=np.uint8)
+        sc, m = oracle.q4_k_scales_mins(raw)
+        assert list(sc) == sc_in and list(m) == m_in
+
+
+# ---------------------------------------------------------------------------
+# 3. one-hot codes pin every weight's position
+# ---------------------------------------------------------------------------
+def test_q4_k_one_hot_positions():
+    sc = [1, 2, 3, 4, 5, 6, 7, 8]
+    for i in range(256):
+        q = [0] * 256
+        q[i] = 9
+        blk = packing.pack_q4_k_block(0x3C00, 0x0000, sc, [5] * 8, q)
+        w = oracle.dequant_q4_k(np.frombuffer(blk, dtype=np.uint8), 1, 256)[0]
+        nz = np.flatnonzero(w)
+        assert list(nz) == [i] and w[i] == 9 * sc[i // 32], i
+
+
+def test_q6_k_one_hot_positions():
+    sc = list(range(1, 17))
+    for i in range(256):
+        q = [32] * 256          # q = 32 dequantizes to exactly 0
+        q[i] = 45
+        blk = packing.pack_q6_k_block(0x3C00, sc, q)
+        w = oracle.dequant_q6_k(np.frombuffer(blk, dtype=np.uint8), 1, 256)[0]
+        nz = np.flatnonzero(w)
+        assert list(nz) == [i] and w[i] == 13 * sc[i // 16], i
+
+
+def test_q8_0_one_hot_positions():
+    for i in range(32):
+        q = [0] * 32
+        q[i] = -7
+        blk = packing.pack_q8_0_block(0x4000, q)   # d = 2
+        w = oracle.dequant_q8_0(np.frombuffer(blk, dtype=np.uint8), 1, 32)[0]
+        assert list(np.flatnonzero(w)) == [i] and w[i] == -14
+
+
+# ---------------------------------------------------------------------------
+# 4. special cases
+# ---------------------------------------------------------------------------
+def test_q4_k_special_cases():
+    rng = np.random.default_rng(7)
+    _, _, sc, m, q = random_q4_k_fields(rng)
+    d, dmin = 0x3555, 0x2AAA
+    # q = 0 -> -dmin*m
+    w = oracle.dequant_q4_k(np.frombuffer(packing.pack_q4_k_block(d, dmin, sc, m, [0] * 256), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [-f16_value(dmin) * m[i // 32] for i in range(256)]
+    # sc = 0 -> constant -dmin*m per sub-block, whatever the codes
+    w = oracle.dequant_q4_k(np.frombuffer(packing.pack_q4_k_block(d, dmin, [0] * 8, m, q), np.uint8), 1, 256)[0]
+    for j in range(8):
+        assert np.all(w[32 * j:32 * j + 32] == w[32 * j])
+    # d = 0 -> -dmin*m
+    w = oracle.dequant_q4_k(np.frombuffer(packing.pack_q4_k_block(0, dmin, sc, m, q), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [-f16_value(dmin) * m[i // 32] for i in range(256)]
+    # subnormal d: w = 2^-24 * sc * q exactly
+    w = oracle.dequant_q4_k(np.frombuffer(packing.pack_q4_k_block(0x0001, 0, sc, m, q), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * sc[i // 32] * q[i] for i in range(256)]
+
+
+def test_q6_k_special_cases():
+    rng = np.random.default_rng(8)
+    _, sc, q = random_q6_k_fields(rng)
+    w = oracle.dequant_q6_k(np.frombuffer(packing.pack_q6_k_block(0x3C00, sc, [32] * 256), np.uint8), 1, 256)[0]
+    assert np.all(w == 0)
+    w = oracle.dequant_q6_k(np.frombuffer(packing.pack_q6_k_block(0, sc, q), np.uint8), 1, 256)[0]
+    assert np.all(w == 0)
+    w = oracle.dequant_q6_k(np.frombuffer(packing.pack_q6_k_block(0x0001, sc, q), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * sc[i // 16] * (q[i] - 32) for i in range(256)]
+
+
+def test_q8_0_special_cases():
+    rng = np.random.default_rng(9)
+    _, q = random_q8_0_fields(rng)
+    w = oracle.dequant_q8_0(np.frombuffer(packing.pack_q8_0_block(0, q), np.uint8), 1, 32)[0]
+    assert np.all(w == 0)
+    w = oracle.dequant_q8_0(np.frombuffer(packing.pack_q8_0_block(0x7BFF, [-128] * 32), np.uint8), 1, 32)[0]
+    assert np.all(w == -65504.0 * 128)
+
+
+# ---------------------------------------------------------------------------
+# 5. padding columns are dropped and their bytes do not matter
+# ---------------------------------------------------------------------------
+def _padding_masks_in128():
+    """Byte masks (bit set = may change) of what only weights 128..255 use."""
+    q4 = np.zeros(144, dtype=np.uint8)
+    q4[4:8] = 0xC0          # top bits of scales 4..7
+    q4[8:12] = 0xC0         # top bits of mins 4..7
+    q4[12:16] = 0xFF        # low bits of scales/mins 4..7
+    q4[16 + 64:144] = 0xFF  # code runs 2 and 3
+    q6 = np.zeros(210, dtype=np.uint8)
+    q6[64:128] = 0xFF       # low parts of h = 1
+    q6[128 + 32:192] = 0xFF  # high parts of h = 1
+    q6[192 + 8:208] = 0xFF  # scales of sub-blocks 8..15
+    return {"q4_k": q4, "q6_k": q6}
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+def test_padding_bytes_do_not_matter(fmt):
+    rng = np.random.default_rng(11)
+    mask = _padding_masks_in128()[fmt]
+    nb = oracle.BLOCK_BYTES[fmt]
+    base = rng.integers(0, 256, size=(3, nb), dtype=np.uint8)
+    d_off = 0 if fmt == "q4_k" else 208
+    base[:, d_off:d_off + 2] = [0x00, 0x3C]           # d = 1.0
+    w0 = oracle.dequantize(fmt, base, 3, 128)
+    assert w0.shape == (3, 128)
+    for trial in range(5):
+        noise = rng.integers(0, 256, size=base.shape, dtype=np.uint8) & mask
+        alt = (base & ~mask) | noise
+        assert np.array_equal(oracle.dequantize(fmt, alt, 3, 128), w0)
+    # and the kept columns equal the full-block decode's first 128 columns
+    assert np.array_equal(w0, oracle.dequantize(fmt, base, 3, 256)[:, :128])
+
+
+# ---------------------------------------------------------------------------
+# 6. brute force: exact rational mat-vec from the fields
+# ---------------------------------------------------------------------------
+def _exact_gemv(w_exact_rows, x, bias):
+    out = []
+    for b in range(x.shape[0]):
+        row = []
+        for o, wrow in enumerate(w_exact_rows):
+            acc = sum((wv * Fraction(float(xv)) for wv, xv in zip(wrow, x[b])), Fraction(0))
+            if bias is not None:
+                acc += Fraction(float(bias[o]))
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+def _build(fmt, rng, rows, in_features):
+    """Packed matrix and its exact weights from random fields."""
+    qk = 32 if fmt == "q8_0" else 256
+    nblk = -(-in_features // qk)
+    packed_rows, exact_rows = [], []
+    for _ in range(rows):
+        blocks, exact = [], []
+        for _ in range(nblk):
+            if fmt == "q8_0":
+                d, q = random_q8_0_fields(rng)
+                blocks.append(packing.pack_q8_0_block(d, q))
+                exact += q8_0_exact(d, q)
+            elif fmt == "q4_k":
+                d, dmin, sc, m, q = random_q4_k_fields(rng)
+                blocks.append(packing.pack_q4_k_block(d, dmin, sc, m, q))
+                exact += q4_k_exact(d, dmin, sc, m, q)
+            else:
+                d, sc, q = random_q6_k_fields(rng)
+                blocks.append(packing.pack_q6_k_block(d, sc, q))
+                exact += q6_k_exact(d, sc, q)
+        packed_rows.append(blocks)
+        exact_rows.append(exact[:in_features])
+    return packing.rows_to_array(packed_rows), exact_rows
+
+
+BRUTE_CASES = [("q8_0", 4, 32), ("q8_0", 8, 64), ("q4_k", 4, 256), ("q4_k", 8, 256),
+               ("q6_k", 4, 256), ("q6_k", 8, 256), ("q4_k", 4, 128), ("q6_k", 4, 128),
+               ("q4_k", 3, 384)]
+
+
+@pytest.mark.parametrize("fmt,rows,inf", BRUTE_CASES)
+def test_gemv_brute_force(fmt, rows, inf):
+    rng = np.random.default_rng([4, rows, inf])
+    data, exact_w = _build(fmt, rng, rows, inf)
+    x = rng.standard_normal((2, inf)).astype(np.float32)
+    bias = rng.normal(0, 0.02, rows).astype(np.float32)
+    y, s = oracle.gemv_packed(fmt, data, rows, inf, x, bias)
+    ex = _exact_gemv(exact_w, x, bias)
+    assert y.shape == (2, rows)
+    for b in range(2):
+        for o in range(rows):
+            err = abs(Fraction(float(y[b, o])) - ex[b][o])
+            assert err <= Fraction(2.0 ** -50) * Fraction(float(s[b, o])) + Fraction(1, 2 ** 200), (b, o)
+            # the error scale is sum |w x| + |b| itself
+            ref_s = sum(abs(wv * Fraction(float(xv))) for wv, xv in zip(exact_w[o], x[b])) \
+                + abs(Fraction(float(bias[o])))
+            assert abs(Fraction(float(s[b, o])) - ref_s) <= Fraction(2.0 ** -48) * ref_s
+
+
+@pytest.mark.parametrize("rows,inf", [(4, 32), (8, 64)])
+def test_i8row_brute_force(rows, inf):
+    rng = np.random.default_rng([5, rows])
+    codes = rng.integers(-127, 128, size=(rows, inf)).astype(np.int8)
+    scales = (rng.random(rows) * 0.01).astype(np.float32)
+    x = rng.standard_normal((3, inf)).astype(np.float32)
+    y, s = oracle.gemv_packed("i8row", codes.view(np.uint8), rows, inf, x, None, scales)
+    for b in range(3):
+        for o in range(rows):
+            ex = sum(Fraction(float(scales[o])) * int(codes[o, i]) * Fraction(float(x[b, i]))
+                     for i in range(inf))
+            assert abs(Fraction(float(y[b, o])) - ex) <= Fraction(2.0 ** -50) * Fraction(float(s[b, o]))
+
+
+# ---------------------------------------------------------------------------
+# 7. textbook reductions
+# ---------------------------------------------------------------------------
+def test_i8row_unit_scale_is_integer_matmul():
+    rng = np.random.default_rng(12)
+    codes = rng.integers(-127, 128, size=(16, 96)).astype(np.int8)
+    xi = rng.integers(-1000, 1000, size=(2, 96))
+    y, _ = oracle.gemv_packed("i8row", codes.view(np.uint8), 16, 96, xi.astype(np.float32),
+                              None, np.ones(16, np.float32))
+    assert np.array_equal(y, (xi @ codes.astype(np.int64).T).astype(np.float64))
+
+
+def test_gemm_f16_identity_and_brute_force():
+    rng = np.random.default_rng(13)
+    w = rng.normal(0, 0.02, size=(5, 8)).astype(np.float16)
+    bias = rng.normal(0, 0.02, 5).astype(np.float32)
+    eye = np.eye(8, dtype=np.float16)[:3]
+    y, _ = oracle.gemm_f16(eye, w, bias)
+    for m in range(3):
+        assert np.array_equal(y[m], w[:, m].astype(np.float64) + bias.astype(np.float64))
+    x = rng.standard_normal((3, 8)).astype(np.float16)
+    y, s = oracle.gemm_f16(x, w, bias)
+    for m in range(3):
+        for n in range(5):
+            ex = sum(Fraction(float(x[m, k])) * Fraction(float(w[n, k])) for k in range(8)) \
+                + Fraction(float(bias[n]))
+            assert abs(Fraction(float(y[m, n])) - ex) <= Fraction(2.0 ** -50) * Fraction(float(s[m, n]))
+
+
+def test_quantize_i8row_round_trip():
+    rng = np.random.default_rng(14)
+    w = rng.normal(0, 0.02, size=(32, 200)).astype(np.float32)
+    w[3] = 0.0
+    codes, scales = oracle.quantize_i8row(w)
+    assert scales[3] == 0 and np.all(codes[3] == 0)
+    for r in range(32):
+        if r == 3:
+            continue
+        assert scales[r] == np.float32(np.max(np.abs(w[r])) / 127.0)
+        amax_at = int(np.argmax(np.abs(w[r])))
+        assert abs(int(codes[r, amax_at])) == 127
+        deq = scales[r].astype(np.float64) * codes[r].astype(np.float64)
+        assert np.all(np.abs(deq - w[r]) <= scales[r] * 0.5 * (1 + 1e-6))
+    assert codes.min() >= -127 and codes.max() <= 127
+    # halves round away from zero
+    c, s = oracle.quantize_i8row(np.array([[127.0, 0.5, -0.5, 1.5, -2.5]], np.float32))
+    assert s[0] == 1.0 and list(c[0]) == [127, 1, -1, 2, -3]
+
+
+def test_tolerance_helper():
+    y_ref = np.array([[1.0, 2.0]])
+    s_ref = np.array([[10.0, 0.0]])
+    ok = oracle.within_tolerance(np.array([[1.0 + 9e-4, 2.0 + 2e-6]]), y_ref, s_ref, 1e-4)
+    assert list(ok[0]) == [True, False]
+
+
+# ---------------------------------------------------------------------------
+# 8. planted mistakes are caught by the pins above
+# ---------------------------------------------------------------------------
+def _all_dequant_fixtures_pass():
+    return all(check_dequant_fixture(n) and check_gemv_fixture(n) for n in golden_io.all_fixtures())
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    mod = oracle.oracle
+    good_codes4, good_codes6, good_sm = mod.q4_k_codes, mod.q6_k_codes, mod.q4_k_scales_mins
+    good_gemv = mod.gemv
+    assert _all_dequant_fixtures_pass()
+
+    def codes4_swapped(qs):          # low/high nibble order exchanged
+        q = good_codes4(qs)
+        out = q.copy()
+        for r in range(4):
+            out[..., 64 * r:64 * r + 32] = q[..., 64 * r + 32:64 * r + 64]
+            out[..., 64 * r + 32:64 * r + 64] = q[..., 64 * r:64 * r + 32]
+        return out
+
+    def sm_swapped(S):               # scales and mins exchanged
+        sc, m = good_sm(S)
+        return m, sc
+
+    def sm_no_high_bits(S):          # top bits of scales 4..7 dropped
+        sc, m = good_sm(S)
+        sc = sc.copy()
+        sc[..., 4:] &= 15
+        return sc, m
+
+    def codes6_offset(ql, qh):       # high 2 bits in the wrong place
+        q = good_codes6(ql, qh)
+        return (q & 15) | ((q >> 4) << 5) & 63
+
+    def gemv_no_bias(w64, x, bias=None):
+        return good_gemv(w64, x, None)
+
+    for name, bad in [("q4_k_codes", codes4_swapped), ("q4_k_scales_mins", sm_swapped),
+                      ("q4_k_scales_mins", sm_no_high_bits), ("q6_k_codes", codes6_offset),
+                      ("gemv", gemv_no_bias)]:
+        monkeypatch.setattr(mod, name, bad)
+        assert not _all_dequant_fixtures_pass(), name
+        monkeypatch.undo()
+    assert _all_dequant_fixtures_pass()
+
+
+def test_planted_transpose_and_dropped_min_are_caught(monkeypatch):
+    mod = oracle.oracle
+    # a dropped min term in Q4_K
+    good = mod.dequant_q4_k
+
+    def no_min(packed, rows, in_features):
+        blk = mod._blocks(packed, rows, in_features, "q4_k")
+        d = mod._binary16(blk[:, :, 0:2])
+        sc, _ = mod.q4_k_scales_mins(blk[:, :, 4:16])
+        q = mod.q4_k_codes(blk[:, :, 16:144])
+        sub = np.arange(256) // 32
+        return (d[:, :, None] * sc[:, :, sub] * q).reshape(rows, -1)[:, :in_features]
+
+    monkeypatch.setattr(mod, "dequant_q4_k", no_min)
+    assert not check_dequant_fixture("q4_k_hand.txt")
+    monkeypatch.setattr(mod, "dequant_q4_k", good)
+
+    # a transposed operand in the mat-vec: caught by a non-square brute force
+    def transposed(w64, x, bias=None):
+        x64 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+        wt = w64.T.reshape(w64.shape)           # same shape, wrong element order
+        y = x64 @ wt.T
+        s = np.abs(x64) @ np.abs(wt).T
+        if bias is not None:
+            y = y + bias
+            s = s + np.abs(bias)
+        return y, s
+
+    monkeypatch.setattr(mod, "gemv", transposed)
+    with pytest.raises(AssertionError):
+        test_gemv_brute_force("q8_0", 4, 32)
