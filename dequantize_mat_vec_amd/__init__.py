@@ -1,0 +1,17 @@
+"""MI355X (gfx950) fused dequantize + mat-vec for block-quantized weights.
+
+y = W x + b with W in Q8_0, Q4_K, Q6_K or per-row int8 and x, y in float32,
+plus a small-M binary16 linear layer, all as hand-written HIP kernels behind
+the C ABI of include/pesti.h.  This package is the thin Python binding
+(argument marshalling only) and the seeded synthetic-input generator.
+"""
+from ._lib import (FORMAT_IDS, LIB_PATH, PESTI_ERR_ALIGN, PESTI_ERR_BATCH,  # noqa: F401
+                   PESTI_ERR_DEVICE, PESTI_ERR_LAUNCH, PESTI_ERR_NULL, PESTI_ERR_SHAPE,
+                   PESTI_OK, PestiError, dequant, gemv, load, pesti_abi_version,
+                   pesti_dequant_i8row, pesti_dequant_q4_k, pesti_dequant_q6_k,
+                   pesti_dequant_q8_0, pesti_gemm_f16_smallm, pesti_gemv_i8row,
+                   pesti_gemv_q4_k, pesti_gemv_q6_k, pesti_gemv_q8_0, pesti_row_bytes,
+                   strerror)
+
+__all__ = [n for n in dir() if n.startswith("pesti_")] + [
+    "PestiError", "gemv", "dequant", "load", "strerror", "FORMAT_IDS", "LIB_PATH"]

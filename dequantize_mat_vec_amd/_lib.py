@@ -1,0 +1,180 @@
+"""ctypes binding of libpesti.so (the C ABI declared in include/pesti.h).
+
+Argument marshalling only: every function here has the C entry point's name
+and arguments, accepts torch tensors (device memory) or raw integer device
+pointers, fills in the current torch stream when none is given, calls the
+library and raises PestiError on a non-zero status.  All arithmetic happens
+in the HIP kernels; there is no fallback of any kind - if the shared library
+is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().with_name("libpesti.so")
+
+PESTI_OK = 0
+PESTI_ERR_NULL = -1
+PESTI_ERR_SHAPE = -2
+PESTI_ERR_BATCH = -3
+PESTI_ERR_ALIGN = -4
+PESTI_ERR_LAUNCH = -5
+PESTI_ERR_DEVICE = -6
+
+FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3}
+
+_i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+_c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
+
+_SIGNATURES = {
+    "pesti_gemv_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
+    "pesti_row_bytes": (_i64, [_i32, _i64]),
+    "pesti_strerror": (_c_char_p, [_c_int]),
+    "pesti_abi_version": (_i32, []),
+}
+
+_lib = None
+
+
+class PestiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+def load(path: os.PathLike | None = None) -> ctypes.CDLL:
+    """Load libpesti.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"{p} is missing: build the HIP library first "
+                          "(python -m dequantize_mat_vec_amd.build)")
+    lib = ctypes.CDLL(str(p))
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(obj):
+    """Device pointer of a torch tensor, an int, or None (NULL)."""
+    if obj is None:
+        return None
+    if isinstance(obj, int):
+        return obj
+    if hasattr(obj, "data_ptr"):
+        if not obj.is_cuda:
+            raise ValueError("tensor arguments must live in device memory")
+        if not obj.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous")
+        return obj.data_ptr()
+    raise TypeError(f"cannot pass {type(obj).__name__} as a device pointer")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(name: str, status: int) -> int:
+    if status != PESTI_OK:
+        raise PestiError(name, status)
+    return status
+
+
+def strerror(status: int) -> str:
+    return load().pesti_strerror(status).decode()
+
+
+def pesti_abi_version() -> int:
+    return load().pesti_abi_version()
+
+
+def pesti_row_bytes(fmt, in_features: int) -> int:
+    fid = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
+    return load().pesti_row_bytes(fid, in_features)
+
+
+def _gemv(name, out_features, in_features, blocks, x, y, bias, batch, stream):
+    fn = getattr(load(), name)
+    return _check(name, fn(out_features, in_features, _ptr(blocks), _ptr(x), _ptr(y),
+                           _ptr(bias), batch, _stream(stream)))
+
+
+def pesti_gemv_q8_0(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q8_0", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
+def pesti_gemv_q4_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q4_k", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
+def pesti_gemv_q6_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q6_k", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
+def pesti_gemv_i8row(out_features, in_features, codes, row_scales, x, y, bias=None, batch=1,
+                     stream=None):
+    return _check("pesti_gemv_i8row", load().pesti_gemv_i8row(
+        out_features, in_features, _ptr(codes), _ptr(row_scales), _ptr(x), _ptr(y), _ptr(bias),
+        batch, _stream(stream)))
+
+
+def pesti_gemm_f16_smallm(m, out_features, in_features, w, x, y, bias=None, stream=None):
+    return _check("pesti_gemm_f16_smallm", load().pesti_gemm_f16_smallm(
+        m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias), _stream(stream)))
+
+
+def _dequant(name, rows, in_features, blocks, w_out, stream):
+    return _check(name, getattr(load(), name)(rows, in_features, _ptr(blocks), _ptr(w_out),
+                                              _stream(stream)))
+
+
+def pesti_dequant_q8_0(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q8_0", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_q4_k(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q4_k", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_q6_k(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q6_k", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_i8row(rows, in_features, codes, row_scales, w_out, stream=None):
+    return _check("pesti_dequant_i8row", load().pesti_dequant_i8row(
+        rows, in_features, _ptr(codes), _ptr(row_scales), _ptr(w_out), _stream(stream)))
+
+
+# --- format-generic conveniences (still marshalling only) -------------------
+def gemv(fmt, out_features, in_features, w, x, y, bias=None, batch=1, scales=None, stream=None):
+    """Dispatch y = W x + b to the entry point of format `fmt`."""
+    if fmt == "i8row":
+        return pesti_gemv_i8row(out_features, in_features, w, scales, x, y, bias, batch, stream)
+    return _gemv(f"pesti_gemv_{fmt}", out_features, in_features, w, x, y, bias, batch, stream)
+
+
+def dequant(fmt, rows, in_features, w, w_out, scales=None, stream=None):
+    if fmt == "i8row":
+        return pesti_dequant_i8row(rows, in_features, w, scales, w_out, stream)
+    return _dequant(f"pesti_dequant_{fmt}", rows, in_features, w, w_out, stream)

@@ -1,0 +1,66 @@
+// Host-only part of the C ABI: device check, packed row sizes, status text.
+#include <atomic>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per device: 0 = unknown, 1 = gfx950, 2 = other.  Benign races only (every
+// writer stores the same value).
+std::atomic<int> g_arch[kMaxDevices];
+std::atomic<size_t> g_lds[kMaxDevices];
+
+}  // namespace
+
+namespace pesti_host {
+
+int current_device(int* device, size_t* lds_per_group) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PESTI_ERR_DEVICE;
+  int known = g_arch[dev].load(std::memory_order_relaxed);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PESTI_ERR_DEVICE;
+    known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_lds[dev].store(prop.sharedMemPerBlock, std::memory_order_relaxed);
+    g_arch[dev].store(known, std::memory_order_relaxed);
+  }
+  if (known != 1) return PESTI_ERR_DEVICE;
+  *device = dev;
+  *lds_per_group = g_lds[dev].load(std::memory_order_relaxed);
+  return PESTI_OK;
+}
+
+}  // namespace pesti_host
+
+extern "C" {
+
+int64_t pesti_row_bytes(int32_t format, int64_t in_features) {
+  if (in_features < 0 || in_features % 32 != 0) return -1;
+  switch (format) {
+    case PESTI_FMT_Q8_0: return (in_features / 32) * 34;
+    case PESTI_FMT_Q4_K: return ((in_features + 255) / 256) * 144;
+    case PESTI_FMT_Q6_K: return ((in_features + 255) / 256) * 210;
+    case PESTI_FMT_I8ROW: return in_features;
+    default: return -1;
+  }
+}
+
+const char* pesti_strerror(int status) {
+  switch (status) {
+    case PESTI_OK: return "success";
+    case PESTI_ERR_NULL: return "a required pointer is NULL";
+    case PESTI_ERR_SHAPE: return "unsupported shape (negative size, in_features not a multiple of 32, or too large)";
+    case PESTI_ERR_BATCH: return "batch (or GEMM m) out of range";
+    case PESTI_ERR_ALIGN: return "pointer not aligned (16 bytes for data, 4 for bias/scales)";
+    case PESTI_ERR_LAUNCH: return "HIP kernel launch failed";
+    case PESTI_ERR_DEVICE: return "current HIP device is missing or not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int32_t pesti_abi_version(void) { return PESTI_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// Shared device and host helpers of the gfx950 mat-vec kernels.
+//
+// Execution model used by every mat-vec kernel (one wavefront per row tile):
+//   * a workgroup is 4 wavefronts of 64 lanes;
+//   * a row is served by a group of L lanes (L = 16, 32 or 64), so a wave
+//     holds 64/L rows at once; each lane walks the row's "units" (a fixed
+//     run of packed bytes and the weights it encodes) with stride L;
+//   * x (and, for Q4_K, its per-32 sums) is staged once per workgroup in
+//     LDS; weights stream from HBM straight into registers and are decoded
+//     there, never written back;
+//   * per-lane float32 partial sums are combined across the L lanes with
+//     DPP row operations (plus one swizzle step per doubling beyond 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pesti.h"
+
+namespace pesti {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWave * kWavesPerGroup;
+
+// ---------------------------------------------------------------------------
+// LDS layout of x: logical float i lives at phys(i) = i + 4 * (i / 64), i.e.
+// every 64-float chunk is followed by 4 padding floats.  Lanes of a row group
+// read 64-float chunks 64 floats apart; the padding puts consecutive chunks
+// 16 bytes apart in bank space so their 16-byte reads do not collide.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int64_t xs_phys(int64_t i) { return i + 4 * (i >> 6); }
+
+// Floats of LDS per staged batch row when the row is padded to `pad_to`.
+__host__ __device__ constexpr int64_t xs_stride(int64_t in_features, int64_t pad_to) {
+  return xs_phys(((in_features + pad_to - 1) / pad_to) * pad_to);
+}
+
+// Unaligned-safe vector types: global loads of these need only 4-byte
+// alignment.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4), aligned(16)));
+
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 load_u32x4_a16(const void* p) {
+  return *reinterpret_cast<const u32x4a*>(p);
+}
+__device__ __forceinline__ uint32_t load_u32(const void* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+__device__ __forceinline__ uint16_t load_u16(const void* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// binary16 bit pattern (low 16 bits) -> float32, exact (subnormals kept).
+__device__ __forceinline__ float f16_lo(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits >> 16)));
+}
+
+// Signed byte k of a dword as float32 (one SDWA sign-extending convert).
+template <int K>
+__device__ __forceinline__ float sbyte(uint32_t v) {
+  return static_cast<float>(static_cast<int8_t>(v >> (8 * K)));
+}
+// Unsigned byte k of a dword as float32 (v_cvt_f32_ubyte{k}).
+template <int K>
+__device__ __forceinline__ float ubyte(uint32_t v) {
+  return static_cast<float>((v >> (8 * K)) & 0xFFu);
+}
+
+// (hi:lo) >> (8 * shift) for shift in 0..3 (v_alignbyte_b32).
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t shift) {
+  return __builtin_amdgcn_alignbyte(hi, lo, shift);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums within groups of L lanes; every lane of the group ends with
+// the group's total.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(L == 16 || L == 32 || L == 64, "group of 16, 32 or 64 lanes");
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp<0x141>(v);   // row_half_mirror: lane i <-> 7 - i within 8
+  v += dpp<0x140>(v);   // row_mirror: lane i <-> 15 - i within 16
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Stage x [batch][in] (float32, global) into LDS in the padded layout, zero
+// filling logical columns in..padded_len-1.
+// ---------------------------------------------------------------------------
+template <int B>
+__device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int64_t in_features,
+                                        int64_t padded_len, int64_t stride) {
+  const int64_t n4 = padded_len >> 2;   // float4 slots per row
+  for (int b = 0; b < B; ++b) {
+    const float* xb = x + b * in_features;
+    float* dst = xs + b * stride;
+    for (int64_t s = threadIdx.x; s < n4; s += kThreads) {
+      const int64_t i = s << 2;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (i < in_features) v = *reinterpret_cast<const f32x4*>(xb + i);
+      *reinterpret_cast<f32x4*>(dst + xs_phys(i)) = v;
+    }
+  }
+}
+
+// Read 4 consecutive logical floats starting at logical index i (i % 4 == 0).
+__device__ __forceinline__ f32x4 xs4(const float* xs, int64_t i) {
+  return *reinterpret_cast<const f32x4*>(xs + xs_phys(i));
+}
+
+}  // namespace pesti
+
+// ---------------------------------------------------------------------------
+// Host-side helpers shared by the entry points.
+// ---------------------------------------------------------------------------
+namespace pesti_host {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks that the current device is gfx950 and reports its per-workgroup
+// LDS limit.  Returns PESTI_OK or PESTI_ERR_DEVICE.
+int current_device(int* device, size_t* lds_per_group);
+
+// Largest batch that fits LDS when one staged row takes `bytes_per_row`.
+inline int batch_per_launch(size_t lds_limit, size_t bytes_per_row, size_t fixed_bytes, int batch) {
+  if (bytes_per_row == 0) return batch;
+  size_t room = lds_limit > fixed_bytes ? lds_limit - fixed_bytes : 0;
+  size_t fit = room / bytes_per_row;
+  return fit >= static_cast<size_t>(batch) ? batch : static_cast<int>(fit);
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
+// Workgroups for a grid-stride kernel over `tiles` row tiles.
+inline unsigned grid_for(int64_t tiles, int64_t cap) {
+  int64_t g = tiles < cap ? tiles : cap;
+  return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+}  // namespace pesti_host

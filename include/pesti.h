@@ -1,0 +1,149 @@
+/*
+ * pesti.h - C ABI of the MI355X (gfx950) quantized mat-vec library.
+ *
+ * What is computed
+ *   The decode-step linear layer y = W x (+ b) with block-quantized W, as the
+ *   row-major matrix-vector product that dominates a decode step and the
+ *   fused dequantize + mat-vec that never expands W to float32 ("Project
+ *   scaffold: modules, CLI, and correctness harness", file summaries of
+ *   tensor.rs and quant.rs), over the GGUF K-family formats that "PESTI -
+ *   Portable Execution Substrate for Transformer Inference" dequantizes
+ *   byte-exactly ("What This Is").  The same boundary carries the small-M
+ *   prompt-width linear layer x @ w + b ("inferno" README, "Design notes"
+ *   and "Benchmarks": c_attn / c_proj / mlp_fc at 32 prompt tokens).
+ *
+ * Block formats (the pages name them; the byte layouts are the GGUF ones):
+ *   Q8_0   34 B / 32 weights : binary16 d, int8 q[32].          w = d*q
+ *   Q4_K  144 B / 256 weights: binary16 d, binary16 dmin, 12 B of packed
+ *          6-bit scales sc[8] and mins m[8], 128 B of 4-bit codes.
+ *                                                  w = d*sc[j]*q - dmin*m[j]
+ *   Q6_K  210 B / 256 weights: 128 B low 4-bit parts, 64 B high 2-bit parts,
+ *          int8 sc[16], binary16 d.                w = d*sc[i/16]*(q - 32)
+ *   i8row int8 codes [out][in] plus one float32 scale per row. w = s[o]*q
+ *
+ * Layouts and conventions (every entry point)
+ *   - W has out_features rows.  A packed row is ceil(in/QK) whole blocks
+ *     (QK = 32 for Q8_0, 256 for Q4_K/Q6_K); rows follow each other with
+ *     stride pesti_row_bytes(format, in_features) bytes.  When in_features
+ *     is not a multiple of 256, the columns in_features..end of the last
+ *     super-block are padding: they are never read into the result and
+ *     their bytes may hold anything.
+ *   - x is float32 [batch][in_features], y is float32 [batch][out_features],
+ *     bias is float32 [out_features] or NULL.  y is overwritten:
+ *     y[b][o] = sum_i w[o][i] * x[b][i] + bias[o].
+ *   - Accumulation is float32; dequantized weights are never written out.
+ *     Result bound: |y - exact| <= 1e-4 * sum_i |w_i x_i| + 1e-6 for the
+ *     mat-vec (2e-3 for the f16 GEMM).
+ *   - Pointers are device pointers owned by the caller, on the calling
+ *     thread's current HIP device, and must be 16-byte aligned (blocks, x,
+ *     y, w, codes; bias and row_scales 4-byte aligned).  x and y must not
+ *     overlap.  `stream` is a hipStream_t (NULL = the legacy default
+ *     stream).
+ *   - Calls only enqueue work on `stream` and return; they never allocate,
+ *     free or synchronize, and keep no state between calls, so they may be
+ *     issued concurrently on any number of streams.
+ *
+ * Errors
+ *   Return 0 on success or a negative PESTI_ERR_* code.  On any non-zero
+ *   return nothing was enqueued and y is untouched.  An empty output
+ *   (out_features == 0 or batch == 0, or rows == 0 for dequant) returns 0
+ *   without touching any pointer.  in_features == 0 is a valid shape:
+ *   y = bias (or 0).  Faults inside a kernel surface at the caller's next
+ *   synchronization, as with any HIP kernel.  Nothing falls back to the CPU.
+ */
+#ifndef PESTI_H
+#define PESTI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PESTI_ABI_VERSION 1
+
+#define PESTI_OK 0
+#define PESTI_ERR_NULL (-1)   /* a required pointer is NULL                 */
+#define PESTI_ERR_SHAPE (-2)  /* negative size, in_features % 32 != 0, or  */
+                              /* in_features above PESTI_MAX_IN_FEATURES    */
+#define PESTI_ERR_BATCH (-3)  /* batch outside [0, 8]; GEMM m outside [0,  */
+                              /* PESTI_MAX_GEMM_M]                           */
+#define PESTI_ERR_ALIGN (-4)  /* a pointer breaks the alignment rule above  */
+#define PESTI_ERR_LAUNCH (-5) /* the HIP launch reported an error           */
+#define PESTI_ERR_DEVICE (-6) /* current device is not gfx950, or no device */
+
+#define PESTI_FMT_Q8_0 0
+#define PESTI_FMT_Q4_K 1
+#define PESTI_FMT_Q6_K 2
+#define PESTI_FMT_I8ROW 3
+
+#define PESTI_MAX_BATCH 8
+#define PESTI_MAX_IN_FEATURES 32768
+#define PESTI_MAX_GEMM_M 4096
+
+/* --- quantized mat-vec, y = W x + b ------------------------------------ */
+
+/* Q8_0 (34-byte blocks of 32 weights).  blocks: out_features rows of
+ * in_features/32 blocks.  batch in [0, 8]. */
+int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+
+/* Q4_K (144-byte super-blocks of 256 weights, rows padded to whole
+ * super-blocks).  Same arguments as pesti_gemv_q8_0. */
+int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+
+/* Q6_K (210-byte super-blocks of 256 weights, rows padded to whole
+ * super-blocks).  Same arguments as pesti_gemv_q8_0. */
+int pesti_gemv_q6_k(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+
+/* Per-row symmetric int8 ("Project scaffold ...", quant.rs): codes int8
+ * [out][in] row-major, row_scales float32 [out]. */
+int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* codes,
+                     const float* row_scales, const float* x, float* y,
+                     const float* bias, int32_t batch, void* stream);
+
+/* --- small-M binary16 linear layer, Y = X W^T + b ------------------------
+ * X binary16 [m][in], W binary16 [out][in] (the same row orientation as the
+ * mat-vec; a GPT-2 c_attn "768x2304" has in = 768, out = 2304), Y float32
+ * [m][out], bias float32 [out] or NULL.  m in [0, PESTI_MAX_GEMM_M]; float32
+ * accumulation; matrix cores for m >= 16, vector ALUs below. */
+int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                          const uint16_t* w, const uint16_t* x, float* y,
+                          const float* bias, void* stream);
+
+/* --- dequantization to float32 (bit-exact; checks the unpacking) --------
+ * w_out float32 [rows][in_features]: each weight rounded once from its
+ * exact value (all formats here dequantize exactly in float32 except the
+ * final subtraction of Q4_K and the scale product of i8row). */
+int pesti_dequant_q8_0(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_q6_k(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_i8row(int64_t rows, int64_t in_features, const int8_t* codes,
+                        const float* row_scales, float* w_out, void* stream);
+
+/* --- host-only helpers (no device work) --------------------------------- */
+
+/* Packed bytes per row for a PESTI_FMT_* format (code bytes only for
+ * i8row); -1 for an unknown format or a negative / non-multiple-of-32
+ * in_features. */
+int64_t pesti_row_bytes(int32_t format, int64_t in_features);
+
+/* Static text for a status code. */
+const char* pesti_strerror(int status);
+
+/* PESTI_ABI_VERSION of the built library. */
+int32_t pesti_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PESTI_H */

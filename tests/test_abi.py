@@ -1,0 +1,134 @@
+"""The C ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-only logic (row sizes, status text, argument checks
+that reject a call before any device work) behaves as documented."""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import oracle
+import dequantize_mat_vec_amd as dmv
+from dequantize_mat_vec_amd import _lib, synth
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "pesti.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pesti_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(_lib.LIB_PATH))
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib._SIGNATURES), "binding and header disagree"
+
+
+def test_header_constants_match_binding():
+    text = HEADER.read_text()
+    for name in ("PESTI_OK", "PESTI_ERR_NULL", "PESTI_ERR_SHAPE", "PESTI_ERR_BATCH",
+                 "PESTI_ERR_ALIGN", "PESTI_ERR_LAUNCH", "PESTI_ERR_DEVICE"):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(_lib, name), name
+    for fmt, fid in _lib.FORMAT_IDS.items():
+        m = re.search(rf"#define PESTI_FMT_{fmt.upper()} (\d+)", text)
+        assert m and int(m.group(1)) == fid
+
+
+def test_abi_version():
+    assert dmv.pesti_abi_version() == 1
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "i8row"])
+@pytest.mark.parametrize("inf", [0, 32, 64, 96, 256, 288, 768, 896, 4864, 16384])
+def test_row_bytes_agree_with_oracle_and_generator(fmt, inf):
+    rb = dmv.pesti_row_bytes(fmt, inf)
+    assert rb == oracle.row_bytes(fmt, inf) == synth.packed_row_bytes(fmt, inf)
+
+
+def test_row_bytes_rejects_bad_input():
+    assert dmv.pesti_row_bytes(0, 33) == -1
+    assert dmv.pesti_row_bytes(0, -32) == -1
+    assert dmv.pesti_row_bytes(9, 64) == -1
+
+
+def test_strerror_covers_every_status():
+    for st in range(-6, 1):
+        assert dmv.strerror(st) and dmv.strerror(st) != "unknown status"
+    assert dmv.strerror(-99) == "unknown status"
+
+
+# Argument checks that fire before any device query: safe with or without a
+# GPU because nothing is launched.
+FAKE = 0x100000   # 16-byte aligned, never dereferenced (calls are rejected)
+
+
+def _raw():
+    return _lib.load()
+
+
+@pytest.mark.parametrize("name", ["pesti_gemv_q8_0", "pesti_gemv_q4_k", "pesti_gemv_q6_k"])
+def test_gemv_argument_checks(name):
+    fn = getattr(_raw(), name)
+    assert fn(-1, 64, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(8, -32, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(8, 64, FAKE, FAKE, FAKE, None, 9, None) == _lib.PESTI_ERR_BATCH
+    assert fn(8, 64, FAKE, FAKE, FAKE, None, -1, None) == _lib.PESTI_ERR_BATCH
+    assert fn(8, 48, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(8, 65536, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(8, 64, None, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(8, 64, FAKE, None, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(8, 64, FAKE, FAKE, None, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(8, 64, FAKE + 4, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(8, 64, FAKE, FAKE + 8, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(8, 64, FAKE, FAKE, FAKE + 4, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(8, 64, FAKE, FAKE, FAKE, FAKE + 2, 1, None) == _lib.PESTI_ERR_ALIGN
+    # empty outputs succeed without touching anything (NULL pointers allowed)
+    assert fn(0, 64, None, None, None, None, 1, None) == _lib.PESTI_OK
+    assert fn(8, 64, None, None, None, None, 0, None) == _lib.PESTI_OK
+
+
+def test_i8row_and_gemm_argument_checks():
+    lib = _raw()
+    assert lib.pesti_gemv_i8row(8, 64, FAKE, None, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_gemv_i8row(8, 64, FAKE, FAKE + 2, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemm_f16_smallm(-1, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
+    assert lib.pesti_gemm_f16_smallm(5000, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
+    assert lib.pesti_gemm_f16_smallm(4, 8, 40, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemm_f16_smallm(4, 8, 64, None, FAKE, FAKE, None, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_gemm_f16_smallm(4, 8, 64, FAKE, FAKE, FAKE + 4, None, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemm_f16_smallm(0, 8, 64, None, None, None, None, None) == _lib.PESTI_OK
+
+
+@pytest.mark.parametrize("name", ["pesti_dequant_q8_0", "pesti_dequant_q4_k", "pesti_dequant_q6_k"])
+def test_dequant_argument_checks(name):
+    fn = getattr(_raw(), name)
+    assert fn(-1, 64, FAKE, FAKE, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(4, 40, FAKE, FAKE, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(4, 64, None, FAKE, None) == _lib.PESTI_ERR_NULL
+    assert fn(4, 64, FAKE, FAKE + 4, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(0, 64, None, None, None) == _lib.PESTI_OK
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(_lib.PestiError) as e:
+        dmv.pesti_gemv_q8_0(8, 48, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == _lib.PESTI_ERR_SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        dmv.pesti_gemv_q8_0(1, 32, torch.zeros(34, dtype=torch.uint8), FAKE, FAKE, stream=0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(tmp_path / "libpesti.so")

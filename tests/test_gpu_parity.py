@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: dequantized weights bit-exact (value equality with the oracle's
+float32 rounding); mat-vec |y - y_oracle| <= 1e-4 * sum|w x| + 1e-6; binary16
+GEMM the same with 2e-3.  Inputs come from the seeded generator; shapes span
+several row tiles and ragged tails; the full decode-step shapes are checked
+on sampled rows in the launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dequantize_mat_vec_amd import synth
+from gpu_util import announce, assert_within, run_dequant, run_gemm, run_gemv
+
+pytestmark = pytest.mark.gpu
+
+GEMV_REL = 1e-4
+GEMM_REL = 2e-3
+FORMATS = ("q8_0", "q4_k", "q6_k", "i8row")
+
+
+@pytest.fixture(autouse=True)
+def _name_case(request):
+    announce(request.node.nodeid)
+    yield
+
+
+def make(fmt, out, inf, seed, batch=1, with_bias=True):
+    rng = np.random.default_rng([777, seed, out, inf, batch])
+    packed, scales = synth.matrix(fmt, rng, out, inf)
+    x = synth.activations(rng, batch, inf)
+    bias = synth.bias(rng, out) if with_bias else None
+    return packed, scales, x, bias
+
+
+# ---------------------------------------------------------------------------
+# dequantization: bit-exact
+# ---------------------------------------------------------------------------
+DEQUANT_SHAPES = [(1, 32), (7, 256), (19, 896), (33, 288), (5, 4864)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,inf", DEQUANT_SHAPES)
+def test_dequant_bit_exact(fmt, rows, inf):
+    packed, scales, _, _ = make(fmt, rows, inf, 1)
+    got = run_dequant(fmt, packed, scales, rows, inf)
+    want = oracle.dequantize_f32(fmt, packed, rows, inf, scales)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
+def test_dequant_forced_scales(fmt, d_bits):
+    rng = np.random.default_rng([5, d_bits])
+    packed = synth.quant_blocks(fmt, rng, 9, 512, force_d=d_bits)
+    got = run_dequant(fmt, packed, None, 9, 512)
+    assert np.array_equal(got, oracle.dequantize_f32(fmt, packed, 9, 512))
+
+
+# ---------------------------------------------------------------------------
+# mat-vec parity
+# ---------------------------------------------------------------------------
+GEMV_SHAPES = [(1, 32), (5, 64), (67, 896), (130, 288), (37, 1056), (300, 4864), (16, 768)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("out,inf", GEMV_SHAPES)
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_parity(fmt, out, inf, batch):
+    packed, scales, x, bias = make(fmt, out, inf, 2, batch)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} {out}x{inf} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("batch", [2, 4, 5, 6, 7])
+def test_gemv_every_batch(fmt, batch):
+    packed, scales, x, bias = make(fmt, 45, 896, 3, batch)
+    y = run_gemv(fmt, packed, scales, 45, 896, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, 45, 896, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemv_large_in_batch_split(fmt):
+    """A staged x that cannot hold every batch row at once is split."""
+    packed, scales, x, bias = make(fmt, 24, 16384, 4, 8)
+    y = run_gemv(fmt, packed, scales, 24, 16384, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, 24, 16384, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} in=16384 b8")
+
+
+# ---------------------------------------------------------------------------
+# invariants and edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_one_hot_x_gives_dequantized_column(fmt):
+    """x = e_j makes y column j of W, bit-exact: every other term is 0."""
+    out, inf = 40, 896
+    packed, scales, _, _ = make(fmt, out, inf, 5)
+    w32 = oracle.dequantize_f32(fmt, packed, out, inf, scales)
+    cols = [0, 1, 31, 32, 255, 256, 511, 767, 768, 895]
+    x = np.zeros((8, inf), np.float32)
+    for b, j in enumerate(cols[:8]):
+        x[b, j] = 1.0
+    y = run_gemv(fmt, packed, scales, out, inf, x)
+    for b, j in enumerate(cols[:8]):
+        assert np.array_equal(y[b], w32[:, j]), (fmt, j)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_power_of_two_scaling_is_exact(fmt):
+    out, inf = 50, 896
+    packed, scales, x, _ = make(fmt, out, inf, 6)
+    y1 = run_gemv(fmt, packed, scales, out, inf, x)
+    y2 = run_gemv(fmt, packed, scales, out, inf, x * np.float32(8.0))
+    assert np.array_equal(y2, y1 * np.float32(8.0))
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+def test_padding_bytes_do_not_matter(fmt):
+    """Rows of 896 hold 3.5 super-blocks; the padding half must be ignored."""
+    out, inf = 33, 896
+    packed, _, x, bias = make(fmt, out, inf, 7)
+    rng = np.random.default_rng(99)
+    other = packed.copy().reshape(out, -1)
+    nb = 144 if fmt == "q4_k" else 210
+    last = other[:, 3 * nb:4 * nb]
+    if fmt == "q4_k":
+        last[:, 16 + 64:] = rng.integers(0, 256, last[:, 16 + 64:].shape, dtype=np.uint8)
+        last[:, 12:16] = rng.integers(0, 256, last[:, 12:16].shape, dtype=np.uint8)
+        last[:, 4:12] = (last[:, 4:12] & 0x3F) | (rng.integers(0, 4, last[:, 4:12].shape,
+                                                             dtype=np.uint8) << 6)
+    else:
+        last[:, 64:128] = rng.integers(0, 256, last[:, 64:128].shape, dtype=np.uint8)
+        last[:, 160:192] = rng.integers(0, 256, last[:, 160:192].shape, dtype=np.uint8)
+        last[:, 200:208] = rng.integers(0, 256, last[:, 200:208].shape, dtype=np.uint8)
+    y1 = run_gemv(fmt, packed, None, out, inf, x, bias)
+    y2 = run_gemv(fmt, other, None, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_in_features_zero_gives_bias(fmt):
+    rng = np.random.default_rng(8)
+    bias = synth.bias(rng, 21)
+    import torch
+    from gpu_util import guarded_y, guards_intact, to_dev
+    import dequantize_mat_vec_amd as dmv
+    fbuf, y = guarded_y(2 * 21)
+    scales = to_dev(np.ones(21, np.float32)) if fmt == "i8row" else None
+    dmv.gemv(fmt, 21, 0, None, None, y, to_dev(bias), 2, scales=scales)
+    torch.cuda.synchronize()
+    assert guards_intact(fbuf, 42)
+    got = y.cpu().numpy().reshape(2, 21)
+    assert np.array_equal(got, np.stack([bias, bias]))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_empty_output_touches_nothing(fmt):
+    import torch
+    from gpu_util import guarded_y, guards_intact
+    import dequantize_mat_vec_amd as dmv
+    fbuf, y = guarded_y(0)
+    dmv.gemv(fmt, 0, 64, None, None, y, None, 1)
+    dmv.gemv(fmt, 16, 64, None, None, y, None, 0)
+    torch.cuda.synchronize()
+    assert guards_intact(fbuf, 0)
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
+def test_gemv_forced_scales(fmt, d_bits):
+    rng = np.random.default_rng([9, d_bits])
+    packed = synth.quant_blocks(fmt, rng, 40, 896, force_d=d_bits)
+    x = synth.activations(rng, 2, 896)
+    y = run_gemv(fmt, packed, None, 40, 896, x)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, 40, 896, x)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} d={d_bits:#06x}")
+
+
+def test_q6_k_all_codes_32_is_zero():
+    """q = 32 everywhere dequantizes to 0: y must equal the bias exactly
+    (the (q - 32) factor is formed exactly, never as q*x - 32*x)."""
+    rng = np.random.default_rng(10)
+    out, inf = 20, 896
+    packed = synth.quant_blocks("q6_k", rng, out, inf).reshape(out, -1, 210)
+    packed[:, :, 0:128] = 0x00      # low parts 0
+    packed[:, :, 128:192] = 0xAA    # high parts 2 -> q = 32
+    packed = packed.reshape(out, -1)
+    assert np.all(oracle.dequant_q6_k(packed, out, inf) == 0)
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q6_k", packed, None, out, inf, x, bias)
+    assert np.array_equal(y[0], bias)
+
+
+def test_q8_0_zero_codes_is_exact_bias():
+    rng = np.random.default_rng(11)
+    out, inf = 20, 896
+    packed = synth.quant_blocks("q8_0", rng, out, inf).reshape(out, -1, 34)
+    packed[:, :, 2:] = 0
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q8_0", packed.reshape(out, -1), None, out, inf, x, bias)
+    assert np.array_equal(y[0], bias)
+
+
+def test_odd_rows_misaligned_blocks():
+    """Q8_0 rows of an odd block count start 2 bytes off a dword boundary;
+    Q6_K super-blocks do so every other one."""
+    for fmt, inf in (("q8_0", 96), ("q8_0", 4896), ("q6_k", 4864), ("q6_k", 1280)):
+        packed, scales, x, bias = make(fmt, 31, inf, 12, 2)
+        y = run_gemv(fmt, packed, scales, 31, inf, x, bias)
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, 31, inf, x, bias, scales)
+        assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} in={inf}")
+
+
+# ---------------------------------------------------------------------------
+# full decode-step shapes, sampled rows, benchmark launch configuration
+# ---------------------------------------------------------------------------
+FULL = [("q8_0", synth.QWEN_VOCAB, 896, 1), ("q8_0", synth.QWEN_VOCAB, 896, 8),
+        ("q4_k", synth.QWEN_VOCAB, 896, 4), ("q6_k", synth.QWEN_VOCAB, 896, 2),
+        ("q8_0", synth.GPT2_VOCAB, 768, 1),
+        ("q4_k", 4864, 896, 1), ("q4_k", 896, 4864, 1), ("q6_k", 896, 4864, 1),
+        ("q4_k", 128, 896, 1), ("i8row", 896, 896, 1)]
+
+
+@pytest.mark.parametrize("fmt,out,inf,batch", FULL)
+def test_full_size_sampled_rows(fmt, out, inf, batch):
+    rng = np.random.default_rng([13, out, inf, batch])
+    packed, scales = synth.matrix(fmt, rng, out, inf)
+    x = synth.activations(rng, batch, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    rows = np.unique(np.concatenate([rng.integers(0, out, 384), [0, out - 1]]))
+    sub = packed.reshape(out, -1)[rows]
+    y_ref, s_ref = oracle.gemv_packed(fmt, sub, len(rows), inf, x, bias[rows],
+                                      None if scales is None else scales[rows])
+    assert_within(y[:, rows], y_ref, s_ref, GEMV_REL, f"{fmt} {out}x{inf} b{batch}")
+
+
+# ---------------------------------------------------------------------------
+# binary16 small-M GEMM
+# ---------------------------------------------------------------------------
+GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
+              (1, 64, 40), (15, 96, 33), (16, 32, 16), (17, 160, 70), (100, 256, 48),
+              (8, 3072, 768), (32, 3072, 768)]
+
+
+@pytest.mark.parametrize("m,k,n", GEMM_CASES)
+def test_gemm_f16_parity(m, k, n):
+    rng = np.random.default_rng([14, m, k, n])
+    x = synth.f16_activations(rng, m, k)
+    w = synth.f16_weights(rng, n, k)
+    bias = synth.bias(rng, n)
+    y = run_gemm(x, w, bias)
+    y_ref, s_ref = oracle.gemm_f16(x, w, bias)
+    assert_within(y, y_ref, s_ref, GEMM_REL, f"gemm m{m} k{k} n{n}")
