@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark: one Qwen2.5-0.5B-shaped decode step of quantized mat-vecs.
+
+A step is the decode step's linear work at batch 1, in stream order: for each
+of 24 layers Q, K, V (with bias), O, gate, up (Q4_K) and down (Q4_K, Q6_K on
+even layers), then the tied 151936 x 896 Q8_0 LM head - 169 calls of the C
+ABI.  Weights are seeded random bytes of those shapes (the pages' model file
+is not available), resident in HBM; two copies of the step's weights are
+alternated so that the 256 MB last-level cache cannot hold a step's bytes.
+
+Prints one JSON line: HBM GB/s over the step (nominal algorithmic bytes per
+step / time per step), microseconds per step, the roofline of the dominant
+kernel (timed with HIP events around each of its launches on the launch
+stream) and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "batch-1 dequant-GEMV HBM GB/s (% of peak), µs per Qwen2.5-0.5B decode step"
+CONFIG_INDEX = 2          # the decode-step workload
+NOMINAL_BYTES_PER_WEIGHT = {"q8_0": 34 / 32, "q4_k": 144 / 256, "q6_k": 210 / 256, "i8row": 1.0}
+
+
+def call_bytes(fmt, out, inf, batch, has_bias):
+    """Nominal algorithmic bytes of one mat-vec: packed weights at the
+    format's bits per weight (no row padding), x, y and bias."""
+    w = out * inf * NOMINAL_BYTES_PER_WEIGHT[fmt] + (4 * out if fmt == "i8row" else 0)
+    return int(w + 4 * batch * (inf + out) + (4 * out if has_bias else 0))
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--mode", choices=("graph", "plain"), default="graph",
+                   help="launch the step as a captured HIP graph or as plain launches")
+    p.add_argument("--copies", type=int, default=2, help="weight copies alternated per step")
+    p.add_argument("--kernel-steps", type=int, default=20,
+                   help="plain steps with events around every launch (per-kernel times)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
+    return p.parse_args(argv)
+
+
+# ---------------------------------------------------------------------------
+# workload
+# ---------------------------------------------------------------------------
+def build_inputs(copies):
+    import numpy as np
+    import torch
+    from dequantize_mat_vec_amd import synth
+    dev = torch.device("cuda:0")
+    calls = synth.decode_step_calls()
+    weights = [[] for _ in range(copies)]
+    xs, ys, biases = [], [], []
+    for layer, name, fmt, out, inf, has_bias in calls:
+        tidx = synth.TENSOR_INDEX[name]
+        packed = synth.quant_blocks(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), out, inf)
+        host = torch.from_numpy(packed.reshape(-1))
+        for c in range(copies):
+            weights[c].append(host.to(dev))
+        x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
+        xs.append(torch.from_numpy(x).to(dev))
+        ys.append(torch.empty(out, dtype=torch.float32, device=dev))
+        if has_bias:
+            b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), out)
+            biases.append(torch.from_numpy(b).to(dev))
+        else:
+            biases.append(None)
+    torch.cuda.synchronize()
+    return calls, weights, xs, ys, biases
+
+
+def make_step(lib, calls, weights, xs, ys, biases):
+    """A function issuing the step's 169 calls on a stream handle; raw
+    pointers are resolved once so a step is only the C calls."""
+    fns = {"q8_0": lib.pesti_gemv_q8_0, "q4_k": lib.pesti_gemv_q4_k, "q6_k": lib.pesti_gemv_q6_k}
+    plans = []
+    for c, wl in enumerate(weights):
+        plan = []
+        for i, (layer, name, fmt, out, inf, has_bias) in enumerate(calls):
+            b = biases[i]
+            plan.append((fns[fmt], out, inf, wl[i].data_ptr(), xs[i].data_ptr(), ys[i].data_ptr(),
+                         b.data_ptr() if b is not None else None))
+        plans.append(plan)
+
+    def step(copy, stream_handle, around=None):
+        for idx, (fn, out, inf, w, x, y, b) in enumerate(plans[copy]):
+            if around is not None:
+                around(idx, True)
+            st = fn(out, inf, w, x, y, b, 1, stream_handle)
+            if st != 0:
+                raise RuntimeError(f"call {idx} failed with status {st}")
+            if around is not None:
+                around(idx, False)
+    return step
+
+
+def kernel_name(fmt, inf):
+    units = {"q8_0": inf // 32, "q4_k": -(-inf // 64), "q6_k": 4 * -(-inf // 256)}[fmt]
+    lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
+    return f"gemv_kernel<{fmt}, L={lanes}, B=1>"
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same step
+# ---------------------------------------------------------------------------
+def cpu_leg(seconds):
+    """Runs in a child process with one BLAS/OpenMP thread: times the
+    oracle (float64 dequantize + dot) on whole calls of the step, layer by
+    layer, then on LM-head row slices, until `seconds` of work is done."""
+    import numpy as np
+    from dequantize_mat_vec_amd import synth
+    import oracle
+    calls = synth.decode_step_calls()
+    done_bytes, spent, ncalls = 0, 0.0, 0
+    sample = []
+    for layer, name, fmt, out, inf, has_bias in calls:
+        if spent >= seconds:
+            break
+        tidx = synth.TENSOR_INDEX[name]
+        rng = synth.rng_for(CONFIG_INDEX, layer, tidx)
+        if name == "lm_head":
+            rows = min(out, 16384)
+            packed = synth.quant_blocks(fmt, rng, rows, inf)
+        else:
+            rows = out
+            packed = synth.quant_blocks(fmt, rng, out, inf)
+        x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
+        b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
+        t0 = time.perf_counter()
+        oracle.gemv_packed(fmt, packed, rows, inf, x, b)
+        spent += time.perf_counter() - t0
+        done_bytes += call_bytes(fmt, rows, inf, 1, has_bias)
+        ncalls += 1
+        sample.append(f"{name}{layer}" if name != "lm_head" else f"lm_head[{rows} rows]")
+    gbs = done_bytes / spent / 1e9
+    return {"value": gbs, "seconds": spent, "bytes": done_bytes, "calls": ncalls,
+            "first": sample[0], "last": sample[-1]}
+
+
+def run_cpu_baseline(seconds):
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        env[k] = "1"
+    env["HIP_VISIBLE_DEVICES"] = ""
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg",
+           "--cpu-sample-seconds", str(seconds)]
+    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline failed: {res.stderr[-2000:]}")
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    return {"value": round(r["value"], 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"float64 oracle, 1 thread, {r['calls']} calls of the decode step in "
+                       f"stream order ({r['first']} .. {r['last']}), {r['bytes']} nominal bytes "
+                       f"in {r['seconds']:.1f} s")}
+
+
+# ---------------------------------------------------------------------------
+def main(argv=None):
+    args = parse_args(argv)
+    if args.cpu_leg:
+        print(json.dumps(cpu_leg(args.cpu_sample_seconds)))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the decode-step mat-vec runs on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    lib = dmv.load()
+    torch.cuda.set_device(0)
+    calls, weights, xs, ys, biases = build_inputs(args.copies)
+    step = make_step(lib, calls, weights, xs, ys, biases)
+    bytes_per_step = sum(call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    graphs = None
+    with torch.cuda.stream(stream):
+        for i in range(2):
+            step(i % args.copies, sh)
+        torch.cuda.synchronize()
+        if args.mode == "graph":
+            graphs = []
+            for c in range(args.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(c, torch.cuda.current_stream().cuda_stream)
+                graphs.append(g)
+            torch.cuda.synchronize()
+
+        def run(i):
+            if graphs is not None:
+                graphs[i % args.copies].replay()
+            else:
+                step(i % args.copies, sh)
+
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            run(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+
+        # per-kernel durations: plain steps with events around every launch
+        names = [kernel_name(fmt, inf) for _, _, fmt, _, inf, _ in calls]
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in calls] for _ in range(args.kernel_steps)]
+        cur = {}
+
+        def around(idx, before):
+            e = cur["evs"][idx]
+            (e[0] if before else e[1]).record(stream)
+
+        for s in range(args.kernel_steps):
+            cur["evs"] = evs[s]
+            step(s % args.copies, sh, around)
+        torch.cuda.synchronize()
+
+    per_name = {}
+    for s in range(args.kernel_steps):
+        for i, (layer, name, fmt, out, inf, hb) in enumerate(calls):
+            ms = evs[s][i][0].elapsed_time(evs[s][i][1])
+            d = per_name.setdefault(names[i], {"ms": 0.0, "launches": 0, "bytes": 0})
+            d["ms"] += ms
+            d["launches"] += 1
+            d["bytes"] += call_bytes(fmt, out, inf, 1, hb)
+    dom_name, dom = max(per_name.items(), key=lambda kv: kv[1]["ms"])
+    avg_s = dom["ms"] / dom["launches"] / 1e3
+    bytes_per_launch = dom["bytes"] / dom["launches"]
+    achieved = bytes_per_launch / avg_s / 1e9
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = bytes_per_step / (ms_per_step / 1e3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (Q4_K/Q6_K/Q8_0 weights)",
+        "data": "synthetic (seeded random blocks of the model's shapes)",
+        "config": {"workload": "Qwen2.5-0.5B decode step, linear layers, batch 1: 24 x "
+                               "{Q,K,V,O,gate,up Q4_K; down Q4_K/Q6_K} + 151936x896 Q8_0 LM head "
+                               "= 169 calls", "bytes_per_step": bytes_per_step,
+                   "launch": args.mode, "weight_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(bytes_per_launch),
+                     "avg_launch_us": round(avg_s * 1e6, 3)},
+        "kernels": {k: {"launches_per_step": v["launches"] // args.kernel_steps,
+                        "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
+                        "GB/s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)}
+                    for k, v in sorted(per_name.items(), key=lambda kv: -kv[1]["ms"])},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_cpu_baseline(args.cpu_sample_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
