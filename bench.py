@@ -3,8 +3,9 @@
 
 A step is the decode step's linear work at batch 1, in stream order: for each
 of 24 layers Q, K, V (with bias), O, gate, up (Q4_K) and down (Q4_K, Q6_K on
-even layers), then the tied 151936 x 896 Q8_0 LM head - 169 calls of the C
-ABI.  Weights are seeded random bytes of those shapes (the pages' model file
+even layers), then the tied 151936 x 896 Q8_0 LM head - 169 mat-vecs.  The
+mat-vecs of one dependency stage (Q/K/V; gate/up) share one grouped launch
+of the C ABI, so a step is 97 dependent launches (--grouping none: 169).  Weights are seeded random bytes of those shapes (the pages' model file
 is not available), resident in HBM; two copies of the step's weights are
 alternated so that the 256 MB last-level cache cannot hold a step's bytes.
 
@@ -46,6 +47,8 @@ def parse_args(argv=None):
     p.add_argument("--mode", choices=("graph", "plain"), default="graph",
                    help="launch the step as a captured HIP graph or as plain launches")
     p.add_argument("--copies", type=int, default=2, help="weight copies alternated per step")
+    p.add_argument("--grouping", choices=("stage", "none"), default="stage",
+                   help="one launch per dependency stage (Q/K/V, O, gate/up, down) or per call")
     p.add_argument("--kernel-steps", type=int, default=20,
                    help="plain steps with events around every launch (per-kernel times)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,33 +86,62 @@ def build_inputs(copies):
     return calls, weights, xs, ys, biases
 
 
-def make_step(lib, calls, weights, xs, ys, biases):
-    """A function issuing the step's 169 calls on a stream handle; raw
-    pointers are resolved once so a step is only the C calls."""
-    fns = {"q8_0": lib.pesti_gemv_q8_0, "q4_k": lib.pesti_gemv_q4_k, "q6_k": lib.pesti_gemv_q6_k}
+def plan_launches(calls, grouping):
+    """Launches of one step as (format, [call indices]).  With grouping
+    "stage", the projections of one dependency stage that read the same
+    activations share a launch: Q/K/V, then O, then gate/up, then down, per
+    layer (97 launches); with "none" every call is its own launch (169)."""
+    if grouping == "none":
+        return [(fmt, [i]) for i, (_, _, fmt, _, _, _) in enumerate(calls)]
+    launches, i = [], 0
+    stage_of = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3, "lm_head": 4}
+    while i < len(calls):
+        layer, name, fmt, _, _, _ = calls[i]
+        group = [i]
+        j = i + 1
+        while (j < len(calls) and calls[j][0] == layer and calls[j][2] == fmt
+               and stage_of[calls[j][1]] == stage_of[name]):
+            group.append(j)
+            j += 1
+        launches.append((fmt, group))
+        i = j
+    return launches
+
+
+def make_step(lib, calls, launches, weights, xs, ys, biases):
+    """A function issuing the step's launches on a stream handle; the op
+    tables are built once so a step is only the C calls."""
+    import ctypes
+    from dequantize_mat_vec_amd import _lib
     plans = []
-    for c, wl in enumerate(weights):
+    for wl in weights:
         plan = []
-        for i, (layer, name, fmt, out, inf, has_bias) in enumerate(calls):
-            b = biases[i]
-            plan.append((fns[fmt], out, inf, wl[i].data_ptr(), xs[i].data_ptr(), ys[i].data_ptr(),
-                         b.data_ptr() if b is not None else None))
+        for fmt, idx in launches:
+            arr = (_lib.GemvOp * len(idx))()
+            for k, i in enumerate(idx):
+                _, _, _, out, inf, _ = calls[i]
+                b = biases[i]
+                arr[k] = _lib.GemvOp(out, inf, wl[i].data_ptr(), None, xs[i].data_ptr(),
+                                     ys[i].data_ptr(), b.data_ptr() if b is not None else None)
+            plan.append((_lib.FORMAT_IDS[fmt], len(idx), ctypes.cast(arr, ctypes.c_void_p), arr))
         plans.append(plan)
+    fn = lib.pesti_gemv_group
 
     def step(copy, stream_handle, around=None):
-        for idx, (fn, out, inf, w, x, y, b) in enumerate(plans[copy]):
+        for idx, (fid, n, ptr, _keep) in enumerate(plans[copy]):
             if around is not None:
                 around(idx, True)
-            st = fn(out, inf, w, x, y, b, 1, stream_handle)
+            st = fn(fid, n, ptr, 1, stream_handle)
             if st != 0:
-                raise RuntimeError(f"call {idx} failed with status {st}")
+                raise RuntimeError(f"launch {idx} failed with status {st}")
             if around is not None:
                 around(idx, False)
     return step
 
 
-def kernel_name(fmt, inf):
-    units = {"q8_0": inf // 32, "q4_k": -(-inf // 64), "q6_k": 4 * -(-inf // 256)}[fmt]
+def kernel_name(fmt, infs):
+    units = max({"q8_0": inf // 64 if inf % 64 == 0 else inf // 32, "q4_k": -(-inf // 64),
+                 "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     return f"gemv_kernel<{fmt}, L={lanes}, B=1>"
 
@@ -184,7 +216,8 @@ def main(argv=None):
     lib = dmv.load()
     torch.cuda.set_device(0)
     calls, weights, xs, ys, biases = build_inputs(args.copies)
-    step = make_step(lib, calls, weights, xs, ys, biases)
+    launches = plan_launches(calls, args.grouping)
+    step = make_step(lib, calls, launches, weights, xs, ys, biases)
     bytes_per_step = sum(call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
@@ -219,9 +252,9 @@ def main(argv=None):
         elapsed = time.perf_counter() - t0
 
         # per-kernel durations: plain steps with events around every launch
-        names = [kernel_name(fmt, inf) for _, _, fmt, _, inf, _ in calls]
+        names = [kernel_name(fmt, [calls[i][4] for i in idx]) for fmt, idx in launches]
         evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in calls] for _ in range(args.kernel_steps)]
+                for _ in launches] for _ in range(args.kernel_steps)]
         cur = {}
 
         def around(idx, before):
@@ -235,12 +268,13 @@ def main(argv=None):
 
     per_name = {}
     for s in range(args.kernel_steps):
-        for i, (layer, name, fmt, out, inf, hb) in enumerate(calls):
-            ms = evs[s][i][0].elapsed_time(evs[s][i][1])
-            d = per_name.setdefault(names[i], {"ms": 0.0, "launches": 0, "bytes": 0})
+        for li, (fmt, idx) in enumerate(launches):
+            ms = evs[s][li][0].elapsed_time(evs[s][li][1])
+            d = per_name.setdefault(names[li], {"ms": 0.0, "launches": 0, "bytes": 0})
             d["ms"] += ms
             d["launches"] += 1
-            d["bytes"] += call_bytes(fmt, out, inf, 1, hb)
+            d["bytes"] += sum(call_bytes(calls[i][2], calls[i][3], calls[i][4], 1, calls[i][5])
+                              for i in idx)
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1]["ms"])
     avg_s = dom["ms"] / dom["launches"] / 1e3
     bytes_per_launch = dom["bytes"] / dom["launches"]
@@ -265,8 +299,9 @@ def main(argv=None):
         "data": "synthetic (seeded random blocks of the model's shapes)",
         "config": {"workload": "Qwen2.5-0.5B decode step, linear layers, batch 1: 24 x "
                                "{Q,K,V,O,gate,up Q4_K; down Q4_K/Q6_K} + 151936x896 Q8_0 LM head "
-                               "= 169 calls", "bytes_per_step": bytes_per_step,
-                   "launch": args.mode, "weight_copies": args.copies},
+                               "= 169 mat-vecs", "bytes_per_step": bytes_per_step,
+                   "launch": args.mode, "launches_per_step": len(launches),
+                   "grouping": args.grouping, "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "bytes_per_launch": int(bytes_per_launch),

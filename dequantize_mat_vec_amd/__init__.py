@@ -7,11 +7,12 @@ the C ABI of include/pesti.h.  This package is the thin Python binding
 """
 from ._lib import (FORMAT_IDS, LIB_PATH, PESTI_ERR_ALIGN, PESTI_ERR_BATCH,  # noqa: F401
                    PESTI_ERR_DEVICE, PESTI_ERR_LAUNCH, PESTI_ERR_NULL, PESTI_ERR_SHAPE,
-                   PESTI_OK, PestiError, dequant, gemv, load, pesti_abi_version,
+                   PESTI_OK, GemvOp, MAX_GROUP, PestiError, dequant, gemv, gemv_ops, load, pesti_abi_version,
                    pesti_dequant_i8row, pesti_dequant_q4_k, pesti_dequant_q6_k,
-                   pesti_dequant_q8_0, pesti_gemm_f16_smallm, pesti_gemv_i8row,
+                   pesti_dequant_q8_0, pesti_gemm_f16_smallm, pesti_gemv_group, pesti_gemv_i8row,
                    pesti_gemv_q4_k, pesti_gemv_q6_k, pesti_gemv_q8_0, pesti_row_bytes,
                    strerror)
 
 __all__ = [n for n in dir() if n.startswith("pesti_")] + [
-    "PestiError", "gemv", "dequant", "load", "strerror", "FORMAT_IDS", "LIB_PATH"]
+    "PestiError", "GemvOp", "MAX_GROUP", "gemv", "gemv_ops", "dequant", "load", "strerror",
+    "FORMAT_IDS", "LIB_PATH"]

@@ -33,6 +33,7 @@ _SIGNATURES = {
     "pesti_gemv_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_group": (_c_int, [_i32, _i32, _vp, _i32, _vp]),
     "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -44,6 +45,15 @@ _SIGNATURES = {
 }
 
 _lib = None
+
+MAX_GROUP = 8
+
+
+class GemvOp(ctypes.Structure):
+    """pesti_gemv_op: one mat-vec of a grouped launch."""
+    _fields_ = [("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64),
+                ("w", ctypes.c_void_p), ("row_scales", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
 class PestiError(RuntimeError):
@@ -142,6 +152,27 @@ def pesti_gemv_i8row(out_features, in_features, codes, row_scales, x, y, bias=No
 def pesti_gemm_f16_smallm(m, out_features, in_features, w, x, y, bias=None, stream=None):
     return _check("pesti_gemm_f16_smallm", load().pesti_gemm_f16_smallm(
         m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias), _stream(stream)))
+
+
+def gemv_ops(ops):
+    """ctypes array of pesti_gemv_op from (out, in, w, x, y, bias, row_scales)
+    tuples whose pointer fields are tensors, ints or None."""
+    arr = (GemvOp * max(len(ops), 1))()
+    for i, (out, inf, w, x, y, bias, scales) in enumerate(ops):
+        arr[i] = GemvOp(out, inf, _ptr(w), _ptr(scales), _ptr(x), _ptr(y), _ptr(bias))
+    return arr
+
+
+def pesti_gemv_group(fmt, ops, batch=1, stream=None):
+    """Grouped launch.  `ops` is a list of (out, in, w, x, y, bias, row_scales)
+    tuples, or a ctypes array built by gemv_ops()."""
+    fid = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
+    if isinstance(ops, ctypes.Array):
+        arr, n = ops, len(ops)
+    else:
+        arr, n = gemv_ops(ops), len(ops)
+    return _check("pesti_gemv_group", load().pesti_gemv_group(
+        fid, n, ctypes.cast(arr, ctypes.c_void_p), batch, _stream(stream)))
 
 
 def _dequant(name, rows, in_features, blocks, w_out, stream):

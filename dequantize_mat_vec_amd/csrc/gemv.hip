@@ -15,7 +15,8 @@
 //
 // Work decomposition (see common.h): L lanes per row, each lane walks the
 // row's units with stride L.  A unit is:
-//   Q8_0  one 34-byte block (32 weights);
+//   Q8_0  two consecutive 34-byte blocks (68 bytes, 64 weights) when a row
+//         has an even number of blocks, else one block;
 //   Q4_K  one 64-weight run of a super-block: its 32 code bytes (low nibbles
 //         = sub-block 2g, high nibbles = sub-block 2g+1) plus the 16-byte
 //         super-block header;
@@ -23,9 +24,17 @@
 //         32-weight groups g (64 weights from 16+16 low-part bytes and 16
 //         high-part bytes);
 //   i8row 64 consecutive code bytes.
-// Every lane keeps float32 partial sums per batch column; the sub-block
-// scales are applied once per sub-block (d sc sum(q x) - dmin m sum(x) for
-// Q4_K, with sum(x) per 32 staged in LDS next to x).
+// Each unit is split into issue() - the global loads, returning raw dwords -
+// and compute() - decode and FMA against x in LDS.  The kernel issues the
+// loads of a lane's next unit before computing the current one, and issues
+// the first unit's loads before staging x, so the weight stream overlaps
+// both the x staging and the arithmetic.  Partial sums are float32 per
+// batch column; sub-block scales are applied once per sub-block.
+//
+// One workgroup serves one tile of rows, and one launch may carry several
+// independent mat-vecs of one format (a grouped launch, e.g. the Q/K/V or
+// gate/up projections that read the same activations), which shortens a
+// decode step's chain of dependent launches.
 #include <type_traits>
 
 #include "common.h"
@@ -41,40 +50,116 @@ struct GemvArgs {
   int64_t out;
   int64_t in;
   int64_t row_bytes;
-  int64_t units;          // units per row (loop bound)
+  int64_t units;          // units per row
   int64_t xpad;           // logical x length staged (zero filled past in)
   int64_t xstride;        // LDS floats per staged batch row
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four 4-bit codes (bits 0-3 of each byte of v) as float32 times 2^-9: a
+// nibble in the low bits of an otherwise zero OCP e4m3 byte encodes exactly
+// q * 2^-9 (subnormal for q < 8, exponent field 1 for q >= 8), and one
+// v_cvt_pk_f32_fp8 converts two bytes.
+__device__ __forceinline__ void nibbles_x512(uint32_t v, float& a, float& b, float& c, float& d) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v), false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v), true);
+  a = lo.x; b = lo.y; c = hi.x; d = hi.y;
+}
+
 // ---------------------------------------------------------------------------
-// Q8_0: one 34-byte block per unit.  Blocks start 2-byte aligned; the lane
-// reads the dwords covering the block and realigns the codes in registers.
+// Q8_0, two blocks per unit: the 68 bytes of blocks 2u, 2u+1 start on a
+// dword boundary (rows are 34 * even bytes).  Block A = d in dword 0 low
+// half, codes at bytes 2..33; block B = d in dword 8 high half, codes in
+// dwords 9..16.
+// ---------------------------------------------------------------------------
+struct FmtQ8_0x2 {
+  static constexpr bool kSums = false;
+  static constexpr int kPad = 64;
+  struct Raw { uint32_t w[17]; };
+  struct Lane {};
+  __device__ static Lane lane_state(int) { return {}; }
+  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+    const uint8_t* p = rp + u * 68;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = load_u32x4(p + 16 * i);
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+    r.w[16] = load_u32(p + 64);
+  }
+
+  template <int B>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+                                                 const float* xs, const float*, int64_t,
+                                                 const Lane&, float* acc) {
+    const float dA = f16_lo(r.w[0]), dB = f16_hi(r.w[8]);
+    float pa[B], pb[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) { pa[b] = 0.f; pb[b] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ca = align_bytes(r.w[j + 1], r.w[j], 2);
+      const uint32_t cb = r.w[9 + j];
+      const float a0 = sbyte<0>(ca), a1 = sbyte<1>(ca), a2 = sbyte<2>(ca), a3 = sbyte<3>(ca);
+      const float b0 = sbyte<0>(cb), b1 = sbyte<1>(cb), b2 = sbyte<2>(cb), b3 = sbyte<3>(cb);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* xb = xs + b * a.xstride;
+        const f32x4 xa = xs4(xb, 64 * u + 4 * j);
+        const f32x4 xc = xs4(xb, 64 * u + 32 + 4 * j);
+        pa[b] = fmaf(a0, xa.x, pa[b]); pa[b] = fmaf(a1, xa.y, pa[b]);
+        pa[b] = fmaf(a2, xa.z, pa[b]); pa[b] = fmaf(a3, xa.w, pa[b]);
+        pb[b] = fmaf(b0, xc.x, pb[b]); pb[b] = fmaf(b1, xc.y, pb[b]);
+        pb[b] = fmaf(b2, xc.z, pb[b]); pb[b] = fmaf(b3, xc.w, pb[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = fmaf(dB, pb[b], fmaf(dA, pa[b], acc[b]));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Q8_0, one block per unit (rows with an odd block count start 2 bytes off a
+// dword boundary every other row): read the dwords covering the block and
+// realign.  The ninth dword is whole only when the block starts 2 bytes
+// past a boundary; otherwise only its lower half belongs to the block (and
+// the upper half may lie past the buffer), so only 16 bits are read.
 // ---------------------------------------------------------------------------
 struct FmtQ8_0 {
   static constexpr bool kSums = false;
   static constexpr int kPad = 64;
+  struct Raw { uint32_t w[9]; uint32_t s; };
+  struct Lane {};
+  __device__ static Lane lane_state(int) { return {}; }
+  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
 
-  template <int B>
-  __device__ __forceinline__ static void unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
-                                              const float* xs, const float*, int64_t, float* acc) {
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
     const uint8_t* p = rp + u * 34;
     const uint32_t s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);   // 0 or 2
     const uint8_t* pa = p - s;
     const u32x4 w0 = load_u32x4(pa);
     const u32x4 w1 = load_u32x4(pa + 16);
-    // The ninth dword is whole only when s = 2; for s = 0 its upper half lies
-    // past the block (and, for the last block, past the buffer), so only the
-    // lower 16 bits are read.
-    const uint32_t w8 = static_cast<uint32_t>(load_u16(pa + 32)) |
-                        (s ? static_cast<uint32_t>(load_u16(pa + 34)) << 16 : 0u);
-    const uint32_t w[9] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w8};
-    const float d = s ? f16_hi(w[0]) : f16_lo(w[0]);
+    r.w[0] = w0.x; r.w[1] = w0.y; r.w[2] = w0.z; r.w[3] = w0.w;
+    r.w[4] = w1.x; r.w[5] = w1.y; r.w[6] = w1.z; r.w[7] = w1.w;
+    r.w[8] = static_cast<uint32_t>(load_u16(pa + 32)) |
+             (s ? static_cast<uint32_t>(load_u16(pa + 34)) << 16 : 0u);
+    r.s = s;
+  }
+
+  template <int B>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+                                                 const float* xs, const float*, int64_t,
+                                                 const Lane&, float* acc) {
+    const float d = r.s ? f16_hi(r.w[0]) : f16_lo(r.w[0]);
     float part[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) part[b] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t c = s ? w[j + 1] : align_bytes(w[j + 1], w[j], 2);
+      const uint32_t c = r.s ? r.w[j + 1] : align_bytes(r.w[j + 1], r.w[j], 2);
       const float q0 = sbyte<0>(c), q1 = sbyte<1>(c), q2 = sbyte<2>(c), q3 = sbyte<3>(c);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
@@ -88,8 +173,6 @@ struct FmtQ8_0 {
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = fmaf(d, part[b], acc[b]);
   }
-
-  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
 };
 
 // ---------------------------------------------------------------------------
@@ -97,48 +180,53 @@ struct FmtQ8_0 {
 // multiple of 4), so the bit positions of its two scales and mins are
 // computed once per lane.
 // ---------------------------------------------------------------------------
-struct Q4KLane {
-  uint32_t lo_sc_shift0, lo_sc_shift1, lo_m_shift0, lo_m_shift1, lo_width;
-  uint32_t hi_shift0, hi_shift1, hi_width;
-  bool low_half;   // sub-blocks 0..3 (g < 2)
-};
-
-__device__ __forceinline__ Q4KLane q4k_lane(int g) {
-  Q4KLane s;
-  const int j0 = 2 * g, j1 = 2 * g + 1;
-  s.low_half = g < 2;
-  if (g < 2) {
-    // sc[j] = S[j] & 63 and m[j] = S[j+4] & 63: byte j of dwords 1 and 2.
-    s.lo_sc_shift0 = 8 * j0; s.lo_sc_shift1 = 8 * j1;
-    s.lo_m_shift0 = 8 * j0;  s.lo_m_shift1 = 8 * j1;
-    s.lo_width = 6; s.hi_width = 0; s.hi_shift0 = 0; s.hi_shift1 = 0;
-  } else {
-    // sc[j] = (S[j+4] & 15) | (S[j-4] >> 6) << 4,
-    // m[j]  = (S[j+4] >> 4) | (S[j] >> 6) << 4, with k = j - 4:
-    // low parts in byte k of dword 3, high parts in bits 6-7 of byte k of
-    // dwords 1 (scales) and 2 (mins).
-    const int k0 = j0 - 4, k1 = j1 - 4;
-    s.lo_sc_shift0 = 8 * k0; s.lo_sc_shift1 = 8 * k1;
-    s.lo_m_shift0 = 8 * k0 + 4; s.lo_m_shift1 = 8 * k1 + 4;
-    s.lo_width = 4; s.hi_width = 2; s.hi_shift0 = 8 * k0 + 6; s.hi_shift1 = 8 * k1 + 6;
-  }
-  return s;
-}
-
 struct FmtQ4_K {
   static constexpr bool kSums = true;
   static constexpr int kPad = 256;
+  struct Raw { u32x4 hdr, qa, qb; };
+  struct Lane {
+    uint32_t lo_sc_shift0, lo_sc_shift1, lo_m_shift0, lo_m_shift1, lo_width;
+    uint32_t hi_shift0, hi_shift1, hi_width;
+    bool low_half;   // sub-blocks 0..3 (g < 2)
+  };
+  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+
+  __device__ static Lane lane_state(int sub) {
+    const int g = sub & 3;
+    Lane s;
+    const int j0 = 2 * g, j1 = 2 * g + 1;
+    s.low_half = g < 2;
+    if (g < 2) {
+      // sc[j] = S[j] & 63 and m[j] = S[j+4] & 63: byte j of dwords 1 and 2.
+      s.lo_sc_shift0 = 8 * j0; s.lo_sc_shift1 = 8 * j1;
+      s.lo_m_shift0 = 8 * j0;  s.lo_m_shift1 = 8 * j1;
+      s.lo_width = 6; s.hi_width = 0; s.hi_shift0 = 0; s.hi_shift1 = 0;
+    } else {
+      // sc[j] = (S[j+4] & 15) | (S[j-4] >> 6) << 4,
+      // m[j]  = (S[j+4] >> 4) | (S[j] >> 6) << 4, with k = j - 4:
+      // low parts in byte k of dword 3, high parts in bits 6-7 of byte k of
+      // dwords 1 (scales) and 2 (mins).
+      const int k0 = j0 - 4, k1 = j1 - 4;
+      s.lo_sc_shift0 = 8 * k0; s.lo_sc_shift1 = 8 * k1;
+      s.lo_m_shift0 = 8 * k0 + 4; s.lo_m_shift1 = 8 * k1 + 4;
+      s.lo_width = 4; s.hi_width = 2; s.hi_shift0 = 8 * k0 + 6; s.hi_shift1 = 8 * k1 + 6;
+    }
+    return s;
+  }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+    const uint8_t* sbp = rp + (u >> 2) * 144;
+    const int g = static_cast<int>(u & 3);
+    r.hdr = load_u32x4_a16(sbp);
+    r.qa = load_u32x4_a16(sbp + 16 + 32 * g);
+    r.qb = load_u32x4_a16(sbp + 32 + 32 * g);
+  }
 
   template <int B>
-  __device__ __forceinline__ static void unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
-                                              const float* xs, const float* sums, int64_t nsub,
-                                              float* acc, const Q4KLane& L) {
-    const int64_t sb = u >> 2;
-    const int g = static_cast<int>(u & 3);
-    const uint8_t* sbp = rp + sb * 144;
-    const u32x4 hdr = load_u32x4_a16(sbp);
-    const u32x4 qa = load_u32x4_a16(sbp + 16 + 32 * g);
-    const u32x4 qb = load_u32x4_a16(sbp + 32 + 32 * g);
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+                                                 const float* xs, const float* sums, int64_t nsub,
+                                                 const Lane& L, float* acc) {
+    const u32x4 hdr = r.hdr;
     const float d = f16_lo(hdr.x), dmin = f16_hi(hdr.x);
     const uint32_t src_sc = L.low_half ? hdr.y : hdr.w;
     const uint32_t src_m = L.low_half ? hdr.z : hdr.w;
@@ -150,17 +238,16 @@ struct FmtQ4_K {
                         (__builtin_amdgcn_ubfe(hdr.z, L.hi_shift0, L.hi_width) << 4);
     const uint32_t m1 = __builtin_amdgcn_ubfe(src_m, L.lo_m_shift1, L.lo_width) |
                         (__builtin_amdgcn_ubfe(hdr.z, L.hi_shift1, L.hi_width) << 4);
-    const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
     float p0[B], p1[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) { p0[b] = 0.f; p1[b] = 0.f; }
     const int64_t x0 = 64 * u;   // first weight of the run (sub-block 2g)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t lo = q[t] & 0x0F0F0F0Fu;
-      const uint32_t hi = (q[t] >> 4) & 0x0F0F0F0Fu;
-      const float l0 = ubyte<0>(lo), l1 = ubyte<1>(lo), l2 = ubyte<2>(lo), l3 = ubyte<3>(lo);
-      const float h0 = ubyte<0>(hi), h1 = ubyte<1>(hi), h2 = ubyte<2>(hi), h3 = ubyte<3>(hi);
+      float l0, l1, l2, l3, h0, h1, h2, h3;
+      nibbles_x512(q[t] & 0x0F0F0F0Fu, l0, l1, l2, l3);
+      nibbles_x512((q[t] >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float* xb = xs + b * a.xstride;
@@ -172,17 +259,19 @@ struct FmtQ4_K {
         p1[b] = fmaf(h2, xh.z, p1[b]); p1[b] = fmaf(h3, xh.w, p1[b]);
       }
     }
-    const float ds0 = d * static_cast<float>(sc0), ds1 = d * static_cast<float>(sc1);
+    // p0, p1 carry a factor 2^-9 from the code conversion: scale d by 2^9.
+    const float d512 = d * 512.0f;
+    const float ds0 = d512 * static_cast<float>(sc0), ds1 = d512 * static_cast<float>(sc1);
     const float dm0 = dmin * static_cast<float>(m0), dm1 = dmin * static_cast<float>(m1);
     const int64_t j0 = 2 * u;    // sub-block index of the row (32 weights each)
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float* sb_sums = sums + b * nsub;
-      float r = ds0 * p0[b];
-      r = fmaf(ds1, p1[b], r);
-      r = fmaf(-dm0, sb_sums[j0], r);
-      r = fmaf(-dm1, sb_sums[j0 + 1], r);
-      acc[b] += r;
+      float v = ds0 * p0[b];
+      v = fmaf(ds1, p1[b], v);
+      v = fmaf(-dm0, sb_sums[j0], v);
+      v = fmaf(-dm1, sb_sums[j0 + 1], v);
+      acc[b] += v;
     }
   }
 };
@@ -198,56 +287,69 @@ struct FmtQ4_K {
 struct FmtQ6_K {
   static constexpr bool kSums = false;
   static constexpr int kPad = 256;
-
-  __device__ __forceinline__ static void load16(const uint8_t* p, uint32_t s, uint32_t* out) {
-    const u32x4 v = load_u32x4(p);
-    const uint32_t e = load_u32(p + 16);
-    out[0] = align_bytes(v.y, v.x, s);
-    out[1] = align_bytes(v.z, v.y, s);
-    out[2] = align_bytes(v.w, v.z, s);
-    out[3] = align_bytes(e, v.w, s);
-  }
+  // Three 20-byte windows (low parts of g = 0/2, of g = 1/3, high parts),
+  // three dwords around the unit's scales, and d.
+  struct Raw { uint32_t la[5], lb[5], hh[5], sc[3]; uint32_t d; uint32_t s; };
+  struct Lane {};
+  __device__ static Lane lane_state(int) { return {}; }
 
   __device__ static bool valid(const GemvArgs& a, int64_t u) {
     return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1) < a.in;
   }
 
-  template <int B>
-  __device__ __forceinline__ static void unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
-                                              const float* xs, const float*, int64_t, float* acc) {
-    const int64_t sb = u >> 2;
+  __device__ __forceinline__ static void load20(const uint8_t* p, uint32_t* w) {
+    const u32x4 v = load_u32x4(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    w[4] = load_u32(p + 16);
+  }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
     const int h = static_cast<int>((u >> 1) & 1);
     const int c = static_cast<int>(u & 1);
-    const uint8_t* sbp = rp + sb * 210;
+    const uint8_t* sbp = rp + (u >> 2) * 210;
     const uint32_t s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sbp) & 3u);   // 0 or 2
     const uint8_t* base = sbp - s;
-    uint32_t qla[4], qlb[4], qh[4];
-    load16(base + 64 * h + 16 * c, s, qla);
-    load16(base + 64 * h + 32 + 16 * c, s, qlb);
-    load16(base + 128 + 32 * h + 16 * c, s, qh);
-    // int8 scales sc[8h + 2g + c], g = 0..3: bytes c, c+2 of the realigned
-    // dwords at offset 192 + 8h.  The third dword is only needed when s = 2;
-    // for s = 0 it is re-read from in-bounds memory.
+    load20(base + 64 * h + 16 * c, r.la);
+    load20(base + 64 * h + 32 + 16 * c, r.lb);
+    load20(base + 128 + 32 * h + 16 * c, r.hh);
+    // int8 scales sc[8h + 2g + c], g = 0..3, live in the 8 bytes at offset
+    // 192 + 8h.  The third dword is needed only when s = 2; for s = 0 it is
+    // re-read from in-bounds memory.
     const uint8_t* scp = base + 192 + 8 * h;
-    const uint32_t s0 = load_u32(scp), s1 = load_u32(scp + 4), s2 = load_u32(scp + (s ? 8 : 4));
-    const uint32_t S0 = align_bytes(s1, s0, s) >> (8 * c);
-    const uint32_t S1 = align_bytes(s2, s1, s) >> (8 * c);
+    r.sc[0] = load_u32(scp);
+    r.sc[1] = load_u32(scp + 4);
+    r.sc[2] = load_u32(scp + (s ? 8 : 4));
+    r.d = load_u16(sbp + 208);
+    r.s = s;
+  }
+
+  template <int B>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+                                                 const float* xs, const float*, int64_t,
+                                                 const Lane&, float* acc) {
+    const int h = static_cast<int>((u >> 1) & 1);
+    const int c = static_cast<int>(u & 1);
+    const uint32_t s = r.s;
+    const uint32_t S0 = align_bytes(r.sc[1], r.sc[0], s) >> (8 * c);
+    const uint32_t S1 = align_bytes(r.sc[2], r.sc[1], s) >> (8 * c);
     const float sc[4] = {sbyte<0>(S0), sbyte<2>(S0), sbyte<0>(S1), sbyte<2>(S1)};
-    const float dq = 0.25f * f16_lo(load_u16(sbp + 208));
+    const float dq = 0.25f * f16_lo(r.d);
     float p[4][B];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int b = 0; b < B; ++b) p[g][b] = 0.f;
-    const int64_t xbase = 256 * sb + 128 * h + 16 * c;
+    const int64_t xbase = 256 * (u >> 2) + 128 * h + 16 * c;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t hf = qh[j] ^ 0xAAAAAAAAu;   // each 2-bit high part XOR 2
+      const uint32_t la = align_bytes(r.la[j + 1], r.la[j], s);
+      const uint32_t lb = align_bytes(r.lb[j + 1], r.lb[j], s);
+      const uint32_t hf = align_bytes(r.hh[j + 1], r.hh[j], s) ^ 0xAAAAAAAAu;   // high part XOR 2
       uint32_t v[4];
-      v[0] = ((qla[j] << 2) & 0x3C3C3C3Cu) | ((hf << 6) & 0xC0C0C0C0u);
-      v[1] = ((qlb[j] << 2) & 0x3C3C3C3Cu) | ((hf << 4) & 0xC0C0C0C0u);
-      v[2] = ((qla[j] >> 2) & 0x3C3C3C3Cu) | ((hf << 2) & 0xC0C0C0C0u);
-      v[3] = ((qlb[j] >> 2) & 0x3C3C3C3Cu) | (hf & 0xC0C0C0C0u);
+      v[0] = ((la << 2) & 0x3C3C3C3Cu) | ((hf << 6) & 0xC0C0C0C0u);
+      v[1] = ((lb << 2) & 0x3C3C3C3Cu) | ((hf << 4) & 0xC0C0C0C0u);
+      v[2] = ((la >> 2) & 0x3C3C3C3Cu) | ((hf << 2) & 0xC0C0C0C0u);
+      v[3] = ((lb >> 2) & 0x3C3C3C3Cu) | (hf & 0xC0C0C0C0u);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float q0 = sbyte<0>(v[g]), q1 = sbyte<1>(v[g]), q2 = sbyte<2>(v[g]), q3 = sbyte<3>(v[g]);
@@ -263,40 +365,46 @@ struct FmtQ6_K {
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      float r = (dq * sc[0]) * p[0][b];
-      r = fmaf(dq * sc[1], p[1][b], r);
-      r = fmaf(dq * sc[2], p[2][b], r);
-      r = fmaf(dq * sc[3], p[3][b], r);
-      acc[b] += r;
+      float v = (dq * sc[0]) * p[0][b];
+      v = fmaf(dq * sc[1], p[1][b], v);
+      v = fmaf(dq * sc[2], p[2][b], v);
+      v = fmaf(dq * sc[3], p[3][b], v);
+      acc[b] += v;
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// i8row: 64 code bytes per unit; the row scale is applied after the sum.
+// i8row: 64 code bytes per unit; the row scale is applied after the sum.  A
+// row whose length is 32 mod 64 ends with a half unit.
 // ---------------------------------------------------------------------------
 struct FmtI8Row {
   static constexpr bool kSums = false;
   static constexpr int kPad = 64;
-
+  struct Raw { uint32_t q[16]; };
+  struct Lane {};
+  __device__ static Lane lane_state(int) { return {}; }
   __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
 
-  template <int B>
-  __device__ __forceinline__ static void unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
-                                              const float* xs, const float*, int64_t, float* acc) {
+  __device__ __forceinline__ static void issue_n(const uint8_t* rp, int64_t u, int64_t in, Raw& r) {
     const uint8_t* p = rp + u * 64;
-    uint32_t q[16];
-    const bool full = 64 * u + 64 <= a.in;   // a 32-weight tail ends the row
     const u32x4 v0 = load_u32x4_a16(p), v1 = load_u32x4_a16(p + 16);
     u32x4 v2 = {0u, 0u, 0u, 0u}, v3 = {0u, 0u, 0u, 0u};
-    if (full) { v2 = load_u32x4_a16(p + 32); v3 = load_u32x4_a16(p + 48); }
-    q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
-    q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
-    q[8] = v2.x; q[9] = v2.y; q[10] = v2.z; q[11] = v2.w;
-    q[12] = v3.x; q[13] = v3.y; q[14] = v3.z; q[15] = v3.w;
+    if (64 * u + 64 <= in) { v2 = load_u32x4_a16(p + 32); v3 = load_u32x4_a16(p + 48); }
+    r.q[0] = v0.x; r.q[1] = v0.y; r.q[2] = v0.z; r.q[3] = v0.w;
+    r.q[4] = v1.x; r.q[5] = v1.y; r.q[6] = v1.z; r.q[7] = v1.w;
+    r.q[8] = v2.x; r.q[9] = v2.y; r.q[10] = v2.z; r.q[11] = v2.w;
+    r.q[12] = v3.x; r.q[13] = v3.y; r.q[14] = v3.z; r.q[15] = v3.w;
+  }
+
+  template <int B>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+                                                 const float* xs, const float*, int64_t,
+                                                 const Lane&, float* acc) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const float q0 = sbyte<0>(q[t]), q1 = sbyte<1>(q[t]), q2 = sbyte<2>(q[t]), q3 = sbyte<3>(q[t]);
+      const uint32_t v = r.q[t];
+      const float q0 = sbyte<0>(v), q1 = sbyte<1>(v), q2 = sbyte<2>(v), q3 = sbyte<3>(v);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const f32x4 xv = xs4(xs + b * a.xstride, 64 * u + 4 * t);
@@ -309,67 +417,122 @@ struct FmtI8Row {
   }
 };
 
+template <class F>
+__device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
+                                           typename F::Raw& r) {
+  if constexpr (std::is_same<F, FmtI8Row>::value) {
+    F::issue_n(rp, u, a.in, r);
+  } else {
+    F::issue(rp, u, r);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// The kernel: stage x (and Q4_K sub-block sums), then walk row tiles.
+// Staging: x into LDS (padded layout, zero past `in`), and for Q4_K the sum
+// of every 32 consecutive x next to it.  One pass, one barrier.
 // ---------------------------------------------------------------------------
-template <class F, int L, int B>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
-  extern __shared__ float lds[];
-  float* xs = lds;
-  float* sums = lds + B * a.xstride;
-  const int64_t nsub = a.xpad / 32;
-  stage_x<B>(xs, a.x, a.in, a.xpad, a.xstride);
-  if constexpr (F::kSums) {
-    __syncthreads();
-    // sum of x over each 32-weight sub-block, sequential within the block
+template <bool kSums, int B>
+__device__ __forceinline__ void stage(const GemvArgs& a, float* xs, float* sums) {
+  if constexpr (kSums) {
+    const int64_t nsub = a.xpad / 32;
     for (int64_t t = threadIdx.x; t < B * nsub; t += kThreads) {
       const int64_t b = t / nsub, j = t % nsub;
-      const float* xb = xs + b * a.xstride;
+      const float* src = a.x + b * a.in + 32 * j;
+      float* dst = xs + b * a.xstride;
+      f32x4 v[8];
+      const bool live = 32 * j < a.in;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live) v[i] = *reinterpret_cast<const f32x4*>(src + 4 * i);
+      }
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const f32x4 v = xs4(xb, 32 * j + i);
-        s += v.x; s += v.y; s += v.z; s += v.w;
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<f32x4*>(dst + xs_phys(32 * j + 4 * i)) = v[i];
+        s += v[i].x; s += v[i].y; s += v[i].z; s += v[i].w;
       }
       sums[b * nsub + j] = s;
     }
+  } else {
+    stage_x<B>(xs, a.x, a.in, a.xpad, a.xstride);
   }
-  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped launch: up to kMaxGroup independent mat-vecs of one format (and
+// batch) in one grid.  Workgroup w serves tile w of the concatenated tile
+// list: op k owns tiles [tile_begin[k], tile_begin[k+1]).
+// ---------------------------------------------------------------------------
+constexpr int kMaxGroup = PESTI_MAX_GROUP;
+
+struct GroupArgs {
+  GemvArgs op[kMaxGroup];
+  int64_t tile_begin[kMaxGroup + 1];
+  int32_t n_ops;
+};
+
+// The kernel.  One workgroup = one tile of kRowsPerGroup rows of one op.
+// Every lane walks j = 0 .. ipt-1 (unit = sub + L*j) in lock step with its
+// wave, so the DPP reduction at the end sees a full wave.  The first unit's
+// loads are issued before x is staged; each next unit's loads are issued
+// before the current unit is computed.
+template <class F, int L, int B>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
+  extern __shared__ float lds[];
+  constexpr int kRowsPerWave = kWave / L;
+  constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;
+
+  const int64_t tile = blockIdx.x;
+  int k = 0;
+  while (k + 1 < g.n_ops && tile >= g.tile_begin[k + 1]) ++k;
+  const GemvArgs& a = g.op[k];
+  float* xs = lds;
+  float* sums = lds + B * a.xstride;
+  const int64_t nsub = a.xpad / 32;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int sub = lane & (L - 1);
-  const int grp = lane / L;
-  constexpr int kRowsPerWave = kWave / L;
-  constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;
+  const int64_t row = (tile - g.tile_begin[k]) * kRowsPerGroup + wave * kRowsPerWave + lane / L;
+  const int64_t ipt = (a.units + L - 1) / L;
+  const typename F::Lane ls = F::lane_state(sub);
+  const bool row_live = row < a.out;
+  const uint8_t* rp = a.w + (row_live ? row : 0) * a.row_bytes;
 
-  [[maybe_unused]] Q4KLane q4l;
-  if constexpr (F::kSums) q4l = q4k_lane(sub & 3);
+  auto live = [&](int64_t jj) {
+    const int64_t u = sub + L * jj;
+    return row_live && u < a.units && F::valid(a, u);
+  };
 
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerGroup; r0 < a.out;
-       r0 += static_cast<int64_t>(gridDim.x) * kRowsPerGroup) {
-    const int64_t row = r0 + wave * kRowsPerWave + grp;
-    float acc[B];
+  typename F::Raw cur;
+  bool have = ipt > 0 && live(0);
+  if (have) issue_unit<F>(a, rp, sub, cur);
+
+  stage<F::kSums, B>(a, xs, sums);
+  __syncthreads();
+
+  float acc[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
-    if (row < a.out) {
-      const uint8_t* rp = a.w + row * a.row_bytes;
-      for (int64_t u = sub; u < a.units; u += L) {
-        if constexpr (F::kSums) {
-          F::template unit<B>(a, rp, u, xs, sums, nsub, acc, q4l);
-        } else {
-          if (F::valid(a, u)) F::template unit<B>(a, rp, u, xs, sums, nsub, acc);
-        }
-      }
+  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  for (int64_t j = 0; j < ipt; ++j) {
+    typename F::Raw nxt;
+    bool have_n = false;
+    if (j + 1 < ipt) {
+      have_n = live(j + 1);
+      if (have_n) issue_unit<F>(a, rp, sub + L * (j + 1), nxt);
     }
+    if (have) F::template compute<B>(a, cur, sub + L * j, xs, sums, nsub, ls, acc);
+    cur = nxt;
+    have = have_n;
+  }
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = group_sum<L>(acc[b]);
-    if (sub == 0 && row < a.out) {
-      const float bv = a.bias ? a.bias[row] : 0.f;
-      const float rs = a.scales ? a.scales[row] : 1.f;
+  for (int b = 0; b < B; ++b) acc[b] = group_sum<L>(acc[b]);
+  if (sub == 0 && row_live) {
+    const float bv = a.bias ? a.bias[row] : 0.f;
+    const float rs = a.scales ? a.scales[row] : 1.f;
 #pragma unroll
-      for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[b], rs, bv);
-    }
+    for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[b], rs, bv);
   }
 }
 
@@ -381,30 +544,31 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 namespace {
 
 using pesti::GemvArgs;
+using pesti::GroupArgs;
 
 template <class F, int L, int B>
-int launch_one(const GemvArgs& a, size_t lds_bytes, hipStream_t stream) {
-  constexpr int kRowsPerGroup = pesti::kWavesPerGroup * (pesti::kWave / L);
-  const int64_t tiles = (a.out + kRowsPerGroup - 1) / kRowsPerGroup;
-  const unsigned grid = pesti_host::grid_for(tiles, 8192);
-  GemvArgs args = a;
+int launch_one(const GroupArgs& g, size_t lds_bytes, hipStream_t stream) {
+  const int64_t tiles = g.tile_begin[g.n_ops];
+  if (tiles <= 0) return PESTI_OK;
+  GroupArgs args = g;
   void* params[] = {&args};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_kernel<F, L, B>),
-                                 dim3(grid), dim3(pesti::kThreads), params, lds_bytes, stream);
+                                 dim3(static_cast<unsigned>(tiles)), dim3(pesti::kThreads), params,
+                                 lds_bytes, stream);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
 template <class F, int L>
-int launch_b(const GemvArgs& a, int batch, size_t lds, hipStream_t st) {
+int launch_b(const GroupArgs& g, int batch, size_t lds, hipStream_t st) {
   switch (batch) {
-    case 1: return launch_one<F, L, 1>(a, lds, st);
-    case 2: return launch_one<F, L, 2>(a, lds, st);
-    case 3: return launch_one<F, L, 3>(a, lds, st);
-    case 4: return launch_one<F, L, 4>(a, lds, st);
-    case 5: return launch_one<F, L, 5>(a, lds, st);
-    case 6: return launch_one<F, L, 6>(a, lds, st);
-    case 7: return launch_one<F, L, 7>(a, lds, st);
-    case 8: return launch_one<F, L, 8>(a, lds, st);
+    case 1: return launch_one<F, L, 1>(g, lds, st);
+    case 2: return launch_one<F, L, 2>(g, lds, st);
+    case 3: return launch_one<F, L, 3>(g, lds, st);
+    case 4: return launch_one<F, L, 4>(g, lds, st);
+    case 5: return launch_one<F, L, 5>(g, lds, st);
+    case 6: return launch_one<F, L, 6>(g, lds, st);
+    case 7: return launch_one<F, L, 7>(g, lds, st);
+    case 8: return launch_one<F, L, 8>(g, lds, st);
     default: return PESTI_ERR_BATCH;
   }
 }
@@ -417,46 +581,95 @@ inline int lanes_for(int64_t units) {
   return 64;
 }
 
+// Format-specific packing: packed row bytes and units per row.
 template <class F>
-int gemv_dispatch(int64_t out, int64_t in, const void* w, const float* scales, const float* x,
-                  float* y, const float* bias, int32_t batch, void* stream, int64_t row_bytes,
-                  int64_t units) {
-  if (out < 0 || in < 0) return PESTI_ERR_SHAPE;
-  if (batch < 0 || batch > PESTI_MAX_BATCH) return PESTI_ERR_BATCH;
-  if (out == 0 || batch == 0) return PESTI_OK;
-  if (in % 32 != 0 || in > PESTI_MAX_IN_FEATURES) return PESTI_ERR_SHAPE;
-  if (!y || (in > 0 && (!w || !x))) return PESTI_ERR_NULL;
-  if (scales == nullptr && std::is_same<F, pesti::FmtI8Row>::value && in > 0) return PESTI_ERR_NULL;
-  if (!pesti_host::aligned(y, 16) || (w && !pesti_host::aligned(w, 16)) ||
-      (x && !pesti_host::aligned(x, 16)) || (bias && !pesti_host::aligned(bias, 4)) ||
-      (scales && !pesti_host::aligned(scales, 4)))
+void shape_of(int64_t in, int64_t* row_bytes, int64_t* units);
+template <> void shape_of<pesti::FmtQ8_0x2>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = (in / 32) * 34; *u = in / 64;
+}
+template <> void shape_of<pesti::FmtQ8_0>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = (in / 32) * 34; *u = in / 32;
+}
+template <> void shape_of<pesti::FmtQ4_K>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 144; *u = (in + 63) / 64;
+}
+template <> void shape_of<pesti::FmtQ6_K>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 210; *u = ((in + 255) / 256) * 4;
+}
+template <> void shape_of<pesti::FmtI8Row>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = in; *u = (in + 63) / 64;
+}
+
+// Validate one op; returns PESTI_OK, an error, or 1 for "empty, skip".
+template <class F>
+int check_op(const pesti_gemv_op& o, int32_t batch) {
+  if (o.out_features < 0 || o.in_features < 0) return PESTI_ERR_SHAPE;
+  if (o.out_features == 0 || batch == 0) return 1;
+  if (o.in_features % 32 != 0 || o.in_features > PESTI_MAX_IN_FEATURES) return PESTI_ERR_SHAPE;
+  const bool has_in = o.in_features > 0;
+  if (!o.y || (has_in && (!o.w || !o.x))) return PESTI_ERR_NULL;
+  if (std::is_same<F, pesti::FmtI8Row>::value && has_in && !o.row_scales) return PESTI_ERR_NULL;
+  if (!pesti_host::aligned(o.y, 16) || (o.w && !pesti_host::aligned(o.w, 16)) ||
+      (o.x && !pesti_host::aligned(o.x, 16)) || (o.bias && !pesti_host::aligned(o.bias, 4)) ||
+      (o.row_scales && !pesti_host::aligned(o.row_scales, 4)))
     return PESTI_ERR_ALIGN;
+  return PESTI_OK;
+}
+
+template <class F>
+int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
+  if (n_ops < 0 || n_ops > PESTI_MAX_GROUP) return PESTI_ERR_SHAPE;
+  if (n_ops > 0 && !ops) return PESTI_ERR_NULL;
+  if (batch < 0 || batch > PESTI_MAX_BATCH) return PESTI_ERR_BATCH;
+  int live[PESTI_MAX_GROUP];
+  int n_live = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    const int st = check_op<F>(ops[i], batch);
+    if (st < 0) return st;
+    if (st == PESTI_OK) live[n_live++] = i;
+  }
+  if (n_live == 0) return PESTI_OK;
   int dev = 0;
   size_t lds_limit = 0;
-  int st = pesti_host::current_device(&dev, &lds_limit);
+  const int st = pesti_host::current_device(&dev, &lds_limit);
   if (st != PESTI_OK) return st;
 
-  GemvArgs a{};
-  a.w = static_cast<const uint8_t*>(w);
-  a.scales = scales;
-  a.bias = bias;
-  a.out = out;
-  a.in = in;
-  a.row_bytes = row_bytes;
-  a.units = units;
-  const int64_t pad = F::kPad;
-  a.xpad = ((in + pad - 1) / pad) * pad;
-  a.xstride = pesti::xs_stride(in, pad);
-  const size_t row_lds = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
+  GroupArgs g{};
+  int64_t max_units = 0;
+  size_t row_lds = 0;
+  for (int i = 0; i < n_live; ++i) {
+    const pesti_gemv_op& o = ops[live[i]];
+    GemvArgs& a = g.op[i];
+    a.w = static_cast<const uint8_t*>(o.w);
+    a.scales = o.row_scales;
+    a.bias = o.bias;
+    a.out = o.out_features;
+    a.in = o.in_features;
+    shape_of<F>(o.in_features, &a.row_bytes, &a.units);
+    const int64_t pad = F::kPad;
+    a.xpad = ((a.in + pad - 1) / pad) * pad;
+    a.xstride = pesti::xs_stride(a.in, pad);
+    const size_t r = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
+    if (r > row_lds) row_lds = r;
+    if (a.units > max_units) max_units = a.units;
+  }
+  g.n_ops = n_live;
   const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
-  const int L = lanes_for(units);
+  const int L = lanes_for(max_units);
+  const int64_t rows_per_group = pesti::kWavesPerGroup * (pesti::kWave / L);
+  g.tile_begin[0] = 0;
+  for (int i = 0; i < n_live; ++i)
+    g.tile_begin[i + 1] = g.tile_begin[i] + (g.op[i].out + rows_per_group - 1) / rows_per_group;
   hipStream_t stream_h = static_cast<hipStream_t>(stream);
   for (int b0 = 0; b0 < batch; b0 += per_launch) {
     const int nb = batch - b0 < per_launch ? batch - b0 : per_launch;
-    GemvArgs c = a;
-    c.x = x ? x + static_cast<int64_t>(b0) * in : nullptr;
-    c.y = y + static_cast<int64_t>(b0) * out;
+    GroupArgs c = g;
+    for (int i = 0; i < n_live; ++i) {
+      const pesti_gemv_op& o = ops[live[i]];
+      c.op[i].x = o.x ? o.x + static_cast<int64_t>(b0) * o.in_features : nullptr;
+      c.op[i].y = o.y + static_cast<int64_t>(b0) * o.out_features;
+    }
     const size_t lds = row_lds * nb;
     int r;
     if (L == 16) r = launch_b<F, 16>(c, nb, lds, stream_h);
@@ -467,36 +680,67 @@ int gemv_dispatch(int64_t out, int64_t in, const void* w, const float* scales, c
   return PESTI_OK;
 }
 
+inline pesti_gemv_op make_op(int64_t out, int64_t in, const void* w, const float* scales,
+                             const float* x, float* y, const float* bias) {
+  pesti_gemv_op o;
+  o.out_features = out;
+  o.in_features = in;
+  o.w = w;
+  o.row_scales = scales;
+  o.x = x;
+  o.y = y;
+  o.bias = bias;
+  return o;
+}
+
+// Q8_0 rows with an even block count use the two-block unit; a group uses
+// it only if every op qualifies.
+int q8_0_group(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
+  bool pairs = true;
+  for (int i = 0; i < n_ops && ops; ++i)
+    if (ops[i].in_features % 64 != 0) pairs = false;
+  return pairs ? group_dispatch<pesti::FmtQ8_0x2>(n_ops, ops, batch, stream)
+               : group_dispatch<pesti::FmtQ8_0>(n_ops, ops, batch, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
+int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, int32_t batch,
+                     void* stream) {
+  switch (format) {
+    case PESTI_FMT_Q8_0: return q8_0_group(n_ops, ops, batch, stream);
+    case PESTI_FMT_Q4_K: return group_dispatch<pesti::FmtQ4_K>(n_ops, ops, batch, stream);
+    case PESTI_FMT_Q6_K: return group_dispatch<pesti::FmtQ6_K>(n_ops, ops, batch, stream);
+    case PESTI_FMT_I8ROW: return group_dispatch<pesti::FmtI8Row>(n_ops, ops, batch, stream);
+    default: return PESTI_ERR_SHAPE;
+  }
+}
+
 int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
                     float* y, const float* bias, int32_t batch, void* stream) {
-  const int64_t nb = in_features / 32;
-  return gemv_dispatch<pesti::FmtQ8_0>(out_features, in_features, blocks, nullptr, x, y, bias, batch,
-                                       stream, nb * 34, nb);
+  const pesti_gemv_op o = make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return q8_0_group(1, &o, batch, stream);
 }
 
 int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
                     float* y, const float* bias, int32_t batch, void* stream) {
-  const int64_t nsb = (in_features + 255) / 256;
-  return gemv_dispatch<pesti::FmtQ4_K>(out_features, in_features, blocks, nullptr, x, y, bias, batch,
-                                       stream, nsb * 144, (in_features + 63) / 64);
+  const pesti_gemv_op o = make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return group_dispatch<pesti::FmtQ4_K>(1, &o, batch, stream);
 }
 
 int pesti_gemv_q6_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
                     float* y, const float* bias, int32_t batch, void* stream) {
-  const int64_t nsb = (in_features + 255) / 256;
-  return gemv_dispatch<pesti::FmtQ6_K>(out_features, in_features, blocks, nullptr, x, y, bias, batch,
-                                       stream, nsb * 210, nsb * 4);
+  const pesti_gemv_op o = make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return group_dispatch<pesti::FmtQ6_K>(1, &o, batch, stream);
 }
 
 int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* codes,
                      const float* row_scales, const float* x, float* y, const float* bias,
                      int32_t batch, void* stream) {
-  return gemv_dispatch<pesti::FmtI8Row>(out_features, in_features, codes, row_scales, x, y, bias,
-                                        batch, stream, in_features, (in_features + 63) / 64);
+  const pesti_gemv_op o = make_op(out_features, in_features, codes, row_scales, x, y, bias);
+  return group_dispatch<pesti::FmtI8Row>(1, &o, batch, stream);
 }
 
 }  // extern "C"

@@ -107,6 +107,33 @@ int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* co
                      const float* row_scales, const float* x, float* y,
                      const float* bias, int32_t batch, void* stream);
 
+/* --- grouped mat-vec: several independent products in one launch ---------
+ * One mat-vec of a group: y = W x + b with the layouts above (w is the
+ * packed rows, or the int8 codes for i8row; row_scales only for i8row). */
+typedef struct pesti_gemv_op {
+  int64_t out_features;
+  int64_t in_features;
+  const void* w;
+  const float* row_scales;
+  const float* x;
+  float* y;
+  const float* bias;
+} pesti_gemv_op;
+
+#define PESTI_MAX_GROUP 8
+
+/* Up to PESTI_MAX_GROUP independent mat-vecs of one PESTI_FMT_* format and
+ * one batch size, computed by one kernel launch.  This is the decode-step
+ * case of projections that read the same activations (Q, K and V; gate and
+ * up: "PESTI ..." README, "Conformance", per-head GQA and SwiGLU), where
+ * one launch replaces several dependent ones.  ops is a host array read
+ * during the call; each op follows the conventions and checks of the
+ * single-matrix entry points (an op with out_features == 0 is skipped);
+ * the y buffers of different ops must not overlap.  Returns the first
+ * failing op's error, before anything is enqueued. */
+int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, int32_t batch,
+                     void* stream);
+
 /* --- small-M binary16 linear layer, Y = X W^T + b ------------------------
  * X binary16 [m][in], W binary16 [out][in] (the same row orientation as the
  * mat-vec; a GPT-2 c_attn "768x2304" has in = 768, out = 2304), Y float32

@@ -132,3 +132,33 @@ def test_binding_refuses_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(tmp_path / "libpesti.so")
+
+
+def test_group_argument_checks():
+    lib = _raw()
+    ops = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None)] * 2)
+    ptr = ctypes.cast(ops, ctypes.c_void_p)
+    assert lib.pesti_gemv_group(0, 9, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_group(7, 2, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_group(1, 2, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_gemv_group(1, 2, ptr, 9, None) == _lib.PESTI_ERR_BATCH
+    bad = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None), (8, 48, FAKE, FAKE, FAKE, None, None)])
+    assert lib.pesti_gemv_group(1, 2, ctypes.cast(bad, ctypes.c_void_p), 1, None) == _lib.PESTI_ERR_SHAPE
+    bad = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE + 4, None, None)])
+    assert lib.pesti_gemv_group(2, 1, ctypes.cast(bad, ctypes.c_void_p), 1, None) == _lib.PESTI_ERR_ALIGN
+    bad = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None)])
+    assert lib.pesti_gemv_group(3, 1, ctypes.cast(bad, ctypes.c_void_p), 1, None) == _lib.PESTI_ERR_NULL
+    empty = _lib.gemv_ops([(0, 64, None, None, None, None, None)] * 3)
+    assert lib.pesti_gemv_group(1, 3, ctypes.cast(empty, ctypes.c_void_p), 1, None) == _lib.PESTI_OK
+    assert lib.pesti_gemv_group(1, 0, None, 1, None) == _lib.PESTI_OK
+    assert lib.pesti_gemv_group(1, 2, ptr, 0, None) == _lib.PESTI_OK
+
+
+def test_group_struct_layout_matches_header():
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct pesti_gemv_op \{(.*?)\} pesti_gemv_op;", text, re.S).group(1)
+    fields = re.findall(r"\b(\w+);", body)
+    assert fields == [f[0] for f in _lib.GemvOp._fields_]
+    assert ctypes.sizeof(_lib.GemvOp) == 56
+    m = re.search(r"#define PESTI_MAX_GROUP (\d+)", text)
+    assert int(m.group(1)) == _lib.MAX_GROUP

@@ -261,3 +261,58 @@ def test_gemm_f16_parity(m, k, n):
     y = run_gemm(x, w, bias)
     y_ref, s_ref = oracle.gemm_f16(x, w, bias)
     assert_within(y, y_ref, s_ref, GEMM_REL, f"gemm m{m} k{k} n{n}")
+
+
+# ---------------------------------------------------------------------------
+# grouped launches
+# ---------------------------------------------------------------------------
+GROUP_SHAPES = [(37, 896), (130, 288), (8, 4864), (0, 896), (1, 32), (300, 896), (64, 1056)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("batch", [1, 3])
+def test_group_matches_oracle_per_op(fmt, batch):
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import guarded_y, guards_intact, to_dev
+    cases, ops, bufs = [], [], []
+    for i, (out, inf) in enumerate(GROUP_SHAPES):
+        packed, scales, x, bias = make(fmt, out, inf, 40 + i, batch, with_bias=(i % 2 == 0))
+        fbuf, y = guarded_y(batch * out)
+        w_d = to_dev(packed.reshape(-1).view(np.uint8)) if packed.size else None
+        s_d = to_dev(scales) if scales is not None and scales.size else None
+        x_d = to_dev(x) if x.size else None
+        b_d = to_dev(bias) if bias is not None and bias.size else None
+        bufs.append((w_d, s_d, x_d, b_d, fbuf))
+        ops.append((out, inf, w_d, x_d, y, b_d, s_d))
+        cases.append((packed, scales, x, bias, out, inf, fbuf, y))
+    dmv.pesti_gemv_group(fmt, ops, batch)
+    torch.cuda.synchronize()
+    for packed, scales, x, bias, out, inf, fbuf, y in cases:
+        assert guards_intact(fbuf, batch * out)
+        if out == 0:
+            continue
+        got = y.cpu().numpy().reshape(batch, out)
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias, scales)
+        assert_within(got, y_ref, s_ref, GEMV_REL, f"group {fmt} {out}x{inf}")
+
+
+def test_group_equals_single_calls_bitwise():
+    """A grouped launch runs the same arithmetic as the single-matrix call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for i, (out, inf) in enumerate([(896, 896), (128, 896), (128, 896)]):
+        packed, _, x, bias = make("q4_k", out, inf, 60 + i, 1)
+        w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yg = torch.empty(out, dtype=torch.float32, device="cuda")
+        ys = torch.empty(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        singles.append((out, inf, w_d, x_d, ys, b_d))
+    dmv.pesti_gemv_group("q4_k", ops, 1)
+    for out, inf, w_d, x_d, ys, b_d in singles:
+        dmv.pesti_gemv_q4_k(out, inf, w_d, x_d, ys, b_d, 1)
+    torch.cuda.synchronize()
+    for (o, _, _, _, yg, _, _), (_, _, _, _, ys, _) in zip(ops, singles):
+        assert torch.equal(yg, ys)
