@@ -108,15 +108,29 @@ __device__ __forceinline__ float group_sum(float v) {
 template <int B>
 __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int64_t in_features,
                                         int64_t padded_len, int64_t stride) {
-  const int64_t n4 = padded_len >> 2;   // float4 slots per row
+  // All loads of a chunk are issued before any LDS store, so a wide x costs
+  // one memory round trip per chunk of kPer * kThreads float4 per batch
+  // row, not one per float4 a thread stages.
+  constexpr int kPer = 8;
+  const int n4 = static_cast<int>(padded_len >> 2);   // float4 slots per batch row
+  const int in4 = static_cast<int>(in_features >> 2);
+#pragma unroll
   for (int b = 0; b < B; ++b) {
-    const float* xb = x + b * in_features;
+    const f32x4* src = reinterpret_cast<const f32x4*>(x + b * in_features);
     float* dst = xs + b * stride;
-    for (int64_t s = threadIdx.x; s < n4; s += kThreads) {
-      const int64_t i = s << 2;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (i < in_features) v = *reinterpret_cast<const f32x4*>(xb + i);
-      *reinterpret_cast<f32x4*>(dst + xs_phys(i)) = v;
+    for (int base = 0; base < n4; base += kPer * kThreads) {
+      f32x4 v[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int s = base + r * kThreads + static_cast<int>(threadIdx.x);
+        v[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s < in4) v[r] = src[s];
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int s = base + r * kThreads + static_cast<int>(threadIdx.x);
+        if (s < n4) *reinterpret_cast<f32x4*>(dst + xs_phys(4 * s)) = v[r];
+      }
     }
   }
 }

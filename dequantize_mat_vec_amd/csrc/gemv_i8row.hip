@@ -1,0 +1,10 @@
+// I8ROW instantiation of the grouped mat-vec kernels (gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace pesti_gemv {
+
+int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
+  return group_dispatch<pesti::FmtI8Row>(n_ops, ops, batch, stream);
+}
+
+}  // namespace pesti_gemv

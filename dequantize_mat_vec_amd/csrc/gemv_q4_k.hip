@@ -1,0 +1,10 @@
+// Q4_K instantiation of the grouped mat-vec kernels (gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace pesti_gemv {
+
+int group_q4_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
+  return group_dispatch<pesti::FmtQ4_K>(n_ops, ops, batch, stream);
+}
+
+}  // namespace pesti_gemv
