@@ -11,8 +11,9 @@ alternated so that the 256 MB last-level cache cannot hold a step's bytes.
 
 Prints one JSON line: HBM GB/s over the step (nominal algorithmic bytes per
 step / time per step), microseconds per step, the roofline of the dominant
-kernel (timed with HIP events around each of its launches on the launch
-stream) and the CPU oracle's rate on a bounded sample.
+kernel (the kernel with the most time per step, timed by replaying a graph
+of only its launches between HIP events on the launch stream) and the CPU
+oracle's rate on a bounded sample.
 """
 from __future__ import annotations
 
@@ -50,10 +51,15 @@ def parse_args(argv=None):
     p.add_argument("--grouping", choices=("stage", "none"), default="stage",
                    help="one launch per dependency stage (Q/K/V, O, gate/up, down) or per call")
     p.add_argument("--kernel-steps", type=int, default=20,
-                   help="plain steps with events around every launch (per-kernel times)")
+                   help="replays of each per-kernel graph (per-kernel times)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     p.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the counter summary from two rocprofv3 --pmc runs and exit")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="before the step, copy this many MiB device-to-device three times "
+                        "(a kernel of known traffic for scaling HBM counters)")
     return p.parse_args(argv)
 
 
@@ -127,15 +133,14 @@ def make_step(lib, calls, launches, weights, xs, ys, biases):
         plans.append(plan)
     fn = lib.pesti_gemv_group
 
-    def step(copy, stream_handle, around=None):
+    def step(copy, stream_handle, only=None):
+        """One step (or, with `only`, just the launches whose indices are in it)."""
         for idx, (fid, n, ptr, _keep) in enumerate(plans[copy]):
-            if around is not None:
-                around(idx, True)
+            if only is not None and idx not in only:
+                continue
             st = fn(fid, n, ptr, 1, stream_handle)
             if st != 0:
                 raise RuntimeError(f"launch {idx} failed with status {st}")
-            if around is not None:
-                around(idx, False)
     return step
 
 
@@ -144,6 +149,78 @@ def kernel_name(fmt, infs):
                  "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     return f"gemv_kernel<{fmt}, L={lanes}, B=1>"
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# ---------------------------------------------------------------------------
+PMC_SUMMARY = os.path.join(HERE, "profiles", "decode_step_pmc.txt")
+SRC_DIR = os.path.join(HERE, "dequantize_mat_vec_amd", "csrc")
+
+
+def source_digest():
+    """sha256 over the HIP sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(SRC_DIR)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(SRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv, write_csv, calib_mib=256):
+    """Per-launch HBM bytes of every mat-vec kernel shape in a bench run, from
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
+    same counter reads for the device-to-device copy of calib_mib MiB that
+    the run starts with (it moves calib_mib MiB each way)."""
+    import csv
+    import statistics
+    known_kib = calib_mib * 1024.0
+    out = {"source_sha256": source_digest(), "calibration": {}, "kernels": {}}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = list(csv.DictReader(open(path)))
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > known_kib / 4]
+        factor = known_kib / statistics.median(copies)
+        out["calibration"][counter] = {"copy_mib": calib_mib, "counter_kib": statistics.median(copies),
+                                       "factor": round(factor, 5)}
+        per = {}
+        for r in rows:
+            if "gemv_kernel" not in r["Kernel_Name"]:
+                continue
+            key = f"{r['Kernel_Name'].split('(')[0]} grid={r['Grid_Size']}"
+            per.setdefault(key, []).append(float(r["Counter_Value"]) * factor * 1024.0)
+        for key, vals in per.items():
+            d = out["kernels"].setdefault(key, {})
+            d[counter.lower() + "_bytes"] = round(statistics.median(vals))
+            d["dispatches"] = len(vals)
+    with open(PMC_SUMMARY, "w") as f:
+        f.write(json.dumps(out, indent=1) + "\n")
+    return out
+
+
+def dominant_traffic(kernel_label):
+    """Average HBM bytes per launch of the dominant kernel from the committed
+    counter summary, or None if it is missing or was taken on other sources."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    try:
+        summ = json.load(open(PMC_SUMMARY))
+    except ValueError:
+        return None
+    if summ.get("source_sha256") != source_digest():
+        return None
+    fmt = kernel_label.split("<")[1].split(",")[0]
+    lanes = kernel_label.split("L=")[1].split(",")[0]
+    tag = {"q8_0": "FmtQ8_0", "q4_k": "FmtQ4_K", "q6_k": "FmtQ6_K"}[fmt]
+    # one entry per launch shape of the kernel; every shape of the decode step
+    # occurs equally often (once per layer), so the per-launch average is
+    # the plain mean over shapes
+    vals = [d.get("fetch_size_bytes", 0) + d.get("write_size_bytes", 0)
+            for key, d in summ["kernels"].items() if f"{tag}, {lanes}, 1," in key]
+    return sum(vals) / len(vals) if vals else None
 
 
 # ---------------------------------------------------------------------------
@@ -206,6 +283,9 @@ def main(argv=None):
     if args.cpu_leg:
         print(json.dumps(cpu_leg(args.cpu_sample_seconds)))
         return 0
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the decode-step mat-vec runs on a single MI355X)", file=sys.stderr)
@@ -221,6 +301,16 @@ def main(argv=None):
     bytes_per_step = sum(call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     graphs = None
     with torch.cuda.stream(stream):
@@ -251,35 +341,45 @@ def main(argv=None):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
-        # per-kernel durations: plain steps with events around every launch
+        # Per-kernel durations.  Inside a HIP graph the step's kernels run
+        # back to back, so a kernel's duration is measured by replaying a
+        # graph of only that kernel's launches of the step (same buffers,
+        # weight copies alternated) between two HIP events on the launch
+        # stream: time per replay / launches per replay.
         names = [kernel_name(fmt, [calls[i][4] for i in idx]) for fmt, idx in launches]
-        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in launches] for _ in range(args.kernel_steps)]
-        cur = {}
-
-        def around(idx, before):
-            e = cur["evs"][idx]
-            (e[0] if before else e[1]).record(stream)
-
-        for s in range(args.kernel_steps):
-            cur["evs"] = evs[s]
-            step(s % args.copies, sh, around)
-        torch.cuda.synchronize()
+        per_kernel = {}
+        for name in sorted(set(names)):
+            only = {i for i, n in enumerate(names) if n == name}
+            subs = []
+            for c in range(args.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(c, torch.cuda.current_stream().cuda_stream, only)
+                subs.append(g)
+            for i in range(3):
+                subs[i % args.copies].replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.kernel_steps):
+                subs[i % args.copies].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_kernel[name] = (e0.elapsed_time(e1), only)
 
     per_name = {}
-    for s in range(args.kernel_steps):
-        for li, (fmt, idx) in enumerate(launches):
-            ms = evs[s][li][0].elapsed_time(evs[s][li][1])
-            d = per_name.setdefault(names[li], {"ms": 0.0, "launches": 0, "bytes": 0})
-            d["ms"] += ms
-            d["launches"] += 1
-            d["bytes"] += sum(call_bytes(calls[i][2], calls[i][3], calls[i][4], 1, calls[i][5])
-                              for i in idx)
+    for name, (ms, only) in per_kernel.items():
+        per_name[name] = {
+            "ms": ms, "launches": len(only) * args.kernel_steps,
+            "bytes": args.kernel_steps * sum(
+                call_bytes(calls[i][2], calls[i][3], calls[i][4], 1, calls[i][5])
+                for li in only for i in launches[li][1])}
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1]["ms"])
     avg_s = dom["ms"] / dom["launches"] / 1e3
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / avg_s / 1e9
 
+    traffic = dominant_traffic(dom_name)
     ms_per_step = elapsed / args.steps * 1e3
     value = bytes_per_step / (ms_per_step / 1e3) / 1e9
     result = {
@@ -304,7 +404,8 @@ def main(argv=None):
                    "grouping": args.grouping, "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": int(bytes_per_launch),
+                     "traffic": (None if traffic is None else int(traffic)),
+                     "bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_us": round(avg_s * 1e6, 3)},
         "kernels": {k: {"launches_per_step": v["launches"] // args.kernel_steps,
                         "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
