@@ -55,6 +55,10 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     p.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--suite", action="store_true",
+                   help="instead of the decode step, time every other workload (int8, Q4_K FFN, "
+                        "f16 GEMM, LM-head sweep) and print one JSON line per case")
+    p.add_argument("--suite-filter", default="", help="only suite cases whose name contains this")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the counter summary from two rocprofv3 --pmc runs and exit")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -149,6 +153,112 @@ def kernel_name(fmt, infs):
                  "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     return f"gemv_kernel<{fmt}, L={lanes}, B=1>"
+
+
+# ---------------------------------------------------------------------------
+# Suite: the other workloads, one call shape at a time
+# ---------------------------------------------------------------------------
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def suite_cases():
+    """(name, kind, params) for every non-step workload."""
+    from dequantize_mat_vec_amd import synth
+    cases = [("i8row 896x896 b1", "gemv", ("i8row", 896, 896, 1)),
+             ("q4_k 4864x896 b1 (gate/up)", "gemv", ("q4_k", 4864, 896, 1)),
+             ("q4_k 896x4864 b1 (down)", "gemv", ("q4_k", 896, 4864, 1))]
+    for m in (8, 32, 64):
+        for name, k, n in synth.GPT2_LINEARS:
+            cases.append((f"f16 gemm {name} m{m} ({k}->{n})", "gemm", (m, k, n)))
+    for fmt in ("q8_0", "q4_k", "q6_k"):
+        for b in (1, 2, 4, 8):
+            cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
+    cases.append(("q8_0 gpt2 lm-head 50257x768 b1", "gemv", ("q8_0", synth.GPT2_VOCAB, 768, 1)))
+    return cases
+
+
+def run_suite(lib, args):
+    """Each case: enough weight copies to pass 640 MB (so the 256 MB
+    last-level cache holds none between uses), a HIP graph of `reps`
+    launches cycling over them, timed between two events; µs per call =
+    graph time / reps."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dequantize_mat_vec_amd import _lib, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    out_lines = []
+    for idx, (name, kind, prm) in enumerate(suite_cases()):
+        if args.suite_filter and args.suite_filter not in name:
+            continue
+        rng = synth.rng_for(4 if "lm-head" in name else (0 if kind == "gemv" and prm[0] == "i8row" else 1), idx, 0)
+        if kind == "gemv":
+            fmt, out, inf, batch = prm
+            packed, scales = synth.matrix(fmt, rng, out, inf)
+            nbytes = packed.size
+            x = torch.from_numpy(synth.activations(rng, batch, inf)).to(dev)
+            y = torch.empty(batch * out, dtype=torch.float32, device=dev)
+            sc = torch.from_numpy(scales).to(dev) if scales is not None else None
+            algo = call_bytes(fmt, out, inf, batch, False)
+            flops = 2.0 * out * inf * batch
+        else:
+            m, k, n = prm
+            w16 = synth.f16_weights(rng, n, k)
+            x16 = torch.from_numpy(synth.f16_activations(rng, m, k).view(np.uint16)).to(dev)
+            b = torch.from_numpy(synth.bias(rng, n)).to(dev)
+            y = torch.empty(m * n, dtype=torch.float32, device=dev)
+            packed = w16.view(np.uint8)
+            nbytes = packed.size
+            algo = 2 * n * k + 2 * m * k + 4 * m * n + 4 * n
+            flops = 2.0 * m * n * k
+        copies = max(2, int(np.ceil(640e6 / nbytes)))
+        host = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
+        ws = [host.to(dev) for _ in range(copies)]
+        reps = int(min(max(copies, 40), 400))
+
+        def launch(i, sh):
+            if kind == "gemv":
+                st = (lib.pesti_gemv_i8row(out, inf, ws[i % copies].data_ptr(), sc.data_ptr(),
+                                           x.data_ptr(), y.data_ptr(), None, batch, sh)
+                      if fmt == "i8row" else
+                      getattr(lib, f"pesti_gemv_{fmt}")(out, inf, ws[i % copies].data_ptr(),
+                                                       x.data_ptr(), y.data_ptr(), None, batch, sh))
+            else:
+                st = lib.pesti_gemm_f16_smallm(m, n, k, ws[i % copies].data_ptr(), x16.data_ptr(),
+                                               y.data_ptr(), b.data_ptr(), sh)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st}")
+
+        with torch.cuda.stream(stream):
+            launch(0, stream.cuda_stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(reps):
+                    launch(i, torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            best = None
+            for _ in range(3):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) * 1e3 / reps
+                best = t if best is None else min(best, t)
+        gbs = algo / best / 1e3
+        rec = {"case": name, "us_per_call": round(best, 3), "GB/s": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(flops / best / 1e6, 3),
+               "algorithmic_bytes": int(algo), "weight_copies": copies}
+        if kind == "gemm":
+            rec["mfma_frac"] = round(flops / best / 1e6 / MFMA_F16_PEAK_TFLOPS, 5)
+        print(json.dumps(rec), flush=True)
+        out_lines.append(rec)
+        del ws, g
+        torch.cuda.empty_cache()
+    return out_lines
 
 
 # ---------------------------------------------------------------------------
@@ -295,6 +405,9 @@ def main(argv=None):
     import dequantize_mat_vec_amd as dmv
     lib = dmv.load()
     torch.cuda.set_device(0)
+    if args.suite:
+        run_suite(lib, args)
+        return 0
     calls, weights, xs, ys, biases = build_inputs(args.copies)
     launches = plan_launches(calls, args.grouping)
     step = make_step(lib, calls, launches, weights, xs, ys, biases)
