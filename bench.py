@@ -148,11 +148,14 @@ def make_step(lib, calls, launches, weights, xs, ys, biases):
     return step
 
 
-def kernel_name(fmt, infs):
+def kernel_name(fmt, infs, outs):
+    """Label of the mat-vec kernel instance one batch-1 launch uses: lanes
+    per row L by the longest row (one row per lane group at batch 1)."""
     units = max({"q8_0": inf // 64 if inf % 64 == 0 else inf // 32, "q4_k": -(-inf // 64),
                  "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
-    return f"gemv_kernel<{fmt}, L={lanes}, B=1>"
+    rows = 1
+    return f"gemv_kernel<{fmt}, L={lanes}, B=1, R={rows}>"
 
 
 # ---------------------------------------------------------------------------
@@ -459,7 +462,8 @@ def main(argv=None):
         # graph of only that kernel's launches of the step (same buffers,
         # weight copies alternated) between two HIP events on the launch
         # stream: time per replay / launches per replay.
-        names = [kernel_name(fmt, [calls[i][4] for i in idx]) for fmt, idx in launches]
+        names = [kernel_name(fmt, [calls[i][4] for i in idx], [calls[i][3] for i in idx])
+                 for fmt, idx in launches]
         per_kernel = {}
         for name in sorted(set(names)):
             only = {i for i, n in enumerate(names) if n == name}

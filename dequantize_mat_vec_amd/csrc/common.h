@@ -91,11 +91,11 @@ __device__ __forceinline__ float dpp(float v) {
 
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(L == 16 || L == 32 || L == 64, "group of 16, 32 or 64 lanes");
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "group of 4 to 64 lanes");
   v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
   v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp<0x141>(v);   // row_half_mirror: lane i <-> 7 - i within 8
-  v += dpp<0x140>(v);   // row_mirror: lane i <-> 15 - i within 16
+  if constexpr (L >= 8) v += dpp<0x141>(v);    // row_half_mirror: lane i <-> 7 - i within 8
+  if constexpr (L >= 16) v += dpp<0x140>(v);   // row_mirror: lane i <-> 15 - i within 16
   if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
   if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
   return v;

@@ -3,6 +3,37 @@
 // gemv_i8row.hip).
 #include "gemv_impl.h"
 
+namespace pesti {
+
+// Ops with in_features == 0: y = bias (or zeros), every batch column.
+__global__ __launch_bounds__(kThreads) void bias_fill_kernel(GroupArgs g, int batch) {
+  const GemvArgs a = g.op[blockIdx.y];
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (o >= a.out) return;
+  const float v = a.bias ? a.bias[o] : 0.f;
+  for (int b = 0; b < batch; ++b) a.y[b * a.out + o] = v;
+}
+
+}  // namespace pesti
+
+namespace pesti_gemv {
+
+int fill_bias(const GroupArgs& g, int batch, hipStream_t stream) {
+  int64_t rows = 0;
+  for (int i = 0; i < g.n_ops; ++i) rows = g.op[i].out > rows ? g.op[i].out : rows;
+  if (rows <= 0 || batch <= 0) return PESTI_OK;
+  const int64_t blocks = (rows + pesti::kThreads - 1) / pesti::kThreads;
+  GroupArgs args = g;
+  int nb = batch;
+  void* params[] = {&args, &nb};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::bias_fill_kernel),
+                                       dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(g.n_ops)),
+                                       dim3(pesti::kThreads), params, 0, stream);
+  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
+}  // namespace pesti_gemv
+
 extern "C" {
 
 int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, int32_t batch,

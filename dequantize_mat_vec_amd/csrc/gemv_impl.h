@@ -37,6 +37,7 @@
 // decode step's chain of dependent launches.
 #pragma once
 
+#include <cstdint>
 #include <type_traits>
 
 #include "common.h"
@@ -81,9 +82,9 @@ struct FmtQ8_0x2 {
   struct Raw { uint32_t w[17]; };
   struct Lane {};
   __device__ static Lane lane_state(int) { return {}; }
-  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
 
-  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
     const uint8_t* p = rp + u * 68;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -93,33 +94,46 @@ struct FmtQ8_0x2 {
     r.w[16] = load_u32(p + 64);
   }
 
-  template <int B>
-  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+  // r[0..R-1]: the same unit of R rows; acc[k * B + b] is row k, column b.
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
                                                  const float* xs, const float*, int64_t,
                                                  const Lane&, float* acc) {
-    const float dA = f16_lo(r.w[0]), dB = f16_hi(r.w[8]);
-    float pa[B], pb[B];
+    float pa[R][B], pb[R][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) { pa[b] = 0.f; pb[b] = 0.f; }
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { pa[k][b] = 0.f; pb[k][b] = 0.f; }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t ca = align_bytes(r.w[j + 1], r.w[j], 2);
-      const uint32_t cb = r.w[9 + j];
-      const float a0 = sbyte<0>(ca), a1 = sbyte<1>(ca), a2 = sbyte<2>(ca), a3 = sbyte<3>(ca);
-      const float b0 = sbyte<0>(cb), b1 = sbyte<1>(cb), b2 = sbyte<2>(cb), b3 = sbyte<3>(cb);
+      f32x4 xa[B], xc[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float* xb = xs + b * a.xstride;
-        const f32x4 xa = xs4(xb, 64 * u + 4 * j);
-        const f32x4 xc = xs4(xb, 64 * u + 32 + 4 * j);
-        pa[b] = fmaf(a0, xa.x, pa[b]); pa[b] = fmaf(a1, xa.y, pa[b]);
-        pa[b] = fmaf(a2, xa.z, pa[b]); pa[b] = fmaf(a3, xa.w, pa[b]);
-        pb[b] = fmaf(b0, xc.x, pb[b]); pb[b] = fmaf(b1, xc.y, pb[b]);
-        pb[b] = fmaf(b2, xc.z, pb[b]); pb[b] = fmaf(b3, xc.w, pb[b]);
+        xa[b] = xs4(xs + b * a.xstride, 64 * u + 4 * j);
+        xc[b] = xs4(xs + b * a.xstride, 64 * u + 32 + 4 * j);
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t ca = align_bytes(r[k].w[j + 1], r[k].w[j], 2);
+        const uint32_t cb = r[k].w[9 + j];
+        const float a0 = sbyte<0>(ca), a1 = sbyte<1>(ca), a2 = sbyte<2>(ca), a3 = sbyte<3>(ca);
+        const float b0 = sbyte<0>(cb), b1 = sbyte<1>(cb), b2 = sbyte<2>(cb), b3 = sbyte<3>(cb);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          pa[k][b] = fmaf(a0, xa[b].x, pa[k][b]); pa[k][b] = fmaf(a1, xa[b].y, pa[k][b]);
+          pa[k][b] = fmaf(a2, xa[b].z, pa[k][b]); pa[k][b] = fmaf(a3, xa[b].w, pa[k][b]);
+          pb[k][b] = fmaf(b0, xc[b].x, pb[k][b]); pb[k][b] = fmaf(b1, xc[b].y, pb[k][b]);
+          pb[k][b] = fmaf(b2, xc[b].z, pb[k][b]); pb[k][b] = fmaf(b3, xc[b].w, pb[k][b]);
+        }
       }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = fmaf(dB, pb[b], fmaf(dA, pa[b], acc[b]));
+    for (int k = 0; k < R; ++k) {
+      const float dA = f16_lo(r[k].w[0]), dB = f16_hi(r[k].w[8]);
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        acc[k * B + b] = fmaf(dB, pb[k][b], fmaf(dA, pa[k][b], acc[k * B + b]));
+    }
   }
 };
 
@@ -136,9 +150,9 @@ struct FmtQ8_0 {
   struct Raw { uint32_t w[9]; uint32_t s; };
   struct Lane {};
   __device__ static Lane lane_state(int) { return {}; }
-  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
 
-  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
     const uint8_t* p = rp + u * 34;
     const uint32_t s = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);   // 0 or 2
     const uint8_t* pa = p - s;
@@ -151,72 +165,78 @@ struct FmtQ8_0 {
     r.s = s;
   }
 
-  template <int B>
-  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+  // The realignment s is per row: with an odd block count, consecutive rows
+  // start on alternating dword phases.
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
                                                  const float* xs, const float*, int64_t,
                                                  const Lane&, float* acc) {
-    const float d = r.s ? f16_hi(r.w[0]) : f16_lo(r.w[0]);
-    float part[B];
+    float part[R][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) part[b] = 0.f;
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) part[k][b] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t c = r.s ? r.w[j + 1] : align_bytes(r.w[j + 1], r.w[j], 2);
-      const float q0 = sbyte<0>(c), q1 = sbyte<1>(c), q2 = sbyte<2>(c), q3 = sbyte<3>(c);
+      f32x4 xv[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const f32x4 xv = xs4(xs + b * a.xstride, u * 32 + 4 * j);
-        part[b] = fmaf(q0, xv.x, part[b]);
-        part[b] = fmaf(q1, xv.y, part[b]);
-        part[b] = fmaf(q2, xv.z, part[b]);
-        part[b] = fmaf(q3, xv.w, part[b]);
+      for (int b = 0; b < B; ++b) xv[b] = xs4(xs + b * a.xstride, u * 32 + 4 * j);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t c = r[k].s ? r[k].w[j + 1] : align_bytes(r[k].w[j + 1], r[k].w[j], 2);
+        const float q0 = sbyte<0>(c), q1 = sbyte<1>(c), q2 = sbyte<2>(c), q3 = sbyte<3>(c);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          part[k][b] = fmaf(q0, xv[b].x, part[k][b]);
+          part[k][b] = fmaf(q1, xv[b].y, part[k][b]);
+          part[k][b] = fmaf(q2, xv[b].z, part[k][b]);
+          part[k][b] = fmaf(q3, xv[b].w, part[k][b]);
+        }
       }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = fmaf(d, part[b], acc[b]);
+    for (int k = 0; k < R; ++k) {
+      const float d = r[k].s ? f16_hi(r[k].w[0]) : f16_lo(r[k].w[0]);
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[k * B + b] = fmaf(d, part[k][b], acc[k * B + b]);
+    }
   }
 };
 
 // ---------------------------------------------------------------------------
 // Q4_K: unit u = super-block u/4, run g = u%4.  g is fixed per lane (L is a
-// multiple of 4), so the bit positions of its two scales and mins are
-// computed once per lane.
+// multiple of 4), so the byte selectors that gather its two scales and
+// mins are computed once per lane.
 // ---------------------------------------------------------------------------
 struct FmtQ4_K {
   static constexpr bool kSums = true;
   static constexpr int kPad = 256;
   struct Raw { u32x4 hdr, qa, qb; };
+  // Per lane (run g = sub % 4, sub-blocks 2g and 2g+1), byte selectors that
+  // gather the unit's raw scale/min bytes, a = 2 * (g % 2):
+  //   sel_yz: [S[a], S[a+1], S[a+4], S[a+5]]   (header dwords 1 and 2)
+  //   sel_w:  [S[a+8], S[a+9], S[a+8], S[a+9]] (header dword 3)
+  // For g < 2 the four 6-bit values (sc, sc, m, m) are the low 6 bits of
+  // the first gather; for g >= 2 their low 4 bits come from the second
+  // gather (low nibbles for sc, high nibbles for m) and their top 2 bits
+  // from bits 6-7 of the first.
   struct Lane {
-    uint32_t lo_sc_shift0, lo_sc_shift1, lo_m_shift0, lo_m_shift1, lo_width;
-    uint32_t hi_shift0, hi_shift1, hi_width;
-    bool low_half;   // sub-blocks 0..3 (g < 2)
+    uint32_t sel_yz, sel_w;
+    bool high;   // g >= 2
   };
-  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
 
   __device__ static Lane lane_state(int sub) {
-    const int g = sub & 3;
+    const uint32_t a = 2u * (static_cast<uint32_t>(sub) & 1u);
     Lane s;
-    const int j0 = 2 * g, j1 = 2 * g + 1;
-    s.low_half = g < 2;
-    if (g < 2) {
-      // sc[j] = S[j] & 63 and m[j] = S[j+4] & 63: byte j of dwords 1 and 2.
-      s.lo_sc_shift0 = 8 * j0; s.lo_sc_shift1 = 8 * j1;
-      s.lo_m_shift0 = 8 * j0;  s.lo_m_shift1 = 8 * j1;
-      s.lo_width = 6; s.hi_width = 0; s.hi_shift0 = 0; s.hi_shift1 = 0;
-    } else {
-      // sc[j] = (S[j+4] & 15) | (S[j-4] >> 6) << 4,
-      // m[j]  = (S[j+4] >> 4) | (S[j] >> 6) << 4, with k = j - 4:
-      // low parts in byte k of dword 3, high parts in bits 6-7 of byte k of
-      // dwords 1 (scales) and 2 (mins).
-      const int k0 = j0 - 4, k1 = j1 - 4;
-      s.lo_sc_shift0 = 8 * k0; s.lo_sc_shift1 = 8 * k1;
-      s.lo_m_shift0 = 8 * k0 + 4; s.lo_m_shift1 = 8 * k1 + 4;
-      s.lo_width = 4; s.hi_width = 2; s.hi_shift0 = 8 * k0 + 6; s.hi_shift1 = 8 * k1 + 6;
-    }
+    // v_perm_b32 numbers the bytes of (src0:src1) 0-3 in src1, 4-7 in src0.
+    s.sel_yz = (4u + a) | (5u + a) << 8 | a << 16 | (a + 1u) << 24;
+    s.sel_w = a | (a + 1u) << 8 | a << 16 | (a + 1u) << 24;
+    s.high = (sub & 2) != 0;
     return s;
   }
 
-  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
     const uint8_t* sbp = rp + (u >> 2) * 144;
     const int g = static_cast<int>(u & 3);
     r.hdr = load_u32x4_a16(sbp);
@@ -224,56 +244,84 @@ struct FmtQ4_K {
     r.qb = load_u32x4_a16(sbp + 32 + 32 * g);
   }
 
-  template <int B>
-  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+  // Code dword t (0..7) of the unit: bytes 4t..4t+3 of its 32-byte run.
+  __device__ __forceinline__ static uint32_t code_word(const Raw& r, int t) {
+    switch (t) {
+      case 0: return r.qa.x;
+      case 1: return r.qa.y;
+      case 2: return r.qa.z;
+      case 3: return r.qa.w;
+      case 4: return r.qb.x;
+      case 5: return r.qb.y;
+      case 6: return r.qb.z;
+      default: return r.qb.w;
+    }
+  }
+
+  // Scale factors of the unit's two sub-blocks: d*sc (times 2^9, undoing the
+  // code conversion's 2^-9) and dmin*m.
+  __device__ __forceinline__ static void scales(const u32x4& hdr, const Lane& L, float& ds0,
+                                                float& ds1, float& dm0, float& dm1) {
+    const float d = f16_lo(hdr.x), dmin = f16_hi(hdr.x);
+    const uint32_t p = __builtin_amdgcn_perm(hdr.y, hdr.z, L.sel_yz);   // [sc0 sc1 m0 m1] raw
+    const uint32_t q = __builtin_amdgcn_perm(hdr.w, hdr.w, L.sel_w);
+    const uint32_t lo4 = (q & 0x00000F0Fu) | ((q >> 4) & 0x0F0F0000u);
+    const uint32_t hi = (lo4 | ((p >> 2) & 0x30303030u));
+    const uint32_t v = L.high ? hi : (p & 0x3F3F3F3Fu);
+    const float d512 = d * 512.0f;
+    ds0 = d512 * ubyte<0>(v);
+    ds1 = d512 * ubyte<1>(v);
+    dm0 = dmin * ubyte<2>(v);
+    dm1 = dmin * ubyte<3>(v);
+  }
+
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
                                                  const float* xs, const float* sums, int64_t nsub,
                                                  const Lane& L, float* acc) {
-    const u32x4 hdr = r.hdr;
-    const float d = f16_lo(hdr.x), dmin = f16_hi(hdr.x);
-    const uint32_t src_sc = L.low_half ? hdr.y : hdr.w;
-    const uint32_t src_m = L.low_half ? hdr.z : hdr.w;
-    const uint32_t sc0 = __builtin_amdgcn_ubfe(src_sc, L.lo_sc_shift0, L.lo_width) |
-                         (__builtin_amdgcn_ubfe(hdr.y, L.hi_shift0, L.hi_width) << 4);
-    const uint32_t sc1 = __builtin_amdgcn_ubfe(src_sc, L.lo_sc_shift1, L.lo_width) |
-                         (__builtin_amdgcn_ubfe(hdr.y, L.hi_shift1, L.hi_width) << 4);
-    const uint32_t m0 = __builtin_amdgcn_ubfe(src_m, L.lo_m_shift0, L.lo_width) |
-                        (__builtin_amdgcn_ubfe(hdr.z, L.hi_shift0, L.hi_width) << 4);
-    const uint32_t m1 = __builtin_amdgcn_ubfe(src_m, L.lo_m_shift1, L.lo_width) |
-                        (__builtin_amdgcn_ubfe(hdr.z, L.hi_shift1, L.hi_width) << 4);
-    const uint32_t q[8] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w, r.qb.x, r.qb.y, r.qb.z, r.qb.w};
-    float p0[B], p1[B];
+    float p0[R][B], p1[R][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) { p0[b] = 0.f; p1[b] = 0.f; }
-    const int64_t x0 = 64 * u;   // first weight of the run (sub-block 2g)
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { p0[k][b] = 0.f; p1[k][b] = 0.f; }
+    const int x0 = 64 * u;   // first weight of the run (sub-block 2g)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      float l0, l1, l2, l3, h0, h1, h2, h3;
-      nibbles_x512(q[t] & 0x0F0F0F0Fu, l0, l1, l2, l3);
-      nibbles_x512((q[t] >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);
+      f32x4 xl[B], xh[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float* xb = xs + b * a.xstride;
-        const f32x4 xl = xs4(xb, x0 + 4 * t);
-        const f32x4 xh = xs4(xb, x0 + 32 + 4 * t);
-        p0[b] = fmaf(l0, xl.x, p0[b]); p0[b] = fmaf(l1, xl.y, p0[b]);
-        p0[b] = fmaf(l2, xl.z, p0[b]); p0[b] = fmaf(l3, xl.w, p0[b]);
-        p1[b] = fmaf(h0, xh.x, p1[b]); p1[b] = fmaf(h1, xh.y, p1[b]);
-        p1[b] = fmaf(h2, xh.z, p1[b]); p1[b] = fmaf(h3, xh.w, p1[b]);
+        xl[b] = xs4(xs + b * a.xstride, x0 + 4 * t);
+        xh[b] = xs4(xs + b * a.xstride, x0 + 32 + 4 * t);
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t q = code_word(r[k], t);
+        float l0, l1, l2, l3, h0, h1, h2, h3;
+        nibbles_x512(q & 0x0F0F0F0Fu, l0, l1, l2, l3);
+        nibbles_x512((q >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          p0[k][b] = fmaf(l0, xl[b].x, p0[k][b]); p0[k][b] = fmaf(l1, xl[b].y, p0[k][b]);
+          p0[k][b] = fmaf(l2, xl[b].z, p0[k][b]); p0[k][b] = fmaf(l3, xl[b].w, p0[k][b]);
+          p1[k][b] = fmaf(h0, xh[b].x, p1[k][b]); p1[k][b] = fmaf(h1, xh[b].y, p1[k][b]);
+          p1[k][b] = fmaf(h2, xh[b].z, p1[k][b]); p1[k][b] = fmaf(h3, xh[b].w, p1[k][b]);
+        }
       }
     }
-    // p0, p1 carry a factor 2^-9 from the code conversion: scale d by 2^9.
-    const float d512 = d * 512.0f;
-    const float ds0 = d512 * static_cast<float>(sc0), ds1 = d512 * static_cast<float>(sc1);
-    const float dm0 = dmin * static_cast<float>(m0), dm1 = dmin * static_cast<float>(m1);
-    const int64_t j0 = 2 * u;    // sub-block index of the row (32 weights each)
+    const int j0 = 2 * u;    // sub-block index of the row (32 weights each)
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float* sb_sums = sums + b * nsub;
-      float v = ds0 * p0[b];
-      v = fmaf(ds1, p1[b], v);
-      v = fmaf(-dm0, sb_sums[j0], v);
-      v = fmaf(-dm1, sb_sums[j0 + 1], v);
-      acc[b] += v;
+    for (int k = 0; k < R; ++k) {
+      float ds0, ds1, dm0, dm1;
+      scales(r[k].hdr, L, ds0, ds1, dm0, dm1);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* sb_sums = sums + b * nsub;
+        float v = ds0 * p0[k][b];
+        v = fmaf(ds1, p1[k][b], v);
+        v = fmaf(-dm0, sb_sums[j0], v);
+        v = fmaf(-dm1, sb_sums[j0 + 1], v);
+        acc[k * B + b] += v;
+      }
     }
   }
 };
@@ -295,7 +343,7 @@ struct FmtQ6_K {
   struct Lane {};
   __device__ static Lane lane_state(int) { return {}; }
 
-  __device__ static bool valid(const GemvArgs& a, int64_t u) {
+  __device__ static bool valid(const GemvArgs& a, int u) {
     return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1) < a.in;
   }
 
@@ -305,7 +353,7 @@ struct FmtQ6_K {
     w[4] = load_u32(p + 16);
   }
 
-  __device__ __forceinline__ static void issue(const uint8_t* rp, int64_t u, Raw& r) {
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
     const int h = static_cast<int>((u >> 1) & 1);
     const int c = static_cast<int>(u & 1);
     const uint8_t* sbp = rp + (u >> 2) * 210;
@@ -325,53 +373,68 @@ struct FmtQ6_K {
     r.s = s;
   }
 
-  template <int B>
-  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
                                                  const float* xs, const float*, int64_t,
                                                  const Lane&, float* acc) {
     const int h = static_cast<int>((u >> 1) & 1);
     const int c = static_cast<int>(u & 1);
-    const uint32_t s = r.s;
-    const uint32_t S0 = align_bytes(r.sc[1], r.sc[0], s) >> (8 * c);
-    const uint32_t S1 = align_bytes(r.sc[2], r.sc[1], s) >> (8 * c);
-    const float sc[4] = {sbyte<0>(S0), sbyte<2>(S0), sbyte<0>(S1), sbyte<2>(S1)};
-    const float dq = 0.25f * f16_lo(r.d);
-    float p[4][B];
+    float p[R][4][B];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int k = 0; k < R; ++k)
 #pragma unroll
-      for (int b = 0; b < B; ++b) p[g][b] = 0.f;
-    const int64_t xbase = 256 * (u >> 2) + 128 * h + 16 * c;
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int b = 0; b < B; ++b) p[k][g][b] = 0.f;
+    const int xbase = 256 * (u >> 2) + 128 * h + 16 * c;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t la = align_bytes(r.la[j + 1], r.la[j], s);
-      const uint32_t lb = align_bytes(r.lb[j + 1], r.lb[j], s);
-      const uint32_t hf = align_bytes(r.hh[j + 1], r.hh[j], s) ^ 0xAAAAAAAAu;   // high part XOR 2
-      uint32_t v[4];
-      v[0] = ((la << 2) & 0x3C3C3C3Cu) | ((hf << 6) & 0xC0C0C0C0u);
-      v[1] = ((lb << 2) & 0x3C3C3C3Cu) | ((hf << 4) & 0xC0C0C0C0u);
-      v[2] = ((la >> 2) & 0x3C3C3C3Cu) | ((hf << 2) & 0xC0C0C0C0u);
-      v[3] = ((lb >> 2) & 0x3C3C3C3Cu) | (hf & 0xC0C0C0C0u);
+      uint32_t v[R][4];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t s = r[k].s;
+        const uint32_t la = align_bytes(r[k].la[j + 1], r[k].la[j], s);
+        const uint32_t lb = align_bytes(r[k].lb[j + 1], r[k].lb[j], s);
+        const uint32_t hf = align_bytes(r[k].hh[j + 1], r[k].hh[j], s) ^ 0xAAAAAAAAu;   // high part XOR 2
+        v[k][0] = ((la << 2) & 0x3C3C3C3Cu) | ((hf << 6) & 0xC0C0C0C0u);
+        v[k][1] = ((lb << 2) & 0x3C3C3C3Cu) | ((hf << 4) & 0xC0C0C0C0u);
+        v[k][2] = ((la >> 2) & 0x3C3C3C3Cu) | ((hf << 2) & 0xC0C0C0C0u);
+        v[k][3] = ((lb >> 2) & 0x3C3C3C3Cu) | (hf & 0xC0C0C0C0u);
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float q0 = sbyte<0>(v[g]), q1 = sbyte<1>(v[g]), q2 = sbyte<2>(v[g]), q3 = sbyte<3>(v[g]);
+        f32x4 xv[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const f32x4 xv = xs4(xs + b * a.xstride, xbase + 32 * g + 4 * j);
-          p[g][b] = fmaf(q0, xv.x, p[g][b]);
-          p[g][b] = fmaf(q1, xv.y, p[g][b]);
-          p[g][b] = fmaf(q2, xv.z, p[g][b]);
-          p[g][b] = fmaf(q3, xv.w, p[g][b]);
+        for (int b = 0; b < B; ++b) xv[b] = xs4(xs + b * a.xstride, xbase + 32 * g + 4 * j);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          const uint32_t w = v[k][g];
+          const float q0 = sbyte<0>(w), q1 = sbyte<1>(w), q2 = sbyte<2>(w), q3 = sbyte<3>(w);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            p[k][g][b] = fmaf(q0, xv[b].x, p[k][g][b]);
+            p[k][g][b] = fmaf(q1, xv[b].y, p[k][g][b]);
+            p[k][g][b] = fmaf(q2, xv[b].z, p[k][g][b]);
+            p[k][g][b] = fmaf(q3, xv[b].w, p[k][g][b]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float v = (dq * sc[0]) * p[0][b];
-      v = fmaf(dq * sc[1], p[1][b], v);
-      v = fmaf(dq * sc[2], p[2][b], v);
-      v = fmaf(dq * sc[3], p[3][b], v);
-      acc[b] += v;
+    for (int k = 0; k < R; ++k) {
+      const uint32_t s = r[k].s;
+      const uint32_t S0 = align_bytes(r[k].sc[1], r[k].sc[0], s) >> (8 * c);
+      const uint32_t S1 = align_bytes(r[k].sc[2], r[k].sc[1], s) >> (8 * c);
+      const float sc[4] = {sbyte<0>(S0), sbyte<2>(S0), sbyte<0>(S1), sbyte<2>(S1)};
+      const float dq = 0.25f * f16_lo(r[k].d);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float t = (dq * sc[0]) * p[k][0][b];
+        t = fmaf(dq * sc[1], p[k][1][b], t);
+        t = fmaf(dq * sc[2], p[k][2][b], t);
+        t = fmaf(dq * sc[3], p[k][3][b], t);
+        acc[k * B + b] += t;
+      }
     }
   }
 };
@@ -386,41 +449,52 @@ struct FmtI8Row {
   struct Raw { uint32_t q[16]; };
   struct Lane {};
   __device__ static Lane lane_state(int) { return {}; }
-  __device__ static bool valid(const GemvArgs&, int64_t) { return true; }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
 
-  __device__ __forceinline__ static void issue_n(const uint8_t* rp, int64_t u, int64_t in, Raw& r) {
+  __device__ __forceinline__ static void issue_n(const uint8_t* rp, int u, int64_t in, Raw& r) {
     const uint8_t* p = rp + u * 64;
+    // A half unit (the last of a row 32 mod 64 long) re-reads its own first
+    // half instead of the missing second half (loads stay branch-free) and
+    // zeroes it.
+    const bool full = 64 * u + 64 <= in;
+    const uint8_t* p2 = full ? p + 32 : p;
     const u32x4 v0 = load_u32x4_a16(p), v1 = load_u32x4_a16(p + 16);
-    u32x4 v2 = {0u, 0u, 0u, 0u}, v3 = {0u, 0u, 0u, 0u};
-    if (64 * u + 64 <= in) { v2 = load_u32x4_a16(p + 32); v3 = load_u32x4_a16(p + 48); }
+    u32x4 v2 = load_u32x4_a16(p2), v3 = load_u32x4_a16(p2 + 16);
+    if (!full) { v2 = u32x4{0u, 0u, 0u, 0u}; v3 = u32x4{0u, 0u, 0u, 0u}; }
     r.q[0] = v0.x; r.q[1] = v0.y; r.q[2] = v0.z; r.q[3] = v0.w;
     r.q[4] = v1.x; r.q[5] = v1.y; r.q[6] = v1.z; r.q[7] = v1.w;
     r.q[8] = v2.x; r.q[9] = v2.y; r.q[10] = v2.z; r.q[11] = v2.w;
     r.q[12] = v3.x; r.q[13] = v3.y; r.q[14] = v3.z; r.q[15] = v3.w;
   }
 
-  template <int B>
-  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw& r, int64_t u,
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
                                                  const float* xs, const float*, int64_t,
                                                  const Lane&, float* acc) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint32_t v = r.q[t];
-      const float q0 = sbyte<0>(v), q1 = sbyte<1>(v), q2 = sbyte<2>(v), q3 = sbyte<3>(v);
+      f32x4 xv[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const f32x4 xv = xs4(xs + b * a.xstride, 64 * u + 4 * t);
-        acc[b] = fmaf(q0, xv.x, acc[b]);
-        acc[b] = fmaf(q1, xv.y, acc[b]);
-        acc[b] = fmaf(q2, xv.z, acc[b]);
-        acc[b] = fmaf(q3, xv.w, acc[b]);
+      for (int b = 0; b < B; ++b) xv[b] = xs4(xs + b * a.xstride, 64 * u + 4 * t);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t v = r[k].q[t];
+        const float q0 = sbyte<0>(v), q1 = sbyte<1>(v), q2 = sbyte<2>(v), q3 = sbyte<3>(v);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float& s = acc[k * B + b];
+          s = fmaf(q0, xv[b].x, s);
+          s = fmaf(q1, xv[b].y, s);
+          s = fmaf(q2, xv[b].z, s);
+          s = fmaf(q3, xv[b].w, s);
+        }
       }
     }
   }
 };
 
 template <class F>
-__device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp, int64_t u,
+__device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp, int u,
                                            typename F::Raw& r) {
   if constexpr (std::is_same<F, FmtI8Row>::value) {
     F::issue_n(rp, u, a.in, r);
@@ -437,39 +511,74 @@ __device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp,
 // weights).  The per-32 sums reduce the 8 float4 of a sub-block, held by 8
 // consecutive lanes, with DPP.  One barrier follows.
 // ---------------------------------------------------------------------------
-template <bool kSums, int B, int XS>
-__device__ __forceinline__ void stage(const GemvArgs& a, float* xs, float* sums) {
-  const int n4 = static_cast<int>(a.xpad >> 2);   // float4 slots per batch row
+template <int B, int XS>
+struct XChunk {
+  f32x4 v[B][XS];
+};
+
+template <int B, int XS>
+__device__ __forceinline__ void stage_load(const GemvArgs& a, int base, XChunk<B, XS>& c) {
   const int in4 = static_cast<int>(a.in >> 2);
-  const int nsub = static_cast<int>(a.xpad >> 5);
   const int tid = static_cast<int>(threadIdx.x);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const f32x4* src = reinterpret_cast<const f32x4*>(a.x + b * a.in);
+#pragma unroll
+    for (int r = 0; r < XS; ++r) {
+      const int s = base + r * kThreads + tid;
+      const f32x4 t = src[s < in4 ? s : 0];   // branch-free: slot 0 stands in
+      c.v[b][r] = s < in4 ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+template <bool kSums, int B, int XS>
+__device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float* sums, int base,
+                                            const XChunk<B, XS>& c) {
+  const int n4 = static_cast<int>(a.xpad >> 2);   // float4 slots per batch row
+  const int nsub = static_cast<int>(a.xpad >> 5);
+  const int tid = static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
     float* dst = xs + b * a.xstride;
-    for (int base = 0; base < n4; base += XS * kThreads) {
-      f32x4 v[XS];
 #pragma unroll
-      for (int r = 0; r < XS; ++r) {
-        const int s = base + r * kThreads + tid;
-        v[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s < in4) v[r] = src[s];
-      }
-#pragma unroll
-      for (int r = 0; r < XS; ++r) {
-        const int s = base + r * kThreads + tid;
-        if (s < n4) *reinterpret_cast<f32x4*>(dst + xs_phys(4 * s)) = v[r];
-        if constexpr (kSums) {
-          float part = (v[r].x + v[r].y) + (v[r].z + v[r].w);
-          part += dpp<0xB1>(part);    // lane ^ 1
-          part += dpp<0x4E>(part);    // lane ^ 2
-          part += dpp<0x141>(part);   // lane i <-> 7 - i within 8
-          if ((tid & 7) == 0 && s < n4) sums[b * nsub + (s >> 3)] = part;
-        }
+    for (int r = 0; r < XS; ++r) {
+      const int s = base + r * kThreads + tid;
+      const f32x4 v = c.v[b][r];
+      if (s < n4) *reinterpret_cast<f32x4*>(dst + xs_phys(4 * s)) = v;
+      if constexpr (kSums) {
+        float part = (v.x + v.y) + (v.z + v.w);
+        part += dpp<0xB1>(part);    // lane ^ 1
+        part += dpp<0x4E>(part);    // lane ^ 2
+        part += dpp<0x141>(part);   // lane i <-> 7 - i within 8
+        if ((tid & 7) == 0 && s < n4) sums[b * nsub + (s >> 3)] = part;
       }
     }
   }
 }
+
+// Chunks after the first (rows longer than 1024, 2048 or 8192 weights for
+// XS = 1, 2, 8), one batch column at a time.
+template <bool kSums, int B, int XS>
+__device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* sums, int from) {
+  const int n4 = static_cast<int>(a.xpad >> 2);
+  for (int base = from; base < n4; base += XS * kThreads) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      GemvArgs ab = a;
+      ab.x = a.x + b * a.in;
+      XChunk<1, XS> c;
+      stage_load<1, XS>(ab, base, c);
+      stage_store<kSums, 1, XS>(ab, xs + b * a.xstride, sums + b * (a.xpad >> 5), base, c);
+    }
+  }
+}
+
+// Whether a kernel loads its first x chunk ahead of its weights: only when
+// the chunk is small (the registers it holds stay live across the weight
+// loads).
+template <int B, int XS>
+constexpr bool kEarlyX = XS <= 2 && XS * B <= 8;
 
 // ---------------------------------------------------------------------------
 // Grouped launch: up to kMaxGroup independent mat-vecs of one format (and
@@ -483,23 +592,31 @@ struct GroupArgs {
   int32_t n_ops;
 };
 
-// The kernel.  One workgroup = one tile of kRowsPerGroup rows of one op.
-// A lane serves units sub + L*j, j = 0 .. ipt-1, in lock step with its wave
-// (so the DPP reduction at the end sees a full wave).  When ipt <= U all of
-// a lane's units are loaded at once, before x is staged: one memory round
-// trip per launch.  Longer rows walk their units with the next unit's loads
-// issued before the current one is computed.
-template <class F, int L, int B, int U>
+// The kernel.  One workgroup = one tile of kRowsPerTile rows of one op.
+// A group of L lanes serves R rows, kRowsPerSlab apart, with one lane
+// layout: lane `sub` holds units sub + L*j, j = 0 .. ipt-1, of every one of
+// the R rows, so each x value it reads from LDS feeds R rows.  Lanes walk
+// in lock step with their wave (the DPP reduction at the end sees a full
+// wave).  When ipt <= U all of a lane's units are loaded at once, before x
+// is staged: one memory round trip per launch.  Longer rows (whole-wave
+// lane groups only) walk their units with the next unit's loads issued
+// before the current one is computed.  Rows past the op's end read the
+// tile's first row (in bounds) and are not stored.
+template <class F, int L, int B, int U, int R>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   extern __shared__ float lds[];
-  constexpr int XS = L == 16 ? 1 : (L == 32 ? 2 : 8);
+  constexpr int XS = L <= 16 ? 1 : (L == 32 ? 2 : 8);
   constexpr int kRowsPerWave = kWave / L;
-  constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;
+  constexpr int kRowsPerSlab = kWavesPerGroup * kRowsPerWave;
+  constexpr int kRowsPerTile = kRowsPerSlab * R;
+  static_assert(R == 1 || L < 64 || U == 1, "several rows per lane group need short rows");
 
   // blockIdx.y picks the op, so the op's arguments are read in one round
   // trip without first scanning the group.
   const GemvArgs a = g.op[blockIdx.y];
   const int64_t tile = blockIdx.x;
+  const int64_t first = tile * kRowsPerTile;
+  if (first >= a.out) return;   // this op has fewer tiles (uniform)
   float* xs = lds;
   float* sums = lds + B * a.xstride;
   const int64_t nsub = a.xpad / 32;
@@ -507,63 +624,90 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int sub = lane & (L - 1);
-  const int64_t row = tile * kRowsPerGroup + wave * kRowsPerWave + lane / L;
-  const int64_t ipt = (a.units + L - 1) / L;
+  const int rofs = wave * kRowsPerWave + lane / L;   // row within a slab
+  const int ipt = static_cast<int>((a.units + L - 1) / L);
   const typename F::Lane ls = F::lane_state(sub);
-  const bool row_live = row < a.out;
-  const uint8_t* rp = a.w + (row_live ? row : 0) * a.row_bytes;
+  // Row k of the lane sits rofs + k * kRowsPerSlab rows past the tile's
+  // first row; rows past the end read the first row instead.  Offsets
+  // within a tile fit 24 bits (at most 256 rows of at most 34816 bytes).
+  const uint8_t* tile_base = a.w + first * a.row_bytes;
+  const int64_t left = a.out - first;
+  const uint8_t* rp[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int r = rofs + k * kRowsPerSlab;
+    rp[k] = tile_base + (r < left ? __umul24(static_cast<uint32_t>(r),
+                                              static_cast<uint32_t>(a.row_bytes)) : 0u);
+  }
 
-  auto live = [&](int64_t jj) {
-    const int64_t u = sub + L * jj;
-    return row_live && u < a.units && F::valid(a, u);
+  auto live = [&](int jj) {
+    const int u = sub + L * jj;
+    return u < a.units && F::valid(a, u);
   };
 
-  float acc[B];
+  float acc[R * B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  for (int i = 0; i < R * B; ++i) acc[i] = 0.f;
 
   // Rows of up to L units (every launch with L < 64) always take the first
   // path; only whole-wave rows can be longer than U units.
+  // x is loaded before the weights: vector loads retire in order, so x can
+  // reach LDS (and the barrier pass) while the weights are still in flight.
+  constexpr bool kEarly = kEarlyX<B, XS>;
+  XChunk<kEarly ? B : 1, XS> xc;
+  if constexpr (kEarly) stage_load<B, XS>(a, 0, xc);
   if (L < 64 || ipt <= U) {
-    typename F::Raw r[U];
+    typename F::Raw r[U][R];
     bool have[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
+      // Every lane loads (lanes without a unit load unit 0 of their row, in
+      // bounds): branch-free loads keep the in-order load count exact, so
+      // the x stores below wait for x alone.
       have[j] = j < ipt && live(j);
-      if (have[j]) issue_unit<F>(a, rp, sub + L * j, r[j]);
+      const int uj = have[j] ? sub + L * j : 0;
+#pragma unroll
+      for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], uj, r[j][k]);
     }
-    if (tile * kRowsPerGroup >= a.out) return;   // this op has fewer tiles
-    stage<F::kSums, B, XS>(a, xs, sums);
+    if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
+    stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < U; ++j)
-      if (have[j]) F::template compute<B>(a, r[j], sub + L * j, xs, sums, nsub, ls, acc);
-  } else if constexpr (L == 64) {
-    typename F::Raw cur;
+      if (have[j]) F::template compute<B, R>(a, r[j], sub + L * j, xs, sums, nsub, ls, acc);
+  } else if constexpr (L == 64 && R == 1) {
+    typename F::Raw cur[1];
     bool have = live(0);
-    if (have) issue_unit<F>(a, rp, sub, cur);
-    if (tile * kRowsPerGroup >= a.out) return;   // this op has fewer tiles
-    stage<F::kSums, B, XS>(a, xs, sums);
+    issue_unit<F>(a, rp[0], have ? sub : 0, cur[0]);
+    if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
+    stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
-    for (int64_t j = 0; j < ipt; ++j) {
-      typename F::Raw nxt;
+    for (int j = 0; j < ipt; ++j) {
+      typename F::Raw nxt[1];
       bool have_n = false;
       if (j + 1 < ipt) {
         have_n = live(j + 1);
-        if (have_n) issue_unit<F>(a, rp, sub + L * (j + 1), nxt);
+        issue_unit<F>(a, rp[0], have_n ? sub + L * (j + 1) : 0, nxt[0]);
       }
-      if (have) F::template compute<B>(a, cur, sub + L * j, xs, sums, nsub, ls, acc);
-      cur = nxt;
+      if (have) F::template compute<B, 1>(a, cur, sub + L * j, xs, sums, nsub, ls, acc);
+      cur[0] = nxt[0];
       have = have_n;
     }
   }
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = group_sum<L>(acc[b]);
-  if (sub == 0 && row_live) {
-    const float bv = a.bias ? a.bias[row] : 0.f;
-    const float rs = a.scales ? a.scales[row] : 1.f;
+  for (int i = 0; i < R * B; ++i) acc[i] = group_sum<L>(acc[i]);
+  // Every lane of the group now holds all R * B sums; lane k of the group
+  // stores row k.
 #pragma unroll
-    for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[b], rs, bv);
+  for (int k = 0; k < R; ++k) {
+    const int r = rofs + k * kRowsPerSlab;
+    if (sub == k && r < left) {
+      const int64_t row = first + r;
+      const float bv = a.bias ? a.bias[row] : 0.f;
+      const float rs = a.scales ? a.scales[row] : 1.f;
+#pragma unroll
+      for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[k * B + b], rs, bv);
+    }
   }
 }
 
@@ -577,49 +721,70 @@ namespace pesti_gemv {
 using pesti::GemvArgs;
 using pesti::GroupArgs;
 
-template <class F, int L, int B, int U>
+template <class F, int L, int B, int U, int R>
 int launch_one(const GroupArgs& g, size_t lds_bytes, hipStream_t stream) {
-  constexpr int64_t kRowsPerGroup = pesti::kWavesPerGroup * (pesti::kWave / L);
+  constexpr int64_t kRowsPerTile = pesti::kWavesPerGroup * (pesti::kWave / L) * R;
   int64_t tiles = 0;
   for (int i = 0; i < g.n_ops; ++i) {
-    const int64_t t = (g.op[i].out + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t t = (g.op[i].out + kRowsPerTile - 1) / kRowsPerTile;
     if (t > tiles) tiles = t;
   }
   if (tiles <= 0) return PESTI_OK;
   GroupArgs args = g;
   void* params[] = {&args};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_kernel<F, L, B, U>),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_kernel<F, L, B, U, R>),
                                  dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(g.n_ops)),
                                  dim3(pesti::kThreads), params, lds_bytes, stream);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-template <class F, int L, int U>
+template <class F, int L, int U, int R>
 int launch_b(const GroupArgs& g, int batch, size_t lds, hipStream_t st) {
   switch (batch) {
-    case 1: return launch_one<F, L, 1, U>(g, lds, st);
-    case 2: return launch_one<F, L, 2, U>(g, lds, st);
-    case 3: return launch_one<F, L, 3, U>(g, lds, st);
-    case 4: return launch_one<F, L, 4, U>(g, lds, st);
-    case 5: return launch_one<F, L, 5, U>(g, lds, st);
-    case 6: return launch_one<F, L, 6, U>(g, lds, st);
-    case 7: return launch_one<F, L, 7, U>(g, lds, st);
-    case 8: return launch_one<F, L, 8, U>(g, lds, st);
+    case 1:
+      if constexpr (R == 1) return launch_one<F, L, 1, U, R>(g, lds, st);
+      return PESTI_ERR_BATCH;   // several rows per lane group serve batches of 2+
+    case 2: return launch_one<F, L, 2, U, R>(g, lds, st);
+    case 3: return launch_one<F, L, 3, U, R>(g, lds, st);
+    case 4: return launch_one<F, L, 4, U, R>(g, lds, st);
+    case 5: return launch_one<F, L, 5, U, R>(g, lds, st);
+    case 6: return launch_one<F, L, 6, U, R>(g, lds, st);
+    case 7: return launch_one<F, L, 7, U, R>(g, lds, st);
+    case 8: return launch_one<F, L, 8, U, R>(g, lds, st);
     default: return PESTI_ERR_BATCH;
   }
 }
 
-// (lanes per row L, units held per lane U) for the longest row of a launch:
-// rows of up to 16 / 32 units take 16 / 32 lanes and one unit per lane;
-// longer rows take a whole wave and hold 2 or 4 units per lane at once.
+// Rows per lane group for short rows: with two or more batch columns a
+// lane group serves 2 rows of a tall matrix (each x value read from LDS
+// feeds both, and the workgroup carries twice the bytes), as long as the
+// launch keeps at least kMinTiles workgroups.  With one batch column the
+// extra registers cost more occupancy than the sharing gains.
+#ifndef PESTI_MIN_TILES
+#define PESTI_MIN_TILES 2048
+#endif
+constexpr int64_t kMinTiles = PESTI_MIN_TILES;
+
+template <class F, int L>
+int launch_r(const GroupArgs& g, int64_t max_out, int batch, size_t lds, hipStream_t st) {
+  const int64_t tiles1 = (max_out + 4 * (64 / L) - 1) / (4 * (64 / L));
+  if (batch >= 2 && tiles1 >= 2 * kMinTiles) return launch_b<F, L, 1, 2>(g, batch, lds, st);
+  return launch_b<F, L, 1, 1>(g, batch, lds, st);
+}
+
+// (lanes per row L, units held per lane U, rows per lane group R) for the
+// longest row of a launch: rows of up to 16 / 32 units take 16 / 32 lanes
+// and one unit per lane; longer rows take a whole wave and hold 2 or 4
+// units per lane at once.
 template <class F>
-int launch_lu(const GroupArgs& g, int64_t max_units, int batch, size_t lds, hipStream_t st) {
-  if (max_units <= 16) return launch_b<F, 16, 1>(g, batch, lds, st);
-  if (max_units <= 32) return launch_b<F, 32, 1>(g, batch, lds, st);
+int launch_lu(const GroupArgs& g, int64_t max_units, int64_t max_out, int batch, size_t lds,
+              hipStream_t st) {
+  if (max_units <= 16) return launch_r<F, 16>(g, max_out, batch, lds, st);
+  if (max_units <= 32) return launch_r<F, 32>(g, max_out, batch, lds, st);
   const int64_t ipt = (max_units + 63) / 64;
-  if (ipt <= 1) return launch_b<F, 64, 1>(g, batch, lds, st);
-  if (ipt <= 2) return launch_b<F, 64, 2>(g, batch, lds, st);
-  return launch_b<F, 64, 4>(g, batch, lds, st);
+  if (ipt <= 1) return launch_b<F, 64, 1, 1>(g, batch, lds, st);
+  if (ipt <= 2) return launch_b<F, 64, 2, 1>(g, batch, lds, st);
+  return launch_b<F, 64, 4, 1>(g, batch, lds, st);
 }
 
 
@@ -641,6 +806,10 @@ template <> inline void shape_of<pesti::FmtQ6_K>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtI8Row>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = in; *u = (in + 63) / 64;
 }
+
+// y[b][o] = bias[o] (or 0) for every op of `g` and b < batch (ops with
+// in_features == 0); defined in gemv.hip.
+int fill_bias(const GroupArgs& g, int batch, hipStream_t stream);
 
 // Validate one op; returns PESTI_OK, an error, or 1 for "empty, skip".
 template <class F>
@@ -676,12 +845,23 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
   const int st = pesti_host::current_device(&dev, &lds_limit);
   if (st != PESTI_OK) return st;
 
-  GroupArgs g{};
-  int64_t max_units = 0;
+  // Ops with no columns only write their bias (or zeros); the mat-vec
+  // kernel assumes every row has at least one unit.
+  GroupArgs g{}, fill{};
+  int n_mv = 0;
+  int64_t max_units = 0, max_out = 0;
   size_t row_lds = 0;
   for (int i = 0; i < n_live; ++i) {
     const pesti_gemv_op& o = ops[live[i]];
-    GemvArgs& a = g.op[i];
+    if (o.in_features == 0) {
+      GemvArgs& f = fill.op[fill.n_ops++];
+      f.y = o.y;
+      f.bias = o.bias;
+      f.out = o.out_features;
+      continue;
+    }
+    live[n_mv] = live[i];
+    GemvArgs& a = g.op[n_mv++];
     a.w = static_cast<const uint8_t*>(o.w);
     a.scales = o.row_scales;
     a.bias = o.bias;
@@ -694,21 +874,27 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     const size_t r = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
     if (r > row_lds) row_lds = r;
     if (a.units > max_units) max_units = a.units;
+    if (a.out > max_out) max_out = a.out;
   }
-  g.n_ops = n_live;
+  g.n_ops = n_mv;
+  hipStream_t stream_h = static_cast<hipStream_t>(stream);
+  if (fill.n_ops > 0) {
+    const int r = fill_bias(fill, batch, stream_h);
+    if (r != PESTI_OK) return r;
+  }
+  if (n_mv == 0) return PESTI_OK;
   const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
-  hipStream_t stream_h = static_cast<hipStream_t>(stream);
   for (int b0 = 0; b0 < batch; b0 += per_launch) {
     const int nb = batch - b0 < per_launch ? batch - b0 : per_launch;
     GroupArgs c = g;
-    for (int i = 0; i < n_live; ++i) {
+    for (int i = 0; i < n_mv; ++i) {
       const pesti_gemv_op& o = ops[live[i]];
       c.op[i].x = o.x ? o.x + static_cast<int64_t>(b0) * o.in_features : nullptr;
       c.op[i].y = o.y + static_cast<int64_t>(b0) * o.out_features;
     }
     const size_t lds = row_lds * nb;
-    const int r = launch_lu<F>(c, max_units, nb, lds, stream_h);
+    const int r = launch_lu<F>(c, max_units, max_out, nb, lds, stream_h);
     if (r != PESTI_OK) return r;
   }
   return PESTI_OK;

@@ -316,3 +316,44 @@ def test_group_equals_single_calls_bitwise():
     torch.cuda.synchronize()
     for (o, _, _, _, yg, _, _), (_, _, _, _, ys, _) in zip(ops, singles):
         assert torch.equal(yg, ys)
+
+
+# ---------------------------------------------------------------------------
+# tall matrices: launches where a lane group serves 2 or 4 rows, with a
+# ragged last tile, checked on every row
+# ---------------------------------------------------------------------------
+TALL = [("q8_0", 65536 + 37, 64, 1), ("q8_0", 131072 + 53, 64, 3), ("q8_0", 131072 + 11, 96, 1),
+        ("q4_k", 65536 + 37, 256, 2), ("q4_k", 131072 + 53, 896, 1), ("q4_k", 65536 + 29, 1280, 1),
+        ("q6_k", 65536 + 37, 256, 1), ("q6_k", 131072 + 53, 256, 8), ("q6_k", 65536 + 5, 1280, 1),
+        ("i8row", 131072 + 53, 64, 1), ("i8row", 65536 + 37, 160, 4)]
+
+
+@pytest.mark.parametrize("fmt,out,inf,batch", TALL)
+def test_tall_matrix_every_row(fmt, out, inf, batch):
+    packed, scales, x, bias = make(fmt, out, inf, 70, batch)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall {fmt} {out}x{inf} b{batch}")
+
+
+def test_group_with_tall_op_equals_single_calls_bitwise():
+    """The tallest op of a group sets the rows per lane group for all of
+    them; small ops then run with several rows per lane group, yet every op
+    gives the same bits as its own single call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for i, (out, inf) in enumerate([(131072 + 53, 896), (896, 896), (37, 896), (4864, 896)]):
+        packed, _, x, bias = make("q4_k", out, inf, 80 + i, 1)
+        w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yg = torch.empty(out, dtype=torch.float32, device="cuda")
+        ys = torch.empty(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        singles.append((out, inf, w_d, x_d, ys, b_d))
+    dmv.pesti_gemv_group("q4_k", ops, 1)
+    for out, inf, w_d, x_d, ys, b_d in singles:
+        dmv.pesti_gemv_q4_k(out, inf, w_d, x_d, ys, b_d, 1)
+    torch.cuda.synchronize()
+    for (o, _, _, _, yg, _, _), (_, _, _, _, ys, _) in zip(ops, singles):
+        assert torch.equal(yg, ys), o
