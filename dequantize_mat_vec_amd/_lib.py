@@ -71,6 +71,12 @@ def load(path: os.PathLike | None = None) -> ctypes.CDLL:
     if not p.exists():
         raise ImportError(f"{p} is missing: build the HIP library first "
                           "(python -m dequantize_mat_vec_amd.build)")
+    # PyTorch's HIP runtime goes in first.  The library asks for the
+    # runtime by its soname (libamdhip64.so.7), which then resolves to the
+    # copy PyTorch already loaded; loaded the other way round, PyTorch
+    # would bring in a second runtime, and pointers and streams would not
+    # cross between the two.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(str(p))
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -5,12 +5,9 @@
 // float32 accumulation.
 //
 // For m >= 16 the product is a dense contraction and runs on the matrix
-// cores (v_mfma_f32_16x16x32_f16): a workgroup owns 16 output columns and up
-// to 64 rows of X; its 4 wavefronts split K four ways, each streaming its
-// slice of the 16 W rows once and reusing it for every 16-row tile of X;
-// the four partial tiles are summed through LDS.  Below 16 rows the matrix
-// cores would idle most of their rows, so a vector-ALU kernel treats the
-// rows of X as a batch of mat-vecs over binary16 weights.
+// cores (v_mfma_f32_16x16x32_f16); below 16 rows the matrix cores would
+// idle most of their rows, so a vector-ALU kernel treats the rows of X as a
+// batch of mat-vecs over binary16 weights.
 #include "common.h"
 
 namespace pesti {
@@ -26,130 +23,193 @@ struct GemmArgs {
   int64_t m, n, k;
 };
 
-constexpr int kGemmRowsPerGroup = 64;   // rows of X per workgroup (4 MFMA tiles)
-
+// MFMA path (m >= 16).  A workgroup of NW wavefronts owns 16 output
+// columns (16 rows of W) and up to 16 * MT rows of X; its wavefronts split K
+// into NW contiguous slices, so even a narrow layer (N = 768) runs
+// 48 * NW wavefronts per 16 * MT rows of X.  Each wavefront streams its
+// slice C k-steps (32 weights each) at a time with two register buffers:
+// the loads of the next C steps are in flight while the current ones feed
+// the matrix cores.  Every load is unconditional (k-steps past the slice,
+// rows past N or M read in-bounds stand-ins whose W operand is zeroed), so
+// the in-order load count stays exact.  The NW partial tiles are summed in
+// a fixed order through LDS, so results do not depend on timing.
+//
 // Operand layout of v_mfma_f32_16x16x32_f16 for lane l (i = l % 16,
 // kg = l / 16): A row i, k = 8kg..8kg+7; B column i, the same k; C column i,
 // rows 4kg..4kg+3.  Only the pairing of A and B k-slots matters for the sum,
 // so both read the same 8 consecutive k of their row.
-__global__ __launch_bounds__(256) void gemm_f16_mfma_kernel(GemmArgs a) {
-  __shared__ floatx4 part[kWavesPerGroup][4][kWave];   // per wave: 4 row tiles
+constexpr int kGemmC = 2;   // k-steps per buffer
+
+template <int NW, int MT, int C>
+struct GemmBuf {
+  half8 w[C];
+  half8 x[C][MT];
+};
+
+template <int NW, int MT, int C>
+__global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
+  __shared__ floatx4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kGemmRowsPerGroup;
-  const int64_t ksteps = a.k / 32;
-  const int64_t per_wave = (ksteps + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t s_begin = wave * per_wave;
-  const int64_t s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
-  const int64_t mtiles = (a.m - m0 + 15) / 16 < 4 ? (a.m - m0 + 15) / 16 : 4;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+  const int ksteps = static_cast<int>(a.k / 32);
+  const int per_wave = (ksteps + NW - 1) / NW;
+  const int s_begin = wave * per_wave;
+  const int s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
 
-  floatx4 acc[4];
+  const int64_t wn = n0 + i < a.n ? n0 + i : a.n - 1;
+  const uint16_t* wrow = a.w + wn * a.k + 8 * kg;
+  const uint16_t* xrow[MT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t wn = n0 + i;
-  const bool wvalid = wn < a.n;
-  const uint16_t* wrow = a.w + (wvalid ? wn : 0) * a.k + 8 * kg;
-  for (int64_t s = s_begin; s < s_end; ++s) {
-    half8 bv = {};
-    if (wvalid) bv = *reinterpret_cast<const half8*>(wrow + 32 * s);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < mtiles) {
-        const int64_t xm = m0 + 16 * t + i;
-        half8 av = {};
-        if (xm < a.m) av = *reinterpret_cast<const half8*>(a.x + xm * a.k + 32 * s + 8 * kg);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[t], 0, 0, 0);
-      }
-    }
+  for (int t = 0; t < MT; ++t) {
+    const int64_t xm = m0 + 16 * t + i < a.m ? m0 + 16 * t + i : a.m - 1;
+    xrow[t] = a.x + xm * a.k + 8 * kg;
   }
+
+  auto load = [&](int s, GemmBuf<NW, MT, C>& b) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) part[wave][t][lane] = acc[t];
+    for (int c = 0; c < C; ++c) {
+      const int sc = s + c < s_end ? s + c : (s_begin < ksteps ? s_begin : 0);
+      b.w[c] = *reinterpret_cast<const half8*>(wrow + 32 * sc);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const half8*>(xrow[t] + 32 * sc);
+    }
+  };
+  floatx4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int s, const GemmBuf<NW, MT, C>& b) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const half8 wv = s + c < s_end ? b.w[c] : half8{};
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, acc[t], 0, 0, 0);
+    }
+  };
+
+  GemmBuf<NW, MT, C> ba, bb;
+  load(s_begin, ba);
+  for (int s = s_begin; s < s_end; s += 2 * C) {
+    load(s + C, bb);
+    mma(s, ba);
+    if (s + C >= s_end) break;
+    load(s + 2 * C, ba);
+    mma(s + C, bb);
+  }
+
+#pragma unroll
+  for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
-  // wave w finishes row tile w: sum the four K-slices, add bias, store.
-  const int t = wave;
-  if (t < mtiles) {
-    floatx4 r = part[0][t][lane];
+  // Thread e sums entry e (tile e / 64, lane e % 64) over the NW slices in
+  // slice order, adds the bias and stores its four values.
+  for (int e = threadIdx.x; e < MT * kWave; e += NW * kWave) {
+    const int t = e / kWave, l = e % kWave;
+    floatx4 r = part[0][t][l];
 #pragma unroll
-    for (int w = 1; w < kWavesPerGroup; ++w) {
-      const floatx4 p = part[w][t][lane];
+    for (int w = 1; w < NW; ++w) {
+      const floatx4 p = part[w][t][l];
       r.x += p.x; r.y += p.y; r.z += p.z; r.w += p.w;
     }
-    const int64_t col = n0 + i;
+    const int64_t col = n0 + (l & 15);
     if (col < a.n) {
       const float bv = a.bias ? a.bias[col] : 0.f;
       const float v[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + 16 * t + 4 * kg + q;
+        const int64_t row = m0 + 16 * t + 4 * (l >> 4) + q;
         if (row < a.m) a.y[row * a.n + col] = v[q] + bv;
       }
     }
   }
 }
 
-// Vector-ALU path for m < 16: every W row is read once and applied to all
-// rows of X (staged in LDS as float32).  L lanes per W row, 32 weights
-// (64 bytes) per unit.
-template <int L, int B>
-__global__ __launch_bounds__(kThreads) void gemm_f16_valu_kernel(GemmArgs a, int64_t xstride) {
-  extern __shared__ float xs[];
-  const int64_t kpad = ((a.k + 63) / 64) * 64;
-  for (int b = 0; b < B; ++b) {
-    for (int64_t i = threadIdx.x; i < kpad; i += kThreads) {
-      float v = 0.f;
-      if (i < a.k) v = static_cast<float>(__builtin_bit_cast(_Float16, a.x[b * a.k + i]));
-      xs[b * xstride + xs_phys(i)] = v;
-    }
-  }
-  __syncthreads();
+// y[r][c] = bias[c] (or 0): the K = 0 case.
+__global__ __launch_bounds__(256) void gemm_bias_fill_kernel(GemmArgs a) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= a.m * a.n) return;
+  a.y[e] = a.bias ? a.bias[e % a.n] : 0.f;
+}
+
+// Vector-ALU path for m < 16: the rows of X are a batch of B <= 8 columns
+// applied to every W row, which is read once.  L lanes per W row, a unit
+// is 32 weights (64 bytes); a lane loads up to U units of its row at once
+// (longer rows take several such rounds).  X stays binary16 in LDS and
+// v_dot2_f32_f16 multiplies two weight/activation pairs per instruction
+// into a float32 sum (the products of two binary16 values are exact in
+// float32).  Rows past N and lanes past the row end load in-bounds
+// stand-ins that are dropped, keeping every load unconditional.
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+
+// LDS position (in halves) of x element i: 8 halves of padding every 128.
+__device__ __forceinline__ int xh_phys(int i) { return i + 8 * (i >> 7); }
+__host__ __device__ constexpr int64_t xh_stride(int64_t k) { return ((k + 127) / 128) * 136; }
+
+template <int L, int U, int B>
+__global__ __launch_bounds__(kThreads) void gemm_f16_valu_kernel(GemmArgs a) {
+  extern __shared__ uint16_t xh[];
+  constexpr int kRowsPerWave = kWave / L;
+  constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane & (L - 1);
-  const int grp = lane / L;
-  constexpr int kRowsPerWave = kWave / L;
-  constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;
-  const int64_t units = a.k / 32;
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerGroup; r0 < a.n;
-       r0 += static_cast<int64_t>(gridDim.x) * kRowsPerGroup) {
-    const int64_t row = r0 + wave * kRowsPerWave + grp;
-    float acc[B];
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerGroup + wave * kRowsPerWave + lane / L;
+  const int units = static_cast<int>(a.k / 32);
+  const int stride = static_cast<int>(xh_stride(a.k));
+  const uint16_t* wr = a.w + (row < a.n ? row : a.n - 1) * a.k;
+
+  float acc[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
-    if (row < a.n) {
-      const uint16_t* wr = a.w + row * a.k;
-      for (int64_t u = sub; u < units; u += L) {
-        const uint16_t* p = wr + 32 * u;
-        u32x4 v[4];
+  for (int b = 0; b < B; ++b) acc[b] = 0.f;
+  for (int j0 = 0; j0 * L < units; j0 += U) {
+    u32x4 wv[U][4];
+    bool have[U];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = load_u32x4_a16(p + 8 * c);
+    for (int j = 0; j < U; ++j) {
+      const int u = sub + L * (j0 + j);
+      have[j] = u < units;
+      const uint16_t* p = wr + 32 * (have[j] ? u : 0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t d4[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+      for (int c = 0; c < 4; ++c) wv[j][c] = load_u32x4_a16(p + 8 * c);
+    }
+    if (j0 == 0) {
+      // X (B rows of K halves) into LDS, 16 bytes per thread and step.
+      const int chunks = B * (units * 4);
+      for (int e = threadIdx.x; e < chunks; e += kThreads) {
+        const int b = e / (units * 4), q = e % (units * 4);
+        const u32x4 v = load_u32x4_a16(a.x + b * a.k + 8 * q);
+        *reinterpret_cast<u32x4*>(xh + b * stride + xh_phys(8 * q)) = v;
+      }
+      __syncthreads();
+    }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float w0 = f16_lo(d4[e]), w1 = f16_hi(d4[e]);
-            const int64_t kk = 32 * u + 8 * c + 2 * e;
+    for (int j = 0; j < U; ++j) {
+      if (!have[j]) continue;
+      const int u = sub + L * (j0 + j);
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-              const float* xb = xs + b * xstride;
-              acc[b] = fmaf(w0, xb[xs_phys(kk)], acc[b]);
-              acc[b] = fmaf(w1, xb[xs_phys(kk + 1)], acc[b]);
-            }
-          }
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w4[4] = {wv[j][c].x, wv[j][c].y, wv[j][c].z, wv[j][c].w};
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xh + b * stride + xh_phys(32 * u + 8 * c));
+          const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, w4[e]),
+                                            __builtin_bit_cast(half2, x4[e]), acc[b], false);
         }
       }
     }
+  }
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = group_sum<L>(acc[b]);
-    if (sub == 0 && row < a.n) {
-      const float bv = a.bias ? a.bias[row] : 0.f;
+  for (int b = 0; b < B; ++b) acc[b] = group_sum<L>(acc[b]);
+  if (sub == 0 && row < a.n) {
+    const float bv = a.bias ? a.bias[row] : 0.f;
 #pragma unroll
-      for (int b = 0; b < B; ++b) a.y[b * a.n + row] = acc[b] + bv;
-    }
+    for (int b = 0; b < B; ++b) a.y[b * a.n + row] = acc[b] + bv;
   }
 }
 
@@ -159,34 +219,54 @@ namespace {
 
 using pesti::GemmArgs;
 
-template <int L, int B>
+template <int L, int U, int B>
 int launch_valu(const GemmArgs& a, hipStream_t st) {
   constexpr int kRowsPerGroup = pesti::kWavesPerGroup * (pesti::kWave / L);
-  const int64_t xstride = pesti::xs_stride(a.k, 64);
-  const size_t lds = sizeof(float) * xstride * B;
+  const size_t lds = sizeof(uint16_t) * pesti::xh_stride(a.k) * B;
   const int64_t tiles = (a.n + kRowsPerGroup - 1) / kRowsPerGroup;
   GemmArgs args = a;
-  int64_t xs = xstride;
-  void* params[] = {&args, &xs};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_f16_valu_kernel<L, B>),
-                                 dim3(pesti_host::grid_for(tiles, 8192)), dim3(pesti::kThreads), params,
-                                 lds, st);
+  void* params[] = {&args};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_f16_valu_kernel<L, U, B>),
+                                 dim3(static_cast<unsigned>(tiles)), dim3(pesti::kThreads), params, lds, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-template <int L>
+template <int L, int U>
 int launch_valu_b(const GemmArgs& a, int b, hipStream_t st) {
   switch (b) {
-    case 1: return launch_valu<L, 1>(a, st);
-    case 2: return launch_valu<L, 2>(a, st);
-    case 3: return launch_valu<L, 3>(a, st);
-    case 4: return launch_valu<L, 4>(a, st);
-    case 5: return launch_valu<L, 5>(a, st);
-    case 6: return launch_valu<L, 6>(a, st);
-    case 7: return launch_valu<L, 7>(a, st);
-    case 8: return launch_valu<L, 8>(a, st);
+    case 1: return launch_valu<L, U, 1>(a, st);
+    case 2: return launch_valu<L, U, 2>(a, st);
+    case 3: return launch_valu<L, U, 3>(a, st);
+    case 4: return launch_valu<L, U, 4>(a, st);
+    case 5: return launch_valu<L, U, 5>(a, st);
+    case 6: return launch_valu<L, U, 6>(a, st);
+    case 7: return launch_valu<L, U, 7>(a, st);
+    case 8: return launch_valu<L, U, 8>(a, st);
     default: return PESTI_ERR_BATCH;
   }
+}
+
+template <int NW, int MT>
+int launch_mfma_t(const GemmArgs& a, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
+  GemmArgs args = a;
+  void* params[] = {&args};
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC>), grid,
+      dim3(NW * 64), params, 0, st);
+  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
+// Launch shape by how many 16-column tiles the layer has: narrow layers
+// (under 96 tiles, e.g. N = 768) give every 16-row tile of X its own
+// workgroup of 8 K slices, so that enough workgroups stream W; wider ones
+// let a workgroup of 16 K slices reuse each W load for 2 or 4 tiles of X.
+int launch_mfma(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
+  if (tiles_n < 96) return launch_mfma_t<8, 1>(a, st);
+  if (tiles_m <= 1) return launch_mfma_t<16, 1>(a, st);
+  if (tiles_m <= 2) return launch_mfma_t<16, 2>(a, st);
+  return launch_mfma_t<16, 4>(a, st);
 }
 
 }  // namespace
@@ -208,29 +288,32 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
   if (st != PESTI_OK) return st;
   hipStream_t sh = static_cast<hipStream_t>(stream);
   GemmArgs a{w, x, y, bias, m, out_features, in_features};
-  if (m >= 16) {
-    dim3 grid(static_cast<unsigned>((out_features + 15) / 16),
-              static_cast<unsigned>((m + pesti::kGemmRowsPerGroup - 1) / pesti::kGemmRowsPerGroup));
+  if (in_features == 0) {
     void* params[] = {&a};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel), grid,
-                                   dim3(256), params, 0, sh);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_bias_fill_kernel),
+                                         dim3(static_cast<unsigned>((m * out_features + 255) / 256)),
+                                         dim3(256), params, 0, sh);
     return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
   }
-  // m < 16: rows of X in chunks of up to 8 as a batch of binary16 mat-vecs
-  const size_t row_lds = sizeof(float) * pesti::xs_stride(in_features, 64);
+  if (m >= 16) return launch_mfma(a, sh);
+  // m < 16: rows of X in chunks of up to 8 as a batch of binary16 mat-vecs;
+  // 32 lanes per W row holding up to 4 units each (rows of up to 4096
+  // weights in one round), 64 lanes and several rounds beyond that.
+  const size_t row_lds = sizeof(uint16_t) * pesti::xh_stride(in_features);
   int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, 8);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
   const int64_t units = in_features / 32;
   for (int64_t r0 = 0; r0 < m; r0 += per_launch) {
     const int nb = static_cast<int>(m - r0 < per_launch ? m - r0 : per_launch);
     GemmArgs c = a;
-    c.x = x ? x + r0 * in_features : nullptr;
+    c.x = x + r0 * in_features;
     c.y = y + r0 * out_features;
     c.m = nb;
     int r;
-    if (units <= 16) r = launch_valu_b<16>(c, nb, sh);
-    else if (units <= 32) r = launch_valu_b<32>(c, nb, sh);
-    else r = launch_valu_b<64>(c, nb, sh);
+    if (units <= 32) r = launch_valu_b<32, 1>(c, nb, sh);
+    else if (units <= 64) r = launch_valu_b<32, 2>(c, nb, sh);
+    else if (units <= 128) r = launch_valu_b<32, 4>(c, nb, sh);
+    else r = launch_valu_b<64, 4>(c, nb, sh);
     if (r != PESTI_OK) return r;
   }
   return PESTI_OK;

@@ -162,3 +162,23 @@ def test_group_struct_layout_matches_header():
     assert ctypes.sizeof(_lib.GemvOp) == 56
     m = re.search(r"#define PESTI_MAX_GROUP (\d+)", text)
     assert int(m.group(1)) == _lib.MAX_GROUP
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before anything else imports torch still leaves a
+    single HIP runtime mapped (the library binds to PyTorch's copy)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from dequantize_mat_vec_amd import _lib\n"
+        "_lib.load()\n"
+        "import torch\n"
+        "paths = set()\n"
+        "for line in open('/proc/self/maps'):\n"
+        "    p = line.split()[-1]\n"
+        "    if 'libamdhip64' in p: paths.add(p)\n"
+        "print(len(paths), sorted(paths))\n" % str(HEADER.parent.parent))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.split()[0] == "1", out.stdout
