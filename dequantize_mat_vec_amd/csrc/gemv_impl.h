@@ -649,14 +649,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
   for (int i = 0; i < R * B; ++i) acc[i] = 0.f;
 
-  // Rows of up to L units (every launch with L < 64) always take the first
-  // path; only whole-wave rows can be longer than U units.
   // x is loaded before the weights: vector loads retire in order, so x can
   // reach LDS (and the barrier pass) while the weights are still in flight.
   constexpr bool kEarly = kEarlyX<B, XS>;
   XChunk<kEarly ? B : 1, XS> xc;
   if constexpr (kEarly) stage_load<B, XS>(a, 0, xc);
-  if (L < 64 || ipt <= U) {
+  // A lane's unit j (j < ipt): sub + L*j when it exists, else unit 0 of the
+  // same row as an in-bounds stand-in (loads stay branch-free).
+  auto unit = [&](int j) { return (j < ipt && live(j)) ? sub + L * j : 0; };
+  if (ipt <= U) {
+    // All of a lane's units are loaded at once.
     typename F::Raw r[U][R];
     bool have[U];
 #pragma unroll
@@ -665,9 +667,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
       // bounds): branch-free loads keep the in-order load count exact, so
       // the x stores below wait for x alone.
       have[j] = j < ipt && live(j);
-      const int uj = have[j] ? sub + L * j : 0;
 #pragma unroll
-      for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], uj, r[j][k]);
+      for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), r[j][k]);
     }
     if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
     stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
@@ -675,23 +676,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
       if (have[j]) F::template compute<B, R>(a, r[j], sub + L * j, xs, sums, nsub, ls, acc);
-  } else if constexpr (L == 64 && R == 1) {
-    typename F::Raw cur[1];
-    bool have = live(0);
-    issue_unit<F>(a, rp[0], have ? sub : 0, cur[0]);
+  } else if constexpr (R == 1 && L == 64) {
+    // Rows longer than U units (whole-wave lane groups only: 16 and 32
+    // lanes per row always hold all units at once): the lane walks its
+    // units with two register buffers, the
+    // next unit's loads in flight while the current one is decoded.  One
+    // stand-in load past the last unit keeps the loop branch-free.
+    typename F::Raw ra[1], rb[1];
+    issue_unit<F>(a, rp[0], unit(0), ra[0]);
     if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
     stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
-    for (int j = 0; j < ipt; ++j) {
-      typename F::Raw nxt[1];
-      bool have_n = false;
-      if (j + 1 < ipt) {
-        have_n = live(j + 1);
-        issue_unit<F>(a, rp[0], have_n ? sub + L * (j + 1) : 0, nxt[0]);
-      }
-      if (have) F::template compute<B, 1>(a, cur, sub + L * j, xs, sums, nsub, ls, acc);
-      cur[0] = nxt[0];
-      have = have_n;
+    for (int j = 0; j < ipt; j += 2) {
+      issue_unit<F>(a, rp[0], unit(j + 1), rb[0]);
+      if (live(j)) F::template compute<B, 1>(a, ra, sub + L * j, xs, sums, nsub, ls, acc);
+      if (j + 1 >= ipt) break;
+      issue_unit<F>(a, rp[0], unit(j + 2), ra[0]);
+      if (live(j + 1)) F::template compute<B, 1>(a, rb, sub + L * (j + 1), xs, sums, nsub, ls, acc);
     }
   }
 #pragma unroll

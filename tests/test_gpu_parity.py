@@ -94,6 +94,17 @@ def test_gemv_large_in_batch_split(fmt):
     assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} in=16384 b8")
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("inf,batch", [(20480, 1), (32768, 3), (16416, 2)])
+def test_gemv_rows_longer_than_one_load_round(fmt, inf, batch):
+    """Rows of more than 256 units: whole-wave lane groups walk their units
+    with two register buffers (odd and even unit counts per lane)."""
+    packed, scales, x, bias = make(fmt, 9, inf, 5, batch)
+    y = run_gemv(fmt, packed, scales, 9, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, 9, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} in={inf} b{batch}")
+
+
 # ---------------------------------------------------------------------------
 # invariants and edge cases
 # ---------------------------------------------------------------------------
