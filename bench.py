@@ -71,19 +71,24 @@ def parse_args(argv=None):
 # workload
 # ---------------------------------------------------------------------------
 def build_inputs(copies):
+    """Step inputs.  Each weight copy is one contiguous device buffer holding
+    the step's tensors in the order they are used (Q, K, V, O, gate, up,
+    down per layer, then the LM head), each at a 256-byte boundary, as a
+    mapped model file would lay them out; weights[c][i] is a view of call
+    i's tensor in copy c."""
     import numpy as np
     import torch
     from dequantize_mat_vec_amd import synth
     dev = torch.device("cuda:0")
     calls = synth.decode_step_calls()
-    weights = [[] for _ in range(copies)]
+    packs, offsets, total = [], [], 0
     xs, ys, biases = [], [], []
     for layer, name, fmt, out, inf, has_bias in calls:
         tidx = synth.TENSOR_INDEX[name]
         packed = synth.quant_blocks(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), out, inf)
-        host = torch.from_numpy(packed.reshape(-1))
-        for c in range(copies):
-            weights[c].append(host.to(dev))
+        packs.append(packed.reshape(-1))
+        offsets.append(total)
+        total += -(-packed.size // 256) * 256
         x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
         xs.append(torch.from_numpy(x).to(dev))
         ys.append(torch.empty(out, dtype=torch.float32, device=dev))
@@ -92,6 +97,14 @@ def build_inputs(copies):
             biases.append(torch.from_numpy(b).to(dev))
         else:
             biases.append(None)
+    host = np.zeros(total, dtype=np.uint8)
+    for off, p in zip(offsets, packs):
+        host[off:off + p.size] = p
+    host_t = torch.from_numpy(host)
+    weights = []
+    for _ in range(copies):
+        buf = host_t.to(dev)
+        weights.append([buf[off:off + p.size] for off, p in zip(offsets, packs)])
     torch.cuda.synchronize()
     return calls, weights, xs, ys, biases
 
