@@ -182,7 +182,12 @@ def suite_cases():
     from dequantize_mat_vec_amd import synth
     cases = [("i8row 896x896 b1", "gemv", ("i8row", 896, 896, 1)),
              ("q4_k 4864x896 b1 (gate/up)", "gemv", ("q4_k", 4864, 896, 1)),
-             ("q4_k 896x4864 b1 (down)", "gemv", ("q4_k", 896, 4864, 1))]
+             ("q4_k 896x4864 b1 (down)", "gemv", ("q4_k", 896, 4864, 1)),
+             # sustained rate at the FFN shapes: 8 independent matrices (each
+             # with its own x and y) in one grouped launch
+             ("q4_k 4864x896 b1 (gate/up) x8 grouped", "group", ("q4_k", 4864, 896, 8)),
+             ("q4_k 896x4864 b1 (down) x8 grouped", "group", ("q4_k", 896, 4864, 8)),
+             ("q8_0 4864x896 b1 x8 grouped", "group", ("q8_0", 4864, 896, 8))]
     for m in (8, 32, 64):
         for name, k, n in synth.GPT2_LINEARS:
             cases.append((f"f16 gemm {name} m{m} ({k}->{n})", "gemm", (m, k, n)))
@@ -209,7 +214,18 @@ def run_suite(lib, args):
         if args.suite_filter and args.suite_filter not in name:
             continue
         rng = synth.rng_for(4 if "lm-head" in name else (0 if kind == "gemv" and prm[0] == "i8row" else 1), idx, 0)
-        if kind == "gemv":
+        nops = 1
+        if kind == "group":
+            fmt, out, inf, nops = prm
+            batch = 1
+            packed, scales = synth.matrix(fmt, rng, out, inf)
+            packed = np.concatenate([packed.reshape(-1)] * nops)
+            nbytes = packed.size
+            xg = [torch.from_numpy(synth.activations(rng, 1, inf)).to(dev) for _ in range(nops)]
+            yg = [torch.empty(out, dtype=torch.float32, device=dev) for _ in range(nops)]
+            algo = nops * call_bytes(fmt, out, inf, 1, False)
+            flops = 2.0 * out * inf * nops
+        elif kind == "gemv":
             fmt, out, inf, batch = prm
             packed, scales = synth.matrix(fmt, rng, out, inf)
             nbytes = packed.size
@@ -232,9 +248,21 @@ def run_suite(lib, args):
         host = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
         ws = [host.to(dev) for _ in range(copies)]
         reps = int(min(max(copies, 40), 400))
+        if kind == "group":
+            per = nbytes // nops
+            tables = []
+            for w in ws:
+                arr = (_lib.GemvOp * nops)()
+                for k in range(nops):
+                    arr[k] = _lib.GemvOp(out, inf, w.data_ptr() + k * per, None, xg[k].data_ptr(),
+                                         yg[k].data_ptr(), None)
+                tables.append(arr)
 
         def launch(i, sh):
-            if kind == "gemv":
+            if kind == "group":
+                st = lib.pesti_gemv_group(_lib.FORMAT_IDS[fmt], nops,
+                                          ctypes.cast(tables[i % copies], ctypes.c_void_p), 1, sh)
+            elif kind == "gemv":
                 st = (lib.pesti_gemv_i8row(out, inf, ws[i % copies].data_ptr(), sc.data_ptr(),
                                            x.data_ptr(), y.data_ptr(), None, batch, sh)
                       if fmt == "i8row" else
