@@ -574,11 +574,13 @@ __device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* 
   }
 }
 
-// Whether a kernel loads its first x chunk ahead of its weights: only when
-// the chunk is small (the registers it holds stay live across the weight
-// loads).
+// Whether a kernel loads its first x chunk ahead of its weights: when the
+// chunk is small (the registers it holds stay live across the weight
+// loads), and always at batch 1, where even a whole-wave row's 8 float4
+// per thread pay for themselves (the down projection of a decode step is
+// short, so x's L2 round trip otherwise adds to every launch).
 template <int B, int XS>
-constexpr bool kEarlyX = XS <= 2 && XS * B <= 8;
+constexpr bool kEarlyX = (XS <= 2 && XS * B <= 8) || B == 1;
 
 // ---------------------------------------------------------------------------
 // Grouped launch: up to kMaxGroup independent mat-vecs of one format (and

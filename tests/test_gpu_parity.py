@@ -95,6 +95,18 @@ def test_gemv_large_in_batch_split(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("out,inf,batch", [(37, 4160, 1), (37, 4352, 3), (5, 4864, 1), (130, 12288, 2),
+                                           (2, 16384, 8)])
+def test_gemv_rows_split_across_wavefronts(fmt, out, inf, batch):
+    """Long rows of short matrices: each row's units are split over 2 or 4
+    wavefronts (unit counts that do not divide evenly, ragged tiles)."""
+    packed, scales, x, bias = make(fmt, out, inf, 6, batch)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} {out}x{inf} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("inf,batch", [(20480, 1), (32768, 3), (16416, 2)])
 def test_gemv_rows_longer_than_one_load_round(fmt, inf, batch):
     """Rows of more than 256 units: whole-wave lane groups walk their units
