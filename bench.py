@@ -175,6 +175,7 @@ def kernel_name(fmt, infs, outs):
 # Suite: the other workloads, one call shape at a time
 # ---------------------------------------------------------------------------
 MFMA_F16_PEAK_TFLOPS = 2500.0
+SUITE_REPLAYS = 10   # graph replays per suite case (median, p10, p90 of their per-call times)
 
 
 def suite_cases():
@@ -201,8 +202,10 @@ def suite_cases():
 def run_suite(lib, args):
     """Each case: enough weight copies to pass 640 MB (so the 256 MB
     last-level cache holds none between uses), a HIP graph of `reps`
-    launches cycling over them, timed between two events; µs per call =
-    graph time / reps."""
+    launches cycling over them, timed between two events over 10 replays;
+    µs per call = graph time / reps (median, p10, p90 over replays).  The
+    same copies are then read by the library's streaming-read hook: the
+    size-matched read ceiling the case is compared with."""
     import ctypes
     import numpy as np
     import torch
@@ -274,33 +277,55 @@ def run_suite(lib, args):
             if st != 0:
                 raise RuntimeError(f"{name}: status {st}")
 
-        with torch.cuda.stream(stream):
-            launch(0, stream.cuda_stream)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(reps):
-                    launch(i, torch.cuda.current_stream().cuda_stream)
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            best = None
-            for _ in range(3):
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
+        def timed(fn_launch):
+            """Per-call µs of `reps` launches captured in one graph, over
+            SUITE_REPLAYS replays: (median, p10, p90)."""
+            with torch.cuda.stream(stream):
+                fn_launch(0, stream.cuda_stream)
                 torch.cuda.synchronize()
-                t = e0.elapsed_time(e1) * 1e3 / reps
-                best = t if best is None else min(best, t)
-        gbs = algo / best / 1e3
-        rec = {"case": name, "us_per_call": round(best, 3), "GB/s": round(gbs, 1),
-               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(flops / best / 1e6, 3),
-               "algorithmic_bytes": int(algo), "weight_copies": copies}
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(reps):
+                        fn_launch(i, torch.cuda.current_stream().cuda_stream)
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                per = []
+                for _ in range(SUITE_REPLAYS):
+                    e0.record(stream)
+                    g.replay()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    per.append(e0.elapsed_time(e1) * 1e3 / reps)
+            del g
+            q = np.percentile(per, [50, 10, 90])
+            return float(q[0]), float(q[1]), float(q[2])
+
+        med, p10, p90 = timed(launch)
+        # Size-matched streaming-read ceiling: the same stored bytes, read from
+        # the same rotating copies by a plain vector-load kernel.
+        partial = torch.empty(_lib.READ_GROUPS, dtype=torch.int32, device=dev)
+        rbytes = nbytes - nbytes % 16
+
+        def read_launch(i, sh):
+            st = lib.pesti_stream_read(ws[i % copies].data_ptr(), rbytes, partial.data_ptr(), sh)
+            if st != 0:
+                raise RuntimeError(f"stream read: status {st}")
+
+        read_us = timed(read_launch)[0]
+        gbs = algo / med / 1e3
+        rec = {"case": name, "us_per_call": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
+               "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+               "TFLOP/s": round(flops / med / 1e6, 3), "algorithmic_bytes": int(algo),
+               "stored_bytes": int(nbytes), "read_ceiling_GB/s": round(rbytes / read_us / 1e3, 1),
+               "stored_GB/s": round(nbytes / med / 1e3, 1),
+               "frac_of_read_ceiling": round(read_us * nbytes / rbytes / med, 4) if rbytes else None,
+               "weight_copies": copies}
         if kind == "gemm":
-            rec["mfma_frac"] = round(flops / best / 1e6 / MFMA_F16_PEAK_TFLOPS, 5)
+            rec["mfma_frac"] = round(flops / med / 1e6 / MFMA_F16_PEAK_TFLOPS, 5)
         print(json.dumps(rec), flush=True)
         out_lines.append(rec)
-        del ws, g
+        del ws
         torch.cuda.empty_cache()
     return out_lines
 
@@ -381,54 +406,80 @@ def dominant_traffic(kernel_label):
 # CPU baseline: the oracle on a bounded sample of the same step
 # ---------------------------------------------------------------------------
 def cpu_leg(seconds):
-    """Runs in a child process with one BLAS/OpenMP thread: times the
-    oracle (float64 dequantize + dot) on whole calls of the step, layer by
-    layer, then on LM-head row slices, until `seconds` of work is done."""
-    import numpy as np
+    """Runs in a child process (BLAS/OpenMP threads set by the parent): times
+    the oracle (float64 dequantize + dot) on whole calls of the step in
+    stream order (the LM head as a 16384-row slice), passing over the step
+    again until `seconds` of work is done."""
     from dequantize_mat_vec_amd import synth
     import oracle
     calls = synth.decode_step_calls()
-    done_bytes, spent, ncalls = 0, 0.0, 0
-    sample = []
-    for layer, name, fmt, out, inf, has_bias in calls:
-        if spent >= seconds:
-            break
-        tidx = synth.TENSOR_INDEX[name]
-        rng = synth.rng_for(CONFIG_INDEX, layer, tidx)
-        if name == "lm_head":
-            rows = min(out, 16384)
+    done_bytes, spent, ncalls, passes = 0, 0.0, 0, 0
+    first = last = None
+    while spent < seconds:
+        passes += 1
+        for layer, name, fmt, out, inf, has_bias in calls:
+            if spent >= seconds:
+                break
+            tidx = synth.TENSOR_INDEX[name]
+            rng = synth.rng_for(CONFIG_INDEX, layer, tidx)
+            rows = min(out, 16384) if name == "lm_head" else out
             packed = synth.quant_blocks(fmt, rng, rows, inf)
-        else:
-            rows = out
-            packed = synth.quant_blocks(fmt, rng, out, inf)
-        x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
-        b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
-        t0 = time.perf_counter()
-        oracle.gemv_packed(fmt, packed, rows, inf, x, b)
-        spent += time.perf_counter() - t0
-        done_bytes += call_bytes(fmt, rows, inf, 1, has_bias)
-        ncalls += 1
-        sample.append(f"{name}{layer}" if name != "lm_head" else f"lm_head[{rows} rows]")
-    gbs = done_bytes / spent / 1e9
-    return {"value": gbs, "seconds": spent, "bytes": done_bytes, "calls": ncalls,
-            "first": sample[0], "last": sample[-1]}
+            x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
+            b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
+            t0 = time.perf_counter()
+            oracle.gemv_packed(fmt, packed, rows, inf, x, b)
+            spent += time.perf_counter() - t0
+            done_bytes += call_bytes(fmt, rows, inf, 1, has_bias)
+            ncalls += 1
+            last = f"{name}{layer}" if name != "lm_head" else f"lm_head[{rows} rows]"
+            first = first or last
+    return {"value": done_bytes / spent / 1e9, "seconds": spent, "bytes": done_bytes,
+            "calls": ncalls, "passes": passes, "first": first, "last": last}
 
 
-def run_cpu_baseline(seconds):
+def host_cpu():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def run_cpu_leg(seconds, threads):
     env = dict(os.environ)
     for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
-        env[k] = "1"
+        env[k] = str(threads)
     env["HIP_VISIBLE_DEVICES"] = ""
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg",
            "--cpu-sample-seconds", str(seconds)]
-    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
     if res.returncode != 0:
         raise RuntimeError(f"cpu baseline failed: {res.stderr[-2000:]}")
-    r = json.loads(res.stdout.strip().splitlines()[-1])
-    return {"value": round(r["value"], 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"float64 oracle, 1 thread, {r['calls']} calls of the decode step in "
-                       f"stream order ({r['first']} .. {r['last']}), {r['bytes']} nominal bytes "
-                       f"in {r['seconds']:.1f} s")}
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+def run_cpu_baseline(seconds):
+    """The oracle on the host cores, twice: one BLAS/OpenMP thread (the
+    reported value) and the process's whole CPU share (OMP_NUM_THREADS if
+    set, else the affinity mask)."""
+    host = host_cpu()
+    share = int(os.environ.get("OMP_NUM_THREADS") or host["affinity"])
+    one = run_cpu_leg(seconds, 1)
+    many = run_cpu_leg(seconds / 2, share)
+
+    def sample(r, threads):
+        return (f"float64 oracle, {threads} thread(s), {r['calls']} calls of the decode step in "
+                f"stream order ({r['first']} .. {r['last']}, {r['passes']} pass(es)), "
+                f"{r['bytes']} nominal bytes in {r['seconds']:.1f} s")
+    return {"value": round(one["value"], 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": sample(one, 1), "host": host,
+            "all_cores": {"value": round(many["value"], 4), "unit": "GB/s", "cores": share,
+                          "sample": sample(many, share)}}
 
 
 # ---------------------------------------------------------------------------

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
+    "pesti_stream_read": (_c_int, [_vp, _i64, _vp, _vp]),
     "pesti_row_bytes": (_i64, [_i32, _i64]),
     "pesti_strerror": (_c_char_p, [_c_int]),
     "pesti_abi_version": (_i32, []),
@@ -179,6 +180,16 @@ def pesti_gemv_group(fmt, ops, batch=1, stream=None):
         arr, n = gemv_ops(ops), len(ops)
     return _check("pesti_gemv_group", load().pesti_gemv_group(
         fid, n, ctypes.cast(arr, ctypes.c_void_p), batch, _stream(stream)))
+
+
+READ_GROUPS = 4096
+
+
+def pesti_stream_read(buf, nbytes, partial, stream=None):
+    """Streaming read of `nbytes` bytes of `buf` (measurement hook); each of
+    READ_GROUPS workgroups writes the XOR of what it read to `partial`."""
+    return _check("pesti_stream_read", load().pesti_stream_read(_ptr(buf), nbytes, _ptr(partial),
+                                                                _stream(stream)))
 
 
 def _dequant(name, rows, in_features, blocks, w_out, stream):

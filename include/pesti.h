@@ -156,6 +156,16 @@ int pesti_dequant_q6_k(int64_t rows, int64_t in_features, const void* blocks,
 int pesti_dequant_i8row(int64_t rows, int64_t in_features, const int8_t* codes,
                         const float* row_scales, float* w_out, void* stream);
 
+/* --- measurement hook ----------------------------------------------------
+ * A plain streaming read of `bytes` bytes (a multiple of 16) at `buf`
+ * (16-byte aligned): the streaming-read ceiling that a mat-vec reading the
+ * same number of bytes is measured against.  PESTI_READ_GROUPS workgroups
+ * each write the XOR of the dwords they read to partial[group] (the XOR of
+ * all entries is the XOR of the whole buffer); `partial` is a device array
+ * of PESTI_READ_GROUPS uint32 owned by the caller. */
+#define PESTI_READ_GROUPS 4096
+int pesti_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* stream);
+
 /* --- host-only helpers (no device work) --------------------------------- */
 
 /* Packed bytes per row for a PESTI_FMT_* format (code bytes only for

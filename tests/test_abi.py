@@ -182,3 +182,16 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.split()[0] == "1", out.stdout
+
+
+def test_stream_read_argument_checks():
+    lib = _raw()
+    part = FAKE + 0x1000
+    assert lib.pesti_stream_read(FAKE, 20, part, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_stream_read(FAKE, -16, part, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_stream_read(FAKE, 64, None, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_stream_read(None, 64, part, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_stream_read(FAKE + 4, 64, part, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_stream_read(FAKE, 64, part + 2, None) == _lib.PESTI_ERR_ALIGN
+    m = re.search(r"#define PESTI_READ_GROUPS (\d+)", HEADER.read_text())
+    assert int(m.group(1)) == _lib.READ_GROUPS

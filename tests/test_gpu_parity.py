@@ -387,3 +387,20 @@ def test_group_with_tall_op_equals_single_calls_bitwise():
     torch.cuda.synchronize()
     for (o, _, _, _, yg, _, _), (_, _, _, _, ys, _) in zip(ops, singles):
         assert torch.equal(yg, ys), o
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096, 1 << 20, (1 << 22) * 4 + 48, 80 << 20])
+def test_stream_read_xor(nbytes):
+    """The streaming-read hook reads every byte once: the XOR of its
+    per-workgroup results is the XOR of the buffer's dwords."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from dequantize_mat_vec_amd import _lib
+    rng = np.random.default_rng([21, nbytes])
+    host = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda")
+    partial = torch.full((_lib.READ_GROUPS,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    dmv.pesti_stream_read(buf, nbytes, partial)
+    got = np.bitwise_xor.reduce(partial.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host) if host.size else np.uint32(0)
+    assert int(got) == int(want)
