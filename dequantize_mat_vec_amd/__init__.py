@@ -1,7 +1,7 @@
 """MI355X (gfx950) fused dequantize + mat-vec for block-quantized weights.
 
 y = W x + b with W in Q8_0, Q4_K, Q6_K or per-row int8 and x, y in float32,
-plus a small-M binary16 linear layer, all as hand-written HIP kernels behind
+plus small-M linear layers on binary16 X (binary16 or quantized W), all as hand-written HIP kernels behind
 the C ABI of include/pesti.h.  This package is the thin Python binding
 (argument marshalling only) and the seeded synthetic-input generator.
 """
@@ -11,9 +11,9 @@ from ._lib import (FORMAT_IDS, LIB_PATH, PESTI_ERR_ALIGN, PESTI_ERR_BATCH,  # no
                    pesti_dequant_i8row, pesti_dequant_q4_k, pesti_dequant_q6_k,
                    pesti_dequant_q8_0, pesti_gemm_f16_smallm, pesti_gemv_group, pesti_gemv_i8row,
                    pesti_gemv_q4_k, pesti_gemv_q6_k, pesti_gemv_q8_0, pesti_row_bytes,
-                   pesti_stream_read,
+                   pesti_stream_read, pesti_gemm_q8_0_smallm, pesti_gemm_q4_k_smallm, gemm_quant,
                    strerror)
 
 __all__ = [n for n in dir() if n.startswith("pesti_")] + [
-    "PestiError", "GemvOp", "MAX_GROUP", "gemv", "gemv_ops", "dequant", "load", "strerror",
+    "PestiError", "GemvOp", "MAX_GROUP", "gemv", "gemv_ops", "gemm_quant", "dequant", "load", "strerror",
     "FORMAT_IDS", "LIB_PATH"]

@@ -35,6 +35,8 @@ _SIGNATURES = {
     "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_group": (_c_int, [_i32, _i32, _vp, _i32, _vp]),
     "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q8_0_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q4_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -161,6 +163,21 @@ def pesti_gemm_f16_smallm(m, out_features, in_features, w, x, y, bias=None, stre
         m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias), _stream(stream)))
 
 
+def _gemm_q(name, m, out_features, in_features, blocks, x, y, bias, stream):
+    return _check(name, getattr(load(), name)(m, out_features, in_features, _ptr(blocks), _ptr(x),
+                                              _ptr(y), _ptr(bias), _stream(stream)))
+
+
+def pesti_gemm_q8_0_smallm(m, out_features, in_features, blocks, x, y, bias=None, stream=None):
+    return _gemm_q("pesti_gemm_q8_0_smallm", m, out_features, in_features, blocks, x, y, bias,
+                   stream)
+
+
+def pesti_gemm_q4_k_smallm(m, out_features, in_features, blocks, x, y, bias=None, stream=None):
+    return _gemm_q("pesti_gemm_q4_k_smallm", m, out_features, in_features, blocks, x, y, bias,
+                   stream)
+
+
 def gemv_ops(ops):
     """ctypes array of pesti_gemv_op from (out, in, w, x, y, bias, row_scales)
     tuples whose pointer fields are tensors, ints or None."""
@@ -220,6 +237,13 @@ def gemv(fmt, out_features, in_features, w, x, y, bias=None, batch=1, scales=Non
     if fmt == "i8row":
         return pesti_gemv_i8row(out_features, in_features, w, scales, x, y, bias, batch, stream)
     return _gemv(f"pesti_gemv_{fmt}", out_features, in_features, w, x, y, bias, batch, stream)
+
+
+def gemm_quant(fmt, m, out_features, in_features, blocks, x, y, bias=None, stream=None):
+    """Dispatch Y = X W^T + b (binary16 X, packed W) to the entry point of
+    format `fmt` (q8_0 or q4_k)."""
+    return _gemm_q(f"pesti_gemm_{fmt}_smallm", m, out_features, in_features, blocks, x, y, bias,
+                   stream)
 
 
 def dequant(fmt, rows, in_features, w, w_out, scales=None, stream=None):

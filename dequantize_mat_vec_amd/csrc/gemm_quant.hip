@@ -1,0 +1,323 @@
+// Small-M prefill GEMM with block-quantized weights: Y = X W^T + b with W in
+// Q8_0 or Q4_K (packed rows, the layouts of the mat-vec), X binary16 [m][K],
+// Y float32 [m][N].  This is the prompt-width case of the decode step's
+// linear layer ("inferno" README, "Benchmarks": linear = x @ w + b at prompt
+// width; "Bottlenecks are the big prompt-width GEMMs") with the weights kept
+// in the quantized form of the mat-vec ("Project scaffold ...", quant.rs:
+// the fused dequantize + mat-vec that never expands W to float32).
+//
+// The product runs on the matrix cores on exact operands.  Every code is an
+// integer that binary16 represents exactly (Q8_0 int8 through a float32 and
+// a round-to-zero pack; Q4_K nibbles through v_cvt_scalef32_pk_f16_fp8 of
+// the nibble read as an e4m3 byte, exactly q * 2^-9), and X is binary16, so
+// every product is exact in the float32 accumulator of
+// v_mfma_f32_16x16x32_f16.  One MFMA k-step is one 32-weight sub-block
+// (a Q8_0 block, a Q4_K sub-block), so its scales are applied to the
+// step's 16x16 partial tile in float32: acc += (d * sc) * sum(q x), and for
+// Q4_K acc -= (dmin * m) * sum(x), sum(x) coming from a second MFMA against
+// a tile of ones.
+//
+// Work split as in the binary16 GEMM: a workgroup owns 16 output columns
+// (16 rows of W) and 16 * MT rows of X, its NW wavefronts take contiguous
+// slices of K, each streamed one pair of k-steps ahead with two register
+// buffers (branch-free loads; steps past the slice read in-bounds
+// stand-ins and are skipped), and the partial tiles are summed in a
+// fixed order through LDS.
+//
+// MFMA operand layout, lane l (i = l % 16, kg = l / 16): A = X row i,
+// k = 8kg..8kg+7; B = W row i (output column i), the same k; C = column i,
+// rows 4kg..4kg+3.
+#include "common.h"
+
+namespace pesti {
+
+typedef _Float16 qhalf8 __attribute__((ext_vector_type(8)));
+typedef _Float16 qhalf2 __attribute__((ext_vector_type(2)));
+typedef float qfloat4 __attribute__((ext_vector_type(4)));
+
+struct QGemmArgs {
+  const uint8_t* w;    // packed rows of W [N]
+  const uint16_t* x;   // [M][K] binary16
+  float* y;            // [M][N]
+  const float* bias;   // [N] or null
+  int64_t m, n, k;
+  int64_t row_bytes;
+};
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0: k-step s = block s of the row (34 bytes: binary16 d, 32 int8).  A
+// lane's 8 codes start at byte 2 + 8kg of the block, 2 bytes off a dword
+// boundary in every other block; the lane reads the two dwords that start
+// at or before them and, when misaligned, the 16 bits that follow (else an
+// in-bounds re-read), never a byte outside the block, and realigns them.
+// ---------------------------------------------------------------------------
+struct QPolQ8_0 {
+  static constexpr bool kMin = false;
+  struct Step { uint32_t c[3]; uint32_t d; uint32_t s; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* blk = row + 34 * s;
+    const uint8_t* p = blk + 2 + 8 * kg;
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);   // 0 or 2
+    const uint8_t* pa = p - mis;
+    st.c[0] = load_u32(pa);
+    st.c[1] = load_u32(pa + 4);
+    st.c[2] = load_u16(pa + (mis ? 8 : 4));
+    st.d = load_u16(blk);
+    st.s = mis;
+  }
+
+  __device__ __forceinline__ static qhalf8 codes(const Step& st) {
+    const uint32_t lo = align_bytes(st.c[1], st.c[0], st.s);
+    const uint32_t hi = align_bytes(st.c[2], st.c[1], st.s);
+    uint32_t h[4];
+    h[0] = pack_f16(sbyte<0>(lo), sbyte<1>(lo));
+    h[1] = pack_f16(sbyte<2>(lo), sbyte<3>(lo));
+    h[2] = pack_f16(sbyte<0>(hi), sbyte<1>(hi));
+    h[3] = pack_f16(sbyte<2>(hi), sbyte<3>(hi));
+    return __builtin_bit_cast(qhalf8, h);
+  }
+
+  __device__ __forceinline__ static void scales(const Step& st, float& ds, float& dm) {
+    ds = f16_lo(st.d);
+    dm = 0.f;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Q4_K: k-step s = sub-block j = s % 8 of super-block s / 8 (144 bytes:
+// d, dmin, 12 bytes of 6-bit scales/mins, 128 code bytes).  Sub-blocks 2g
+// and 2g+1 are the low and high nibbles of code bytes 32g..32g+31; a lane's
+// 8 codes are bytes 32g + 8kg..+7 (8-byte aligned: rows are whole 144-byte
+// super-blocks).
+// ---------------------------------------------------------------------------
+struct QPolQ4_K {
+  static constexpr bool kMin = true;
+  struct Step { uint32_t c[2]; u32x4 hdr; uint32_t j; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* sb = row + 144 * (s >> 3);
+    const int j = s & 7;
+    const uint8_t* p = sb + 16 + 32 * (j >> 1) + 8 * kg;
+    st.c[0] = load_u32(p);
+    st.c[1] = load_u32(p + 4);
+    st.hdr = load_u32x4_a16(sb);
+    st.j = static_cast<uint32_t>(j);
+  }
+
+  __device__ __forceinline__ static qhalf8 codes(const Step& st) {
+    const uint32_t sh = 4u * (st.j & 1u);   // high nibbles for odd sub-blocks
+    const uint32_t a = (st.c[0] >> sh) & 0x0F0F0F0Fu;
+    const uint32_t b = (st.c[1] >> sh) & 0x0F0F0F0Fu;
+    // A nibble in an otherwise zero e4m3 byte is q * 2^-9; scale 1.
+    uint32_t h[4];
+    h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false));
+    h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true));
+    h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
+    h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true));
+    return __builtin_bit_cast(qhalf8, h);
+  }
+
+  // d * sc * 2^9 (undoing the 2^-9 of the code conversion) and dmin * m of
+  // sub-block j.  Sub-blocks 0..3: sc = S[j] & 63, m = S[j+4] & 63; 4..7
+  // (t = j - 4): sc = (S[j+4] & 15) | (S[t] >> 6) << 4, m = (S[j+4] >> 4)
+  // | (S[j] >> 6) << 4, where S[0..11] are header bytes 4..15.
+  __device__ __forceinline__ static void scales(const Step& st, float& ds, float& dm) {
+    const uint32_t j = st.j;
+    const uint32_t t = j & 3u;
+    const uint32_t y = st.hdr.y, z = st.hdr.z, w = st.hdr.w;
+    const uint32_t sy = (y >> (8 * t)) & 0xFFu, sz = (z >> (8 * t)) & 0xFFu, sw = (w >> (8 * t)) & 0xFFu;
+    uint32_t sc, mn;
+    if (j < 4) {
+      sc = sy & 63u;
+      mn = sz & 63u;
+    } else {
+      sc = (sw & 15u) | ((sy >> 6) << 4);
+      mn = (sw >> 4) | ((sz >> 6) << 4);
+    }
+    const float d = f16_lo(st.hdr.x), dmin = f16_hi(st.hdr.x);
+    ds = d * 512.0f * static_cast<float>(sc);
+    dm = dmin * static_cast<float>(mn);
+  }
+};
+
+template <class Q, int MT>
+struct QBuf {
+  typename Q::Step w[2];
+  qhalf8 x[2][MT];
+};
+
+template <class Q, int NW, int MT>
+__global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
+  __shared__ qfloat4 part[NW][MT][kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int i = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+  const int ksteps = static_cast<int>(a.k / 32);
+  // Slices of whole k-step pairs.
+  const int pairs = (ksteps + 1) / 2;
+  const int per_wave = 2 * ((pairs + NW - 1) / NW);
+  const int s_begin = wave * per_wave;
+  const int s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
+
+  const int64_t wn = n0 + i < a.n ? n0 + i : a.n - 1;
+  const uint8_t* wrow = a.w + wn * a.row_bytes;
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t xm = m0 + 16 * t + i < a.m ? m0 + 16 * t + i : a.m - 1;
+    xrow[t] = a.x + xm * a.k + 8 * kg;
+  }
+
+  auto load = [&](int s, QBuf<Q, MT>& b) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int sc = s + c < s_end ? s + c : (s_begin < ksteps ? s_begin : 0);
+      Q::load(wrow, sc, kg, b.w[c]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const qhalf8*>(xrow[t] + 32 * sc);
+    }
+  };
+  qfloat4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = qfloat4{0.f, 0.f, 0.f, 0.f};
+  const qhalf8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  auto mma = [&](int s, const QBuf<Q, MT>& b) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (s + c >= s_end) continue;   // wave-uniform
+      float ds, dm;
+      Q::scales(b.w[c], ds, dm);
+      const qhalf8 wv = Q::codes(b.w[c]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, qfloat4{0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0);
+        acc[t] += ds * p;
+        if constexpr (Q::kMin) {
+          const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
+                                                                    qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc[t] -= dm * sx;
+        }
+      }
+    }
+  };
+
+  QBuf<Q, MT> ba, bb;
+  load(s_begin, ba);
+  for (int s = s_begin; s < s_end; s += 4) {
+    load(s + 2, bb);
+    mma(s, ba);
+    if (s + 2 >= s_end) break;
+    load(s + 4, ba);
+    mma(s + 2, bb);
+  }
+
+#pragma unroll
+  for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int e = threadIdx.x; e < MT * kWave; e += NW * kWave) {
+    const int t = e / kWave, l = e % kWave;
+    qfloat4 r = part[0][t][l];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r += part[w][t][l];
+    const int64_t col = n0 + (l & 15);
+    if (col < a.n) {
+      const float bv = a.bias ? a.bias[col] : 0.f;
+      const float v[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = m0 + 16 * t + 4 * (l >> 4) + q;
+        if (row < a.m) a.y[row * a.n + col] = v[q] + bv;
+      }
+    }
+  }
+}
+
+// y[r][c] = bias[c] (or 0): the K = 0 case.
+__global__ __launch_bounds__(256) void gemm_quant_bias_kernel(QGemmArgs a) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= a.m * a.n) return;
+  a.y[e] = a.bias ? a.bias[e % a.n] : 0.f;
+}
+
+}  // namespace pesti
+
+namespace {
+
+using pesti::QGemmArgs;
+
+template <class Q, int NW, int MT>
+int launch_q(const QGemmArgs& a, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
+  QGemmArgs args = a;
+  void* params[] = {&args};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT>),
+                                       grid, dim3(NW * 64), params, 0, st);
+  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
+// Launch shape as for the binary16 GEMM: narrow layers give every 16-row
+// tile of X its own workgroup of 8 K slices; wider ones share each W load
+// across 2 or 4 row tiles in workgroups of 16 K slices.
+template <class Q>
+int launch_quant(const QGemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
+  if (tiles_n < 96) return launch_q<Q, 8, 1>(a, st);
+  if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, st);
+  if (tiles_m <= 2) return launch_q<Q, 16, 2>(a, st);
+  return launch_q<Q, 16, 4>(a, st);
+}
+
+template <class Q>
+int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+               const uint16_t* x, float* y, const float* bias, int64_t row_bytes, void* stream) {
+  if (out_features < 0 || in_features < 0) return PESTI_ERR_SHAPE;
+  if (m < 0 || m > PESTI_MAX_GEMM_M) return PESTI_ERR_BATCH;
+  if (m == 0 || out_features == 0) return PESTI_OK;
+  if (in_features % 32 != 0 || in_features > PESTI_MAX_IN_FEATURES) return PESTI_ERR_SHAPE;
+  if (!y || (in_features > 0 && (!blocks || !x))) return PESTI_ERR_NULL;
+  if (!pesti_host::aligned(y, 16) || (blocks && !pesti_host::aligned(blocks, 16)) ||
+      (x && !pesti_host::aligned(x, 16)) || (bias && !pesti_host::aligned(bias, 4)))
+    return PESTI_ERR_ALIGN;
+  int dev = 0;
+  size_t lds_limit = 0;
+  const int st = pesti_host::current_device(&dev, &lds_limit);
+  (void)lds_limit;
+  if (st != PESTI_OK) return st;
+  hipStream_t sh = static_cast<hipStream_t>(stream);
+  QGemmArgs a{static_cast<const uint8_t*>(blocks), x, y, bias, m, out_features, in_features, row_bytes};
+  if (in_features == 0) {
+    void* params[] = {&a};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_quant_bias_kernel),
+                                         dim3(static_cast<unsigned>((m * out_features + 255) / 256)),
+                                         dim3(256), params, 0, sh);
+    return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+  }
+  return launch_quant<Q>(a, sh);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ8_0>(m, out_features, in_features, blocks, x, y, bias,
+                                     (in_features / 32) * 34, stream);
+}
+
+int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
+                                     ((in_features + 255) / 256) * 144, stream);
+}
+
+}  // extern "C"

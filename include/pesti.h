@@ -143,6 +143,25 @@ int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
                           const uint16_t* w, const uint16_t* x, float* y,
                           const float* bias, void* stream);
 
+/* --- small-M linear layer on quantized weights, Y = X W^T + b -------------
+ * The prompt-width product of the same layer ("inferno" README,
+ * "Benchmarks": x @ w + b at prompt width) with W kept in the block format
+ * of the mat-vec ("Project scaffold ...", quant.rs: dequantize fused into
+ * the product, W never expanded).  blocks: out_features packed rows exactly
+ * as for pesti_gemv_q8_0 / pesti_gemv_q4_k; X binary16 [m][in] (16-byte
+ * aligned), Y float32 [m][out], bias float32 [out] or NULL; m in [0,
+ * PESTI_MAX_GEMM_M].  The matrix cores multiply the exact integer codes by
+ * X (every product exact in float32) one 32-weight block or sub-block at a
+ * time, and the block scales are applied to each partial sum in float32.
+ * Any m >= 1 works; for m <= 8 the batched mat-vec on float32 X is the
+ * faster call.  Errors as for pesti_gemm_f16_smallm. */
+int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
+int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
+
 /* --- dequantization to float32 (bit-exact; checks the unpacking) --------
  * w_out float32 [rows][in_features]: each weight rounded once from its
  * exact value (all formats here dequantize exactly in float32 except the

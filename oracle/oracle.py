@@ -258,6 +258,16 @@ def gemm_f16(x16, w16, bias=None):
     return gemv(w64, x64, bias)
 
 
+def gemm_packed(fmt: str, packed, rows: int, in_features: int, x16, bias=None):
+    """Small-M linear layer Y = X W^T + b at prompt width ("inferno" README,
+    "Benchmarks") with W in a block format ("Project scaffold ...", quant.rs:
+    the weights stay quantized): binary16 X [M, K], packed W [N rows].  The
+    exact float64 weights times the exact float64 X - the same product as
+    the mat-vec, with every row of X one batch row."""
+    x64 = np.atleast_2d(np.asarray(x16, dtype=np.float16)).astype(np.float64)
+    return gemv_packed(fmt, packed, rows, in_features, x64, bias)
+
+
 def within_tolerance(y_test, y_ref, s_ref, rel: float, abs_: float = 1e-6) -> np.ndarray:
     """Elementwise |y_test - y_ref| <= rel * s_ref + abs_ (s_ref from gemv)."""
     return np.abs(np.asarray(y_test, dtype=np.float64) - y_ref) <= rel * s_ref + abs_

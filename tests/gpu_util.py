@@ -94,3 +94,16 @@ def assert_within(y, y_ref, s_ref, rel, what=""):
                            f"err {err[tuple(i)]:.3g} bound {bound[tuple(i)]:.3g}" for i in idx)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; {detail}")
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+
+
+def run_gemm_quant(fmt, packed, m, n, k, x16, bias=None):
+    import dequantize_mat_vec_amd as dmv
+    torch, _ = torch_dev()
+    w_d = to_dev(np.asarray(packed).reshape(-1).view(np.uint8))
+    x_d = to_dev(np.ascontiguousarray(x16).view(np.uint16))
+    b_d = to_dev(bias.astype(np.float32)) if bias is not None else None
+    fbuf, y_d = guarded_y(m * n)
+    dmv.gemm_quant(fmt, m, n, k, w_d, x_d, y_d, b_d)
+    torch.cuda.synchronize()
+    assert guards_intact(fbuf, m * n), "quantized GEMM wrote outside Y"
+    return y_d.cpu().numpy().reshape(m, n)

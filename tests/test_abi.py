@@ -107,6 +107,24 @@ def test_i8row_and_gemm_argument_checks():
     assert lib.pesti_gemm_f16_smallm(0, 8, 64, None, None, None, None, None) == _lib.PESTI_OK
 
 
+@pytest.mark.parametrize("name", ["pesti_gemm_q8_0_smallm", "pesti_gemm_q4_k_smallm"])
+def test_gemm_quant_argument_checks(name):
+    fn = getattr(_raw(), name)
+    assert fn(-1, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
+    assert fn(5000, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
+    assert fn(4, -8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(4, 8, 40, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(4, 8, 32800, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(4, 8, 64, None, FAKE, FAKE, None, None) == _lib.PESTI_ERR_NULL
+    assert fn(4, 8, 64, FAKE, None, FAKE, None, None) == _lib.PESTI_ERR_NULL
+    assert fn(4, 8, 64, FAKE, FAKE, None, None, None) == _lib.PESTI_ERR_NULL
+    assert fn(4, 8, 64, FAKE, FAKE + 8, FAKE, None, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(4, 8, 64, FAKE + 2, FAKE, FAKE, None, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(4, 8, 64, FAKE, FAKE, FAKE, FAKE + 2, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(0, 8, 64, None, None, None, None, None) == _lib.PESTI_OK
+    assert fn(4, 0, 64, None, None, None, None, None) == _lib.PESTI_OK
+
+
 @pytest.mark.parametrize("name", ["pesti_dequant_q8_0", "pesti_dequant_q4_k", "pesti_dequant_q6_k"])
 def test_dequant_argument_checks(name):
     fn = getattr(_raw(), name)

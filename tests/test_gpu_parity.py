@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from dequantize_mat_vec_amd import synth
-from gpu_util import announce, assert_within, run_dequant, run_gemm, run_gemv
+from gpu_util import announce, assert_within, run_dequant, run_gemm, run_gemm_quant, run_gemv
 
 pytestmark = pytest.mark.gpu
 
@@ -291,6 +291,68 @@ def test_gemm_f16_parity(m, k, n):
     y = run_gemm(x, w, bias)
     y_ref, s_ref = oracle.gemm_f16(x, w, bias)
     assert_within(y, y_ref, s_ref, GEMM_REL, f"gemm m{m} k{k} n{n}")
+
+
+# ---------------------------------------------------------------------------
+# small-M GEMM on quantized weights: exact codes on the matrix cores, block
+# scales in float32, so the mat-vec's bound applies
+# ---------------------------------------------------------------------------
+QGEMM_REL = GEMV_REL
+QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
+               (1, 64, 40), (5, 96, 33), (16, 32, 16), (100, 1056, 48),
+               # ragged K split: 3 k-steps over the workgroup's wavefronts;
+               # Q8_0 rows of an odd block count (misaligned blocks); Q4_K
+               # rows padded to whole super-blocks
+               (33, 96, 17), (40, 320, 77), (19, 4896, 31),
+               # no columns: Y is the bias; long rows
+               (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
+               # wide layers: 1, 2 and 4 row tiles per workgroup
+               (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536)]
+
+
+@pytest.mark.parametrize("fmt", ("q8_0", "q4_k"))
+@pytest.mark.parametrize("m,k,n", QGEMM_CASES)
+def test_gemm_quant_parity(fmt, m, k, n):
+    rng = np.random.default_rng([15, m, k, n])
+    packed = synth.quant_blocks(fmt, rng, n, k) if k else np.zeros((n, 0), np.uint8)
+    x = synth.f16_activations(rng, m, k)
+    bias = synth.bias(rng, n)
+    y = run_gemm_quant(fmt, packed, m, n, k, x, bias)
+    y_ref, s_ref = oracle.gemm_packed(fmt, packed, n, k, x, bias)
+    assert_within(y, y_ref, s_ref, QGEMM_REL, f"{fmt} gemm m{m} k{k} n{n}")
+
+
+@pytest.mark.parametrize("fmt", ("q8_0", "q4_k"))
+def test_gemm_quant_no_bias_and_one_hot(fmt):
+    """Unit rows of X return dequantized columns of W (no bias)."""
+    rng = np.random.default_rng([16, len(fmt)])
+    n, k = 40, 512
+    packed = synth.quant_blocks(fmt, rng, n, k)
+    ks = [0, 1, 31, 32, 255, 256, 300, 511] * 2 + [7] * 4
+    x = np.zeros((len(ks), k), np.float16)
+    for m, kk in enumerate(ks):
+        x[m, kk] = 1.0
+    y = run_gemm_quant(fmt, packed, len(ks), n, k, x)
+    w32 = oracle.dequantize_f32(fmt, packed, n, k)
+    for m, kk in enumerate(ks):
+        assert np.array_equal(y[m], w32[:, kk]), (fmt, m, kk)
+
+
+QGEMM_FULL = [("q8_0", 16, synth.QWEN_VOCAB, 896), ("q4_k", 64, synth.QWEN_VOCAB, 896),
+              ("q4_k", 64, 4864, 896), ("q4_k", 32, 896, 4864), ("q8_0", 64, 896, 4864)]
+
+
+@pytest.mark.parametrize("fmt,m,n,k", QGEMM_FULL)
+def test_gemm_quant_full_size_sampled_columns(fmt, m, n, k):
+    rng = np.random.default_rng([17, m, n, k])
+    packed = synth.quant_blocks(fmt, rng, n, k)
+    x = synth.f16_activations(rng, m, k)
+    bias = synth.bias(rng, n)
+    y = run_gemm_quant(fmt, packed, m, n, k, x, bias)
+    cols = np.unique(np.concatenate([rng.integers(0, n, 256), [0, n - 1]]))
+    sub = packed.reshape(n, -1)[cols]
+    y_ref, s_ref = oracle.gemm_packed(fmt, sub, len(cols), k, x, bias[cols])
+    assert_within(y[:, cols], y_ref, s_ref, QGEMM_REL, f"{fmt} gemm m{m} {n}x{k}")
 
 
 # ---------------------------------------------------------------------------

@@ -399,6 +399,54 @@ def test_gemm_f16_identity_and_brute_force():
             assert abs(Fraction(float(y[m, n])) - ex) <= Fraction(2.0 ** -50) * Fraction(float(s[m, n]))
 
 
+def test_gemm_packed_unit_rows_pick_columns():
+    """Rows of X that are unit vectors pick columns of W: Y[m] = W[:, k_m] + b,
+    with W from the field-level decode (orientation and the f16 X path)."""
+    rng = np.random.default_rng(14)
+    for fmt, rows, inf in [("q8_0", 5, 64), ("q4_k", 3, 256), ("q4_k", 4, 128)]:
+        data, exact_w = _build(fmt, rng, rows, inf)
+        ks = [0, 31, 32, inf - 1]
+        x = np.zeros((len(ks), inf), np.float16)
+        for m, k in enumerate(ks):
+            x[m, k] = 1.0
+        bias = rng.normal(0, 0.02, rows).astype(np.float32)
+        y, _ = oracle.gemm_packed(fmt, data, rows, inf, x, bias)
+        for m, k in enumerate(ks):
+            for n in range(rows):
+                # one rounding of the exact sum (weights can reach 2^23)
+                assert float(y[m, n]) == float(exact_w[n][k] + Fraction(float(bias[n]))), (fmt, m, n)
+
+
+def test_gemm_packed_unit_scale_q8_0_is_f16_matmul():
+    """Q8_0 blocks with d = 1 hold the integer codes themselves, which
+    binary16 represents exactly: the packed product reduces to the binary16
+    GEMM on the code matrix."""
+    rng = np.random.default_rng(15)
+    rows, inf = 6, 96
+    codes = rng.integers(-128, 128, size=(rows, inf))
+    one = packing.f16_bits(1.0)
+    data = packing.rows_to_array([[packing.pack_q8_0_block(one, codes[r, 32 * b:32 * b + 32])
+                                   for b in range(inf // 32)] for r in range(rows)])
+    x = rng.standard_normal((5, inf)).astype(np.float16)
+    y, s = oracle.gemm_packed("q8_0", data, rows, inf, x)
+    y2, s2 = oracle.gemm_f16(x, codes.astype(np.float16))
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
+
+
+def test_gemm_packed_brute_force():
+    rng = np.random.default_rng(16)
+    for fmt, rows, inf in [("q8_0", 3, 64), ("q4_k", 3, 256)]:
+        data, exact_w = _build(fmt, rng, rows, inf)
+        x = rng.standard_normal((4, inf)).astype(np.float16)
+        bias = rng.normal(0, 0.02, rows).astype(np.float32)
+        y, s = oracle.gemm_packed(fmt, data, rows, inf, x, bias)
+        ex = _exact_gemv(exact_w, x, bias)
+        for m in range(4):
+            for n in range(rows):
+                err = abs(Fraction(float(y[m, n])) - ex[m][n])
+                assert err <= Fraction(2.0 ** -50) * Fraction(float(s[m, n])) + Fraction(1, 2 ** 200)
+
+
 def test_quantize_i8row_round_trip():
     rng = np.random.default_rng(14)
     w = rng.normal(0, 0.02, size=(32, 200)).astype(np.float32)
