@@ -196,6 +196,15 @@ def suite_cases():
         for b in (1, 2, 4, 8):
             cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
     cases.append(("q8_0 gpt2 lm-head 50257x768 b1", "gemv", ("q8_0", synth.GPT2_VOCAB, 768, 1)))
+    # prompt-width products on quantized weights, with the binary16-weight
+    # GEMM at the same shapes for comparison
+    qshapes = (("gate/up", synth.QWEN_FFN, synth.QWEN_HIDDEN), ("down", synth.QWEN_HIDDEN, synth.QWEN_FFN),
+               ("lm-head", synth.QWEN_VOCAB, synth.QWEN_HIDDEN))
+    for m in (16, 64):
+        for label, n, k in qshapes:
+            for fmt in ("q8_0", "q4_k"):
+                cases.append((f"{fmt} gemm {label} {n}x{k} m{m}", "qgemm", (fmt, m, n, k)))
+            cases.append((f"f16 gemm {label} {n}x{k} m{m}", "gemm", (m, k, n)))
     return cases
 
 
@@ -237,6 +246,15 @@ def run_suite(lib, args):
             sc = torch.from_numpy(scales).to(dev) if scales is not None else None
             algo = call_bytes(fmt, out, inf, batch, False)
             flops = 2.0 * out * inf * batch
+        elif kind == "qgemm":
+            fmt, m, n, k = prm
+            packed = synth.quant_blocks(fmt, rng, n, k)
+            x16 = torch.from_numpy(synth.f16_activations(rng, m, k).view(np.uint16)).to(dev)
+            b = torch.from_numpy(synth.bias(rng, n)).to(dev)
+            y = torch.empty(m * n, dtype=torch.float32, device=dev)
+            nbytes = packed.size
+            algo = int(n * k * NOMINAL_BYTES_PER_WEIGHT[fmt]) + 2 * m * k + 4 * m * n + 4 * n
+            flops = 2.0 * m * n * k
         else:
             m, k, n = prm
             w16 = synth.f16_weights(rng, n, k)
@@ -271,6 +289,9 @@ def run_suite(lib, args):
                       if fmt == "i8row" else
                       getattr(lib, f"pesti_gemv_{fmt}")(out, inf, ws[i % copies].data_ptr(),
                                                        x.data_ptr(), y.data_ptr(), None, batch, sh))
+            elif kind == "qgemm":
+                st = getattr(lib, f"pesti_gemm_{fmt}_smallm")(m, n, k, ws[i % copies].data_ptr(),
+                                                              x16.data_ptr(), y.data_ptr(), b.data_ptr(), sh)
             else:
                 st = lib.pesti_gemm_f16_smallm(m, n, k, ws[i % copies].data_ptr(), x16.data_ptr(),
                                                y.data_ptr(), b.data_ptr(), sh)
@@ -321,7 +342,7 @@ def run_suite(lib, args):
                "stored_GB/s": round(nbytes / med / 1e3, 1),
                "frac_of_read_ceiling": round(read_us * nbytes / rbytes / med, 4) if rbytes else None,
                "weight_copies": copies}
-        if kind == "gemm":
+        if kind in ("gemm", "qgemm"):
             rec["mfma_frac"] = round(flops / med / 1e6 / MFMA_F16_PEAK_TFLOPS, 5)
         print(json.dumps(rec), flush=True)
         out_lines.append(rec)

@@ -8,7 +8,7 @@
 // cores (v_mfma_f32_16x16x32_f16); below 16 rows the matrix cores would
 // idle most of their rows, so a vector-ALU kernel treats the rows of X as a
 // batch of mat-vecs over binary16 weights.
-#include "common.h"
+#include "gemm_wide.h"
 
 namespace pesti {
 
@@ -50,7 +50,7 @@ template <int NW, int MT, int C>
 __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
   __shared__ floatx4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
@@ -269,6 +269,24 @@ int launch_mfma(const GemmArgs& a, hipStream_t st) {
   return launch_mfma_t<16, 4>(a, st);
 }
 
+// binary16 weights for the wide-layer kernel: a unit is one k-step, 32
+// consecutive weights of the row, the lane's 8 of them one 16-byte load.
+struct WPolF16 {
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = false;
+  static constexpr bool kChained = false;
+  static constexpr int kSteps = 1;
+  static constexpr int kRing = 12;
+  struct Unit { pesti::u32x4 v; };
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    un.v = pesti::load_u32x4_a16(row + 64 * u + 16 * kg);
+  }
+  __device__ __forceinline__ static pesti::whalf8 codes(const Unit& un, int) {
+    return __builtin_bit_cast(pesti::whalf8, un.v);
+  }
+  __device__ __forceinline__ static void scales(const Unit&, int, float&, float&) {}
+};
+
 }  // namespace
 
 extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
@@ -295,7 +313,14 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
                                          dim3(256), params, 0, sh);
     return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
   }
-  if (m >= 16) return launch_mfma(a, sh);
+  if (m >= 16) {
+    const int wide = pesti_host::launch_wide<WPolF16>(
+        pesti::WideArgs{reinterpret_cast<const uint8_t*>(w), x, y, bias, m, out_features, in_features,
+                        2 * in_features},
+        lds_limit, sh);
+    if (wide != 1) return wide;
+    return launch_mfma(a, sh);
+  }
   // m < 16: rows of X in chunks of up to 8 as a batch of binary16 mat-vecs;
   // 32 lanes per W row holding up to 4 units each (rows of up to 4096
   // weights in one round), 64 lanes and several rounds beyond that.

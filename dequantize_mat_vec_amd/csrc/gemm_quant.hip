@@ -27,7 +27,7 @@
 // MFMA operand layout, lane l (i = l % 16, kg = l / 16): A = X row i,
 // k = 8kg..8kg+7; B = W row i (output column i), the same k; C = column i,
 // rows 4kg..4kg+3.
-#include "common.h"
+#include "gemm_wide.h"
 
 namespace pesti {
 
@@ -57,6 +57,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // ---------------------------------------------------------------------------
 struct QPolQ8_0 {
   static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
   struct Step { uint32_t c[3]; uint32_t d; uint32_t s; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
@@ -97,6 +98,7 @@ struct QPolQ8_0 {
 // ---------------------------------------------------------------------------
 struct QPolQ4_K {
   static constexpr bool kMin = true;
+  static constexpr bool kScaled = true;
   struct Step { uint32_t c[2]; u32x4 hdr; uint32_t j; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
@@ -145,6 +147,90 @@ struct QPolQ4_K {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Units of the wide-layer kernel (whole rows per wavefront, X in LDS).
+// Q8_0: one block per unit, the step's loads as above.  Q4_K: one
+// super-block per unit - the 16-byte header once, and each lane's 8 code
+// bytes of the four sub-block pairs - so a unit feeds eight k-steps.
+// ---------------------------------------------------------------------------
+struct WPolQ8_0 {
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = false;
+  static constexpr int kSteps = 1;
+  static constexpr int kRing = 8;
+  using Unit = QPolQ8_0::Step;
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    QPolQ8_0::load(row, u, kg, un);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int) { return QPolQ8_0::codes(un); }
+  __device__ __forceinline__ static void scales(const Unit& un, int, float& ds, float& dm) {
+    QPolQ8_0::scales(un, ds, dm);
+  }
+};
+
+struct WPolQ4_K {
+  static constexpr bool kMin = true;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = true;
+  static constexpr int kSteps = 8;
+  static constexpr int kRing = 4;
+  struct Unit { u32x4 hdr; uint32_t c[4][2]; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint8_t* sb = row + 144 * u;
+    un.hdr = load_u32x4_a16(sb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint8_t* p = sb + 16 + 32 * g + 8 * kg;
+      un.c[g][0] = load_u32(p);
+      un.c[g][1] = load_u32(p + 4);
+    }
+  }
+
+  // Operand of sub-block j: q * sc_j, an integer of at most 945, exact in
+  // binary16, so the super-block's eight k-steps accumulate in the matrix
+  // core and d is applied once.  A code byte q becomes binary16 1024 + q by
+  // placing 0x64 above it (v_perm_b32); one packed FMA then gives
+  // (1024 + q) * sc - 1024 * sc = q * sc, exact (one rounding of an exact
+  // small integer).  sc_j itself comes the same way: 1024 + sc, minus 1024.
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j) {
+    const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
+    const uint32_t a = (un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu;
+    const uint32_t b = (un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu;
+    // Scale bytes of sub-blocks 0..3 and 4..7 (S = header bytes 4..15).
+    const uint32_t sc_lo = un.hdr.y & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (un.hdr.w & 0x0F0F0F0Fu) | ((un.hdr.y >> 2) & 0x30303030u);
+    const uint32_t t = static_cast<uint32_t>(j & 3);
+    const uint32_t sel_sc = 0x04000400u | (t << 16) | t;   // [t, 0x64, t, 0x64]
+    const qhalf2 sc1024 = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, j < 4 ? sc_lo : sc_hi, sel_sc));
+    const qhalf2 sc = sc1024 - qhalf2{1024, 1024};
+    const qhalf2 off = sc * qhalf2{-1024, -1024};
+    uint32_t h[4];
+    h[0] = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);   // [q0, 0x64, q1, 0x64]
+    h[1] = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);   // [q2, 0x64, q3, 0x64]
+    h[2] = __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u);
+    h[3] = __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(qhalf2, h[e]), sc, off));
+    return __builtin_bit_cast(qhalf8, h);
+  }
+
+  __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
+
+  // -dmin * m_j for sub-block j = 4 * half + kg: the B operand of the
+  // 16x16x4 float32 product that subtracts the mins.  m_kg = S[4+kg] & 63;
+  // m_{4+kg} = (S[8+kg] >> 4) | (S[kg+4] >> 6) << 4.
+  __device__ __forceinline__ static float neg_min(const Unit& un, int half, int kg) {
+    const uint32_t z = (un.hdr.z >> (8 * kg)) & 0xFFu;
+    const uint32_t w = (un.hdr.w >> (8 * kg)) & 0xFFu;
+    const uint32_t m = half == 0 ? (z & 63u) : ((w >> 4) | ((z >> 6) << 4));
+    return -f16_hi(un.hdr.x) * static_cast<float>(m);
+  }
+  __device__ __forceinline__ static void scales(const Unit&, int, float&, float&) {}
+};
+
 template <class Q, int MT>
 struct QBuf {
   typename Q::Step w[2];
@@ -155,7 +241,7 @@ template <class Q, int NW, int MT>
 __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   __shared__ qfloat4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
@@ -276,7 +362,7 @@ int launch_quant(const QGemmArgs& a, hipStream_t st) {
   return launch_q<Q, 16, 4>(a, st);
 }
 
-template <class Q>
+template <class Q, class W>
 int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                const uint16_t* x, float* y, const float* bias, int64_t row_bytes, void* stream) {
   if (out_features < 0 || in_features < 0) return PESTI_ERR_SHAPE;
@@ -290,10 +376,12 @@ int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void*
   int dev = 0;
   size_t lds_limit = 0;
   const int st = pesti_host::current_device(&dev, &lds_limit);
-  (void)lds_limit;
   if (st != PESTI_OK) return st;
   hipStream_t sh = static_cast<hipStream_t>(stream);
   QGemmArgs a{static_cast<const uint8_t*>(blocks), x, y, bias, m, out_features, in_features, row_bytes};
+  const int wide = pesti_host::launch_wide<W>(
+      pesti::WideArgs{a.w, x, y, bias, m, out_features, in_features, row_bytes}, lds_limit, sh);
+  if (wide != 1) return wide;
   if (in_features == 0) {
     void* params[] = {&a};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_quant_bias_kernel),
@@ -310,13 +398,13 @@ extern "C" {
 
 int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ8_0>(m, out_features, in_features, blocks, x, y, bias,
+  return gemm_quant<pesti::QPolQ8_0, pesti::WPolQ8_0>(m, out_features, in_features, blocks, x, y, bias,
                                      (in_features / 32) * 34, stream);
 }
 
 int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
+  return gemm_quant<pesti::QPolQ4_K, pesti::WPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
                                      ((in_features + 255) / 256) * 144, stream);
 }
 

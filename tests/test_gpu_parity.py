@@ -279,7 +279,10 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               (33, 96, 17),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
-              (16, 64, 1600), (20, 128, 2000), (40, 96, 1540)]
+              (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
+              # wide layers: X rows staged in LDS once per workgroup
+              (17, 96, 2049), (65, 1024, 2048), (130, 256, 2100), (16, 4096, 2048),
+              (40, 32, 33000), (64, 896, 4864)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_CASES)
@@ -308,6 +311,13 @@ QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
                (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
                # wide layers: 1, 2 and 4 row tiles per workgroup
                (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536)]
+# Wide layers (128+ column tiles, X rows staged in LDS): ragged N and M,
+# several 64-row chunks of X, one k-step, rows of several wavefronts' tiles,
+# wavefronts left without a tile.
+QGEMM_WIDE = [(16, 896, 2100), (17, 96, 2049), (33, 320, 2050), (64, 1024, 2048),
+              (65, 32, 2064), (130, 256, 2100), (1, 64, 2048), (8, 4096, 2048),
+              (48, 896, 4864), (100, 96, 33000), (3, 32, 40000)]
+QGEMM_CASES += QGEMM_WIDE
 
 
 @pytest.mark.parametrize("fmt", ("q8_0", "q4_k"))
