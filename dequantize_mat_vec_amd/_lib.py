@@ -37,6 +37,7 @@ _SIGNATURES = {
     "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q8_0_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q4_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q6_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -178,6 +179,11 @@ def pesti_gemm_q4_k_smallm(m, out_features, in_features, blocks, x, y, bias=None
                    stream)
 
 
+def pesti_gemm_q6_k_smallm(m, out_features, in_features, blocks, x, y, bias=None, stream=None):
+    return _gemm_q("pesti_gemm_q6_k_smallm", m, out_features, in_features, blocks, x, y, bias,
+                   stream)
+
+
 def gemv_ops(ops):
     """ctypes array of pesti_gemv_op from (out, in, w, x, y, bias, row_scales)
     tuples whose pointer fields are tensors, ints or None."""
@@ -241,7 +247,7 @@ def gemv(fmt, out_features, in_features, w, x, y, bias=None, batch=1, scales=Non
 
 def gemm_quant(fmt, m, out_features, in_features, blocks, x, y, bias=None, stream=None):
     """Dispatch Y = X W^T + b (binary16 X, packed W) to the entry point of
-    format `fmt` (q8_0 or q4_k)."""
+    format `fmt` (q8_0, q4_k or q6_k)."""
     return _gemm_q(f"pesti_gemm_{fmt}_smallm", m, out_features, in_features, blocks, x, y, bias,
                    stream)
 

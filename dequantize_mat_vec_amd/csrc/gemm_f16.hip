@@ -272,6 +272,7 @@ int launch_mfma(const GemmArgs& a, hipStream_t st) {
 // binary16 weights for the wide-layer kernel: a unit is one k-step, 32
 // consecutive weights of the row, the lane's 8 of them one 16-byte load.
 struct WPolF16 {
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = false;
   static constexpr bool kChained = false;
@@ -281,10 +282,11 @@ struct WPolF16 {
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
     un.v = pesti::load_u32x4_a16(row + 64 * u + 16 * kg);
   }
-  __device__ __forceinline__ static pesti::whalf8 codes(const Unit& un, int) {
+  static constexpr int kParts = 1;
+  __device__ __forceinline__ static pesti::whalf8 codes(const Unit& un, int, int, int) {
     return __builtin_bit_cast(pesti::whalf8, un.v);
   }
-  __device__ __forceinline__ static void scales(const Unit&, int, float&, float&) {}
+  __device__ __forceinline__ static float scale(const Unit&, int, int) { return 1.f; }
 };
 
 }  // namespace

@@ -58,6 +58,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 struct QPolQ8_0 {
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
   struct Step { uint32_t c[3]; uint32_t d; uint32_t s; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
@@ -87,6 +88,10 @@ struct QPolQ8_0 {
     ds = f16_lo(st.d);
     dm = 0.f;
   }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) { return codes(st); }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    scales(st, ds, dm);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -99,6 +104,7 @@ struct QPolQ8_0 {
 struct QPolQ4_K {
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
   struct Step { uint32_t c[2]; u32x4 hdr; uint32_t j; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
@@ -145,6 +151,74 @@ struct QPolQ4_K {
     ds = d * 512.0f * static_cast<float>(sc);
     dm = dmin * static_cast<float>(mn);
   }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) { return codes(st); }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    scales(st, ds, dm);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Q6_K: 210-byte super-blocks (ql[128], qh[64], 16 int8 scales, binary16 d)
+// of sixteen 16-weight sub-blocks.  Weight 128h + 32g + l (h < 2, g < 4,
+// l < 32) has its low 4 bits in ql[64h + 32(g % 2) + l] (high nibble for
+// g >= 2) and its high 2 bits at bit 2g of qh[32h + l]; k-step t = 4h + g
+// covers l = 0..31, so a lane's 8 codes (l = 8kg..8kg+7) are 8 bytes of ql
+// and 8 of qh, and the step spans sub-blocks 2t (lanes kg < 2) and 2t + 1.
+// Super-blocks sit 2 bytes off a dword boundary every other one; the loads
+// are 2-byte aligned vector loads.  A code q (0..63) becomes binary16
+// 1024 + q by placing 0x64 above its byte, and q - 32 by one exact packed
+// subtraction of 1056.  (q - 32) * sc can exceed binary16's integers, so
+// the two sub-blocks of a step are two products with the other half of
+// the operand zeroed, each scaled by its own d * sc in float32.
+// ---------------------------------------------------------------------------
+typedef uint32_t q6u2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t q6u4 __attribute__((ext_vector_type(4), aligned(2)));
+
+__device__ __forceinline__ qhalf8 q6_k_codes(uint32_t l0, uint32_t l1, uint32_t h0, uint32_t h1, int g) {
+  const uint32_t ls = 4u * static_cast<uint32_t>(g >> 1);
+  const uint32_t hs = 2u * static_cast<uint32_t>(g);
+  const uint32_t q0 = ((l0 >> ls) & 0x0F0F0F0Fu) | (((h0 >> hs) & 0x03030303u) << 4);
+  const uint32_t q1 = ((l1 >> ls) & 0x0F0F0F0Fu) | (((h1 >> hs) & 0x03030303u) << 4);
+  qhalf2 v[4];
+  v[0] = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, q0, 0x04010400u));
+  v[1] = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, q0, 0x04030402u));
+  v[2] = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, q1, 0x04010400u));
+  v[3] = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, q1, 0x04030402u));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = v[e] - qhalf2{1056, 1056};
+  return __builtin_bit_cast(qhalf8, v);
+}
+
+// The half of a step's operand that belongs to sub-block part (lanes
+// kg = 2 part, 2 part + 1); the other lanes' codes are zeroed.
+__device__ __forceinline__ qhalf8 q6_k_part(qhalf8 v, int part, int kg) {
+  return (kg >> 1) == part ? v : qhalf8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+struct QPolQ6_K {
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr int kParts = 2;
+  struct Step { uint32_t l[2]; uint32_t h[2]; uint32_t sc; uint32_t d; uint32_t g; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* sb = row + 210 * (s >> 3);
+    const int t = s & 7, h = t >> 2, g = t & 3;
+    const q6u2 lv = *reinterpret_cast<const q6u2*>(sb + 64 * h + 32 * (g & 1) + 8 * kg);
+    const q6u2 hv = *reinterpret_cast<const q6u2*>(sb + 128 + 32 * h + 8 * kg);
+    st.l[0] = lv.x; st.l[1] = lv.y;
+    st.h[0] = hv.x; st.h[1] = hv.y;
+    st.sc = load_u16(sb + 192 + 2 * t);   // scales of sub-blocks 2t, 2t + 1
+    st.d = load_u16(sb + 208);
+    st.g = static_cast<uint32_t>(g);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int part, int kg) {
+    return q6_k_part(q6_k_codes(st.l[0], st.l[1], st.h[0], st.h[1], static_cast<int>(st.g)), part, kg);
+  }
+  __device__ __forceinline__ static void scales(const Step& st, int part, float& ds, float& dm) {
+    ds = f16_lo(st.d) * static_cast<float>(static_cast<int8_t>(st.sc >> (8 * part)));
+    dm = 0.f;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -154,25 +228,69 @@ struct QPolQ4_K {
 // bytes of the four sub-block pairs - so a unit feeds eight k-steps.
 // ---------------------------------------------------------------------------
 struct WPolQ8_0 {
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr bool kChained = false;
   static constexpr int kSteps = 1;
   static constexpr int kRing = 8;
+  static constexpr int kParts = 1;
   using Unit = QPolQ8_0::Step;
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
     QPolQ8_0::load(row, u, kg, un);
   }
-  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int) { return QPolQ8_0::codes(un); }
-  __device__ __forceinline__ static void scales(const Unit& un, int, float& ds, float& dm) {
-    QPolQ8_0::scales(un, ds, dm);
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int, int, int) { return QPolQ8_0::codes(un); }
+  __device__ __forceinline__ static float scale(const Unit& un, int, int) { return f16_lo(un.d); }
+};
+
+// Q6_K unit: one super-block - per lane its 8-byte pieces of ql (four) and
+// qh (two), the 16 scale bytes and d; a unit feeds eight k-steps of two
+// scaled parts each.
+struct WPolQ6_K {
+  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = false;
+  static constexpr int kParts = 2;
+  static constexpr int kSteps = 8;
+  static constexpr int kRing = 3;
+  struct Unit { uint32_t l[4][2]; uint32_t h[2][2]; q6u4 sc; uint32_t d; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint8_t* sb = row + 210 * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // e = 2h + g % 2
+      const q6u2 v = *reinterpret_cast<const q6u2*>(sb + 32 * e + 8 * kg);
+      un.l[e][0] = v.x;
+      un.l[e][1] = v.y;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const q6u2 v = *reinterpret_cast<const q6u2*>(sb + 128 + 32 * h + 8 * kg);
+      un.h[h][0] = v.x;
+      un.h[h][1] = v.y;
+    }
+    un.sc = *reinterpret_cast<const q6u4*>(sb + 192);
+    un.d = load_u16(sb + 208);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int part, int kg) {
+    const int h = j >> 2, g = j & 3, e = 2 * h + (g & 1);
+    return q6_k_part(q6_k_codes(un.l[e][0], un.l[e][1], un.h[h][0], un.h[h][1], g), part, kg);
+  }
+  // d * sc[2j + part]
+  __device__ __forceinline__ static float scale(const Unit& un, int j, int part) {
+    const int b = 2 * j + part;
+    const uint32_t w = b < 4 ? un.sc.x : (b < 8 ? un.sc.y : (b < 12 ? un.sc.z : un.sc.w));
+    return f16_lo(un.d) * static_cast<float>(static_cast<int8_t>(w >> (8 * (b & 3))));
   }
 };
 
 struct WPolQ4_K {
+  static constexpr int64_t kWideMinTiles = 256;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr bool kChained = true;
+  static constexpr int kParts = 1;
   static constexpr int kSteps = 8;
   static constexpr int kRing = 4;
   struct Unit { u32x4 hdr; uint32_t c[4][2]; };
@@ -228,7 +346,7 @@ struct WPolQ4_K {
     const uint32_t m = half == 0 ? (z & 63u) : ((w >> 4) | ((z >> 6) << 4));
     return -f16_hi(un.hdr.x) * static_cast<float>(m);
   }
-  __device__ __forceinline__ static void scales(const Unit&, int, float&, float&) {}
+  __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
 };
 
 template <class Q, int MT>
@@ -279,18 +397,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       if (s + c >= s_end) continue;   // wave-uniform
-      float ds, dm;
-      Q::scales(b.w[c], ds, dm);
-      const qhalf8 wv = Q::codes(b.w[c]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, qfloat4{0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0);
-        acc[t] += ds * p;
-        if constexpr (Q::kMin) {
-          const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
-                                                                    qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          acc[t] -= dm * sx;
+      for (int pt = 0; pt < Q::kParts; ++pt) {
+        float ds, dm;
+        Q::scales(b.w[c], pt, ds, dm);
+        const qhalf8 wv = Q::codes(b.w[c], pt, kg);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, qfloat4{0.f, 0.f, 0.f, 0.f},
+                                                                   0, 0, 0);
+          acc[t] += ds * p;
+          if constexpr (Q::kMin) {
+            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
+                                                                      qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            acc[t] -= dm * sx;
+          }
         }
       }
     }
@@ -406,6 +527,12 @@ int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
   return gemm_quant<pesti::QPolQ4_K, pesti::WPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
                                      ((in_features + 255) / 256) * 144, stream);
+}
+
+int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ6_K, pesti::WPolQ6_K>(m, out_features, in_features, blocks, x, y, bias,
+                                     ((in_features + 255) / 256) * 210, stream);
 }
 
 }  // extern "C"

@@ -15,15 +15,20 @@
 // is unconditional and in bounds.  No reduction: a wavefront owns its
 // tile's outputs over all of K and writes them once.
 //
-// Weight policy Q: a Unit holds the raw bytes of kSteps consecutive k-steps
+// Weight policy Q (kWideMinTiles: the layer width, in 16-column tiles,
+// from which this kernel is used): a Unit holds the raw bytes of kSteps consecutive k-steps
 // (a Q4_K super-block, a Q8_0 block, 32 binary16 weights), kRing units are
 // in flight per wavefront; load(row, u, kg, Unit&) reads unit u of a row
-// (whole units stay inside the row's padded length), codes(Unit, j) gives
-// step j's 8 binary16 operand values (j is a constant after unrolling) and,
-// when kScaled, scales(Unit, j, ds, dm) its scales: the step's partial tile is added as ds * P, and for kMin
-// formats dm * (sum of the step's 32 x) is subtracted, the sums taken once
-// per workgroup into LDS.  Unscaled (binary16) weights accumulate in the
-// matrix core directly.
+// (whole units stay inside the row's padded length).  Unscaled (binary16)
+// weights: codes(Unit, j, 0, kg) gives step j's 8 operand values, which
+// accumulate in the matrix core directly.  Scaled formats: each of the
+// step's kParts parts - codes(Unit, j, part, kg), scale(Unit, j, part) - is
+// its own product, added to the float32 sum times its scale.  Chained
+// formats (kChained) carry the sub-block scales in the operand:
+// codes(Unit, j) for the eight steps of a unit accumulate in the matrix
+// core, d(Unit) scales the sum once, and for kMin formats neg_min(Unit,
+// half, kg) times the per-step sums of X (taken once per workgroup into
+// LDS) removes the mins.  j, part and half are constants after unrolling.
 //
 // Operand layout, lane l (i = l % 16, kg = l / 16): A = X row i,
 // k = 8kg..8kg+7 of the step; B = W row i (output column i), the same k;
@@ -221,22 +226,23 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
         for (int j = 0; j < KS; ++j) {
           const int s = c_u * KS + j;
           if (KS > 1 && s >= S) break;   // wave-uniform: the row's last, partial unit
-          const whalf8 wv = Q::codes(ring[u].un, j);
           if constexpr (Q::kScaled) {
-            float ds, dm;
-            Q::scales(ring[u].un, j, ds, dm);
+            // Each scaled part (a block, or a sub-block's half of the
+            // operand) is its own product, added times its scale.
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              const whalf8 xv = xf[(t * S + s) * 64 + lane];
-              const wfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, wfloat4{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0);
-              acc[t] += ds * p;
-              if constexpr (Q::kMin) {
-                const wfloat4 s4 = *reinterpret_cast<const wfloat4*>(sx + s * 16 * MT + 16 * t + 4 * kg);
-                acc[t] -= dm * s4;
+            for (int pt = 0; pt < Q::kParts; ++pt) {
+              const whalf8 wv = Q::codes(ring[u].un, j, pt, kg);
+              const float ds = Q::scale(ring[u].un, j, pt);
+#pragma unroll
+              for (int t = 0; t < MT; ++t) {
+                const whalf8 xv = xf[(t * S + s) * 64 + lane];
+                const wfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, wfloat4{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0);
+                acc[t] += ds * p;
               }
             }
           } else {
+            const whalf8 wv = Q::codes(ring[u].un, j, 0, kg);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
               const whalf8 xv = xf[(t * S + s) * 64 + lane];
@@ -284,11 +290,12 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
 
 namespace pesti_host {
 
-// Launches the wide-layer kernel when it applies: at least kWideMinTiles
-// column tiles, and the workgroup's rows of X (16 per M-tile; 1, 2 or 4
-// M-tiles by m, more rows in further workgroups along y) fit in LDS.
-// Returns 1 (and launches nothing) when it does not apply.
-constexpr int64_t kWideMinTiles = 128;
+// Launches the wide-layer kernel when it applies: at least Q::kWideMinTiles
+// column tiles (below that the K-split kernels, whose wavefronts split K
+// and so issue more loads at once, finish sooner), and the workgroup's rows
+// of X (16 per M-tile; 1, 2 or 4 M-tiles by m, more rows in further
+// workgroups along y) fit in LDS.  Returns 1 (and launches nothing) when it
+// does not apply.
 // Workgroups per CU that the grid is sized for (also capped by LDS): each
 // stages its rows of X once, so fewer, longer-lived workgroups amortise the
 // staging, more of them balance the tiles better.
@@ -324,7 +331,7 @@ int launch_wide_m(const pesti::WideArgs& a, int64_t lds, size_t lds_limit, hipSt
 template <class Q>
 int launch_wide(const pesti::WideArgs& a, size_t lds_limit, hipStream_t st) {
   const int64_t tiles = (a.n + 15) / 16;
-  if (tiles < kWideMinTiles || a.k == 0) return 1;
+  if (tiles < Q::kWideMinTiles || a.k == 0) return 1;
   const int mt = a.m <= 16 ? 1 : (a.m <= 32 ? 2 : 4);
   const int64_t lds = pesti::wide_lds_bytes<Q>(mt, a.k);
   if (lds > static_cast<int64_t>(lds_limit)) return 1;

@@ -148,7 +148,7 @@ int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
  * "Benchmarks": x @ w + b at prompt width) with W kept in the block format
  * of the mat-vec ("Project scaffold ...", quant.rs: dequantize fused into
  * the product, W never expanded).  blocks: out_features packed rows exactly
- * as for pesti_gemv_q8_0 / pesti_gemv_q4_k; X binary16 [m][in] (16-byte
+ * as for pesti_gemv_q8_0 / pesti_gemv_q4_k / pesti_gemv_q6_k; X binary16 [m][in] (16-byte
  * aligned), Y float32 [m][out], bias float32 [out] or NULL; m in [0,
  * PESTI_MAX_GEMM_M].  The matrix cores multiply the exact integer codes by
  * X (every product exact in float32) one 32-weight block or sub-block at a
@@ -159,6 +159,12 @@ int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const void* blocks, const uint16_t* x, float* y,
                            const float* bias, void* stream);
 int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
+/* Q6_K rows as for pesti_gemv_q6_k.  Its codes are exact too (q - 32), but
+ * each 32-weight k-step spans two 16-weight sub-blocks, so a step is two
+ * products (each on half the operand) scaled apart. */
+int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const void* blocks, const uint16_t* x, float* y,
                            const float* bias, void* stream);
 

@@ -280,8 +280,9 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
               (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
-              # wide layers: X rows staged in LDS once per workgroup
-              (17, 96, 2049), (65, 1024, 2048), (130, 256, 2100), (16, 4096, 2048),
+              # wide layers (1024+ column tiles): X rows staged in LDS once
+              # per workgroup
+              (17, 96, 16385), (65, 1024, 16400), (130, 256, 16500), (16, 4096, 16384),
               (40, 32, 33000), (64, 896, 4864)]
 
 
@@ -311,16 +312,19 @@ QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
                (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
                # wide layers: 1, 2 and 4 row tiles per workgroup
                (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536)]
-# Wide layers (128+ column tiles, X rows staged in LDS): ragged N and M,
-# several 64-row chunks of X, one k-step, rows of several wavefronts' tiles,
-# wavefronts left without a tile.
-QGEMM_WIDE = [(16, 896, 2100), (17, 96, 2049), (33, 320, 2050), (64, 1024, 2048),
-              (65, 32, 2064), (130, 256, 2100), (1, 64, 2048), (8, 4096, 2048),
+# Wide layers (1024+ column tiles, 256+ for Q4_K; X rows staged in LDS):
+# ragged N and M, several 64-row chunks of X, one k-step, rows of several
+# wavefronts' tiles, wavefronts left without a tile.
+QGEMM_WIDE = [(16, 896, 16400), (17, 96, 16385), (33, 320, 16390), (64, 1024, 16384),
+              (65, 32, 16400), (130, 256, 16500), (1, 64, 16384), (8, 4096, 16384),
               (48, 896, 4864), (100, 96, 33000), (3, 32, 40000)]
 QGEMM_CASES += QGEMM_WIDE
 
 
-@pytest.mark.parametrize("fmt", ("q8_0", "q4_k"))
+QGEMM_FORMATS = ("q8_0", "q4_k", "q6_k")
+
+
+@pytest.mark.parametrize("fmt", QGEMM_FORMATS)
 @pytest.mark.parametrize("m,k,n", QGEMM_CASES)
 def test_gemm_quant_parity(fmt, m, k, n):
     rng = np.random.default_rng([15, m, k, n])
@@ -332,7 +336,7 @@ def test_gemm_quant_parity(fmt, m, k, n):
     assert_within(y, y_ref, s_ref, QGEMM_REL, f"{fmt} gemm m{m} k{k} n{n}")
 
 
-@pytest.mark.parametrize("fmt", ("q8_0", "q4_k"))
+@pytest.mark.parametrize("fmt", QGEMM_FORMATS)
 def test_gemm_quant_no_bias_and_one_hot(fmt):
     """Unit rows of X return dequantized columns of W (no bias)."""
     rng = np.random.default_rng([16, len(fmt)])
@@ -349,7 +353,8 @@ def test_gemm_quant_no_bias_and_one_hot(fmt):
 
 
 QGEMM_FULL = [("q8_0", 16, synth.QWEN_VOCAB, 896), ("q4_k", 64, synth.QWEN_VOCAB, 896),
-              ("q4_k", 64, 4864, 896), ("q4_k", 32, 896, 4864), ("q8_0", 64, 896, 4864)]
+              ("q4_k", 64, 4864, 896), ("q4_k", 32, 896, 4864), ("q8_0", 64, 896, 4864),
+              ("q6_k", 64, 896, 4864), ("q6_k", 16, 4864, 896), ("q6_k", 32, synth.QWEN_VOCAB, 896)]
 
 
 @pytest.mark.parametrize("fmt,m,n,k", QGEMM_FULL)

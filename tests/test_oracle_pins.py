@@ -403,7 +403,8 @@ def test_gemm_packed_unit_rows_pick_columns():
     """Rows of X that are unit vectors pick columns of W: Y[m] = W[:, k_m] + b,
     with W from the field-level decode (orientation and the f16 X path)."""
     rng = np.random.default_rng(14)
-    for fmt, rows, inf in [("q8_0", 5, 64), ("q4_k", 3, 256), ("q4_k", 4, 128)]:
+    for fmt, rows, inf in [("q8_0", 5, 64), ("q4_k", 3, 256), ("q4_k", 4, 128), ("q6_k", 3, 256),
+                           ("q6_k", 2, 96)]:
         data, exact_w = _build(fmt, rng, rows, inf)
         ks = [0, 31, 32, inf - 1]
         x = np.zeros((len(ks), inf), np.float16)
@@ -435,7 +436,7 @@ def test_gemm_packed_unit_scale_q8_0_is_f16_matmul():
 
 def test_gemm_packed_brute_force():
     rng = np.random.default_rng(16)
-    for fmt, rows, inf in [("q8_0", 3, 64), ("q4_k", 3, 256)]:
+    for fmt, rows, inf in [("q8_0", 3, 64), ("q4_k", 3, 256), ("q6_k", 2, 256)]:
         data, exact_w = _build(fmt, rng, rows, inf)
         x = rng.standard_normal((4, inf)).astype(np.float16)
         bias = rng.normal(0, 0.02, rows).astype(np.float32)
