@@ -165,7 +165,8 @@ struct QPolQ4_K {
 // covers l = 0..31, so a lane's 8 codes (l = 8kg..8kg+7) are 8 bytes of ql
 // and 8 of qh, and the step spans sub-blocks 2t (lanes kg < 2) and 2t + 1.
 // Super-blocks sit 2 bytes off a dword boundary every other one; the loads
-// are 2-byte aligned vector loads.  A code q (0..63) becomes binary16
+// are 2-byte aligned vector loads (measured faster than dword loads
+// realigned in registers).  A code q (0..63) becomes binary16
 // 1024 + q by placing 0x64 above its byte, and q - 32 by one exact packed
 // subtraction of 1056.  (q - 32) * sc can exceed binary16's integers, so
 // the two sub-blocks of a step are two products with the other half of
@@ -372,6 +373,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   const int s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
 
   const int64_t wn = n0 + i < a.n ? n0 + i : a.n - 1;
+  // The bias of the lane's output column, loaded first (branch-free: without
+  // a bias, a word of X scaled by 0), so the epilogue never waits on a load
+  // issued after the weights.
+  static_assert(NW >= MT, "one epilogue element per thread");
+  const float bias_v = (a.bias ? 1.f : 0.f) *
+                       (a.bias ? a.bias : reinterpret_cast<const float*>(a.x))[a.bias ? wn : 0];
   const uint8_t* wrow = a.w + wn * a.row_bytes;
   const uint16_t* xrow[MT];
 #pragma unroll
@@ -417,15 +424,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
     }
   };
 
-  QBuf<Q, MT> ba, bb;
-  load(s_begin, ba);
-  for (int s = s_begin; s < s_end; s += 4) {
-    load(s + 2, bb);
-    mma(s, ba);
-    if (s + 2 >= s_end) break;
-    load(s + 4, ba);
-    mma(s + 2, bb);
+  // One buffer of two k-steps, refilled right after it is consumed and
+  // only while steps remain (the last pass is peeled, so no pass skips a
+  // refill: a buffer kept across a skipped refill would make the compiler
+  // copy it, and the copy wait for every load in flight).  Deeper rings
+  // measured slower: a layer runs hundreds of wavefronts, whose own loads
+  // overlap, and more loads in flight per wavefront congest the memory
+  // pipeline.
+  QBuf<Q, MT> buf;
+  load(s_begin, buf);
+  int s = s_begin;
+  for (; s + 2 < s_end; s += 2) {
+    mma(s, buf);
+    load(s + 2, buf);
   }
+  mma(s, buf);
 
 #pragma unroll
   for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
@@ -437,7 +450,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
     for (int w = 1; w < NW; ++w) r += part[w][t][l];
     const int64_t col = n0 + (l & 15);
     if (col < a.n) {
-      const float bv = a.bias ? a.bias[col] : 0.f;
+      const float bv = bias_v;   // e = threadIdx.x: column n0 + i
       const float v[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
