@@ -50,6 +50,9 @@ def parse_args(argv=None):
     p.add_argument("--copies", type=int, default=2, help="weight copies alternated per step")
     p.add_argument("--grouping", choices=("stage", "none"), default="stage",
                    help="one launch per dependency stage (Q/K/V, O, gate/up, down) or per call")
+    p.add_argument("--ffn", choices=("separate", "swiglu"), default="separate",
+                   help="gate and up as two mat-vecs (the 169-call step) or one fused launch "
+                        "writing silu(gate) * up, which the down projection then reads")
     p.add_argument("--kernel-steps", type=int, default=20,
                    help="replays of each per-kernel graph (per-kernel times)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -131,31 +134,56 @@ def plan_launches(calls, grouping):
     return launches
 
 
-def make_step(lib, calls, launches, weights, xs, ys, biases):
+def make_step(lib, calls, launches, weights, xs, ys, biases, ffn="separate"):
     """A function issuing the step's launches on a stream handle; the op
-    tables are built once so a step is only the C calls."""
+    tables are built once so a step is only the C calls.  With ffn
+    "swiglu" each layer's gate/up launch is the fused pesti_gemv_swiglu,
+    writing h = silu(gate) * up into the gate call's output buffer, and the
+    down projection reads h as its x (the step's data dependence in a
+    model)."""
     import ctypes
     from dequantize_mat_vec_amd import _lib
+    h_of_layer = {}
+    if ffn == "swiglu":
+        for fmt, idx in launches:
+            names = [calls[i][1] for i in idx]
+            if names == ["gate", "up"]:
+                h_of_layer[calls[idx[0]][0]] = idx[0]
     plans = []
     for wl in weights:
         plan = []
         for fmt, idx in launches:
+            names = [calls[i][1] for i in idx]
+            if ffn == "swiglu" and names == ["gate", "up"]:
+                g, u = idx
+                _, _, _, out, inf, _ = calls[g]
+                plan.append(("swiglu", (_lib.FORMAT_IDS[fmt], out, inf, wl[g].data_ptr(), wl[u].data_ptr(),
+                                        xs[g].data_ptr(), ys[g].data_ptr())))
+                continue
             arr = (_lib.GemvOp * len(idx))()
             for k, i in enumerate(idx):
-                _, _, _, out, inf, _ = calls[i]
+                layer, name, _, out, inf, _ = calls[i]
                 b = biases[i]
-                arr[k] = _lib.GemvOp(out, inf, wl[i].data_ptr(), None, xs[i].data_ptr(),
+                x_ptr = xs[i].data_ptr()
+                if name == "down" and layer in h_of_layer:
+                    x_ptr = ys[h_of_layer[layer]].data_ptr()
+                arr[k] = _lib.GemvOp(out, inf, wl[i].data_ptr(), None, x_ptr,
                                      ys[i].data_ptr(), b.data_ptr() if b is not None else None)
-            plan.append((_lib.FORMAT_IDS[fmt], len(idx), ctypes.cast(arr, ctypes.c_void_p), arr))
+            plan.append(("group", (_lib.FORMAT_IDS[fmt], len(idx), ctypes.cast(arr, ctypes.c_void_p), arr)))
         plans.append(plan)
     fn = lib.pesti_gemv_group
+    fn_swiglu = lib.pesti_gemv_swiglu
 
     def step(copy, stream_handle, only=None):
         """One step (or, with `only`, just the launches whose indices are in it)."""
-        for idx, (fid, n, ptr, _keep) in enumerate(plans[copy]):
+        for idx, (kind, a) in enumerate(plans[copy]):
             if only is not None and idx not in only:
                 continue
-            st = fn(fid, n, ptr, 1, stream_handle)
+            if kind == "group":
+                st = fn(a[0], a[1], a[2], 1, stream_handle)
+            else:
+                fid, out, inf, wg, wu, x, h = a
+                st = fn_swiglu(fid, out, inf, wg, wu, None, None, x, h, 1, stream_handle)
             if st != 0:
                 raise RuntimeError(f"launch {idx} failed with status {st}")
     return step
@@ -526,7 +554,10 @@ def main(argv=None):
         return 0
     calls, weights, xs, ys, biases = build_inputs(args.copies)
     launches = plan_launches(calls, args.grouping)
-    step = make_step(lib, calls, launches, weights, xs, ys, biases)
+    if args.ffn == "swiglu" and args.grouping != "stage":
+        print("--ffn swiglu fuses the gate/up stage: it needs --grouping stage", file=sys.stderr)
+        return 2
+    step = make_step(lib, calls, launches, weights, xs, ys, biases, args.ffn)
     bytes_per_step = sum(call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
@@ -577,6 +608,10 @@ def main(argv=None):
         # stream: time per replay / launches per replay.
         names = [kernel_name(fmt, [calls[i][4] for i in idx], [calls[i][3] for i in idx])
                  for fmt, idx in launches]
+        if args.ffn == "swiglu":
+            names = [n.replace("R=1>", "R=1, gate/up paired, SwiGLU>")
+                     if [calls[i][1] for i in idx] == ["gate", "up"] else n
+                     for n, (_, idx) in zip(names, launches)]
         per_kernel = {}
         for name in sorted(set(names)):
             only = {i for i, n in enumerate(names) if n == name}
@@ -631,7 +666,7 @@ def main(argv=None):
                                "{Q,K,V,O,gate,up Q4_K; down Q4_K/Q6_K} + 151936x896 Q8_0 LM head "
                                "= 169 mat-vecs", "bytes_per_step": bytes_per_step,
                    "launch": args.mode, "launches_per_step": len(launches),
-                   "grouping": args.grouping, "weight_copies": args.copies},
+                   "grouping": args.grouping, "ffn": args.ffn, "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (None if traffic is None else int(traffic)),

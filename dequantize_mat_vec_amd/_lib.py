@@ -34,6 +34,7 @@ _SIGNATURES = {
     "pesti_gemv_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_group": (_c_int, [_i32, _i32, _vp, _i32, _vp]),
+    "pesti_gemv_swiglu": (_c_int, [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q8_0_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q4_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -157,6 +158,15 @@ def pesti_gemv_i8row(out_features, in_features, codes, row_scales, x, y, bias=No
     return _check("pesti_gemv_i8row", load().pesti_gemv_i8row(
         out_features, in_features, _ptr(codes), _ptr(row_scales), _ptr(x), _ptr(y), _ptr(bias),
         batch, _stream(stream)))
+
+
+def pesti_gemv_swiglu(fmt, out_features, in_features, w_gate, w_up, x, h, batch=1,
+                      gate_scales=None, up_scales=None, stream=None):
+    """h = silu(W_gate x) * (W_up x) in one launch (row scales for i8row only)."""
+    fid = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
+    return _check("pesti_gemv_swiglu", load().pesti_gemv_swiglu(
+        fid, out_features, in_features, _ptr(w_gate), _ptr(w_up), _ptr(gate_scales), _ptr(up_scales),
+        _ptr(x), _ptr(h), batch, _stream(stream)))
 
 
 def pesti_gemm_f16_smallm(m, out_features, in_features, w, x, y, bias=None, stream=None):

@@ -47,6 +47,26 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
   }
 }
 
+int pesti_gemv_swiglu(int32_t format, int64_t out_features, int64_t in_features, const void* w_gate,
+                      const void* w_up, const float* gate_scales, const float* up_scales, const float* x,
+                      float* h, int32_t batch, void* stream) {
+  switch (format) {
+    case PESTI_FMT_Q8_0:
+      return pesti_gemv::swiglu_q8_0(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
+                                     stream);
+    case PESTI_FMT_Q4_K:
+      return pesti_gemv::swiglu_q4_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
+                                     stream);
+    case PESTI_FMT_Q6_K:
+      return pesti_gemv::swiglu_q6_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
+                                     stream);
+    case PESTI_FMT_I8ROW:
+      return pesti_gemv::swiglu_i8row(out_features, in_features, w_gate, w_up, gate_scales, up_scales, x, h,
+                                      batch, stream);
+    default: return PESTI_ERR_SHAPE;
+  }
+}
+
 int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
                     float* y, const float* bias, int32_t batch, void* stream) {
   const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);

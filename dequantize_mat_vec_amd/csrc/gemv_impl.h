@@ -56,6 +56,8 @@ struct GemvArgs {
   int64_t units;          // units per row
   int64_t xpad;           // logical x length staged (zero filled past in)
   int64_t xstride;        // LDS floats per staged batch row
+  const uint8_t* w2;      // paired launches: the up projection's rows
+  const float* scales2;   // paired launches: its i8row row scales
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -604,14 +606,28 @@ struct GroupArgs {
 // lane groups only) walk their units with the next unit's loads issued
 // before the current one is computed.  Rows past the op's end read the
 // tile's first row (in bounds) and are not stored.
-template <class F, int L, int B, int U, int R>
+//
+// Paired launches (P) compute row r of W (the gate projection) and row r of
+// w2 (the up projection) together and write silu(gate) * up with silu(g) =
+// g * sigmoid(g) ("PESTI ..." README, "Conformance": SwiGLU with the
+// sigmoid-based SiLU), so the feed-forward input never leaves registers
+// between the two products.  With 16 or 32 lanes per row (R = 1) adjacent
+// lane groups of a wave take the gate and the up row, one exchange across
+// the pair joins their sums, and a tile keeps the unpaired launch's lanes
+// per row; whole-wave rows (R = 2) hold both rows in one lane group.
+template <int L, int R, bool P>
+constexpr int kTileRows = P ? (R == 1 ? kWavesPerGroup * (kWave / L) / 2 : kWavesPerGroup * (kWave / L))
+                            : kWavesPerGroup * (kWave / L) * R;
+
+template <class F, int L, int B, int U, int R, bool P = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   extern __shared__ float lds[];
   constexpr int XS = L <= 16 ? 1 : (L == 32 ? 2 : 8);
   constexpr int kRowsPerWave = kWave / L;
   constexpr int kRowsPerSlab = kWavesPerGroup * kRowsPerWave;
-  constexpr int kRowsPerTile = kRowsPerSlab * R;
+  constexpr int kRowsPerTile = kTileRows<L, R, P>;
   static_assert(R == 1 || L < 64 || U == 1, "several rows per lane group need short rows");
+  static_assert(!P || (R == 1 && L < 64) || R == 2, "paired rows: lane-group pairs or two rows per group");
 
   // blockIdx.y picks the op, so the op's arguments are read in one round
   // trip without first scanning the group.
@@ -637,9 +653,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   const uint8_t* rp[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const int r = rofs + k * kRowsPerSlab;
-    rp[k] = tile_base + (r < left ? __umul24(static_cast<uint32_t>(r),
-                                              static_cast<uint32_t>(a.row_bytes)) : 0u);
+    if constexpr (P && R == 1) {   // even lane groups: gate row rofs / 2; odd: up row
+      const int pr = rofs >> 1;
+      const uint8_t* base = ((rofs & 1) ? a.w2 : a.w) + first * a.row_bytes;
+      rp[k] = base + (pr < left ? __umul24(static_cast<uint32_t>(pr),
+                                           static_cast<uint32_t>(a.row_bytes)) : 0u);
+    } else if constexpr (P) {   // row rofs of the gate (k = 0) and up (k = 1) rows
+      const uint8_t* base = (k == 0 ? a.w : a.w2) + first * a.row_bytes;
+      rp[k] = base + (rofs < left ? __umul24(static_cast<uint32_t>(rofs),
+                                             static_cast<uint32_t>(a.row_bytes)) : 0u);
+    } else {
+      const int r = rofs + k * kRowsPerSlab;
+      rp[k] = tile_base + (r < left ? __umul24(static_cast<uint32_t>(r),
+                                                static_cast<uint32_t>(a.row_bytes)) : 0u);
+    }
   }
 
   auto live = [&](int jj) {
@@ -700,7 +727,39 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
   for (int i = 0; i < R * B; ++i) acc[i] = group_sum<L>(acc[i]);
   // Every lane of the group now holds all R * B sums; lane k of the group
-  // stores row k.
+  // stores row k (a paired launch: lane 0 stores silu(gate) * up).
+  if constexpr (P && R == 1) {
+    // The up sums sit in the odd lane group of the pair, L lanes up.
+    float up[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) up[b] = __shfl_xor(acc[b], L, kWave);
+    const int pr = rofs >> 1;
+    if (sub == 0 && (rofs & 1) == 0 && pr < left) {
+      const int64_t row = first + pr;
+      const float rs0 = a.scales ? a.scales[row] : 1.f;
+      const float rs1 = a.scales2 ? a.scales2[row] : 1.f;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float gv = acc[b] * rs0;
+        const float uv = up[b] * rs1;
+        a.y[b * a.out + row] = gv / (1.f + expf(-gv)) * uv;
+      }
+    }
+    return;
+  } else if constexpr (P) {
+    if (sub == 0 && rofs < left) {
+      const int64_t row = first + rofs;
+      const float rs0 = a.scales ? a.scales[row] : 1.f;
+      const float rs1 = a.scales2 ? a.scales2[row] : 1.f;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float gv = acc[b] * rs0;
+        const float uv = acc[B + b] * rs1;
+        a.y[b * a.out + row] = gv / (1.f + expf(-gv)) * uv;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int r = rofs + k * kRowsPerSlab;
@@ -724,9 +783,9 @@ namespace pesti_gemv {
 using pesti::GemvArgs;
 using pesti::GroupArgs;
 
-template <class F, int L, int B, int U, int R>
+template <class F, int L, int B, int U, int R, bool P = false>
 int launch_one(const GroupArgs& g, size_t lds_bytes, hipStream_t stream) {
-  constexpr int64_t kRowsPerTile = pesti::kWavesPerGroup * (pesti::kWave / L) * R;
+  constexpr int64_t kRowsPerTile = pesti::kTileRows<L, R, P>;
   int64_t tiles = 0;
   for (int i = 0; i < g.n_ops; ++i) {
     const int64_t t = (g.op[i].out + kRowsPerTile - 1) / kRowsPerTile;
@@ -735,7 +794,7 @@ int launch_one(const GroupArgs& g, size_t lds_bytes, hipStream_t stream) {
   if (tiles <= 0) return PESTI_OK;
   GroupArgs args = g;
   void* params[] = {&args};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_kernel<F, L, B, U, R>),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_kernel<F, L, B, U, R, P>),
                                  dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(g.n_ops)),
                                  dim3(pesti::kThreads), params, lds_bytes, stream);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
@@ -926,4 +985,92 @@ int group_q8_0(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* str
 int group_q4_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q6_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+// Paired gate/up launches with the SwiGLU epilogue (swiglu_dispatch below).
+#define PESTI_SWIGLU_ARGS                                                                          \
+  int64_t out_features, int64_t in_features, const void *w_gate, const void *w_up,                 \
+      const float *gate_scales, const float *up_scales, const float *x, float *h, int32_t batch,    \
+      void *stream
+int swiglu_q8_0(PESTI_SWIGLU_ARGS);
+int swiglu_q4_k(PESTI_SWIGLU_ARGS);
+int swiglu_q6_k(PESTI_SWIGLU_ARGS);
+int swiglu_i8row(PESTI_SWIGLU_ARGS);
+
+// ---------------------------------------------------------------------------
+// Paired gate/up launch with the SwiGLU epilogue: h = silu(W_gate x) *
+// (W_up x), both matrices of one format and shape.  Rows must fit the
+// one-round path (at most 64 units, all held at once).
+// ---------------------------------------------------------------------------
+template <class F, int L>
+int launch_pair_b(const GroupArgs& g, int batch, size_t lds, hipStream_t st) {
+  constexpr int R = L < 64 ? 1 : 2;   // lane-group pairs, or both rows in a whole wave
+  switch (batch) {
+    case 1: return launch_one<F, L, 1, 1, R, true>(g, lds, st);
+    case 2: return launch_one<F, L, 2, 1, R, true>(g, lds, st);
+    case 3: return launch_one<F, L, 3, 1, R, true>(g, lds, st);
+    case 4: return launch_one<F, L, 4, 1, R, true>(g, lds, st);
+    case 5: return launch_one<F, L, 5, 1, R, true>(g, lds, st);
+    case 6: return launch_one<F, L, 6, 1, R, true>(g, lds, st);
+    case 7: return launch_one<F, L, 7, 1, R, true>(g, lds, st);
+    case 8: return launch_one<F, L, 8, 1, R, true>(g, lds, st);
+    default: return PESTI_ERR_BATCH;
+  }
+}
+
+template <class F>
+int swiglu_dispatch(int64_t out_features, int64_t in_features, const void* w_gate, const void* w_up,
+                    const float* gate_scales, const float* up_scales, const float* x, float* h,
+                    int32_t batch, void* stream) {
+  if (batch < 0 || batch > PESTI_MAX_BATCH) return PESTI_ERR_BATCH;
+  const pesti_gemv_op gate = make_op(out_features, in_features, w_gate, gate_scales, x, h, nullptr);
+  const pesti_gemv_op up = make_op(out_features, in_features, w_up, up_scales, x, h, nullptr);
+  int st = check_op<F>(gate, batch);
+  if (st < 0) return st;
+  const int st_up = check_op<F>(up, batch);
+  if (st_up < 0) return st_up;
+  if (st == 1) return PESTI_OK;   // nothing to compute
+  int64_t rb = 0, units = 0;
+  shape_of<F>(in_features, &rb, &units);
+  if (units > 64) return PESTI_ERR_SHAPE;   // rows beyond the one-round path
+  int dev = 0;
+  size_t lds_limit = 0;
+  st = pesti_host::current_device(&dev, &lds_limit);
+  if (st != PESTI_OK) return st;
+  hipStream_t sh = static_cast<hipStream_t>(stream);
+  GroupArgs g{};
+  g.n_ops = 1;
+  GemvArgs& a = g.op[0];
+  if (in_features == 0) {   // silu(0) * 0 = 0
+    a.y = h;
+    a.out = out_features;
+    return fill_bias(g, batch, sh);
+  }
+  a.w = static_cast<const uint8_t*>(w_gate);
+  a.w2 = static_cast<const uint8_t*>(w_up);
+  a.scales = gate_scales;
+  a.scales2 = up_scales;
+  a.out = out_features;
+  a.in = in_features;
+  a.row_bytes = rb;
+  a.units = units;
+  const int64_t pad = F::kPad;
+  a.xpad = ((a.in + pad - 1) / pad) * pad;
+  a.xstride = pesti::xs_stride(a.in, pad);
+  const size_t row_lds = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
+  const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
+  if (per_launch < 1) return PESTI_ERR_SHAPE;
+  for (int b0 = 0; b0 < batch; b0 += per_launch) {
+    const int nb = batch - b0 < per_launch ? batch - b0 : per_launch;
+    GroupArgs c = g;
+    c.op[0].x = x + static_cast<int64_t>(b0) * in_features;
+    c.op[0].y = h + static_cast<int64_t>(b0) * out_features;
+    const size_t lds = row_lds * nb;
+    int r;
+    if (units <= 16) r = launch_pair_b<F, 16>(c, nb, lds, sh);
+    else if (units <= 32) r = launch_pair_b<F, 32>(c, nb, lds, sh);
+    else r = launch_pair_b<F, 64>(c, nb, lds, sh);
+    if (r != PESTI_OK) return r;
+  }
+  return PESTI_OK;
+}
+
 }  // namespace pesti_gemv

@@ -7,4 +7,9 @@ int group_q6_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* str
   return group_dispatch<pesti::FmtQ6_K>(n_ops, ops, batch, stream);
 }
 
+int swiglu_q6_k(PESTI_SWIGLU_ARGS) {
+  return swiglu_dispatch<pesti::FmtQ6_K>(out_features, in_features, w_gate, w_up, gate_scales, up_scales, x,
+                                       h, batch, stream);
+}
+
 }  // namespace pesti_gemv

@@ -13,4 +13,12 @@ int group_q8_0(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* str
                : group_dispatch<pesti::FmtQ8_0>(n_ops, ops, batch, stream);
 }
 
+int swiglu_q8_0(PESTI_SWIGLU_ARGS) {
+  return in_features % 64 == 0
+             ? swiglu_dispatch<pesti::FmtQ8_0x2>(out_features, in_features, w_gate, w_up, gate_scales,
+                                                 up_scales, x, h, batch, stream)
+             : swiglu_dispatch<pesti::FmtQ8_0>(out_features, in_features, w_gate, w_up, gate_scales,
+                                               up_scales, x, h, batch, stream);
+}
+
 }  // namespace pesti_gemv

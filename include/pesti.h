@@ -134,6 +134,24 @@ typedef struct pesti_gemv_op {
 int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, int32_t batch,
                      void* stream);
 
+/* --- fused SwiGLU feed-forward input, h = silu(W_gate x) * (W_up x) ------
+ * The gate and up projections of a decode step's feed-forward block and
+ * the SwiGLU that joins them ("PESTI ..." README, "Conformance": SwiGLU =
+ * silu(gate) * up with the sigmoid-based SiLU, silu(g) = g / (1 + e^-g)),
+ * in one launch: each lane group computes row o of both matrices and writes
+ * only h[b][o].  w_gate and w_up are two matrices of one PESTI_FMT_* format
+ * and the same shape, laid out as for the single mat-vecs (no bias);
+ * gate_scales / up_scales are their row scales for PESTI_FMT_I8ROW and are
+ * ignored otherwise.  x float32 [batch][in], h float32 [batch][out].  Rows
+ * must fit one load round: in_features up to 4096 (Q4_K, Q6_K, i8row,
+ * Q8_0 with in % 64 == 0) or 2048 (other Q8_0), else PESTI_ERR_SHAPE.
+ * Bound: |h - exact| <= 1.1 * eg * |u| + |silu(g)| * eu + 2 * eg * eu
+ * + 1e-6 * |h| + 1e-6, with eg, eu the mat-vec bounds of g and u. */
+int pesti_gemv_swiglu(int32_t format, int64_t out_features, int64_t in_features,
+                      const void* w_gate, const void* w_up, const float* gate_scales,
+                      const float* up_scales, const float* x, float* h, int32_t batch,
+                      void* stream);
+
 /* --- small-M binary16 linear layer, Y = X W^T + b ------------------------
  * X binary16 [m][in], W binary16 [out][in] (the same row orientation as the
  * mat-vec; a GPT-2 c_attn "768x2304" has in = 768, out = 2304), Y float32

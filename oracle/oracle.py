@@ -268,6 +268,35 @@ def gemm_packed(fmt: str, packed, rows: int, in_features: int, x16, bias=None):
     return gemv_packed(fmt, packed, rows, in_features, x64, bias)
 
 
+def silu(g):
+    """SiLU with the sigmoid: silu(g) = g * sigmoid(g) = g / (1 + e^-g)
+    ("PESTI ..." README, "Conformance": SwiGLU = silu(gate) * up, the
+    sigmoid-based SiLU, not silu squared).  float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_packed(fmt: str, w_gate, w_up, rows: int, in_features: int, x,
+                  gate_scales=None, up_scales=None):
+    """The decode step's feed-forward input h = silu(W_gate x) * (W_up x)
+    (same passage): the two quantized mat-vecs, then SiLU and the product,
+    all in float64.  Returns h and the two mat-vecs' (value, error scale)
+    pairs, from which a tolerance is derived."""
+    g, sg = gemv_packed(fmt, w_gate, rows, in_features, x, None, gate_scales)
+    u, su = gemv_packed(fmt, w_up, rows, in_features, x, None, up_scales)
+    return silu(g) * u, (g, sg), (u, su)
+
+
+def swiglu_tolerance(g, sg, u, su, h, rel: float = 1e-4, abs_: float = 1e-6):
+    """Bound on |h_test - h| when g and u are each within rel * s + abs_:
+    |silu'| <= 1.1 everywhere, so |dh| <= 1.1 eg |u| + |silu(g)| eu +
+    2 eg eu, plus float32 rounding of the SiLU and the product."""
+    eg = rel * np.asarray(sg) + abs_
+    eu = rel * np.asarray(su) + abs_
+    return 1.1 * eg * np.abs(u) + np.abs(silu(g)) * eu + 2.0 * eg * eu + 1e-6 * np.abs(h) + 1e-6
+
+
 def within_tolerance(y_test, y_ref, s_ref, rel: float, abs_: float = 1e-6) -> np.ndarray:
     """Elementwise |y_test - y_ref| <= rel * s_ref + abs_ (s_ref from gemv)."""
     return np.abs(np.asarray(y_test, dtype=np.float64) - y_ref) <= rel * s_ref + abs_

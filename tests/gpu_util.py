@@ -107,3 +107,19 @@ def run_gemm_quant(fmt, packed, m, n, k, x16, bias=None):
     torch.cuda.synchronize()
     assert guards_intact(fbuf, m * n), "quantized GEMM wrote outside Y"
     return y_d.cpu().numpy().reshape(m, n)
+
+
+def run_swiglu(fmt, w_gate, w_up, gate_scales, up_scales, out, inf, x):
+    import dequantize_mat_vec_amd as dmv
+    torch, _ = torch_dev()
+    batch = x.shape[0]
+    g_d = to_dev(np.asarray(w_gate).reshape(-1).view(np.uint8))
+    u_d = to_dev(np.asarray(w_up).reshape(-1).view(np.uint8))
+    gs = to_dev(gate_scales.astype(np.float32)) if gate_scales is not None else None
+    us = to_dev(up_scales.astype(np.float32)) if up_scales is not None else None
+    x_d = to_dev(np.ascontiguousarray(x, dtype=np.float32))
+    fbuf, h_d = guarded_y(batch * out)
+    dmv.pesti_gemv_swiglu(fmt, out, inf, g_d, u_d, x_d, h_d, batch, gs, us)
+    torch.cuda.synchronize()
+    assert guards_intact(fbuf, batch * out), "SwiGLU wrote outside h"
+    return h_d.cpu().numpy().reshape(batch, out)

@@ -126,6 +126,27 @@ def test_gemm_quant_argument_checks(name):
     assert fn(4, 0, 64, None, None, None, None, None) == _lib.PESTI_OK
 
 
+def test_swiglu_argument_checks():
+    fn = _raw().pesti_gemv_swiglu
+    Q4, Q8, I8 = _lib.FORMAT_IDS["q4_k"], _lib.FORMAT_IDS["q8_0"], _lib.FORMAT_IDS["i8row"]
+    assert fn(9, 8, 64, FAKE, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(Q4, 8, 64, FAKE, FAKE, None, None, FAKE, FAKE, 9, None) == _lib.PESTI_ERR_BATCH
+    assert fn(Q4, 8, 64, FAKE, FAKE, None, None, FAKE, FAKE, -1, None) == _lib.PESTI_ERR_BATCH
+    assert fn(Q4, 8, 40, FAKE, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(Q4, 8, 4160, FAKE, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(Q8, 8, 2080, FAKE, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert fn(Q4, 8, 64, None, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(Q4, 8, 64, FAKE, None, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(Q4, 8, 64, FAKE, FAKE, None, None, None, FAKE, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(Q4, 8, 64, FAKE, FAKE, None, None, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(I8, 8, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_NULL
+    assert fn(Q4, 8, 64, FAKE + 8, FAKE, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(Q4, 8, 64, FAKE, FAKE + 8, None, None, FAKE, FAKE, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(Q4, 8, 64, FAKE, FAKE, None, None, FAKE, FAKE + 4, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert fn(Q4, 0, 64, None, None, None, None, None, None, 1, None) == _lib.PESTI_OK
+    assert fn(Q4, 8, 64, None, None, None, None, None, None, 0, None) == _lib.PESTI_OK
+
+
 @pytest.mark.parametrize("name", ["pesti_dequant_q8_0", "pesti_dequant_q4_k", "pesti_dequant_q6_k"])
 def test_dequant_argument_checks(name):
     fn = getattr(_raw(), name)

@@ -448,6 +448,44 @@ def test_gemm_packed_brute_force():
                 assert err <= Fraction(2.0 ** -50) * Fraction(float(s[m, n])) + Fraction(1, 2 ** 200)
 
 
+def test_silu_closed_forms():
+    """silu(0) = 0; silu(g) - silu(-g) = g (sigmoid(g) + sigmoid(-g) = 1);
+    silu(g) = g * scipy's logistic sigmoid; the tails go to g and to 0."""
+    from scipy.special import expit
+    g = np.linspace(-30, 30, 241)
+    assert oracle.silu(0.0) == 0.0
+    assert np.allclose(oracle.silu(g) - oracle.silu(-g), g, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.silu(g), g * expit(g), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(800.0) == 800.0 and oracle.silu(-800.0) == 0.0
+    # a known value: silu(1) = 1 / (1 + 1/e)
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+
+
+def test_swiglu_is_silu_of_gate_times_up():
+    """The fused result is the product of the two pinned mat-vecs through the
+    SiLU: swapping the roles of gate and up changes it, and a zero up matrix
+    (i8row codes 0) gives 0."""
+    rng = np.random.default_rng(17)
+    codes_g = rng.integers(-127, 128, size=(6, 64)).astype(np.int8)
+    codes_u = rng.integers(-127, 128, size=(6, 64)).astype(np.int8)
+    sc = np.full(6, 0.01, np.float32)
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    h, (g, _), (u, _) = oracle.swiglu_packed("i8row", codes_g.view(np.uint8), codes_u.view(np.uint8), 6, 64,
+                                             x, sc, sc)
+    g_ref, _ = oracle.gemv_packed("i8row", codes_g.view(np.uint8), 6, 64, x, None, sc)
+    u_ref, _ = oracle.gemv_packed("i8row", codes_u.view(np.uint8), 6, 64, x, None, sc)
+    assert np.array_equal(g, g_ref) and np.array_equal(u, u_ref)
+    for b in range(2):
+        for o in range(6):
+            ex = Fraction(float(g[b, o])) / (1 + Fraction(float(np.exp(-g[b, o])))) * Fraction(float(u[b, o]))
+            assert abs(Fraction(float(h[b, o])) - ex) <= Fraction(2.0 ** -50) * abs(ex) + Fraction(1, 2 ** 300)
+    h2, _, _ = oracle.swiglu_packed("i8row", codes_u.view(np.uint8), codes_g.view(np.uint8), 6, 64, x, sc, sc)
+    assert not np.allclose(h, h2)
+    h0, _, _ = oracle.swiglu_packed("i8row", codes_g.view(np.uint8), np.zeros_like(codes_u).view(np.uint8),
+                                    6, 64, x, sc, sc)
+    assert np.all(h0 == 0)
+
+
 def test_quantize_i8row_round_trip():
     rng = np.random.default_rng(14)
     w = rng.normal(0, 0.02, size=(32, 200)).astype(np.float32)
