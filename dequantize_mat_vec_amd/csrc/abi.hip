@@ -42,6 +42,7 @@ int64_t pesti_row_bytes(int32_t format, int64_t in_features) {
   switch (format) {
     case PESTI_FMT_Q8_0: return (in_features / 32) * 34;
     case PESTI_FMT_Q4_K: return ((in_features + 255) / 256) * 144;
+    case PESTI_FMT_Q5_K: return ((in_features + 255) / 256) * 176;
     case PESTI_FMT_Q6_K: return ((in_features + 255) / 256) * 210;
     case PESTI_FMT_I8ROW: return in_features;
     default: return -1;

@@ -5,8 +5,8 @@
 // points exist so the unpacking itself can be checked bit for bit.
 //
 // Exactness in float32: binary16 d has 11 significant bits, so d*q (Q8_0),
-// d*sc*(q-32) (Q6_K, |sc*(q-32)| <= 4096) and the two Q4_K terms d*sc*q and
-// dmin*m are exact; the Q4_K subtraction is the single rounding, and an FMA
+// d*sc*(q-32) (Q6_K, |sc*(q-32)| <= 4096) and the two Q4_K / Q5_K terms
+// d*sc*q and dmin*m are exact; their subtraction is the single rounding, and an FMA
 // of the exact product with the exact negated min rounds the same way.
 #include "common.h"
 
@@ -63,6 +63,38 @@ __global__ __launch_bounds__(256) void dequant_q4_k_kernel(DequantArgs a) {
   for (int k = 0; k < 32; ++k) {
     const float q = static_cast<float>((qs[k] >> shift) & 15u);
     o[k] = fmaf(dsc, q, -dmm);
+  }
+}
+
+// Q5_K: Q4_K's header and code runs, plus a fifth bit per weight: weight
+// 64r + 32c + l takes bit 2r + c of high-bit byte l (bytes 16..47); the
+// low-nibble runs start at byte 48.  d*sc*q (22 bits) and dmin*m are exact.
+__global__ __launch_bounds__(256) void dequant_q5_k_kernel(DequantArgs a) {
+  const int64_t nsub = a.in / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= a.rows * nsub) return;
+  const int64_t row = t / nsub, j = t % nsub;
+  const uint8_t* sb = a.w + row * a.row_bytes + (j / 8) * 176;
+  const int s = static_cast<int>(j % 8);   // sub-block = 2 * run + half
+  const float d = f16_at(sb), dmin = f16_at(sb + 2);
+  const uint8_t* S = sb + 4;
+  uint32_t sc, m;
+  if (s < 4) {
+    sc = S[s] & 63u;
+    m = S[s + 4] & 63u;
+  } else {
+    sc = (S[s + 4] & 15u) | ((S[s - 4] >> 6) << 4);
+    m = (S[s + 4] >> 4) | ((S[s] >> 6) << 4);
+  }
+  const float dsc = d * static_cast<float>(sc);
+  const float dmm = dmin * static_cast<float>(m);
+  const uint8_t* qh = sb + 16;
+  const uint8_t* qs = sb + 48 + 32 * (s / 2);
+  const int shift = (s & 1) ? 4 : 0;
+  float* o = a.out + row * a.in + j * 32;
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t q = ((qs[k] >> shift) & 15u) | (((qh[k] >> s) & 1u) << 4);
+    o[k] = fmaf(dsc, static_cast<float>(q), -dmm);
   }
 }
 
@@ -138,6 +170,12 @@ int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks, fl
                        void* stream) {
   return dequant_launch(pesti::dequant_q4_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,
                         ((in_features + 255) / 256) * 144, false);
+}
+
+int pesti_dequant_q5_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,
+                       void* stream) {
+  return dequant_launch(pesti::dequant_q5_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,
+                        ((in_features + 255) / 256) * 176, false);
 }
 
 int pesti_dequant_q6_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,

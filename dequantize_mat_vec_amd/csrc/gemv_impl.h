@@ -329,6 +329,113 @@ struct FmtQ4_K {
 };
 
 // ---------------------------------------------------------------------------
+// Q5_K: Q4_K's units (run g = u % 4 of super-block u / 4: sub-blocks 2g and
+// 2g+1) on 176-byte super-blocks whose codes have a fifth bit: weight
+// 64g + 32c + l takes bit 2g + c of high-bit byte l (bytes 16..47, shared by
+// the four runs); the runs' low nibbles start at byte 48.  Codes reach 31,
+// past the e4m3 nibble trick, so they convert with v_cvt_f32_ubyte (exact);
+// the scale gather is Q4_K's.
+// ---------------------------------------------------------------------------
+struct FmtQ5_K {
+  static constexpr bool kSums = true;
+  static constexpr int kPad = 256;
+  struct Raw { u32x4 hdr, ha, hb, qa, qb; };
+  using Lane = FmtQ4_K::Lane;
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+  __device__ static Lane lane_state(int sub) { return FmtQ4_K::lane_state(sub); }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* sbp = rp + (u >> 2) * 176;
+    const int g = static_cast<int>(u & 3);
+    r.hdr = load_u32x4_a16(sbp);
+    r.ha = load_u32x4_a16(sbp + 16);
+    r.hb = load_u32x4_a16(sbp + 32);
+    r.qa = load_u32x4_a16(sbp + 48 + 32 * g);
+    r.qb = load_u32x4_a16(sbp + 64 + 32 * g);
+  }
+
+  __device__ __forceinline__ static uint32_t high_word(const Raw& r, int t) {
+    switch (t) {
+      case 0: return r.ha.x;
+      case 1: return r.ha.y;
+      case 2: return r.ha.z;
+      case 3: return r.ha.w;
+      case 4: return r.hb.x;
+      case 5: return r.hb.y;
+      case 6: return r.hb.z;
+      default: return r.hb.w;
+    }
+  }
+  __device__ __forceinline__ static uint32_t code_word(const Raw& r, int t) {
+    switch (t) {
+      case 0: return r.qa.x;
+      case 1: return r.qa.y;
+      case 2: return r.qa.z;
+      case 3: return r.qa.w;
+      case 4: return r.qb.x;
+      case 5: return r.qb.y;
+      case 6: return r.qb.z;
+      default: return r.qb.w;
+    }
+  }
+
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const float* sums, int64_t nsub,
+                                                 const Lane& L, float* acc) {
+    float p0[R][B], p1[R][B];
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { p0[k][b] = 0.f; p1[k][b] = 0.f; }
+    const int x0 = 64 * u;
+    const uint32_t g2 = 2u * static_cast<uint32_t>(u & 3);   // fifth-bit position of the first half
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 xl[B], xh[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        xl[b] = xs4(xs + b * a.xstride, x0 + 4 * t);
+        xh[b] = xs4(xs + b * a.xstride, x0 + 32 + 4 * t);
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t q = code_word(r[k], t);
+        const uint32_t hq = high_word(r[k], t);
+        const uint32_t lo = (q & 0x0F0F0F0Fu) | (((hq >> g2) & 0x01010101u) << 4);
+        const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (((hq >> (g2 + 1u)) & 0x01010101u) << 4);
+        const float l0 = ubyte<0>(lo), l1 = ubyte<1>(lo), l2 = ubyte<2>(lo), l3 = ubyte<3>(lo);
+        const float h0 = ubyte<0>(hi), h1 = ubyte<1>(hi), h2 = ubyte<2>(hi), h3 = ubyte<3>(hi);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          p0[k][b] = fmaf(l0, xl[b].x, p0[k][b]); p0[k][b] = fmaf(l1, xl[b].y, p0[k][b]);
+          p0[k][b] = fmaf(l2, xl[b].z, p0[k][b]); p0[k][b] = fmaf(l3, xl[b].w, p0[k][b]);
+          p1[k][b] = fmaf(h0, xh[b].x, p1[k][b]); p1[k][b] = fmaf(h1, xh[b].y, p1[k][b]);
+          p1[k][b] = fmaf(h2, xh[b].z, p1[k][b]); p1[k][b] = fmaf(h3, xh[b].w, p1[k][b]);
+        }
+      }
+    }
+    const int j0 = 2 * u;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float ds0, ds1, dm0, dm1;
+      FmtQ4_K::scales(r[k].hdr, L, ds0, ds1, dm0, dm1);   // d*sc*2^9: Q4_K's codes carry 2^-9
+      ds0 *= 1.0f / 512.0f;
+      ds1 *= 1.0f / 512.0f;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* sb_sums = sums + b * nsub;
+        float v = ds0 * p0[k][b];
+        v = fmaf(ds1, p1[k][b], v);
+        v = fmaf(-dm0, sb_sums[j0], v);
+        v = fmaf(-dm1, sb_sums[j0 + 1], v);
+        acc[k * B + b] += v;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Q6_K: unit u = super-block u/4, half h = (u/2)%2, column block c = u%2;
 // it covers weights 128h + 32g + 16c + [0, 16) for g = 0..3.  Super-blocks
 // are 210 bytes, so every other one starts 2 bytes past a dword boundary:
@@ -862,6 +969,9 @@ template <> inline void shape_of<pesti::FmtQ8_0>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtQ4_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 144; *u = (in + 63) / 64;
 }
+template <> inline void shape_of<pesti::FmtQ5_K>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 176; *u = (in + 63) / 64;
+}
 template <> inline void shape_of<pesti::FmtQ6_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 210; *u = ((in + 255) / 256) * 4;
 }
@@ -983,6 +1093,7 @@ namespace pesti_gemv {
 // (gemv_<format>.hip) so the kernels of the four formats compile in parallel.
 int group_q8_0(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q4_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+int group_q5_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q6_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 // Paired gate/up launches with the SwiGLU epilogue (swiglu_dispatch below).
@@ -992,6 +1103,7 @@ int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* st
       void *stream
 int swiglu_q8_0(PESTI_SWIGLU_ARGS);
 int swiglu_q4_k(PESTI_SWIGLU_ARGS);
+int swiglu_q5_k(PESTI_SWIGLU_ARGS);
 int swiglu_q6_k(PESTI_SWIGLU_ARGS);
 int swiglu_i8row(PESTI_SWIGLU_ARGS);
 

@@ -17,13 +17,16 @@
  *   Q4_K  144 B / 256 weights: binary16 d, binary16 dmin, 12 B of packed
  *          6-bit scales sc[8] and mins m[8], 128 B of 4-bit codes.
  *                                                  w = d*sc[j]*q - dmin*m[j]
+ *   Q5_K  176 B / 256 weights: d, dmin, the 12 scale/min bytes of Q4_K,
+ *          32 B of fifth bits, 128 B of low 4-bit codes (Q4_K's runs).
+ *                                                  w = d*sc[j]*q - dmin*m[j]
  *   Q6_K  210 B / 256 weights: 128 B low 4-bit parts, 64 B high 2-bit parts,
  *          int8 sc[16], binary16 d.                w = d*sc[i/16]*(q - 32)
  *   i8row int8 codes [out][in] plus one float32 scale per row. w = s[o]*q
  *
  * Layouts and conventions (every entry point)
  *   - W has out_features rows.  A packed row is ceil(in/QK) whole blocks
- *     (QK = 32 for Q8_0, 256 for Q4_K/Q6_K); rows follow each other with
+ *     (QK = 32 for Q8_0, 256 for Q4_K/Q5_K/Q6_K); rows follow each other with
  *     stride pesti_row_bytes(format, in_features) bytes.  When in_features
  *     is not a multiple of 256, the columns in_features..end of the last
  *     super-block are padding: they are never read into the result and
@@ -76,6 +79,7 @@ extern "C" {
 #define PESTI_FMT_Q4_K 1
 #define PESTI_FMT_Q6_K 2
 #define PESTI_FMT_I8ROW 3
+#define PESTI_FMT_Q5_K 4
 
 #define PESTI_MAX_BATCH 8
 #define PESTI_MAX_IN_FEATURES 32768
@@ -92,6 +96,13 @@ int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* block
 /* Q4_K (144-byte super-blocks of 256 weights, rows padded to whole
  * super-blocks).  Same arguments as pesti_gemv_q8_0. */
 int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+
+/* Q5_K (176-byte super-blocks of 256 weights, rows padded to whole
+ * super-blocks; "PESTI ..." README, "What This Is": all K-family
+ * quantizations).  Same arguments as pesti_gemv_q8_0. */
+int pesti_gemv_q5_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
 
@@ -189,10 +200,12 @@ int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
 /* --- dequantization to float32 (bit-exact; checks the unpacking) --------
  * w_out float32 [rows][in_features]: each weight rounded once from its
  * exact value (all formats here dequantize exactly in float32 except the
- * final subtraction of Q4_K and the scale product of i8row). */
+ * final subtraction of Q4_K / Q5_K and the scale product of i8row). */
 int pesti_dequant_q8_0(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_q5_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q6_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);

@@ -30,6 +30,12 @@ plainest reading of "GGUF parsing + dequantization ... verified byte-exact":
   pack eight 6-bit sub-block scales sc[j] and eight 6-bit mins m[j], then 128
   bytes of 4-bit codes.  Sub-block j holds weights 32j .. 32j+31.
   w[i] = d * sc[j] * q[i] - dmin * m[j].
+* Q5_K, 176 bytes per 256 weights: binary16 d, binary16 dmin, the same 12
+  bytes of 6-bit scales and mins as Q4_K, 32 bytes of high bits qh, then
+  128 bytes of low 4-bit codes in Q4_K's arrangement.  Weight 64r + l
+  (l < 32) has high bit r*2 of qh[l], weight 64r + 32 + l bit 2r+1.
+  w[i] = d * sc[j] * q[i] - dmin * m[j], q in 0..31.  (The pages name
+  "all K-family quantizations"; this is the GGUF arrangement.)
 * Q6_K, 210 bytes per 256 weights: 128 bytes of low 4-bit code parts, 64
   bytes of high 2-bit code parts, 16 int8 sub-block scales (16 weights
   each), binary16 d.   w[i] = d * sc[i // 16] * (q[i] - 32), q in 0..63.
@@ -42,7 +48,7 @@ the oracle drops them after decoding (their bytes may hold anything).
 
 All dequantized values are exact in float64 (binary16 d times a small
 integer, minus binary16 dmin times a 6-bit integer, needs at most 50
-significant bits), so float64 is the exact reference; the float32 value of a
+significant bits; Q5_K's 5-bit codes one more), so float64 is the exact reference; the float32 value of a
 weight is the float64 value rounded once to nearest-even.
 """
 from __future__ import annotations
@@ -52,8 +58,8 @@ import numpy as np
 QK8_0 = 32          # weights per Q8_0 block
 QK_K = 256          # weights per K-family super-block
 
-BLOCK_WEIGHTS = {"q8_0": QK8_0, "q4_k": QK_K, "q6_k": QK_K}
-BLOCK_BYTES = {"q8_0": 34, "q4_k": 144, "q6_k": 210}
+BLOCK_WEIGHTS = {"q8_0": QK8_0, "q4_k": QK_K, "q5_k": QK_K, "q6_k": QK_K}
+BLOCK_BYTES = {"q8_0": 34, "q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
 # ---------------------------------------------------------------------------
@@ -147,6 +153,36 @@ def dequant_q4_k(packed, rows: int, in_features: int) -> np.ndarray:
     return w.reshape(rows, -1)[:, :in_features]
 
 
+def q5_k_codes(qh: np.ndarray, qs: np.ndarray) -> np.ndarray:
+    """The 256 5-bit codes (0..31) of a Q5_K super-block: the low four bits
+    are the Q4_K codes of the 128 bytes qs; weight i = 64r + 32c + l (run r,
+    half c, l < 32) takes bit 2r + c of qh[l] as its fifth bit."""
+    low = q4_k_codes(qs)
+    qh = qh.astype(np.int64)
+    q = np.zeros_like(low)
+    for i in range(QK_K):
+        r, rest = divmod(i, 64)
+        c, l = divmod(rest, 32)
+        q[..., i] = low[..., i] | (((qh[..., l] >> (2 * r + c)) & 1) << 4)
+    return q
+
+
+def dequant_q5_k(packed, rows: int, in_features: int) -> np.ndarray:
+    """Q5_K: w = d * sc[j] * q - dmin * m[j] in sub-block j, q in 0..31.
+    float64 [rows, in]."""
+    if in_features % 32:
+        raise ValueError("Q5_K needs in_features % 32 == 0")
+    blk = _blocks(packed, rows, in_features, "q5_k")
+    d = _binary16(blk[:, :, 0:2])
+    dmin = _binary16(blk[:, :, 2:4])
+    sc, m = q4_k_scales_mins(blk[:, :, 4:16])
+    q = q5_k_codes(blk[:, :, 16:48], blk[:, :, 48:176])
+    sub = np.arange(QK_K) // 32
+    w = (d[:, :, None] * sc[:, :, sub] * q
+         - dmin[:, :, None] * m[:, :, sub])
+    return w.reshape(rows, -1)[:, :in_features]
+
+
 def q6_k_codes(ql: np.ndarray, qh: np.ndarray) -> np.ndarray:
     """The 256 6-bit codes (0..63) of a Q6_K super-block.
     Write i = 128*h + 32*g + l (h in 0..1, g in 0..3, l in 0..31).  The low
@@ -196,6 +232,8 @@ def dequantize(fmt: str, packed, rows: int, in_features: int, scales=None) -> np
         return dequant_q8_0(packed, rows, in_features)
     if fmt == "q4_k":
         return dequant_q4_k(packed, rows, in_features)
+    if fmt == "q5_k":
+        return dequant_q5_k(packed, rows, in_features)
     if fmt == "q6_k":
         return dequant_q6_k(packed, rows, in_features)
     if fmt == "i8row":

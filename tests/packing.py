@@ -65,6 +65,26 @@ def pack_q4_k_block(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
     return bytes(buf)
 
 
+def pack_q5_k_block(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
+    """176 bytes: d, dmin, packed scales/mins (as Q4_K), 32 high-bit bytes,
+    128 low-nibble bytes.  Weight 64r + 32c + l (l < 32) keeps its low four
+    bits in the low (c = 0) or high (c = 1) nibble of low byte 32r + l, and
+    its fifth bit at bit 2r + c of high-bit byte l."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    buf = bytearray(176)
+    _put_u16(buf, 0, d_bits)
+    _put_u16(buf, 2, dmin_bits)
+    buf[4:16] = pack_q4_k_scales(sc, m)
+    for r in range(4):
+        for c in range(2):
+            for l in range(32):
+                v = q[64 * r + 32 * c + l]
+                buf[48 + 32 * r + l] |= (v & 0xF) << (4 * c)
+                buf[16 + l] |= (v >> 4) << (2 * r + c)
+    return bytes(buf)
+
+
 def pack_q6_k_block(d_bits: int, sc, q) -> bytes:
     """210 bytes: 128 low-part bytes, 64 high-part bytes, 16 int8 scales, d.
     Weight i = 128h + 32g + l keeps its low four bits in the low (g < 2) or

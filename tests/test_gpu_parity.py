@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 GEMV_REL = 1e-4
 GEMM_REL = 2e-3
-FORMATS = ("q8_0", "q4_k", "q6_k", "i8row")
+FORMATS = ("q8_0", "q4_k", "q5_k", "q6_k", "i8row")
 
 
 @pytest.fixture(autouse=True)
@@ -52,7 +52,7 @@ def test_dequant_bit_exact(fmt, rows, inf):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
 def test_dequant_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([5, d_bits])
@@ -145,16 +145,23 @@ def test_power_of_two_scaling_is_exact(fmt):
     assert np.array_equal(y2, y1 * np.float32(8.0))
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
 def test_padding_bytes_do_not_matter(fmt):
     """Rows of 896 hold 3.5 super-blocks; the padding half must be ignored."""
     out, inf = 33, 896
     packed, _, x, bias = make(fmt, out, inf, 7)
     rng = np.random.default_rng(99)
     other = packed.copy().reshape(out, -1)
-    nb = 144 if fmt == "q4_k" else 210
+    nb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}[fmt]
     last = other[:, 3 * nb:4 * nb]
-    if fmt == "q4_k":
+    if fmt == "q5_k":
+        last[:, 48 + 64:] = rng.integers(0, 256, last[:, 48 + 64:].shape, dtype=np.uint8)
+        last[:, 16:48] = (last[:, 16:48] & 0x0F) | (rng.integers(0, 16, last[:, 16:48].shape,
+                                                               dtype=np.uint8) << 4)
+        last[:, 12:16] = rng.integers(0, 256, last[:, 12:16].shape, dtype=np.uint8)
+        last[:, 4:12] = (last[:, 4:12] & 0x3F) | (rng.integers(0, 4, last[:, 4:12].shape,
+                                                             dtype=np.uint8) << 6)
+    elif fmt == "q4_k":
         last[:, 16 + 64:] = rng.integers(0, 256, last[:, 16 + 64:].shape, dtype=np.uint8)
         last[:, 12:16] = rng.integers(0, 256, last[:, 12:16].shape, dtype=np.uint8)
         last[:, 4:12] = (last[:, 4:12] & 0x3F) | (rng.integers(0, 4, last[:, 4:12].shape,
@@ -196,7 +203,7 @@ def test_empty_output_touches_nothing(fmt):
     assert guards_intact(fbuf, 0)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
 def test_gemv_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([9, d_bits])
@@ -251,7 +258,8 @@ FULL = [("q8_0", synth.QWEN_VOCAB, 896, 1), ("q8_0", synth.QWEN_VOCAB, 896, 8),
         ("q4_k", synth.QWEN_VOCAB, 896, 4), ("q6_k", synth.QWEN_VOCAB, 896, 2),
         ("q8_0", synth.GPT2_VOCAB, 768, 1),
         ("q4_k", 4864, 896, 1), ("q4_k", 896, 4864, 1), ("q6_k", 896, 4864, 1),
-        ("q4_k", 128, 896, 1), ("i8row", 896, 896, 1)]
+        ("q4_k", 128, 896, 1), ("i8row", 896, 896, 1),
+        ("q5_k", synth.QWEN_VOCAB, 896, 1), ("q5_k", 4864, 896, 1), ("q5_k", 896, 4864, 3)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", FULL)
@@ -487,7 +495,8 @@ def test_group_equals_single_calls_bitwise():
 TALL = [("q8_0", 65536 + 37, 64, 1), ("q8_0", 131072 + 53, 64, 3), ("q8_0", 131072 + 11, 96, 1),
         ("q4_k", 65536 + 37, 256, 2), ("q4_k", 131072 + 53, 896, 1), ("q4_k", 65536 + 29, 1280, 1),
         ("q6_k", 65536 + 37, 256, 1), ("q6_k", 131072 + 53, 256, 8), ("q6_k", 65536 + 5, 1280, 1),
-        ("i8row", 131072 + 53, 64, 1), ("i8row", 65536 + 37, 160, 4)]
+        ("i8row", 131072 + 53, 64, 1), ("i8row", 65536 + 37, 160, 4),
+        ("q5_k", 65536 + 37, 256, 2), ("q5_k", 131072 + 53, 896, 1)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", TALL)

@@ -4,7 +4,7 @@ The oracle is checked against things other than itself:
 * hand-worked fixtures under tests/golden/ (values derived by hand from the
   block definitions, with the derivation in each file);
 * fields packed by an independent forward packer (tests/packing.py) and the
-  closed forms w = d*sc*q - dmin*m (Q4_K), d*sc*(q-32) (Q6_K), d*q (Q8_0),
+  closed forms w = d*sc*q - dmin*m (Q4_K, Q5_K), d*sc*(q-32) (Q6_K), d*q (Q8_0),
   scale*q (int8) evaluated in exact rationals;
 * one-hot codes, which pin each weight's position;
 * exact rational mat-vec (brute force) on 4x32 .. 8x256 matrices;
@@ -67,6 +67,12 @@ def random_q4_k_fields(rng):
             [int(v) for v in rng.integers(0, 16, 256)])
 
 
+def random_q5_k_fields(rng):
+    return (random_f16_bits(rng, 1)[0], random_f16_bits(rng, 1)[0],
+            [int(v) for v in rng.integers(0, 64, 8)], [int(v) for v in rng.integers(0, 64, 8)],
+            [int(v) for v in rng.integers(0, 32, 256)])
+
+
 def random_q6_k_fields(rng):
     return (random_f16_bits(rng, 1)[0], [int(v) for v in rng.integers(-128, 128, 16)],
             [int(v) for v in rng.integers(0, 64, 256)])
@@ -114,7 +120,7 @@ def test_golden_fixture(name):
 
 def test_fixture_set_covers_every_format():
     fmts = {golden_io.load(n)["format"] for n in golden_io.all_fixtures()}
-    assert fmts == {"q8_0", "q4_k", "q6_k", "i8row"}
+    assert fmts == {"q8_0", "q4_k", "q5_k", "q6_k", "i8row"}
 
 
 # ---------------------------------------------------------------------------
@@ -135,6 +141,23 @@ def test_q4_k_fields_and_closed_form(seed):
         assert list(oracle.q4_k_codes(raw[16:144])) == q
     data = packing.rows_to_array([blocks[:4], blocks[4:]])
     w = oracle.dequant_q4_k(data, 2, 1024)
+    assert as_fraction_array(w) == exact
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_q5_k_fields_and_closed_form(seed):
+    rng = np.random.default_rng([21, seed])
+    blocks, exact = [], []
+    for _ in range(6):
+        d, dmin, sc, m, q = random_q5_k_fields(rng)
+        blocks.append(packing.pack_q5_k_block(d, dmin, sc, m, q))
+        exact.extend(q4_k_exact(d, dmin, sc, m, q))   # same closed form, q in 0..31
+        raw = np.frombuffer(blocks[-1], dtype=np.uint8)
+        sc_o, m_o = oracle.q4_k_scales_mins(raw[4:16])
+        assert list(sc_o) == sc and list(m_o) == m
+        assert list(oracle.q5_k_codes(raw[16:48], raw[48:176])) == q
+    data = packing.rows_to_array([blocks[:3], blocks[3:]])
+    w = oracle.dequant_q5_k(data, 2, 768)
     assert as_fraction_array(w) == exact
 
 
@@ -194,6 +217,18 @@ def test_q4_k_one_hot_positions():
         assert list(nz) == [i] and w[i] == 9 * sc[i // 32], i
 
 
+def test_q5_k_one_hot_positions():
+    """Code 25 (fifth bit set, low nibble 9) at one position, zero elsewhere."""
+    sc = [1, 2, 3, 4, 5, 6, 7, 8]
+    for i in range(256):
+        q = [0] * 256
+        q[i] = 25
+        blk = packing.pack_q5_k_block(0x3C00, 0x0000, sc, [5] * 8, q)
+        w = oracle.dequant_q5_k(np.frombuffer(blk, dtype=np.uint8), 1, 256)[0]
+        nz = np.flatnonzero(w)
+        assert list(nz) == [i] and w[i] == 25 * sc[i // 32], i
+
+
 def test_q6_k_one_hot_positions():
     sc = list(range(1, 17))
     for i in range(256):
@@ -236,6 +271,28 @@ def test_q4_k_special_cases():
     assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * sc[i // 32] * q[i] for i in range(256)]
 
 
+def test_q5_k_special_cases():
+    rng = np.random.default_rng(22)
+    _, _, sc, m, q = random_q5_k_fields(rng)
+    d, dmin = 0x3555, 0x2AAA
+    pack = packing.pack_q5_k_block
+    # q = 0 -> -dmin*m; q = 16 (fifth bit alone) -> 16 d sc - dmin m
+    for qv in (0, 16, 31):
+        w = oracle.dequant_q5_k(np.frombuffer(pack(d, dmin, sc, m, [qv] * 256), np.uint8), 1, 256)[0]
+        assert as_fraction_array(w) == [f16_value(d) * sc[i // 32] * qv - f16_value(dmin) * m[i // 32]
+                                        for i in range(256)]
+    # the fifth bit of code q equals 16 * (q >> 4) on top of the Q4_K decode of the low nibbles
+    blk = np.frombuffer(pack(0x3C00, 0, sc, m, q), np.uint8)
+    low = [v & 15 for v in q]
+    blk4 = np.frombuffer(packing.pack_q4_k_block(0x3C00, 0, sc, m, low), np.uint8)
+    w5 = oracle.dequant_q5_k(blk, 1, 256)[0]
+    w4 = oracle.dequant_q4_k(blk4, 1, 256)[0]
+    assert np.array_equal(w5 - w4, np.array([16 * sc[i // 32] * (q[i] >> 4) for i in range(256)], float))
+    # subnormal d: w = 2^-24 * sc * q exactly
+    w = oracle.dequant_q5_k(np.frombuffer(pack(0x0001, 0, sc, m, q), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * sc[i // 32] * q[i] for i in range(256)]
+
+
 def test_q6_k_special_cases():
     rng = np.random.default_rng(8)
     _, sc, q = random_q6_k_fields(rng)
@@ -270,16 +327,20 @@ def _padding_masks_in128():
     q6[64:128] = 0xFF       # low parts of h = 1
     q6[128 + 32:192] = 0xFF  # high parts of h = 1
     q6[192 + 8:208] = 0xFF  # scales of sub-blocks 8..15
-    return {"q4_k": q4, "q6_k": q6}
+    q5 = np.zeros(176, dtype=np.uint8)
+    q5[4:16] = q4[4:16]     # the same scale/min bits as Q4_K
+    q5[16:48] = 0xF0        # fifth bits of runs 2 and 3
+    q5[48 + 64:176] = 0xFF  # low-nibble runs 2 and 3
+    return {"q4_k": q4, "q5_k": q5, "q6_k": q6}
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
 def test_padding_bytes_do_not_matter(fmt):
     rng = np.random.default_rng(11)
     mask = _padding_masks_in128()[fmt]
     nb = oracle.BLOCK_BYTES[fmt]
     base = rng.integers(0, 256, size=(3, nb), dtype=np.uint8)
-    d_off = 0 if fmt == "q4_k" else 208
+    d_off = 208 if fmt == "q6_k" else 0
     base[:, d_off:d_off + 2] = [0x00, 0x3C]           # d = 1.0
     w0 = oracle.dequantize(fmt, base, 3, 128)
     assert w0.shape == (3, 128)
@@ -323,6 +384,10 @@ def _build(fmt, rng, rows, in_features):
                 d, dmin, sc, m, q = random_q4_k_fields(rng)
                 blocks.append(packing.pack_q4_k_block(d, dmin, sc, m, q))
                 exact += q4_k_exact(d, dmin, sc, m, q)
+            elif fmt == "q5_k":
+                d, dmin, sc, m, q = random_q5_k_fields(rng)
+                blocks.append(packing.pack_q5_k_block(d, dmin, sc, m, q))
+                exact += q4_k_exact(d, dmin, sc, m, q)
             else:
                 d, sc, q = random_q6_k_fields(rng)
                 blocks.append(packing.pack_q6_k_block(d, sc, q))
@@ -334,7 +399,7 @@ def _build(fmt, rng, rows, in_features):
 
 BRUTE_CASES = [("q8_0", 4, 32), ("q8_0", 8, 64), ("q4_k", 4, 256), ("q4_k", 8, 256),
                ("q6_k", 4, 256), ("q6_k", 8, 256), ("q4_k", 4, 128), ("q6_k", 4, 128),
-               ("q4_k", 3, 384)]
+               ("q4_k", 3, 384), ("q5_k", 4, 256), ("q5_k", 3, 384), ("q5_k", 4, 128)]
 
 
 @pytest.mark.parametrize("fmt,rows,inf", BRUTE_CASES)
@@ -551,9 +616,21 @@ def test_planted_mistakes_are_caught(monkeypatch):
     def gemv_no_bias(w64, x, bias=None):
         return good_gemv(w64, x, None)
 
+    good_codes5 = mod.q5_k_codes
+
+    def codes5_half_swapped(qh, qs):   # fifth bits of the two halves of a run exchanged
+        q = good_codes5(qh, qs)
+        low = q & 15
+        high = q >> 4
+        out = q.copy()
+        for r in range(4):
+            out[..., 64 * r:64 * r + 32] = low[..., 64 * r:64 * r + 32] | (high[..., 64 * r + 32:64 * r + 64] << 4)
+            out[..., 64 * r + 32:64 * r + 64] = low[..., 64 * r + 32:64 * r + 64] | (high[..., 64 * r:64 * r + 32] << 4)
+        return out
+
     for name, bad in [("q4_k_codes", codes4_swapped), ("q4_k_scales_mins", sm_swapped),
                       ("q4_k_scales_mins", sm_no_high_bits), ("q6_k_codes", codes6_offset),
-                      ("gemv", gemv_no_bias)]:
+                      ("gemv", gemv_no_bias), ("q5_k_codes", codes5_half_swapped)]:
         monkeypatch.setattr(mod, name, bad)
         assert not _all_dequant_fixtures_pass(), name
         monkeypatch.undo()
