@@ -37,12 +37,14 @@ D_VARIANCE = 1e-3
 # binary16 scale fields inside the block).
 _GEOMETRY = {
     "q8_0": (32, 34, (0,)),
+    "q2_k": (256, 84, (80, 82)),
+    "q3_k": (256, 110, (108,)),
     "q4_k": (256, 144, (0, 2)),
     "q5_k": (256, 176, (0, 2)),
     "q6_k": (256, 210, (208,)),
 }
 
-FORMATS = ("q8_0", "q4_k", "q5_k", "q6_k", "i8row")
+FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row")
 
 
 def rng_for(config_idx: int, layer_idx: int = 0, tensor_idx: int = 0,
@@ -67,7 +69,7 @@ def f16_abs_normal(rng: np.random.Generator, shape, variance: float = D_VARIANCE
 
 def quant_blocks(fmt: str, rng: np.random.Generator, rows: int, in_features: int,
                  force_d=None) -> np.ndarray:
-    """Packed [rows, row_bytes] uint8 matrix in Q8_0, Q4_K, Q5_K or Q6_K.
+    """Packed [rows, row_bytes] uint8 matrix in Q8_0 or a K-family format.
 
     force_d: optional binary16 bit pattern (or array of patterns, cycled over
     the blocks) written into every scale field instead of random draws - used

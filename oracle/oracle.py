@@ -36,6 +36,18 @@ plainest reading of "GGUF parsing + dequantization ... verified byte-exact":
   (l < 32) has high bit r*2 of qh[l], weight 64r + 32 + l bit 2r+1.
   w[i] = d * sc[j] * q[i] - dmin * m[j], q in 0..31.  (The pages name
   "all K-family quantizations"; this is the GGUF arrangement.)
+* Q2_K, 84 bytes per 256 weights: 16 bytes, one per 16-weight sub-block,
+  holding a 4-bit scale (low nibble) and a 4-bit min (high nibble); 64
+  bytes of 2-bit codes; binary16 d; binary16 dmin.  Weight 128h + 32j +
+  16c + l (h < 2, j < 4, c < 2, l < 16) is bits 2j, 2j+1 of code byte
+  32h + 16c + l, in sub-block 8h + 2j + c.  w = d*sc*q - dmin*m, q in 0..3.
+* Q3_K, 110 bytes per 256 weights: 32 bytes of high bits, 64 bytes of
+  2-bit codes (arranged as in Q2_K), 12 bytes packing sixteen 6-bit scales,
+  binary16 d.  Weight 128h + 32j + 16c + l has its low two bits as in Q2_K
+  and its high bit at bit 4h + j of high-bit byte 16c + l; its code is the
+  low two bits, minus 4 when the high bit is clear (q in -4..3).  Scale k:
+  bits 0-3 are bits 4(k // 8) .. +3 of byte k % 8, bits 4-5 are bits
+  2(k // 4) .. +1 of byte 8 + k % 4; w = d * (scale - 32) * q.
 * Q6_K, 210 bytes per 256 weights: 128 bytes of low 4-bit code parts, 64
   bytes of high 2-bit code parts, 16 int8 sub-block scales (16 weights
   each), binary16 d.   w[i] = d * sc[i // 16] * (q[i] - 32), q in 0..63.
@@ -48,8 +60,8 @@ the oracle drops them after decoding (their bytes may hold anything).
 
 All dequantized values are exact in float64 (binary16 d times a small
 integer, minus binary16 dmin times a 6-bit integer, needs at most 50
-significant bits; Q5_K's 5-bit codes one more), so float64 is the exact reference; the float32 value of a
-weight is the float64 value rounded once to nearest-even.
+significant bits; Q5_K's 5-bit codes one more; Q2_K and Q3_K fewer), so
+float64 is the exact reference; the float32 value of a weight is the float64 value rounded once to nearest-even.
 """
 from __future__ import annotations
 
@@ -58,8 +70,8 @@ import numpy as np
 QK8_0 = 32          # weights per Q8_0 block
 QK_K = 256          # weights per K-family super-block
 
-BLOCK_WEIGHTS = {"q8_0": QK8_0, "q4_k": QK_K, "q5_k": QK_K, "q6_k": QK_K}
-BLOCK_BYTES = {"q8_0": 34, "q4_k": 144, "q5_k": 176, "q6_k": 210}
+BLOCK_WEIGHTS = {"q8_0": QK8_0, "q2_k": QK_K, "q3_k": QK_K, "q4_k": QK_K, "q5_k": QK_K, "q6_k": QK_K}
+BLOCK_BYTES = {"q8_0": 34, "q2_k": 84, "q3_k": 110, "q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
 # ---------------------------------------------------------------------------
@@ -103,6 +115,80 @@ def dequant_q8_0(packed, rows: int, in_features: int) -> np.ndarray:
     d = _binary16(blk[:, :, 0:2])                       # [rows, nblk]
     q = blk[:, :, 2:34].view(np.int8).astype(np.float64)  # [rows, nblk, 32]
     w = d[:, :, None] * q
+    return w.reshape(rows, -1)[:, :in_features]
+
+
+def q2_k_codes(qs: np.ndarray) -> np.ndarray:
+    """The 256 2-bit codes (0..3) of a Q2_K or the low bits of a Q3_K
+    super-block from its 64 code bytes: weight i = 128h + 32j + 16c + l
+    takes bits 2j, 2j+1 of byte 32h + 16c + l."""
+    qs = qs.astype(np.int64)
+    q = np.zeros(qs.shape[:-1] + (QK_K,), dtype=np.int64)
+    for i in range(QK_K):
+        h, rest = divmod(i, 128)
+        j, rest = divmod(rest, 32)
+        c, l = divmod(rest, 16)
+        q[..., i] = (qs[..., 32 * h + 16 * c + l] >> (2 * j)) & 3
+    return q
+
+
+def dequant_q2_k(packed, rows: int, in_features: int) -> np.ndarray:
+    """Q2_K: w = d * sc[s] * q - dmin * m[s] over 16-weight sub-blocks s
+    (sc, m the nibbles of scale byte s).  float64 [rows, in]."""
+    if in_features % 32:
+        raise ValueError("Q2_K needs in_features % 32 == 0")
+    blk = _blocks(packed, rows, in_features, "q2_k")
+    S = blk[:, :, 0:16].astype(np.int64)
+    sc, m = S & 15, S >> 4
+    q = q2_k_codes(blk[:, :, 16:80])
+    d = _binary16(blk[:, :, 80:82])
+    dmin = _binary16(blk[:, :, 82:84])
+    sub = np.arange(QK_K) // 16
+    w = d[:, :, None] * sc[:, :, sub] * q - dmin[:, :, None] * m[:, :, sub]
+    return w.reshape(rows, -1)[:, :in_features]
+
+
+def q3_k_scales(S: np.ndarray) -> np.ndarray:
+    """The sixteen 6-bit scales (0..63, before the -32 offset) of a Q3_K
+    super-block from its 12 scale bytes: scale k has bits 0-3 from bits
+    4(k // 8) .. +3 of byte k % 8 and bits 4-5 from bits 2(k // 4) .. +1 of
+    byte 8 + k % 4."""
+    S = S.astype(np.int64)
+    out = np.zeros(S.shape[:-1] + (16,), dtype=np.int64)
+    for k in range(16):
+        low = (S[..., k % 8] >> (4 * (k // 8))) & 15
+        high = (S[..., 8 + k % 4] >> (2 * (k // 4))) & 3
+        out[..., k] = low | (high << 4)
+    return out
+
+
+def q3_k_codes(hm: np.ndarray, qs: np.ndarray) -> np.ndarray:
+    """The 256 signed 3-bit codes (-4..3) of a Q3_K super-block: the Q2_K
+    arrangement's low two bits, minus 4 where the high bit (bit 4h + j of
+    high-bit byte 16c + l) is clear."""
+    low = q2_k_codes(qs)
+    hm = hm.astype(np.int64)
+    q = np.zeros_like(low)
+    for i in range(QK_K):
+        h, rest = divmod(i, 128)
+        j, rest = divmod(rest, 32)
+        c, l = divmod(rest, 16)
+        hbit = (hm[..., 16 * c + l] >> (4 * h + j)) & 1
+        q[..., i] = low[..., i] - 4 * (1 - hbit)
+    return q
+
+
+def dequant_q3_k(packed, rows: int, in_features: int) -> np.ndarray:
+    """Q3_K: w = d * (scale[s] - 32) * q over 16-weight sub-blocks s.
+    float64 [rows, in]."""
+    if in_features % 32:
+        raise ValueError("Q3_K needs in_features % 32 == 0")
+    blk = _blocks(packed, rows, in_features, "q3_k")
+    q = q3_k_codes(blk[:, :, 0:32], blk[:, :, 32:96])
+    sc = q3_k_scales(blk[:, :, 96:108]) - 32
+    d = _binary16(blk[:, :, 108:110])
+    sub = np.arange(QK_K) // 16
+    w = d[:, :, None] * sc[:, :, sub] * q
     return w.reshape(rows, -1)[:, :in_features]
 
 
@@ -230,6 +316,10 @@ def dequantize(fmt: str, packed, rows: int, in_features: int, scales=None) -> np
     """Exact float64 weights [rows, in_features] of a packed matrix."""
     if fmt == "q8_0":
         return dequant_q8_0(packed, rows, in_features)
+    if fmt == "q2_k":
+        return dequant_q2_k(packed, rows, in_features)
+    if fmt == "q3_k":
+        return dequant_q3_k(packed, rows, in_features)
     if fmt == "q4_k":
         return dequant_q4_k(packed, rows, in_features)
     if fmt == "q5_k":

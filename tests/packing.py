@@ -85,6 +85,52 @@ def pack_q5_k_block(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
     return bytes(buf)
 
 
+def pack_q2_k_block(d_bits: int, dmin_bits: int, sc, m, q) -> bytes:
+    """84 bytes: 16 scale bytes (scale | min << 4, one per 16-weight
+    sub-block), 64 code bytes, d, dmin.  Weight 128h + 32j + 16c + l keeps
+    its 2-bit code at bit 2j of code byte 32h + 16c + l."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 4 for v in q)
+    assert len(sc) == 16 and len(m) == 16 and all(0 <= v < 16 for v in list(sc) + list(m))
+    buf = bytearray(84)
+    for s in range(16):
+        buf[s] = sc[s] | (m[s] << 4)
+    for h in range(2):
+        for j in range(4):
+            for c in range(2):
+                for l in range(16):
+                    buf[16 + 32 * h + 16 * c + l] |= q[128 * h + 32 * j + 16 * c + l] << (2 * j)
+    _put_u16(buf, 80, d_bits)
+    _put_u16(buf, 82, dmin_bits)
+    return bytes(buf)
+
+
+def pack_q3_k_block(d_bits: int, scales, q) -> bytes:
+    """110 bytes: 32 high-bit bytes, 64 low-bit bytes, 12 scale bytes, d.
+    A code q in -4..3 is stored as its low two bits (q, or q + 4 when
+    negative) at bit 2j of byte 32h + 16c + l and a high bit (set when
+    q >= 0) at bit 4h + j of high-bit byte 16c + l.  Scale k (0..63) keeps
+    bits 0-3 at bit 4(k // 8) of byte k % 8 and bits 4-5 at bit 2(k // 4) of
+    byte 8 + k % 4."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(-4 <= v <= 3 for v in q)
+    assert len(scales) == 16 and all(0 <= v < 64 for v in scales)
+    buf = bytearray(110)
+    for h in range(2):
+        for j in range(4):
+            for c in range(2):
+                for l in range(16):
+                    v = q[128 * h + 32 * j + 16 * c + l]
+                    buf[32 + 32 * h + 16 * c + l] |= (v if v >= 0 else v + 4) << (2 * j)
+                    if v >= 0:
+                        buf[16 * c + l] |= 1 << (4 * h + j)
+    for k in range(16):
+        buf[96 + k % 8] |= (scales[k] & 15) << (4 * (k // 8))
+        buf[96 + 8 + k % 4] |= (scales[k] >> 4) << (2 * (k // 4))
+    _put_u16(buf, 108, d_bits)
+    return bytes(buf)
+
+
 def pack_q6_k_block(d_bits: int, sc, q) -> bytes:
     """210 bytes: 128 low-part bytes, 64 high-part bytes, 16 int8 scales, d.
     Weight i = 128h + 32g + l keeps its low four bits in the low (g < 2) or

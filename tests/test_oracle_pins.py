@@ -73,6 +73,27 @@ def random_q5_k_fields(rng):
             [int(v) for v in rng.integers(0, 32, 256)])
 
 
+def q2_k_exact(d_bits, dmin_bits, sc, m, q):
+    d, dmin = f16_value(d_bits), f16_value(dmin_bits)
+    return [d * sc[i // 16] * q[i] - dmin * m[i // 16] for i in range(256)]
+
+
+def q3_k_exact(d_bits, scales, q):
+    d = f16_value(d_bits)
+    return [d * (scales[i // 16] - 32) * q[i] for i in range(256)]
+
+
+def random_q2_k_fields(rng):
+    return (random_f16_bits(rng, 1)[0], random_f16_bits(rng, 1)[0],
+            [int(v) for v in rng.integers(0, 16, 16)], [int(v) for v in rng.integers(0, 16, 16)],
+            [int(v) for v in rng.integers(0, 4, 256)])
+
+
+def random_q3_k_fields(rng):
+    return (random_f16_bits(rng, 1)[0], [int(v) for v in rng.integers(0, 64, 16)],
+            [int(v) for v in rng.integers(-4, 4, 256)])
+
+
 def random_q6_k_fields(rng):
     return (random_f16_bits(rng, 1)[0], [int(v) for v in rng.integers(-128, 128, 16)],
             [int(v) for v in rng.integers(0, 64, 256)])
@@ -120,7 +141,7 @@ def test_golden_fixture(name):
 
 def test_fixture_set_covers_every_format():
     fmts = {golden_io.load(n)["format"] for n in golden_io.all_fixtures()}
-    assert fmts == {"q8_0", "q4_k", "q5_k", "q6_k", "i8row"}
+    assert fmts == {"q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row"}
 
 
 # ---------------------------------------------------------------------------
@@ -142,6 +163,42 @@ def test_q4_k_fields_and_closed_form(seed):
     data = packing.rows_to_array([blocks[:4], blocks[4:]])
     w = oracle.dequant_q4_k(data, 2, 1024)
     assert as_fraction_array(w) == exact
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_q2_k_fields_and_closed_form(seed):
+    rng = np.random.default_rng([23, seed])
+    blocks, exact = [], []
+    for _ in range(6):
+        d, dmin, sc, m, q = random_q2_k_fields(rng)
+        blocks.append(packing.pack_q2_k_block(d, dmin, sc, m, q))
+        exact.extend(q2_k_exact(d, dmin, sc, m, q))
+        raw = np.frombuffer(blocks[-1], dtype=np.uint8)
+        assert list(oracle.q2_k_codes(raw[16:80])) == q
+    data = packing.rows_to_array([blocks[:3], blocks[3:]])
+    assert as_fraction_array(oracle.dequant_q2_k(data, 2, 768)) == exact
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_q3_k_fields_and_closed_form(seed):
+    rng = np.random.default_rng([24, seed])
+    blocks, exact = [], []
+    for _ in range(6):
+        d, scales, q = random_q3_k_fields(rng)
+        blocks.append(packing.pack_q3_k_block(d, scales, q))
+        exact.extend(q3_k_exact(d, scales, q))
+        raw = np.frombuffer(blocks[-1], dtype=np.uint8)
+        assert list(oracle.q3_k_scales(raw[96:108])) == scales
+        assert list(oracle.q3_k_codes(raw[0:32], raw[32:96])) == q
+    data = packing.rows_to_array([blocks[:3], blocks[3:]])
+    assert as_fraction_array(oracle.dequant_q3_k(data, 2, 768)) == exact
+
+
+def test_q3_k_scale_extremes_round_trip():
+    for k in range(16):
+        sc_in = [63 if i == k else 0 for i in range(16)]
+        raw = np.frombuffer(packing.pack_q3_k_block(0x3C00, sc_in, [0] * 256), dtype=np.uint8)
+        assert list(oracle.q3_k_scales(raw[96:108])) == sc_in
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -229,6 +286,27 @@ def test_q5_k_one_hot_positions():
         assert list(nz) == [i] and w[i] == 25 * sc[i // 32], i
 
 
+def test_q2_k_one_hot_positions():
+    sc = [min(k + 1, 15) for k in range(16)]
+    for i in range(256):
+        q = [0] * 256
+        q[i] = 3
+        blk = packing.pack_q2_k_block(0x3C00, 0x3C00, sc, [0] * 16, q)
+        w = oracle.dequant_q2_k(np.frombuffer(blk, dtype=np.uint8), 1, 256)[0]
+        assert list(np.flatnonzero(w)) == [i] and w[i] == 3 * sc[i // 16], i
+
+
+def test_q3_k_one_hot_positions():
+    """Code 0 everywhere (high bit set, low bits 0) but -3 at one position."""
+    scales = [33 + k for k in range(16)]     # scale - 32 = 1 .. 16
+    for i in range(256):
+        q = [0] * 256
+        q[i] = -3
+        blk = packing.pack_q3_k_block(0x3C00, scales, q)
+        w = oracle.dequant_q3_k(np.frombuffer(blk, dtype=np.uint8), 1, 256)[0]
+        assert list(np.flatnonzero(w)) == [i] and w[i] == -3 * (scales[i // 16] - 32), i
+
+
 def test_q6_k_one_hot_positions():
     sc = list(range(1, 17))
     for i in range(256):
@@ -293,6 +371,31 @@ def test_q5_k_special_cases():
     assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * sc[i // 32] * q[i] for i in range(256)]
 
 
+def test_q2_k_q3_k_special_cases():
+    rng = np.random.default_rng(25)
+    _, _, sc, m, q = random_q2_k_fields(rng)
+    # Q2_K: codes 0 -> -dmin*m; scale 0 -> constant -dmin*m per sub-block
+    w = oracle.dequant_q2_k(np.frombuffer(packing.pack_q2_k_block(0x3555, 0x2AAA, sc, m, [0] * 256),
+                                          np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [-f16_value(0x2AAA) * m[i // 16] for i in range(256)]
+    w = oracle.dequant_q2_k(np.frombuffer(packing.pack_q2_k_block(0x3555, 0x2AAA, [0] * 16, m, q),
+                                          np.uint8), 1, 256)[0]
+    for s in range(16):
+        assert np.all(w[16 * s:16 * s + 16] == w[16 * s])
+    # Q3_K: scale 32 -> 0 whatever the codes; code -4 (all bits clear) -> -4 d (scale - 32)
+    _, scales, q3 = random_q3_k_fields(rng)
+    w = oracle.dequant_q3_k(np.frombuffer(packing.pack_q3_k_block(0x3C00, [32] * 16, q3), np.uint8), 1, 256)[0]
+    assert np.all(w == 0)
+    raw = bytearray(110)
+    raw[96:108] = packing.pack_q3_k_block(0x3C00, scales, [0] * 256)[96:108]
+    raw[108:110] = bytes([0x00, 0x3C])
+    w = oracle.dequant_q3_k(np.frombuffer(bytes(raw), np.uint8), 1, 256)[0]
+    assert list(w) == [-4.0 * (scales[i // 16] - 32) for i in range(256)]
+    # subnormal d
+    w = oracle.dequant_q3_k(np.frombuffer(packing.pack_q3_k_block(0x0001, scales, q3), np.uint8), 1, 256)[0]
+    assert as_fraction_array(w) == [Fraction(1, 2 ** 24) * (scales[i // 16] - 32) * q3[i] for i in range(256)]
+
+
 def test_q6_k_special_cases():
     rng = np.random.default_rng(8)
     _, sc, q = random_q6_k_fields(rng)
@@ -331,16 +434,24 @@ def _padding_masks_in128():
     q5[4:16] = q4[4:16]     # the same scale/min bits as Q4_K
     q5[16:48] = 0xF0        # fifth bits of runs 2 and 3
     q5[48 + 64:176] = 0xFF  # low-nibble runs 2 and 3
-    return {"q4_k": q4, "q5_k": q5, "q6_k": q6}
+    q2 = np.zeros(84, dtype=np.uint8)
+    q2[8:16] = 0xFF         # scale/min bytes of sub-blocks 8..15
+    q2[16 + 32:80] = 0xFF   # code bytes of h = 1
+    q3 = np.zeros(110, dtype=np.uint8)
+    q3[0:32] = 0xF0         # high bits of h = 1
+    q3[32 + 32:96] = 0xFF   # low-bit bytes of h = 1
+    q3[96:104] = 0xF0       # low scale bits of sub-blocks 8..15
+    q3[104:108] = 0xF0      # high scale bits of sub-blocks 8..15
+    return {"q2_k": q2, "q3_k": q3, "q4_k": q4, "q5_k": q5, "q6_k": q6}
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q2_k", "q3_k", "q4_k", "q5_k", "q6_k"])
 def test_padding_bytes_do_not_matter(fmt):
     rng = np.random.default_rng(11)
     mask = _padding_masks_in128()[fmt]
     nb = oracle.BLOCK_BYTES[fmt]
     base = rng.integers(0, 256, size=(3, nb), dtype=np.uint8)
-    d_off = 208 if fmt == "q6_k" else 0
+    d_off = {"q6_k": 208, "q2_k": 80, "q3_k": 108}.get(fmt, 0)
     base[:, d_off:d_off + 2] = [0x00, 0x3C]           # d = 1.0
     w0 = oracle.dequantize(fmt, base, 3, 128)
     assert w0.shape == (3, 128)
@@ -384,6 +495,14 @@ def _build(fmt, rng, rows, in_features):
                 d, dmin, sc, m, q = random_q4_k_fields(rng)
                 blocks.append(packing.pack_q4_k_block(d, dmin, sc, m, q))
                 exact += q4_k_exact(d, dmin, sc, m, q)
+            elif fmt == "q2_k":
+                d, dmin, sc, m, q = random_q2_k_fields(rng)
+                blocks.append(packing.pack_q2_k_block(d, dmin, sc, m, q))
+                exact += q2_k_exact(d, dmin, sc, m, q)
+            elif fmt == "q3_k":
+                d, scales, q = random_q3_k_fields(rng)
+                blocks.append(packing.pack_q3_k_block(d, scales, q))
+                exact += q3_k_exact(d, scales, q)
             elif fmt == "q5_k":
                 d, dmin, sc, m, q = random_q5_k_fields(rng)
                 blocks.append(packing.pack_q5_k_block(d, dmin, sc, m, q))
@@ -399,7 +518,8 @@ def _build(fmt, rng, rows, in_features):
 
 BRUTE_CASES = [("q8_0", 4, 32), ("q8_0", 8, 64), ("q4_k", 4, 256), ("q4_k", 8, 256),
                ("q6_k", 4, 256), ("q6_k", 8, 256), ("q4_k", 4, 128), ("q6_k", 4, 128),
-               ("q4_k", 3, 384), ("q5_k", 4, 256), ("q5_k", 3, 384), ("q5_k", 4, 128)]
+               ("q4_k", 3, 384), ("q5_k", 4, 256), ("q5_k", 3, 384), ("q5_k", 4, 128),
+               ("q2_k", 4, 256), ("q2_k", 3, 384), ("q3_k", 4, 256), ("q3_k", 3, 384)]
 
 
 @pytest.mark.parametrize("fmt,rows,inf", BRUTE_CASES)
@@ -617,6 +737,18 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return good_gemv(w64, x, None)
 
     good_codes5 = mod.q5_k_codes
+    good_codes2, good_scales3 = mod.q2_k_codes, mod.q3_k_scales
+
+    def codes2_halves_swapped(qs):     # the 16-weight halves c = 0, 1 exchanged
+        q = good_codes2(qs)
+        out = q.copy()
+        for b in range(0, 256, 32):
+            out[..., b:b + 16], out[..., b + 16:b + 32] = q[..., b + 16:b + 32], q[..., b:b + 16]
+        return out
+
+    def scales3_halves_swapped(S):     # scales 0..7 and 8..15 exchanged
+        sc = good_scales3(S)
+        return np.concatenate([sc[..., 8:], sc[..., :8]], axis=-1)
 
     def codes5_half_swapped(qh, qs):   # fifth bits of the two halves of a run exchanged
         q = good_codes5(qh, qs)
@@ -630,7 +762,8 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     for name, bad in [("q4_k_codes", codes4_swapped), ("q4_k_scales_mins", sm_swapped),
                       ("q4_k_scales_mins", sm_no_high_bits), ("q6_k_codes", codes6_offset),
-                      ("gemv", gemv_no_bias), ("q5_k_codes", codes5_half_swapped)]:
+                      ("gemv", gemv_no_bias), ("q5_k_codes", codes5_half_swapped),
+                      ("q2_k_codes", codes2_halves_swapped), ("q3_k_scales", scales3_halves_swapped)]:
         monkeypatch.setattr(mod, name, bad)
         assert not _all_dequant_fixtures_pass(), name
         monkeypatch.undo()
