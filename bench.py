@@ -30,8 +30,8 @@ sys.path.insert(0, HERE)
 HBM_PEAK_GBS = 8000.0
 METRIC = "batch-1 dequant-GEMV HBM GB/s (% of peak), µs per Qwen2.5-0.5B decode step"
 CONFIG_INDEX = 2          # the decode-step workload
-NOMINAL_BYTES_PER_WEIGHT = {"q8_0": 34 / 32, "q4_k": 144 / 256, "q5_k": 176 / 256, "q6_k": 210 / 256,
-                            "i8row": 1.0}
+NOMINAL_BYTES_PER_WEIGHT = {"q8_0": 34 / 32, "q2_k": 84 / 256, "q3_k": 110 / 256, "q4_k": 144 / 256,
+                            "q5_k": 176 / 256, "q6_k": 210 / 256, "i8row": 1.0}
 
 
 def call_bytes(fmt, out, inf, batch, has_bias):
@@ -224,9 +224,10 @@ def suite_cases():
     for fmt in ("q8_0", "q4_k", "q6_k"):
         for b in (1, 2, 4, 8):
             cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
-    for b in (1, 8):
-        cases.append((f"q5_k lm-head 151936x896 b{b}", "gemv", ("q5_k", synth.QWEN_VOCAB, 896, b)))
-    cases.append(("q5_k 4864x896 b1 (gate/up)", "gemv", ("q5_k", 4864, 896, 1)))
+    for fmt in ("q2_k", "q3_k", "q5_k"):
+        for b in (1, 8):
+            cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
+        cases.append((f"{fmt} 4864x896 b1 (gate/up)", "gemv", (fmt, 4864, 896, 1)))
     cases.append(("q8_0 gpt2 lm-head 50257x768 b1", "gemv", ("q8_0", synth.GPT2_VOCAB, 768, 1)))
     # prompt-width products on quantized weights, with the binary16-weight
     # GEMM at the same shapes for comparison

@@ -14,6 +14,7 @@ from ._lib import (FORMAT_IDS, LIB_PATH, PESTI_ERR_ALIGN, PESTI_ERR_BATCH,  # no
                    pesti_stream_read, pesti_gemm_q8_0_smallm, pesti_gemm_q4_k_smallm,
                    pesti_gemm_q6_k_smallm, gemm_quant,
                    pesti_gemv_swiglu, pesti_gemv_q5_k, pesti_dequant_q5_k,
+                   pesti_gemv_q2_k, pesti_gemv_q3_k, pesti_dequant_q2_k, pesti_dequant_q3_k,
                    strerror)
 
 __all__ = [n for n in dir() if n.startswith("pesti_")] + [

@@ -23,7 +23,7 @@ PESTI_ERR_ALIGN = -4
 PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
 
-FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4}
+FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6}
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
@@ -31,6 +31,8 @@ _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
 _SIGNATURES = {
     "pesti_gemv_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_q2_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_q3_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
@@ -42,6 +44,8 @@ _SIGNATURES = {
     "pesti_gemm_q6_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_q2_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_q3_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
@@ -151,6 +155,14 @@ def pesti_gemv_q4_k(out_features, in_features, blocks, x, y, bias=None, batch=1,
     return _gemv("pesti_gemv_q4_k", out_features, in_features, blocks, x, y, bias, batch, stream)
 
 
+def pesti_gemv_q2_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q2_k", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
+def pesti_gemv_q3_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q3_k", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
 def pesti_gemv_q5_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
     return _gemv("pesti_gemv_q5_k", out_features, in_features, blocks, x, y, bias, batch, stream)
 
@@ -242,6 +254,14 @@ def pesti_dequant_q8_0(rows, in_features, blocks, w_out, stream=None):
 
 def pesti_dequant_q4_k(rows, in_features, blocks, w_out, stream=None):
     return _dequant("pesti_dequant_q4_k", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_q2_k(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q2_k", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_q3_k(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q3_k", rows, in_features, blocks, w_out, stream)
 
 
 def pesti_dequant_q5_k(rows, in_features, blocks, w_out, stream=None):

@@ -43,6 +43,8 @@ int64_t pesti_row_bytes(int32_t format, int64_t in_features) {
     case PESTI_FMT_Q8_0: return (in_features / 32) * 34;
     case PESTI_FMT_Q4_K: return ((in_features + 255) / 256) * 144;
     case PESTI_FMT_Q5_K: return ((in_features + 255) / 256) * 176;
+    case PESTI_FMT_Q2_K: return ((in_features + 255) / 256) * 84;
+    case PESTI_FMT_Q3_K: return ((in_features + 255) / 256) * 110;
     case PESTI_FMT_Q6_K: return ((in_features + 255) / 256) * 210;
     case PESTI_FMT_I8ROW: return in_features;
     default: return -1;

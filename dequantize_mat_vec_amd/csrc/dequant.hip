@@ -66,6 +66,54 @@ __global__ __launch_bounds__(256) void dequant_q4_k_kernel(DequantArgs a) {
   }
 }
 
+// Q2_K: one thread per 32 weights = two 16-weight sub-blocks s, s + 1 of
+// one j (weight 128h + 32j + 16c + l: bits 2j of code byte 32h + 16c + l,
+// sub-block 8h + 2j + c).  d*sc*q and dmin*m are exact.
+__global__ __launch_bounds__(256) void dequant_q2_k_kernel(DequantArgs a) {
+  const int64_t nsub = a.in / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= a.rows * nsub) return;
+  const int64_t row = t / nsub, jj = t % nsub;
+  const uint8_t* sb = a.w + row * a.row_bytes + (jj / 8) * 84;
+  const int g = static_cast<int>(jj % 8), h = g / 4, j = g % 4;   // weights 128h + 32j + [0, 32)
+  const float d = f16_at(sb + 80), dmin = f16_at(sb + 82);
+  float* o = a.out + row * a.in + jj * 32;
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t sc = sb[8 * h + 2 * j + c];
+    const float dsc = d * static_cast<float>(sc & 15u), dmm = dmin * static_cast<float>(sc >> 4);
+    for (int l = 0; l < 16; ++l) {
+      const uint32_t q = (sb[16 + 32 * h + 16 * c + l] >> (2 * j)) & 3u;
+      o[16 * c + l] = fmaf(dsc, static_cast<float>(q), -dmm);
+    }
+  }
+}
+
+// Q3_K: as Q2_K's arrangement, the code minus 4 where its high bit (bit
+// 4h + j of high-bit byte 16c + l) is clear, 6-bit scales minus 32.
+// d*(scale - 32)*q needs at most 20 bits: exact.
+__global__ __launch_bounds__(256) void dequant_q3_k_kernel(DequantArgs a) {
+  const int64_t nsub = a.in / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= a.rows * nsub) return;
+  const int64_t row = t / nsub, jj = t % nsub;
+  const uint8_t* sb = a.w + row * a.row_bytes + (jj / 8) * 110;
+  const int g = static_cast<int>(jj % 8), h = g / 4, j = g % 4;
+  const float d = f16_at(sb + 108);
+  const uint8_t* S = sb + 96;
+  float* o = a.out + row * a.in + jj * 32;
+  for (int c = 0; c < 2; ++c) {
+    const int k = 8 * h + 2 * j + c;
+    const int scale = static_cast<int>(((S[k % 8] >> (4 * (k / 8))) & 15u) |
+                                       (((S[8 + k % 4] >> (2 * (k / 4))) & 3u) << 4)) - 32;
+    const float ds = d * static_cast<float>(scale);
+    for (int l = 0; l < 16; ++l) {
+      const int low = (sb[32 + 32 * h + 16 * c + l] >> (2 * j)) & 3;
+      const int high = (sb[16 * c + l] >> (4 * h + j)) & 1;
+      o[16 * c + l] = ds * static_cast<float>(low - 4 * (1 - high));
+    }
+  }
+}
+
 // Q5_K: Q4_K's header and code runs, plus a fifth bit per weight: weight
 // 64r + 32c + l takes bit 2r + c of high-bit byte l (bytes 16..47); the
 // low-nibble runs start at byte 48.  d*sc*q (22 bits) and dmin*m are exact.
@@ -170,6 +218,18 @@ int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks, fl
                        void* stream) {
   return dequant_launch(pesti::dequant_q4_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,
                         ((in_features + 255) / 256) * 144, false);
+}
+
+int pesti_dequant_q2_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,
+                       void* stream) {
+  return dequant_launch(pesti::dequant_q2_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,
+                        ((in_features + 255) / 256) * 84, false);
+}
+
+int pesti_dequant_q3_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,
+                       void* stream) {
+  return dequant_launch(pesti::dequant_q3_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,
+                        ((in_features + 255) / 256) * 110, false);
 }
 
 int pesti_dequant_q5_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,

@@ -1,6 +1,6 @@
 // C entry points of the fused dequantize + mat-vec (kernels in gemv_impl.h,
-// instantiated per format in gemv_q8_0.hip, gemv_q4_k.hip, gemv_q5_k.hip,
-// gemv_q6_k.hip and gemv_i8row.hip).
+// instantiated per format in gemv_q8_0.hip, gemv_q2_k.hip, gemv_q3_k.hip,
+// gemv_q4_k.hip, gemv_q5_k.hip, gemv_q6_k.hip and gemv_i8row.hip).
 #include "gemv_impl.h"
 
 namespace pesti {
@@ -42,6 +42,8 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
     case PESTI_FMT_Q8_0: return pesti_gemv::group_q8_0(n_ops, ops, batch, stream);
     case PESTI_FMT_Q4_K: return pesti_gemv::group_q4_k(n_ops, ops, batch, stream);
     case PESTI_FMT_Q5_K: return pesti_gemv::group_q5_k(n_ops, ops, batch, stream);
+    case PESTI_FMT_Q2_K: return pesti_gemv::group_q2_k(n_ops, ops, batch, stream);
+    case PESTI_FMT_Q3_K: return pesti_gemv::group_q3_k(n_ops, ops, batch, stream);
     case PESTI_FMT_Q6_K: return pesti_gemv::group_q6_k(n_ops, ops, batch, stream);
     case PESTI_FMT_I8ROW: return pesti_gemv::group_i8row(n_ops, ops, batch, stream);
     default: return PESTI_ERR_SHAPE;
@@ -57,6 +59,12 @@ int pesti_gemv_swiglu(int32_t format, int64_t out_features, int64_t in_features,
                                      stream);
     case PESTI_FMT_Q4_K:
       return pesti_gemv::swiglu_q4_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
+                                     stream);
+    case PESTI_FMT_Q2_K:
+      return pesti_gemv::swiglu_q2_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
+                                     stream);
+    case PESTI_FMT_Q3_K:
+      return pesti_gemv::swiglu_q3_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
                                      stream);
     case PESTI_FMT_Q5_K:
       return pesti_gemv::swiglu_q5_k(out_features, in_features, w_gate, w_up, nullptr, nullptr, x, h, batch,
@@ -81,6 +89,18 @@ int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* block
                     float* y, const float* bias, int32_t batch, void* stream) {
   const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);
   return pesti_gemv::group_q4_k(1, &o, batch, stream);
+}
+
+int pesti_gemv_q2_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
+                    float* y, const float* bias, int32_t batch, void* stream) {
+  const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return pesti_gemv::group_q2_k(1, &o, batch, stream);
+}
+
+int pesti_gemv_q3_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
+                    float* y, const float* bias, int32_t batch, void* stream) {
+  const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return pesti_gemv::group_q3_k(1, &o, batch, stream);
 }
 
 int pesti_gemv_q5_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,

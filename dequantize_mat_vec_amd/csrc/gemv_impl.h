@@ -80,6 +80,7 @@ __device__ __forceinline__ void nibbles_x512(uint32_t v, float& a, float& b, flo
 // ---------------------------------------------------------------------------
 struct FmtQ8_0x2 {
   static constexpr bool kSums = false;
+  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t w[17]; };
   struct Lane {};
@@ -148,6 +149,7 @@ struct FmtQ8_0x2 {
 // ---------------------------------------------------------------------------
 struct FmtQ8_0 {
   static constexpr bool kSums = false;
+  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t w[9]; uint32_t s; };
   struct Lane {};
@@ -212,6 +214,7 @@ struct FmtQ8_0 {
 // ---------------------------------------------------------------------------
 struct FmtQ4_K {
   static constexpr bool kSums = true;
+  static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
   struct Raw { u32x4 hdr, qa, qb; };
   // Per lane (run g = sub % 4, sub-blocks 2g and 2g+1), byte selectors that
@@ -329,6 +332,167 @@ struct FmtQ4_K {
 };
 
 // ---------------------------------------------------------------------------
+// Q2_K and Q3_K share a unit: half h and column c of super-block u / 4
+// (h = (u >> 1) & 1, c = u & 1), i.e. code bytes 32h + 16c .. +15 of the
+// super-block, whose bits 2j, 2j+1 hold weights 128h + 32j + 16c + [0, 16)
+// (16-weight sub-block 8h + 2j + c) for j = 0..3.  A row has
+// 2 * ceil(in / 128) units, so every unit's super-block holds real weights
+// (padding weights inside a unit meet x = 0).  u % 4 is the lane's sub % 4.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4u2 __attribute__((ext_vector_type(4), aligned(2)));
+
+// Q2_K, 84-byte super-blocks: 16 scale bytes (4-bit scale, 4-bit min per
+// sub-block), 64 code bytes, d, dmin.  w = d*sc*q - dmin*m with q in 0..3:
+// the codes convert as e4m3 bytes (q * 2^-9, exact), the mins take the
+// staged 16-weight sums of x.
+struct FmtQ2_K {
+  static constexpr bool kSums = true;
+  static constexpr int kSumWidth = 16;
+  static constexpr int kPad = 256;
+  struct Raw { u32x4 q; uint32_t sc0, sc1, dd; };
+  struct Lane { uint32_t h, c; };
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+  __device__ static Lane lane_state(int sub) {
+    return Lane{static_cast<uint32_t>((sub >> 1) & 1), static_cast<uint32_t>(sub & 1)};
+  }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* sbp = rp + (u >> 2) * 84;
+    const int h = (u >> 1) & 1, c = u & 1;
+    r.q = load_u32x4(sbp + 16 + 32 * h + 16 * c);
+    r.sc0 = load_u32(sbp + 8 * h);       // scale bytes of sub-blocks 8h .. 8h+3
+    r.sc1 = load_u32(sbp + 8 * h + 4);   // and 8h+4 .. 8h+7
+    r.dd = load_u32(sbp + 80);           // d | dmin << 16
+  }
+
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const float* sums, int64_t nsub,
+                                                 const Lane& L, float* acc) {
+    const int x0 = 256 * (u >> 2) + 128 * static_cast<int>(L.h) + 16 * static_cast<int>(L.c);
+    const int s0 = 16 * (u >> 2) + 8 * static_cast<int>(L.h) + static_cast<int>(L.c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float p[R][B];
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int b = 0; b < B; ++b) p[k][b] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 xv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv[b] = xs4(xs + b * a.xstride, x0 + 32 * j + 4 * t);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          const uint32_t w = t == 0 ? r[k].q.x : (t == 1 ? r[k].q.y : (t == 2 ? r[k].q.z : r[k].q.w));
+          float q0, q1, q2, q3;
+          nibbles_x512((w >> (2 * j)) & 0x03030303u, q0, q1, q2, q3);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            p[k][b] = fmaf(q0, xv[b].x, p[k][b]); p[k][b] = fmaf(q1, xv[b].y, p[k][b]);
+            p[k][b] = fmaf(q2, xv[b].z, p[k][b]); p[k][b] = fmaf(q3, xv[b].w, p[k][b]);
+          }
+        }
+      }
+      // scale byte of sub-block 8h + 2j + c: byte 2j + c of the lane's eight
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t word = j < 2 ? r[k].sc0 : r[k].sc1;
+        const uint32_t sbyte_v = (word >> (8 * (2 * (j & 1) + L.c))) & 0xFFu;
+        const float ds = f16_lo(r[k].dd) * 512.0f * static_cast<float>(sbyte_v & 15u);
+        const float dm = f16_hi(r[k].dd) * static_cast<float>(sbyte_v >> 4);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float v = ds * p[k][b];
+          v = fmaf(-dm, sums[b * nsub + s0 + 2 * j], v);
+          acc[k * B + b] += v;
+        }
+      }
+    }
+  }
+};
+
+// Q3_K, 110-byte super-blocks (2-byte aligned every other one): 32
+// high-bit bytes, 64 low-bit bytes (the Q2_K arrangement), 12 scale bytes,
+// d.  Weight 128h + 32j + 16c + l has its high bit at bit 4h + j of
+// high-bit byte 16c + l; its code is the low two bits, minus 4 where the
+// high bit is clear - as a signed byte, low2 | 0xFC where clear (-4..-1),
+// converted with the signed-byte convert.  Scale k (6 bits, minus 32): bits
+// 0-3 at bit 4(k / 8) of byte k % 8, bits 4-5 at bit 2(k / 4) of byte
+// 8 + k % 4; w = d * (scale - 32) * q.
+struct FmtQ3_K {
+  static constexpr bool kSums = false;
+  static constexpr int kSumWidth = 32;
+  static constexpr int kPad = 256;
+  struct Raw { u32x4 q, hm; uint32_t s0, s1, s2, d; };
+  using Lane = FmtQ2_K::Lane;
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+  __device__ static Lane lane_state(int sub) { return FmtQ2_K::lane_state(sub); }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* sbp = rp + (u >> 2) * 110;
+    const int h = (u >> 1) & 1, c = u & 1;
+    const u32x4u2 qv = *reinterpret_cast<const u32x4u2*>(sbp + 32 + 32 * h + 16 * c);
+    const u32x4u2 hv = *reinterpret_cast<const u32x4u2*>(sbp + 16 * c);
+    r.q = u32x4{qv.x, qv.y, qv.z, qv.w};
+    r.hm = u32x4{hv.x, hv.y, hv.z, hv.w};
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+    r.s0 = *reinterpret_cast<const u32a2*>(sbp + 96);
+    r.s1 = *reinterpret_cast<const u32a2*>(sbp + 100);
+    r.s2 = *reinterpret_cast<const u32a2*>(sbp + 104);
+    r.d = load_u16(sbp + 108);
+  }
+
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const float*, int64_t,
+                                                 const Lane& L, float* acc) {
+    const int x0 = 256 * (u >> 2) + 128 * static_cast<int>(L.h) + 16 * static_cast<int>(L.c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hs = 4u * L.h + static_cast<uint32_t>(j);   // high-bit position
+      float p[R][B];
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int b = 0; b < B; ++b) p[k][b] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 xv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv[b] = xs4(xs + b * a.xstride, x0 + 32 * j + 4 * t);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          const uint32_t w = t == 0 ? r[k].q.x : (t == 1 ? r[k].q.y : (t == 2 ? r[k].q.z : r[k].q.w));
+          const uint32_t hw = t == 0 ? r[k].hm.x : (t == 1 ? r[k].hm.y : (t == 2 ? r[k].hm.z : r[k].hm.w));
+          const uint32_t low2 = (w >> (2 * j)) & 0x03030303u;
+          const uint32_t clear = (~(hw >> hs)) & 0x01010101u;   // 1 where the high bit is clear
+          const uint32_t qb = low2 | (clear * 0xFCu);            // signed bytes -4..3
+          const float q0 = sbyte<0>(qb), q1 = sbyte<1>(qb), q2 = sbyte<2>(qb), q3 = sbyte<3>(qb);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            p[k][b] = fmaf(q0, xv[b].x, p[k][b]); p[k][b] = fmaf(q1, xv[b].y, p[k][b]);
+            p[k][b] = fmaf(q2, xv[b].z, p[k][b]); p[k][b] = fmaf(q3, xv[b].w, p[k][b]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        // local scale index 8h + 2j + c: low bits in byte 2j + c (nibble h),
+        // high bits in byte 8 + 2(j % 2) + c at bit 4h + 2(j / 2)
+        const uint32_t lw = j < 2 ? r[k].s0 : r[k].s1;
+        const uint32_t lo4 = (lw >> (8 * (2 * (j & 1) + L.c) + 4 * L.h)) & 15u;
+        const uint32_t hi2 = (r[k].s2 >> (8 * (2 * (j & 1) + L.c) + 4 * L.h + 2 * (j >> 1))) & 3u;
+        const float ds = f16_lo(r[k].d) * static_cast<float>(static_cast<int>(lo4 | (hi2 << 4)) - 32);
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[k * B + b] = fmaf(ds, p[k][b], acc[k * B + b]);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Q5_K: Q4_K's units (run g = u % 4 of super-block u / 4: sub-blocks 2g and
 // 2g+1) on 176-byte super-blocks whose codes have a fifth bit: weight
 // 64g + 32c + l takes bit 2g + c of high-bit byte l (bytes 16..47, shared by
@@ -338,6 +502,7 @@ struct FmtQ4_K {
 // ---------------------------------------------------------------------------
 struct FmtQ5_K {
   static constexpr bool kSums = true;
+  static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
   struct Raw { u32x4 hdr, ha, hb, qa, qb; };
   using Lane = FmtQ4_K::Lane;
@@ -445,6 +610,7 @@ struct FmtQ5_K {
 // ---------------------------------------------------------------------------
 struct FmtQ6_K {
   static constexpr bool kSums = false;
+  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 256;
   // Three 20-byte windows (low parts of g = 0/2, of g = 1/3, high parts),
   // three dwords around the unit's scales, and d.
@@ -554,6 +720,7 @@ struct FmtQ6_K {
 // ---------------------------------------------------------------------------
 struct FmtI8Row {
   static constexpr bool kSums = false;
+  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t q[16]; };
   struct Lane {};
@@ -641,11 +808,12 @@ __device__ __forceinline__ void stage_load(const GemvArgs& a, int base, XChunk<B
   }
 }
 
-template <bool kSums, int B, int XS>
+template <bool kSums, int SW, int B, int XS>
 __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float* sums, int base,
                                             const XChunk<B, XS>& c) {
+  static_assert(SW == 16 || SW == 32, "sums over 16 or 32 weights");
   const int n4 = static_cast<int>(a.xpad >> 2);   // float4 slots per batch row
-  const int nsub = static_cast<int>(a.xpad >> 5);
+  const int nsub = static_cast<int>(a.xpad / SW);
   const int tid = static_cast<int>(threadIdx.x);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
@@ -659,8 +827,8 @@ __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float*
         float part = (v.x + v.y) + (v.z + v.w);
         part += dpp<0xB1>(part);    // lane ^ 1
         part += dpp<0x4E>(part);    // lane ^ 2
-        part += dpp<0x141>(part);   // lane i <-> 7 - i within 8
-        if ((tid & 7) == 0 && s < n4) sums[b * nsub + (s >> 3)] = part;
+        if constexpr (SW == 32) part += dpp<0x141>(part);   // lane i <-> 7 - i within 8
+        if ((tid & (SW / 4 - 1)) == 0 && s < n4) sums[b * nsub + s / (SW / 4)] = part;
       }
     }
   }
@@ -668,7 +836,7 @@ __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float*
 
 // Chunks after the first (rows longer than 1024, 2048 or 8192 weights for
 // XS = 1, 2, 8), one batch column at a time.
-template <bool kSums, int B, int XS>
+template <bool kSums, int SW, int B, int XS>
 __device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* sums, int from) {
   const int n4 = static_cast<int>(a.xpad >> 2);
   for (int base = from; base < n4; base += XS * kThreads) {
@@ -678,7 +846,7 @@ __device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* 
       ab.x = a.x + b * a.in;
       XChunk<1, XS> c;
       stage_load<1, XS>(ab, base, c);
-      stage_store<kSums, 1, XS>(ab, xs + b * a.xstride, sums + b * (a.xpad >> 5), base, c);
+      stage_store<kSums, SW, 1, XS>(ab, xs + b * a.xstride, sums + b * (a.xpad / SW), base, c);
     }
   }
 }
@@ -744,7 +912,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
   float* xs = lds;
   float* sums = lds + B * a.xstride;
-  const int64_t nsub = a.xpad / 32;
+  const int64_t nsub = a.xpad / F::kSumWidth;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -806,8 +974,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
       for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), r[j][k]);
     }
-    if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
-    stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
+    if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
+    stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < U; ++j)
@@ -820,8 +988,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     // stand-in load past the last unit keeps the loop branch-free.
     typename F::Raw ra[1], rb[1];
     issue_unit<F>(a, rp[0], unit(0), ra[0]);
-    if constexpr (kEarly) stage_store<F::kSums, B, XS>(a, xs, sums, 0, xc);
-    stage_rest<F::kSums, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
+    if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
+    stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
     for (int j = 0; j < ipt; j += 2) {
       issue_unit<F>(a, rp[0], unit(j + 1), rb[0]);
@@ -969,6 +1137,12 @@ template <> inline void shape_of<pesti::FmtQ8_0>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtQ4_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 144; *u = (in + 63) / 64;
 }
+template <> inline void shape_of<pesti::FmtQ2_K>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 84; *u = ((in + 127) / 128) * 2;
+}
+template <> inline void shape_of<pesti::FmtQ3_K>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 110; *u = ((in + 127) / 128) * 2;
+}
 template <> inline void shape_of<pesti::FmtQ5_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 176; *u = (in + 63) / 64;
 }
@@ -1043,7 +1217,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     const int64_t pad = F::kPad;
     a.xpad = ((a.in + pad - 1) / pad) * pad;
     a.xstride = pesti::xs_stride(a.in, pad);
-    const size_t r = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
+    const size_t r = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / F::kSumWidth : 0));
     if (r > row_lds) row_lds = r;
     if (a.units > max_units) max_units = a.units;
     if (a.out > max_out) max_out = a.out;
@@ -1093,6 +1267,8 @@ namespace pesti_gemv {
 // (gemv_<format>.hip) so the kernels of the four formats compile in parallel.
 int group_q8_0(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q4_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+int group_q2_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+int group_q3_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q5_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q6_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
@@ -1103,6 +1279,8 @@ int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* st
       void *stream
 int swiglu_q8_0(PESTI_SWIGLU_ARGS);
 int swiglu_q4_k(PESTI_SWIGLU_ARGS);
+int swiglu_q2_k(PESTI_SWIGLU_ARGS);
+int swiglu_q3_k(PESTI_SWIGLU_ARGS);
 int swiglu_q5_k(PESTI_SWIGLU_ARGS);
 int swiglu_q6_k(PESTI_SWIGLU_ARGS);
 int swiglu_i8row(PESTI_SWIGLU_ARGS);
@@ -1167,7 +1345,7 @@ int swiglu_dispatch(int64_t out_features, int64_t in_features, const void* w_gat
   const int64_t pad = F::kPad;
   a.xpad = ((a.in + pad - 1) / pad) * pad;
   a.xstride = pesti::xs_stride(a.in, pad);
-  const size_t row_lds = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / 32 : 0));
+  const size_t row_lds = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / F::kSumWidth : 0));
   const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
   for (int b0 = 0; b0 < batch; b0 += per_launch) {

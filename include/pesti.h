@@ -17,6 +17,14 @@
  *   Q4_K  144 B / 256 weights: binary16 d, binary16 dmin, 12 B of packed
  *          6-bit scales sc[8] and mins m[8], 128 B of 4-bit codes.
  *                                                  w = d*sc[j]*q - dmin*m[j]
+ *   Q2_K   84 B / 256 weights: 16 bytes of (4-bit scale, 4-bit min) per
+ *          16-weight sub-block, 64 B of 2-bit codes, binary16 d, dmin.
+ *          Weight 128h+32j+16c+l: bits 2j of code byte 32h+16c+l, sub-block
+ *          8h+2j+c.                                w = d*sc[s]*q - dmin*m[s]
+ *   Q3_K  110 B / 256 weights: 32 B of high bits, 64 B of 2-bit codes (as
+ *          Q2_K), 12 B of sixteen 6-bit scales, binary16 d.  The code is
+ *          the low bits minus 4 where its high bit (bit 4h+j of byte 16c+l)
+ *          is clear.                               w = d*(scale[s]-32)*q
  *   Q5_K  176 B / 256 weights: d, dmin, the 12 scale/min bytes of Q4_K,
  *          32 B of fifth bits, 128 B of low 4-bit codes (Q4_K's runs).
  *                                                  w = d*sc[j]*q - dmin*m[j]
@@ -26,7 +34,7 @@
  *
  * Layouts and conventions (every entry point)
  *   - W has out_features rows.  A packed row is ceil(in/QK) whole blocks
- *     (QK = 32 for Q8_0, 256 for Q4_K/Q5_K/Q6_K); rows follow each other with
+ *     (QK = 32 for Q8_0, 256 for the K family); rows follow each other with
  *     stride pesti_row_bytes(format, in_features) bytes.  When in_features
  *     is not a multiple of 256, the columns in_features..end of the last
  *     super-block are padding: they are never read into the result and
@@ -80,6 +88,8 @@ extern "C" {
 #define PESTI_FMT_Q6_K 2
 #define PESTI_FMT_I8ROW 3
 #define PESTI_FMT_Q5_K 4
+#define PESTI_FMT_Q2_K 5
+#define PESTI_FMT_Q3_K 6
 
 #define PESTI_MAX_BATCH 8
 #define PESTI_MAX_IN_FEATURES 32768
@@ -96,6 +106,17 @@ int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* block
 /* Q4_K (144-byte super-blocks of 256 weights, rows padded to whole
  * super-blocks).  Same arguments as pesti_gemv_q8_0. */
 int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+
+/* Q2_K (84-byte) and Q3_K (110-byte) super-blocks of 256 weights, rows
+ * padded to whole super-blocks ("PESTI ..." README, "What This Is": all
+ * K-family quantizations, Q2_K to Q8_0).  Same arguments as
+ * pesti_gemv_q8_0. */
+int pesti_gemv_q2_k(int64_t out_features, int64_t in_features, const void* blocks,
+                    const float* x, float* y, const float* bias, int32_t batch,
+                    void* stream);
+int pesti_gemv_q3_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
 
@@ -154,8 +175,8 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
  * and the same shape, laid out as for the single mat-vecs (no bias);
  * gate_scales / up_scales are their row scales for PESTI_FMT_I8ROW and are
  * ignored otherwise.  x float32 [batch][in], h float32 [batch][out].  Rows
- * must fit one load round: in_features up to 4096 (Q4_K, Q6_K, i8row,
- * Q8_0 with in % 64 == 0) or 2048 (other Q8_0), else PESTI_ERR_SHAPE.
+ * must fit one load round: in_features up to 4096 (K family, i8row, Q8_0
+ * with in % 64 == 0) or 2048 (other Q8_0), else PESTI_ERR_SHAPE.
  * Bound: |h - exact| <= 1.1 * eg * |u| + |silu(g)| * eu + 2 * eg * eu
  * + 1e-6 * |h| + 1e-6, with eg, eu the mat-vec bounds of g and u. */
 int pesti_gemv_swiglu(int32_t format, int64_t out_features, int64_t in_features,
@@ -200,10 +221,15 @@ int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
 /* --- dequantization to float32 (bit-exact; checks the unpacking) --------
  * w_out float32 [rows][in_features]: each weight rounded once from its
  * exact value (all formats here dequantize exactly in float32 except the
- * final subtraction of Q4_K / Q5_K and the scale product of i8row). */
+ * final subtraction of Q2_K / Q4_K / Q5_K and the scale product of
+ * i8row). */
 int pesti_dequant_q8_0(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_q2_k(int64_t rows, int64_t in_features, const void* blocks,
+                       float* w_out, void* stream);
+int pesti_dequant_q3_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q5_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);

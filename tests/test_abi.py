@@ -46,7 +46,7 @@ def test_abi_version():
     assert dmv.pesti_abi_version() == 1
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q5_k", "q6_k", "i8row"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row"])
 @pytest.mark.parametrize("inf", [0, 32, 64, 96, 256, 288, 768, 896, 4864, 16384])
 def test_row_bytes_agree_with_oracle_and_generator(fmt, inf):
     rb = dmv.pesti_row_bytes(fmt, inf)
@@ -74,8 +74,8 @@ def _raw():
     return _lib.load()
 
 
-@pytest.mark.parametrize("name", ["pesti_gemv_q8_0", "pesti_gemv_q4_k", "pesti_gemv_q5_k",
-                                  "pesti_gemv_q6_k"])
+@pytest.mark.parametrize("name", ["pesti_gemv_q8_0", "pesti_gemv_q2_k", "pesti_gemv_q3_k",
+                                  "pesti_gemv_q4_k", "pesti_gemv_q5_k", "pesti_gemv_q6_k"])
 def test_gemv_argument_checks(name):
     fn = getattr(_raw(), name)
     assert fn(-1, 64, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
@@ -148,8 +148,8 @@ def test_swiglu_argument_checks():
     assert fn(Q4, 8, 64, None, None, None, None, None, None, 0, None) == _lib.PESTI_OK
 
 
-@pytest.mark.parametrize("name", ["pesti_dequant_q8_0", "pesti_dequant_q4_k", "pesti_dequant_q5_k",
-                                  "pesti_dequant_q6_k"])
+@pytest.mark.parametrize("name", ["pesti_dequant_q8_0", "pesti_dequant_q2_k", "pesti_dequant_q3_k",
+                                  "pesti_dequant_q4_k", "pesti_dequant_q5_k", "pesti_dequant_q6_k"])
 def test_dequant_argument_checks(name):
     fn = getattr(_raw(), name)
     assert fn(-1, 64, FAKE, FAKE, None) == _lib.PESTI_ERR_SHAPE

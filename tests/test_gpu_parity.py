@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 GEMV_REL = 1e-4
 GEMM_REL = 2e-3
-FORMATS = ("q8_0", "q4_k", "q5_k", "q6_k", "i8row")
+FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row")
 
 
 @pytest.fixture(autouse=True)
@@ -52,7 +52,7 @@ def test_dequant_bit_exact(fmt, rows, inf):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q5_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
 def test_dequant_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([5, d_bits])
@@ -145,16 +145,27 @@ def test_power_of_two_scaling_is_exact(fmt):
     assert np.array_equal(y2, y1 * np.float32(8.0))
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q2_k", "q3_k", "q4_k", "q5_k", "q6_k"])
 def test_padding_bytes_do_not_matter(fmt):
     """Rows of 896 hold 3.5 super-blocks; the padding half must be ignored."""
     out, inf = 33, 896
     packed, _, x, bias = make(fmt, out, inf, 7)
     rng = np.random.default_rng(99)
     other = packed.copy().reshape(out, -1)
-    nb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}[fmt]
+    nb = {"q2_k": 84, "q3_k": 110, "q4_k": 144, "q5_k": 176, "q6_k": 210}[fmt]
     last = other[:, 3 * nb:4 * nb]
-    if fmt == "q5_k":
+
+    def high_nibbles(lo, hi):   # randomize bits 4-7 of bytes lo..hi-1
+        last[:, lo:hi] = (last[:, lo:hi] & 0x0F) | (rng.integers(0, 16, last[:, lo:hi].shape,
+                                                                  dtype=np.uint8) << 4)
+    if fmt == "q2_k":
+        last[:, 8:16] = rng.integers(0, 256, last[:, 8:16].shape, dtype=np.uint8)
+        last[:, 48:80] = rng.integers(0, 256, last[:, 48:80].shape, dtype=np.uint8)
+    elif fmt == "q3_k":
+        high_nibbles(0, 32)       # high bits of the second half (bits 4..7)
+        last[:, 64:96] = rng.integers(0, 256, last[:, 64:96].shape, dtype=np.uint8)
+        high_nibbles(96, 108)     # scale bits of sub-blocks 8..15
+    elif fmt == "q5_k":
         last[:, 48 + 64:] = rng.integers(0, 256, last[:, 48 + 64:].shape, dtype=np.uint8)
         last[:, 16:48] = (last[:, 16:48] & 0x0F) | (rng.integers(0, 16, last[:, 16:48].shape,
                                                                dtype=np.uint8) << 4)
@@ -203,7 +214,7 @@ def test_empty_output_touches_nothing(fmt):
     assert guards_intact(fbuf, 0)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q5_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
 def test_gemv_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([9, d_bits])
@@ -259,7 +270,9 @@ FULL = [("q8_0", synth.QWEN_VOCAB, 896, 1), ("q8_0", synth.QWEN_VOCAB, 896, 8),
         ("q8_0", synth.GPT2_VOCAB, 768, 1),
         ("q4_k", 4864, 896, 1), ("q4_k", 896, 4864, 1), ("q6_k", 896, 4864, 1),
         ("q4_k", 128, 896, 1), ("i8row", 896, 896, 1),
-        ("q5_k", synth.QWEN_VOCAB, 896, 1), ("q5_k", 4864, 896, 1), ("q5_k", 896, 4864, 3)]
+        ("q5_k", synth.QWEN_VOCAB, 896, 1), ("q5_k", 4864, 896, 1), ("q5_k", 896, 4864, 3),
+        ("q2_k", synth.QWEN_VOCAB, 896, 1), ("q2_k", 896, 4864, 2), ("q3_k", synth.QWEN_VOCAB, 896, 1),
+        ("q3_k", 896, 4864, 4)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", FULL)
@@ -496,7 +509,8 @@ TALL = [("q8_0", 65536 + 37, 64, 1), ("q8_0", 131072 + 53, 64, 3), ("q8_0", 1310
         ("q4_k", 65536 + 37, 256, 2), ("q4_k", 131072 + 53, 896, 1), ("q4_k", 65536 + 29, 1280, 1),
         ("q6_k", 65536 + 37, 256, 1), ("q6_k", 131072 + 53, 256, 8), ("q6_k", 65536 + 5, 1280, 1),
         ("i8row", 131072 + 53, 64, 1), ("i8row", 65536 + 37, 160, 4),
-        ("q5_k", 65536 + 37, 256, 2), ("q5_k", 131072 + 53, 896, 1)]
+        ("q5_k", 65536 + 37, 256, 2), ("q5_k", 131072 + 53, 896, 1),
+        ("q2_k", 65536 + 37, 256, 3), ("q3_k", 131072 + 53, 896, 1), ("q3_k", 65536 + 5, 1280, 2)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", TALL)
