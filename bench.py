@@ -62,7 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--suite", action="store_true",
                    help="instead of the decode step, time every other workload (int8, Q4_K FFN, "
                         "f16 GEMM, LM-head sweep) and print one JSON line per case")
-    p.add_argument("--suite-filter", default="", help="only suite cases whose name contains this")
+    p.add_argument("--suite-filter", default="",
+                   help="only suite cases whose name contains this (comma-separated alternatives)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the counter summary from two rocprofv3 --pmc runs and exit")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -256,7 +257,7 @@ def run_suite(lib, args):
     stream = torch.cuda.Stream()
     out_lines = []
     for idx, (name, kind, prm) in enumerate(suite_cases()):
-        if args.suite_filter and args.suite_filter not in name:
+        if args.suite_filter and not any(f in name for f in args.suite_filter.split(",")):
             continue
         rng = synth.rng_for(4 if "lm-head" in name else (0 if kind == "gemv" and prm[0] == "i8row" else 1), idx, 0)
         nops = 1
