@@ -236,7 +236,7 @@ def suite_cases():
                ("lm-head", synth.QWEN_VOCAB, synth.QWEN_HIDDEN))
     for m in (16, 64):
         for label, n, k in qshapes:
-            for fmt in ("q8_0", "q4_k", "q6_k"):
+            for fmt in ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k"):
                 cases.append((f"{fmt} gemm {label} {n}x{k} m{m}", "qgemm", (fmt, m, n, k)))
             cases.append((f"f16 gemm {label} {n}x{k} m{m}", "gemm", (m, k, n)))
     return cases

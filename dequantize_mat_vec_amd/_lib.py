@@ -42,6 +42,9 @@ _SIGNATURES = {
     "pesti_gemm_q8_0_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q4_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q6_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q2_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q3_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_q5_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q2_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -287,7 +290,7 @@ def gemv(fmt, out_features, in_features, w, x, y, bias=None, batch=1, scales=Non
 
 def gemm_quant(fmt, m, out_features, in_features, blocks, x, y, bias=None, stream=None):
     """Dispatch Y = X W^T + b (binary16 X, packed W) to the entry point of
-    format `fmt` (q8_0, q4_k or q6_k)."""
+    format `fmt` (q8_0 or a K-family format)."""
     return _gemm_q(f"pesti_gemm_{fmt}_smallm", m, out_features, in_features, blocks, x, y, bias,
                    stream)
 

@@ -272,6 +272,7 @@ int launch_mfma(const GemmArgs& a, hipStream_t st) {
 // binary16 weights for the wide-layer kernel: a unit is one k-step, 32
 // consecutive weights of the row, the lane's 8 of them one 16-byte load.
 struct WPolF16 {
+  static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = false;

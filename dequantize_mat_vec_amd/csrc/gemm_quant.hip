@@ -56,6 +56,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // in-bounds re-read), never a byte outside the block, and realigns them.
 // ---------------------------------------------------------------------------
 struct QPolQ8_0 {
+  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -102,6 +103,7 @@ struct QPolQ8_0 {
 // super-blocks).
 // ---------------------------------------------------------------------------
 struct QPolQ4_K {
+  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -197,6 +199,7 @@ __device__ __forceinline__ qhalf8 q6_k_part(qhalf8 v, int part, int kg) {
 }
 
 struct QPolQ6_K {
+  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 2;
@@ -223,12 +226,198 @@ struct QPolQ6_K {
 };
 
 // ---------------------------------------------------------------------------
+// Operands carrying their scale: 8 small unsigned code bytes v (two dwords)
+// become binary16 1024 + v by writing 0x64 above each byte (v_perm_b32),
+// and one packed FMA per pair gives (1024 + v) * s - 1024 * s = v * s,
+// exact because -1024 * s, the exact product inside the FMA and the result
+// are all binary16 values (Q5_K q * sc <= 31 * 63 = 1953, Q2_K q * sc <= 45).
+// Q3_K's offset code (v - 4) * (sc - 32) takes a packed subtraction and a
+// packed product instead (1028 * s is not always a binary16 value).  s is
+// per lane, so a k-step whose lanes belong to different sub-blocks needs
+// no second product.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ qhalf8 scaled_codes(uint32_t lo, uint32_t hi, qhalf2 s, qhalf2 off) {
+  uint32_t h[4];
+  h[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);   // [v0, 0x64, v1, 0x64]
+  h[1] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
+  h[2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
+  h[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    h[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(qhalf2, h[e]), s, off));
+  return __builtin_bit_cast(qhalf8, h);
+}
+
+// (v - (base - 1024)) * s for the same code bytes, as an exact packed
+// subtraction then an exact packed product (for offsets whose FMA constant
+// -base * s would not be a binary16 integer).
+__device__ __forceinline__ qhalf8 offset_codes(uint32_t lo, uint32_t hi, qhalf2 s, qhalf2 base) {
+  uint32_t h[4];
+  h[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
+  h[1] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
+  h[2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
+  h[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(qhalf2, h[e]) - base) * s);
+  return __builtin_bit_cast(qhalf8, h);
+}
+
+// A small non-negative integer as a binary16 pair, exactly.
+__device__ __forceinline__ qhalf2 half_pair(uint32_t v) {
+  const _Float16 f = static_cast<_Float16>(static_cast<float>(v));
+  return qhalf2{f, f};
+}
+__device__ __forceinline__ qhalf2 half_pair_signed(int v) {
+  const _Float16 f = static_cast<_Float16>(static_cast<float>(v));
+  return qhalf2{f, f};
+}
+
+// 6-bit scale / min of Q4_K-style packing for sub-block j (0..7) from the
+// header dwords y, z, w (bytes 4..15).
+__device__ __forceinline__ void k4_scale_min(uint32_t y, uint32_t z, uint32_t w, int j, uint32_t& sc,
+                                             uint32_t& mn) {
+  const uint32_t t = static_cast<uint32_t>(j & 3);
+  const uint32_t sy = (y >> (8 * t)) & 0xFFu, sz = (z >> (8 * t)) & 0xFFu, sw = (w >> (8 * t)) & 0xFFu;
+  if (j < 4) {
+    sc = sy & 63u;
+    mn = sz & 63u;
+  } else {
+    sc = (sw & 15u) | ((sy >> 6) << 4);
+    mn = (sw >> 4) | ((sz >> 6) << 4);
+  }
+}
+
+// Q5_K step s (sub-block j = s % 8 of super-block s / 8, 176 bytes): the
+// lane's 8 low nibbles (bytes 48 + 32(j / 2) + 8kg) and their fifth bits
+// (bit j of bytes 16 + 8kg); operand q * sc_j, scaled by d; mins dmin * m_j
+// times the step's sum of x (product against ones).
+struct QPolQ5_K {
+  static constexpr bool kMin = true;
+  static constexpr bool kMinOperand = false;
+  static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
+  struct Step { uint32_t c[2]; uint32_t h[2]; u32x4 hdr; uint32_t j; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* sb = row + 176 * (s >> 3);
+    const int j = s & 7;
+    const uint8_t* p = sb + 48 + 32 * (j >> 1) + 8 * kg;
+    st.c[0] = load_u32(p);
+    st.c[1] = load_u32(p + 4);
+    st.h[0] = load_u32(sb + 16 + 8 * kg);
+    st.h[1] = load_u32(sb + 20 + 8 * kg);
+    st.hdr = load_u32x4_a16(sb);
+    st.j = static_cast<uint32_t>(j);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) {
+    const uint32_t sh = 4u * (st.j & 1u);
+    const uint32_t lo = ((st.c[0] >> sh) & 0x0F0F0F0Fu) | (((st.h[0] >> st.j) & 0x01010101u) << 4);
+    const uint32_t hi = ((st.c[1] >> sh) & 0x0F0F0F0Fu) | (((st.h[1] >> st.j) & 0x01010101u) << 4);
+    uint32_t sc, mn;
+    k4_scale_min(st.hdr.y, st.hdr.z, st.hdr.w, static_cast<int>(st.j), sc, mn);
+    const qhalf2 s = half_pair(sc);
+    return scaled_codes(lo, hi, s, s * qhalf2{-1024, -1024});
+  }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    uint32_t sc, mn;
+    k4_scale_min(st.hdr.y, st.hdr.z, st.hdr.w, static_cast<int>(st.j), sc, mn);
+    ds = f16_lo(st.hdr.x);
+    dm = f16_hi(st.hdr.x) * static_cast<float>(mn);
+  }
+  __device__ __forceinline__ static qhalf8 min_codes(const Step&, int) { return qhalf8{}; }
+};
+
+// Q3_K step s (t = s % 8 of super-block s / 8, 110 bytes, 2-byte aligned):
+// t = 4h + j covers weights 128h + 32j + [0, 32); lane kg holds c = kg / 2,
+// l = 8(kg % 2) .. +7 of sub-block 8h + 2j + c: low bits at bit 2j of bytes
+// 32 + 32h + 16c + l, high bit at bit 4h + j of bytes 16c + l.  Operand
+// (low | high << 2) - 4 = q times the lane's own scale - 32, scaled by d.
+struct QPolQ3_K {
+  static constexpr bool kMin = false;
+  static constexpr bool kMinOperand = false;
+  static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
+  struct Step { uint32_t q[2]; uint32_t hm[2]; uint32_t s01, s2; uint32_t d; uint32_t t; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* sb = row + 110 * (s >> 3);
+    const int t = s & 7, h = t >> 2, c = kg >> 1, l = 8 * (kg & 1);
+    const q6u2 qv = *reinterpret_cast<const q6u2*>(sb + 32 + 32 * h + 16 * c + l);
+    const q6u2 hv = *reinterpret_cast<const q6u2*>(sb + 16 * c + l);
+    st.q[0] = qv.x; st.q[1] = qv.y;
+    st.hm[0] = hv.x; st.hm[1] = hv.y;
+    // the lane's scale k = 8h + 2j + c: low bits in byte k % 8 = 2j + c
+    // (nibble h), high bits in byte 8 + k % 4 (bits 4h + 2(j / 2))
+    const int j = t & 3;
+    st.s01 = load_u16(sb + 96 + 2 * j);        // bytes 2j, 2j + 1
+    st.s2 = load_u16(sb + 104 + 2 * (j & 1));  // bytes 8 + 2(j % 2), +1
+    st.d = load_u16(sb + 108);
+    st.t = static_cast<uint32_t>(t | (kg << 3));
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int kg) {
+    const uint32_t t = st.t & 7u, h = t >> 2, j = t & 3u, c = static_cast<uint32_t>(kg >> 1);
+    const uint32_t hs = 4u * h + j;
+    const uint32_t lo = ((st.q[0] >> (2 * j)) & 0x03030303u) | (((st.hm[0] >> hs) & 0x01010101u) << 2);
+    const uint32_t hi = ((st.q[1] >> (2 * j)) & 0x03030303u) | (((st.hm[1] >> hs) & 0x01010101u) << 2);
+    const uint32_t lo4 = (st.s01 >> (8 * c + 4 * h)) & 15u;
+    const uint32_t hi2 = (st.s2 >> (8 * c + 4 * h + 2 * (j >> 1))) & 3u;
+    const int sc = static_cast<int>(lo4 | (hi2 << 4)) - 32;
+    const qhalf2 s = half_pair_signed(sc);
+    return offset_codes(lo, hi, s, qhalf2{1028, 1028});   // (v - 4) * s, v = q + 4
+  }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    ds = f16_lo(st.d);
+    dm = 0.f;
+  }
+  __device__ __forceinline__ static qhalf8 min_codes(const Step&, int) { return qhalf8{}; }
+};
+
+// Q2_K step s (t = 4h + j of super-block s / 8, 84 bytes): lane kg holds
+// c = kg / 2, l = 8(kg % 2) .. +7 of sub-block k = 8h + 2j + c: codes at bit
+// 2j of bytes 16 + 32h + 16c + l, scale and min nibbles of byte k.  Operand
+// q * sc, scaled by d; the mins are a second product against the lane's
+// min m (every k of a lane shares it), scaled by dmin.
+struct QPolQ2_K {
+  static constexpr bool kMin = true;
+  static constexpr bool kMinOperand = true;
+  static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
+  struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+    const uint8_t* sb = row + 84 * (s >> 3);
+    const int t = s & 7, h = t >> 2, j = t & 3, c = kg >> 1, l = 8 * (kg & 1);
+    const uint8_t* p = sb + 16 + 32 * h + 16 * c + l;
+    st.q[0] = load_u32(p);
+    st.q[1] = load_u32(p + 4);
+    st.scb = load_u16(sb + 8 * h + 2 * j) >> (8 * c);   // byte k = 8h + 2j + c in bits 0-7
+    st.dd = load_u32(sb + 80);
+    st.j = static_cast<uint32_t>(j);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) {
+    const uint32_t lo = (st.q[0] >> (2 * st.j)) & 0x03030303u;
+    const uint32_t hi = (st.q[1] >> (2 * st.j)) & 0x03030303u;
+    const qhalf2 s = half_pair(st.scb & 15u);
+    return scaled_codes(lo, hi, s, s * qhalf2{-1024, -1024});
+  }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    ds = f16_lo(st.dd);
+    dm = f16_hi(st.dd);
+  }
+  __device__ __forceinline__ static qhalf8 min_codes(const Step& st, int) {
+    const _Float16 m = static_cast<_Float16>(static_cast<float>((st.scb >> 4) & 15u));
+    return qhalf8{m, m, m, m, m, m, m, m};
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Units of the wide-layer kernel (whole rows per wavefront, X in LDS).
 // Q8_0: one block per unit, the step's loads as above.  Q4_K: one
 // super-block per unit - the 16-byte header once, and each lane's 8 code
 // bytes of the four sub-block pairs - so a unit feeds eight k-steps.
 // ---------------------------------------------------------------------------
 struct WPolQ8_0 {
+  static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
@@ -248,6 +437,7 @@ struct WPolQ8_0 {
 // qh (two), the 16 scale bytes and d; a unit feeds eight k-steps of two
 // scaled parts each.
 struct WPolQ6_K {
+  static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 256;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
@@ -287,6 +477,7 @@ struct WPolQ6_K {
 };
 
 struct WPolQ4_K {
+  static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 256;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
@@ -313,7 +504,7 @@ struct WPolQ4_K {
   // placing 0x64 above it (v_perm_b32); one packed FMA then gives
   // (1024 + q) * sc - 1024 * sc = q * sc, exact (one rounding of an exact
   // small integer).  sc_j itself comes the same way: 1024 + sc, minus 1024.
-  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j) {
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int) {
     const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
     const uint32_t a = (un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu;
     const uint32_t b = (un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu;
@@ -346,6 +537,148 @@ struct WPolQ4_K {
     const uint32_t w = (un.hdr.w >> (8 * kg)) & 0xFFu;
     const uint32_t m = half == 0 ? (z & 63u) : ((w >> 4) | ((z >> 6) << 4));
     return -f16_hi(un.hdr.x) * static_cast<float>(m);
+  }
+  __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
+};
+
+// Q5_K unit: one super-block - the header, the lane's 8 low-nibble bytes of
+// each run and its 8 fifth-bit bytes; chained like Q4_K with q * sc_j
+// (q <= 31) in the operand.
+struct WPolQ5_K {
+  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int kSumWidth = 32;
+  static constexpr bool kMin = true;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = true;
+  static constexpr int kParts = 1;
+  static constexpr int kSteps = 8;
+  static constexpr int kRing = 4;
+  struct Unit { u32x4 hdr; uint32_t c[4][2]; uint32_t h[2]; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint8_t* sb = row + 176 * u;
+    un.hdr = load_u32x4_a16(sb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint8_t* p = sb + 48 + 32 * g + 8 * kg;
+      un.c[g][0] = load_u32(p);
+      un.c[g][1] = load_u32(p + 4);
+    }
+    un.h[0] = load_u32(sb + 16 + 8 * kg);
+    un.h[1] = load_u32(sb + 20 + 8 * kg);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int) {
+    const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
+    const uint32_t lo = ((un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu) | (((un.h[0] >> j) & 0x01010101u) << 4);
+    const uint32_t hi = ((un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu) | (((un.h[1] >> j) & 0x01010101u) << 4);
+    uint32_t sc, mn;
+    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, j, sc, mn);
+    const qhalf2 sv = half_pair(sc);
+    return scaled_codes(lo, hi, sv, sv * qhalf2{-1024, -1024});
+  }
+  __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
+  __device__ __forceinline__ static float neg_min(const Unit& un, int half, int kg) {
+    uint32_t sc, mn;
+    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, 4 * half + kg, sc, mn);
+    return -f16_hi(un.hdr.x) * static_cast<float>(mn);
+  }
+  __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
+};
+
+// Q3_K unit: one super-block (2-byte aligned) - the lane's code bytes of
+// both halves (c = kg / 2, l = 8(kg % 2) .. +7), its high-bit bytes, the 12
+// scale bytes and d; step j = 4h + jj carries (q) * (scale - 32) of the
+// lane's sub-block 8h + 2jj + c in the operand.
+struct WPolQ3_K {
+  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int kSumWidth = 32;
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = true;
+  static constexpr int kParts = 1;
+  static constexpr int kSteps = 8;
+  static constexpr int kRing = 4;
+  struct Unit { uint32_t q[2][2]; uint32_t hm[2]; uint32_t s0, s1, s2; uint32_t d; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint8_t* sb = row + 110 * u;
+    const int c = kg >> 1, l = 8 * (kg & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const q6u2 v = *reinterpret_cast<const q6u2*>(sb + 32 + 32 * h + 16 * c + l);
+      un.q[h][0] = v.x;
+      un.q[h][1] = v.y;
+    }
+    const q6u2 hv = *reinterpret_cast<const q6u2*>(sb + 16 * c + l);
+    un.hm[0] = hv.x;
+    un.hm[1] = hv.y;
+    const q6u2 sv = *reinterpret_cast<const q6u2*>(sb + 96);
+    un.s0 = sv.x;
+    un.s1 = sv.y;
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+    un.s2 = *reinterpret_cast<const u32a2*>(sb + 104);
+    un.d = load_u16(sb + 108);
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int kg) {
+    const int h = j >> 2, jj = j & 3;
+    const uint32_t c = static_cast<uint32_t>(kg >> 1);
+    const uint32_t hs = static_cast<uint32_t>(4 * h + jj);
+    const uint32_t lo = ((un.q[h][0] >> (2 * jj)) & 0x03030303u) | (((un.hm[0] >> hs) & 0x01010101u) << 2);
+    const uint32_t hi = ((un.q[h][1] >> (2 * jj)) & 0x03030303u) | (((un.hm[1] >> hs) & 0x01010101u) << 2);
+    const uint32_t idx = static_cast<uint32_t>(2 * jj) + c;                    // byte k % 8
+    const uint32_t lw = jj < 2 ? un.s0 : un.s1;
+    const uint32_t lo4 = (lw >> (8 * (idx & 3u) + 4u * h)) & 15u;
+    const uint32_t hi2 = (un.s2 >> (8 * (idx & 3u) + 4u * h + 2u * (jj >> 1))) & 3u;
+    const qhalf2 sv = half_pair_signed(static_cast<int>(lo4 | (hi2 << 4)) - 32);
+    return offset_codes(lo, hi, sv, qhalf2{1028, 1028});
+  }
+  __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.d); }
+  __device__ __forceinline__ static float neg_min(const Unit&, int, int) { return 0.f; }
+  __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
+};
+
+// Q2_K unit: one super-block - the lane's code bytes of both halves, the 16
+// scale bytes and d, dmin; operand q * sc of the lane's sub-block; the 16
+// mins (one per 16 weights) take 16-weight sums of X, four per product.
+struct WPolQ2_K {
+  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int kSumWidth = 16;
+  static constexpr bool kMin = true;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = true;
+  static constexpr int kParts = 1;
+  static constexpr int kSteps = 8;
+  static constexpr int kRing = 4;
+  struct Unit { uint32_t q[2][2]; u32x4 sc; uint32_t dd; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint8_t* sb = row + 84 * u;
+    const int c = kg >> 1, l = 8 * (kg & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint8_t* p = sb + 16 + 32 * h + 16 * c + l;
+      un.q[h][0] = load_u32(p);
+      un.q[h][1] = load_u32(p + 4);
+    }
+    un.sc = load_u32x4(sb);
+    un.dd = load_u32(sb + 80);
+  }
+  __device__ __forceinline__ static uint32_t scale_byte(const Unit& un, uint32_t k) {
+    const uint32_t w = k < 4 ? un.sc.x : (k < 8 ? un.sc.y : (k < 12 ? un.sc.z : un.sc.w));
+    return (w >> (8 * (k & 3u))) & 0xFFu;
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int kg) {
+    const int h = j >> 2, jj = j & 3;
+    const uint32_t lo = (un.q[h][0] >> (2 * jj)) & 0x03030303u;
+    const uint32_t hi = (un.q[h][1] >> (2 * jj)) & 0x03030303u;
+    const uint32_t k = static_cast<uint32_t>(8 * h + 2 * jj + (kg >> 1));
+    const qhalf2 sv = half_pair(scale_byte(un, k) & 15u);
+    return scaled_codes(lo, hi, sv, sv * qhalf2{-1024, -1024});
+  }
+  __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.dd); }
+  // sub-block 4h + kg (16 weights each)
+  __device__ __forceinline__ static float neg_min(const Unit& un, int h, int kg) {
+    return -f16_hi(un.dd) * static_cast<float>(scale_byte(un, static_cast<uint32_t>(4 * h + kg)) >> 4);
   }
   __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
 };
@@ -415,7 +748,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
                                                                    0, 0, 0);
           acc[t] += ds * p;
           if constexpr (Q::kMin) {
-            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
+            // the step's sum of x (ones), or x against the lanes' mins
+            qhalf8 mv = ones;
+            if constexpr (Q::kMinOperand) mv = Q::min_codes(b.w[c], kg);
+            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], mv,
                                                                       qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             acc[t] -= dm * sx;
           }
@@ -540,6 +876,24 @@ int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
   return gemm_quant<pesti::QPolQ4_K, pesti::WPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
                                      ((in_features + 255) / 256) * 144, stream);
+}
+
+int pesti_gemm_q2_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ2_K, pesti::WPolQ2_K>(m, out_features, in_features, blocks, x, y, bias,
+                                     ((in_features + 255) / 256) * 84, stream);
+}
+
+int pesti_gemm_q3_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ3_K, pesti::WPolQ3_K>(m, out_features, in_features, blocks, x, y, bias,
+                                     ((in_features + 255) / 256) * 110, stream);
+}
+
+int pesti_gemm_q5_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
+                           const uint16_t* x, float* y, const float* bias, void* stream) {
+  return gemm_quant<pesti::QPolQ5_K, pesti::WPolQ5_K>(m, out_features, in_features, blocks, x, y, bias,
+                                     ((in_features + 255) / 256) * 176, stream);
 }
 
 int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,

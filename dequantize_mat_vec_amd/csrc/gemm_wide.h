@@ -25,10 +25,11 @@
 // step's kParts parts - codes(Unit, j, part, kg), scale(Unit, j, part) - is
 // its own product, added to the float32 sum times its scale.  Chained
 // formats (kChained) carry the sub-block scales in the operand:
-// codes(Unit, j) for the eight steps of a unit accumulate in the matrix
-// core, d(Unit) scales the sum once, and for kMin formats neg_min(Unit,
-// half, kg) times the per-step sums of X (taken once per workgroup into
-// LDS) removes the mins.  j, part and half are constants after unrolling.
+// codes(Unit, j, kg) for the steps of a unit accumulate in the matrix core,
+// d(Unit) scales the sum once, and for kMin formats neg_min(Unit, h, kg)
+// times the sums of X over each kSumWidth weights (taken once per
+// workgroup into LDS) removes the mins, four sum groups per 16x16x4
+// product.  j, part and h are constants after unrolling.
 //
 // Operand layout, lane l (i = l % 16, kg = l / 16): A = X row i,
 // k = 8kg..8kg+7 of the step; B = W row i (output column i), the same k;
@@ -50,11 +51,11 @@ struct WideArgs {
   int64_t row_bytes;
 };
 
-// LDS bytes: X fragments [MT][S][64] of 16 bytes, then (kMin) the step sums
-// of X [S][16 * MT] float32.
+// LDS bytes: X fragments [MT][S][64] of 16 bytes, then (kMin) the sums of
+// X over each kSumWidth (32 or 16) weights, [K / kSumWidth][16 * MT] float32.
 template <class Q>
 __host__ __device__ constexpr int64_t wide_lds_bytes(int mt, int64_t k) {
-  return static_cast<int64_t>(mt) * (k / 32) * 64 * 16 + (Q::kMin ? (k / 32) * 16 * mt * 4 : 0);
+  return static_cast<int64_t>(mt) * (k / 32) * 64 * 16 + (Q::kMin ? (k / Q::kSumWidth) * 16 * mt * 4 : 0);
 }
 
 template <class Q, int MT, int NWV>
@@ -108,15 +109,19 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
       if (rr[b] < 16 * MT)
         xf[((rr[b] >> 4) * S + (qq[b] >> 2)) * 64 + (rr[b] & 15) + 16 * (qq[b] & 3)] = v[b];
   }
+  constexpr int SPS = 32 / Q::kSumWidth;   // sums per k-step
   if constexpr (Q::kMin) {
     __syncthreads();
-    // sx[s][r]: the 32 values of row r in step s summed in float32, in k order.
-    for (int c = tid; c < 16 * MT * S; c += NWV * 64) {
-      const int s = c / (16 * MT), r = c - s * (16 * MT);
+    // sx[q][r]: the kSumWidth values of row r in sum group q (lanes
+    // kg = 4 / SPS * (q % SPS) .. of step q / SPS) summed in float32, in k
+    // order.
+    for (int c = tid; c < 16 * MT * S * SPS; c += NWV * 64) {
+      const int q = c / (16 * MT), r = c - q * (16 * MT);
+      const int s = q / SPS, g0 = (4 / SPS) * (q % SPS);
       float t = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const whalf8 v = xf[((r >> 4) * S + s) * 64 + (r & 15) + 16 * g];
+      for (int g = 0; g < 4 / SPS; ++g) {
+        const whalf8 v = xf[((r >> 4) * S + s) * 64 + (r & 15) + 16 * (g0 + g)];
 #pragma unroll
         for (int e = 0; e < 8; ++e) t += static_cast<float>(v[e]);
       }
@@ -188,9 +193,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
       if constexpr (Q::kChained) {
         // The unit's k-steps accumulate in the matrix core on operands that
         // carry their sub-block scales; d scales the sum once, and the mins
-        // are subtracted by 16x16x4 float32 products of the per-step sums
-        // of X (A: lane (i, kg) = row i, step 4h + kg) with -dmin * m (B:
-        // the same step, column i).
+        // are subtracted by 16x16x4 float32 products of the sums of X (A:
+        // lane (i, kg) = row i, sum group 4h + kg of the unit) with
+        // -dmin * m (B: the same group, column i).
         if (live) {
           wfloat4 pc[MT];
 #pragma unroll
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
           for (int j = 0; j < KS; ++j) {
             const int s = c_u * KS + j;
             if (s >= S) break;   // wave-uniform: the row's last, partial unit
-            const whalf8 wv = Q::codes(ring[u].un, j);
+            const whalf8 wv = Q::codes(ring[u].un, j, kg);
 #pragma unroll
             for (int t = 0; t < MT; ++t)
               pc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[(t * S + s) * 64 + lane], wv, pc[t], 0, 0, 0);
@@ -207,17 +212,19 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
           const float dd = Q::d(ring[u].un);
 #pragma unroll
           for (int t = 0; t < MT; ++t) acc[t] += dd * pc[t];
+          if constexpr (Q::kMin) {
 #pragma unroll
-          for (int h = 0; h < KS / 4; ++h) {
-            const int s0 = c_u * KS + 4 * h;
-            if (s0 >= S) break;   // wave-uniform
-            const float bm = Q::neg_min(ring[u].un, h, kg);
-            const int sk = s0 + kg < S ? s0 + kg : S - 1;
-            const float keep = s0 + kg < S ? 1.f : 0.f;
+            for (int h = 0; h < KS * SPS / 4; ++h) {
+              const int s0 = c_u * KS * SPS + 4 * h;   // first sum group of the product
+              if (s0 >= S * SPS) break;   // wave-uniform
+              const float bm = Q::neg_min(ring[u].un, h, kg);
+              const int sk = s0 + kg < S * SPS ? s0 + kg : S * SPS - 1;
+              const float keep = s0 + kg < S * SPS ? 1.f : 0.f;
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              const float av = keep * sx[sk * 16 * MT + 16 * t + i];
-              accm[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm, accm[t], 0, 0, 0);
+              for (int t = 0; t < MT; ++t) {
+                const float av = keep * sx[sk * 16 * MT + 16 * t + i];
+                accm[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm, accm[t], 0, 0, 0);
+              }
             }
           }
         }

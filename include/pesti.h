@@ -211,6 +211,20 @@ int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features,
 int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const void* blocks, const uint16_t* x, float* y,
                            const float* bias, void* stream);
+/* Q2_K, Q3_K and Q5_K rows as for their mat-vecs.  Their codes times the
+ * code's own sub-block scale are small binary16 integers (q * sc <= 45,
+ * |q * (sc - 32)| <= 128, q * sc <= 1953), so the operand carries the scale
+ * and each lane its own sub-block's; mins (Q2_K, Q5_K) are products of X
+ * sums or of X against the mins. */
+int pesti_gemm_q2_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
+int pesti_gemm_q3_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
+int pesti_gemm_q5_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                           const void* blocks, const uint16_t* x, float* y,
+                           const float* bias, void* stream);
 /* Q6_K rows as for pesti_gemv_q6_k.  Its codes are exact too (q - 32), but
  * each 32-weight k-step spans two 16-weight sub-blocks, so a step is two
  * products (each on half the operand) scaled apart. */

@@ -108,8 +108,9 @@ def test_i8row_and_gemm_argument_checks():
     assert lib.pesti_gemm_f16_smallm(0, 8, 64, None, None, None, None, None) == _lib.PESTI_OK
 
 
-@pytest.mark.parametrize("name", ["pesti_gemm_q8_0_smallm", "pesti_gemm_q4_k_smallm",
-                                  "pesti_gemm_q6_k_smallm"])
+@pytest.mark.parametrize("name", ["pesti_gemm_q8_0_smallm", "pesti_gemm_q2_k_smallm",
+                                  "pesti_gemm_q3_k_smallm", "pesti_gemm_q4_k_smallm",
+                                  "pesti_gemm_q5_k_smallm", "pesti_gemm_q6_k_smallm"])
 def test_gemm_quant_argument_checks(name):
     fn = getattr(_raw(), name)
     assert fn(-1, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH

@@ -343,7 +343,7 @@ QGEMM_WIDE = [(16, 896, 16400), (17, 96, 16385), (33, 320, 16390), (64, 1024, 16
 QGEMM_CASES += QGEMM_WIDE
 
 
-QGEMM_FORMATS = ("q8_0", "q4_k", "q6_k")
+QGEMM_FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k")
 
 
 @pytest.mark.parametrize("fmt", QGEMM_FORMATS)
@@ -376,7 +376,10 @@ def test_gemm_quant_no_bias_and_one_hot(fmt):
 
 QGEMM_FULL = [("q8_0", 16, synth.QWEN_VOCAB, 896), ("q4_k", 64, synth.QWEN_VOCAB, 896),
               ("q4_k", 64, 4864, 896), ("q4_k", 32, 896, 4864), ("q8_0", 64, 896, 4864),
-              ("q6_k", 64, 896, 4864), ("q6_k", 16, 4864, 896), ("q6_k", 32, synth.QWEN_VOCAB, 896)]
+              ("q6_k", 64, 896, 4864), ("q6_k", 16, 4864, 896), ("q6_k", 32, synth.QWEN_VOCAB, 896),
+              ("q2_k", 64, synth.QWEN_VOCAB, 896), ("q3_k", 16, synth.QWEN_VOCAB, 896),
+              ("q5_k", 32, synth.QWEN_VOCAB, 896), ("q2_k", 32, 896, 4864), ("q3_k", 64, 896, 4864),
+              ("q5_k", 16, 896, 4864)]
 
 
 @pytest.mark.parametrize("fmt,m,n,k", QGEMM_FULL)
