@@ -305,7 +305,9 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               # wide layers (1024+ column tiles): X rows staged in LDS once
               # per workgroup
               (17, 96, 16385), (65, 1024, 16400), (130, 256, 16500), (16, 4096, 16384),
-              (40, 32, 33000), (64, 896, 4864)]
+              (40, 32, 33000), (64, 896, 4864),
+              # the largest m the entry point takes (PESTI_MAX_GEMM_M)
+              (4096, 64, 40)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_CASES)
@@ -333,7 +335,9 @@ QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
                # no columns: Y is the bias; long rows
                (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
                # wide layers: 1, 2 and 4 row tiles per workgroup
-               (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536)]
+               (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536),
+               # the largest m the entry points take (PESTI_MAX_GEMM_M)
+               (4096, 96, 40)]
 # Wide layers (1024+ column tiles, 256+ for Q4_K; X rows staged in LDS):
 # ragged N and M, several 64-row chunks of X, one k-step, rows of several
 # wavefronts' tiles, wavefronts left without a tile.
