@@ -44,7 +44,7 @@ _GEOMETRY = {
     "q6_k": (256, 210, (208,)),
 }
 
-FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row")
+FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row")
 
 
 def rng_for(config_idx: int, layer_idx: int = 0, tensor_idx: int = 0,
@@ -54,9 +54,12 @@ def rng_for(config_idx: int, layer_idx: int = 0, tensor_idx: int = 0,
 
 
 def packed_row_bytes(fmt: str, in_features: int) -> int:
-    """Bytes per packed row (whole blocks); i8row rows are in_features bytes."""
+    """Bytes per packed row (whole blocks); i8row rows are in_features bytes,
+    i4row rows 32 bytes per 64 weights."""
     if fmt == "i8row":
         return in_features
+    if fmt == "i4row":
+        return -(-in_features // 64) * 32
     qk, nbytes, _ = _GEOMETRY[fmt]
     return -(-in_features // qk) * nbytes
 
@@ -118,12 +121,24 @@ def f16_activations(rng: np.random.Generator, rows: int, cols: int) -> np.ndarra
     return rng.standard_normal(size=(rows, cols)).astype(np.float16)
 
 
+def i4row(rng: np.random.Generator, rows: int, in_features: int):
+    """(packed uint8 [rows, ceil(in/64)*32], float32 scales [rows]) for the
+    per-row int4 format: random bytes (every code -8..7, padding included)
+    and scale = max|w| / 7 of one w ~ N(0, 0.02^2) row."""
+    rb = -(-in_features // 64) * 32
+    w = rng.normal(0.0, 0.02, size=(rows, in_features)).astype(np.float32)
+    scales = (np.max(np.abs(w), axis=1).astype(np.float64) / 7.0).astype(np.float32)
+    return rng.integers(0, 256, size=(rows, rb), dtype=np.uint8), scales
+
+
 def matrix(fmt: str, rng: np.random.Generator, rows: int, in_features: int):
     """(packed bytes, scales-or-None) for any format; i8row codes are returned
     as a uint8 view so every format travels as bytes."""
     if fmt == "i8row":
         codes, scales = i8row(rng, rows, in_features)
         return codes.view(np.uint8), scales
+    if fmt == "i4row":
+        return i4row(rng, rows, in_features)
     return quant_blocks(fmt, rng, rows, in_features), None
 
 

@@ -53,6 +53,10 @@ plainest reading of "GGUF parsing + dequantization ... verified byte-exact":
   each), binary16 d.   w[i] = d * sc[i // 16] * (q[i] - 32), q in 0..63.
 * per-row int8 ("i8row"): int8 codes [rows][in] and one f32 scale per row.
   w[o][i] = scale[o] * q[o][i].
+* per-row int4 ("i4row"; the scaffold's quant.rs lists INT4 beside INT8):
+  4-bit two's complement codes, two per byte (weight 2k in the low nibble
+  of byte k, 2k + 1 in the high nibble), rows padded to 64 weights (32
+  bytes), one f32 scale per row.  w[o][i] = scale[o] * q[o][i], q in -8..7.
 
 Rows whose length is not a multiple of the 256-weight super-block are padded
 to whole super-blocks; the padding columns are never part of the matrix and
@@ -82,6 +86,8 @@ def row_bytes(fmt: str, in_features: int) -> int:
     blocks).  For i8row this is the code bytes only; the scale is separate."""
     if fmt == "i8row":
         return in_features
+    if fmt == "i4row":
+        return -(-in_features // 64) * 32
     qk = BLOCK_WEIGHTS[fmt]
     nblk = -(-in_features // qk)
     return nblk * BLOCK_BYTES[fmt]
@@ -312,6 +318,30 @@ def dequant_i8row(codes, scales) -> np.ndarray:
     return s[:, None] * q
 
 
+def i4_codes(packed: np.ndarray) -> np.ndarray:
+    """Signed 4-bit codes of packed bytes (last axis): weight 2k is the low
+    nibble of byte k, 2k + 1 the high nibble; nibbles 8..15 are -8..-1."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = b & 15, b >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    return np.where(q >= 8, q - 16, q)
+
+
+def dequant_i4row(packed, rows: int, in_features: int, scales) -> np.ndarray:
+    """Per-row symmetric int4: w[o][i] = scale[o] * q[o][i].  float64."""
+    if in_features % 32:
+        raise ValueError("i4row needs in_features % 32 == 0")
+    rb = row_bytes("i4row", in_features)
+    b = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    if b.size != rows * rb:
+        raise ValueError(f"i4row: expected {rows * rb} bytes, got {b.size}")
+    q = i4_codes(b.reshape(rows, rb))[:, :in_features].astype(np.float64)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    if s.shape != (rows,):
+        raise ValueError("i4row: scales [rows]")
+    return s[:, None] * q
+
+
 def dequantize(fmt: str, packed, rows: int, in_features: int, scales=None) -> np.ndarray:
     """Exact float64 weights [rows, in_features] of a packed matrix."""
     if fmt == "q8_0":
@@ -328,6 +358,8 @@ def dequantize(fmt: str, packed, rows: int, in_features: int, scales=None) -> np
         return dequant_q6_k(packed, rows, in_features)
     if fmt == "i8row":
         return dequant_i8row(np.asarray(packed).reshape(rows, in_features), scales)
+    if fmt == "i4row":
+        return dequant_i4row(packed, rows, in_features, scales)
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -368,6 +400,8 @@ def gemv_packed(fmt: str, packed, rows: int, in_features: int, x, bias=None,
             part = flat[r0 * in_features:r1 * in_features]
             w = dequant_i8row(part.view(np.int8).reshape(r1 - r0, in_features),
                               np.asarray(scales)[r0:r1])
+        elif fmt == "i4row":
+            w = dequant_i4row(flat[r0 * rb:r1 * rb], r1 - r0, in_features, np.asarray(scales)[r0:r1])
         else:
             w = dequantize(fmt, flat[r0 * rb:r1 * rb], r1 - r0, in_features)
         b = None if bias is None else np.asarray(bias)[r0:r1]
@@ -433,6 +467,24 @@ def within_tolerance(y_test, y_ref, s_ref, rel: float, abs_: float = 1e-6) -> np
 # ---------------------------------------------------------------------------
 # per-row symmetric int8 quantizer ("quant.rs" in ember PR #1)
 # ---------------------------------------------------------------------------
+def quantize_i4row(w):
+    """Per-row symmetric int4 quantization of float32 weights [rows, in]
+    (in % 32 == 0): scale = max|w| / 7 (as float32), q = round-half-away-
+    from-zero(w / scale) clamped to [-7, 7]; a row of zeros gets scale 0 and
+    codes 0.  Returns (packed uint8 [rows, row_bytes], float32 scales)."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, n = w.shape
+    amax = np.max(np.abs(w), axis=1) if n else np.zeros(rows, np.float32)
+    scales = (amax.astype(np.float64) / 7.0).astype(np.float32)
+    q = np.zeros((rows, -(-n // 64) * 64), dtype=np.int64)
+    nz = scales > 0
+    v = w[nz].astype(np.float64) / scales[nz, None].astype(np.float64)
+    q[nz, :n] = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -7, 7)
+    nib = q & 15
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
+
+
 def quantize_i8row(w):
     """Per-row symmetric int8 quantization of float32 weights [rows, in]:
     scale = max|w| / 127 (as float32), q = round-half-away-from-zero(w / scale)

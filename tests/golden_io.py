@@ -1,10 +1,10 @@
 """Reader for the hand-worked fixtures under tests/golden/.
 
 Grammar, one item per line ('#' starts a comment):
-  format <q8_0|q4_k|q6_k|i8row>   rows <n>   in_features <n>
+  format <q8_0|q2_k|...|q6_k|i8row|i4row>   rows <n>   in_features <n>
   hex <tokens>      packed bytes; a token is two hex digits, or XX*N for N copies
   codes <values>    i8row int8 codes of one row (values as below)
-  scales <values>   i8row float32 scales
+  scales <values>   i8row / i4row float32 scales (i4row codes travel as hex)
   f64 <values>      exact dequantized weights, row-major
   f32 <values>      float32 weights when they differ from rounding f64
   x / bias / y      a mat-vec case: input, bias and exact output
@@ -75,7 +75,10 @@ def packed(fx: dict):
     if fx["format"] == "i8row":
         codes = np.array(fx["codes"], dtype=np.int64).astype(np.int8)
         return codes.view(np.uint8).reshape(-1), fx["scales"].astype(np.float32)
-    return np.frombuffer(fx["hex"], dtype=np.uint8).copy(), None
+    data = np.frombuffer(fx["hex"], dtype=np.uint8).copy()
+    if fx["format"] == "i4row":
+        return data, fx["scales"].astype(np.float32)
+    return data, None
 
 
 def all_fixtures():

@@ -159,3 +159,13 @@ def pack_q6_k_block(d_bits: int, sc, q) -> bytes:
 def rows_to_array(rows_of_blocks) -> np.ndarray:
     """[[block bytes, ...] per row] -> uint8 [rows, row_bytes]."""
     return np.array([np.frombuffer(b"".join(r), dtype=np.uint8) for r in rows_of_blocks])
+
+
+def pack_i4_row(q) -> bytes:
+    """Bytes of one int4 row: codes -8..7 as 4-bit two's complement, weight
+    2k in the low nibble of byte k, 2k + 1 in the high nibble, the row
+    padded with zero codes to a multiple of 64 weights."""
+    q = [int(v) for v in q]
+    assert all(-8 <= v <= 7 for v in q)
+    q = q + [0] * (-len(q) % 64)
+    return bytes(((q[2 * k] & 15) | ((q[2 * k + 1] & 15) << 4)) for k in range(len(q) // 2))

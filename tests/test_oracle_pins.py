@@ -141,7 +141,7 @@ def test_golden_fixture(name):
 
 def test_fixture_set_covers_every_format():
     fmts = {golden_io.load(n)["format"] for n in golden_io.all_fixtures()}
-    assert fmts == {"q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row"}
+    assert fmts == {"q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row"}
 
 
 # ---------------------------------------------------------------------------
@@ -671,6 +671,62 @@ def test_swiglu_is_silu_of_gate_times_up():
     assert np.all(h0 == 0)
 
 
+@pytest.mark.parametrize("inf", [32, 64, 96, 896])
+def test_i4row_codes_and_closed_form(inf):
+    rng = np.random.default_rng([26, inf])
+    rows = 5
+    q = rng.integers(-8, 8, size=(rows, inf))
+    scales = (rng.random(rows) * 0.01).astype(np.float32)
+    data = np.array([np.frombuffer(packing.pack_i4_row(q[r]), np.uint8) for r in range(rows)])
+    assert list(oracle.i4_codes(data)[0, :inf]) == list(q[0])
+    w = oracle.dequant_i4row(data, rows, inf, scales)
+    for r in range(rows):
+        assert as_fraction_array(w[r]) == [Fraction(float(scales[r])) * int(v) for v in q[r]]
+
+
+def test_i4row_one_hot_positions():
+    for i in range(64):
+        q = [0] * 64
+        q[i] = -3
+        data = np.frombuffer(packing.pack_i4_row(q), np.uint8)
+        w = oracle.dequant_i4row(data, 1, 64, np.array([2.0], np.float32))[0]
+        assert list(np.flatnonzero(w)) == [i] and w[i] == -6.0
+
+
+@pytest.mark.parametrize("rows,inf", [(4, 32), (6, 96)])
+def test_i4row_brute_force(rows, inf):
+    rng = np.random.default_rng([27, rows])
+    q = rng.integers(-8, 8, size=(rows, inf))
+    scales = (rng.random(rows) * 0.01).astype(np.float32)
+    data = np.array([np.frombuffer(packing.pack_i4_row(q[r]), np.uint8) for r in range(rows)])
+    x = rng.standard_normal((2, inf)).astype(np.float32)
+    y, s = oracle.gemv_packed("i4row", data, rows, inf, x, None, scales)
+    for b in range(2):
+        for o in range(rows):
+            ex = sum(Fraction(float(scales[o])) * int(q[o, i]) * Fraction(float(x[b, i])) for i in range(inf))
+            assert abs(Fraction(float(y[b, o])) - ex) <= Fraction(2.0 ** -50) * Fraction(float(s[b, o]))
+
+
+def test_quantize_i4row_round_trip():
+    rng = np.random.default_rng(28)
+    w = rng.normal(0, 0.02, size=(16, 96)).astype(np.float32)
+    w[2] = 0.0
+    packed, scales = oracle.quantize_i4row(w)
+    assert packed.shape == (16, 64) and scales[2] == 0
+    codes = oracle.i4_codes(packed)[:, :96]
+    assert np.all(codes[2] == 0) and codes.min() >= -7 and codes.max() <= 7
+    for r in range(16):
+        if r == 2:
+            continue
+        assert scales[r] == np.float32(np.max(np.abs(w[r])) / 7.0)
+        assert abs(int(codes[r, int(np.argmax(np.abs(w[r])))])) == 7
+        deq = scales[r].astype(np.float64) * codes[r].astype(np.float64)
+        assert np.all(np.abs(deq - w[r]) <= scales[r] * 0.5 * (1 + 1e-6))
+    # halves round away from zero
+    p, s = oracle.quantize_i4row(np.array([[7.0, 0.5, -0.5, 1.5, -2.5] + [0.0] * 27], np.float32))
+    assert s[0] == 1.0 and list(oracle.i4_codes(p)[0, :5]) == [7, 1, -1, 2, -3]
+
+
 def test_quantize_i8row_round_trip():
     rng = np.random.default_rng(14)
     w = rng.normal(0, 0.02, size=(32, 200)).astype(np.float32)
@@ -746,6 +802,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
             out[..., b:b + 16], out[..., b + 16:b + 32] = q[..., b + 16:b + 32], q[..., b:b + 16]
         return out
 
+    good_i4 = mod.i4_codes
+
+    def i4_nibbles_swapped(packed):     # high nibble taken as the even weight
+        q = good_i4(packed)
+        out = q.copy()
+        out[..., 0::2], out[..., 1::2] = q[..., 1::2], q[..., 0::2]
+        return out
+
     def scales3_halves_swapped(S):     # scales 0..7 and 8..15 exchanged
         sc = good_scales3(S)
         return np.concatenate([sc[..., 8:], sc[..., :8]], axis=-1)
@@ -763,7 +827,8 @@ def test_planted_mistakes_are_caught(monkeypatch):
     for name, bad in [("q4_k_codes", codes4_swapped), ("q4_k_scales_mins", sm_swapped),
                       ("q4_k_scales_mins", sm_no_high_bits), ("q6_k_codes", codes6_offset),
                       ("gemv", gemv_no_bias), ("q5_k_codes", codes5_half_swapped),
-                      ("q2_k_codes", codes2_halves_swapped), ("q3_k_scales", scales3_halves_swapped)]:
+                      ("q2_k_codes", codes2_halves_swapped), ("q3_k_scales", scales3_halves_swapped),
+                      ("i4_codes", i4_nibbles_swapped)]:
         monkeypatch.setattr(mod, name, bad)
         assert not _all_dequant_fixtures_pass(), name
         monkeypatch.undo()
