@@ -31,13 +31,14 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "batch-1 dequant-GEMV HBM GB/s (% of peak), µs per Qwen2.5-0.5B decode step"
 CONFIG_INDEX = 2          # the decode-step workload
 NOMINAL_BYTES_PER_WEIGHT = {"q8_0": 34 / 32, "q2_k": 84 / 256, "q3_k": 110 / 256, "q4_k": 144 / 256,
-                            "q5_k": 176 / 256, "q6_k": 210 / 256, "i8row": 1.0}
+                            "q5_k": 176 / 256, "q6_k": 210 / 256, "i8row": 1.0,
+                            "i4row": 0.5}
 
 
 def call_bytes(fmt, out, inf, batch, has_bias):
     """Nominal algorithmic bytes of one mat-vec: packed weights at the
     format's bits per weight (no row padding), x, y and bias."""
-    w = out * inf * NOMINAL_BYTES_PER_WEIGHT[fmt] + (4 * out if fmt == "i8row" else 0)
+    w = out * inf * NOMINAL_BYTES_PER_WEIGHT[fmt] + (4 * out if fmt in ("i8row", "i4row") else 0)
     return int(w + 4 * batch * (inf + out) + (4 * out if has_bias else 0))
 
 
@@ -229,6 +230,10 @@ def suite_cases():
         for b in (1, 8):
             cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
         cases.append((f"{fmt} 4864x896 b1 (gate/up)", "gemv", (fmt, 4864, 896, 1)))
+    for b in (1, 8):
+        cases.append((f"i4row lm-head 151936x896 b{b}", "gemv", ("i4row", synth.QWEN_VOCAB, 896, b)))
+    cases += [("i4row 4864x896 b1 (gate/up)", "gemv", ("i4row", 4864, 896, 1)),
+              ("i4row 896x4864 b1 (down)", "gemv", ("i4row", 896, 4864, 1))]
     cases.append(("q8_0 gpt2 lm-head 50257x768 b1", "gemv", ("q8_0", synth.GPT2_VOCAB, 768, 1)))
     # prompt-width products on quantized weights, with the binary16-weight
     # GEMM at the same shapes for comparison
@@ -318,9 +323,9 @@ def run_suite(lib, args):
                 st = lib.pesti_gemv_group(_lib.FORMAT_IDS[fmt], nops,
                                           ctypes.cast(tables[i % copies], ctypes.c_void_p), 1, sh)
             elif kind == "gemv":
-                st = (lib.pesti_gemv_i8row(out, inf, ws[i % copies].data_ptr(), sc.data_ptr(),
-                                           x.data_ptr(), y.data_ptr(), None, batch, sh)
-                      if fmt == "i8row" else
+                st = (getattr(lib, f"pesti_gemv_{fmt}")(out, inf, ws[i % copies].data_ptr(), sc.data_ptr(),
+                                                       x.data_ptr(), y.data_ptr(), None, batch, sh)
+                      if fmt in ("i8row", "i4row") else
                       getattr(lib, f"pesti_gemv_{fmt}")(out, inf, ws[i % copies].data_ptr(),
                                                        x.data_ptr(), y.data_ptr(), None, batch, sh))
             elif kind == "qgemm":

@@ -23,7 +23,7 @@ PESTI_ERR_ALIGN = -4
 PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
 
-FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6}
+FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7}
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
@@ -36,6 +36,7 @@ _SIGNATURES = {
     "pesti_gemv_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_i4row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_group": (_c_int, [_i32, _i32, _vp, _i32, _vp]),
     "pesti_gemv_swiglu": (_c_int, [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemm_f16_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "pesti_dequant_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q6_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_i8row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
+    "pesti_dequant_i4row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
     "pesti_stream_read": (_c_int, [_vp, _i64, _vp, _vp]),
     "pesti_row_bytes": (_i64, [_i32, _i64]),
     "pesti_strerror": (_c_char_p, [_c_int]),
@@ -181,9 +183,16 @@ def pesti_gemv_i8row(out_features, in_features, codes, row_scales, x, y, bias=No
         batch, _stream(stream)))
 
 
+def pesti_gemv_i4row(out_features, in_features, packed, row_scales, x, y, bias=None, batch=1,
+                     stream=None):
+    return _check("pesti_gemv_i4row", load().pesti_gemv_i4row(
+        out_features, in_features, _ptr(packed), _ptr(row_scales), _ptr(x), _ptr(y), _ptr(bias),
+        batch, _stream(stream)))
+
+
 def pesti_gemv_swiglu(fmt, out_features, in_features, w_gate, w_up, x, h, batch=1,
                       gate_scales=None, up_scales=None, stream=None):
-    """h = silu(W_gate x) * (W_up x) in one launch (row scales for i8row only)."""
+    """h = silu(W_gate x) * (W_up x) in one launch (row scales for i8row and i4row only)."""
     fid = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
     return _check("pesti_gemv_swiglu", load().pesti_gemv_swiglu(
         fid, out_features, in_features, _ptr(w_gate), _ptr(w_up), _ptr(gate_scales), _ptr(up_scales),
@@ -280,11 +289,18 @@ def pesti_dequant_i8row(rows, in_features, codes, row_scales, w_out, stream=None
         rows, in_features, _ptr(codes), _ptr(row_scales), _ptr(w_out), _stream(stream)))
 
 
+def pesti_dequant_i4row(rows, in_features, packed, row_scales, w_out, stream=None):
+    return _check("pesti_dequant_i4row", load().pesti_dequant_i4row(
+        rows, in_features, _ptr(packed), _ptr(row_scales), _ptr(w_out), _stream(stream)))
+
+
 # --- format-generic conveniences (still marshalling only) -------------------
 def gemv(fmt, out_features, in_features, w, x, y, bias=None, batch=1, scales=None, stream=None):
     """Dispatch y = W x + b to the entry point of format `fmt`."""
     if fmt == "i8row":
         return pesti_gemv_i8row(out_features, in_features, w, scales, x, y, bias, batch, stream)
+    if fmt == "i4row":
+        return pesti_gemv_i4row(out_features, in_features, w, scales, x, y, bias, batch, stream)
     return _gemv(f"pesti_gemv_{fmt}", out_features, in_features, w, x, y, bias, batch, stream)
 
 
@@ -298,4 +314,6 @@ def gemm_quant(fmt, m, out_features, in_features, blocks, x, y, bias=None, strea
 def dequant(fmt, rows, in_features, w, w_out, scales=None, stream=None):
     if fmt == "i8row":
         return pesti_dequant_i8row(rows, in_features, w, scales, w_out, stream)
+    if fmt == "i4row":
+        return pesti_dequant_i4row(rows, in_features, w, scales, w_out, stream)
     return _dequant(f"pesti_dequant_{fmt}", rows, in_features, w, w_out, stream)

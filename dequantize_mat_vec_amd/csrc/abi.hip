@@ -47,6 +47,7 @@ int64_t pesti_row_bytes(int32_t format, int64_t in_features) {
     case PESTI_FMT_Q3_K: return ((in_features + 255) / 256) * 110;
     case PESTI_FMT_Q6_K: return ((in_features + 255) / 256) * 210;
     case PESTI_FMT_I8ROW: return in_features;
+    case PESTI_FMT_I4ROW: return ((in_features + 63) / 64) * 32;
     default: return -1;
   }
 }

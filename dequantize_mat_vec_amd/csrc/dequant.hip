@@ -179,6 +179,23 @@ __global__ __launch_bounds__(256) void dequant_i8row_kernel(DequantArgs a) {
   for (int k = 0; k < 32; ++k) o[k] = s * static_cast<float>(q[k]);
 }
 
+// i4row: weight i of a row is nibble i % 2 (low first) of byte i / 2, a
+// 4-bit two's complement code; the row is 32 bytes per 64 weights.
+__global__ __launch_bounds__(256) void dequant_i4row_kernel(DequantArgs a) {
+  const int64_t nsub = a.in / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= a.rows * nsub) return;
+  const int64_t row = t / nsub, j = t % nsub;
+  const uint8_t* q = a.w + row * a.row_bytes + j * 16;
+  const float s = a.scales[row];
+  float* o = a.out + row * a.in + j * 32;
+  for (int k = 0; k < 16; ++k) {
+    const int lo = static_cast<int>(q[k] & 15u), hi = static_cast<int>(q[k] >> 4);
+    o[2 * k] = s * static_cast<float>(lo - ((lo & 8) << 1));
+    o[2 * k + 1] = s * static_cast<float>(hi - ((hi & 8) << 1));
+  }
+}
+
 }  // namespace pesti
 
 namespace {
@@ -248,6 +265,12 @@ int pesti_dequant_i8row(int64_t rows, int64_t in_features, const int8_t* codes,
                         const float* row_scales, float* w_out, void* stream) {
   return dequant_launch(pesti::dequant_i8row_kernel, rows, in_features, codes, row_scales, w_out,
                         stream, in_features, true);
+}
+
+int pesti_dequant_i4row(int64_t rows, int64_t in_features, const void* packed,
+                        const float* row_scales, float* w_out, void* stream) {
+  return dequant_launch(pesti::dequant_i4row_kernel, rows, in_features, packed, row_scales, w_out,
+                        stream, ((in_features + 63) / 64) * 32, true);
 }
 
 }  // extern "C"

@@ -1,6 +1,6 @@
 // C entry points of the fused dequantize + mat-vec (kernels in gemv_impl.h,
 // instantiated per format in gemv_q8_0.hip, gemv_q2_k.hip, gemv_q3_k.hip,
-// gemv_q4_k.hip, gemv_q5_k.hip, gemv_q6_k.hip and gemv_i8row.hip).
+// gemv_q4_k.hip, gemv_q5_k.hip, gemv_q6_k.hip, gemv_i8row.hip and gemv_i4row.hip).
 #include "gemv_impl.h"
 
 namespace pesti {
@@ -46,6 +46,7 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
     case PESTI_FMT_Q3_K: return pesti_gemv::group_q3_k(n_ops, ops, batch, stream);
     case PESTI_FMT_Q6_K: return pesti_gemv::group_q6_k(n_ops, ops, batch, stream);
     case PESTI_FMT_I8ROW: return pesti_gemv::group_i8row(n_ops, ops, batch, stream);
+    case PESTI_FMT_I4ROW: return pesti_gemv::group_i4row(n_ops, ops, batch, stream);
     default: return PESTI_ERR_SHAPE;
   }
 }
@@ -74,6 +75,9 @@ int pesti_gemv_swiglu(int32_t format, int64_t out_features, int64_t in_features,
                                      stream);
     case PESTI_FMT_I8ROW:
       return pesti_gemv::swiglu_i8row(out_features, in_features, w_gate, w_up, gate_scales, up_scales, x, h,
+                                      batch, stream);
+    case PESTI_FMT_I4ROW:
+      return pesti_gemv::swiglu_i4row(out_features, in_features, w_gate, w_up, gate_scales, up_scales, x, h,
                                       batch, stream);
     default: return PESTI_ERR_SHAPE;
   }
@@ -120,6 +124,13 @@ int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* co
                      int32_t batch, void* stream) {
   const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, codes, row_scales, x, y, bias);
   return pesti_gemv::group_i8row(1, &o, batch, stream);
+}
+
+int pesti_gemv_i4row(int64_t out_features, int64_t in_features, const void* packed,
+                     const float* row_scales, const float* x, float* y, const float* bias,
+                     int32_t batch, void* stream) {
+  const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, packed, row_scales, x, y, bias);
+  return pesti_gemv::group_i4row(1, &o, batch, stream);
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
 // Fused dequantize + mat-vec kernels for gfx950: y = W x + b with W in
-// Q8_0, Q4_K, Q6_K or per-row int8, x and y in float32.
+// Q8_0, Q2_K .. Q6_K, per-row int8 or per-row int4, x and y in float32.
 //
 // The operation is the row-major matrix-vector product of a decode step and
 // the fused dequantize + mat-vec that never expands weights to float32
@@ -12,6 +12,9 @@
 //   Q6_K  : 128 B low nibbles | 64 B 2-bit highs | int8 sc[16] | d
 //                                                             w = d sc (q - 32)
 //   i8row : int8 q[out][in] + float32 scale[out]              w = s q
+//   i4row : 4-bit two's complement q, two per byte, rows padded to 64
+//           weights, + float32 scale[out]                     w = s q
+// (Q2_K, Q3_K and Q5_K are described beside their format structs.)
 //
 // Work decomposition (see common.h): L lanes per row, each lane walks the
 // row's units with stride L.  A unit is:
@@ -23,7 +26,8 @@
 //   Q6_K  16 consecutive positions l of one 128-weight half h, for all four
 //         32-weight groups g (64 weights from 16+16 low-part bytes and 16
 //         high-part bytes);
-//   i8row 64 consecutive code bytes.
+//   i8row 64 consecutive code bytes;
+//   i4row 32 consecutive code bytes (64 weights).
 // Each unit is split into issue() - the global loads, returning raw dwords -
 // and compute() - decode and FMA against x in LDS.  The kernel issues the
 // loads of a lane's next unit before computing the current one, and issues
@@ -46,7 +50,7 @@ namespace pesti {
 
 struct GemvArgs {
   const uint8_t* w;       // packed rows
-  const float* scales;    // i8row row scales (else null)
+  const float* scales;    // i8row / i4row row scales (else null)
   const float* x;         // [batch][in]
   float* y;               // [batch][out]
   const float* bias;      // [out] or null
@@ -57,7 +61,7 @@ struct GemvArgs {
   int64_t xpad;           // logical x length staged (zero filled past in)
   int64_t xstride;        // LDS floats per staged batch row
   const uint8_t* w2;      // paired launches: the up projection's rows
-  const float* scales2;   // paired launches: its i8row row scales
+  const float* scales2;   // paired launches: its i8row / i4row row scales
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -79,6 +83,7 @@ __device__ __forceinline__ void nibbles_x512(uint32_t v, float& a, float& b, flo
 // dwords 9..16.
 // ---------------------------------------------------------------------------
 struct FmtQ8_0x2 {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
@@ -148,6 +153,7 @@ struct FmtQ8_0x2 {
 // the upper half may lie past the buffer), so only 16 bits are read.
 // ---------------------------------------------------------------------------
 struct FmtQ8_0 {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
@@ -213,6 +219,7 @@ struct FmtQ8_0 {
 // mins are computed once per lane.
 // ---------------------------------------------------------------------------
 struct FmtQ4_K {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = true;
   static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
@@ -346,6 +353,7 @@ typedef uint32_t u32x4u2 __attribute__((ext_vector_type(4), aligned(2)));
 // the codes convert as e4m3 bytes (q * 2^-9, exact), the mins take the
 // staged 16-weight sums of x.
 struct FmtQ2_K {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = true;
   static constexpr int kSumWidth = 16;
   static constexpr int kPad = 256;
@@ -422,6 +430,7 @@ struct FmtQ2_K {
 // 0-3 at bit 4(k / 8) of byte k % 8, bits 4-5 at bit 2(k / 4) of byte
 // 8 + k % 4; w = d * (scale - 32) * q.
 struct FmtQ3_K {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 256;
@@ -501,6 +510,7 @@ struct FmtQ3_K {
 // the scale gather is Q4_K's.
 // ---------------------------------------------------------------------------
 struct FmtQ5_K {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = true;
   static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
@@ -609,6 +619,7 @@ struct FmtQ5_K {
 // one sign-extending convert yields it.
 // ---------------------------------------------------------------------------
 struct FmtQ6_K {
+  static constexpr bool kRowScales = false;
   static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 256;
@@ -719,6 +730,7 @@ struct FmtQ6_K {
 // row whose length is 32 mod 64 ends with a half unit.
 // ---------------------------------------------------------------------------
 struct FmtI8Row {
+  static constexpr bool kRowScales = true;
   static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
@@ -766,6 +778,88 @@ struct FmtI8Row {
         }
       }
     }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// i4row: 32 code bytes per unit (64 weights; rows are padded to whole
+// units).  Dword t of the unit holds weights 8t .. 8t+7, the even ones in
+// the low nibbles.  XOR with 8 turns each two's complement nibble q into
+// the offset code q + 8 in 0..15, which converts exactly as an e4m3 byte
+// ((q + 8) * 2^-9); the offset is removed per 32 weights with the staged
+// sums of x, and the row scale is applied after the sum.
+// ---------------------------------------------------------------------------
+struct FmtI4Row {
+  static constexpr bool kRowScales = true;
+  static constexpr bool kSums = true;
+  static constexpr int kSumWidth = 32;
+  static constexpr int kPad = 64;
+  struct Raw { u32x4 a, b; };
+  struct Lane {};
+  __device__ static Lane lane_state(int) { return {}; }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* p = rp + u * 32;
+    r.a = load_u32x4_a16(p);
+    r.b = load_u32x4_a16(p + 16);
+  }
+
+  __device__ __forceinline__ static uint32_t word(const Raw& r, int t) {
+    switch (t) {
+      case 0: return r.a.x;
+      case 1: return r.a.y;
+      case 2: return r.a.z;
+      case 3: return r.a.w;
+      case 4: return r.b.x;
+      case 5: return r.b.y;
+      case 6: return r.b.z;
+      default: return r.b.w;
+    }
+  }
+
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const float* sums, int64_t nsub,
+                                                 const Lane&, float* acc) {
+    float p[R][2][B];
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { p[k][0][b] = 0.f; p[k][1][b] = 0.f; }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 xa[B], xb[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        xa[b] = xs4(xs + b * a.xstride, 64 * u + 8 * t);
+        xb[b] = xs4(xs + b * a.xstride, 64 * u + 8 * t + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t v = word(r[k], t) ^ 0x88888888u;
+        float e0, e1, e2, e3, o0, o1, o2, o3;
+        nibbles_x512(v & 0x0F0F0F0Fu, e0, e1, e2, e3);
+        nibbles_x512((v >> 4) & 0x0F0F0F0Fu, o0, o1, o2, o3);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float& s = p[k][t >> 2][b];
+          s = fmaf(e0, xa[b].x, s); s = fmaf(o0, xa[b].y, s);
+          s = fmaf(e1, xa[b].z, s); s = fmaf(o1, xa[b].w, s);
+          s = fmaf(e2, xb[b].x, s); s = fmaf(o2, xb[b].y, s);
+          s = fmaf(e3, xb[b].z, s); s = fmaf(o3, xb[b].w, s);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* sb = sums + b * nsub + 2 * u;
+        float v = fmaf(512.f, p[k][0][b], -8.f * sb[0]);
+        v += fmaf(512.f, p[k][1][b], -8.f * sb[1]);
+        acc[k * B + b] += v;
+      }
   }
 };
 
@@ -1152,6 +1246,9 @@ template <> inline void shape_of<pesti::FmtQ6_K>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtI8Row>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = in; *u = (in + 63) / 64;
 }
+template <> inline void shape_of<pesti::FmtI4Row>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 63) / 64) * 32; *u = (in + 63) / 64;
+}
 
 // y[b][o] = bias[o] (or 0) for every op of `g` and b < batch (ops with
 // in_features == 0); defined in gemv.hip.
@@ -1165,7 +1262,7 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   if (o.in_features % 32 != 0 || o.in_features > PESTI_MAX_IN_FEATURES) return PESTI_ERR_SHAPE;
   const bool has_in = o.in_features > 0;
   if (!o.y || (has_in && (!o.w || !o.x))) return PESTI_ERR_NULL;
-  if (std::is_same<F, pesti::FmtI8Row>::value && has_in && !o.row_scales) return PESTI_ERR_NULL;
+  if (F::kRowScales && has_in && !o.row_scales) return PESTI_ERR_NULL;
   if (!pesti_host::aligned(o.y, 16) || (o.w && !pesti_host::aligned(o.w, 16)) ||
       (o.x && !pesti_host::aligned(o.x, 16)) || (o.bias && !pesti_host::aligned(o.bias, 4)) ||
       (o.row_scales && !pesti_host::aligned(o.row_scales, 4)))
@@ -1272,6 +1369,7 @@ int group_q3_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* str
 int group_q5_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q6_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_i8row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+int group_i4row(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 // Paired gate/up launches with the SwiGLU epilogue (swiglu_dispatch below).
 #define PESTI_SWIGLU_ARGS                                                                          \
   int64_t out_features, int64_t in_features, const void *w_gate, const void *w_up,                 \
@@ -1284,6 +1382,7 @@ int swiglu_q3_k(PESTI_SWIGLU_ARGS);
 int swiglu_q5_k(PESTI_SWIGLU_ARGS);
 int swiglu_q6_k(PESTI_SWIGLU_ARGS);
 int swiglu_i8row(PESTI_SWIGLU_ARGS);
+int swiglu_i4row(PESTI_SWIGLU_ARGS);
 
 // ---------------------------------------------------------------------------
 // Paired gate/up launch with the SwiGLU epilogue: h = silu(W_gate x) *

@@ -31,6 +31,10 @@
  *   Q6_K  210 B / 256 weights: 128 B low 4-bit parts, 64 B high 2-bit parts,
  *          int8 sc[16], binary16 d.                w = d*sc[i/16]*(q - 32)
  *   i8row int8 codes [out][in] plus one float32 scale per row. w = s[o]*q
+ *   i4row 4-bit two's complement codes (-8..7), two per byte: weight 2k in
+ *          the low nibble of byte k, 2k+1 in the high nibble; a row is
+ *          32 B per 64 weights (padded with codes that are never read into
+ *          the result), plus one float32 scale per row.      w = s[o]*q
  *
  * Layouts and conventions (every entry point)
  *   - W has out_features rows.  A packed row is ceil(in/QK) whole blocks
@@ -44,7 +48,9 @@
  *     y[b][o] = sum_i w[o][i] * x[b][i] + bias[o].
  *   - Accumulation is float32; dequantized weights are never written out.
  *     Result bound: |y - exact| <= 1e-4 * sum_i |w_i x_i| + 1e-6 for the
- *     mat-vec (2e-3 for the f16 GEMM).
+ *     mat-vec (2e-3 for the f16 GEMM).  i4row accumulates the codes with
+ *     an offset of 8 that is taken out per 32 weights, which adds
+ *     4e-5 * s[o] * sum_i |x_i| to its bound (rows of mostly zero codes).
  *   - Pointers are device pointers owned by the caller, on the calling
  *     thread's current HIP device, and must be 16-byte aligned (blocks, x,
  *     y, w, codes; bias and row_scales 4-byte aligned).  x and y must not
@@ -90,6 +96,7 @@ extern "C" {
 #define PESTI_FMT_Q5_K 4
 #define PESTI_FMT_Q2_K 5
 #define PESTI_FMT_Q3_K 6
+#define PESTI_FMT_I4ROW 7
 
 #define PESTI_MAX_BATCH 8
 #define PESTI_MAX_IN_FEATURES 32768
@@ -139,9 +146,17 @@ int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* co
                      const float* row_scales, const float* x, float* y,
                      const float* bias, int32_t batch, void* stream);
 
+/* Per-row symmetric int4 ("Project scaffold ...", quant.rs lists INT4 beside
+ * INT8): packed int4 rows of pesti_row_bytes(PESTI_FMT_I4ROW, in) bytes,
+ * row_scales float32 [out]. */
+int pesti_gemv_i4row(int64_t out_features, int64_t in_features, const void* packed,
+                     const float* row_scales, const float* x, float* y,
+                     const float* bias, int32_t batch, void* stream);
+
 /* --- grouped mat-vec: several independent products in one launch ---------
  * One mat-vec of a group: y = W x + b with the layouts above (w is the
- * packed rows, or the int8 codes for i8row; row_scales only for i8row). */
+ * packed rows, or the int8 codes for i8row; row_scales only for i8row and
+ * i4row). */
 typedef struct pesti_gemv_op {
   int64_t out_features;
   int64_t in_features;
@@ -173,9 +188,9 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
  * in one launch: each lane group computes row o of both matrices and writes
  * only h[b][o].  w_gate and w_up are two matrices of one PESTI_FMT_* format
  * and the same shape, laid out as for the single mat-vecs (no bias);
- * gate_scales / up_scales are their row scales for PESTI_FMT_I8ROW and are
- * ignored otherwise.  x float32 [batch][in], h float32 [batch][out].  Rows
- * must fit one load round: in_features up to 4096 (K family, i8row, Q8_0
+ * gate_scales / up_scales are their row scales for PESTI_FMT_I8ROW and
+ * PESTI_FMT_I4ROW and are ignored otherwise.  x float32 [batch][in], h float32 [batch][out].  Rows
+ * must fit one load round: in_features up to 4096 (K family, i8row, i4row, Q8_0
  * with in % 64 == 0) or 2048 (other Q8_0), else PESTI_ERR_SHAPE.
  * Bound: |h - exact| <= 1.1 * eg * |u| + |silu(g)| * eu + 2 * eg * eu
  * + 1e-6 * |h| + 1e-6, with eg, eu the mat-vec bounds of g and u. */
@@ -236,7 +251,7 @@ int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
  * w_out float32 [rows][in_features]: each weight rounded once from its
  * exact value (all formats here dequantize exactly in float32 except the
  * final subtraction of Q2_K / Q4_K / Q5_K and the scale product of
- * i8row). */
+ * i8row and i4row). */
 int pesti_dequant_q8_0(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks,
@@ -250,6 +265,8 @@ int pesti_dequant_q5_k(int64_t rows, int64_t in_features, const void* blocks,
 int pesti_dequant_q6_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_i8row(int64_t rows, int64_t in_features, const int8_t* codes,
+                        const float* row_scales, float* w_out, void* stream);
+int pesti_dequant_i4row(int64_t rows, int64_t in_features, const void* packed,
                         const float* row_scales, float* w_out, void* stream);
 
 /* --- measurement hook ----------------------------------------------------

@@ -46,7 +46,7 @@ def test_abi_version():
     assert dmv.pesti_abi_version() == 1
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row"])
 @pytest.mark.parametrize("inf", [0, 32, 64, 96, 256, 288, 768, 896, 4864, 16384])
 def test_row_bytes_agree_with_oracle_and_generator(fmt, inf):
     rb = dmv.pesti_row_bytes(fmt, inf)
@@ -100,6 +100,13 @@ def test_i8row_and_gemm_argument_checks():
     lib = _raw()
     assert lib.pesti_gemv_i8row(8, 64, FAKE, None, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
     assert lib.pesti_gemv_i8row(8, 64, FAKE, FAKE + 2, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemv_i4row(8, 64, FAKE, None, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_gemv_i4row(8, 64, FAKE, FAKE + 2, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemv_i4row(8, 48, FAKE, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_i4row(8, 64, FAKE + 8, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemv_i4row(0, 64, None, None, None, None, None, 1, None) == _lib.PESTI_OK
+    assert lib.pesti_dequant_i4row(4, 64, FAKE, None, FAKE, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_dequant_i4row(4, 40, FAKE, FAKE, FAKE, None) == _lib.PESTI_ERR_SHAPE
     assert lib.pesti_gemm_f16_smallm(-1, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
     assert lib.pesti_gemm_f16_smallm(5000, 8, 64, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_BATCH
     assert lib.pesti_gemm_f16_smallm(4, 8, 40, FAKE, FAKE, FAKE, None, None) == _lib.PESTI_ERR_SHAPE
@@ -182,7 +189,8 @@ def test_group_argument_checks():
     ops = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None)] * 2)
     ptr = ctypes.cast(ops, ctypes.c_void_p)
     assert lib.pesti_gemv_group(0, 9, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
-    assert lib.pesti_gemv_group(7, 2, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_group(8, 2, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_group(7, 2, ptr, 1, None) == _lib.PESTI_ERR_NULL   # i4row without row scales
     assert lib.pesti_gemv_group(1, 2, None, 1, None) == _lib.PESTI_ERR_NULL
     assert lib.pesti_gemv_group(1, 2, ptr, 9, None) == _lib.PESTI_ERR_BATCH
     bad = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None), (8, 48, FAKE, FAKE, FAKE, None, None)])

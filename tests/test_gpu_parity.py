@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 GEMV_REL = 1e-4
 GEMM_REL = 2e-3
-FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row")
+FORMATS = ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row")
 
 
 @pytest.fixture(autouse=True)
@@ -194,7 +194,7 @@ def test_in_features_zero_gives_bias(fmt):
     from gpu_util import guarded_y, guards_intact, to_dev
     import dequantize_mat_vec_amd as dmv
     fbuf, y = guarded_y(2 * 21)
-    scales = to_dev(np.ones(21, np.float32)) if fmt == "i8row" else None
+    scales = to_dev(np.ones(21, np.float32)) if fmt in ("i8row", "i4row") else None
     dmv.gemv(fmt, 21, 0, None, None, y, to_dev(bias), 2, scales=scales)
     torch.cuda.synchronize()
     assert guards_intact(fbuf, 42)
@@ -241,6 +241,40 @@ def test_q6_k_all_codes_32_is_zero():
     assert np.array_equal(y[0], bias)
 
 
+def test_i4row_padding_codes_do_not_matter():
+    """Rows of 800 weights take 13 units of 64; the last 16 bytes of every
+    row are padding codes and never reach the result."""
+    out, inf = 45, 800
+    packed, scales, x, bias = make("i4row", out, inf, 14, 2)
+    other = packed.copy().reshape(out, -1)
+    assert other.shape[1] == 13 * 32
+    other[:, 400:] = np.random.default_rng(15).integers(0, 256, (out, 16), dtype=np.uint8)
+    y1 = run_gemv("i4row", packed, scales, out, inf, x, bias)
+    y2 = run_gemv("i4row", other, scales, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
+    assert_within(y1, y_ref, s_ref, GEMV_REL, "i4row in=800")
+
+
+@pytest.mark.parametrize("density", [0.0, 0.02, 0.3])
+def test_i4row_sparse_codes_within_offset_bound(density):
+    """The int4 kernel carries each code with an offset of 8 that it takes
+    out per 32 weights; rows of mostly zero codes are held to the stated
+    bound 1e-4 * sum|w x| + 4e-5 * s * sum|x| + 1e-6."""
+    import packing
+    rng = np.random.default_rng([16, int(density * 100)])
+    out, inf, batch = 96, 4864, 2
+    q = rng.integers(-8, 8, (out, inf)) * (rng.random((out, inf)) < density)
+    packed = np.array([np.frombuffer(packing.pack_i4_row(q[r]), np.uint8) for r in range(out)])
+    scales = (0.005 + 0.01 * rng.random(out)).astype(np.float32)
+    x = synth.activations(rng, batch, inf)
+    y = run_gemv("i4row", packed, scales, out, inf, x)
+    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, None, scales)
+    extra = 4e-5 * scales.astype(np.float64)[None, :] * np.abs(x.astype(np.float64)).sum(axis=1)[:, None]
+    err = np.abs(y.astype(np.float64) - y_ref)
+    assert np.all(err <= GEMV_REL * s_ref + extra + 1e-6), float((err - GEMV_REL * s_ref - extra).max())
+
+
 def test_q8_0_zero_codes_is_exact_bias():
     rng = np.random.default_rng(11)
     out, inf = 20, 896
@@ -272,7 +306,8 @@ FULL = [("q8_0", synth.QWEN_VOCAB, 896, 1), ("q8_0", synth.QWEN_VOCAB, 896, 8),
         ("q4_k", 128, 896, 1), ("i8row", 896, 896, 1),
         ("q5_k", synth.QWEN_VOCAB, 896, 1), ("q5_k", 4864, 896, 1), ("q5_k", 896, 4864, 3),
         ("q2_k", synth.QWEN_VOCAB, 896, 1), ("q2_k", 896, 4864, 2), ("q3_k", synth.QWEN_VOCAB, 896, 1),
-        ("q3_k", 896, 4864, 4)]
+        ("q3_k", 896, 4864, 4), ("i4row", synth.QWEN_VOCAB, 896, 1), ("i4row", 4864, 896, 2),
+        ("i4row", 896, 4864, 1)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", FULL)
@@ -517,7 +552,8 @@ TALL = [("q8_0", 65536 + 37, 64, 1), ("q8_0", 131072 + 53, 64, 3), ("q8_0", 1310
         ("q6_k", 65536 + 37, 256, 1), ("q6_k", 131072 + 53, 256, 8), ("q6_k", 65536 + 5, 1280, 1),
         ("i8row", 131072 + 53, 64, 1), ("i8row", 65536 + 37, 160, 4),
         ("q5_k", 65536 + 37, 256, 2), ("q5_k", 131072 + 53, 896, 1),
-        ("q2_k", 65536 + 37, 256, 3), ("q3_k", 131072 + 53, 896, 1), ("q3_k", 65536 + 5, 1280, 2)]
+        ("q2_k", 65536 + 37, 256, 3), ("q3_k", 131072 + 53, 896, 1), ("q3_k", 65536 + 5, 1280, 2),
+        ("i4row", 131072 + 53, 64, 1), ("i4row", 65536 + 37, 800, 3)]
 
 
 @pytest.mark.parametrize("fmt,out,inf,batch", TALL)
