@@ -998,9 +998,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   static_assert(R == 1 || L < 64 || U == 1, "several rows per lane group need short rows");
   static_assert(!P || (R == 1 && L < 64) || R == 2, "paired rows: lane-group pairs or two rows per group");
 
-  // blockIdx.y picks the op, so the op's arguments are read in one round
-  // trip without first scanning the group.
+  // blockIdx.y picks the op, so the op's arguments are read without first
+  // scanning the group.  All of its fields are loaded before the first
+  // branch: left to itself the compiler sinks each scalar load to its
+  // first use behind the branches below, which costs a kernel-argument
+  // round trip per branch before the first weight load is issued.
   const GemvArgs a = g.op[blockIdx.y];
+  asm volatile("" ::"s"(a.w), "s"(a.scales), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in),
+               "s"(a.row_bytes), "s"(a.units), "s"(a.xpad), "s"(a.xstride));
+  if constexpr (P) asm volatile("" ::"s"(a.w2), "s"(a.scales2));
   const int64_t tile = blockIdx.x;
   const int64_t first = tile * kRowsPerTile;
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
@@ -1055,6 +1061,25 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   // A lane's unit j (j < ipt): sub + L*j when it exists, else unit 0 of the
   // same row as an in-bounds stand-in (loads stay branch-free).
   auto unit = [&](int j) { return (j < ipt && live(j)) ? sub + L * j : 0; };
+  // The epilogue's per-row operands (bias, row scales) are loaded with the
+  // weights, not after the reduction, where they would add a memory round
+  // trip to the end of the launch.  Each lane loads those of the row it may
+  // store (row `sub` of its R, or the pair's gate row); absent operands and
+  // rows past the end read a stand-in inside the lane's weight row (loads
+  // stay branch-free), and the value is not used.
+  float ep[3] = {0.f, 0.f, 0.f};
+  auto epilogue_loads = [&]() {
+    int er;
+    if constexpr (P && R == 1) er = rofs >> 1;
+    else if constexpr (P) er = rofs;
+    else er = rofs + (sub < R ? sub : 0) * kRowsPerSlab;
+    const bool in_rows = er < left;
+    const float* stand_in = reinterpret_cast<const float*>(tile_base);   // 4-byte aligned
+    const int64_t row = first + er;
+    ep[0] = *((a.bias && in_rows) ? a.bias + row : stand_in);
+    ep[1] = *((a.scales && in_rows) ? a.scales + row : stand_in);
+    ep[2] = P ? *((a.scales2 && in_rows) ? a.scales2 + row : stand_in) : 0.f;
+  };
   if (ipt <= U) {
     // All of a lane's units are loaded at once.
     typename F::Raw r[U][R];
@@ -1068,6 +1093,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
       for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), r[j][k]);
     }
+    epilogue_loads();
     if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
     stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
@@ -1082,6 +1108,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     // stand-in load past the last unit keeps the loop branch-free.
     typename F::Raw ra[1], rb[1];
     issue_unit<F>(a, rp[0], unit(0), ra[0]);
+    epilogue_loads();
     if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
     stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
     __syncthreads();
@@ -1105,8 +1132,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     const int pr = rofs >> 1;
     if (sub == 0 && (rofs & 1) == 0 && pr < left) {
       const int64_t row = first + pr;
-      const float rs0 = a.scales ? a.scales[row] : 1.f;
-      const float rs1 = a.scales2 ? a.scales2[row] : 1.f;
+      const float rs0 = a.scales ? ep[1] : 1.f;
+      const float rs1 = a.scales2 ? ep[2] : 1.f;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float gv = acc[b] * rs0;
@@ -1118,8 +1145,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   } else if constexpr (P) {
     if (sub == 0 && rofs < left) {
       const int64_t row = first + rofs;
-      const float rs0 = a.scales ? a.scales[row] : 1.f;
-      const float rs1 = a.scales2 ? a.scales2[row] : 1.f;
+      const float rs0 = a.scales ? ep[1] : 1.f;
+      const float rs1 = a.scales2 ? ep[2] : 1.f;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float gv = acc[b] * rs0;
@@ -1134,8 +1161,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     const int r = rofs + k * kRowsPerSlab;
     if (sub == k && r < left) {
       const int64_t row = first + r;
-      const float bv = a.bias ? a.bias[row] : 0.f;
-      const float rs = a.scales ? a.scales[row] : 1.f;
+      const float bv = a.bias ? ep[0] : 0.f;
+      const float rs = a.scales ? ep[1] : 1.f;
 #pragma unroll
       for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[k * B + b], rs, bv);
     }
