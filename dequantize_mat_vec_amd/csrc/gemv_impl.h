@@ -896,8 +896,10 @@ __device__ __forceinline__ void stage_load(const GemvArgs& a, int base, XChunk<B
 #pragma unroll
     for (int r = 0; r < XS; ++r) {
       const int s = base + r * kThreads + tid;
-      const f32x4 t = src[s < in4 ? s : 0];   // branch-free: slot 0 stands in
-      c.v[b][r] = s < in4 ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+      // Branch-free: slot 0 stands in past the row, and stage_store zeroes
+      // it there.  Selecting here would make the kernel wait for x before
+      // the branch that issues the weight loads.
+      c.v[b][r] = src[s < in4 ? s : 0];
     }
   }
 }
@@ -907,6 +909,7 @@ __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float*
                                             const XChunk<B, XS>& c) {
   static_assert(SW == 16 || SW == 32, "sums over 16 or 32 weights");
   const int n4 = static_cast<int>(a.xpad >> 2);   // float4 slots per batch row
+  const int in4 = static_cast<int>(a.in >> 2);
   const int nsub = static_cast<int>(a.xpad / SW);
   const int tid = static_cast<int>(threadIdx.x);
 #pragma unroll
@@ -915,7 +918,7 @@ __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float*
 #pragma unroll
     for (int r = 0; r < XS; ++r) {
       const int s = base + r * kThreads + tid;
-      const f32x4 v = c.v[b][r];
+      const f32x4 v = s < in4 ? c.v[b][r] : f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < n4) *reinterpret_cast<f32x4*>(dst + xs_phys(4 * s)) = v;
       if constexpr (kSums) {
         float part = (v.x + v.y) + (v.z + v.w);
@@ -1080,10 +1083,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     ep[1] = *((a.scales && in_rows) ? a.scales + row : stand_in);
     ep[2] = P ? *((a.scales2 && in_rows) ? a.scales2 + row : stand_in) : 0.f;
   };
-  if (ipt <= U) {
-    // All of a lane's units are loaded at once.
-    typename F::Raw r[U][R];
-    bool have[U];
+  // Rows of more than U units exist only for whole-wave lane groups (16
+  // and 32 lanes per row always hold all units at once); such a lane walks
+  // its units with two register buffers.  Both paths issue their first
+  // weight loads in their own branch and then share the x staging, so no
+  // use of x can be hoisted above the weight loads (which would make the
+  // launch wait for x before asking for its weights).
+  constexpr bool kWalk = R == 1 && L == 64;
+  const bool at_once = !kWalk || ipt <= U;
+  typename F::Raw r[U][R];
+  typename F::Raw rb[1];   // the walk's second buffer
+  bool have[U];
+  if (at_once) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       // Every lane loads (lanes without a unit load unit 0 of their row, in
@@ -1093,31 +1104,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
 #pragma unroll
       for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), r[j][k]);
     }
-    epilogue_loads();
-    if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
-    stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
-    __syncthreads();
+  } else if constexpr (kWalk) {
+    issue_unit<F>(a, rp[0], unit(0), r[0][0]);
+    issue_unit<F>(a, rp[0], unit(1), rb[0]);
+  }
+  epilogue_loads();
+  if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
+  stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
+  __syncthreads();
+  if (at_once) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
       if (have[j]) F::template compute<B, R>(a, r[j], sub + L * j, xs, sums, nsub, ls, acc);
-  } else if constexpr (R == 1 && L == 64) {
-    // Rows longer than U units (whole-wave lane groups only: 16 and 32
-    // lanes per row always hold all units at once): the lane walks its
-    // units with two register buffers, the
-    // next unit's loads in flight while the current one is decoded.  One
-    // stand-in load past the last unit keeps the loop branch-free.
-    typename F::Raw ra[1], rb[1];
-    issue_unit<F>(a, rp[0], unit(0), ra[0]);
-    epilogue_loads();
-    if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
-    stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
-    __syncthreads();
+  } else if constexpr (kWalk) {
+    // Two units in flight: unit j + 2 is requested as soon as unit j's
+    // registers are free.  Requests past the last unit read unit 0 (in
+    // bounds, unused), which keeps the loop branch-free.
     for (int j = 0; j < ipt; j += 2) {
-      issue_unit<F>(a, rp[0], unit(j + 1), rb[0]);
-      if (live(j)) F::template compute<B, 1>(a, ra, sub + L * j, xs, sums, nsub, ls, acc);
+      if (live(j)) F::template compute<B, 1>(a, r[0], sub + L * j, xs, sums, nsub, ls, acc);
       if (j + 1 >= ipt) break;
-      issue_unit<F>(a, rp[0], unit(j + 2), ra[0]);
+      issue_unit<F>(a, rp[0], unit(j + 2), r[0][0]);
       if (live(j + 1)) F::template compute<B, 1>(a, rb, sub + L * (j + 1), xs, sums, nsub, ls, acc);
+      issue_unit<F>(a, rp[0], unit(j + 3), rb[0]);
     }
   }
 #pragma unroll
