@@ -1305,6 +1305,28 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   return PESTI_OK;
 }
 
+// Q4_K ops of at least this many rows, with rows of at most 1024 weights,
+// at batch kMfmaMinBatch..8 go to the matrix-core mat-vec (gemv_mfma.hip);
+// measured on the 151936 x 896 LM head it overtakes the vector-ALU kernel
+// from batch 3.  The choice depends on the op alone (never on the other
+// ops of a group), so a grouped op gives the same bits as its own single
+// call.
+#ifndef PESTI_MFMA_MIN_ROWS
+#define PESTI_MFMA_MIN_ROWS 16384
+#endif
+#ifndef PESTI_MFMA_MIN_BATCH
+#define PESTI_MFMA_MIN_BATCH 3
+#endif
+constexpr int64_t kMfmaMinRows = PESTI_MFMA_MIN_ROWS;
+constexpr int kMfmaMinBatch = PESTI_MFMA_MIN_BATCH;
+inline bool mfma_q4_k_op(const GemvArgs& a, int batch) {
+  return batch >= kMfmaMinBatch && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows && a.in > 0 &&
+         a.in <= 1024;
+}
+// One launch of ops that all pass mfma_q4_k_op and share one row length in
+// super-blocks; x and y of every op set.
+int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st);
+
 template <class F>
 int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
   if (n_ops < 0 || n_ops > PESTI_MAX_GROUP) return PESTI_ERR_SHAPE;
@@ -1361,6 +1383,40 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     if (r != PESTI_OK) return r;
   }
   if (n_mv == 0) return PESTI_OK;
+  if constexpr (std::is_same<F, pesti::FmtQ4_K>::value) {
+    // Matrix-core ops leave the group: one launch per row length (every
+    // batch column at once); the rest stay for the vector-ALU kernel.
+    GroupArgs rest{};
+    int rest_live[PESTI_MAX_GROUP];
+    bool taken[PESTI_MAX_GROUP] = {};
+    for (int i = 0; i < n_mv; ++i) {
+      if (taken[i] || !mfma_q4_k_op(g.op[i], batch)) continue;
+      GroupArgs m{};
+      for (int j = i; j < n_mv; ++j) {
+        if (taken[j] || !mfma_q4_k_op(g.op[j], batch) || g.op[j].row_bytes != g.op[i].row_bytes) continue;
+        taken[j] = true;
+        m.op[m.n_ops] = g.op[j];
+        m.op[m.n_ops].x = ops[live[j]].x;
+        m.op[m.n_ops].y = ops[live[j]].y;
+        ++m.n_ops;
+      }
+      const int r = launch_mfma_q4_k(m, batch, stream_h);
+      if (r != PESTI_OK) return r;
+    }
+    max_units = 0;
+    max_out = 0;
+    for (int i = 0; i < n_mv; ++i) {
+      if (taken[i]) continue;
+      rest_live[rest.n_ops] = live[i];
+      rest.op[rest.n_ops++] = g.op[i];
+      if (g.op[i].units > max_units) max_units = g.op[i].units;
+      if (g.op[i].out > max_out) max_out = g.op[i].out;
+    }
+    if (rest.n_ops == 0) return PESTI_OK;
+    g = rest;
+    n_mv = rest.n_ops;
+    for (int i = 0; i < n_mv; ++i) live[i] = rest_live[i];
+  }
   const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
   for (int b0 = 0; b0 < batch; b0 += per_launch) {
