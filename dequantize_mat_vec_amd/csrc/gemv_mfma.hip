@@ -30,7 +30,7 @@
 // tile, the same k (code bytes 32g + 8kg..+7 of the run g = j / 2, low
 // nibbles for even sub-blocks j, high for odd); C = column n, rows
 // 4kg..4kg+3, i.e. batch columns 2kg and 2kg + 1 of row n.  A workgroup is
-// 4 waves = 64 rows; all of a lane's code and header loads are issued
+// 8 waves = 128 rows; all of a lane's code and header loads are issued
 // before x is staged, so a launch costs one memory round trip.
 #include "gemv_impl.h"
 
@@ -40,8 +40,17 @@ typedef _Float16 mhalf8 __attribute__((ext_vector_type(8)));
 typedef float mfloat4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(8)));
 
+// Wavefronts per workgroup: a workgroup stages x once and serves 16 rows
+// per wave.  Measured on the 151936 x 896 LM head (batch 1 / 4 / 8): 1 wave
+// 26.3 / 42.3 / 82.2 us, 2 waves 24.7 / 32.2 / 44.4, 4 waves 24.9 / 28.2 /
+// 31.3, 8 waves 24.7 / 26.3 / 30.0, 16 waves 35.3 / 36.9 / 37.8.
+#ifndef PESTI_MFMA_WAVES
+#define PESTI_MFMA_WAVES 8
+#endif
+constexpr int kMfmaWaves = PESTI_MFMA_WAVES;
+constexpr int kMfmaThreads = kMfmaWaves * kWave;
 constexpr int kMfmaTileRows = 16;
-constexpr int kMfmaGroupRows = kWavesPerGroup * kMfmaTileRows;
+constexpr int kMfmaGroupRows = kMfmaWaves * kMfmaTileRows;
 
 // Scale and min of sub-block j (0..7) from the header dwords y, z, w
 // (bytes S[0..11]): j < 4: sc = S[j] & 63, m = S[j+4] & 63; j >= 4:
@@ -93,7 +102,7 @@ __device__ __forceinline__ void q4k_step(const u32x2& c, const u32x4& hdr, float
 
 // NSB = super-blocks per row (every op of the launch has this many).
 template <int B, int NSB>
-__global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(GroupArgs g) {
+__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g) {
   extern __shared__ float lds[];
   static_assert(B >= 1 && B <= 8 && NSB >= 1 && NSB <= 4, "batch 1..8, rows of at most 1024 weights");
   // The op's arguments, all loaded before the first branch (see gemv_kernel).
@@ -112,13 +121,13 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(GroupArgs g) {
   // (8 floats at 32 s + 8 q); items past the end load item 0 (in bounds)
   // and store nothing.  Branch-free, so the weight loads below are issued
   // while x is in flight.
-  constexpr int kRounds = (B * NSB + 7) / 8;   // B * nsteps * 4 <= 32 * B * NSB items
+  constexpr int kRounds = (32 * B * NSB + kMfmaThreads - 1) / kMfmaThreads;   // B * nsteps * 4 <= 32 B NSB items
   const int per_b = nsteps * 4;
   const int total = B * per_b;
   f32x4 xv[kRounds][2];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    const int item = tid + r * kThreads;
+    const int item = tid + r * kMfmaThreads;
     const int it = item < total ? item : 0;
     const int b = it / per_b;
     const float* src = a.x + b * a.in + 8 * (it - b * per_b);
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_q4k_kernel(GroupArgs g) {
   if (tid < 16) reinterpret_cast<float*>(zero_row)[tid] = 0.f;
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    const int item = tid + r * kThreads;
+    const int item = tid + r * kMfmaThreads;
     const float v[8] = {xv[r][0].x, xv[r][0].y, xv[r][0].z, xv[r][0].w,
                         xv[r][1].x, xv[r][1].y, xv[r][1].z, xv[r][1].w};
     float mx = 0.f;
@@ -244,7 +253,7 @@ int launch_mfma_bn(const GroupArgs& g, hipStream_t st) {
   void* params[] = {&args};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_mfma_q4k_kernel<B, NSB>),
                                        dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(g.n_ops)),
-                                       dim3(pesti::kThreads), params, lds, st);
+                                       dim3(pesti::kMfmaThreads), params, lds, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
