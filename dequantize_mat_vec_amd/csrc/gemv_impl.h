@@ -1305,27 +1305,40 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   return PESTI_OK;
 }
 
-// Q4_K ops of at least this many rows, with rows of at most 1024 weights,
-// at batch kMfmaMinBatch..8 go to the matrix-core mat-vec (gemv_mfma.hip);
-// measured on the 151936 x 896 LM head it overtakes the vector-ALU kernel
-// from batch 3.  The choice depends on the op alone (never on the other
-// ops of a group), so a grouped op gives the same bits as its own single
-// call.
+// Q4_K and Q6_K ops of at least this many rows, with rows of at most 1024
+// weights, at batch kMfmaMinBatch..8 go to the matrix-core mat-vec
+// (gemv_mfma.hip); measured on the 151936 x 896 LM head it overtakes the
+// vector-ALU kernel from batch 3 (Q4_K) and batch 5 (Q6_K).  The choice depends on the op alone (never on the other ops of
+// a group), so a grouped op gives the same bits as its own single call.
 #ifndef PESTI_MFMA_MIN_ROWS
 #define PESTI_MFMA_MIN_ROWS 16384
 #endif
 #ifndef PESTI_MFMA_MIN_BATCH
 #define PESTI_MFMA_MIN_BATCH 3
 #endif
+#ifndef PESTI_MFMA_MIN_BATCH_Q6_K
+#define PESTI_MFMA_MIN_BATCH_Q6_K 5
+#endif
 constexpr int64_t kMfmaMinRows = PESTI_MFMA_MIN_ROWS;
-constexpr int kMfmaMinBatch = PESTI_MFMA_MIN_BATCH;
-inline bool mfma_q4_k_op(const GemvArgs& a, int batch) {
-  return batch >= kMfmaMinBatch && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows && a.in > 0 &&
-         a.in <= 1024;
+template <class F>
+constexpr int kMfmaMinBatch = std::is_same<F, pesti::FmtQ6_K>::value ? PESTI_MFMA_MIN_BATCH_Q6_K
+                                                                     : PESTI_MFMA_MIN_BATCH;
+template <class F>
+constexpr bool kHasMfma = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ6_K>::value;
+template <class F>
+inline bool mfma_op(const GemvArgs& a, int batch) {
+  return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
+         a.in > 0 && a.in <= 1024;
 }
-// One launch of ops that all pass mfma_q4_k_op and share one row length in
+// One launch of ops that all pass mfma_op and share one row length in
 // super-blocks; x and y of every op set.
 int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_mfma_q6_k(const GroupArgs& g, int batch, hipStream_t st);
+template <class F>
+inline int launch_mfma(const GroupArgs& g, int batch, hipStream_t st) {
+  if constexpr (std::is_same<F, pesti::FmtQ6_K>::value) return launch_mfma_q6_k(g, batch, st);
+  else return launch_mfma_q4_k(g, batch, st);
+}
 
 template <class F>
 int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream) {
@@ -1383,24 +1396,24 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     if (r != PESTI_OK) return r;
   }
   if (n_mv == 0) return PESTI_OK;
-  if constexpr (std::is_same<F, pesti::FmtQ4_K>::value) {
+  if constexpr (kHasMfma<F>) {
     // Matrix-core ops leave the group: one launch per row length (every
     // batch column at once); the rest stay for the vector-ALU kernel.
     GroupArgs rest{};
     int rest_live[PESTI_MAX_GROUP];
     bool taken[PESTI_MAX_GROUP] = {};
     for (int i = 0; i < n_mv; ++i) {
-      if (taken[i] || !mfma_q4_k_op(g.op[i], batch)) continue;
+      if (taken[i] || !mfma_op<F>(g.op[i], batch)) continue;
       GroupArgs m{};
       for (int j = i; j < n_mv; ++j) {
-        if (taken[j] || !mfma_q4_k_op(g.op[j], batch) || g.op[j].row_bytes != g.op[i].row_bytes) continue;
+        if (taken[j] || !mfma_op<F>(g.op[j], batch) || g.op[j].row_bytes != g.op[i].row_bytes) continue;
         taken[j] = true;
         m.op[m.n_ops] = g.op[j];
         m.op[m.n_ops].x = ops[live[j]].x;
         m.op[m.n_ops].y = ops[live[j]].y;
         ++m.n_ops;
       }
-      const int r = launch_mfma_q4_k(m, batch, stream_h);
+      const int r = launch_mfma<F>(m, batch, stream_h);
       if (r != PESTI_OK) return r;
     }
     max_units = 0;

@@ -1,13 +1,14 @@
-// Matrix-core mat-vec for tall Q4_K matrices (the LM head, wide projections):
-// y = W x + b with W in Q4_K, x and y in float32, batch 1..8, rows of at
-// most 1024 weights.
+// Matrix-core mat-vec for tall Q4_K and Q6_K matrices (the LM head):
+// y = W x + b with W in Q4_K or Q6_K, x and y in float32, batch 1..8, rows
+// of at most 1024 weights.
 //
 // The operation is the decode step's row-major matrix-vector product with
 // the weights kept quantized ("Project scaffold: modules, CLI, and
 // correctness harness", file summaries of tensor.rs and quant.rs); the
-// block layout is the GGUF Q4_K one of "PESTI - Portable Execution
-// Substrate for Transformer Inference" ("What This Is"), w = d sc q - dmin m
-// per 32-weight sub-block.
+// block layouts are the GGUF ones of "PESTI - Portable Execution
+// Substrate for Transformer Inference" ("What This Is"): Q4_K w = d sc q -
+// dmin m per 32-weight sub-block, Q6_K w = d sc (q - 32) per 16 weights
+// (the Q6_K steps are described at MfmaQ6K).
 //
 // At batch 1 the vector-ALU kernel spends one FMA, half a convert and a
 // quarter of a mask per weight, which on the 151936-row LM head is more
@@ -100,9 +101,149 @@ __device__ __forceinline__ void q4k_step(const u32x2& c, const u32x4& hdr, float
   }
 }
 
-// NSB = super-blocks per row (every op of the launch has this many).
-template <int B, int NSB>
-__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g) {
+// ---------------------------------------------------------------------------
+// Per-format parts of the kernel: a row's loads (every super-block of the
+// lane's row, issued at once) and its k-steps.  xa / xb: the lane's x
+// operand for the step's product(s) (see the kernel), es0 / es1: (2^-e,
+// block sum) of the lane's two batch columns per block.
+// ---------------------------------------------------------------------------
+struct MfmaQ4K {
+  static constexpr int kBytes = 144;
+  template <int NSB>
+  struct Tile {
+    u32x4 hdr[NSB];
+    u32x2 cw[NSB][4];
+  };
+  // the header and the lane's 8 code bytes of each 64-weight run
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const uint8_t* sb = rp + 144 * S;
+      w.hdr[S] = load_u32x4_a16(sb);
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        w.cw[S][gi] = *reinterpret_cast<const u32x2*>(sb + 16 + 32 * gi + 8 * kg);
+    }
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const float d512 = f16_lo(w.hdr[S].x) * 512.0f;
+      const float dmin = f16_hi(w.hdr[S].x);
+      const int s0 = 8 * S;
+      // Sub-blocks past in (a padded super-block) are skipped (uniform).
+#define PESTI_Q4K_STEP(J)                                                                          \
+      if (s0 + J < nsteps)                                                                         \
+        q4k_step<B, J>(w.cw[S][J / 2], w.hdr[S], d512, dmin, xa + (s0 + J) * xsa, es0[s0 + J],     \
+                       es1[s0 + J], acc0, acc1);
+      PESTI_Q4K_STEP(0) PESTI_Q4K_STEP(1) PESTI_Q4K_STEP(2) PESTI_Q4K_STEP(3)
+      PESTI_Q4K_STEP(4) PESTI_Q4K_STEP(5) PESTI_Q4K_STEP(6) PESTI_Q4K_STEP(7)
+#undef PESTI_Q4K_STEP
+    }
+  }
+};
+
+// Q6_K (210-byte super-blocks: ql[128], qh[64], int8 sc[16], d).  k-step
+// s = 8S + 4h + g covers weights 128h + 32g + l, l = 0..31, of super-block
+// S: low 4 bits in ql[64h + 32(g % 2) + l] (low nibble for g < 2, high
+// for g >= 2), high 2 bits at bit 2g of qh[32h + l].  Lane kg holds
+// l = 8kg..8kg+7, so lanes kg < 2 belong to 16-weight sub-block 8h + 2g and
+// lanes kg >= 2 to sub-block 8h + 2g + 1: each step is two products with
+// the same codes, one against x with the second half's lanes pointed at a
+// zero row (xa), one with the first half's (xb), each scaled by its own
+// d sc.  The codes enter as q - 32 (binary16 1024 + q built by a byte
+// permute, minus 1056: exact).  Super-blocks sit 2 bytes off a dword
+// boundary every other one; their pieces are read with 2-byte-aligned
+// loads.
+typedef uint32_t u32x2u2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef _Float16 mhalf2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t q6k_pair(uint32_t q, uint32_t sel) {
+  // bytes [q_i, 0x64, q_j, 0x64]: binary16 1024 + q_i, 1024 + q_j; minus 1056
+  const uint32_t v = __builtin_amdgcn_perm(0x64646464u, q, sel);
+  const mhalf2 h = __builtin_bit_cast(mhalf2, v) + mhalf2{static_cast<_Float16>(-1056.0f),
+                                                          static_cast<_Float16>(-1056.0f)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+struct MfmaQ6K {
+  static constexpr int kBytes = 210;
+  template <int NSB>
+  struct Tile {
+    u32x2u2 lo[NSB][2][2];   // [S][h][g % 2]: ql bytes 64h + 32(g % 2) + 8kg..+7
+    u32x2u2 hq[NSB][2];      // [S][h]: qh bytes 128 + 32h + 8kg..+7
+    u32x4u2 sc[NSB];         // the 16 scales
+    uint32_t d[NSB];
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const uint8_t* sb = rp + 210 * S;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        w.lo[S][h][0] = *reinterpret_cast<const u32x2u2*>(sb + 64 * h + 8 * kg);
+        w.lo[S][h][1] = *reinterpret_cast<const u32x2u2*>(sb + 64 * h + 32 + 8 * kg);
+        w.hq[S][h] = *reinterpret_cast<const u32x2u2*>(sb + 128 + 32 * h + 8 * kg);
+      }
+      w.sc[S] = *reinterpret_cast<const u32x4u2*>(sb + 192);
+      w.d[S] = load_u16(sb + 208);
+    }
+  }
+  template <int B, int H, int G>
+  __device__ __forceinline__ static void step(const u32x2u2& l, const u32x2u2& hq, const u32x4u2& scv, float d,
+                                              const uint8_t* xa, const uint8_t* xb, const f32x2& e0,
+                                              const f32x2& e1, float& acc0, float& acc1) {
+    constexpr int kLoShift = 4 * (G >> 1);
+    constexpr int kHiShift = 2 * G;
+    const uint32_t q0 = ((l.x >> kLoShift) & 0x0F0F0F0Fu) | (((hq.x >> kHiShift) & 0x03030303u) << 4);
+    const uint32_t q1 = ((l.y >> kLoShift) & 0x0F0F0F0Fu) | (((hq.y >> kHiShift) & 0x03030303u) << 4);
+    uint32_t hw[4];
+    hw[0] = q6k_pair(q0, 0x04010400u);
+    hw[1] = q6k_pair(q0, 0x04030402u);
+    hw[2] = q6k_pair(q1, 0x04010400u);
+    hw[3] = q6k_pair(q1, 0x04030402u);
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
+    const mhalf8 x0 = *reinterpret_cast<const mhalf8*>(xa);
+    const mhalf8 x1 = *reinterpret_cast<const mhalf8*>(xb);
+    const mfloat4 pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const mfloat4 pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    // scales 8H + 2G and 8H + 2G + 1: bytes 2G, 2G + 1 of dword 2H + G / 2
+    constexpr int kSc = 8 * H + 2 * G;
+    const uint32_t sw = kSc < 4 ? scv.x : (kSc < 8 ? scv.y : (kSc < 12 ? scv.z : scv.w));
+    const float da = d * static_cast<float>(static_cast<int8_t>(sw >> (8 * (kSc & 3))));
+    const float db = d * static_cast<float>(static_cast<int8_t>(sw >> (8 * ((kSc & 3) + 1))));
+    acc0 = fmaf(e0.x, fmaf(da, pa[0] + pa[1], db * (pb[0] + pb[1])), acc0);
+    if constexpr (B > 1) acc1 = fmaf(e1.x, fmaf(da, pa[2] + pa[3], db * (pb[2] + pb[3])), acc1);
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t* xb, int xsb, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const float d = f16_lo(w.d[S]);
+      const int s0 = 8 * S;
+      // Halves past in (a padded super-block) are skipped (uniform).
+#define PESTI_Q6K_STEP(H, G)                                                                       \
+      if (s0 + 4 * H + G < nsteps)                                                                 \
+        step<B, H, G>(w.lo[S][H][G & 1], w.hq[S][H], w.sc[S], d, xa + (s0 + 4 * H + G) * xsa,       \
+                      xb + (s0 + 4 * H + G) * xsb, es0[s0 + 4 * H + G], es1[s0 + 4 * H + G], acc0, acc1);
+      PESTI_Q6K_STEP(0, 0) PESTI_Q6K_STEP(0, 1) PESTI_Q6K_STEP(0, 2) PESTI_Q6K_STEP(0, 3)
+      PESTI_Q6K_STEP(1, 0) PESTI_Q6K_STEP(1, 1) PESTI_Q6K_STEP(1, 2) PESTI_Q6K_STEP(1, 3)
+#undef PESTI_Q6K_STEP
+    }
+  }
+};
+
+// P = format, NSB = super-blocks per row (every op of the launch has this
+// many).
+template <class P, int B, int NSB>
+__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   extern __shared__ float lds[];
   static_assert(B >= 1 && B <= 8 && NSB >= 1 && NSB <= 4, "batch 1..8, rows of at most 1024 weights");
   // The op's arguments, all loaded before the first branch (see gemv_kernel).
@@ -110,7 +251,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g
   asm volatile("" ::"s"(a.w), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in), "s"(a.row_bytes));
   const int64_t first = static_cast<int64_t>(blockIdx.x) * kMfmaGroupRows;
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
-  const int nsteps = static_cast<int>(a.in >> 5);   // sub-blocks holding weights
+  const int nsteps = static_cast<int>(a.in >> 5);   // 32-weight blocks holding weights
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,20 +277,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g
   }
 
   // Weights: the lane's row of the wave's tile (rows past the end read the
-  // launch tile's first row and are not stored), every super-block's
-  // header and the lane's 8 code bytes of each 64-weight run.
+  // launch tile's first row and are not stored).
   const int64_t row = first + wave * kMfmaTileRows + n;
   const bool live = row < a.out;
   const uint8_t* rp = a.w + (live ? row : first) * a.row_bytes;
-  u32x4 hdr[NSB];
-  u32x2 cw[NSB][4];
-#pragma unroll
-  for (int S = 0; S < NSB; ++S) {
-    const uint8_t* sb = rp + 144 * S;
-    hdr[S] = load_u32x4_a16(sb);
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) cw[S][gi] = *reinterpret_cast<const u32x2*>(sb + 16 + 32 * gi + 8 * kg);
-  }
+  typename P::template Tile<NSB> w;
+  P::template issue<NSB>(rp, kg, w);
   const float bv = *(a.bias ? a.bias + (live ? row : first) : reinterpret_cast<const float*>(rp));
 
   // Stage x: operand rows [nsteps][2B][32 binary16] (64 bytes each), a zero
@@ -206,28 +339,21 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g
 
   // Lane (n, kg): A row n (x hi/lo of batch n / 2, or the zero row), batch
   // columns 2kg and 2kg + 1 (clamped to a real column; unused ones are not
-  // stored).
+  // stored).  xa / xb: the operand with lanes kg >= 2 / kg < 2 at the zero
+  // row (Q6_K's two sub-blocks per step); Q4_K uses the whole operand.
   const bool arow = n < 2 * B;
   const uint8_t* xop = arow ? base + n * 64 + 16 * kg : zero_row + 16 * kg;
   const int xstep = arow ? 2 * B * 64 : 0;
+  const bool half0 = kg < 2;
+  const uint8_t* xa = std::is_same<P, MfmaQ6K>::value && !half0 ? zero_row + 16 * kg : xop;
+  const int xsa = std::is_same<P, MfmaQ6K>::value && !half0 ? 0 : xstep;
+  const uint8_t* xb = half0 ? zero_row + 16 * kg : xop;
+  const int xsb = half0 ? 0 : xstep;
   const int b0 = 2 * kg, b1 = 2 * kg + 1;
   const f32x2* xs0 = xsc + (b0 < B ? b0 : B - 1) * nsteps;
   const f32x2* xs1 = xsc + (b1 < B ? b1 : B - 1) * nsteps;
   float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-  for (int S = 0; S < NSB; ++S) {
-    const float d512 = f16_lo(hdr[S].x) * 512.0f;
-    const float dmin = f16_hi(hdr[S].x);
-    const int s0 = 8 * S;
-    // Sub-blocks past in (a padded super-block) are skipped (uniform).
-#define PESTI_Q4K_STEP(J)                                                                          \
-    if (s0 + J < nsteps)                                                                           \
-      q4k_step<B, J>(cw[S][J / 2], hdr[S], d512, dmin, xop + (s0 + J) * xstep, xs0[s0 + J], xs1[s0 + J], \
-                     acc0, acc1);
-    PESTI_Q4K_STEP(0) PESTI_Q4K_STEP(1) PESTI_Q4K_STEP(2) PESTI_Q4K_STEP(3)
-    PESTI_Q4K_STEP(4) PESTI_Q4K_STEP(5) PESTI_Q4K_STEP(6) PESTI_Q4K_STEP(7)
-#undef PESTI_Q4K_STEP
-  }
+  P::template run<B, NSB>(w, nsteps, xa, xsa, xb, xsb, xs0, xs1, acc0, acc1);
   if (live) {
     const float bias = a.bias ? bv : 0.f;
     if (b0 < B) a.y[b0 * a.out + row] = acc0 + bias;
@@ -239,7 +365,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_q4k_kernel(GroupArgs g
 
 namespace pesti_gemv {
 
-template <int B, int NSB>
+template <class P, int B, int NSB>
 int launch_mfma_bn(const GroupArgs& g, hipStream_t st) {
   int64_t max_in = 0, max_out = 0;
   for (int i = 0; i < g.n_ops; ++i) {
@@ -251,36 +377,45 @@ int launch_mfma_bn(const GroupArgs& g, hipStream_t st) {
   const int64_t tiles = (max_out + pesti::kMfmaGroupRows - 1) / pesti::kMfmaGroupRows;
   GroupArgs args = g;
   void* params[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_mfma_q4k_kernel<B, NSB>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_mfma_kernel<P, B, NSB>),
                                        dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(g.n_ops)),
                                        dim3(pesti::kMfmaThreads), params, lds, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-template <int NSB>
+template <class P, int NSB>
 int launch_mfma_n(const GroupArgs& g, int batch, hipStream_t st) {
   switch (batch) {
-    case 1: return launch_mfma_bn<1, NSB>(g, st);
-    case 2: return launch_mfma_bn<2, NSB>(g, st);
-    case 3: return launch_mfma_bn<3, NSB>(g, st);
-    case 4: return launch_mfma_bn<4, NSB>(g, st);
-    case 5: return launch_mfma_bn<5, NSB>(g, st);
-    case 6: return launch_mfma_bn<6, NSB>(g, st);
-    case 7: return launch_mfma_bn<7, NSB>(g, st);
-    case 8: return launch_mfma_bn<8, NSB>(g, st);
+    case 1: return launch_mfma_bn<P, 1, NSB>(g, st);
+    case 2: return launch_mfma_bn<P, 2, NSB>(g, st);
+    case 3: return launch_mfma_bn<P, 3, NSB>(g, st);
+    case 4: return launch_mfma_bn<P, 4, NSB>(g, st);
+    case 5: return launch_mfma_bn<P, 5, NSB>(g, st);
+    case 6: return launch_mfma_bn<P, 6, NSB>(g, st);
+    case 7: return launch_mfma_bn<P, 7, NSB>(g, st);
+    case 8: return launch_mfma_bn<P, 8, NSB>(g, st);
     default: return PESTI_ERR_BATCH;
   }
 }
 
-int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st) {
-  if (g.n_ops < 1 || g.op[0].row_bytes % 144 != 0) return PESTI_ERR_SHAPE;
-  switch (g.op[0].row_bytes / 144) {
-    case 1: return launch_mfma_n<1>(g, batch, st);
-    case 2: return launch_mfma_n<2>(g, batch, st);
-    case 3: return launch_mfma_n<3>(g, batch, st);
-    case 4: return launch_mfma_n<4>(g, batch, st);
+template <class P>
+int launch_mfma_p(const GroupArgs& g, int batch, hipStream_t st) {
+  if (g.n_ops < 1 || g.op[0].row_bytes % P::kBytes != 0) return PESTI_ERR_SHAPE;
+  switch (g.op[0].row_bytes / P::kBytes) {
+    case 1: return launch_mfma_n<P, 1>(g, batch, st);
+    case 2: return launch_mfma_n<P, 2>(g, batch, st);
+    case 3: return launch_mfma_n<P, 3>(g, batch, st);
+    case 4: return launch_mfma_n<P, 4>(g, batch, st);
     default: return PESTI_ERR_SHAPE;
   }
+}
+
+int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ4K>(g, batch, st);
+}
+
+int launch_mfma_q6_k(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ6K>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

@@ -141,7 +141,10 @@ int pesti_gemv_q5_k(int64_t out_features, int64_t in_features, const void* block
                     void* stream);
 
 /* Q6_K (210-byte super-blocks of 256 weights, rows padded to whole
- * super-blocks).  Same arguments as pesti_gemv_q8_0. */
+ * super-blocks).  Same arguments as pesti_gemv_q8_0.  Matrices of at least
+ * 16384 rows with rows of at most 1024 weights, at batch 5..8, run on the
+ * matrix cores with x split as described for pesti_gemv_q4_k (same
+ * bound). */
 int pesti_gemv_q6_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);

@@ -605,109 +605,136 @@ def test_stream_read_xor(nbytes):
 
 
 # ---------------------------------------------------------------------------
-# matrix-core mat-vec: Q4_K ops of at least 16384 rows with rows of at most
-# 1024 weights at batch 3..8 (x split into binary16 high and low parts per
-# 32-weight block), checked on every row; batches 1 and 2 of the same
-# shapes run the vector-ALU kernel
+# matrix-core mat-vec: Q4_K and Q6_K ops of at least 16384 rows with rows of
+# at most 1024 weights, at batch 3..8 (Q4_K) or 5..8 (Q6_K), x split into
+# binary16 high and low parts per 32-weight block; checked on every row.
+# Smaller batches of the same shapes run the vector-ALU kernel.
 # ---------------------------------------------------------------------------
 MFMA_ROWS = 16384
+MFMA_FORMATS = ("q4_k", "q6_k")
 MFMA_CASES = [(MFMA_ROWS, 896, 3), (MFMA_ROWS + 37, 896, 4), (MFMA_ROWS + 5, 32, 3),
               (MFMA_ROWS + 11, 800, 3), (20000 + 7, 1024, 8), (MFMA_ROWS + 63, 768, 5),
-              (MFMA_ROWS + 1, 256, 4), (MFMA_ROWS + 29, 288, 6), (MFMA_ROWS + 50, 544, 7)]
+              (MFMA_ROWS + 1, 256, 4), (MFMA_ROWS + 29, 288, 6), (MFMA_ROWS + 50, 544, 7),
+              (MFMA_ROWS + 3, 160, 8)]
 
 
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
 @pytest.mark.parametrize("out,inf,batch", MFMA_CASES)
-def test_mfma_q4_k_every_row(out, inf, batch):
-    packed, _, x, bias = make("q4_k", out, inf, 90, batch)
-    y = run_gemv("q4_k", packed, None, out, inf, x, bias)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x, bias)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma q4_k {out}x{inf} b{batch}")
+def test_mfma_every_row(fmt, out, inf, batch):
+    packed, _, x, bias = make(fmt, out, inf, 90, batch)
+    y = run_gemv(fmt, packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma {fmt} {out}x{inf} b{batch}")
 
 
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_mfma_q4_k_every_batch_no_bias(batch):
+def test_mfma_every_batch_no_bias(fmt, batch):
     out, inf = MFMA_ROWS + 37, 896
-    packed, _, x, _ = make("q4_k", out, inf, 91, batch, with_bias=False)
-    y = run_gemv("q4_k", packed, None, out, inf, x)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma q4_k b{batch}")
+    packed, _, x, _ = make(fmt, out, inf, 91, batch, with_bias=False)
+    y = run_gemv(fmt, packed, None, out, inf, x)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma {fmt} b{batch}")
 
 
-def test_mfma_q4_k_one_hot_x_gives_dequantized_column():
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
+def test_mfma_one_hot_x_gives_dequantized_column(fmt):
     """x = e_j: the block of j scales x_j to an exact binary16 power of two
     times its mantissa (here 1.0), every other block is zero, so y is
     column j of the float32 dequantized W, bit-exact."""
     out, inf = MFMA_ROWS + 37, 896
-    packed, _, _, _ = make("q4_k", out, inf, 92)
-    w32 = oracle.dequantize_f32("q4_k", packed, out, inf)
-    cols = [0, 1, 31, 32, 255, 256, 767, 895]
+    packed, _, _, _ = make(fmt, out, inf, 92)
+    w32 = oracle.dequantize_f32(fmt, packed, out, inf)
+    cols = [0, 1, 15, 16, 31, 32, 767, 895]
     x = np.zeros((8, inf), np.float32)
     for b, j in enumerate(cols):
         x[b, j] = 1.0
-    y = run_gemv("q4_k", packed, None, out, inf, x)
+    y = run_gemv(fmt, packed, None, out, inf, x)
     for b, j in enumerate(cols):
         assert np.array_equal(y[b], w32[:, j]), j
 
 
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
 @pytest.mark.parametrize("k", [3, -20, 40])
-def test_mfma_q4_k_power_of_two_scaling_is_exact(k):
+def test_mfma_power_of_two_scaling_is_exact(fmt, k):
     out, inf = MFMA_ROWS + 3, 896
-    packed, _, x, _ = make("q4_k", out, inf, 93, 3)
-    y1 = run_gemv("q4_k", packed, None, out, inf, x)
-    y2 = run_gemv("q4_k", packed, None, out, inf, np.ldexp(x, k).astype(np.float32))
+    packed, _, x, _ = make(fmt, out, inf, 93, 5)
+    y1 = run_gemv(fmt, packed, None, out, inf, x)
+    y2 = run_gemv(fmt, packed, None, out, inf, np.ldexp(x, k).astype(np.float32))
     assert np.array_equal(y2, np.ldexp(y1, k).astype(np.float32))
 
 
-def test_mfma_q4_k_padding_bytes_do_not_matter():
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
+def test_mfma_padding_bytes_do_not_matter(fmt):
     out, inf = MFMA_ROWS + 9, 896
-    packed, _, x, bias = make("q4_k", out, inf, 94, 3)
+    packed, _, x, bias = make(fmt, out, inf, 94, 5)
     rng = np.random.default_rng(95)
+    nb = {"q4_k": 144, "q6_k": 210}[fmt]
     other = packed.copy().reshape(out, -1)
-    last = other[:, 3 * 144:4 * 144]
-    last[:, 16 + 64:] = rng.integers(0, 256, last[:, 16 + 64:].shape, dtype=np.uint8)
-    last[:, 12:16] = rng.integers(0, 256, last[:, 12:16].shape, dtype=np.uint8)
-    last[:, 4:12] = (last[:, 4:12] & 0x3F) | (rng.integers(0, 4, last[:, 4:12].shape, dtype=np.uint8) << 6)
-    y1 = run_gemv("q4_k", packed, None, out, inf, x, bias)
-    y2 = run_gemv("q4_k", other, None, out, inf, x, bias)
+    last = other[:, 3 * nb:4 * nb]
+    if fmt == "q4_k":
+        last[:, 16 + 64:] = rng.integers(0, 256, last[:, 16 + 64:].shape, dtype=np.uint8)
+        last[:, 12:16] = rng.integers(0, 256, last[:, 12:16].shape, dtype=np.uint8)
+        last[:, 4:12] = (last[:, 4:12] & 0x3F) | (rng.integers(0, 4, last[:, 4:12].shape, dtype=np.uint8) << 6)
+    else:
+        last[:, 64:128] = rng.integers(0, 256, last[:, 64:128].shape, dtype=np.uint8)
+        last[:, 160:192] = rng.integers(0, 256, last[:, 160:192].shape, dtype=np.uint8)
+        last[:, 200:208] = rng.integers(0, 256, last[:, 200:208].shape, dtype=np.uint8)
+    y1 = run_gemv(fmt, packed, None, out, inf, x, bias)
+    y2 = run_gemv(fmt, other, None, out, inf, x, bias)
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
-def test_mfma_q4_k_forced_scales(d_bits):
+def test_mfma_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([96, d_bits])
     out, inf = MFMA_ROWS + 21, 512
-    packed = synth.quant_blocks("q4_k", rng, out, inf, force_d=d_bits)
-    x = synth.activations(rng, 3, inf)
-    y = run_gemv("q4_k", packed, None, out, inf, x)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma q4_k d={d_bits:#06x}")
+    packed = synth.quant_blocks(fmt, rng, out, inf, force_d=d_bits)
+    x = synth.activations(rng, 5, inf)
+    y = run_gemv(fmt, packed, None, out, inf, x)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma {fmt} d={d_bits:#06x}")
 
 
+def test_mfma_q6_k_all_codes_32_is_bias():
+    """q = 32 everywhere: every code enters as exactly 0, so y is the bias."""
+    out, inf = MFMA_ROWS + 5, 896
+    packed, _, x, bias = make("q6_k", out, inf, 99, 5)
+    blocks = packed.reshape(out, -1, 210)
+    blocks[:, :, 0:128] = 0x00            # low 4 bits 0
+    blocks[:, :, 128:192] = 0xAA          # high 2 bits 2 (q = 32) for every g
+    y = run_gemv("q6_k", packed, None, out, inf, x, bias)
+    assert np.array_equal(y, np.broadcast_to(bias, y.shape))
+
+
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
 @pytest.mark.parametrize("kind", ["wide_range", "tiny", "huge", "sparse"])
-def test_mfma_q4_k_x_dynamic_range(kind):
+def test_mfma_x_dynamic_range(fmt, kind):
     """The per-block power-of-two scaling keeps the binary16 split accurate
     whatever the magnitudes: elements 2^-40 .. 2^20 mixed within a block,
     vectors near the float32 extremes, blocks of zeros beside nonzeros."""
-    out, inf, batch = MFMA_ROWS + 13, 896, 4
-    packed, _, x, bias = make("q4_k", out, inf, 97, batch)
+    out, inf, batch = MFMA_ROWS + 13, 896, 5
+    packed, _, x, bias = make(fmt, out, inf, 97, batch)
     rng = np.random.default_rng([98, len(kind)])
     if kind == "wide_range":
         x = (x * np.exp2(rng.integers(-40, 21, x.shape))).astype(np.float32)
     elif kind == "tiny":
         x = np.ldexp(x, -110).astype(np.float32)
     elif kind == "huge":
-        x = np.ldexp(x, 90).astype(np.float32)
+        x = np.ldexp(x, 80).astype(np.float32)
         bias = None
     else:
         x = np.where(rng.random(x.shape) < 0.9, np.float32(0), x).astype(np.float32)
-    y = run_gemv("q4_k", packed, None, out, inf, x, bias).astype(np.float64)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x, bias)
+    y = run_gemv(fmt, packed, None, out, inf, x, bias).astype(np.float64)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
     if kind == "tiny":   # compare at unit scale: the 1e-6 floor would hide everything
         y, y_ref, s_ref = np.ldexp(y, 110), np.ldexp(y_ref, 110), np.ldexp(s_ref, 110)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma q4_k x {kind}")
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"mfma {fmt} x {kind}")
 
 
-def test_mfma_group_mixed_row_lengths_equals_single_calls_bitwise():
+@pytest.mark.parametrize("fmt", MFMA_FORMATS)
+def test_mfma_group_mixed_row_lengths_equals_single_calls_bitwise(fmt):
     """Tall ops of different row lengths and a short op in one group: each
     op takes the kernel its own single call takes, and the same bits."""
     import torch
@@ -716,17 +743,18 @@ def test_mfma_group_mixed_row_lengths_equals_single_calls_bitwise():
     ops, singles = [], []
     for i, (out, inf) in enumerate([(MFMA_ROWS + 7, 896), (300, 896), (MFMA_ROWS + 100, 256),
                                     (MFMA_ROWS, 800), (MFMA_ROWS + 1, 1280)]):
-        packed, _, x, bias = make("q4_k", out, inf, 100 + i, 3)
+        packed, _, x, bias = make(fmt, out, inf, 100 + i, 5)
         w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
-        yg = torch.empty(3 * out, dtype=torch.float32, device="cuda")
-        ys = torch.empty(3 * out, dtype=torch.float32, device="cuda")
+        yg = torch.empty(5 * out, dtype=torch.float32, device="cuda")
+        ys = torch.empty(5 * out, dtype=torch.float32, device="cuda")
         ops.append((out, inf, w_d, x_d, yg, b_d, None))
         singles.append((out, inf, w_d, x_d, ys, b_d, packed, x, bias))
-    dmv.pesti_gemv_group("q4_k", ops, 3)
+    dmv.pesti_gemv_group(fmt, ops, 5)
+    single = getattr(dmv, f"pesti_gemv_{fmt}")
     for out, inf, w_d, x_d, ys, b_d, *_ in singles:
-        dmv.pesti_gemv_q4_k(out, inf, w_d, x_d, ys, b_d, 3)
+        single(out, inf, w_d, x_d, ys, b_d, 5)
     torch.cuda.synchronize()
     for (o, _, _, _, yg, _, _), (out, inf, _, _, ys, _, packed, x, bias) in zip(ops, singles):
         assert torch.equal(yg, ys), o
-        y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x, bias)
-        assert_within(ys.cpu().numpy().reshape(3, out), y_ref, s_ref, GEMV_REL, f"group {out}x{inf}")
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+        assert_within(ys.cpu().numpy().reshape(5, out), y_ref, s_ref, GEMV_REL, f"group {out}x{inf}")
