@@ -1307,9 +1307,10 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
 
 // Q4_K and Q6_K ops of at least this many rows, with rows of at most 1024
 // weights, at batch kMfmaMinBatch..8 go to the matrix-core mat-vec
-// (gemv_mfma.hip); measured on the 151936 x 896 LM head it overtakes the
-// vector-ALU kernel from batch 3 (Q4_K) and batch 5 (Q6_K).  The choice depends on the op alone (never on the other ops of
-// a group), so a grouped op gives the same bits as its own single call.
+// (gemv_mfma.hip), which overtakes the vector-ALU kernel on the
+// 151936 x 896 LM head from batch 3 (Q4_K) and batch 5 (Q6_K).  The choice
+// depends on the op alone (never on the other ops of a group), so a
+// grouped op gives the same bits as its own single call.
 #ifndef PESTI_MFMA_MIN_ROWS
 #define PESTI_MFMA_MIN_ROWS 16384
 #endif

@@ -522,6 +522,31 @@ def test_group_matches_oracle_per_op(fmt, batch):
         assert_within(got, y_ref, s_ref, GEMV_REL, f"group {fmt} {out}x{inf}")
 
 
+def test_q8_0_group_of_both_units_equals_single_calls_bitwise():
+    """Q8_0 rows of an even block count take the two-block unit, the others
+    the one-block unit; the unit is chosen per op, so a group holding both
+    gives every op the bits of its own single call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for i, (out, inf) in enumerate([(300, 896), (77, 800), (40, 4864), (9, 32), (130, 288)]):
+        packed, _, x, bias = make("q8_0", out, inf, 110 + i, 2)
+        w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yg = torch.empty(2 * out, dtype=torch.float32, device="cuda")
+        ys = torch.empty(2 * out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        singles.append((out, inf, w_d, x_d, ys, b_d, packed, x, bias))
+    dmv.pesti_gemv_group("q8_0", ops, 2)
+    for out, inf, w_d, x_d, ys, b_d, *_ in singles:
+        dmv.pesti_gemv_q8_0(out, inf, w_d, x_d, ys, b_d, 2)
+    torch.cuda.synchronize()
+    for (o, _, _, _, yg, _, _), (out, inf, _, _, ys, _, packed, x, bias) in zip(ops, singles):
+        assert torch.equal(yg, ys), o
+        y_ref, s_ref = oracle.gemv_packed("q8_0", packed, out, inf, x, bias)
+        assert_within(ys.cpu().numpy().reshape(2, out), y_ref, s_ref, GEMV_REL, f"q8_0 group {out}x{inf}")
+
+
 def test_group_equals_single_calls_bitwise():
     """A grouped launch runs the same arithmetic as the single-matrix call."""
     import torch
