@@ -283,7 +283,6 @@ struct WPolF16 {
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
     un.v = pesti::load_u32x4_a16(row + 64 * u + 16 * kg);
   }
-  static constexpr int kParts = 1;
   __device__ __forceinline__ static pesti::whalf8 codes(const Unit& un, int, int, int) {
     return __builtin_bit_cast(pesti::whalf8, un.v);
   }

@@ -135,13 +135,20 @@ struct MfmaQ4K {
       const float d512 = f16_lo(w.hdr[S].x) * 512.0f;
       const float dmin = f16_hi(w.hdr[S].x);
       const int s0 = 8 * S;
-      // Sub-blocks past in (a padded super-block) are skipped (uniform).
+      // A whole super-block runs its 8 steps as straight-line code (they
+      // overlap); the padded last one tests each step (uniform).
 #define PESTI_Q4K_STEP(J)                                                                          \
-      if (s0 + J < nsteps)                                                                         \
         q4k_step<B, J>(w.cw[S][J / 2], w.hdr[S], d512, dmin, xa + (s0 + J) * xsa, es0[s0 + J],     \
                        es1[s0 + J], acc0, acc1);
-      PESTI_Q4K_STEP(0) PESTI_Q4K_STEP(1) PESTI_Q4K_STEP(2) PESTI_Q4K_STEP(3)
-      PESTI_Q4K_STEP(4) PESTI_Q4K_STEP(5) PESTI_Q4K_STEP(6) PESTI_Q4K_STEP(7)
+      if (s0 + 8 <= nsteps) {
+        PESTI_Q4K_STEP(0) PESTI_Q4K_STEP(1) PESTI_Q4K_STEP(2) PESTI_Q4K_STEP(3)
+        PESTI_Q4K_STEP(4) PESTI_Q4K_STEP(5) PESTI_Q4K_STEP(6) PESTI_Q4K_STEP(7)
+      } else {
+        if (s0 + 0 < nsteps) PESTI_Q4K_STEP(0) if (s0 + 1 < nsteps) PESTI_Q4K_STEP(1)
+        if (s0 + 2 < nsteps) PESTI_Q4K_STEP(2) if (s0 + 3 < nsteps) PESTI_Q4K_STEP(3)
+        if (s0 + 4 < nsteps) PESTI_Q4K_STEP(4) if (s0 + 5 < nsteps) PESTI_Q4K_STEP(5)
+        if (s0 + 6 < nsteps) PESTI_Q4K_STEP(6)
+      }
 #undef PESTI_Q4K_STEP
     }
   }
@@ -228,13 +235,20 @@ struct MfmaQ6K {
     for (int S = 0; S < NSB; ++S) {
       const float d = f16_lo(w.d[S]);
       const int s0 = 8 * S;
-      // Halves past in (a padded super-block) are skipped (uniform).
+      // A whole super-block runs its 8 steps as straight-line code (they
+      // overlap); the padded last one tests each step (uniform).
 #define PESTI_Q6K_STEP(H, G)                                                                       \
-      if (s0 + 4 * H + G < nsteps)                                                                 \
         step<B, H, G>(w.lo[S][H][G & 1], w.hq[S][H], w.sc[S], d, xa + (s0 + 4 * H + G) * xsa,       \
                       xb + (s0 + 4 * H + G) * xsb, es0[s0 + 4 * H + G], es1[s0 + 4 * H + G], acc0, acc1);
-      PESTI_Q6K_STEP(0, 0) PESTI_Q6K_STEP(0, 1) PESTI_Q6K_STEP(0, 2) PESTI_Q6K_STEP(0, 3)
-      PESTI_Q6K_STEP(1, 0) PESTI_Q6K_STEP(1, 1) PESTI_Q6K_STEP(1, 2) PESTI_Q6K_STEP(1, 3)
+      if (s0 + 8 <= nsteps) {
+        PESTI_Q6K_STEP(0, 0) PESTI_Q6K_STEP(0, 1) PESTI_Q6K_STEP(0, 2) PESTI_Q6K_STEP(0, 3)
+        PESTI_Q6K_STEP(1, 0) PESTI_Q6K_STEP(1, 1) PESTI_Q6K_STEP(1, 2) PESTI_Q6K_STEP(1, 3)
+      } else {
+        if (s0 + 0 < nsteps) PESTI_Q6K_STEP(0, 0) if (s0 + 1 < nsteps) PESTI_Q6K_STEP(0, 1)
+        if (s0 + 2 < nsteps) PESTI_Q6K_STEP(0, 2) if (s0 + 3 < nsteps) PESTI_Q6K_STEP(0, 3)
+        if (s0 + 4 < nsteps) PESTI_Q6K_STEP(1, 0) if (s0 + 5 < nsteps) PESTI_Q6K_STEP(1, 1)
+        if (s0 + 6 < nsteps) PESTI_Q6K_STEP(1, 2)
+      }
 #undef PESTI_Q6K_STEP
     }
   }
