@@ -179,7 +179,11 @@ typedef struct pesti_gemv_op {
 #define PESTI_MAX_GROUP 8
 
 /* Up to PESTI_MAX_GROUP independent mat-vecs of one PESTI_FMT_* format and
- * one batch size, computed by one kernel launch.  This is the decode-step
+ * one batch size, computed by one kernel launch (two or three when the ops
+ * need different kernels: each op takes the kernel its own single call
+ * would take - Q8_0 rows of an odd or even block count, tall Q4_K / Q6_K
+ * matrices on the matrix cores - so every op's y has the bits of its single
+ * call).  This is the decode-step
  * case of projections that read the same activations (Q, K and V; gate and
  * up: "PESTI ..." README, "Conformance", per-head GQA and SwiGLU), where
  * one launch replaces several dependent ones.  ops is a host array read
