@@ -783,3 +783,32 @@ def test_mfma_group_mixed_row_lengths_equals_single_calls_bitwise(fmt):
         assert torch.equal(yg, ys), o
         y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
         assert_within(ys.cpu().numpy().reshape(5, out), y_ref, s_ref, GEMV_REL, f"group {out}x{inf}")
+
+
+@pytest.mark.parametrize("fmt,batch", [("q4_k", 4), ("q6_k", 6)])
+def test_mfma_group_of_eight_tall_ops(fmt, batch):
+    """Eight tall ops in one grouped launch (every op slot of the grid),
+    ragged row counts and two row lengths of one super-block count, each
+    checked on every row against the oracle and bitwise against its single
+    call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, cases = [], []
+    for i in range(8):
+        out, inf = MFMA_ROWS + 13 * i + (i % 3), (512 if i % 2 else 480)
+        packed, _, x, bias = make(fmt, out, inf, 120 + i, batch, with_bias=(i % 4 != 1))
+        w_d, x_d = to_dev(packed.reshape(-1)), to_dev(x)
+        b_d = to_dev(bias) if bias is not None else None
+        yg = torch.empty(batch * out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        cases.append((out, inf, w_d, x_d, b_d, packed, x, bias, yg))
+    dmv.pesti_gemv_group(fmt, ops, batch)
+    single = getattr(dmv, f"pesti_gemv_{fmt}")
+    for out, inf, w_d, x_d, b_d, packed, x, bias, yg in cases:
+        ys = torch.empty(batch * out, dtype=torch.float32, device="cuda")
+        single(out, inf, w_d, x_d, ys, b_d, batch)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ys), (out, inf)
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+        assert_within(yg.cpu().numpy().reshape(batch, out), y_ref, s_ref, GEMV_REL, f"group8 {fmt} {out}x{inf}")
