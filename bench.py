@@ -63,6 +63,10 @@ def parse_args(argv=None):
     p.add_argument("--suite", action="store_true",
                    help="instead of the decode step, time every other workload (int8, Q4_K FFN, "
                         "f16 GEMM, LM-head sweep) and print one JSON line per case")
+    p.add_argument("--launch-floor", action="store_true",
+                   help="instead of the decode step, time graphs of 96 dependent batch-1 Q4_K "
+                        "mat-vec launches (896 columns, 1 to 4864 rows) and of 96 one-element "
+                        "fill kernels, one JSON line per case")
     p.add_argument("--suite-filter", default="",
                    help="only suite cases whose name contains this (comma-separated alternatives)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -409,6 +413,65 @@ def source_digest():
     return h.hexdigest()
 
 
+def run_launch_floor(lib):
+    """Per-launch cost of the decode step's dependent launches against their
+    floor: a graph of 96 dependent batch-1 Q4_K mat-vecs (896 columns, each
+    launch its own x; weight copies rotated so that one replay touches 96
+    of them - at 896 rows and fewer the copies stay in the last-level cache,
+    at 4864 rows 229 copies exceed it), and a graph of 96 dependent fills
+    of one float (torch's fill kernel: launch and completion only)."""
+    import numpy as np
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from dequantize_mat_vec_amd import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    n, inf = 96, 896
+
+    def time_graph(issue):
+        with torch.cuda.stream(stream):
+            issue()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                issue()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 10 / n * 1e3
+
+    for rows in (1, 16, 128, 896, 4864):
+        rng = synth.rng_for(9, rows, 0)
+        packed = synth.quant_blocks("q4_k", rng, rows, inf).reshape(-1)
+        nb = packed.size
+        copies = int(640e6 // nb) + 1 if nb > 1e6 else 64
+        big = torch.from_numpy(np.tile(packed, copies)).to(dev)
+        xs = [torch.from_numpy(synth.activations(rng, 1, inf)).to(dev) for _ in range(n)]
+        y = torch.empty(rows, dtype=torch.float32, device=dev)
+
+        def issue():
+            for i in range(n):
+                c = i % copies
+                dmv.pesti_gemv_q4_k(rows, inf, big[c * nb:(c + 1) * nb], xs[i], y, None, 1, stream=stream)
+        us = time_graph(issue)
+        print(json.dumps({"case": f"q4_k {rows}x{inf} b1, 96 dependent launches", "us_per_launch": round(us, 3),
+                          "weight_copies": copies}), flush=True)
+        del big
+    z = torch.empty(1, device=dev)
+
+    def fills():
+        for i in range(n):
+            z.fill_(float(i))
+    print(json.dumps({"case": "fill of one float, 96 dependent launches", "us_per_launch": round(time_graph(fills), 3)}),
+          flush=True)
+
+
 def summarize_pmc(fetch_csv, write_csv, calib_mib=256):
     """Per-launch HBM bytes of every mat-vec kernel shape in a bench run, from
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
@@ -562,6 +625,9 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.suite:
         run_suite(lib, args)
+        return 0
+    if args.launch_floor:
+        run_launch_floor(lib)
         return 0
     calls, weights, xs, ys, biases = build_inputs(args.copies)
     launches = plan_launches(calls, args.grouping)
