@@ -1392,6 +1392,9 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
   }
   g.n_ops = n_mv;
   hipStream_t stream_h = static_cast<hipStream_t>(stream);
+  // Every check before the first launch: an error enqueues nothing.
+  const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
+  if (n_mv > 0 && per_launch < 1) return PESTI_ERR_SHAPE;
   if (fill.n_ops > 0) {
     const int r = fill_bias(fill, batch, stream_h);
     if (r != PESTI_OK) return r;
@@ -1431,8 +1434,6 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     n_mv = rest.n_ops;
     for (int i = 0; i < n_mv; ++i) live[i] = rest_live[i];
   }
-  const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
-  if (per_launch < 1) return PESTI_ERR_SHAPE;
   for (int b0 = 0; b0 < batch; b0 += per_launch) {
     const int nb = batch - b0 < per_launch ? batch - b0 : per_launch;
     GroupArgs c = g;

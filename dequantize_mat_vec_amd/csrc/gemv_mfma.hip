@@ -10,10 +10,12 @@
 // dmin m per 32-weight sub-block, Q6_K w = d sc (q - 32) per 16 weights
 // (the Q6_K steps are described at MfmaQ6K).
 //
-// At batch 1 the vector-ALU kernel spends one FMA, half a convert and a
-// quarter of a mask per weight, which on the 151936-row LM head is more
-// time than reading its bytes.  Here the k-reduction runs on the matrix
-// cores instead.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
+// The vector-ALU kernel spends one FMA per weight and batch column, so on
+// the 151936-row LM head its time grows with the batch well past the time
+// of reading the bytes.  Here the k-reduction runs on the matrix cores,
+// where up to 8 batch columns share each instruction; the group entry
+// points choose this kernel from batch 3 (Q4_K) and 5 (Q6_K), below which
+// the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
 // exactly), the A operand is x in binary16.  binary16 cannot hold float32
