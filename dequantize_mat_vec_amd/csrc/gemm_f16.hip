@@ -324,8 +324,10 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
     return launch_mfma(a, sh);
   }
   // m < 16: rows of X in chunks of up to 8 as a batch of binary16 mat-vecs;
-  // 32 lanes per W row holding up to 4 units each (rows of up to 4096
-  // weights in one round), 64 lanes and several rounds beyond that.
+  // 32 lanes per W row holding up to 2 units each (rows of up to 2048
+  // weights), 64 lanes holding up to 2 (up to 4096 weights: the 3072-deep
+  // GPT-2 projection, 6.75 us at m = 8 against 7.49 with 32 lanes holding
+  // 3) and up to 4 in several rounds beyond that.
   const size_t row_lds = sizeof(uint16_t) * pesti::xh_stride(in_features);
   int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, 8);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
@@ -339,7 +341,7 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
     int r;
     if (units <= 32) r = launch_valu_b<32, 1>(c, nb, sh);
     else if (units <= 64) r = launch_valu_b<32, 2>(c, nb, sh);
-    else if (units <= 128) r = launch_valu_b<32, 4>(c, nb, sh);
+    else if (units <= 128) r = launch_valu_b<64, 2>(c, nb, sh);
     else r = launch_valu_b<64, 4>(c, nb, sh);
     if (r != PESTI_OK) return r;
   }

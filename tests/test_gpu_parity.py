@@ -329,7 +329,7 @@ def test_full_size_sampled_rows(fmt, out, inf, batch):
 # ---------------------------------------------------------------------------
 GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               (1, 64, 40), (15, 96, 33), (16, 32, 16), (17, 160, 70), (100, 256, 48),
-              (8, 3072, 768), (32, 3072, 768),
+              (8, 3072, 768), (32, 3072, 768), (5, 2080, 33), (15, 4096, 70),
               # no columns: y is the bias; long rows: several load rounds
               (20, 0, 37), (5, 0, 9), (8, 8192, 40), (3, 16384, 24), (48, 16384, 20),
               # a ragged K split: 3 k-steps over the workgroup's wavefronts
