@@ -1,0 +1,118 @@
+"""Host logic of the benchmark (no GPU): the decode step's call list and
+launch plan, its nominal byte count, kernel labels, the counter summary's
+scaling and the one-GPU rule."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from dequantize_mat_vec_amd import synth  # noqa: E402
+
+
+def test_decode_step_has_169_calls_in_stream_order():
+    calls = synth.decode_step_calls()
+    assert len(calls) == 24 * 7 + 1
+    names = [c[1] for c in calls[:7]]
+    assert names == ["q", "k", "v", "o", "gate", "up", "down"]
+    assert calls[-1][1:] == ("lm_head", "q8_0", 151936, 896, False)
+    # Q6_K down projections on even layers only, Q4_K everywhere else
+    for layer, name, fmt, out, inf, has_bias in calls[:-1]:
+        want = "q6_k" if name == "down" and layer % 2 == 0 else "q4_k"
+        assert fmt == want, (layer, name)
+        assert has_bias == (name in ("q", "k", "v"))
+        assert (out, inf) == {"q": (896, 896), "k": (128, 896), "v": (128, 896), "o": (896, 896),
+                              "gate": (4864, 896), "up": (4864, 896), "down": (896, 4864)}[name]
+
+
+def test_plan_groups_each_dependency_stage():
+    calls = synth.decode_step_calls()
+    stage = bench.plan_launches(calls, "stage")
+    assert len(stage) == 97
+    kinds = [tuple(calls[i][1] for i in idx) for _, idx in stage]
+    assert kinds[:4] == [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    assert kinds[-1] == ("lm_head",)
+    covered = sorted(i for _, idx in stage for i in idx)
+    assert covered == list(range(len(calls)))          # every call once, in order
+    for fmt, idx in stage:
+        assert all(calls[i][2] == fmt for i in idx)    # one format per launch
+        assert len({calls[i][0] for i in idx}) == 1    # one layer per launch
+    none = bench.plan_launches(calls, "none")
+    assert len(none) == 169 and all(len(idx) == 1 for _, idx in none)
+
+
+def test_nominal_bytes_of_the_step():
+    """Weights at 4.5 (Q4_K), 6.5625 (Q6_K) and 8.5 (Q8_0) bits per weight:
+    24 layers of Q/K/V/O/gate/up/down plus the 151936 x 896 LM head hold
+    359 403 520 bytes; x, y and the Q/K/V biases add the rest."""
+    calls = synth.decode_step_calls()
+    weights = sum(out * inf * bench.NOMINAL_BYTES_PER_WEIGHT[fmt] for _, _, fmt, out, inf, _ in calls)
+    assert weights == 359403520
+    total = sum(bench.call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
+    xy = sum(4 * (inf + out) for _, _, _, out, inf, _ in calls)
+    bias = sum(4 * out for _, _, _, out, _, hb in calls if hb)
+    assert total == weights + xy + bias == 362324992
+
+
+def test_call_bytes_per_format():
+    assert bench.call_bytes("q8_0", 10, 64, 1, False) == 10 * 68 + 4 * (64 + 10)
+    assert bench.call_bytes("q4_k", 3, 256, 2, True) == 3 * 144 + 8 * (256 + 3) + 12
+    assert bench.call_bytes("i8row", 5, 32, 1, False) == 5 * 32 + 20 + 4 * 37   # codes + row scales
+    assert bench.call_bytes("i4row", 5, 64, 1, False) == 5 * 32 + 20 + 4 * 69
+
+
+@pytest.mark.parametrize("fmt,inf,lanes", [("q4_k", 896, 16), ("q4_k", 4864, 64), ("q6_k", 4864, 64),
+                                          ("q6_k", 896, 16), ("q8_0", 896, 16), ("q8_0", 4864, 64),
+                                          ("q4_k", 2048, 32)])
+def test_kernel_label_lanes(fmt, inf, lanes):
+    assert bench.kernel_name(fmt, [inf], [896]) == f"gemv_kernel<{fmt}, L={lanes}, B=1, R=1>"
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the
+    same counter reads for a copy of known size; medians per kernel shape."""
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(tmp_path / "pmc.txt"))
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+
+    def write(path, counter, copy_kib, kernel_kib):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=fields)
+            w.writeheader()
+            for v in (copy_kib, copy_kib):
+                w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": "512",
+                            "Counter_Name": counter, "Counter_Value": v})
+            for v in kernel_kib:
+                w.writerow({"Kernel_Name": "void pesti::gemv_kernel<pesti::FmtQ4_K, 16, 1, 1, 1, false>(x)",
+                            "Grid_Size": "14336", "Counter_Name": counter, "Counter_Value": v})
+    fetch, write_csv = tmp_path / "f.csv", tmp_path / "w.csv"
+    write(fetch, "FETCH_SIZE", 131072.0, [100.0, 300.0, 200.0])    # copy reads half: factor 2
+    write(write_csv, "WRITE_SIZE", 262144.0, [4.0, 4.0, 4.0])      # factor 1
+    out = bench.summarize_pmc(str(fetch), str(write_csv), calib_mib=256)
+    assert out["calibration"]["FETCH_SIZE"]["factor"] == 2.0
+    assert out["calibration"]["WRITE_SIZE"]["factor"] == 1.0
+    (key, d), = out["kernels"].items()
+    assert key.endswith("grid=14336")
+    assert d["fetch_size_bytes"] == 2 * 200 * 1024 and d["write_size_bytes"] == 4 * 1024
+    assert d["dispatches"] == 3
+    assert json.load(open(tmp_path / "pmc.txt"))["source_sha256"] == bench.source_digest()
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_default_contract_arguments():
+    a = bench.parse_args([])
+    assert (a.gpus, a.steps, a.warmup, a.mode, a.grouping, a.ffn) == (1, 50, 10, "graph", "stage", "separate")
