@@ -1305,10 +1305,10 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   return PESTI_OK;
 }
 
-// Q4_K and Q6_K ops of at least this many rows, with rows of at most 1024
-// weights, at batch kMfmaMinBatch..8 go to the matrix-core mat-vec
+// Q4_K, Q5_K and Q6_K ops of at least this many rows, with rows of at most
+// 1024 weights, at batch kMfmaMinBatch..8 go to the matrix-core mat-vec
 // (gemv_mfma.hip), which overtakes the vector-ALU kernel on the
-// 151936 x 896 LM head from batch 3 (Q4_K) and batch 5 (Q6_K).  The choice
+// 151936 x 896 LM head from batch 3 (Q4_K, Q5_K) and batch 5 (Q6_K).  The choice
 // depends on the op alone (never on the other ops of a group), so a
 // grouped op gives the same bits as its own single call.
 #ifndef PESTI_MFMA_MIN_ROWS
@@ -1320,12 +1320,17 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
 #ifndef PESTI_MFMA_MIN_BATCH_Q6_K
 #define PESTI_MFMA_MIN_BATCH_Q6_K 5
 #endif
+#ifndef PESTI_MFMA_MIN_BATCH_Q5_K
+#define PESTI_MFMA_MIN_BATCH_Q5_K 3
+#endif
 constexpr int64_t kMfmaMinRows = PESTI_MFMA_MIN_ROWS;
 template <class F>
-constexpr int kMfmaMinBatch = std::is_same<F, pesti::FmtQ6_K>::value ? PESTI_MFMA_MIN_BATCH_Q6_K
-                                                                     : PESTI_MFMA_MIN_BATCH;
+constexpr int kMfmaMinBatch = std::is_same<F, pesti::FmtQ6_K>::value   ? PESTI_MFMA_MIN_BATCH_Q6_K
+                              : std::is_same<F, pesti::FmtQ5_K>::value ? PESTI_MFMA_MIN_BATCH_Q5_K
+                                                                       : PESTI_MFMA_MIN_BATCH;
 template <class F>
-constexpr bool kHasMfma = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ6_K>::value;
+constexpr bool kHasMfma = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ6_K>::value ||
+                          std::is_same<F, pesti::FmtQ5_K>::value;
 template <class F>
 inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
@@ -1335,9 +1340,11 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
 // super-blocks; x and y of every op set.
 int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st);
 int launch_mfma_q6_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_mfma_q5_k(const GroupArgs& g, int batch, hipStream_t st);
 template <class F>
 inline int launch_mfma(const GroupArgs& g, int batch, hipStream_t st) {
   if constexpr (std::is_same<F, pesti::FmtQ6_K>::value) return launch_mfma_q6_k(g, batch, st);
+  else if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_mfma_q5_k(g, batch, st);
   else return launch_mfma_q4_k(g, batch, st);
 }
 

@@ -1,20 +1,20 @@
-// Matrix-core mat-vec for tall Q4_K and Q6_K matrices (the LM head):
-// y = W x + b with W in Q4_K or Q6_K, x and y in float32, batch 1..8, rows
-// of at most 1024 weights.
+// Matrix-core mat-vec for tall Q4_K, Q5_K and Q6_K matrices (the LM head):
+// y = W x + b with W in one of those formats, x and y in float32, batch
+// 1..8, rows of at most 1024 weights.
 //
 // The operation is the decode step's row-major matrix-vector product with
 // the weights kept quantized ("Project scaffold: modules, CLI, and
 // correctness harness", file summaries of tensor.rs and quant.rs); the
 // block layouts are the GGUF ones of "PESTI - Portable Execution
 // Substrate for Transformer Inference" ("What This Is"): Q4_K w = d sc q -
-// dmin m per 32-weight sub-block, Q6_K w = d sc (q - 32) per 16 weights
-// (the Q6_K steps are described at MfmaQ6K).
+// dmin m per 32-weight sub-block (Q5_K the same with 5-bit codes), Q6_K
+// w = d sc (q - 32) per 16 weights (described at MfmaQ5K and MfmaQ6K).
 //
 // The vector-ALU kernel spends one FMA per weight and batch column, so on
 // the 151936-row LM head its time grows with the batch well past the time
 // of reading the bytes.  Here the k-reduction runs on the matrix cores,
 // where up to 8 batch columns share each instruction; the group entry
-// points choose this kernel from batch 3 (Q4_K) and 5 (Q6_K), below which
+// points choose this kernel from batch 3 (Q4_K, Q5_K) and 5 (Q6_K), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
@@ -256,6 +256,94 @@ struct MfmaQ6K {
   }
 };
 
+// Q5_K (176-byte super-blocks: Q4_K's d, dmin and 12 scale/min bytes, 32
+// bytes of fifth bits, then Q4_K's 128 low-nibble bytes from byte 48).
+// k-step j = 2g + c of a super-block is Q4_K's: lane kg holds weights
+// 64g + 32c + 8kg..+7, low 4 bits from nibble c of bytes 48 + 32g + 8kg..+7,
+// fifth bit j of bytes 16 + 8kg..+7.  Codes reach 31, past the e4m3 nibble
+// trick, so they enter as binary16 1024 + q (a byte permute) minus 1024:
+// exact.  Scales and mins as Q4_K.
+struct MfmaQ5K {
+  static constexpr int kBytes = 176;
+  template <int NSB>
+  struct Tile {
+    u32x4 hdr[NSB];
+    u32x2 qs[NSB][4];
+    u32x2 qh[NSB];
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const uint8_t* sb = rp + 176 * S;
+      w.hdr[S] = load_u32x4_a16(sb);
+      w.qh[S] = *reinterpret_cast<const u32x2*>(sb + 16 + 8 * kg);
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        w.qs[S][gi] = *reinterpret_cast<const u32x2*>(sb + 48 + 32 * gi + 8 * kg);
+    }
+  }
+  __device__ __forceinline__ static uint32_t pair(uint32_t q, uint32_t sel) {
+    // bytes [q_i, 0x64, q_j, 0x64]: binary16 1024 + q_i, 1024 + q_j; minus 1024
+    const uint32_t v = __builtin_amdgcn_perm(0x64646464u, q, sel);
+    const mhalf2 h = __builtin_bit_cast(mhalf2, v) + mhalf2{static_cast<_Float16>(-1024.0f),
+                                                            static_cast<_Float16>(-1024.0f)};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  template <int B, int J>
+  __device__ __forceinline__ static void step(const u32x2& lo, const u32x2& hb, const u32x4& hdr, float d,
+                                              float dmin, const uint8_t* xa, const f32x2& e0, const f32x2& e1,
+                                              float& acc0, float& acc1) {
+    constexpr uint32_t sh = 4u * (J & 1);
+    const uint32_t q0 = ((lo.x >> sh) & 0x0F0F0F0Fu) | (((hb.x >> J) & 0x01010101u) << 4);
+    const uint32_t q1 = ((lo.y >> sh) & 0x0F0F0F0Fu) | (((hb.y >> J) & 0x01010101u) << 4);
+    uint32_t hw[4];
+    hw[0] = pair(q0, 0x04010400u);
+    hw[1] = pair(q0, 0x04030402u);
+    hw[2] = pair(q1, 0x04010400u);
+    hw[3] = pair(q1, 0x04030402u);
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xa);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    uint32_t sc, m;
+    q4k_scale_min<J>(hdr, sc, m);
+    const float ds = d * static_cast<float>(sc);
+    const float dm = dmin * static_cast<float>(m);
+    acc0 = fmaf(ds * e0.x, p[0] + p[1], acc0);
+    acc0 = fmaf(-dm, e0.y, acc0);
+    if constexpr (B > 1) {
+      acc1 = fmaf(ds * e1.x, p[2] + p[3], acc1);
+      acc1 = fmaf(-dm, e1.y, acc1);
+    }
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const float d = f16_lo(w.hdr[S].x);
+      const float dmin = f16_hi(w.hdr[S].x);
+      const int s0 = 8 * S;
+      // A whole super-block runs its 8 steps as straight-line code; the
+      // padded last one tests each step (uniform).
+#define PESTI_Q5K_STEP(J)                                                                          \
+        step<B, J>(w.qs[S][J / 2], w.qh[S], w.hdr[S], d, dmin, xa + (s0 + J) * xsa, es0[s0 + J],    \
+                   es1[s0 + J], acc0, acc1);
+      if (s0 + 8 <= nsteps) {
+        PESTI_Q5K_STEP(0) PESTI_Q5K_STEP(1) PESTI_Q5K_STEP(2) PESTI_Q5K_STEP(3)
+        PESTI_Q5K_STEP(4) PESTI_Q5K_STEP(5) PESTI_Q5K_STEP(6) PESTI_Q5K_STEP(7)
+      } else {
+        if (s0 + 0 < nsteps) PESTI_Q5K_STEP(0) if (s0 + 1 < nsteps) PESTI_Q5K_STEP(1)
+        if (s0 + 2 < nsteps) PESTI_Q5K_STEP(2) if (s0 + 3 < nsteps) PESTI_Q5K_STEP(3)
+        if (s0 + 4 < nsteps) PESTI_Q5K_STEP(4) if (s0 + 5 < nsteps) PESTI_Q5K_STEP(5)
+        if (s0 + 6 < nsteps) PESTI_Q5K_STEP(6)
+      }
+#undef PESTI_Q5K_STEP
+    }
+  }
+};
+
 // P = format, NSB = super-blocks per row (every op of the launch has this
 // many).
 template <class P, int B, int NSB>
@@ -432,6 +520,10 @@ int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st) {
 
 int launch_mfma_q6_k(const GroupArgs& g, int batch, hipStream_t st) {
   return launch_mfma_p<pesti::MfmaQ6K>(g, batch, st);
+}
+
+int launch_mfma_q5_k(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ5K>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

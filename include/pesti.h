@@ -135,7 +135,10 @@ int pesti_gemv_q3_k(int64_t out_features, int64_t in_features, const void* block
 
 /* Q5_K (176-byte super-blocks of 256 weights, rows padded to whole
  * super-blocks; "PESTI ..." README, "What This Is": all K-family
- * quantizations).  Same arguments as pesti_gemv_q8_0. */
+ * quantizations).  Same arguments as pesti_gemv_q8_0.  Matrices of at least
+ * 16384 rows with rows of at most 1024 weights, at batch 3..8, run on the
+ * matrix cores with x split as described for pesti_gemv_q4_k (same
+ * bound). */
 int pesti_gemv_q5_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
