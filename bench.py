@@ -234,7 +234,7 @@ def suite_cases():
         for b in ((1, 2, 4, 8) if fmt == "q5_k" else (1, 8)):
             cases.append((f"{fmt} lm-head 151936x896 b{b}", "gemv", (fmt, synth.QWEN_VOCAB, 896, b)))
         cases.append((f"{fmt} 4864x896 b1 (gate/up)", "gemv", (fmt, 4864, 896, 1)))
-    for b in (1, 8):
+    for b in (1, 2, 4, 8):
         cases.append((f"i4row lm-head 151936x896 b{b}", "gemv", ("i4row", synth.QWEN_VOCAB, 896, b)))
     cases += [("i4row 4864x896 b1 (gate/up)", "gemv", ("i4row", 4864, 896, 1)),
               ("i4row 896x4864 b1 (down)", "gemv", ("i4row", 896, 4864, 1))]

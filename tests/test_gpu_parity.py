@@ -817,3 +817,67 @@ def test_mfma_group_of_eight_tall_ops(fmt, batch):
         assert torch.equal(yg, ys), (out, inf)
         y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
         assert_within(yg.cpu().numpy().reshape(batch, out), y_ref, s_ref, GEMV_REL, f"group8 {fmt} {out}x{inf}")
+
+
+# tall per-row INT4 matrices at batch 3..8 (vector-ALU kernel; rows of whole
+# 64-weight units, some ending mid 256-weight group), every row checked
+I4_TALL_CASES = [(MFMA_ROWS + 37, 896, 3), (MFMA_ROWS + 5, 800, 4), (MFMA_ROWS, 64, 8),
+                 (MFMA_ROWS + 11, 1024, 5), (MFMA_ROWS + 63, 288, 6), (MFMA_ROWS + 1, 544, 7),
+                 (MFMA_ROWS + 29, 32, 3)]
+
+
+@pytest.mark.parametrize("out,inf,batch", I4_TALL_CASES)
+def test_tall_i4row_every_row(out, inf, batch):
+    packed, scales, x, bias = make("i4row", out, inf, 130, batch)
+    y = run_gemv("i4row", packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall i4row {out}x{inf} b{batch}")
+
+
+def test_tall_i4row_one_hot_and_scaling():
+    out, inf = MFMA_ROWS + 21, 800
+    packed, scales, x, _ = make("i4row", out, inf, 131, 8)
+    w32 = oracle.dequantize_f32("i4row", packed, out, inf, scales)
+    cols = [0, 1, 2, 31, 32, 63, 64, 799]
+    onehot = np.zeros((8, inf), np.float32)
+    for b, j in enumerate(cols):
+        onehot[b, j] = 1.0
+    y = run_gemv("i4row", packed, scales, out, inf, onehot)
+    for b, j in enumerate(cols):
+        assert np.array_equal(y[b], w32[:, j]), j
+    y1 = run_gemv("i4row", packed, scales, out, inf, x[:4])
+    y2 = run_gemv("i4row", packed, scales, out, inf, np.ldexp(x[:4], -9).astype(np.float32))
+    assert np.array_equal(y2, np.ldexp(y1, -9).astype(np.float32))
+
+
+def test_tall_i4row_padding_codes_do_not_matter():
+    """800 = 12.5 units of 64: the last unit's second half is padding."""
+    out, inf = MFMA_ROWS + 3, 800
+    packed, scales, x, bias = make("i4row", out, inf, 132, 3)
+    other = packed.copy().reshape(out, -1)
+    rng = np.random.default_rng(133)
+    other[:, 400:416] = rng.integers(0, 256, (out, 16), dtype=np.uint8)
+    y1 = run_gemv("i4row", packed, scales, out, inf, x, bias)
+    y2 = run_gemv("i4row", other, scales, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+
+
+def test_tall_i4row_group_equals_single_calls_bitwise():
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, cases = [], []
+    for i, (out, inf) in enumerate([(MFMA_ROWS + 7, 896), (300, 896), (MFMA_ROWS + 100, 800), (MFMA_ROWS, 1280)]):
+        packed, scales, x, bias = make("i4row", out, inf, 140 + i, 4)
+        w_d, s_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(scales), to_dev(x), to_dev(bias)
+        yg = torch.empty(4 * out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, s_d))
+        cases.append((out, inf, w_d, s_d, x_d, b_d, packed, scales, x, bias, yg))
+    dmv.pesti_gemv_group("i4row", ops, 4)
+    for out, inf, w_d, s_d, x_d, b_d, packed, scales, x, bias, yg in cases:
+        ys = torch.empty(4 * out, dtype=torch.float32, device="cuda")
+        dmv.pesti_gemv_i4row(out, inf, w_d, s_d, x_d, ys, b_d, 4)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ys), (out, inf)
+        y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
+        assert_within(ys.cpu().numpy().reshape(4, out), y_ref, s_ref, GEMV_REL, f"i4row group {out}x{inf}")
