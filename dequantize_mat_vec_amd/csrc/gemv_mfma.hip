@@ -1,4 +1,5 @@
-// Matrix-core mat-vec for tall Q4_K, Q5_K and Q6_K matrices (the LM head):
+// Matrix-core mat-vec for tall Q4_K, Q5_K, Q6_K and per-row INT4 matrices
+// (the LM head):
 // y = W x + b with W in one of those formats, x and y in float32, batch
 // 1..8, rows of at most 1024 weights.
 //
@@ -14,7 +15,8 @@
 // the 151936-row LM head its time grows with the batch well past the time
 // of reading the bytes.  Here the k-reduction runs on the matrix cores,
 // where up to 8 batch columns share each instruction; the group entry
-// points choose this kernel from batch 3 (Q4_K, Q5_K) and 5 (Q6_K), below which
+// points choose this kernel from batch 3 (Q4_K, Q5_K), 5 (Q6_K) and 2
+// (per-row INT4), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
@@ -344,6 +346,89 @@ struct MfmaQ5K {
   }
 };
 
+// Per-row INT4 (4-bit two's complement codes, two per byte - weight 2k in
+// the low nibble of byte k, 2k + 1 in the high one - rows padded to 64
+// weights, one float32 scale per row applied to the finished sum).  With
+// no per-block scale, a k-step may take its 32 weights from anywhere: in
+// each 128-weight group G a lane kg loads the 16 contiguous bytes
+// 64G + 16kg..+15 (weights 128G + 32kg..+31) and k-step s = 4G + t takes
+// their weights 8t..8t+7 (dword t), so step s's k-value 8kg + i is weight
+// 128G + 32kg + 8t + i; the x operand is staged in that order (kGrouped),
+// with its power-of-two scale per step.  XOR 0x88 per byte makes each
+// nibble q + 8 (0..15); the even and odd weights' nibbles are paired by a
+// byte permute into binary16 1024 + q + 8, minus 1032: q exactly.  Groups
+// past the row's bytes read a stand-in (their x is zero).
+struct MfmaI4 {
+  static constexpr int kBytes = 128;   // a 256-weight "super-block" of the row loop
+  static constexpr bool kGrouped = true;
+  template <int NSB>
+  struct Tile {
+    u32x4 c[2 * NSB];
+    float scale;
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w, int64_t row_bytes,
+                                               const float* scale) {
+#pragma unroll
+    for (int G = 0; G < 2 * NSB; ++G) {
+      const int off = 64 * G + 16 * kg;
+      w.c[G] = *reinterpret_cast<const u32x4*>(rp + (off + 16 <= row_bytes ? off : 0));
+    }
+    w.scale = *scale;
+  }
+  __device__ __forceinline__ static uint32_t pair(uint32_t hi, uint32_t lo, uint32_t sel) {
+    const uint32_t v = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;   // 1024 + q + 8
+    const mhalf2 h = __builtin_bit_cast(mhalf2, v) + mhalf2{static_cast<_Float16>(-1032.0f),
+                                                            static_cast<_Float16>(-1032.0f)};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  template <int B>
+  __device__ __forceinline__ static void step(uint32_t c, const uint8_t* xa, const f32x2& e0, const f32x2& e1,
+                                              float& acc0, float& acc1) {
+    const uint32_t v = c ^ 0x88888888u;
+    const uint32_t lo = v & 0x0F0F0F0Fu;          // weights 0, 2, 4, 6 of the lane's 8
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;   // weights 1, 3, 5, 7
+    uint32_t hw[4];
+    // byte selectors of v_perm_b32(hi, lo): 0..3 pick lo's bytes, 4..7 hi's, 12 a zero
+    hw[0] = pair(hi, lo, 0x0C040C00u);
+    hw[1] = pair(hi, lo, 0x0C050C01u);
+    hw[2] = pair(hi, lo, 0x0C060C02u);
+    hw[3] = pair(hi, lo, 0x0C070C03u);
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xa);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc0 = fmaf(e0.x, p[0] + p[1], acc0);
+    if constexpr (B > 1) acc1 = fmaf(e1.x, p[2] + p[3], acc1);
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int G = 0; G < 2 * NSB; ++G) {
+      const int s0 = 4 * G;
+      if (s0 < nsteps) {   // uniform: nsteps is a multiple of 4 here
+        step<B>(w.c[G].x, xa + (s0 + 0) * xsa, es0[s0 + 0], es1[s0 + 0], acc0, acc1);
+        step<B>(w.c[G].y, xa + (s0 + 1) * xsa, es0[s0 + 1], es1[s0 + 1], acc0, acc1);
+        step<B>(w.c[G].z, xa + (s0 + 2) * xsa, es0[s0 + 2], es1[s0 + 2], acc0, acc1);
+        step<B>(w.c[G].w, xa + (s0 + 3) * xsa, es0[s0 + 3], es1[s0 + 3], acc0, acc1);
+      }
+    }
+  }
+};
+
+// Formats whose x is staged in 128-weight groups (see MfmaI4) and whose
+// rows carry a float32 scale.
+template <class P>
+constexpr bool kGroupedX = std::is_same<P, MfmaI4>::value;
+
+// Index in x of staged item (block s, quarter q): 32 s + 8 q, or for x
+// staged in 128-weight groups 128 (s / 4) + 32 q + 8 (s % 4).
+template <bool kGrouped>
+__device__ __forceinline__ int x_index(int s, int q) {
+  return kGrouped ? 128 * (s >> 2) + 32 * q + 8 * (s & 3) : 32 * s + 8 * q;
+}
+
 // P = format, NSB = super-blocks per row (every op of the launch has this
 // many).
 template <class P, int B, int NSB>
@@ -355,7 +440,9 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   asm volatile("" ::"s"(a.w), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in), "s"(a.row_bytes));
   const int64_t first = static_cast<int64_t>(blockIdx.x) * kMfmaGroupRows;
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
-  const int nsteps = static_cast<int>(a.in >> 5);   // 32-weight blocks holding weights
+  // k-steps: 32-weight blocks holding weights (whole 128-weight groups for
+  // grouped x)
+  const int nsteps = kGroupedX<P> ? static_cast<int>(4 * ((a.in + 127) >> 7)) : static_cast<int>(a.in >> 5);
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -373,9 +460,11 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int item = tid + r * kMfmaThreads;
-    const int it = item < total ? item : 0;
-    const int b = it / per_b;
-    const float* src = a.x + b * a.in + 8 * (it - b * per_b);
+    const int b = item / per_b;
+    const int rem = item - b * per_b;   // 4 s + q
+    const int idx = x_index<kGroupedX<P>>(rem >> 2, rem & 3);
+    const bool real = item < total && idx < a.in;
+    const float* src = real ? a.x + b * a.in + idx : a.x;
     xv[r][0] = *reinterpret_cast<const f32x4*>(src);
     xv[r][1] = *reinterpret_cast<const f32x4*>(src + 4);
   }
@@ -386,7 +475,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   const bool live = row < a.out;
   const uint8_t* rp = a.w + (live ? row : first) * a.row_bytes;
   typename P::template Tile<NSB> w;
-  P::template issue<NSB>(rp, kg, w);
+  if constexpr (kGroupedX<P>) {
+    // with the row's scale (rows past the end read the tile's first row's)
+    P::template issue<NSB>(rp, kg, w, a.row_bytes, a.scales + (live ? row : first));
+  } else {
+    P::template issue<NSB>(rp, kg, w);
+  }
   const float bv = *(a.bias ? a.bias + (live ? row : first) : reinterpret_cast<const float*>(rp));
 
   // Stage x: operand rows [nsteps][2B][32 binary16] (64 bytes each), a zero
@@ -399,8 +493,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int item = tid + r * kMfmaThreads;
-    const float v[8] = {xv[r][0].x, xv[r][0].y, xv[r][0].z, xv[r][0].w,
-                        xv[r][1].x, xv[r][1].y, xv[r][1].z, xv[r][1].w};
+    const int rem0 = item % per_b;
+    const bool real = item < total && x_index<kGroupedX<P>>(rem0 >> 2, rem0 & 3) < a.in;
+    float v[8] = {xv[r][0].x, xv[r][0].y, xv[r][0].z, xv[r][0].w,
+                  xv[r][1].x, xv[r][1].y, xv[r][1].z, xv[r][1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = real ? v[i] : 0.f;
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[i]));
@@ -458,6 +556,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   const f32x2* xs1 = xsc + (b1 < B ? b1 : B - 1) * nsteps;
   float acc0 = 0.f, acc1 = 0.f;
   P::template run<B, NSB>(w, nsteps, xa, xsa, xb, xsb, xs0, xs1, acc0, acc1);
+  if constexpr (kGroupedX<P>) {
+    acc0 *= w.scale;
+    acc1 *= w.scale;
+  }
   if (live) {
     const float bias = a.bias ? bv : 0.f;
     if (b0 < B) a.y[b0 * a.out + row] = acc0 + bias;
@@ -476,7 +578,7 @@ int launch_mfma_bn(const GroupArgs& g, hipStream_t st) {
     max_in = g.op[i].in > max_in ? g.op[i].in : max_in;
     max_out = g.op[i].out > max_out ? g.op[i].out : max_out;
   }
-  const int64_t nsteps = max_in / 32;
+  const int64_t nsteps = pesti::kGroupedX<P> ? 4 * ((max_in + 127) / 128) : max_in / 32;
   const size_t lds = static_cast<size_t>(nsteps * 2 * B * 64 + 64 + 8 * B * nsteps);
   const int64_t tiles = (max_out + pesti::kMfmaGroupRows - 1) / pesti::kMfmaGroupRows;
   GroupArgs args = g;
@@ -504,8 +606,12 @@ int launch_mfma_n(const GroupArgs& g, int batch, hipStream_t st) {
 
 template <class P>
 int launch_mfma_p(const GroupArgs& g, int batch, hipStream_t st) {
-  if (g.n_ops < 1 || g.op[0].row_bytes % P::kBytes != 0) return PESTI_ERR_SHAPE;
-  switch (g.op[0].row_bytes / P::kBytes) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  // per-row INT4 rows are whole 64-weight units and may end inside a
+  // 256-weight group of the row loop; the other formats' rows are whole
+  // super-blocks
+  if (!pesti::kGroupedX<P> && g.op[0].row_bytes % P::kBytes != 0) return PESTI_ERR_SHAPE;
+  switch ((g.op[0].row_bytes + P::kBytes - 1) / P::kBytes) {
     case 1: return launch_mfma_n<P, 1>(g, batch, st);
     case 2: return launch_mfma_n<P, 2>(g, batch, st);
     case 3: return launch_mfma_n<P, 3>(g, batch, st);
@@ -524,6 +630,10 @@ int launch_mfma_q6_k(const GroupArgs& g, int batch, hipStream_t st) {
 
 int launch_mfma_q5_k(const GroupArgs& g, int batch, hipStream_t st) {
   return launch_mfma_p<pesti::MfmaQ5K>(g, batch, st);
+}
+
+int launch_mfma_i4row(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaI4>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

@@ -160,7 +160,10 @@ int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* co
 
 /* Per-row symmetric int4 ("Project scaffold ...", quant.rs lists INT4 beside
  * INT8): packed int4 rows of pesti_row_bytes(PESTI_FMT_I4ROW, in) bytes,
- * row_scales float32 [out]. */
+ * row_scales float32 [out].  Matrices of at least 16384 rows with rows of at
+ * most 1024 weights, at batch 2..8, run on the matrix cores with x split as
+ * described for pesti_gemv_q4_k (the codes enter exactly; the int4 bound
+ * stated above holds for both kernels). */
 int pesti_gemv_i4row(int64_t out_features, int64_t in_features, const void* packed,
                      const float* row_scales, const float* x, float* y,
                      const float* bias, int32_t batch, void* stream);

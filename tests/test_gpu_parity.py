@@ -819,11 +819,12 @@ def test_mfma_group_of_eight_tall_ops(fmt, batch):
         assert_within(yg.cpu().numpy().reshape(batch, out), y_ref, s_ref, GEMV_REL, f"group8 {fmt} {out}x{inf}")
 
 
-# tall per-row INT4 matrices at batch 3..8 (vector-ALU kernel; rows of whole
-# 64-weight units, some ending mid 256-weight group), every row checked
+# tall per-row INT4 matrices at batch 1..8 (matrix cores from batch 2; rows of
+# whole 64-weight units, some ending mid 128-weight group), every row checked
 I4_TALL_CASES = [(MFMA_ROWS + 37, 896, 3), (MFMA_ROWS + 5, 800, 4), (MFMA_ROWS, 64, 8),
                  (MFMA_ROWS + 11, 1024, 5), (MFMA_ROWS + 63, 288, 6), (MFMA_ROWS + 1, 544, 7),
-                 (MFMA_ROWS + 29, 32, 3)]
+                 (MFMA_ROWS + 29, 32, 3), (MFMA_ROWS + 9, 896, 2), (MFMA_ROWS + 2, 320, 2),
+                 (MFMA_ROWS + 4, 192, 1)]
 
 
 @pytest.mark.parametrize("out,inf,batch", I4_TALL_CASES)
@@ -845,9 +846,23 @@ def test_tall_i4row_one_hot_and_scaling():
     y = run_gemv("i4row", packed, scales, out, inf, onehot)
     for b, j in enumerate(cols):
         assert np.array_equal(y[b], w32[:, j]), j
-    y1 = run_gemv("i4row", packed, scales, out, inf, x[:4])
-    y2 = run_gemv("i4row", packed, scales, out, inf, np.ldexp(x[:4], -9).astype(np.float32))
-    assert np.array_equal(y2, np.ldexp(y1, -9).astype(np.float32))
+    for nb in (2, 4):
+        y1 = run_gemv("i4row", packed, scales, out, inf, x[:nb])
+        y2 = run_gemv("i4row", packed, scales, out, inf, np.ldexp(x[:nb], -9).astype(np.float32))
+        assert np.array_equal(y2, np.ldexp(y1, -9).astype(np.float32))
+
+
+def test_tall_i4row_sparse_codes_batch_2():
+    """Rows of mostly zero codes: the matrix-core kernel takes the codes
+    exactly, so the result stays within the stated bound."""
+    out, inf = MFMA_ROWS + 13, 896
+    packed, scales, x, bias = make("i4row", out, inf, 134, 2)
+    rng = np.random.default_rng(135)
+    p = packed.reshape(out, -1).copy()
+    p[rng.random(p.shape) < 0.98] = 0
+    y = run_gemv("i4row", p, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("i4row", p, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, "tall i4row sparse b2")
 
 
 def test_tall_i4row_padding_codes_do_not_matter():
