@@ -896,3 +896,50 @@ def test_tall_i4row_group_equals_single_calls_bitwise():
         assert torch.equal(yg, ys), (out, inf)
         y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
         assert_within(ys.cpu().numpy().reshape(4, out), y_ref, s_ref, GEMV_REL, f"i4row group {out}x{inf}")
+
+
+# ---------------------------------------------------------------------------
+# rows of 65..128 units (one wave per row, some lanes holding two units) and
+# their neighbours at 64 and 129 units, short and medium matrices: every row
+# checked, ragged row counts, batches chunked to fit LDS.
+# ---------------------------------------------------------------------------
+LONG_ROW_CASES = [("q4_k", 896, 4864, 1), ("q4_k", 2048, 8192, 2), ("q4_k", 3, 4160, 1),
+               ("q4_k", 2049, 4864, 1), ("q4_k", 700, 8256, 1),
+               ("q6_k", 896, 4864, 1), ("q6_k", 897, 4864, 3), ("q6_k", 2049, 4864, 1),
+               ("q8_0", 896, 4864, 1), ("q8_0", 1, 2080, 2), ("q8_0", 1537, 4096, 5),
+               ("q5_k", 1000, 4864, 1), ("q2_k", 896, 4864, 1), ("q3_k", 513, 5120, 1),
+               ("i8row", 896, 8192, 8), ("i4row", 2048, 4864, 4), ("i4row", 5, 4160, 1)]
+
+
+@pytest.mark.parametrize("fmt,out,inf,batch", LONG_ROW_CASES)
+def test_long_rows_every_row(fmt, out, inf, batch):
+    packed, scales, x, bias = make(fmt, out, inf, 150, batch)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"long rows {fmt} {out}x{inf} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", ["q6_k", "q8_0"])
+def test_long_rows_group_equals_single_calls_bitwise(fmt):
+    """A group mixing rows of 65..128 units with longer and shorter rows
+    (whose lengths set the launch's lanes per row) gives every op the bits
+    of its own single call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, cases = [], []
+    for i, (out, inf) in enumerate([(896, 4864), (4864, 896), (2049, 4864), (128, 8192), (300, 10240)]):
+        packed, scales, x, bias = make(fmt, out, inf, 160 + i, 2)
+        w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yg = torch.empty(2 * out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        cases.append((out, inf, w_d, x_d, b_d, packed, x, bias, yg))
+    dmv.pesti_gemv_group(fmt, ops, 2)
+    single = getattr(dmv, f"pesti_gemv_{fmt}")
+    for out, inf, w_d, x_d, b_d, packed, x, bias, yg in cases:
+        ys = torch.empty(2 * out, dtype=torch.float32, device="cuda")
+        single(out, inf, w_d, x_d, ys, b_d, 2)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ys), (out, inf)
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+        assert_within(ys.cpu().numpy().reshape(2, out), y_ref, s_ref, GEMV_REL, f"long-row group {fmt} {out}x{inf}")
