@@ -1,5 +1,5 @@
-// Matrix-core mat-vec for tall Q4_K, Q5_K, Q6_K and per-row INT4 matrices
-// (the LM head):
+// Matrix-core mat-vec for tall Q2_K, Q4_K, Q5_K, Q6_K and per-row INT4
+// matrices (the LM head):
 // y = W x + b with W in one of those formats, x and y in float32, batch
 // 1..8, rows of at most 1024 weights.
 //
@@ -9,14 +9,15 @@
 // block layouts are the GGUF ones of "PESTI - Portable Execution
 // Substrate for Transformer Inference" ("What This Is"): Q4_K w = d sc q -
 // dmin m per 32-weight sub-block (Q5_K the same with 5-bit codes), Q6_K
-// w = d sc (q - 32) per 16 weights (described at MfmaQ5K and MfmaQ6K).
+// w = d sc (q - 32) and Q2_K w = d sc q - dmin m per 16 weights (described
+// at MfmaQ5K, MfmaQ6K and MfmaQ2K).
 //
 // The vector-ALU kernel spends one FMA per weight and batch column, so on
 // the 151936-row LM head its time grows with the batch well past the time
 // of reading the bytes.  Here the k-reduction runs on the matrix cores,
 // where up to 8 batch columns share each instruction; the group entry
-// points choose this kernel from batch 3 (Q4_K, Q5_K), 5 (Q6_K) and 2
-// (per-row INT4), below which
+// points choose this kernel from batch 3 (Q2_K, Q4_K, Q5_K), 5 (Q6_K) and
+// 2 (per-row INT4), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
@@ -417,6 +418,89 @@ struct MfmaI4 {
   }
 };
 
+// Q2_K (84-byte super-blocks: 16 scale bytes, 4-bit sc | 4-bit m << 4 per
+// 16-weight sub-block; 64 code bytes; d; dmin).  k-step s = 8S + 4h + j
+// covers weights 128h + 32j + l, l = 0..31, of super-block S, whose 2-bit
+// codes sit at bits 2j of code byte 32h + l; lane kg's weights l = 8kg..+7
+// belong to sub-block 8h + 2j + kg / 2.  The sub-block scale is folded into
+// the B operand (sc q 2^-9, built by one binary16 multiply, is exact: sc q
+// <= 45), so one product covers both sub-blocks of the step; a second
+// product against the same x operand with B = the lanes' sub-block mins
+// gives 2^e sum(m x).  Per step: acc += 2^-e (d 2^9 C - dmin C_min).
+typedef uint32_t u32x2w __attribute__((ext_vector_type(2), aligned(4)));
+
+struct MfmaQ2K {
+  static constexpr int kBytes = 84;
+  template <int NSB>
+  struct Tile {
+    u32x4 sc[NSB];       // the 16 scale bytes
+    u32x2w q[NSB][2];    // [S][h]: code bytes 32h + 8kg..+7
+    uint32_t dd[NSB];    // d | dmin << 16
+    uint32_t sh;         // bit offset of the lane's sub-block in a scale byte pair
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const uint8_t* sb = rp + 84 * S;
+      w.sc[S] = *reinterpret_cast<const u32x4*>(sb);
+      w.q[S][0] = *reinterpret_cast<const u32x2w*>(sb + 16 + 8 * kg);
+      w.q[S][1] = *reinterpret_cast<const u32x2w*>(sb + 48 + 8 * kg);
+      w.dd[S] = *reinterpret_cast<const uint32_t*>(sb + 80);
+    }
+    w.sh = 8u * static_cast<uint32_t>(kg >> 1);
+  }
+  template <int B, int J>
+  __device__ __forceinline__ static void step(const u32x2w& c, uint32_t word, uint32_t sh, float d512,
+                                              float dmin, const uint8_t* xop, const f32x2& e0,
+                                              const f32x2& e1, float& acc0, float& acc1) {
+    const uint32_t qa = (c.x >> (2 * J)) & 0x03030303u;
+    const uint32_t qb = (c.y >> (2 * J)) & 0x03030303u;
+    // scale bytes of sub-blocks 8h + 2j (low) and 8h + 2j + 1 (high)
+    const uint32_t pair = word >> (16 * (J & 1));
+    const _Float16 sc = static_cast<_Float16>(static_cast<float>((pair >> sh) & 15u));
+    const _Float16 mn = static_cast<_Float16>(static_cast<float>((pair >> (sh + 4)) & 15u));
+    const mhalf2 s2{sc, sc};
+    mhalf2 h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, false) * s2;
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, true) * s2;
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, false) * s2;
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, true) * s2;
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, h);
+    const mhalf8 mv{mn, mn, mn, mn, mn, mn, mn, mn};
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xop);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const mfloat4 pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, mv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc0 = fmaf(e0.x, fmaf(d512, p[0] + p[1], -dmin * (pm[0] + pm[1])), acc0);
+    if constexpr (B > 1) acc1 = fmaf(e1.x, fmaf(d512, p[2] + p[3], -dmin * (pm[2] + pm[3])), acc1);
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const float d512 = f16_lo(w.dd[S]) * 512.0f;
+      const float dmin = f16_hi(w.dd[S]);
+      const int s0 = 8 * S;
+#define PESTI_Q2K_STEP(H, J)                                                                       \
+      step<B, J>(w.q[S][H], H == 0 ? (J < 2 ? w.sc[S].x : w.sc[S].y) : (J < 2 ? w.sc[S].z : w.sc[S].w), \
+                 w.sh, d512, dmin, xa + (s0 + 4 * H + J) * xsa, es0[s0 + 4 * H + J], es1[s0 + 4 * H + J], \
+                 acc0, acc1);
+      if (s0 + 8 <= nsteps) {
+        PESTI_Q2K_STEP(0, 0) PESTI_Q2K_STEP(0, 1) PESTI_Q2K_STEP(0, 2) PESTI_Q2K_STEP(0, 3)
+        PESTI_Q2K_STEP(1, 0) PESTI_Q2K_STEP(1, 1) PESTI_Q2K_STEP(1, 2) PESTI_Q2K_STEP(1, 3)
+      } else {
+        if (s0 + 0 < nsteps) PESTI_Q2K_STEP(0, 0) if (s0 + 1 < nsteps) PESTI_Q2K_STEP(0, 1)
+        if (s0 + 2 < nsteps) PESTI_Q2K_STEP(0, 2) if (s0 + 3 < nsteps) PESTI_Q2K_STEP(0, 3)
+        if (s0 + 4 < nsteps) PESTI_Q2K_STEP(1, 0) if (s0 + 5 < nsteps) PESTI_Q2K_STEP(1, 1)
+        if (s0 + 6 < nsteps) PESTI_Q2K_STEP(1, 2)
+      }
+#undef PESTI_Q2K_STEP
+    }
+  }
+};
+
 // Formats whose x is staged in 128-weight groups (see MfmaI4) and whose
 // rows carry a float32 scale.
 template <class P>
@@ -634,6 +718,10 @@ int launch_mfma_q5_k(const GroupArgs& g, int batch, hipStream_t st) {
 
 int launch_mfma_i4row(const GroupArgs& g, int batch, hipStream_t st) {
   return launch_mfma_p<pesti::MfmaI4>(g, batch, st);
+}
+
+int launch_mfma_q2_k(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ2K>(g, batch, st);
 }
 
 }  // namespace pesti_gemv
