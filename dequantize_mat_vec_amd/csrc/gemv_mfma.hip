@@ -1,4 +1,4 @@
-// Matrix-core mat-vec for tall Q2_K, Q4_K, Q5_K, Q6_K and per-row INT4
+// Matrix-core mat-vec for tall K-quant (Q2_K to Q6_K) and per-row INT4
 // matrices (the LM head):
 // y = W x + b with W in one of those formats, x and y in float32, batch
 // 1..8, rows of at most 1024 weights.
@@ -9,15 +9,15 @@
 // block layouts are the GGUF ones of "PESTI - Portable Execution
 // Substrate for Transformer Inference" ("What This Is"): Q4_K w = d sc q -
 // dmin m per 32-weight sub-block (Q5_K the same with 5-bit codes), Q6_K
-// w = d sc (q - 32) and Q2_K w = d sc q - dmin m per 16 weights (described
-// at MfmaQ5K, MfmaQ6K and MfmaQ2K).
+// w = d sc (q - 32), Q2_K w = d sc q - dmin m and Q3_K w = d (sc - 32) q
+// per 16 weights (described at MfmaQ5K, MfmaQ6K, MfmaQ2K and MfmaQ3K).
 //
 // The vector-ALU kernel spends one FMA per weight and batch column, so on
 // the 151936-row LM head its time grows with the batch well past the time
 // of reading the bytes.  Here the k-reduction runs on the matrix cores,
 // where up to 8 batch columns share each instruction; the group entry
-// points choose this kernel from batch 3 (Q2_K, Q4_K, Q5_K), 5 (Q6_K) and
-// 2 (per-row INT4), below which
+// points choose this kernel from batch 3 (Q2_K, Q3_K, Q4_K, Q5_K), 5 (Q6_K)
+// and 2 (per-row INT4), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
@@ -501,6 +501,96 @@ struct MfmaQ2K {
   }
 };
 
+// Q3_K (110-byte super-blocks, 2 bytes off a dword boundary every other
+// one: 32 high-bit bytes, 64 low-bit bytes as Q2_K, 12 bytes of sixteen
+// 6-bit scales, d).  k-step s = 8S + 4h + j as for Q2_K: lane kg's weights
+// 128h + 32j + 8kg + i (i = 0..7) take their low bits from bits 2j of code
+// bytes 32 + 32h + 8kg + i and their high bit from bit 4h + j of high-bit
+// bytes 8kg + i; q = low + 4 high - 4, and they belong to sub-block
+// 8h + 2j + kg / 2 (scale k: low 4 bits at bit 4(k / 8) of byte k % 8, top
+// 2 at bit 2(k / 4) of byte 8 + k % 4; w = d (scale - 32) q).  The byte
+// low | high << 2 converts as e4m3 (b 2^-9), and one binary16 FMA by the
+// lane's signed scale s = scale - 32 gives s (b - 4) 2^-9 = s q 2^-9
+// exactly (|s q| <= 128), so one product covers both sub-blocks of the
+// step and there is no min term: acc += 2^-e d 2^9 C.
+struct MfmaQ3K {
+  static constexpr int kBytes = 110;
+  template <int NSB>
+  struct Tile {
+    u32x2u2 hm[NSB];     // high-bit bytes 8kg..+7
+    u32x2u2 q[NSB][2];   // [S][h]: low-bit bytes 32 + 32h + 8kg..+7
+    u32x2u2 s01[NSB];    // scale bytes 0..7
+    uint32_t s2[NSB];    // scale bytes 8..11
+    uint32_t d[NSB];     // binary16 d in the low half
+    uint32_t c8;         // 8 (kg / 2): the lane's byte within a scale byte pair
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w) {
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const uint8_t* sb = rp + 110 * S;
+      w.hm[S] = *reinterpret_cast<const u32x2u2*>(sb + 8 * kg);
+      w.q[S][0] = *reinterpret_cast<const u32x2u2*>(sb + 32 + 8 * kg);
+      w.q[S][1] = *reinterpret_cast<const u32x2u2*>(sb + 64 + 8 * kg);
+      w.s01[S] = *reinterpret_cast<const u32x2u2*>(sb + 96);
+      w.s2[S] = *reinterpret_cast<const u32a2*>(sb + 104);
+      w.d[S] = *reinterpret_cast<const uint16_t*>(sb + 108);
+    }
+    w.c8 = 8u * static_cast<uint32_t>(kg >> 1);
+  }
+  template <int B, int H, int J>
+  __device__ __forceinline__ static void step(const u32x2u2& c, const u32x2u2& hm, uint32_t slo, uint32_t s2,
+                                              uint32_t c8, float d512, const uint8_t* xop, const f32x2& e0,
+                                              const f32x2& e1, float& acc0, float& acc1) {
+    constexpr uint32_t hb = 4 * H + J;
+    const uint32_t ba = ((c.x >> (2 * J)) & 0x03030303u) | (((hm.x >> hb) & 0x01010101u) << 2);
+    const uint32_t bb = ((c.y >> (2 * J)) & 0x03030303u) | (((hm.y >> hb) & 0x01010101u) << 2);
+    // scale 8h + 2j + kg/2: low 4 bits in byte 2j + kg/2 (nibble h), top 2
+    // in byte 8 + 2(j % 2) + kg/2 at bit 4h + 2(j / 2)
+    const uint32_t pos = 16u * (J & 1) + c8;
+    const uint32_t lo4 = (slo >> (pos + 4 * H)) & 15u;
+    const uint32_t hi2 = (s2 >> (pos + 4 * H + 2 * (J >> 1))) & 3u;
+    const _Float16 s = static_cast<_Float16>(static_cast<float>(static_cast<int>(lo4 | hi2 << 4) - 32));
+    const mhalf2 s2h{s, s};
+    const _Float16 off = s * static_cast<_Float16>(-4.0f / 512.0f);
+    const mhalf2 o2{off, off};
+    mhalf2 h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ba, 1.0f, false) * s2h + o2;
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ba, 1.0f, true) * s2h + o2;
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bb, 1.0f, false) * s2h + o2;
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bb, 1.0f, true) * s2h + o2;
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, h);
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xop);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc0 = fmaf(d512 * e0.x, p[0] + p[1], acc0);
+    if constexpr (B > 1) acc1 = fmaf(d512 * e1.x, p[2] + p[3], acc1);
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+#pragma unroll
+    for (int S = 0; S < NSB; ++S) {
+      const float d512 = f16_lo(w.d[S]) * 512.0f;
+      const int s0 = 8 * S;
+#define PESTI_Q3K_STEP(H, J)                                                                       \
+      step<B, H, J>(w.q[S][H], w.hm[S], J < 2 ? w.s01[S].x : w.s01[S].y, w.s2[S], w.c8, d512,       \
+                    xa + (s0 + 4 * H + J) * xsa, es0[s0 + 4 * H + J], es1[s0 + 4 * H + J], acc0, acc1);
+      if (s0 + 8 <= nsteps) {
+        PESTI_Q3K_STEP(0, 0) PESTI_Q3K_STEP(0, 1) PESTI_Q3K_STEP(0, 2) PESTI_Q3K_STEP(0, 3)
+        PESTI_Q3K_STEP(1, 0) PESTI_Q3K_STEP(1, 1) PESTI_Q3K_STEP(1, 2) PESTI_Q3K_STEP(1, 3)
+      } else {
+        if (s0 + 0 < nsteps) PESTI_Q3K_STEP(0, 0) if (s0 + 1 < nsteps) PESTI_Q3K_STEP(0, 1)
+        if (s0 + 2 < nsteps) PESTI_Q3K_STEP(0, 2) if (s0 + 3 < nsteps) PESTI_Q3K_STEP(0, 3)
+        if (s0 + 4 < nsteps) PESTI_Q3K_STEP(1, 0) if (s0 + 5 < nsteps) PESTI_Q3K_STEP(1, 1)
+        if (s0 + 6 < nsteps) PESTI_Q3K_STEP(1, 2)
+      }
+#undef PESTI_Q3K_STEP
+    }
+  }
+};
+
 // Formats whose x is staged in 128-weight groups (see MfmaI4) and whose
 // rows carry a float32 scale.
 template <class P>
@@ -722,6 +812,10 @@ int launch_mfma_i4row(const GroupArgs& g, int batch, hipStream_t st) {
 
 int launch_mfma_q2_k(const GroupArgs& g, int batch, hipStream_t st) {
   return launch_mfma_p<pesti::MfmaQ2K>(g, batch, st);
+}
+
+int launch_mfma_q3_k(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ3K>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

@@ -125,9 +125,9 @@ int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* block
 /* Q2_K (84-byte) and Q3_K (110-byte) super-blocks of 256 weights, rows
  * padded to whole super-blocks ("PESTI ..." README, "What This Is": all
  * K-family quantizations, Q2_K to Q8_0).  Same arguments as
- * pesti_gemv_q8_0.  Q2_K matrices of at least 16384 rows with rows of at
- * most 1024 weights, at batch 3..8, run on the matrix cores with x split
- * as described for pesti_gemv_q4_k (same bound). */
+ * pesti_gemv_q8_0.  Matrices of at least 16384 rows with rows of at most
+ * 1024 weights, at batch 3..8, run on the matrix cores with x split as
+ * described for pesti_gemv_q4_k (same bound). */
 int pesti_gemv_q2_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
@@ -189,8 +189,8 @@ typedef struct pesti_gemv_op {
 /* Up to PESTI_MAX_GROUP independent mat-vecs of one PESTI_FMT_* format and
  * one batch size, computed by one kernel launch (two or three when the ops
  * need different kernels: each op takes the kernel its own single call
- * would take - Q8_0 rows of an odd or even block count, tall Q2_K / Q4_K /
- * Q5_K / Q6_K / int4 matrices on the matrix cores - so every op's y has the bits of its single
+ * would take - Q8_0 rows of an odd or even block count, tall K-quant and
+ * int4 matrices on the matrix cores - so every op's y has the bits of its single
  * call).  This is the decode-step
  * case of projections that read the same activations (Q, K and V; gate and
  * up: "PESTI ..." README, "Conformance", per-head GQA and SwiGLU), where

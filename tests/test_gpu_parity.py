@@ -630,13 +630,13 @@ def test_stream_read_xor(nbytes):
 
 
 # ---------------------------------------------------------------------------
-# matrix-core mat-vec: Q2_K, Q4_K, Q5_K and Q6_K ops of at least 16384 rows with
-# rows of at most 1024 weights, at batch 3..8 (Q2_K, Q4_K, Q5_K) or 5..8 (Q6_K), x split into
+# matrix-core mat-vec: Q2_K, Q3_K, Q4_K, Q5_K and Q6_K ops of at least 16384 rows with
+# rows of at most 1024 weights, at batch 3..8 (Q2_K, Q3_K, Q4_K, Q5_K) or 5..8 (Q6_K), x split into
 # binary16 high and low parts per 32-weight block; checked on every row.
 # Smaller batches of the same shapes run the vector-ALU kernel.
 # ---------------------------------------------------------------------------
 MFMA_ROWS = 16384
-MFMA_FORMATS = ("q4_k", "q6_k", "q5_k", "q2_k")
+MFMA_FORMATS = ("q4_k", "q6_k", "q5_k", "q2_k", "q3_k")
 MFMA_CASES = [(MFMA_ROWS, 896, 3), (MFMA_ROWS + 37, 896, 4), (MFMA_ROWS + 5, 32, 3),
               (MFMA_ROWS + 11, 800, 3), (20000 + 7, 1024, 8), (MFMA_ROWS + 63, 768, 5),
               (MFMA_ROWS + 1, 256, 4), (MFMA_ROWS + 29, 288, 6), (MFMA_ROWS + 50, 544, 7),
@@ -694,12 +694,20 @@ def test_mfma_padding_bytes_do_not_matter(fmt):
     out, inf = MFMA_ROWS + 9, 896
     packed, _, x, bias = make(fmt, out, inf, 94, 5)
     rng = np.random.default_rng(95)
-    nb = {"q4_k": 144, "q6_k": 210, "q5_k": 176, "q2_k": 84}[fmt]
+    nb = {"q4_k": 144, "q6_k": 210, "q5_k": 176, "q2_k": 84, "q3_k": 110}[fmt]
     other = packed.copy().reshape(out, -1)
     last = other[:, 3 * nb:4 * nb]
+
+    def high_nibbles(lo, hi):   # randomize bits 4-7 of bytes lo..hi-1
+        last[:, lo:hi] = (last[:, lo:hi] & 0x0F) | (rng.integers(0, 16, last[:, lo:hi].shape,
+                                                                  dtype=np.uint8) << 4)
     if fmt == "q2_k":   # weights 896..1023: scale bytes 8..15, code bytes 48..79
         last[:, 8:16] = rng.integers(0, 256, last[:, 8:16].shape, dtype=np.uint8)
         last[:, 48:80] = rng.integers(0, 256, last[:, 48:80].shape, dtype=np.uint8)
+    elif fmt == "q3_k":   # high bits 4..7, low-bit bytes 64..95, scales 8..15
+        high_nibbles(0, 32)
+        last[:, 64:96] = rng.integers(0, 256, last[:, 64:96].shape, dtype=np.uint8)
+        high_nibbles(96, 108)
     elif fmt == "q5_k":
         last[:, 48 + 64:] = rng.integers(0, 256, last[:, 48 + 64:].shape, dtype=np.uint8)
         last[:, 16:48] = (last[:, 16:48] & 0x0F) | (rng.integers(0, 16, last[:, 16:48].shape, dtype=np.uint8) << 4)
