@@ -1305,11 +1305,11 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   return PESTI_OK;
 }
 
-// K-quant and per-row INT4 ops of at least this many rows, with rows of
-// at most 1024 weights, at batch kMfmaMinBatch..8 go to the matrix-core
-// mat-vec (gemv_mfma.hip), which overtakes the vector-ALU kernel on the
-// 151936 x 896 LM head from batch 3 (Q2_K, Q3_K, Q4_K, Q5_K), 5 (Q6_K) and
-// 2 (per-row INT4).  The choice
+// K-quant, per-row INT4 and even-block-count Q8_0 ops of at least this
+// many rows, with rows of at most 1024 weights, at batch kMfmaMinBatch..8
+// go to the matrix-core mat-vec (gemv_mfma.hip), which overtakes the
+// vector-ALU kernel on the 151936 x 896 LM head from batch 3 (Q2_K, Q3_K,
+// Q4_K, Q5_K), 4 (Q8_0), 5 (Q6_K) and 2 (per-row INT4).  The choice
 // depends on the op alone (never on the other ops of a group), so a
 // grouped op gives the same bits as its own single call.
 #ifndef PESTI_MFMA_MIN_ROWS
@@ -1333,6 +1333,9 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
 #ifndef PESTI_MFMA_MIN_BATCH_Q3_K
 #define PESTI_MFMA_MIN_BATCH_Q3_K 3
 #endif
+#ifndef PESTI_MFMA_MIN_BATCH_Q8_0
+#define PESTI_MFMA_MIN_BATCH_Q8_0 4
+#endif
 constexpr int64_t kMfmaMinRows = PESTI_MFMA_MIN_ROWS;
 template <class F>
 constexpr int kMfmaMinBatch = std::is_same<F, pesti::FmtQ6_K>::value    ? PESTI_MFMA_MIN_BATCH_Q6_K
@@ -1340,11 +1343,13 @@ constexpr int kMfmaMinBatch = std::is_same<F, pesti::FmtQ6_K>::value    ? PESTI_
                               : std::is_same<F, pesti::FmtI4Row>::value ? PESTI_MFMA_MIN_BATCH_I4ROW
                               : std::is_same<F, pesti::FmtQ2_K>::value  ? PESTI_MFMA_MIN_BATCH_Q2_K
                               : std::is_same<F, pesti::FmtQ3_K>::value  ? PESTI_MFMA_MIN_BATCH_Q3_K
+                              : std::is_same<F, pesti::FmtQ8_0x2>::value ? PESTI_MFMA_MIN_BATCH_Q8_0
                                                                         : PESTI_MFMA_MIN_BATCH;
 template <class F>
 constexpr bool kHasMfma = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ6_K>::value ||
                           std::is_same<F, pesti::FmtQ5_K>::value || std::is_same<F, pesti::FmtI4Row>::value ||
-                          std::is_same<F, pesti::FmtQ2_K>::value || std::is_same<F, pesti::FmtQ3_K>::value;
+                          std::is_same<F, pesti::FmtQ2_K>::value || std::is_same<F, pesti::FmtQ3_K>::value ||
+                          std::is_same<F, pesti::FmtQ8_0x2>::value;
 template <class F>
 inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
@@ -1358,6 +1363,7 @@ int launch_mfma_q5_k(const GroupArgs& g, int batch, hipStream_t st);
 int launch_mfma_i4row(const GroupArgs& g, int batch, hipStream_t st);
 int launch_mfma_q2_k(const GroupArgs& g, int batch, hipStream_t st);
 int launch_mfma_q3_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_mfma_q8_0(const GroupArgs& g, int batch, hipStream_t st);
 template <class F>
 inline int launch_mfma(const GroupArgs& g, int batch, hipStream_t st) {
   if constexpr (std::is_same<F, pesti::FmtQ6_K>::value) return launch_mfma_q6_k(g, batch, st);
@@ -1365,6 +1371,7 @@ inline int launch_mfma(const GroupArgs& g, int batch, hipStream_t st) {
   else if constexpr (std::is_same<F, pesti::FmtI4Row>::value) return launch_mfma_i4row(g, batch, st);
   else if constexpr (std::is_same<F, pesti::FmtQ2_K>::value) return launch_mfma_q2_k(g, batch, st);
   else if constexpr (std::is_same<F, pesti::FmtQ3_K>::value) return launch_mfma_q3_k(g, batch, st);
+  else if constexpr (std::is_same<F, pesti::FmtQ8_0x2>::value) return launch_mfma_q8_0(g, batch, st);
   else return launch_mfma_q4_k(g, batch, st);
 }
 

@@ -1,5 +1,5 @@
-// Matrix-core mat-vec for tall K-quant (Q2_K to Q6_K) and per-row INT4
-// matrices (the LM head):
+// Matrix-core mat-vec for tall K-quant (Q2_K to Q6_K), Q8_0 and per-row
+// INT4 matrices (the LM head):
 // y = W x + b with W in one of those formats, x and y in float32, batch
 // 1..8, rows of at most 1024 weights.
 //
@@ -16,8 +16,8 @@
 // the 151936-row LM head its time grows with the batch well past the time
 // of reading the bytes.  Here the k-reduction runs on the matrix cores,
 // where up to 8 batch columns share each instruction; the group entry
-// points choose this kernel from batch 3 (Q2_K, Q3_K, Q4_K, Q5_K), 5 (Q6_K)
-// and 2 (per-row INT4), below which
+// points choose this kernel from batch 3 (Q2_K, Q3_K, Q4_K, Q5_K), 4 (Q8_0
+// rows of an even block count), 5 (Q6_K) and 2 (per-row INT4), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
 // rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
 // byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
@@ -591,6 +591,79 @@ struct MfmaQ3K {
   }
 };
 
+// Q8_0 rows of an even block count (34-byte blocks: binary16 d, 32 int8
+// codes).  Two blocks are 68 bytes, so pair P of a row starts on a dword
+// boundary: k-step s is block s, and lane kg reads, for the even block of
+// the pair, the 12 aligned bytes 68P + 8kg..+11 (its codes are bytes 2..9
+// of them, realigned with two byte-aligns) and, for the odd block, the 8
+// aligned bytes 68P + 36 + 8kg..+7.  The even block's d is bytes 0..1 of
+// lane kg = 0's read and the odd block's bytes 10..11 of lane kg = 3's; the
+// other lanes of the row take them with a shuffle.  Codes enter as binary16
+// 1024 + (q + 128) from a byte permute, minus 1152: exact.  Per step:
+// acc += d 2^-e C.  Pairs past the row's end read pair 0 (in bounds) and
+// are skipped.
+__device__ __forceinline__ uint32_t q8_pair(uint32_t u, uint32_t sel) {
+  const uint32_t v = __builtin_amdgcn_perm(0x64646464u, u, sel);
+  const mhalf2 h = __builtin_bit_cast(mhalf2, v) + mhalf2{static_cast<_Float16>(-1152.0f),
+                                                          static_cast<_Float16>(-1152.0f)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+struct MfmaQ8 {
+  static constexpr int kBytes = 272;   // 8 blocks: a 256-weight "super-block" of the row loop
+  template <int NSB>
+  struct Tile {
+    uint32_t e[4 * NSB][3];   // even block of pair P: bytes 68P + 8kg..+11
+    u32x2w o[4 * NSB];        // odd block: bytes 68P + 36 + 8kg..+7
+  };
+  template <int NSB>
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int kg, Tile<NSB>& w, int64_t row_bytes) {
+#pragma unroll
+    for (int P = 0; P < 4 * NSB; ++P) {
+      const uint8_t* pp = rp + (68 * (P + 1) <= row_bytes ? 68 * P : 0);
+      const uint32_t* ev = reinterpret_cast<const uint32_t*>(pp + 8 * kg);
+      w.e[P][0] = ev[0];
+      w.e[P][1] = ev[1];
+      w.e[P][2] = ev[2];
+      w.o[P] = *reinterpret_cast<const u32x2w*>(pp + 36 + 8 * kg);
+    }
+  }
+  template <int B>
+  __device__ __forceinline__ static void step(uint32_t c0, uint32_t c1, float d, const uint8_t* xop,
+                                              const f32x2& e0, const f32x2& e1, float& acc0, float& acc1) {
+    const uint32_t u0 = c0 ^ 0x80808080u, u1 = c1 ^ 0x80808080u;   // q + 128
+    uint32_t hw[4];
+    // byte selectors of v_perm_b32(0x64646464, u): 0..3 pick u's bytes, 4 a 0x64
+    hw[0] = q8_pair(u0, 0x04010400u);
+    hw[1] = q8_pair(u0, 0x04030402u);
+    hw[2] = q8_pair(u1, 0x04010400u);
+    hw[3] = q8_pair(u1, 0x04030402u);
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xop);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc0 = fmaf(d * e0.x, p[0] + p[1], acc0);
+    if constexpr (B > 1) acc1 = fmaf(d * e1.x, p[2] + p[3], acc1);
+  }
+  template <int B, int NSB>
+  __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
+                                             const uint8_t*, int, const f32x2* es0, const f32x2* es1,
+                                             float& acc0, float& acc1) {
+    const int n = static_cast<int>(__lane_id()) & 15;
+#pragma unroll
+    for (int P = 0; P < 4 * NSB; ++P) {
+      const int s = 2 * P;
+      if (s < nsteps) {   // uniform; nsteps is even here
+        const float de = f16_lo(static_cast<uint32_t>(__shfl(static_cast<int>(w.e[P][0]), n, kWave)));
+        const float dodd = f16_hi(static_cast<uint32_t>(__shfl(static_cast<int>(w.e[P][2]), n + 48, kWave)));
+        const uint32_t c0 = __builtin_amdgcn_alignbyte(w.e[P][1], w.e[P][0], 2);
+        const uint32_t c1 = __builtin_amdgcn_alignbyte(w.e[P][2], w.e[P][1], 2);
+        step<B>(c0, c1, de, xa + s * xsa, es0[s], es1[s], acc0, acc1);
+        step<B>(w.o[P].x, w.o[P].y, dodd, xa + (s + 1) * xsa, es0[s + 1], es1[s + 1], acc0, acc1);
+      }
+    }
+  }
+};
+
 // Formats whose x is staged in 128-weight groups (see MfmaI4) and whose
 // rows carry a float32 scale.
 template <class P>
@@ -652,6 +725,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   if constexpr (kGroupedX<P>) {
     // with the row's scale (rows past the end read the tile's first row's)
     P::template issue<NSB>(rp, kg, w, a.row_bytes, a.scales + (live ? row : first));
+  } else if constexpr (std::is_same<P, MfmaQ8>::value) {
+    P::template issue<NSB>(rp, kg, w, a.row_bytes);
   } else {
     P::template issue<NSB>(rp, kg, w);
   }
@@ -784,7 +859,8 @@ int launch_mfma_p(const GroupArgs& g, int batch, hipStream_t st) {
   // per-row INT4 rows are whole 64-weight units and may end inside a
   // 256-weight group of the row loop; the other formats' rows are whole
   // super-blocks
-  if (!pesti::kGroupedX<P> && g.op[0].row_bytes % P::kBytes != 0) return PESTI_ERR_SHAPE;
+  if (!pesti::kGroupedX<P> && !std::is_same<P, pesti::MfmaQ8>::value && g.op[0].row_bytes % P::kBytes != 0)
+    return PESTI_ERR_SHAPE;
   switch ((g.op[0].row_bytes + P::kBytes - 1) / P::kBytes) {
     case 1: return launch_mfma_n<P, 1>(g, batch, st);
     case 2: return launch_mfma_n<P, 2>(g, batch, st);
@@ -816,6 +892,10 @@ int launch_mfma_q2_k(const GroupArgs& g, int batch, hipStream_t st) {
 
 int launch_mfma_q3_k(const GroupArgs& g, int batch, hipStream_t st) {
   return launch_mfma_p<pesti::MfmaQ3K>(g, batch, st);
+}
+
+int launch_mfma_q8_0(const GroupArgs& g, int batch, hipStream_t st) {
+  return launch_mfma_p<pesti::MfmaQ8>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

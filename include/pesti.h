@@ -105,7 +105,10 @@ extern "C" {
 /* --- quantized mat-vec, y = W x + b ------------------------------------ */
 
 /* Q8_0 (34-byte blocks of 32 weights).  blocks: out_features rows of
- * in_features/32 blocks.  batch in [0, 8]. */
+ * in_features/32 blocks.  batch in [0, 8].  Matrices of at least 16384 rows
+ * with rows of an even block count and at most 1024 weights, at batch 4..8,
+ * run on the matrix cores with x split as described for pesti_gemv_q4_k
+ * (same bound). */
 int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
@@ -189,8 +192,8 @@ typedef struct pesti_gemv_op {
 /* Up to PESTI_MAX_GROUP independent mat-vecs of one PESTI_FMT_* format and
  * one batch size, computed by one kernel launch (two or three when the ops
  * need different kernels: each op takes the kernel its own single call
- * would take - Q8_0 rows of an odd or even block count, tall K-quant and
- * int4 matrices on the matrix cores - so every op's y has the bits of its single
+ * would take - Q8_0 rows of an odd or even block count, tall K-quant, Q8_0
+ * and int4 matrices on the matrix cores - so every op's y has the bits of its single
  * call).  This is the decode-step
  * case of projections that read the same activations (Q, K and V; gate and
  * up: "PESTI ..." README, "Conformance", per-head GQA and SwiGLU), where
