@@ -60,6 +60,10 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     p.add_argument("--cpu-leg", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--parity-leg", metavar="NPZ", help=argparse.SUPPRESS)
+    p.add_argument("--suite-oracle-leg", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--no-parity", action="store_true",
+                   help="skip the oracle check of the step's sampled outputs before timing")
     p.add_argument("--suite", action="store_true",
                    help="instead of the decode step, time every other workload (int8, Q4_K FFN, "
                         "f16 GEMM, LM-head sweep) and print one JSON line per case")
@@ -80,7 +84,21 @@ def parse_args(argv=None):
 # ---------------------------------------------------------------------------
 # workload
 # ---------------------------------------------------------------------------
-def build_inputs(copies):
+def host_inputs(calls):
+    """Host (numpy) inputs of the step's calls from the seeded generator:
+    [(packed weight bytes, x [1][in] float32, bias or None)] in call order."""
+    from dequantize_mat_vec_amd import synth
+    out = []
+    for layer, name, fmt, rows, inf, has_bias in calls:
+        tidx = synth.TENSOR_INDEX[name]
+        packed = synth.quant_blocks(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), rows, inf)
+        x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
+        b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
+        out.append((packed, x, b))
+    return out
+
+
+def build_inputs(copies, calls=None, host=None):
     """Step inputs.  Each weight copy is one contiguous device buffer holding
     the step's tensors in the order they are used (Q, K, V, O, gate, up,
     down per layer, then the LM head), each at a 256-byte boundary, as a
@@ -90,31 +108,24 @@ def build_inputs(copies):
     import torch
     from dequantize_mat_vec_amd import synth
     dev = torch.device("cuda:0")
-    calls = synth.decode_step_calls()
-    packs, offsets, total = [], [], 0
+    calls = synth.decode_step_calls() if calls is None else calls
+    host = host_inputs(calls) if host is None else host
+    offsets, total = [], 0
     xs, ys, biases = [], [], []
-    for layer, name, fmt, out, inf, has_bias in calls:
-        tidx = synth.TENSOR_INDEX[name]
-        packed = synth.quant_blocks(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), out, inf)
-        packs.append(packed.reshape(-1))
+    for (packed, x, b), (_, _, _, out, _, _) in zip(host, calls):
         offsets.append(total)
         total += -(-packed.size // 256) * 256
-        x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
-        xs.append(torch.from_numpy(x).to(dev))
+        xs.append(torch.from_numpy(x.reshape(-1)).to(dev))
         ys.append(torch.empty(out, dtype=torch.float32, device=dev))
-        if has_bias:
-            b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), out)
-            biases.append(torch.from_numpy(b).to(dev))
-        else:
-            biases.append(None)
-    host = np.zeros(total, dtype=np.uint8)
-    for off, p in zip(offsets, packs):
-        host[off:off + p.size] = p
-    host_t = torch.from_numpy(host)
+        biases.append(torch.from_numpy(b).to(dev) if b is not None else None)
+    buf_host = np.zeros(total, dtype=np.uint8)
+    for off, (p, _, _) in zip(offsets, host):
+        buf_host[off:off + p.size] = p.reshape(-1)
+    host_t = torch.from_numpy(buf_host)
     weights = []
     for _ in range(copies):
         buf = host_t.to(dev)
-        weights.append([buf[off:off + p.size] for off, p in zip(offsets, packs)])
+        weights.append([buf[off:off + p.size] for off, (p, _, _) in zip(offsets, host)])
     torch.cuda.synchronize()
     return calls, weights, xs, ys, biases
 
@@ -251,63 +262,89 @@ def suite_cases():
     return cases
 
 
+def suite_case_inputs(idx, name, kind, prm, rows_limit=None):
+    """Host inputs of one suite case from the seeded generator (the GPU run
+    and the oracle's timing leg draw the same values).  rows_limit caps the
+    matrix's rows (the oracle is timed on a slice of the largest ones).
+    Returns a dict of numpy arrays and sizes."""
+    import numpy as np
+    from dequantize_mat_vec_amd import synth
+    rng = synth.rng_for(4 if "lm-head" in name else (0 if kind == "gemv" and prm[0] == "i8row" else 1), idx, 0)
+    d = {"kind": kind, "nops": 1}
+    if kind == "group":
+        fmt, out, inf, nops = prm
+        out = out if rows_limit is None else min(out, rows_limit)
+        packed, scales = synth.matrix(fmt, rng, out, inf)
+        d.update(fmt=fmt, out=out, inf=inf, nops=nops, batch=1, packed=packed, scales=scales,
+                 xs=[synth.activations(rng, 1, inf) for _ in range(nops)],
+                 algo=nops * call_bytes(fmt, out, inf, 1, False), flops=2.0 * out * inf * nops)
+    elif kind == "gemv":
+        fmt, out, inf, batch = prm
+        out = out if rows_limit is None else min(out, rows_limit)
+        packed, scales = synth.matrix(fmt, rng, out, inf)
+        d.update(fmt=fmt, out=out, inf=inf, batch=batch, packed=packed, scales=scales,
+                 x=synth.activations(rng, batch, inf), algo=call_bytes(fmt, out, inf, batch, False),
+                 flops=2.0 * out * inf * batch)
+    elif kind == "qgemm":
+        fmt, m, n, k = prm
+        n = n if rows_limit is None else min(n, rows_limit)
+        packed = synth.quant_blocks(fmt, rng, n, k)
+        d.update(fmt=fmt, m=m, n=n, k=k, packed=packed, x16=synth.f16_activations(rng, m, k),
+                 bias=synth.bias(rng, n),
+                 algo=int(n * k * NOMINAL_BYTES_PER_WEIGHT[fmt]) + 2 * m * k + 4 * m * n + 4 * n,
+                 flops=2.0 * m * n * k)
+    else:
+        m, k, n = prm
+        n = n if rows_limit is None else min(n, rows_limit)
+        w16 = synth.f16_weights(rng, n, k)
+        d.update(m=m, n=n, k=k, w16=w16, packed=w16.view(np.uint8), x16=synth.f16_activations(rng, m, k),
+                 bias=synth.bias(rng, n), algo=2 * n * k + 2 * m * k + 4 * m * n + 4 * n,
+                 flops=2.0 * m * n * k)
+    return d
+
+
 def run_suite(lib, args):
     """Each case: enough weight copies to pass 640 MB (so the 256 MB
     last-level cache holds none between uses), a HIP graph of `reps`
     launches cycling over them, timed between two events over 10 replays;
     µs per call = graph time / reps (median, p10, p90 over replays).  The
     same copies are then read by the library's streaming-read hook: the
-    size-matched read ceiling the case is compared with."""
+    size-matched read ceiling the case is compared with.  Unless
+    --no-cpu-baseline, each line also carries the oracle's time per call
+    on the same inputs, measured in child processes (one BLAS thread and
+    the whole CPU share)."""
     import ctypes
     import numpy as np
     import torch
-    from dequantize_mat_vec_amd import _lib, synth
+    from dequantize_mat_vec_amd import _lib
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     out_lines = []
+    oracle_times = {} if args.no_cpu_baseline else run_suite_oracle(args)
     for idx, (name, kind, prm) in enumerate(suite_cases()):
         if args.suite_filter and not any(f in name for f in args.suite_filter.split(",")):
             continue
-        rng = synth.rng_for(4 if "lm-head" in name else (0 if kind == "gemv" and prm[0] == "i8row" else 1), idx, 0)
-        nops = 1
+        inp = suite_case_inputs(idx, name, kind, prm)
+        nops, algo, flops = inp["nops"], inp["algo"], inp["flops"]
+        packed = inp["packed"]
+        nbytes = packed.size * (nops if kind == "group" else 1)
         if kind == "group":
-            fmt, out, inf, nops = prm
-            batch = 1
-            packed, scales = synth.matrix(fmt, rng, out, inf)
+            fmt, out, inf, batch = inp["fmt"], inp["out"], inp["inf"], 1
             packed = np.concatenate([packed.reshape(-1)] * nops)
-            nbytes = packed.size
-            xg = [torch.from_numpy(synth.activations(rng, 1, inf)).to(dev) for _ in range(nops)]
+            xg = [torch.from_numpy(v).to(dev) for v in inp["xs"]]
             yg = [torch.empty(out, dtype=torch.float32, device=dev) for _ in range(nops)]
-            algo = nops * call_bytes(fmt, out, inf, 1, False)
-            flops = 2.0 * out * inf * nops
         elif kind == "gemv":
-            fmt, out, inf, batch = prm
-            packed, scales = synth.matrix(fmt, rng, out, inf)
-            nbytes = packed.size
-            x = torch.from_numpy(synth.activations(rng, batch, inf)).to(dev)
+            fmt, out, inf, batch = inp["fmt"], inp["out"], inp["inf"], inp["batch"]
+            x = torch.from_numpy(inp["x"]).to(dev)
             y = torch.empty(batch * out, dtype=torch.float32, device=dev)
-            sc = torch.from_numpy(scales).to(dev) if scales is not None else None
-            algo = call_bytes(fmt, out, inf, batch, False)
-            flops = 2.0 * out * inf * batch
-        elif kind == "qgemm":
-            fmt, m, n, k = prm
-            packed = synth.quant_blocks(fmt, rng, n, k)
-            x16 = torch.from_numpy(synth.f16_activations(rng, m, k).view(np.uint16)).to(dev)
-            b = torch.from_numpy(synth.bias(rng, n)).to(dev)
-            y = torch.empty(m * n, dtype=torch.float32, device=dev)
-            nbytes = packed.size
-            algo = int(n * k * NOMINAL_BYTES_PER_WEIGHT[fmt]) + 2 * m * k + 4 * m * n + 4 * n
-            flops = 2.0 * m * n * k
+            sc = torch.from_numpy(inp["scales"]).to(dev) if inp["scales"] is not None else None
         else:
-            m, k, n = prm
-            w16 = synth.f16_weights(rng, n, k)
-            x16 = torch.from_numpy(synth.f16_activations(rng, m, k).view(np.uint16)).to(dev)
-            b = torch.from_numpy(synth.bias(rng, n)).to(dev)
+            if kind == "qgemm":
+                fmt = inp["fmt"]
+            m, n, k = inp["m"], inp["n"], inp["k"]
+            x16 = torch.from_numpy(inp["x16"].view(np.uint16)).to(dev)
+            b = torch.from_numpy(inp["bias"]).to(dev)
             y = torch.empty(m * n, dtype=torch.float32, device=dev)
-            packed = w16.view(np.uint8)
-            nbytes = packed.size
-            algo = 2 * n * k + 2 * m * k + 4 * m * n + 4 * n
-            flops = 2.0 * m * n * k
         copies = max(2, int(np.ceil(640e6 / nbytes)))
         host = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
         ws = [host.to(dev) for _ in range(copies)]
@@ -387,11 +424,87 @@ def run_suite(lib, args):
                "weight_copies": copies}
         if kind in ("gemm", "qgemm"):
             rec["mfma_frac"] = round(flops / med / 1e6 / MFMA_F16_PEAK_TFLOPS, 5)
+        if name in oracle_times:
+            one, many = oracle_times[name]
+            rec["cpu_baseline"] = {
+                "kind": "oracle", "unit": "us/call",
+                "us_per_call_1thread": one["us_per_call"], "us_per_call_all_cores": many["us_per_call"],
+                "cores": many["threads"], "gpu_speedup_1thread": round(one["us_per_call"] / med, 1),
+                "gpu_speedup_all_cores": round(many["us_per_call"] / med, 1), "sample": one["sample"]}
         print(json.dumps(rec), flush=True)
         out_lines.append(rec)
         del ws
         torch.cuda.empty_cache()
     return out_lines
+
+
+SUITE_ORACLE_ROWS = 8192     # rows of the largest matrices the oracle is timed on
+
+
+def suite_oracle_leg(filt):
+    """Runs in a child process (BLAS/OpenMP threads set by the parent): the
+    oracle's time per call of every suite case on the same seeded inputs.
+    Matrices of more than SUITE_ORACLE_ROWS rows are timed on their first
+    SUITE_ORACLE_ROWS rows and scaled by rows (the oracle's cost is linear
+    in the rows it expands).  One JSON line per case."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    for idx, (name, kind, prm) in enumerate(suite_cases()):
+        if filt and not any(f in name for f in filt.split(",")):
+            continue
+        full = {"group": prm[1], "gemv": prm[1], "qgemm": prm[2], "gemm": prm[2]}[kind]
+        inp = suite_case_inputs(idx, name, kind, prm, SUITE_ORACLE_ROWS)
+        rows = {"group": "out", "gemv": "out"}.get(kind, "n")
+        timed_rows = inp[rows]
+
+        def once():
+            if kind == "group":
+                for xv in inp["xs"]:
+                    oracle.gemv_packed(inp["fmt"], inp["packed"], inp["out"], inp["inf"], xv, None,
+                                       inp["scales"])
+            elif kind == "gemv":
+                oracle.gemv_packed(inp["fmt"], inp["packed"], inp["out"], inp["inf"], inp["x"], None,
+                                   inp["scales"])
+            elif kind == "qgemm":
+                oracle.gemm_packed(inp["fmt"], inp["packed"], inp["n"], inp["k"], inp["x16"], inp["bias"])
+            else:
+                oracle.gemm_f16(inp["x16"], inp["w16"], inp["bias"])
+
+        reps, spent = 0, 0.0
+        while spent < 0.3 or reps < 2:
+            t0 = time.perf_counter()
+            once()
+            spent += time.perf_counter() - t0
+            reps += 1
+        us = spent / reps * 1e6 * full / timed_rows
+        sample = (f"float64 oracle, {threads} thread(s), {reps} call(s)"
+                  + (f" on the first {timed_rows} of {full} rows, scaled by rows" if timed_rows < full else ""))
+        print(json.dumps({"case": name, "us_per_call": round(us, 1), "threads": threads, "sample": sample}),
+              flush=True)
+
+
+def run_suite_oracle(args):
+    """{case: (1-thread timing, all-cores timing)} from two child runs of
+    suite_oracle_leg."""
+    host = host_cpu()
+    share = int(os.environ.get("OMP_NUM_THREADS") or host["affinity"])
+    res = {}
+    for threads in (1, share):
+        env = dict(os.environ)
+        for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+            env[k] = str(threads)
+        env["HIP_VISIBLE_DEVICES"] = ""
+        cmd = [sys.executable, os.path.abspath(__file__), "--suite-oracle-leg", "--suite-filter",
+               args.suite_filter]
+        out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=1800)
+        if out.returncode != 0:
+            raise RuntimeError(f"suite oracle leg failed: {out.stderr[-2000:]}")
+        for line in out.stdout.splitlines():
+            if line.startswith("{"):
+                r = json.loads(line)
+                res.setdefault(r["case"], []).append(r)
+    print(json.dumps({"suite_oracle_host": host}), flush=True)
+    return {k: tuple(v) for k, v in res.items() if len(v) == 2}
 
 
 # ---------------------------------------------------------------------------
@@ -526,6 +639,90 @@ def dominant_traffic(kernel_label):
 
 
 # ---------------------------------------------------------------------------
+# Parity of the timed step: sampled outputs of the step's own buffers,
+# checked by the oracle in the CPU leg's process
+# ---------------------------------------------------------------------------
+PARITY_LAYERS = (0, 1, 23)      # every kernel shape of the step: Q6_K down on 0, Q4_K down on 1
+PARITY_HEAD_ROWS = 8192
+GEMV_REL = 1e-4
+
+
+def parity_sample(calls, ys, skip_names=()):
+    """Outputs of the step just run, read back from its own y buffers: every
+    row of every call of PARITY_LAYERS and PARITY_HEAD_ROWS rows of the LM
+    head spread over its length (both ends included); calls named in
+    skip_names are left out.  {call index: (rows, y values)}."""
+    import numpy as np
+    sample = {}
+    for i, (layer, name, _, out, _, _) in enumerate(calls):
+        if name in skip_names:
+            continue
+        if name == "lm_head":
+            rng = np.random.default_rng([CONFIG_INDEX, 7])
+            rows = np.unique(np.concatenate([np.linspace(0, out - 1, PARITY_HEAD_ROWS // 2).astype(np.int64),
+                                             rng.integers(0, out, PARITY_HEAD_ROWS // 2)]))
+        elif layer in PARITY_LAYERS:
+            rows = np.arange(out)
+        else:
+            continue
+        sample[i] = (rows, ys[i].cpu().numpy()[rows])
+    return sample
+
+
+def parity_leg(path):
+    """Runs in the CPU leg's child process: regenerates the sampled calls'
+    inputs from the seeds, runs the float64 oracle on the sampled rows and
+    holds every output to 1e-4 * sum|w x| + 1e-6."""
+    import numpy as np
+    from dequantize_mat_vec_amd import synth
+    import oracle
+    data = np.load(path)
+    calls = synth.decode_step_calls()
+    n_out, worst, failures = 0, 0.0, []
+    for i in data["calls"]:
+        i = int(i)
+        layer, name, fmt, out, inf, _ = calls[i]
+        rows, y = data[f"rows_{i}"], data[f"y_{i}"]
+        packed, x, b = host_inputs([calls[i]])[0]
+        sub = packed.reshape(out, -1)[rows]
+        y_ref, s_ref = oracle.gemv_packed(fmt, sub, len(rows), inf, x, None if b is None else b[rows])
+        ratio = np.abs(y.astype(np.float64) - y_ref[0]) / (GEMV_REL * s_ref[0] + 1e-6)
+        bad = ~(ratio <= 1.0)
+        n_out += len(rows)
+        worst = max(worst, float(np.nanmax(np.where(np.isfinite(ratio), ratio, np.inf))))
+        if np.any(bad):
+            failures.append(f"{name}{layer} ({fmt} {out}x{inf}): {int(bad.sum())} rows, "
+                            f"first row {int(rows[np.argmax(bad)])}")
+    return {"ok": not failures, "calls": int(len(data["calls"])), "outputs": n_out,
+            "worst_err_over_bound": round(worst, 4), "failures": failures[:8]}
+
+
+def run_parity(calls, ys, skip_names=()):
+    """parity_sample() in this process, the check in a child process (the
+    oracle runs only in the CPU leg)."""
+    import tempfile
+    import numpy as np
+    sample = parity_sample(calls, ys, skip_names)
+    fd, path = tempfile.mkstemp(suffix=".npz")
+    os.close(fd)
+    try:
+        arrays = {"calls": np.array(sorted(sample), dtype=np.int64)}
+        for i, (rows, y) in sample.items():
+            arrays[f"rows_{i}"] = rows
+            arrays[f"y_{i}"] = y
+        np.savez(path, **arrays)
+        env = dict(os.environ)
+        env["HIP_VISIBLE_DEVICES"] = ""
+        cmd = [sys.executable, os.path.abspath(__file__), "--parity-leg", path]
+        res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
+        if res.returncode != 0:
+            raise RuntimeError(f"parity check failed to run: {res.stderr[-2000:]}")
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    finally:
+        os.unlink(path)
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same step
 # ---------------------------------------------------------------------------
 def cpu_leg(seconds):
@@ -611,6 +808,12 @@ def main(argv=None):
     if args.cpu_leg:
         print(json.dumps(cpu_leg(args.cpu_sample_seconds)))
         return 0
+    if args.parity_leg:
+        print(json.dumps(parity_leg(args.parity_leg)))
+        return 0
+    if args.suite_oracle_leg:
+        suite_oracle_leg(args.suite_filter)
+        return 0
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
         return 0
@@ -672,6 +875,17 @@ def main(argv=None):
         for i in range(args.warmup):
             run(i)
         torch.cuda.synchronize()
+        parity = None
+        if not args.no_parity:
+            # the oracle's check of the buffers the timed steps use: one more
+            # step (weight copy 0), its outputs poisoned first
+            for y in ys:
+                y.fill_(float("nan"))
+            run(0)
+            torch.cuda.synchronize()
+            # with the fused SwiGLU the gate buffer holds h and the down
+            # projection reads it: those calls are checked by the test suite
+            parity = run_parity(calls, ys, ("gate", "up", "down") if args.ffn == "swiglu" else ())
         t0 = time.perf_counter()
         for i in range(args.steps):
             run(i)
@@ -758,8 +972,10 @@ def main(argv=None):
         result["cpu_baseline"] = run_cpu_baseline(args.cpu_sample_seconds)
     else:
         result["cpu_baseline"] = None
+    result["parity"] = None if parity is None else parity["ok"]
+    result["parity_detail"] = parity
     print(json.dumps(result), flush=True)
-    return 0
+    return 0 if parity is None or parity["ok"] else 1
 
 
 if __name__ == "__main__":

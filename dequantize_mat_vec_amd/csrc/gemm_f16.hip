@@ -1,6 +1,6 @@
 // Small-M binary16 linear layer Y = X W^T + b ("inferno" README,
-// "Benchmarks": linear = x @ w + b at prompt width, e.g. 32x768 @ 768x2304;
-// "Bottlenecks are the big prompt-width GEMMs").  X binary16 [m][K],
+// "Benchmarks": linear = x @ w + b at prompt width, e.g. 32x768 @ 768x2304,
+// which the page names as where the prefill time goes).  X binary16 [m][K],
 // W binary16 [N][K] (same row orientation as the mat-vec), Y float32 [m][N],
 // float32 accumulation.
 //

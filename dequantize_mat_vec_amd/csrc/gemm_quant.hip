@@ -2,7 +2,7 @@
 // Q8_0 or Q4_K (packed rows, the layouts of the mat-vec), X binary16 [m][K],
 // Y float32 [m][N].  This is the prompt-width case of the decode step's
 // linear layer ("inferno" README, "Benchmarks": linear = x @ w + b at prompt
-// width; "Bottlenecks are the big prompt-width GEMMs") with the weights kept
+// width, the products that page finds dominate prefill) with the weights kept
 // in the quantized form of the mat-vec ("Project scaffold ...", quant.rs:
 // the fused dequantize + mat-vec that never expands W to float32).
 //

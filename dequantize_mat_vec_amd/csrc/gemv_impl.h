@@ -784,16 +784,19 @@ struct FmtI8Row {
 // ---------------------------------------------------------------------------
 // i4row: 32 code bytes per unit (64 weights; rows are padded to whole
 // units).  Dword t of the unit holds weights 8t .. 8t+7, the even ones in
-// the low nibbles.  XOR with 8 turns each two's complement nibble q into
-// the offset code q + 8 in 0..15, which converts exactly as an e4m3 byte
-// ((q + 8) * 2^-9); the offset is removed per 32 weights with the staged
-// sums of x, and the row scale is applied after the sum.
+// the low nibbles.  A two's complement nibble moved to the top of an
+// otherwise zero byte reads as the signed byte 16 q, so masking the high
+// nibbles in place (odd weights) and shifting the low ones up by 4 (even
+// weights) gives every code exactly through the sign-extending byte
+// converts; the sum carries the factor 16, which the epilogue removes with
+// an exact multiplication by 2^-4 before the row scale.
 // ---------------------------------------------------------------------------
 struct FmtI4Row {
   static constexpr bool kRowScales = true;
-  static constexpr bool kSums = true;
+  static constexpr bool kSums = false;
   static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
+  static constexpr float kAccScale = 0.0625f;
   struct Raw { u32x4 a, b; };
   struct Lane {};
   __device__ static Lane lane_state(int) { return {}; }
@@ -820,13 +823,8 @@ struct FmtI4Row {
 
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float* sums, int64_t nsub,
+                                                 const float* xs, const float*, int64_t,
                                                  const Lane&, float* acc) {
-    float p[R][2][B];
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { p[k][0][b] = 0.f; p[k][1][b] = 0.f; }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       f32x4 xa[B], xb[B];
@@ -837,13 +835,14 @@ struct FmtI4Row {
       }
 #pragma unroll
       for (int k = 0; k < R; ++k) {
-        const uint32_t v = word(r[k], t) ^ 0x88888888u;
-        float e0, e1, e2, e3, o0, o1, o2, o3;
-        nibbles_x512(v & 0x0F0F0F0Fu, e0, e1, e2, e3);
-        nibbles_x512((v >> 4) & 0x0F0F0F0Fu, o0, o1, o2, o3);
+        const uint32_t v = word(r[k], t);
+        const uint32_t ev = (v << 4) & 0xF0F0F0F0u;   // even weights, 16 q each
+        const uint32_t od = v & 0xF0F0F0F0u;          // odd weights
+        const float e0 = sbyte<0>(ev), e1 = sbyte<1>(ev), e2 = sbyte<2>(ev), e3 = sbyte<3>(ev);
+        const float o0 = sbyte<0>(od), o1 = sbyte<1>(od), o2 = sbyte<2>(od), o3 = sbyte<3>(od);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          float& s = p[k][t >> 2][b];
+          float& s = acc[k * B + b];
           s = fmaf(e0, xa[b].x, s); s = fmaf(o0, xa[b].y, s);
           s = fmaf(e1, xa[b].z, s); s = fmaf(o1, xa[b].w, s);
           s = fmaf(e2, xb[b].x, s); s = fmaf(o2, xb[b].y, s);
@@ -851,17 +850,16 @@ struct FmtI4Row {
         }
       }
     }
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float* sb = sums + b * nsub + 2 * u;
-        float v = fmaf(512.f, p[k][0][b], -8.f * sb[0]);
-        v += fmaf(512.f, p[k][1][b], -8.f * sb[1]);
-        acc[k * B + b] += v;
-      }
   }
 };
+
+// Factor the kernel epilogue applies to a finished row sum before the row
+// scale and bias: 1 except where a format's codes enter scaled by a power
+// of two.
+template <class F, class = void>
+struct AccScale { static constexpr float value = 1.0f; };
+template <class F>
+struct AccScale<F, std::void_t<decltype(F::kAccScale)>> { static constexpr float value = F::kAccScale; };
 
 template <class F>
 __device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp, int u,
@@ -1144,8 +1142,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
       const float rs1 = a.scales2 ? ep[2] : 1.f;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float gv = acc[b] * rs0;
-        const float uv = up[b] * rs1;
+        const float gv = (acc[b] * AccScale<F>::value) * rs0;
+        const float uv = (up[b] * AccScale<F>::value) * rs1;
         a.y[b * a.out + row] = gv / (1.f + expf(-gv)) * uv;
       }
     }
@@ -1157,8 +1155,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
       const float rs1 = a.scales2 ? ep[2] : 1.f;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float gv = acc[b] * rs0;
-        const float uv = acc[B + b] * rs1;
+        const float gv = (acc[b] * AccScale<F>::value) * rs0;
+        const float uv = (acc[B + b] * AccScale<F>::value) * rs1;
         a.y[b * a.out + row] = gv / (1.f + expf(-gv)) * uv;
       }
     }
@@ -1172,7 +1170,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
       const float bv = a.bias ? ep[0] : 0.f;
       const float rs = a.scales ? ep[1] : 1.f;
 #pragma unroll
-      for (int b = 0; b < B; ++b) a.y[b * a.out + row] = fmaf(acc[k * B + b], rs, bv);
+      for (int b = 0; b < B; ++b)
+        a.y[b * a.out + row] = fmaf(acc[k * B + b] * AccScale<F>::value, rs, bv);
     }
   }
 }

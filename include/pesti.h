@@ -48,9 +48,7 @@
  *     y[b][o] = sum_i w[o][i] * x[b][i] + bias[o].
  *   - Accumulation is float32; dequantized weights are never written out.
  *     Result bound: |y - exact| <= 1e-4 * sum_i |w_i x_i| + 1e-6 for the
- *     mat-vec (2e-3 for the f16 GEMM).  i4row accumulates the codes with
- *     an offset of 8 that is taken out per 32 weights, which adds
- *     4e-5 * s[o] * sum_i |x_i| to its bound (rows of mostly zero codes).
+ *     mat-vec (2e-3 for the f16 GEMM).
  *   - Pointers are device pointers owned by the caller, on the calling
  *     thread's current HIP device, and must be 16-byte aligned (blocks, x,
  *     y, w, codes; bias and row_scales 4-byte aligned).  x and y must not
@@ -167,8 +165,9 @@ int pesti_gemv_i8row(int64_t out_features, int64_t in_features, const int8_t* co
  * INT8): packed int4 rows of pesti_row_bytes(PESTI_FMT_I4ROW, in) bytes,
  * row_scales float32 [out].  Matrices of at least 16384 rows with rows of at
  * most 1024 weights, at batch 2..8, run on the matrix cores with x split as
- * described for pesti_gemv_q4_k (the codes enter exactly; the int4 bound
- * stated above holds for both kernels). */
+ * described for pesti_gemv_q4_k.  Both kernels take every code exactly
+ * (the vector-ALU kernel as the signed byte 16 q, the sum then scaled by
+ * 2^-4 exactly), so the mat-vec bound above holds unchanged. */
 int pesti_gemv_i4row(int64_t out_features, int64_t in_features, const void* packed,
                      const float* row_scales, const float* x, float* y,
                      const float* bias, int32_t batch, void* stream);

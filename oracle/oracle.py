@@ -21,8 +21,9 @@ What it computes, and the passages it follows
   row-major tensors in and out; a linear layer is x @ w + b.
 
 The pages name the formats (Q8_0, Q4_K, Q6_K, per-row int8) but print no byte
-layout.  The layouts below are the GGUF block arrangements, which is the
-plainest reading of "GGUF parsing + dequantization ... verified byte-exact":
+layout.  The layouts below are the GGUF block arrangements, the plainest
+reading of that page's claim to parse GGUF files and dequantize them
+byte-exactly:
 
 * Q8_0, 34 bytes per 32 weights: binary16 d, then 32 int8 codes q.
   w[i] = d * q[i].
@@ -34,8 +35,8 @@ plainest reading of "GGUF parsing + dequantization ... verified byte-exact":
   bytes of 6-bit scales and mins as Q4_K, 32 bytes of high bits qh, then
   128 bytes of low 4-bit codes in Q4_K's arrangement.  Weight 64r + l
   (l < 32) has high bit r*2 of qh[l], weight 64r + 32 + l bit 2r+1.
-  w[i] = d * sc[j] * q[i] - dmin * m[j], q in 0..31.  (The pages name
-  "all K-family quantizations"; this is the GGUF arrangement.)
+  w[i] = d * sc[j] * q[i] - dmin * m[j], q in 0..31.  (The pages list the
+  whole K family by name only; this is the GGUF arrangement.)
 * Q2_K, 84 bytes per 256 weights: 16 bytes, one per 16-weight sub-block,
   holding a 4-bit scale (low nibble) and a 4-bit min (high nibble); 64
   bytes of 2-bit codes; binary16 d; binary16 dmin.  Weight 128h + 32j +

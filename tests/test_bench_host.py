@@ -116,3 +116,72 @@ def test_more_than_one_gpu_is_refused():
 def test_default_contract_arguments():
     a = bench.parse_args([])
     assert (a.gpus, a.steps, a.warmup, a.mode, a.grouping, a.ffn) == (1, 50, 10, "graph", "stage", "separate")
+
+
+class _HostY:
+    """Stands in for a device y buffer: .cpu().numpy() gives the values."""
+
+    def __init__(self, v):
+        self.v = v
+
+    def cpu(self):
+        return self
+
+    def numpy(self):
+        return self.v
+
+
+def _oracle_outputs(calls, sample_calls):
+    import numpy as np
+    import oracle
+    ys = [None] * len(calls)
+    host = bench.host_inputs([calls[i] for i in sample_calls])
+    for i, (packed, x, b) in zip(sample_calls, host):
+        _, _, fmt, out, inf, _ = calls[i]
+        y, _ = oracle.gemv_packed(fmt, packed, out, inf, x, b)
+        ys[i] = _HostY(y[0].astype(np.float32))
+    return ys
+
+
+def test_parity_leg_accepts_rounded_oracle_and_rejects_a_planted_error(tmp_path, monkeypatch):
+    """The benchmark's parity check (sample of the step's outputs, checked by
+    the oracle in the CPU leg): float32-rounded oracle outputs pass, one
+    output moved past the bound fails and is named."""
+    import numpy as np
+    monkeypatch.setattr(bench, "PARITY_HEAD_ROWS", 64)
+    calls = synth.decode_step_calls(layers=2)
+    # layer 23 does not exist in a 2-layer step; the sample takes layers 0, 1
+    # and the head
+    sample_calls = list(range(len(calls)))
+    ys = _oracle_outputs(calls, sample_calls)
+    monkeypatch.setattr(synth, "decode_step_calls", lambda layers=2: calls)
+    sample = bench.parity_sample(calls, ys)
+    assert sorted(sample) == sample_calls
+    head_rows = sample[len(calls) - 1][0]
+    assert head_rows[0] == 0 and head_rows[-1] == 151935 and len(head_rows) >= 32
+
+    def check(sample):
+        path = tmp_path / "s.npz"
+        arrays = {"calls": np.array(sorted(sample), dtype=np.int64)}
+        for i, (rows, y) in sample.items():
+            arrays[f"rows_{i}"] = rows
+            arrays[f"y_{i}"] = y
+        np.savez(path, **arrays)
+        return bench.parity_leg(str(path))
+
+    res = check(sample)
+    assert res["ok"] and res["calls"] == len(calls) and res["worst_err_over_bound"] < 1.0
+    rows, y = sample[6]                       # layer 0's Q6_K down projection
+    y = y.copy()
+    y[17] += 1e-2 * (np.abs(y[17]) + 1.0)
+    sample[6] = (rows, y)
+    res = check(sample)
+    assert not res["ok"] and "down0" in res["failures"][0] and "first row 17" in res["failures"][0]
+
+
+def test_parity_sample_skips_the_fused_calls():
+    import numpy as np
+    calls = synth.decode_step_calls(layers=2)
+    ys = [_HostY(np.zeros(c[3], np.float32)) for c in calls]
+    sample = bench.parity_sample(calls, ys, ("gate", "up", "down"))
+    assert all(calls[i][1] not in ("gate", "up", "down") for i in sample)

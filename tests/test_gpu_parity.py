@@ -257,22 +257,25 @@ def test_i4row_padding_codes_do_not_matter():
 
 
 @pytest.mark.parametrize("density", [0.0, 0.02, 0.3])
-def test_i4row_sparse_codes_within_offset_bound(density):
-    """The int4 kernel carries each code with an offset of 8 that it takes
-    out per 32 weights; rows of mostly zero codes are held to the stated
-    bound 1e-4 * sum|w x| + 4e-5 * s * sum|x| + 1e-6."""
+@pytest.mark.parametrize("batch", [1, 2])
+def test_i4row_sparse_codes(density, batch):
+    """Rows of mostly zero int4 codes (an all-zero row must give exactly the
+    bias) meet the plain mat-vec bound 1e-4 * sum|w x| + 1e-6 at batch 1
+    (vector ALUs) and 2 (matrix cores for tall matrices, vector ALUs for
+    this 96-row one)."""
     import packing
-    rng = np.random.default_rng([16, int(density * 100)])
-    out, inf, batch = 96, 4864, 2
+    rng = np.random.default_rng([16, int(density * 100), batch])
+    out, inf = 96, 4864
     q = rng.integers(-8, 8, (out, inf)) * (rng.random((out, inf)) < density)
     packed = np.array([np.frombuffer(packing.pack_i4_row(q[r]), np.uint8) for r in range(out)])
     scales = (0.005 + 0.01 * rng.random(out)).astype(np.float32)
     x = synth.activations(rng, batch, inf)
-    y = run_gemv("i4row", packed, scales, out, inf, x)
-    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, None, scales)
-    extra = 4e-5 * scales.astype(np.float64)[None, :] * np.abs(x.astype(np.float64)).sum(axis=1)[:, None]
-    err = np.abs(y.astype(np.float64) - y_ref)
-    assert np.all(err <= GEMV_REL * s_ref + extra + 1e-6), float((err - GEMV_REL * s_ref - extra).max())
+    bias = synth.bias(rng, out)
+    y = run_gemv("i4row", packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"i4row density {density} b{batch}")
+    if density == 0.0:
+        assert np.array_equal(y, np.broadcast_to(bias, y.shape))
 
 
 def test_q8_0_zero_codes_is_exact_bias():
@@ -956,3 +959,66 @@ def test_long_rows_group_equals_single_calls_bitwise(fmt):
         assert torch.equal(yg, ys), (out, inf)
         y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
         assert_within(ys.cpu().numpy().reshape(2, out), y_ref, s_ref, GEMV_REL, f"long-row group {fmt} {out}x{inf}")
+
+
+# ---------------------------------------------------------------------------
+# exact cancellation: d*sc*q == dmin*m in every sub-block, so every weight
+# is 0 and y must be the bias within 1e-4 * |b| + 1e-6
+# ---------------------------------------------------------------------------
+def _cancelling_row(fmt, rng, n_super):
+    """Packed bytes of one row of n_super super-blocks in which every
+    sub-block has one constant code c and scale/min with sc * c == m (and
+    d == dmin), so each of its weights is d*sc*c - dmin*m = 0 exactly."""
+    import packing
+    blocks = []
+    for _ in range(n_super):
+        d = packing.f16_bits(abs(rng.normal(0.0, np.sqrt(1e-3))))
+        if fmt in ("q4_k", "q5_k"):
+            cmax = 15 if fmt == "q4_k" else 31
+            sc, m, q = [], [], []
+            for _ in range(8):
+                c = int(rng.integers(1, cmax + 1))
+                s = int(rng.integers(1, 63 // c + 1))
+                sc.append(s)
+                m.append(s * c)
+                q += [c] * 32
+            pack = packing.pack_q4_k_block if fmt == "q4_k" else packing.pack_q5_k_block
+            blocks.append(pack(d, d, sc, m, q))
+        else:
+            sc, m, q = [], [], [0] * 256
+            for s_idx in range(16):
+                c = int(rng.integers(1, 4))
+                s = int(rng.integers(1, 15 // c + 1))
+                sc.append(s)
+                m.append(s * c)
+            for h in range(2):
+                for j in range(4):
+                    for c2 in range(2):
+                        for l in range(16):
+                            sub = 8 * h + 2 * j + c2
+                            q[128 * h + 32 * j + 16 * c2 + l] = m[sub] // sc[sub]
+            blocks.append(packing.pack_q2_k_block(d, d, sc, m, q))
+    return np.frombuffer(b"".join(blocks), np.uint8)
+
+
+CANCEL_CASES = [(40, 896, 1), (40, 896, 3), (40, 4864, 1), (40, 4864, 3), (MFMA_ROWS + 5, 896, 3)]
+
+
+@pytest.mark.xfail(reason="kernels take the min term from staged sums of x; exact form pending", strict=False)
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q2_k"])
+@pytest.mark.parametrize("out,inf,batch", CANCEL_CASES)
+def test_exact_cancellation_gives_bias(fmt, out, inf, batch):
+    """Rows whose weights are all exactly zero through d*sc*q == dmin*m:
+    the vector-ALU kernels (40 rows) and the matrix-core kernels (tall, at
+    batch 3) must return the bias within the bound's 1e-6 floor."""
+    rng = np.random.default_rng([31, len(fmt), inf, batch])
+    n_super = -(-inf // 256)
+    distinct = np.stack([_cancelling_row(fmt, rng, n_super) for _ in range(48)])
+    packed = np.resize(distinct, (out, distinct.shape[1]))
+    x = synth.activations(rng, batch, inf)
+    bias = synth.bias(rng, out)
+    w64 = oracle.dequantize(fmt, distinct, 48, inf)
+    assert not np.any(w64), "fixture: every weight must be exactly zero"
+    y = run_gemv(fmt, packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} cancelling {out}x{inf} b{batch}")
