@@ -5,9 +5,8 @@
 //   * a row is served by a group of L lanes (L = 16, 32 or 64), so a wave
 //     holds 64/L rows at once; each lane walks the row's "units" (a fixed
 //     run of packed bytes and the weights it encodes) with stride L;
-//   * x (and, for Q4_K, its per-32 sums) is staged once per workgroup in
-//     LDS; weights stream from HBM straight into registers and are decoded
-//     there, never written back;
+//   * x is staged once per workgroup in LDS; weights stream from HBM
+//     straight into registers and are decoded there, never written back;
 //   * per-lane float32 partial sums are combined across the L lanes with
 //     DPP row operations (plus one swizzle step per doubling beyond 16).
 #pragma once
@@ -133,6 +132,23 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
       }
     }
   }
+}
+
+// The code c nearest to dm / ds, the ratio of a sub-block's min term to
+// its scale, if it lies in 0..cmax, else 0.  With it a weight is
+// w = ds (q - c) + (ds c - dm): the matrix cores take the small integers
+// q - c, and the remainder ds c - dm, computed in float32 once per
+// sub-block, is exactly 0 when every weight of the sub-block is (q = c,
+// ds c = dm), where taking ds q and dm apart would leave the rounding
+// errors of two large sums.  The remainder is always exact in float32: it
+// is a multiple of the smaller of d's and dmin's binary16 ulps, and for
+// c >= 1 (dm >= ds / 2) its magnitude, at most ds / 2, is below 2^17 of
+// those; so a one-hot x still yields each weight with a single rounding.
+// v_rcp_f32 is within an ulp, so an integer ratio rounds to itself; ds = 0
+// or a negative ratio gives c = 0.
+__device__ __forceinline__ float nearest_code(float dm, float ds, float cmax) {
+  const float r = rintf(dm * __builtin_amdgcn_rcpf(ds));
+  return (r >= 0.f && r <= cmax) ? r : 0.f;   // false for NaN and infinity
 }
 
 // Read 4 consecutive logical floats starting at logical index i (i % 4 == 0).

@@ -13,9 +13,11 @@
 // every product is exact in the float32 accumulator of
 // v_mfma_f32_16x16x32_f16.  One MFMA k-step is one 32-weight sub-block
 // (a Q8_0 block, a Q4_K sub-block), so its scales are applied to the
-// step's 16x16 partial tile in float32: acc += (d * sc) * sum(q x), and for
-// Q4_K acc -= (dmin * m) * sum(x), sum(x) coming from a second MFMA against
-// a tile of ones.
+// step's 16x16 partial tile in float32: acc += (d * sc) * sum(q x).  Formats
+// with mins take the codes less the sub-block's nearest code c
+// (nearest_code in common.h) and add (d sc c - dmin m) * sum(x), sum(x)
+// coming from a second MFMA against a tile of ones: that remainder is
+// exactly 0 where a sub-block's weights all are.
 //
 // Work split as in the binary16 GEMM: a workgroup owns 16 output columns
 // (16 rows of W) and 16 * MT rows of X, its NW wavefronts take contiguous
@@ -27,6 +29,8 @@
 // MFMA operand layout, lane l (i = l % 16, kg = l / 16): A = X row i,
 // k = 8kg..8kg+7; B = W row i (output column i), the same k; C = column i,
 // rows 4kg..4kg+3.
+#include <type_traits>
+
 #include "gemm_wide.h"
 
 namespace pesti {
@@ -56,7 +60,6 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // in-bounds re-read), never a byte outside the block, and realigns them.
 // ---------------------------------------------------------------------------
 struct QPolQ8_0 {
-  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -103,7 +106,6 @@ struct QPolQ8_0 {
 // super-blocks).
 // ---------------------------------------------------------------------------
 struct QPolQ4_K {
-  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -119,24 +121,37 @@ struct QPolQ4_K {
     st.j = static_cast<uint32_t>(j);
   }
 
+  // The codes less c, (q - c) 2^-9: a nibble in an otherwise zero e4m3 byte
+  // is q * 2^-9 (scale 1), and the binary16 subtraction is exact.
   __device__ __forceinline__ static qhalf8 codes(const Step& st) {
+    float ds, dm, c;
+    sub_block(st, ds, dm, c);
+    const qhalf2 off = __builtin_bit_cast(qhalf2, pack_f16(c * (1.0f / 512.0f), c * (1.0f / 512.0f)));
     const uint32_t sh = 4u * (st.j & 1u);   // high nibbles for odd sub-blocks
     const uint32_t a = (st.c[0] >> sh) & 0x0F0F0F0Fu;
     const uint32_t b = (st.c[1] >> sh) & 0x0F0F0F0Fu;
-    // A nibble in an otherwise zero e4m3 byte is q * 2^-9; scale 1.
-    uint32_t h[4];
-    h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false));
-    h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true));
-    h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
-    h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true));
+    qhalf2 h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false) - off;
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true) - off;
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false) - off;
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true) - off;
     return __builtin_bit_cast(qhalf8, h);
   }
 
-  // d * sc * 2^9 (undoing the 2^-9 of the code conversion) and dmin * m of
-  // sub-block j.  Sub-blocks 0..3: sc = S[j] & 63, m = S[j+4] & 63; 4..7
-  // (t = j - 4): sc = (S[j+4] & 15) | (S[t] >> 6) << 4, m = (S[j+4] >> 4)
-  // | (S[j] >> 6) << 4, where S[0..11] are header bytes 4..15.
+  // d * sc * 2^9 (undoing the 2^-9 of the code conversion) and the part of
+  // the min term the codes leave, dmin * m - d * sc * c (exact).
   __device__ __forceinline__ static void scales(const Step& st, float& ds, float& dm) {
+    float c;
+    sub_block(st, ds, dm, c);
+    dm = -fmaf(ds, c, -dm);
+    ds *= 512.0f;
+  }
+
+  // d * sc, dmin * m and nearest_code of sub-block j.  Sub-blocks 0..3:
+  // sc = S[j] & 63, m = S[j+4] & 63; 4..7 (t = j - 4): sc = (S[j+4] & 15) |
+  // (S[t] >> 6) << 4, m = (S[j+4] >> 4) | (S[j] >> 6) << 4, where S[0..11]
+  // are header bytes 4..15.
+  __device__ __forceinline__ static void sub_block(const Step& st, float& ds, float& dm, float& c) {
     const uint32_t j = st.j;
     const uint32_t t = j & 3u;
     const uint32_t y = st.hdr.y, z = st.hdr.z, w = st.hdr.w;
@@ -150,8 +165,9 @@ struct QPolQ4_K {
       mn = (sw >> 4) | ((sz >> 6) << 4);
     }
     const float d = f16_lo(st.hdr.x), dmin = f16_hi(st.hdr.x);
-    ds = d * 512.0f * static_cast<float>(sc);
+    ds = d * static_cast<float>(sc);
     dm = dmin * static_cast<float>(mn);
+    c = nearest_code(dm, ds, 15.f);
   }
   __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) { return codes(st); }
   __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
@@ -199,7 +215,6 @@ __device__ __forceinline__ qhalf8 q6_k_part(qhalf8 v, int part, int kg) {
 }
 
 struct QPolQ6_K {
-  static constexpr bool kMinOperand = false;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 2;
@@ -227,30 +242,14 @@ struct QPolQ6_K {
 
 // ---------------------------------------------------------------------------
 // Operands carrying their scale: 8 small unsigned code bytes v (two dwords)
-// become binary16 1024 + v by writing 0x64 above each byte (v_perm_b32),
-// and one packed FMA per pair gives (1024 + v) * s - 1024 * s = v * s,
-// exact because -1024 * s, the exact product inside the FMA and the result
-// are all binary16 values (Q5_K q * sc <= 31 * 63 = 1953, Q2_K q * sc <= 45).
-// Q3_K's offset code (v - 4) * (sc - 32) takes a packed subtraction and a
-// packed product instead (1028 * s is not always a binary16 value).  s is
-// per lane, so a k-step whose lanes belong to different sub-blocks needs
-// no second product.
+// become binary16 1024 + v by writing 0x64 above each byte (v_perm_b32);
+// an exact packed subtraction of base (1024 plus the code offset) and an
+// exact packed product by the lane's scale s follow, giving
+// (v - (base - 1024)) * s: Q5_K (q - c) * sc (|.| <= 31 * 63), Q2_K
+// (q - c) * sc (<= 45), Q3_K (v - 4) * (sc - 32) (<= 128), all binary16
+// integers.  s is per lane, so a k-step whose lanes belong to different
+// sub-blocks needs no second product.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ qhalf8 scaled_codes(uint32_t lo, uint32_t hi, qhalf2 s, qhalf2 off) {
-  uint32_t h[4];
-  h[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);   // [v0, 0x64, v1, 0x64]
-  h[1] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
-  h[2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
-  h[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    h[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(qhalf2, h[e]), s, off));
-  return __builtin_bit_cast(qhalf8, h);
-}
-
-// (v - (base - 1024)) * s for the same code bytes, as an exact packed
-// subtraction then an exact packed product (for offsets whose FMA constant
-// -base * s would not be a binary16 integer).
 __device__ __forceinline__ qhalf8 offset_codes(uint32_t lo, uint32_t hi, qhalf2 s, qhalf2 base) {
   uint32_t h[4];
   h[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
@@ -289,11 +288,11 @@ __device__ __forceinline__ void k4_scale_min(uint32_t y, uint32_t z, uint32_t w,
 
 // Q5_K step s (sub-block j = s % 8 of super-block s / 8, 176 bytes): the
 // lane's 8 low nibbles (bytes 48 + 32(j / 2) + 8kg) and their fifth bits
-// (bit j of bytes 16 + 8kg); operand q * sc_j, scaled by d; mins dmin * m_j
-// times the step's sum of x (product against ones).
+// (bit j of bytes 16 + 8kg); operand (q - c) * sc_j with c the sub-block's
+// nearest_code, scaled by d; the remainder dmin * m_j - d sc_j c times the
+// step's sum of x (product against ones).
 struct QPolQ5_K {
   static constexpr bool kMin = true;
-  static constexpr bool kMinOperand = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
   struct Step { uint32_t c[2]; uint32_t h[2]; u32x4 hdr; uint32_t j; };
@@ -315,16 +314,19 @@ struct QPolQ5_K {
     const uint32_t hi = ((st.c[1] >> sh) & 0x0F0F0F0Fu) | (((st.h[1] >> st.j) & 0x01010101u) << 4);
     uint32_t sc, mn;
     k4_scale_min(st.hdr.y, st.hdr.z, st.hdr.w, static_cast<int>(st.j), sc, mn);
-    const qhalf2 s = half_pair(sc);
-    return scaled_codes(lo, hi, s, s * qhalf2{-1024, -1024});
+    const float c = nearest_code(f16_hi(st.hdr.x) * static_cast<float>(mn), f16_lo(st.hdr.x) * static_cast<float>(sc),
+                                 31.f);
+    const qhalf2 base = __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c));
+    return offset_codes(lo, hi, half_pair(sc), base);
   }
   __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
     uint32_t sc, mn;
     k4_scale_min(st.hdr.y, st.hdr.z, st.hdr.w, static_cast<int>(st.j), sc, mn);
     ds = f16_lo(st.hdr.x);
+    const float dsc = ds * static_cast<float>(sc);
     dm = f16_hi(st.hdr.x) * static_cast<float>(mn);
+    dm = -fmaf(dsc, nearest_code(dm, dsc, 31.f), -dm);
   }
-  __device__ __forceinline__ static qhalf8 min_codes(const Step&, int) { return qhalf8{}; }
 };
 
 // Q3_K step s (t = s % 8 of super-block s / 8, 110 bytes, 2-byte aligned):
@@ -334,7 +336,6 @@ struct QPolQ5_K {
 // (low | high << 2) - 4 = q times the lane's own scale - 32, scaled by d.
 struct QPolQ3_K {
   static constexpr bool kMin = false;
-  static constexpr bool kMinOperand = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
   struct Step { uint32_t q[2]; uint32_t hm[2]; uint32_t s01, s2; uint32_t d; uint32_t t; };
@@ -369,17 +370,17 @@ struct QPolQ3_K {
     ds = f16_lo(st.d);
     dm = 0.f;
   }
-  __device__ __forceinline__ static qhalf8 min_codes(const Step&, int) { return qhalf8{}; }
 };
 
 // Q2_K step s (t = 4h + j of super-block s / 8, 84 bytes): lane kg holds
 // c = kg / 2, l = 8(kg % 2) .. +7 of sub-block k = 8h + 2j + c: codes at bit
 // 2j of bytes 16 + 32h + 16c + l, scale and min nibbles of byte k.  Operand
-// q * sc, scaled by d; the mins are a second product against the lane's
-// min m (every k of a lane shares it), scaled by dmin.
+// (q - c_k) * sc with c_k the sub-block's nearest_code, scaled by d; the
+// remainders dmin m - d sc c_k of the step's two sub-blocks multiply sums
+// of x over its two 16-weight halves (products against ones on one half).
 struct QPolQ2_K {
   static constexpr bool kMin = true;
-  static constexpr bool kMinOperand = true;
+  static constexpr bool kHalfMins = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
   struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
@@ -394,19 +395,26 @@ struct QPolQ2_K {
     st.dd = load_u32(sb + 80);
     st.j = static_cast<uint32_t>(j);
   }
+  // d * sc, dmin * m and nearest_code of the lane's sub-block
+  __device__ __forceinline__ static void sub_block(const Step& st, float& ds, float& dm, float& c) {
+    ds = f16_lo(st.dd) * static_cast<float>(st.scb & 15u);
+    dm = f16_hi(st.dd) * static_cast<float>((st.scb >> 4) & 15u);
+    c = nearest_code(dm, ds, 3.f);
+  }
   __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) {
+    float ds, dm, c;
+    sub_block(st, ds, dm, c);
     const uint32_t lo = (st.q[0] >> (2 * st.j)) & 0x03030303u;
     const uint32_t hi = (st.q[1] >> (2 * st.j)) & 0x03030303u;
-    const qhalf2 s = half_pair(st.scb & 15u);
-    return scaled_codes(lo, hi, s, s * qhalf2{-1024, -1024});
+    const qhalf2 base = __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c));
+    return offset_codes(lo, hi, half_pair(st.scb & 15u), base);
   }
+  // ds = d; dm = the lane's sub-block's remainder dmin m - d sc c (exact)
   __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    float dsc, c;
+    sub_block(st, dsc, dm, c);
     ds = f16_lo(st.dd);
-    dm = f16_hi(st.dd);
-  }
-  __device__ __forceinline__ static qhalf8 min_codes(const Step& st, int) {
-    const _Float16 m = static_cast<_Float16>(static_cast<float>((st.scb >> 4) & 15u));
-    return qhalf8{m, m, m, m, m, m, m, m};
+    dm = -fmaf(dsc, c, -dm);
   }
 };
 
@@ -498,52 +506,40 @@ struct WPolQ4_K {
     }
   }
 
-  // Operand of sub-block j: q * sc_j, an integer of at most 945, exact in
-  // binary16, so the super-block's eight k-steps accumulate in the matrix
-  // core and d is applied once.  A code byte q becomes binary16 1024 + q by
-  // placing 0x64 above it (v_perm_b32); one packed FMA then gives
-  // (1024 + q) * sc - 1024 * sc = q * sc, exact (one rounding of an exact
-  // small integer).  sc_j itself comes the same way: 1024 + sc, minus 1024.
+  // Operand of sub-block j: (q - c_j) * sc_j with c_j its nearest_code, an
+  // integer of magnitude at most 945, exact in binary16, so the
+  // super-block's eight k-steps accumulate in the matrix core and d is
+  // applied once.  A code byte q becomes binary16 1024 + q by placing 0x64
+  // above it (v_perm_b32); an exact packed subtraction of 1024 + c_j and an
+  // exact packed product by sc_j follow.
   __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int) {
     const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
     const uint32_t a = (un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu;
     const uint32_t b = (un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu;
-    // Scale bytes of sub-blocks 0..3 and 4..7 (S = header bytes 4..15).
-    const uint32_t sc_lo = un.hdr.y & 0x3F3F3F3Fu;
-    const uint32_t sc_hi = (un.hdr.w & 0x0F0F0F0Fu) | ((un.hdr.y >> 2) & 0x30303030u);
-    const uint32_t t = static_cast<uint32_t>(j & 3);
-    const uint32_t sel_sc = 0x04000400u | (t << 16) | t;   // [t, 0x64, t, 0x64]
-    const qhalf2 sc1024 = __builtin_bit_cast(qhalf2, __builtin_amdgcn_perm(0x64646464u, j < 4 ? sc_lo : sc_hi, sel_sc));
-    const qhalf2 sc = sc1024 - qhalf2{1024, 1024};
-    const qhalf2 off = sc * qhalf2{-1024, -1024};
-    uint32_t h[4];
-    h[0] = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);   // [q0, 0x64, q1, 0x64]
-    h[1] = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);   // [q2, 0x64, q3, 0x64]
-    h[2] = __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u);
-    h[3] = __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      h[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(qhalf2, h[e]), sc, off));
-    return __builtin_bit_cast(qhalf8, h);
+    uint32_t sc, mn;
+    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, j, sc, mn);
+    const float c = nearest_code(f16_hi(un.hdr.x) * static_cast<float>(mn), d(un) * static_cast<float>(sc), 15.f);
+    return offset_codes(a, b, half_pair(sc), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
   }
 
   __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
 
-  // -dmin * m_j for sub-block j = 4 * half + kg: the B operand of the
-  // 16x16x4 float32 product that subtracts the mins.  m_kg = S[4+kg] & 63;
-  // m_{4+kg} = (S[8+kg] >> 4) | (S[kg+4] >> 6) << 4.
+  // d sc_j c_j - dmin m_j for sub-block j = 4 * half + kg (exact, zero for a
+  // sub-block of zero weights): the B operand of the 16x16x4 float32
+  // product that adds what the codes leave of the mins.
   __device__ __forceinline__ static float neg_min(const Unit& un, int half, int kg) {
-    const uint32_t z = (un.hdr.z >> (8 * kg)) & 0xFFu;
-    const uint32_t w = (un.hdr.w >> (8 * kg)) & 0xFFu;
-    const uint32_t m = half == 0 ? (z & 63u) : ((w >> 4) | ((z >> 6) << 4));
-    return -f16_hi(un.hdr.x) * static_cast<float>(m);
+    uint32_t sc, mn;
+    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, 4 * half + kg, sc, mn);
+    const float ds = d(un) * static_cast<float>(sc);
+    const float dm = f16_hi(un.hdr.x) * static_cast<float>(mn);
+    return fmaf(ds, nearest_code(dm, ds, 15.f), -dm);
   }
   __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
 };
 
 // Q5_K unit: one super-block - the header, the lane's 8 low-nibble bytes of
-// each run and its 8 fifth-bit bytes; chained like Q4_K with q * sc_j
-// (q <= 31) in the operand.
+// each run and its 8 fifth-bit bytes; chained like Q4_K with (q - c_j) *
+// sc_j (q <= 31) in the operand.
 struct WPolQ5_K {
   static constexpr int64_t kWideMinTiles = 256;
   static constexpr int kSumWidth = 32;
@@ -573,14 +569,16 @@ struct WPolQ5_K {
     const uint32_t hi = ((un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu) | (((un.h[1] >> j) & 0x01010101u) << 4);
     uint32_t sc, mn;
     k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, j, sc, mn);
-    const qhalf2 sv = half_pair(sc);
-    return scaled_codes(lo, hi, sv, sv * qhalf2{-1024, -1024});
+    const float c = nearest_code(f16_hi(un.hdr.x) * static_cast<float>(mn), d(un) * static_cast<float>(sc), 31.f);
+    return offset_codes(lo, hi, half_pair(sc), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
   }
   __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
   __device__ __forceinline__ static float neg_min(const Unit& un, int half, int kg) {
     uint32_t sc, mn;
     k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, 4 * half + kg, sc, mn);
-    return -f16_hi(un.hdr.x) * static_cast<float>(mn);
+    const float ds = d(un) * static_cast<float>(sc);
+    const float dm = f16_hi(un.hdr.x) * static_cast<float>(mn);
+    return fmaf(ds, nearest_code(dm, ds, 31.f), -dm);
   }
   __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
 };
@@ -638,8 +636,9 @@ struct WPolQ3_K {
 };
 
 // Q2_K unit: one super-block - the lane's code bytes of both halves, the 16
-// scale bytes and d, dmin; operand q * sc of the lane's sub-block; the 16
-// mins (one per 16 weights) take 16-weight sums of X, four per product.
+// scale bytes and d, dmin; operand (q - c) * sc of the lane's sub-block (c
+// its nearest_code); the 16 remainders d sc c - dmin m (one per 16 weights)
+// take 16-weight sums of X, four per product.
 struct WPolQ2_K {
   static constexpr int64_t kWideMinTiles = 256;
   static constexpr int kSumWidth = 16;
@@ -672,16 +671,27 @@ struct WPolQ2_K {
     const uint32_t lo = (un.q[h][0] >> (2 * jj)) & 0x03030303u;
     const uint32_t hi = (un.q[h][1] >> (2 * jj)) & 0x03030303u;
     const uint32_t k = static_cast<uint32_t>(8 * h + 2 * jj + (kg >> 1));
-    const qhalf2 sv = half_pair(scale_byte(un, k) & 15u);
-    return scaled_codes(lo, hi, sv, sv * qhalf2{-1024, -1024});
+    const uint32_t sb = scale_byte(un, k);
+    const float c = nearest_code(f16_hi(un.dd) * static_cast<float>(sb >> 4), d(un) * static_cast<float>(sb & 15u),
+                                 3.f);
+    return offset_codes(lo, hi, half_pair(sb & 15u), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
   }
   __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.dd); }
   // sub-block 4h + kg (16 weights each)
   __device__ __forceinline__ static float neg_min(const Unit& un, int h, int kg) {
-    return -f16_hi(un.dd) * static_cast<float>(scale_byte(un, static_cast<uint32_t>(4 * h + kg)) >> 4);
+    const uint32_t sb = scale_byte(un, static_cast<uint32_t>(4 * h + kg));
+    const float ds = d(un) * static_cast<float>(sb & 15u);
+    const float dm = f16_hi(un.dd) * static_cast<float>(sb >> 4);
+    return fmaf(ds, nearest_code(dm, ds, 3.f), -dm);
   }
   __device__ __forceinline__ static float scale(const Unit&, int, int) { return 0.f; }
 };
+
+// Formats whose k-step spans two sub-blocks with mins (Q2_K).
+template <class Q, class = void>
+struct HalfMins { static constexpr bool value = false; };
+template <class Q>
+struct HalfMins<Q, std::void_t<decltype(Q::kHalfMins)>> { static constexpr bool value = Q::kHalfMins; };
 
 template <class Q, int MT>
 struct QBuf {
@@ -747,11 +757,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
           const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, qfloat4{0.f, 0.f, 0.f, 0.f},
                                                                    0, 0, 0);
           acc[t] += ds * p;
-          if constexpr (Q::kMin) {
-            // the step's sum of x (ones), or x against the lanes' mins
-            qhalf8 mv = ones;
-            if constexpr (Q::kMinOperand) mv = Q::min_codes(b.w[c], kg);
-            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], mv,
+          if constexpr (HalfMins<Q>::value) {
+            // two sub-blocks per step: the sums of x over each 16-weight
+            // half, times the remainders of the column's two sub-blocks (a
+            // lane holds its own; the other half's lanes are 32 away)
+            const float dm_other = __shfl_xor(dm, 32, kWave);
+            const bool first = kg < 2;
+            const qhalf8 zeros = {0, 0, 0, 0, 0, 0, 0, 0};
+            const qfloat4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], first ? ones : zeros,
+                                                                      qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const qfloat4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], first ? zeros : ones,
+                                                                      qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            acc[t] -= (first ? dm : dm_other) * s0;
+            acc[t] -= (first ? dm_other : dm) * s1;
+          } else if constexpr (Q::kMin) {
+            // the step's sum of x (ones)
+            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
                                                                       qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             acc[t] -= dm * sx;
           }

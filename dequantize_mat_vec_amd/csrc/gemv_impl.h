@@ -84,8 +84,6 @@ __device__ __forceinline__ void nibbles_x512(uint32_t v, float& a, float& b, flo
 // ---------------------------------------------------------------------------
 struct FmtQ8_0x2 {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t w[17]; };
   struct Lane {};
@@ -105,8 +103,7 @@ struct FmtQ8_0x2 {
   // r[0..R-1]: the same unit of R rows; acc[k * B + b] is row k, column b.
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane&, float* acc) {
+                                                 const float* xs, const Lane&, float* acc) {
     float pa[R][B], pb[R][B];
 #pragma unroll
     for (int k = 0; k < R; ++k)
@@ -154,8 +151,6 @@ struct FmtQ8_0x2 {
 // ---------------------------------------------------------------------------
 struct FmtQ8_0 {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t w[9]; uint32_t s; };
   struct Lane {};
@@ -179,8 +174,7 @@ struct FmtQ8_0 {
   // start on alternating dword phases.
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane&, float* acc) {
+                                                 const float* xs, const Lane&, float* acc) {
     float part[R][B];
 #pragma unroll
     for (int k = 0; k < R; ++k)
@@ -220,8 +214,6 @@ struct FmtQ8_0 {
 // ---------------------------------------------------------------------------
 struct FmtQ4_K {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = true;
-  static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
   struct Raw { u32x4 hdr, qa, qb; };
   // Per lane (run g = sub % 4, sub-blocks 2g and 2g+1), byte selectors that
@@ -287,15 +279,24 @@ struct FmtQ4_K {
     dm1 = dmin * ubyte<3>(v);
   }
 
+  // Every weight is dequantized on its own, w = d sc q - dmin m with one
+  // rounding (the FMA of the exact d sc 2^9 and q 2^-9 against the exact
+  // dmin m: the weight's float32 value, bit for bit), and then multiplied
+  // into the sum.  Taking the two terms apart per sub-block (d sc sum q x -
+  // dmin m sum x) would cost one FMA less per weight, but when d sc q and
+  // dmin m nearly cancel the two large partial sums leave a rounding error
+  // that is not bounded by sum |w x|.
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float* sums, int64_t nsub,
-                                                 const Lane& L, float* acc) {
-    float p0[R][B], p1[R][B];
+                                                 const float* xs, const Lane& L, float* acc) {
+    float ds0[R], ds1[R], ndm0[R], ndm1[R];
 #pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { p0[k][b] = 0.f; p1[k][b] = 0.f; }
+    for (int k = 0; k < R; ++k) {
+      float dm0, dm1;
+      scales(r[k].hdr, L, ds0[k], ds1[k], dm0, dm1);
+      ndm0[k] = -dm0;
+      ndm1[k] = -dm1;
+    }
     const int x0 = 64 * u;   // first weight of the run (sub-block 2g)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -311,28 +312,18 @@ struct FmtQ4_K {
         float l0, l1, l2, l3, h0, h1, h2, h3;
         nibbles_x512(q & 0x0F0F0F0Fu, l0, l1, l2, l3);
         nibbles_x512((q >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);
+        l0 = fmaf(ds0[k], l0, ndm0[k]); l1 = fmaf(ds0[k], l1, ndm0[k]);
+        l2 = fmaf(ds0[k], l2, ndm0[k]); l3 = fmaf(ds0[k], l3, ndm0[k]);
+        h0 = fmaf(ds1[k], h0, ndm1[k]); h1 = fmaf(ds1[k], h1, ndm1[k]);
+        h2 = fmaf(ds1[k], h2, ndm1[k]); h3 = fmaf(ds1[k], h3, ndm1[k]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          p0[k][b] = fmaf(l0, xl[b].x, p0[k][b]); p0[k][b] = fmaf(l1, xl[b].y, p0[k][b]);
-          p0[k][b] = fmaf(l2, xl[b].z, p0[k][b]); p0[k][b] = fmaf(l3, xl[b].w, p0[k][b]);
-          p1[k][b] = fmaf(h0, xh[b].x, p1[k][b]); p1[k][b] = fmaf(h1, xh[b].y, p1[k][b]);
-          p1[k][b] = fmaf(h2, xh[b].z, p1[k][b]); p1[k][b] = fmaf(h3, xh[b].w, p1[k][b]);
+          float& s = acc[k * B + b];
+          s = fmaf(l0, xl[b].x, s); s = fmaf(l1, xl[b].y, s);
+          s = fmaf(l2, xl[b].z, s); s = fmaf(l3, xl[b].w, s);
+          s = fmaf(h0, xh[b].x, s); s = fmaf(h1, xh[b].y, s);
+          s = fmaf(h2, xh[b].z, s); s = fmaf(h3, xh[b].w, s);
         }
-      }
-    }
-    const int j0 = 2 * u;    // sub-block index of the row (32 weights each)
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      float ds0, ds1, dm0, dm1;
-      scales(r[k].hdr, L, ds0, ds1, dm0, dm1);
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float* sb_sums = sums + b * nsub;
-        float v = ds0 * p0[k][b];
-        v = fmaf(ds1, p1[k][b], v);
-        v = fmaf(-dm0, sb_sums[j0], v);
-        v = fmaf(-dm1, sb_sums[j0 + 1], v);
-        acc[k * B + b] += v;
       }
     }
   }
@@ -350,12 +341,9 @@ typedef uint32_t u32x4u2 __attribute__((ext_vector_type(4), aligned(2)));
 
 // Q2_K, 84-byte super-blocks: 16 scale bytes (4-bit scale, 4-bit min per
 // sub-block), 64 code bytes, d, dmin.  w = d*sc*q - dmin*m with q in 0..3:
-// the codes convert as e4m3 bytes (q * 2^-9, exact), the mins take the
-// staged 16-weight sums of x.
+// the codes convert as e4m3 bytes (q * 2^-9, exact).
 struct FmtQ2_K {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = true;
-  static constexpr int kSumWidth = 16;
   static constexpr int kPad = 256;
   struct Raw { u32x4 q; uint32_t sc0, sc1, dd; };
   struct Lane { uint32_t h, c; };
@@ -373,19 +361,24 @@ struct FmtQ2_K {
     r.dd = load_u32(sbp + 80);           // d | dmin << 16
   }
 
+  // Each weight dequantized on its own (see FmtQ4_K::compute): the 2-bit
+  // code converts as q 2^-9, and w = (d sc 2^9) (q 2^-9) - dmin m is one
+  // rounding of the exact value.
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float* sums, int64_t nsub,
-                                                 const Lane& L, float* acc) {
+                                                 const float* xs, const Lane& L, float* acc) {
     const int x0 = 256 * (u >> 2) + 128 * static_cast<int>(L.h) + 16 * static_cast<int>(L.c);
-    const int s0 = 16 * (u >> 2) + 8 * static_cast<int>(L.h) + static_cast<int>(L.c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float p[R][B];
+      // scale byte of sub-block 8h + 2j + c: byte 2j + c of the lane's eight
+      float ds[R], ndm[R];
 #pragma unroll
-      for (int k = 0; k < R; ++k)
-#pragma unroll
-        for (int b = 0; b < B; ++b) p[k][b] = 0.f;
+      for (int k = 0; k < R; ++k) {
+        const uint32_t word = j < 2 ? r[k].sc0 : r[k].sc1;
+        const uint32_t sbyte_v = (word >> (8 * (2 * (j & 1) + L.c))) & 0xFFu;
+        ds[k] = f16_lo(r[k].dd) * 512.0f * static_cast<float>(sbyte_v & 15u);
+        ndm[k] = -(f16_hi(r[k].dd) * static_cast<float>(sbyte_v >> 4));
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         f32x4 xv[B];
@@ -396,25 +389,14 @@ struct FmtQ2_K {
           const uint32_t w = t == 0 ? r[k].q.x : (t == 1 ? r[k].q.y : (t == 2 ? r[k].q.z : r[k].q.w));
           float q0, q1, q2, q3;
           nibbles_x512((w >> (2 * j)) & 0x03030303u, q0, q1, q2, q3);
+          q0 = fmaf(ds[k], q0, ndm[k]); q1 = fmaf(ds[k], q1, ndm[k]);
+          q2 = fmaf(ds[k], q2, ndm[k]); q3 = fmaf(ds[k], q3, ndm[k]);
 #pragma unroll
           for (int b = 0; b < B; ++b) {
-            p[k][b] = fmaf(q0, xv[b].x, p[k][b]); p[k][b] = fmaf(q1, xv[b].y, p[k][b]);
-            p[k][b] = fmaf(q2, xv[b].z, p[k][b]); p[k][b] = fmaf(q3, xv[b].w, p[k][b]);
+            float& s = acc[k * B + b];
+            s = fmaf(q0, xv[b].x, s); s = fmaf(q1, xv[b].y, s);
+            s = fmaf(q2, xv[b].z, s); s = fmaf(q3, xv[b].w, s);
           }
-        }
-      }
-      // scale byte of sub-block 8h + 2j + c: byte 2j + c of the lane's eight
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const uint32_t word = j < 2 ? r[k].sc0 : r[k].sc1;
-        const uint32_t sbyte_v = (word >> (8 * (2 * (j & 1) + L.c))) & 0xFFu;
-        const float ds = f16_lo(r[k].dd) * 512.0f * static_cast<float>(sbyte_v & 15u);
-        const float dm = f16_hi(r[k].dd) * static_cast<float>(sbyte_v >> 4);
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float v = ds * p[k][b];
-          v = fmaf(-dm, sums[b * nsub + s0 + 2 * j], v);
-          acc[k * B + b] += v;
         }
       }
     }
@@ -431,8 +413,6 @@ struct FmtQ2_K {
 // 8 + k % 4; w = d * (scale - 32) * q.
 struct FmtQ3_K {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 256;
   struct Raw { u32x4 q, hm; uint32_t s0, s1, s2, d; };
   using Lane = FmtQ2_K::Lane;
@@ -455,8 +435,7 @@ struct FmtQ3_K {
 
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane& L, float* acc) {
+                                                 const float* xs, const Lane& L, float* acc) {
     const int x0 = 256 * (u >> 2) + 128 * static_cast<int>(L.h) + 16 * static_cast<int>(L.c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -511,8 +490,6 @@ struct FmtQ3_K {
 // ---------------------------------------------------------------------------
 struct FmtQ5_K {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = true;
-  static constexpr int kSumWidth = 32;   // weights per staged sum of x
   static constexpr int kPad = 256;
   struct Raw { u32x4 hdr, ha, hb, qa, qb; };
   using Lane = FmtQ4_K::Lane;
@@ -554,15 +531,20 @@ struct FmtQ5_K {
     }
   }
 
+  // Each weight dequantized on its own (see FmtQ4_K::compute).
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float* sums, int64_t nsub,
-                                                 const Lane& L, float* acc) {
-    float p0[R][B], p1[R][B];
+                                                 const float* xs, const Lane& L, float* acc) {
+    float ds0[R], ds1[R], ndm0[R], ndm1[R];
 #pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { p0[k][b] = 0.f; p1[k][b] = 0.f; }
+    for (int k = 0; k < R; ++k) {
+      float dm0, dm1;
+      FmtQ4_K::scales(r[k].hdr, L, ds0[k], ds1[k], dm0, dm1);   // d*sc*2^9: Q4_K's codes carry 2^-9
+      ds0[k] *= 1.0f / 512.0f;
+      ds1[k] *= 1.0f / 512.0f;
+      ndm0[k] = -dm0;
+      ndm1[k] = -dm1;
+    }
     const int x0 = 64 * u;
     const uint32_t g2 = 2u * static_cast<uint32_t>(u & 3);   // fifth-bit position of the first half
 #pragma unroll
@@ -579,32 +561,18 @@ struct FmtQ5_K {
         const uint32_t hq = high_word(r[k], t);
         const uint32_t lo = (q & 0x0F0F0F0Fu) | (((hq >> g2) & 0x01010101u) << 4);
         const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (((hq >> (g2 + 1u)) & 0x01010101u) << 4);
-        const float l0 = ubyte<0>(lo), l1 = ubyte<1>(lo), l2 = ubyte<2>(lo), l3 = ubyte<3>(lo);
-        const float h0 = ubyte<0>(hi), h1 = ubyte<1>(hi), h2 = ubyte<2>(hi), h3 = ubyte<3>(hi);
+        const float l0 = fmaf(ds0[k], ubyte<0>(lo), ndm0[k]), l1 = fmaf(ds0[k], ubyte<1>(lo), ndm0[k]);
+        const float l2 = fmaf(ds0[k], ubyte<2>(lo), ndm0[k]), l3 = fmaf(ds0[k], ubyte<3>(lo), ndm0[k]);
+        const float h0 = fmaf(ds1[k], ubyte<0>(hi), ndm1[k]), h1 = fmaf(ds1[k], ubyte<1>(hi), ndm1[k]);
+        const float h2 = fmaf(ds1[k], ubyte<2>(hi), ndm1[k]), h3 = fmaf(ds1[k], ubyte<3>(hi), ndm1[k]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          p0[k][b] = fmaf(l0, xl[b].x, p0[k][b]); p0[k][b] = fmaf(l1, xl[b].y, p0[k][b]);
-          p0[k][b] = fmaf(l2, xl[b].z, p0[k][b]); p0[k][b] = fmaf(l3, xl[b].w, p0[k][b]);
-          p1[k][b] = fmaf(h0, xh[b].x, p1[k][b]); p1[k][b] = fmaf(h1, xh[b].y, p1[k][b]);
-          p1[k][b] = fmaf(h2, xh[b].z, p1[k][b]); p1[k][b] = fmaf(h3, xh[b].w, p1[k][b]);
+          float& s = acc[k * B + b];
+          s = fmaf(l0, xl[b].x, s); s = fmaf(l1, xl[b].y, s);
+          s = fmaf(l2, xl[b].z, s); s = fmaf(l3, xl[b].w, s);
+          s = fmaf(h0, xh[b].x, s); s = fmaf(h1, xh[b].y, s);
+          s = fmaf(h2, xh[b].z, s); s = fmaf(h3, xh[b].w, s);
         }
-      }
-    }
-    const int j0 = 2 * u;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      float ds0, ds1, dm0, dm1;
-      FmtQ4_K::scales(r[k].hdr, L, ds0, ds1, dm0, dm1);   // d*sc*2^9: Q4_K's codes carry 2^-9
-      ds0 *= 1.0f / 512.0f;
-      ds1 *= 1.0f / 512.0f;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float* sb_sums = sums + b * nsub;
-        float v = ds0 * p0[k][b];
-        v = fmaf(ds1, p1[k][b], v);
-        v = fmaf(-dm0, sb_sums[j0], v);
-        v = fmaf(-dm1, sb_sums[j0 + 1], v);
-        acc[k * B + b] += v;
       }
     }
   }
@@ -620,8 +588,6 @@ struct FmtQ5_K {
 // ---------------------------------------------------------------------------
 struct FmtQ6_K {
   static constexpr bool kRowScales = false;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 256;
   // Three 20-byte windows (low parts of g = 0/2, of g = 1/3, high parts),
   // three dwords around the unit's scales, and d.
@@ -661,8 +627,7 @@ struct FmtQ6_K {
 
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane&, float* acc) {
+                                                 const float* xs, const Lane&, float* acc) {
     const int h = static_cast<int>((u >> 1) & 1);
     const int c = static_cast<int>(u & 1);
     float p[R][4][B];
@@ -731,8 +696,6 @@ struct FmtQ6_K {
 // ---------------------------------------------------------------------------
 struct FmtI8Row {
   static constexpr bool kRowScales = true;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   struct Raw { uint32_t q[16]; };
   struct Lane {};
@@ -757,8 +720,7 @@ struct FmtI8Row {
 
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane&, float* acc) {
+                                                 const float* xs, const Lane&, float* acc) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       f32x4 xv[B];
@@ -793,8 +755,6 @@ struct FmtI8Row {
 // ---------------------------------------------------------------------------
 struct FmtI4Row {
   static constexpr bool kRowScales = true;
-  static constexpr bool kSums = false;
-  static constexpr int kSumWidth = 32;
   static constexpr int kPad = 64;
   static constexpr float kAccScale = 0.0625f;
   struct Raw { u32x4 a, b; };
@@ -823,8 +783,7 @@ struct FmtI4Row {
 
   template <int B, int R>
   __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
-                                                 const float* xs, const float*, int64_t,
-                                                 const Lane&, float* acc) {
+                                                 const float* xs, const Lane&, float* acc) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       f32x4 xa[B], xb[B];
@@ -872,12 +831,10 @@ __device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp,
 }
 
 // ---------------------------------------------------------------------------
-// Staging: x into LDS (padded layout, zero past `in`), and for Q4_K the sum
-// of every 32 consecutive x next to it.  A thread holds XS float4 at a time,
-// all loaded before any is stored, so x costs one memory round trip per
-// XS * kThreads float4 (XS = 1, 2 or 8 for rows of up to 1024, 2048 or 8192
-// weights).  The per-32 sums reduce the 8 float4 of a sub-block, held by 8
-// consecutive lanes, with DPP.  One barrier follows.
+// Staging: x into LDS (padded layout, zero past `in`).  A thread holds XS
+// float4 at a time, all loaded before any is stored, so x costs one memory
+// round trip per XS * kThreads float4 (XS = 1, 2 or 8 for rows of up to
+// 1024, 2048 or 8192 weights).  One barrier follows.
 // ---------------------------------------------------------------------------
 template <int B, int XS>
 struct XChunk {
@@ -902,13 +859,10 @@ __device__ __forceinline__ void stage_load(const GemvArgs& a, int base, XChunk<B
   }
 }
 
-template <bool kSums, int SW, int B, int XS>
-__device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float* sums, int base,
-                                            const XChunk<B, XS>& c) {
-  static_assert(SW == 16 || SW == 32, "sums over 16 or 32 weights");
+template <int B, int XS>
+__device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, int base, const XChunk<B, XS>& c) {
   const int n4 = static_cast<int>(a.xpad >> 2);   // float4 slots per batch row
   const int in4 = static_cast<int>(a.in >> 2);
-  const int nsub = static_cast<int>(a.xpad / SW);
   const int tid = static_cast<int>(threadIdx.x);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
@@ -918,21 +872,14 @@ __device__ __forceinline__ void stage_store(const GemvArgs& a, float* xs, float*
       const int s = base + r * kThreads + tid;
       const f32x4 v = s < in4 ? c.v[b][r] : f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < n4) *reinterpret_cast<f32x4*>(dst + xs_phys(4 * s)) = v;
-      if constexpr (kSums) {
-        float part = (v.x + v.y) + (v.z + v.w);
-        part += dpp<0xB1>(part);    // lane ^ 1
-        part += dpp<0x4E>(part);    // lane ^ 2
-        if constexpr (SW == 32) part += dpp<0x141>(part);   // lane i <-> 7 - i within 8
-        if ((tid & (SW / 4 - 1)) == 0 && s < n4) sums[b * nsub + s / (SW / 4)] = part;
-      }
     }
   }
 }
 
 // Chunks after the first (rows longer than 1024, 2048 or 8192 weights for
 // XS = 1, 2, 8), one batch column at a time.
-template <bool kSums, int SW, int B, int XS>
-__device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* sums, int from) {
+template <int B, int XS>
+__device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, int from) {
   const int n4 = static_cast<int>(a.xpad >> 2);
   for (int base = from; base < n4; base += XS * kThreads) {
 #pragma unroll
@@ -941,7 +888,7 @@ __device__ __forceinline__ void stage_rest(const GemvArgs& a, float* xs, float* 
       ab.x = a.x + b * a.in;
       XChunk<1, XS> c;
       stage_load<1, XS>(ab, base, c);
-      stage_store<kSums, SW, 1, XS>(ab, xs + b * a.xstride, sums + b * (a.xpad / SW), base, c);
+      stage_store<1, XS>(ab, xs + b * a.xstride, base, c);
     }
   }
 }
@@ -1012,8 +959,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   const int64_t first = tile * kRowsPerTile;
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
   float* xs = lds;
-  float* sums = lds + B * a.xstride;
-  const int64_t nsub = a.xpad / F::kSumWidth;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -1107,22 +1052,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     issue_unit<F>(a, rp[0], unit(1), rb[0]);
   }
   epilogue_loads();
-  if constexpr (kEarly) stage_store<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, 0, xc);
-  stage_rest<F::kSums, F::kSumWidth, B, XS>(a, xs, sums, kEarly ? XS * kThreads : 0);
+  if constexpr (kEarly) stage_store<B, XS>(a, xs, 0, xc);
+  stage_rest<B, XS>(a, xs, kEarly ? XS * kThreads : 0);
   __syncthreads();
   if (at_once) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
-      if (have[j]) F::template compute<B, R>(a, r[j], sub + L * j, xs, sums, nsub, ls, acc);
+      if (have[j]) F::template compute<B, R>(a, r[j], sub + L * j, xs, ls, acc);
   } else if constexpr (kWalk) {
     // Two units in flight: unit j + 2 is requested as soon as unit j's
     // registers are free.  Requests past the last unit read unit 0 (in
     // bounds, unused), which keeps the loop branch-free.
     for (int j = 0; j < ipt; j += 2) {
-      if (live(j)) F::template compute<B, 1>(a, r[0], sub + L * j, xs, sums, nsub, ls, acc);
+      if (live(j)) F::template compute<B, 1>(a, r[0], sub + L * j, xs, ls, acc);
       if (j + 1 >= ipt) break;
       issue_unit<F>(a, rp[0], unit(j + 2), r[0][0]);
-      if (live(j + 1)) F::template compute<B, 1>(a, rb, sub + L * (j + 1), xs, sums, nsub, ls, acc);
+      if (live(j + 1)) F::template compute<B, 1>(a, rb, sub + L * (j + 1), xs, ls, acc);
       issue_unit<F>(a, rp[0], unit(j + 3), rb[0]);
     }
   }
@@ -1418,7 +1363,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     const int64_t pad = F::kPad;
     a.xpad = ((a.in + pad - 1) / pad) * pad;
     a.xstride = pesti::xs_stride(a.in, pad);
-    const size_t r = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / F::kSumWidth : 0));
+    const size_t r = sizeof(float) * a.xstride;
     if (r > row_lds) row_lds = r;
     if (a.units > max_units) max_units = a.units;
     if (a.out > max_out) max_out = a.out;
@@ -1583,7 +1528,7 @@ int swiglu_dispatch(int64_t out_features, int64_t in_features, const void* w_gat
   const int64_t pad = F::kPad;
   a.xpad = ((a.in + pad - 1) / pad) * pad;
   a.xstride = pesti::xs_stride(a.in, pad);
-  const size_t row_lds = sizeof(float) * (a.xstride + (F::kSums ? a.xpad / F::kSumWidth : 0));
+  const size_t row_lds = sizeof(float) * a.xstride;
   const int per_launch = pesti_host::batch_per_launch(lds_limit, row_lds, 0, batch);
   if (per_launch < 1) return PESTI_ERR_SHAPE;
   for (int b0 = 0; b0 < batch; b0 += per_launch) {

@@ -19,17 +19,19 @@
 // points choose this kernel from batch 3 (Q2_K, Q3_K, Q4_K, Q5_K), 4 (Q8_0
 // rows of an even block count), 5 (Q6_K) and 2 (per-row INT4), below which
 // the vector-ALU kernel is faster.  One v_mfma_f32_16x16x32_f16 k-step is one sub-block of 16
-// rows: the B operand is the rows' 4-bit codes (a nibble read as an e4m3
-// byte is q * 2^-9, which v_cvt_scalef32_pk_f16_fp8 turns into binary16
-// exactly), the A operand is x in binary16.  binary16 cannot hold float32
+// rows: the B operand is the rows' 4-bit codes less the sub-block's
+// nearest_code c (a nibble read as an e4m3 byte is q * 2^-9, which
+// v_cvt_scalef32_pk_f16_fp8 turns into binary16 exactly; subtracting
+// c 2^-9 is exact too), the A operand is x in binary16.  binary16 cannot hold float32
 // x, so x is split: each 32-weight block of x is scaled by a power of two
 // 2^e (its largest magnitude lands in [2^14, 2^15)), then xs = hi + lo with
 // hi = f16(xs), lo = f16(xs - hi); hi and lo of batch column b are rows 2b
 // and 2b + 1 of A, so batches up to 8 share one instruction.  Every
 // product q * hi, q * lo is exact in the float32 accumulator; the split
 // loses at most 2^-22 |xs| + 2^-25 per element.  Per k-step and row:
-//   acc_b += (d sc 2^9 2^-e) (C[2b] + C[2b+1]) - (dmin m) sum(x block)
-// with the block sums of x computed in float32 while staging.
+//   acc_b += (d sc 2^9 2^-e) (C[2b] + C[2b+1]) + (d sc c - dmin m) sum(x block)
+// with the block sums of x computed in float32 while staging; the second
+// term is exactly 0 for a sub-block whose weights are all 0.
 //
 // Layout (MFMA operand layout, lane l: n = l % 16, kg = l / 16): A = row n
 // of the staged x operand, k = 8kg..8kg+7; B = W row n of the wave's 16-row
@@ -43,6 +45,7 @@
 namespace pesti {
 
 typedef _Float16 mhalf8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mhalf2 __attribute__((ext_vector_type(2)));
 typedef float mfloat4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(8)));
 
@@ -76,33 +79,44 @@ __device__ __forceinline__ void q4k_scale_min(const u32x4& h, uint32_t& sc, uint
   }
 }
 
+// Packed binary16 pair (v, v) of a float32 value exact in binary16.
+__device__ __forceinline__ uint32_t f16_pair(float v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v, v));
+}
+
 // One k-step of the tile: the lane's 8 codes of sub-block J (packed
 // nibbles c), its x operand, and the scaled update of its two batch sums
-// ((2^-e, block sum of x) per column).
+// ((2^-e, block sum of x) per column).  The codes enter as (q - c) 2^-9,
+// c = nearest_code of the sub-block: a binary16 subtraction of exact
+// values.
 template <int B, int J>
-__device__ __forceinline__ void q4k_step(const u32x2& c, const u32x4& hdr, float d512, float dmin,
+__device__ __forceinline__ void q4k_step(const u32x2& c, const u32x4& hdr, float d, float dmin,
                                          const uint8_t* xop, const f32x2& e0, const f32x2& e1, float& acc0,
                                          float& acc1) {
   constexpr uint32_t sh = 4u * (J & 1);
+  uint32_t sc, m;
+  q4k_scale_min<J>(hdr, sc, m);
+  const float ds = d * static_cast<float>(sc);
+  const float dm = dmin * static_cast<float>(m);
+  const float cq = nearest_code(dm, ds, 15.f);
+  const mhalf2 off = __builtin_bit_cast(mhalf2, f16_pair(cq * (1.0f / 512.0f)));
   const uint32_t qa = (c.x >> sh) & 0x0F0F0F0Fu;
   const uint32_t qb = (c.y >> sh) & 0x0F0F0F0Fu;
-  uint32_t h[4];
-  h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, false));
-  h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, true));
-  h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, false));
-  h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, true));
+  mhalf2 h[4];
+  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, false) - off;
+  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, true) - off;
+  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, false) - off;
+  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, true) - off;
   const mhalf8 wv = __builtin_bit_cast(mhalf8, h);
   const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xop);
   const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-  uint32_t sc, m;
-  q4k_scale_min<J>(hdr, sc, m);
-  const float ds = d512 * static_cast<float>(sc);
-  const float dm = dmin * static_cast<float>(m);
-  acc0 = fmaf(ds * e0.x, p[0] + p[1], acc0);
-  acc0 = fmaf(-dm, e0.y, acc0);
+  const float ds512 = ds * 512.0f;
+  const float rest = fmaf(ds, cq, -dm);   // ds c - dm, exactly 0 when the sub-block cancels
+  acc0 = fmaf(ds512 * e0.x, p[0] + p[1], acc0);
+  acc0 = fmaf(rest, e0.y, acc0);
   if constexpr (B > 1) {
-    acc1 = fmaf(ds * e1.x, p[2] + p[3], acc1);
-    acc1 = fmaf(-dm, e1.y, acc1);
+    acc1 = fmaf(ds512 * e1.x, p[2] + p[3], acc1);
+    acc1 = fmaf(rest, e1.y, acc1);
   }
 }
 
@@ -137,13 +151,13 @@ struct MfmaQ4K {
                                              float& acc0, float& acc1) {
 #pragma unroll
     for (int S = 0; S < NSB; ++S) {
-      const float d512 = f16_lo(w.hdr[S].x) * 512.0f;
+      const float d = f16_lo(w.hdr[S].x);
       const float dmin = f16_hi(w.hdr[S].x);
       const int s0 = 8 * S;
       // A whole super-block runs its 8 steps as straight-line code (they
       // overlap); the padded last one tests each step (uniform).
 #define PESTI_Q4K_STEP(J)                                                                          \
-        q4k_step<B, J>(w.cw[S][J / 2], w.hdr[S], d512, dmin, xa + (s0 + J) * xsa, es0[s0 + J],     \
+        q4k_step<B, J>(w.cw[S][J / 2], w.hdr[S], d, dmin, xa + (s0 + J) * xsa, es0[s0 + J],        \
                        es1[s0 + J], acc0, acc1);
       if (s0 + 8 <= nsteps) {
         PESTI_Q4K_STEP(0) PESTI_Q4K_STEP(1) PESTI_Q4K_STEP(2) PESTI_Q4K_STEP(3)
@@ -172,7 +186,6 @@ struct MfmaQ4K {
 // boundary every other one; their pieces are read with 2-byte-aligned
 // loads.
 typedef uint32_t u32x2u2 __attribute__((ext_vector_type(2), aligned(2)));
-typedef _Float16 mhalf2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t q6k_pair(uint32_t q, uint32_t sel) {
   // bytes [q_i, 0x64, q_j, 0x64]: binary16 1024 + q_i, 1024 + q_j; minus 1056
@@ -286,37 +299,41 @@ struct MfmaQ5K {
         w.qs[S][gi] = *reinterpret_cast<const u32x2*>(sb + 48 + 32 * gi + 8 * kg);
     }
   }
-  __device__ __forceinline__ static uint32_t pair(uint32_t q, uint32_t sel) {
-    // bytes [q_i, 0x64, q_j, 0x64]: binary16 1024 + q_i, 1024 + q_j; minus 1024
+  __device__ __forceinline__ static uint32_t pair(uint32_t q, uint32_t sel, mhalf2 off) {
+    // bytes [q_i, 0x64, q_j, 0x64]: binary16 1024 + q_i, 1024 + q_j; minus
+    // 1024 + c
     const uint32_t v = __builtin_amdgcn_perm(0x64646464u, q, sel);
-    const mhalf2 h = __builtin_bit_cast(mhalf2, v) + mhalf2{static_cast<_Float16>(-1024.0f),
-                                                            static_cast<_Float16>(-1024.0f)};
-    return __builtin_bit_cast(uint32_t, h);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mhalf2, v) - off);
   }
+  // The codes enter as q - c (c = nearest_code of the sub-block, see
+  // q4k_step).
   template <int B, int J>
   __device__ __forceinline__ static void step(const u32x2& lo, const u32x2& hb, const u32x4& hdr, float d,
                                               float dmin, const uint8_t* xa, const f32x2& e0, const f32x2& e1,
                                               float& acc0, float& acc1) {
-    constexpr uint32_t sh = 4u * (J & 1);
-    const uint32_t q0 = ((lo.x >> sh) & 0x0F0F0F0Fu) | (((hb.x >> J) & 0x01010101u) << 4);
-    const uint32_t q1 = ((lo.y >> sh) & 0x0F0F0F0Fu) | (((hb.y >> J) & 0x01010101u) << 4);
-    uint32_t hw[4];
-    hw[0] = pair(q0, 0x04010400u);
-    hw[1] = pair(q0, 0x04030402u);
-    hw[2] = pair(q1, 0x04010400u);
-    hw[3] = pair(q1, 0x04030402u);
-    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
-    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xa);
-    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     uint32_t sc, m;
     q4k_scale_min<J>(hdr, sc, m);
     const float ds = d * static_cast<float>(sc);
     const float dm = dmin * static_cast<float>(m);
+    const float cq = nearest_code(dm, ds, 31.f);
+    const mhalf2 off = __builtin_bit_cast(mhalf2, f16_pair(1024.0f + cq));
+    constexpr uint32_t sh = 4u * (J & 1);
+    const uint32_t q0 = ((lo.x >> sh) & 0x0F0F0F0Fu) | (((hb.x >> J) & 0x01010101u) << 4);
+    const uint32_t q1 = ((lo.y >> sh) & 0x0F0F0F0Fu) | (((hb.y >> J) & 0x01010101u) << 4);
+    uint32_t hw[4];
+    hw[0] = pair(q0, 0x04010400u, off);
+    hw[1] = pair(q0, 0x04030402u, off);
+    hw[2] = pair(q1, 0x04010400u, off);
+    hw[3] = pair(q1, 0x04030402u, off);
+    const mhalf8 wv = __builtin_bit_cast(mhalf8, hw);
+    const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xa);
+    const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const float rest = fmaf(ds, cq, -dm);
     acc0 = fmaf(ds * e0.x, p[0] + p[1], acc0);
-    acc0 = fmaf(-dm, e0.y, acc0);
+    acc0 = fmaf(rest, e0.y, acc0);
     if constexpr (B > 1) {
       acc1 = fmaf(ds * e1.x, p[2] + p[3], acc1);
-      acc1 = fmaf(-dm, e1.y, acc1);
+      acc1 = fmaf(rest, e1.y, acc1);
     }
   }
   template <int B, int NSB>
@@ -422,15 +439,18 @@ struct MfmaI4 {
 // 16-weight sub-block; 64 code bytes; d; dmin).  k-step s = 8S + 4h + j
 // covers weights 128h + 32j + l, l = 0..31, of super-block S, whose 2-bit
 // codes sit at bits 2j of code byte 32h + l; lane kg's weights l = 8kg..+7
-// belong to sub-block 8h + 2j + kg / 2.  The sub-block scale is folded into
-// the B operand (sc q 2^-9, built by one binary16 multiply, is exact: sc q
-// <= 45), so one product covers both sub-blocks of the step; a second
-// product against the same x operand with B = the lanes' sub-block mins
-// gives 2^e sum(m x).  Per step: acc += 2^-e (d 2^9 C - dmin C_min).
+// belong to sub-block 8h + 2j + kg / 2.  The codes enter as sc (q - c)
+// 2^-9 with c the lane's sub-block's nearest_code (one binary16 FMA, exact:
+// |sc (q - c)| <= 45), so one product covers both sub-blocks of the step;
+// the two sub-blocks' remainders ds c - dm (exactly 0 where a sub-block's
+// weights all are) multiply the staged sums of x over each 16-weight half
+// of the block, the other half's remainder coming from the lane 32 away
+// (kg ^ 2).  Per step: acc += 2^-e d 2^9 C + r_lo sum_lo + r_hi sum_hi.
 typedef uint32_t u32x2w __attribute__((ext_vector_type(2), aligned(4)));
 
 struct MfmaQ2K {
   static constexpr int kBytes = 84;
+  static constexpr bool kHalfSums = true;
   template <int NSB>
   struct Tile {
     u32x4 sc[NSB];       // the 16 scale bytes
@@ -451,42 +471,53 @@ struct MfmaQ2K {
     w.sh = 8u * static_cast<uint32_t>(kg >> 1);
   }
   template <int B, int J>
-  __device__ __forceinline__ static void step(const u32x2w& c, uint32_t word, uint32_t sh, float d512,
+  __device__ __forceinline__ static void step(const u32x2w& c, uint32_t word, uint32_t sh, float d512, float d,
                                               float dmin, const uint8_t* xop, const f32x2& e0,
-                                              const f32x2& e1, float& acc0, float& acc1) {
+                                              const f32x2& e1, const f32x2& hs0, const f32x2& hs1,
+                                              float& acc0, float& acc1) {
     const uint32_t qa = (c.x >> (2 * J)) & 0x03030303u;
     const uint32_t qb = (c.y >> (2 * J)) & 0x03030303u;
     // scale bytes of sub-blocks 8h + 2j (low) and 8h + 2j + 1 (high)
     const uint32_t pair = word >> (16 * (J & 1));
-    const _Float16 sc = static_cast<_Float16>(static_cast<float>((pair >> sh) & 15u));
-    const _Float16 mn = static_cast<_Float16>(static_cast<float>((pair >> (sh + 4)) & 15u));
-    const mhalf2 s2{sc, sc};
+    const float scf = static_cast<float>((pair >> sh) & 15u);
+    const float ds = d * scf;
+    const float dm = dmin * static_cast<float>((pair >> (sh + 4)) & 15u);
+    const float cq = nearest_code(dm, ds, 3.f);
+    const mhalf2 s2 = __builtin_bit_cast(mhalf2, f16_pair(scf));
+    const mhalf2 o2 = __builtin_bit_cast(mhalf2, f16_pair(-scf * cq * (1.0f / 512.0f)));
     mhalf2 h[4];
-    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, false) * s2;
-    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, true) * s2;
-    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, false) * s2;
-    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, true) * s2;
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, false) * s2 + o2;
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qa, 1.0f, true) * s2 + o2;
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, false) * s2 + o2;
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(qb, 1.0f, true) * s2 + o2;
     const mhalf8 wv = __builtin_bit_cast(mhalf8, h);
-    const mhalf8 mv{mn, mn, mn, mn, mn, mn, mn, mn};
     const mhalf8 xv = *reinterpret_cast<const mhalf8*>(xop);
     const mfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    const mfloat4 pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, mv, mfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    acc0 = fmaf(e0.x, fmaf(d512, p[0] + p[1], -dmin * (pm[0] + pm[1])), acc0);
-    if constexpr (B > 1) acc1 = fmaf(e1.x, fmaf(d512, p[2] + p[3], -dmin * (pm[2] + pm[3])), acc1);
+    const float rest = fmaf(ds, cq, -dm);
+    const float other = __shfl_xor(rest, 32, kWave);
+    const bool low = sh == 0u;   // lanes kg < 2 hold the step's first sub-block
+    const float r_lo = low ? rest : other, r_hi = low ? other : rest;
+    acc0 = fmaf(e0.x * d512, p[0] + p[1], acc0);
+    acc0 = fmaf(r_lo, hs0.x, fmaf(r_hi, hs0.y, acc0));
+    if constexpr (B > 1) {
+      acc1 = fmaf(e1.x * d512, p[2] + p[3], acc1);
+      acc1 = fmaf(r_lo, hs1.x, fmaf(r_hi, hs1.y, acc1));
+    }
   }
   template <int B, int NSB>
   __device__ __forceinline__ static void run(const Tile<NSB>& w, int nsteps, const uint8_t* xa, int xsa,
                                              const uint8_t*, int, const f32x2* es0, const f32x2* es1,
-                                             float& acc0, float& acc1) {
+                                             const f32x2* hs0, const f32x2* hs1, float& acc0, float& acc1) {
 #pragma unroll
     for (int S = 0; S < NSB; ++S) {
-      const float d512 = f16_lo(w.dd[S]) * 512.0f;
+      const float d = f16_lo(w.dd[S]);
+      const float d512 = d * 512.0f;
       const float dmin = f16_hi(w.dd[S]);
       const int s0 = 8 * S;
 #define PESTI_Q2K_STEP(H, J)                                                                       \
       step<B, J>(w.q[S][H], H == 0 ? (J < 2 ? w.sc[S].x : w.sc[S].y) : (J < 2 ? w.sc[S].z : w.sc[S].w), \
-                 w.sh, d512, dmin, xa + (s0 + 4 * H + J) * xsa, es0[s0 + 4 * H + J], es1[s0 + 4 * H + J], \
-                 acc0, acc1);
+                 w.sh, d512, d, dmin, xa + (s0 + 4 * H + J) * xsa, es0[s0 + 4 * H + J], es1[s0 + 4 * H + J], \
+                 hs0[s0 + 4 * H + J], hs1[s0 + 4 * H + J], acc0, acc1);
       if (s0 + 8 <= nsteps) {
         PESTI_Q2K_STEP(0, 0) PESTI_Q2K_STEP(0, 1) PESTI_Q2K_STEP(0, 2) PESTI_Q2K_STEP(0, 3)
         PESTI_Q2K_STEP(1, 0) PESTI_Q2K_STEP(1, 1) PESTI_Q2K_STEP(1, 2) PESTI_Q2K_STEP(1, 3)
@@ -664,6 +695,14 @@ struct MfmaQ8 {
   }
 };
 
+// Formats that take the sums of x over each 16-weight half of a block.
+template <class P, class = void>
+struct HalfSums { static constexpr bool value = false; };
+template <class P>
+struct HalfSums<P, std::void_t<decltype(P::kHalfSums)>> { static constexpr bool value = P::kHalfSums; };
+template <class P>
+constexpr bool kHalfSumsOf = HalfSums<P>::value;
+
 // Formats whose x is staged in 128-weight groups (see MfmaI4) and whose
 // rows carry a float32 scale.
 template <class P>
@@ -738,6 +777,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   const int op_bytes = nsteps * 2 * B * 64;
   uint8_t* zero_row = base + op_bytes;
   f32x2* xsc = reinterpret_cast<f32x2*>(base + op_bytes + 64);
+  f32x2* hsc = xsc + B * nsteps;   // per-16 sums of x (formats with 16-weight sub-blocks)
   if (tid < 16) reinterpret_cast<float*>(zero_row)[tid] = 0.f;
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -755,8 +795,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
     // the block's 4 quarters sit in 4 consecutive lanes
     mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
-    sm += __shfl_xor(sm, 1, kWave);
-    sm += __shfl_xor(sm, 2, kWave);
+    sm += __shfl_xor(sm, 1, kWave);   // the sum of the lane's 16-weight half
+    const float other_half = __shfl_xor(sm, 2, kWave);
+    const f32x2 halves{sm, other_half};   // (first, second) in quarter 0's lane
+    sm += other_half;
     int e = 0;
     if (mx > 0.f) {
       int E;
@@ -783,7 +825,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
       uint8_t* dst = base + (s * 2 * B + 2 * b) * 64 + 16 * q;
       *reinterpret_cast<u32x4a*>(dst) = u32x4a{hi[0], hi[1], hi[2], hi[3]};
       *reinterpret_cast<u32x4a*>(dst + 64) = u32x4a{lo[0], lo[1], lo[2], lo[3]};
-      if (q == 0) xsc[b * nsteps + s] = f32x2{ldexpf(1.0f, -e), sm};
+      if (q == 0) {
+        xsc[b * nsteps + s] = f32x2{ldexpf(1.0f, -e), sm};
+        if constexpr (kHalfSumsOf<P>) hsc[b * nsteps + s] = halves;
+      }
     }
   }
   __syncthreads();
@@ -804,7 +849,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_kernel(GroupArgs g) {
   const f32x2* xs0 = xsc + (b0 < B ? b0 : B - 1) * nsteps;
   const f32x2* xs1 = xsc + (b1 < B ? b1 : B - 1) * nsteps;
   float acc0 = 0.f, acc1 = 0.f;
-  P::template run<B, NSB>(w, nsteps, xa, xsa, xb, xsb, xs0, xs1, acc0, acc1);
+  if constexpr (kHalfSumsOf<P>) {
+    P::template run<B, NSB>(w, nsteps, xa, xsa, xb, xsb, xs0, xs1, hsc + (xs0 - xsc), hsc + (xs1 - xsc),
+                            acc0, acc1);
+  } else {
+    P::template run<B, NSB>(w, nsteps, xa, xsa, xb, xsb, xs0, xs1, acc0, acc1);
+  }
   if constexpr (kGroupedX<P>) {
     acc0 *= w.scale;
     acc1 *= w.scale;
@@ -828,7 +878,7 @@ int launch_mfma_bn(const GroupArgs& g, hipStream_t st) {
     max_out = g.op[i].out > max_out ? g.op[i].out : max_out;
   }
   const int64_t nsteps = pesti::kGroupedX<P> ? 4 * ((max_in + 127) / 128) : max_in / 32;
-  const size_t lds = static_cast<size_t>(nsteps * 2 * B * 64 + 64 + 8 * B * nsteps);
+  const size_t lds = static_cast<size_t>(nsteps * 2 * B * 64 + 64 + 8 * B * nsteps * (pesti::kHalfSumsOf<P> ? 2 : 1));
   const int64_t tiles = (max_out + pesti::kMfmaGroupRows - 1) / pesti::kMfmaGroupRows;
   GroupArgs args = g;
   void* params[] = {&args};

@@ -967,44 +967,50 @@ def test_long_rows_group_equals_single_calls_bitwise(fmt):
 # ---------------------------------------------------------------------------
 def _cancelling_row(fmt, rng, n_super):
     """Packed bytes of one row of n_super super-blocks in which every
-    sub-block has one constant code c and scale/min with sc * c == m (and
-    d == dmin), so each of its weights is d*sc*c - dmin*m = 0 exactly."""
+    weight is d*sc*q - dmin*m = 0 exactly: dmin = k d (k = 1, 3 or 5, d
+    with few enough significant bits that k d is a binary16 value), and in
+    every sub-block one constant code c with sc = k s, m = c s."""
     import packing
     blocks = []
     for _ in range(n_super):
-        d = packing.f16_bits(abs(rng.normal(0.0, np.sqrt(1e-3))))
+        k = int(rng.choice([1, 3, 5]))
+        d_val = max(float(np.float16(abs(rng.normal(0.0, np.sqrt(1e-3))))), 2.0 ** -12)
+        mant, ex = np.frexp(d_val)
+        d_val = float(np.ldexp(np.round(mant * 256) / 256, ex))      # 8 significant bits
+        d, dmin = packing.f16_bits(d_val), packing.f16_bits(k * d_val)
+        assert float(np.uint16(dmin).view(np.float16)) == k * float(np.uint16(d).view(np.float16))
         if fmt in ("q4_k", "q5_k"):
-            cmax = 15 if fmt == "q4_k" else 31
+            cmax, smax_bits = (15 if fmt == "q4_k" else 31), 63
             sc, m, q = [], [], []
             for _ in range(8):
                 c = int(rng.integers(1, cmax + 1))
-                s = int(rng.integers(1, 63 // c + 1))
-                sc.append(s)
-                m.append(s * c)
+                s_ = int(rng.integers(1, max(1, min(smax_bits // k, 63 // c)) + 1))
+                sc.append(k * s_)
+                m.append(c * s_)
                 q += [c] * 32
             pack = packing.pack_q4_k_block if fmt == "q4_k" else packing.pack_q5_k_block
-            blocks.append(pack(d, d, sc, m, q))
+            blocks.append(pack(d, dmin, sc, m, q))
         else:
-            sc, m, q = [], [], [0] * 256
-            for s_idx in range(16):
+            sc, m, cs = [], [], []
+            for _ in range(16):
                 c = int(rng.integers(1, 4))
-                s = int(rng.integers(1, 15 // c + 1))
-                sc.append(s)
-                m.append(s * c)
+                s_ = int(rng.integers(1, max(1, min(15 // k, 15 // c)) + 1))
+                sc.append(k * s_)
+                m.append(c * s_)
+                cs.append(c)
+            q = [0] * 256
             for h in range(2):
                 for j in range(4):
                     for c2 in range(2):
                         for l in range(16):
-                            sub = 8 * h + 2 * j + c2
-                            q[128 * h + 32 * j + 16 * c2 + l] = m[sub] // sc[sub]
-            blocks.append(packing.pack_q2_k_block(d, d, sc, m, q))
+                            q[128 * h + 32 * j + 16 * c2 + l] = cs[8 * h + 2 * j + c2]
+            blocks.append(packing.pack_q2_k_block(d, dmin, sc, m, q))
     return np.frombuffer(b"".join(blocks), np.uint8)
 
 
 CANCEL_CASES = [(40, 896, 1), (40, 896, 3), (40, 4864, 1), (40, 4864, 3), (MFMA_ROWS + 5, 896, 3)]
 
 
-@pytest.mark.xfail(reason="kernels take the min term from staged sums of x; exact form pending", strict=False)
 @pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q2_k"])
 @pytest.mark.parametrize("out,inf,batch", CANCEL_CASES)
 def test_exact_cancellation_gives_bias(fmt, out, inf, batch):
@@ -1022,3 +1028,20 @@ def test_exact_cancellation_gives_bias(fmt, out, inf, batch):
     y = run_gemv(fmt, packed, None, out, inf, x, bias)
     y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
     assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} cancelling {out}x{inf} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q2_k"])
+@pytest.mark.parametrize("m,k,n", [(16, 896, 70), (33, 4864, 64), (16, 896, 16400), (64, 512, 16385)])
+def test_gemm_quant_exact_cancellation_gives_bias(fmt, m, k, n):
+    """The quantized small-M GEMM (K-split kernel for narrow layers, wide
+    kernel from 1024 / 256 column tiles) on rows whose weights are all
+    exactly zero: Y must be the bias within 1e-4 * |b| + 1e-6."""
+    rng = np.random.default_rng([32, len(fmt), k, n])
+    n_super = -(-k // 256)
+    distinct = np.stack([_cancelling_row(fmt, rng, n_super) for _ in range(40)])
+    packed = np.resize(distinct, (n, distinct.shape[1]))
+    x16 = synth.f16_activations(rng, m, k)
+    bias = synth.bias(rng, n)
+    y = run_gemm_quant(fmt, packed, m, n, k, x16, bias)
+    y_ref, s_ref = oracle.gemm_packed(fmt, packed, n, k, x16, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"{fmt} gemm cancelling m{m} k{k} n{n}")
