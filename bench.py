@@ -209,8 +209,14 @@ def make_step(lib, calls, launches, weights, xs, ys, biases, ffn="separate"):
 
 def kernel_name(fmt, infs, outs):
     """Label of the mat-vec kernel instance one batch-1 launch uses: lanes
-    per row L by the longest row (one row per lane group at batch 1)."""
-    units = max({"q8_0": inf // 64 if inf % 64 == 0 else inf // 32, "q4_k": -(-inf // 64),
+    per row L by the longest row (one row per lane group at batch 1); Q8_0
+    rows of an even block count take two blocks per unit (q8_0x2), Q4_K rows
+    of at most 1024 weights half units (q4_kh)."""
+    if fmt == "q8_0" and all(inf % 64 == 0 for inf in infs):
+        fmt = "q8_0x2"
+    if fmt == "q4_k" and all(inf <= 1024 for inf in infs):
+        fmt = "q4_kh"
+    units = max({"q8_0x2": inf // 64, "q8_0": inf // 32, "q4_k": -(-inf // 64), "q4_kh": 2 * -(-inf // 64),
                  "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     rows = 1
@@ -629,7 +635,8 @@ def dominant_traffic(kernel_label):
         return None
     fmt = kernel_label.split("<")[1].split(",")[0]
     lanes = kernel_label.split("L=")[1].split(",")[0]
-    tag = {"q8_0": "FmtQ8_0", "q4_k": "FmtQ4_K", "q6_k": "FmtQ6_K"}[fmt]
+    tag = {"q8_0": "FmtQ8_0", "q8_0x2": "FmtQ8_0x2", "q4_k": "FmtQ4_K", "q4_kh": "FmtQ4_KH",
+           "q6_k": "FmtQ6_K"}[fmt]
     # one entry per launch shape of the kernel; every shape of the decode step
     # occurs equally often (once per layer), so the per-launch average is
     # the plain mean over shapes

@@ -330,6 +330,80 @@ struct FmtQ4_K {
 };
 
 // ---------------------------------------------------------------------------
+// Q4_K in half units, for short rows at batch 1: unit u is half h = u % 2 of
+// run r = u / 2 (super-block r / 4, run g = r % 4), i.e. code bytes
+// 32g + 16h .. +15, whose low nibbles are weights 64r + 16h + [0, 16) of
+// sub-block 2g and high nibbles weights 64r + 32 + 16h + [0, 16) of
+// sub-block 2g + 1.  A 896-weight row is 28 half units on 32 lanes: each
+// lane dequantizes and sums 32 weights instead of 64, which halves the
+// arithmetic after a launch's one memory round trip (the decode step's
+// launches are that short).  g = (u / 2) % 4 is fixed per lane (L is a
+// multiple of 8), so the scale gather is FmtQ4_K's for lane sub / 2.
+// ---------------------------------------------------------------------------
+#ifndef PESTI_Q4K_HALF_UNITS
+#define PESTI_Q4K_HALF_UNITS 1
+#endif
+constexpr bool kQ4KHalfUnits = PESTI_Q4K_HALF_UNITS != 0;
+
+struct FmtQ4_KH {
+  static constexpr bool kRowScales = false;
+  static constexpr int kPad = 256;
+  struct Raw { u32x4 hdr, q; };
+  using Lane = FmtQ4_K::Lane;
+  __device__ static Lane lane_state(int sub) { return FmtQ4_K::lane_state(sub >> 1); }
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* sbp = rp + (u >> 3) * 144;
+    r.hdr = load_u32x4_a16(sbp);
+    r.q = load_u32x4_a16(sbp + 16 + 16 * (u & 7));   // 32g + 16h = 16 (u % 8)
+  }
+
+  // Each weight dequantized on its own (see FmtQ4_K::compute).
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const Lane& L, float* acc) {
+    float ds0[R], ds1[R], ndm0[R], ndm1[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float dm0, dm1;
+      FmtQ4_K::scales(r[k].hdr, L, ds0[k], ds1[k], dm0, dm1);
+      ndm0[k] = -dm0;
+      ndm1[k] = -dm1;
+    }
+    const int x0 = 64 * (u >> 1) + 16 * (u & 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 xl[B], xh[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        xl[b] = xs4(xs + b * a.xstride, x0 + 4 * t);
+        xh[b] = xs4(xs + b * a.xstride, x0 + 32 + 4 * t);
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t q = t == 0 ? r[k].q.x : (t == 1 ? r[k].q.y : (t == 2 ? r[k].q.z : r[k].q.w));
+        float l0, l1, l2, l3, h0, h1, h2, h3;
+        nibbles_x512(q & 0x0F0F0F0Fu, l0, l1, l2, l3);
+        nibbles_x512((q >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);
+        l0 = fmaf(ds0[k], l0, ndm0[k]); l1 = fmaf(ds0[k], l1, ndm0[k]);
+        l2 = fmaf(ds0[k], l2, ndm0[k]); l3 = fmaf(ds0[k], l3, ndm0[k]);
+        h0 = fmaf(ds1[k], h0, ndm1[k]); h1 = fmaf(ds1[k], h1, ndm1[k]);
+        h2 = fmaf(ds1[k], h2, ndm1[k]); h3 = fmaf(ds1[k], h3, ndm1[k]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float& s = acc[k * B + b];
+          s = fmaf(l0, xl[b].x, s); s = fmaf(l1, xl[b].y, s);
+          s = fmaf(l2, xl[b].z, s); s = fmaf(l3, xl[b].w, s);
+          s = fmaf(h0, xh[b].x, s); s = fmaf(h1, xh[b].y, s);
+          s = fmaf(h2, xh[b].z, s); s = fmaf(h3, xh[b].w, s);
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Q2_K and Q3_K share a unit: half h and column c of super-block u / 4
 // (h = (u >> 1) & 1, c = u & 1), i.e. code bytes 32h + 16c .. +15 of the
 // super-block, whose bits 2j, 2j+1 hold weights 128h + 32j + 16c + [0, 16)
@@ -1210,6 +1284,9 @@ template <> inline void shape_of<pesti::FmtQ8_0>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtQ4_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 144; *u = (in + 63) / 64;
 }
+template <> inline void shape_of<pesti::FmtQ4_KH>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = ((in + 255) / 256) * 144; *u = 2 * ((in + 63) / 64);
+}
 template <> inline void shape_of<pesti::FmtQ2_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 84; *u = ((in + 127) / 128) * 2;
 }
@@ -1299,6 +1376,21 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
          a.in > 0 && a.in <= 1024;
 }
+// Tall Q4_K matrices with rows of at most 1024 weights at batch 1 take the
+// batch-1 kernel of gemv_tall.hip (128-weight units, a row per U lanes).
+#ifndef PESTI_TALL_MIN_ROWS
+#define PESTI_TALL_MIN_ROWS 16384
+#endif
+constexpr int64_t kTallMinRows = PESTI_TALL_MIN_ROWS;
+template <class F>
+inline bool tall_op(const GemvArgs& a, int batch) {
+  return std::is_same<F, pesti::FmtQ4_K>::value && batch == 1 && a.out >= kTallMinRows && a.in > 0 &&
+         a.in <= 1024;
+}
+// One launch of ops that all pass tall_op and share one row length in
+// 128-weight units; x and y of every op set.
+int launch_tall_q4_k(const GroupArgs& g, hipStream_t st);
+
 // One launch of ops that all pass mfma_op and share one row length in
 // super-blocks; x and y of every op set.
 int launch_mfma_q4_k(const GroupArgs& g, int batch, hipStream_t st);
@@ -1378,6 +1470,41 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     if (r != PESTI_OK) return r;
   }
   if (n_mv == 0) return PESTI_OK;
+  if constexpr (std::is_same<F, pesti::FmtQ4_K>::value) {
+    // Tall batch-1 ops leave the group: one launch per row length in
+    // 128-weight units.
+    GroupArgs rest{};
+    int rest_live[PESTI_MAX_GROUP];
+    bool taken[PESTI_MAX_GROUP] = {};
+    for (int i = 0; i < n_mv; ++i) {
+      if (taken[i] || !tall_op<F>(g.op[i], batch)) continue;
+      GroupArgs t{};
+      for (int j = i; j < n_mv; ++j) {
+        if (taken[j] || !tall_op<F>(g.op[j], batch) || (g.op[j].in + 127) / 128 != (g.op[i].in + 127) / 128)
+          continue;
+        taken[j] = true;
+        t.op[t.n_ops] = g.op[j];
+        t.op[t.n_ops].x = ops[live[j]].x;
+        t.op[t.n_ops].y = ops[live[j]].y;
+        ++t.n_ops;
+      }
+      const int r = launch_tall_q4_k(t, stream_h);
+      if (r != PESTI_OK) return r;
+    }
+    max_units = 0;
+    max_out = 0;
+    for (int i = 0; i < n_mv; ++i) {
+      if (taken[i]) continue;
+      rest_live[rest.n_ops] = live[i];
+      rest.op[rest.n_ops++] = g.op[i];
+      if (g.op[i].units > max_units) max_units = g.op[i].units;
+      if (g.op[i].out > max_out) max_out = g.op[i].out;
+    }
+    if (rest.n_ops == 0) return PESTI_OK;
+    g = rest;
+    n_mv = rest.n_ops;
+    for (int i = 0; i < n_mv; ++i) live[i] = rest_live[i];
+  }
   if constexpr (kHasMfma<F>) {
     // Matrix-core ops leave the group: one launch per row length (every
     // batch column at once); the rest stay for the vector-ALU kernel.
@@ -1421,7 +1548,16 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
       c.op[i].y = o.y + static_cast<int64_t>(b0) * o.out_features;
     }
     const size_t lds = row_lds * nb;
-    const int r = launch_lu<F>(c, max_units, max_out, nb, lds, stream_h);
+    int r = 1;
+    if constexpr (std::is_same<F, pesti::FmtQ4_K>::value && pesti::kQ4KHalfUnits) {
+      if (nb == 1 && max_units <= 16) {
+        // rows of at most 1024 weights at batch 1: half units (FmtQ4_KH)
+        for (int i = 0; i < n_mv; ++i) c.op[i].units = 2 * c.op[i].units;
+        r = max_units <= 8 ? launch_one<pesti::FmtQ4_KH, 16, 1, 1, 1>(c, lds, stream_h)
+                           : launch_one<pesti::FmtQ4_KH, 32, 1, 1, 1>(c, lds, stream_h);
+      }
+    }
+    if (r == 1) r = launch_lu<F>(c, max_units, max_out, nb, lds, stream_h);
     if (r != PESTI_OK) return r;
   }
   return PESTI_OK;

@@ -1,0 +1,186 @@
+// Batch-1 mat-vec for tall Q4_K matrices with short rows (the LM head,
+// 151936 x 896): y = W x + b.
+//
+// The operation is the decode step's row-major matrix-vector product with
+// the weights kept in GGUF Q4_K blocks ("Project scaffold: modules, CLI, and
+// correctness harness", file summaries of tensor.rs and quant.rs; "PESTI -
+// Portable Execution Substrate for Transformer Inference", "What This Is"):
+// w = d sc q - dmin m per 32-weight sub-block.
+//
+// At batch 1 the general kernel (gemv_impl.h) spends most of a lane's
+// instructions on work that does not scale with the weights it reads - x
+// staging, address set-up, scale decode, the reduction - for one 64-weight
+// unit per lane, and 2 of each 16-lane row group stay idle on 896-weight
+// rows (14 units).  Here a lane takes a 128-weight unit (two runs of one
+// super-block: its 16-byte header and 64 code bytes, five 16-byte loads)
+// and a row takes U = in / 128 consecutive lanes, so a wave holds
+// floor(64 / U) rows (9 rows of 7 lanes at 896 columns, one lane idle), and
+// a workgroup of 4 waves stages x once for 36 rows (measured on the
+// 151936 x 896 head: 2 / 4 / 8 / 16 waves 21.5 / 20.0 / 22.6 / 26.8 us).  Each weight is
+// dequantized on its own, w = (d sc 2^9)(q 2^-9) - dmin m, one rounding of
+// the exact value (the float32 weight, bit for bit), then multiplied into
+// the lane's sum; the U partial sums of a row are added in lane order by
+// cross-lane reads (a fixed order: results do not depend on timing).
+#include "gemv_impl.h"
+
+namespace pesti {
+
+#ifndef PESTI_TALL_WAVES
+#define PESTI_TALL_WAVES 4
+#endif
+constexpr int kTallWaves = PESTI_TALL_WAVES;
+constexpr int kTallThreads = kTallWaves * kWave;
+constexpr int kTallMaxIn = 1024;
+
+// One lane's unit u of a row: runs 2(u % 2) and 2(u % 2) + 1 of super-block
+// u / 2 (sub-blocks 4(u % 2) .. +3), weights 128u .. 128u + 127.
+struct TallQ4K {
+  struct Raw { u32x4 hdr, c0, c1, c2, c3; };
+
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
+    const uint8_t* sb = rp + (u >> 1) * 144;
+    const uint8_t* cp = sb + 16 + 64 * (u & 1);
+    r.hdr = load_u32x4_a16(sb);
+    r.c0 = load_u32x4_a16(cp);
+    r.c1 = load_u32x4_a16(cp + 16);
+    r.c2 = load_u32x4_a16(cp + 32);
+    r.c3 = load_u32x4_a16(cp + 48);
+  }
+
+  // Code dword i (0..15) of the unit: bytes 4i..4i+3 of its 64 code bytes.
+  __device__ __forceinline__ static uint32_t word(const Raw& r, int i) {
+    const u32x4& v = i < 4 ? r.c0 : (i < 8 ? r.c1 : (i < 12 ? r.c2 : r.c3));
+    switch (i & 3) {
+      case 0: return v.x;
+      case 1: return v.y;
+      case 2: return v.z;
+      default: return v.w;
+    }
+  }
+
+  // acc += sum over the unit's 128 weights of w * x.  Sub-block 4h + t
+  // (h = u % 2): t = 0..3 for h = 0 take sc = S[t] & 63, m = S[t + 4] & 63;
+  // for h = 1 sc = (S[t + 8] & 15) | (S[t] >> 6) << 4, m = (S[t + 8] >> 4) |
+  // (S[t + 4] >> 6) << 4 (S = header bytes 4..15, dwords y, z, w).
+  __device__ __forceinline__ static float compute(const Raw& r, int u, const float* xs) {
+    const uint32_t y = r.hdr.y, z = r.hdr.z, w = r.hdr.w;
+    const bool h1 = (u & 1) != 0;
+    const uint32_t scv = h1 ? ((w & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u)) : (y & 0x3F3F3F3Fu);
+    const uint32_t mv = h1 ? (((w >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u)) : (z & 0x3F3F3F3Fu);
+    const float d512 = f16_lo(r.hdr.x) * 512.0f, dmin = f16_hi(r.hdr.x);
+    const float ds[4] = {d512 * ubyte<0>(scv), d512 * ubyte<1>(scv), d512 * ubyte<2>(scv), d512 * ubyte<3>(scv)};
+    const float ndm[4] = {-(dmin * ubyte<0>(mv)), -(dmin * ubyte<1>(mv)), -(dmin * ubyte<2>(mv)),
+                          -(dmin * ubyte<3>(mv))};
+    float acc = 0.f;
+    const int x0 = 128 * u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {   // run 2h + k: low nibbles sub-block 4h + 2k, high 4h + 2k + 1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t q = word(r, 8 * k + i);
+        const f32x4 xl = xs4(xs, x0 + 64 * k + 4 * i);
+        const f32x4 xh = xs4(xs, x0 + 64 * k + 32 + 4 * i);
+        float l0, l1, l2, l3, g0, g1, g2, g3;
+        nibbles_x512(q & 0x0F0F0F0Fu, l0, l1, l2, l3);
+        nibbles_x512((q >> 4) & 0x0F0F0F0Fu, g0, g1, g2, g3);
+        acc = fmaf(fmaf(ds[2 * k], l0, ndm[2 * k]), xl.x, acc);
+        acc = fmaf(fmaf(ds[2 * k], l1, ndm[2 * k]), xl.y, acc);
+        acc = fmaf(fmaf(ds[2 * k], l2, ndm[2 * k]), xl.z, acc);
+        acc = fmaf(fmaf(ds[2 * k], l3, ndm[2 * k]), xl.w, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], g0, ndm[2 * k + 1]), xh.x, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], g1, ndm[2 * k + 1]), xh.y, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], g2, ndm[2 * k + 1]), xh.z, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], g3, ndm[2 * k + 1]), xh.w, acc);
+      }
+    }
+    return acc;
+  }
+};
+
+// U = 128-weight units per row (rows of up to 128 U weights, padded to
+// whole super-blocks); a wave serves 64 / U rows, a workgroup kTallWaves
+// times that.  Measured and not taken: two or four row groups per wave with
+// all their loads in flight at once (24.2 / 36.0 us), and register caps of
+// 80 or 64 VGPRs for more waves per SIMD (26.8 us; 46.6 us with spills).
+template <int U>
+__global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g) {
+  __shared__ float xs[xs_phys(kTallMaxIn)];
+  constexpr int kRowsPerWave = kWave / U;
+  constexpr int kRowsPerGroup = kRowsPerWave * kTallWaves;
+  const GemvArgs a = g.op[blockIdx.y];
+  asm volatile("" ::"s"(a.w), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in), "s"(a.row_bytes));
+  const int64_t first_wg = static_cast<int64_t>(blockIdx.x) * kRowsPerGroup;
+  if (first_wg >= a.out) return;   // this op has fewer row groups (uniform)
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int rr = lane / U;   // row of the lane within the wave
+  const int u = lane - rr * U;
+  const int64_t row = first_wg + wave * kRowsPerWave + rr;
+  const bool live = rr < kRowsPerWave && row < a.out;
+  // x first (slots past `in` are zero), then the unit's loads: rows past
+  // the end and the idle lanes read unit 0 of the workgroup's first row (in
+  // bounds).
+  constexpr int kX4 = 32 * U;   // float4 slots of the padded row
+  constexpr int kXPer = (kX4 + kTallThreads - 1) / kTallThreads;
+  const int in4 = static_cast<int>(a.in >> 2);
+  f32x4 xv[kXPer];
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) {
+    const int s = tid + k * kTallThreads;
+    xv[k] = reinterpret_cast<const f32x4*>(a.x)[s < in4 ? s : 0];
+  }
+  const uint8_t* rp = a.w + (live ? row : first_wg) * a.row_bytes;
+  TallQ4K::Raw r;
+  TallQ4K::issue(rp, live ? u : 0, r);
+  const float bv = *(a.bias ? a.bias + (live ? row : first_wg) : reinterpret_cast<const float*>(rp));
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) {
+    const int s = tid + k * kTallThreads;
+    if (s < kX4) *reinterpret_cast<f32x4*>(xs + xs_phys(4 * s)) = s < in4 ? xv[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const float part = live ? TallQ4K::compute(r, u, xs) : 0.f;
+  // the row's U partial sums, added in lane order (reads past the wave take
+  // the lane's own value; only the row's first lane stores)
+  float sum = part;
+#pragma unroll
+  for (int k = 1; k < U; ++k) sum += __shfl(part, lane + k < kWave ? lane + k : lane, kWave);
+  if (u == 0 && live) a.y[row] = sum + (a.bias ? bv : 0.f);
+}
+
+}  // namespace pesti
+
+namespace pesti_gemv {
+
+template <int U>
+int launch_tall_u(const GroupArgs& g, hipStream_t st) {
+  constexpr int64_t kRows = (pesti::kWave / U) * pesti::kTallWaves;
+  int64_t max_out = 0;
+  for (int i = 0; i < g.n_ops; ++i) max_out = g.op[i].out > max_out ? g.op[i].out : max_out;
+  const int64_t groups = (max_out + kRows - 1) / kRows;
+  GroupArgs args = g;
+  void* params[] = {&args};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_q4k_kernel<U>),
+                                       dim3(static_cast<unsigned>(groups), static_cast<unsigned>(g.n_ops)),
+                                       dim3(pesti::kTallThreads), params, 0, st);
+  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
+// One launch of tall batch-1 Q4_K ops that share one row length.
+int launch_tall_q4_k(const GroupArgs& g, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  switch ((g.op[0].in + 127) / 128) {
+    case 1: return launch_tall_u<1>(g, st);
+    case 2: return launch_tall_u<2>(g, st);
+    case 3: return launch_tall_u<3>(g, st);
+    case 4: return launch_tall_u<4>(g, st);
+    case 5: return launch_tall_u<5>(g, st);
+    case 6: return launch_tall_u<6>(g, st);
+    case 7: return launch_tall_u<7>(g, st);
+    case 8: return launch_tall_u<8>(g, st);
+    default: return PESTI_ERR_SHAPE;
+  }
+}
+
+}  // namespace pesti_gemv

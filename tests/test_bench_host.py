@@ -70,11 +70,15 @@ def test_call_bytes_per_format():
     assert bench.call_bytes("i4row", 5, 64, 1, False) == 5 * 32 + 20 + 4 * 69
 
 
-@pytest.mark.parametrize("fmt,inf,lanes", [("q4_k", 896, 16), ("q4_k", 4864, 64), ("q6_k", 4864, 64),
-                                          ("q6_k", 896, 16), ("q8_0", 896, 16), ("q8_0", 4864, 64),
-                                          ("q4_k", 2048, 32)])
-def test_kernel_label_lanes(fmt, inf, lanes):
-    assert bench.kernel_name(fmt, [inf], [896]) == f"gemv_kernel<{fmt}, L={lanes}, B=1, R=1>"
+@pytest.mark.parametrize("fmt,inf,lanes,label", [("q4_k", 896, 32, "q4_kh"), ("q4_k", 4864, 64, "q4_k"),
+                                                ("q6_k", 4864, 64, "q6_k"), ("q6_k", 896, 16, "q6_k"),
+                                                ("q8_0", 896, 16, "q8_0x2"), ("q8_0", 4864, 64, "q8_0x2"),
+                                                ("q8_0", 800, 32, "q8_0"), ("q4_k", 2048, 32, "q4_k"),
+                                                ("q4_k", 512, 16, "q4_kh")])
+def test_kernel_label_lanes(fmt, inf, lanes, label):
+    """Q8_0 rows of an even block count run the two-blocks-per-unit kernel,
+    Q4_K rows of at most 1024 weights the half-unit one."""
+    assert bench.kernel_name(fmt, [inf], [896]) == f"gemv_kernel<{label}, L={lanes}, B=1, R=1>"
 
 
 def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
