@@ -93,6 +93,15 @@ def quant_blocks(fmt: str, rng: np.random.Generator, rows: int, in_features: int
     return raw.reshape(rows, nblk * nbytes)
 
 
+def stream_blocks(rng: np.random.Generator, rows: int, in_features: int, force_d=None) -> np.ndarray:
+    """Packed bytes (flat uint8) of a Q4_K matrix in the stream layout: the
+    row-major weights cut into ceil(rows * in / 256) super-blocks in order,
+    each drawn as quant_blocks draws a Q4_K block (the padding weights at
+    the end of the stream are random too)."""
+    nsb = -(-(rows * in_features) // 256)
+    return quant_blocks("q4_k", rng, 1, nsb * 256, force_d).reshape(-1)
+
+
 def i8row(rng: np.random.Generator, rows: int, in_features: int):
     """(int8 codes [rows, in], float32 scales [rows]) for the per-row format."""
     w = rng.normal(0.0, 0.02, size=(rows, in_features)).astype(np.float32)
@@ -139,6 +148,8 @@ def matrix(fmt: str, rng: np.random.Generator, rows: int, in_features: int):
         return codes.view(np.uint8), scales
     if fmt == "i4row":
         return i4row(rng, rows, in_features)
+    if fmt == "q4_k_stream":
+        return stream_blocks(rng, rows, in_features), None
     return quant_blocks(fmt, rng, rows, in_features), None
 
 

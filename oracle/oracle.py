@@ -63,12 +63,22 @@ Rows whose length is not a multiple of the 256-weight super-block are padded
 to whole super-blocks; the padding columns are never part of the matrix and
 the oracle drops them after decoding (their bytes may hold anything).
 
+* Q4_K stream ("q4_k_stream"; the byte-minimal layout of rows that are not a
+  whole number of super-blocks): the matrix's weights in row-major order,
+  weight (r, c) at position r * in + c of one stream, cut into 256-weight
+  Q4_K super-blocks in stream order; only the last super-block is padded.
+  A 896-weight row is 3.5 super-blocks (504 bytes) and starts at weight 0
+  or 128 of one.  Each super-block decodes as a Q4_K block; the stream is
+  then cut back into rows.
+
 All dequantized values are exact in float64 (binary16 d times a small
 integer, minus binary16 dmin times a 6-bit integer, needs at most 50
 significant bits; Q5_K's 5-bit codes one more; Q2_K and Q3_K fewer), so
 float64 is the exact reference; the float32 value of a weight is the float64 value rounded once to nearest-even.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -82,6 +92,14 @@ BLOCK_BYTES = {"q8_0": 34, "q2_k": 84, "q3_k": 110, "q4_k": 144, "q5_k": 176, "q
 # ---------------------------------------------------------------------------
 # layout helpers
 # ---------------------------------------------------------------------------
+def matrix_bytes(fmt: str, rows: int, in_features: int) -> int:
+    """Bytes of a packed matrix: rows * row_bytes, or for the Q4_K stream
+    layout the whole super-blocks that hold rows * in_features weights."""
+    if fmt == "q4_k_stream":
+        return -(-(rows * in_features) // QK_K) * BLOCK_BYTES["q4_k"]
+    return rows * row_bytes(fmt, in_features)
+
+
 def row_bytes(fmt: str, in_features: int) -> int:
     """Bytes of one packed row of `in_features` weights (row padded to whole
     blocks).  For i8row this is the code bytes only; the scale is separate."""
@@ -246,6 +264,18 @@ def dequant_q4_k(packed, rows: int, in_features: int) -> np.ndarray:
     return w.reshape(rows, -1)[:, :in_features]
 
 
+def dequant_q4_k_stream(packed, rows: int, in_features: int) -> np.ndarray:
+    """Q4_K stream layout: the super-blocks hold the row-major weight stream
+    (see the module notes); decode them as one long Q4_K row, drop the
+    padding at the end of the stream, cut into rows.  float64 [rows, in]."""
+    if in_features % 32:
+        raise ValueError("Q4_K needs in_features % 32 == 0")
+    n = rows * in_features
+    nsb = -(-n // QK_K)
+    flat = dequant_q4_k(np.asarray(packed).reshape(-1), 1, nsb * QK_K)[0]
+    return flat[:n].reshape(rows, in_features)
+
+
 def q5_k_codes(qh: np.ndarray, qs: np.ndarray) -> np.ndarray:
     """The 256 5-bit codes (0..31) of a Q5_K super-block: the low four bits
     are the Q4_K codes of the 128 bytes qs; weight i = 64r + 32c + l (run r,
@@ -353,6 +383,8 @@ def dequantize(fmt: str, packed, rows: int, in_features: int, scales=None) -> np
         return dequant_q3_k(packed, rows, in_features)
     if fmt == "q4_k":
         return dequant_q4_k(packed, rows, in_features)
+    if fmt == "q4_k_stream":
+        return dequant_q4_k_stream(packed, rows, in_features)
     if fmt == "q5_k":
         return dequant_q5_k(packed, rows, in_features)
     if fmt == "q6_k":
@@ -392,12 +424,21 @@ def gemv_packed(fmt: str, packed, rows: int, in_features: int, x, bias=None,
     float64, then a plain dot product, a chunk of rows at a time so that a
     large matrix never has to be expanded whole."""
     x64 = np.atleast_2d(np.asarray(x, dtype=np.float64))
-    rb = row_bytes(fmt, in_features)
     flat = np.asarray(packed).reshape(-1)
     ys, ss = [], []
+    if fmt == "q4_k_stream":
+        # chunks of whole super-blocks: a multiple of the rows that span one
+        step = QK_K // math.gcd(in_features, QK_K)
+        row_chunk = max(step, row_chunk // step * step)
+    else:
+        rb = row_bytes(fmt, in_features)
     for r0 in range(0, rows, row_chunk):
         r1 = min(rows, r0 + row_chunk)
-        if fmt == "i8row":
+        if fmt == "q4_k_stream":
+            b0 = r0 * in_features // QK_K * BLOCK_BYTES["q4_k"]
+            b1 = b0 + matrix_bytes(fmt, r1 - r0, in_features)
+            w = dequant_q4_k_stream(flat[b0:b1], r1 - r0, in_features)
+        elif fmt == "i8row":
             part = flat[r0 * in_features:r1 * in_features]
             w = dequant_i8row(part.view(np.int8).reshape(r1 - r0, in_features),
                               np.asarray(scales)[r0:r1])

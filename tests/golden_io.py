@@ -1,14 +1,15 @@
 """Reader for the hand-worked fixtures under tests/golden/.
 
 Grammar, one item per line ('#' starts a comment):
-  format <q8_0|q2_k|...|q6_k|i8row|i4row>   rows <n>   in_features <n>
+  format <q8_0|q2_k|...|q6_k|q4_k_stream|i8row|i4row>   rows <n>   in_features <n>
   hex <tokens>      packed bytes; a token is two hex digits, or XX*N for N copies
   codes <values>    i8row int8 codes of one row (values as below)
   scales <values>   i8row / i4row float32 scales (i4row codes travel as hex)
   f64 <values>      exact dequantized weights, row-major
   f32 <values>      float32 weights when they differ from rounding f64
   x / bias / y      a mat-vec case: input, bias and exact output
-A value is a decimal or hex float literal, or NxV for N copies of V."""
+Keys other than format, rows and in_features may repeat; their values are
+concatenated in order.  A value is a decimal or hex float literal, or NxV for N copies of V."""
 from __future__ import annotations
 
 from pathlib import Path
@@ -64,7 +65,9 @@ def load(name: str) -> dict:
         elif key == "codes":
             fx["codes"].append([int(v) for v in _values(rest)])
         elif key in ("scales", "f64", "f32", "x", "bias", "y"):
-            fx[key] = np.array(_values(rest), dtype=np.float64)
+            # a key may span several lines: the values are concatenated
+            vals = np.array(_values(rest), dtype=np.float64)
+            fx[key] = np.concatenate([fx[key], vals]) if key in fx else vals
         else:
             raise ValueError(f"{name}: unknown key {key!r}")
     return fx

@@ -141,7 +141,7 @@ def test_golden_fixture(name):
 
 def test_fixture_set_covers_every_format():
     fmts = {golden_io.load(n)["format"] for n in golden_io.all_fixtures()}
-    assert fmts == {"q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row"}
+    assert fmts == {"q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "q4_k_stream", "i8row", "i4row"}
 
 
 # ---------------------------------------------------------------------------
@@ -866,3 +866,115 @@ def test_planted_transpose_and_dropped_min_are_caught(monkeypatch):
     monkeypatch.setattr(mod, "gemv", transposed)
     with pytest.raises(AssertionError):
         test_gemv_brute_force("q8_0", 4, 32)
+
+
+# ---------------------------------------------------------------------------
+# Q4_K stream layout (the byte-minimal layout for rows that are not whole
+# super-blocks): weights in row-major order cut into super-blocks in order
+# ---------------------------------------------------------------------------
+def _stream_from_fields(rng, rows, inf):
+    """Packed stream bytes and the exact weights [rows][inf] from random
+    fields of ceil(rows * inf / 256) super-blocks (independent packer)."""
+    nsb = -(-rows * inf // 256)
+    blocks, exact = [], []
+    for _ in range(nsb):
+        d, dmin, sc, m, q = random_q4_k_fields(rng)
+        blocks.append(packing.pack_q4_k_block(d, dmin, sc, m, q))
+        exact += q4_k_exact(d, dmin, sc, m, q)
+    flat = exact[:rows * inf]
+    return (np.frombuffer(b"".join(blocks), dtype=np.uint8).copy(),
+            [flat[r * inf:(r + 1) * inf] for r in range(rows)])
+
+
+@pytest.mark.parametrize("rows,inf", [(2, 128), (3, 384), (5, 896), (7, 64), (3, 192)])
+def test_q4_k_stream_fields_and_closed_form(rows, inf):
+    rng = np.random.default_rng([71, rows, inf])
+    data, exact = _stream_from_fields(rng, rows, inf)
+    assert data.size == oracle.matrix_bytes("q4_k_stream", rows, inf)
+    w = oracle.dequantize("q4_k_stream", data, rows, inf)
+    assert w.shape == (rows, inf)
+    assert as_fraction_array(w) == [v for row in exact for v in row]
+
+
+@pytest.mark.parametrize("rows,inf", [(3, 256), (2, 512), (2, 4864)])
+def test_q4_k_stream_of_whole_super_block_rows_is_the_row_layout(rows, inf):
+    """When a row is whole super-blocks the stream and the padded row layout
+    are the same bytes, and so are the weights."""
+    rng = np.random.default_rng([72, rows, inf])
+    data, _ = _stream_from_fields(rng, rows, inf)
+    assert oracle.matrix_bytes("q4_k_stream", rows, inf) == rows * oracle.row_bytes("q4_k", inf)
+    assert np.array_equal(oracle.dequantize("q4_k_stream", data, rows, inf),
+                          oracle.dequantize("q4_k", data, rows, inf))
+
+
+def test_q4_k_stream_one_hot_positions():
+    """One code 9 at stream position p lands at row p // in, column p % in
+    (rows of 896 weights: 3.5 super-blocks, starting at weight 0 or 128)."""
+    rows, inf = 3, 896
+    nsb = -(-rows * inf // 256)
+    sc = [1, 2, 3, 4, 5, 6, 7, 8]
+    for p in (0, 31, 127, 128, 255, 895, 896, 1023, 1024, 1151, 1791, 1792, 2687):
+        blocks = []
+        for k in range(nsb):
+            q = [0] * 256
+            if p // 256 == k:
+                q[p % 256] = 9
+            blocks.append(packing.pack_q4_k_block(0x3C00, 0x0000, sc, [5] * 8, q))
+        w = oracle.dequantize("q4_k_stream", np.frombuffer(b"".join(blocks), np.uint8), rows, inf)
+        nz = np.argwhere(w)
+        assert nz.tolist() == [[p // inf, p % inf]], p
+        assert w[p // inf, p % inf] == 9 * sc[(p % 256) // 32]
+
+
+def test_q4_k_stream_padding_at_the_end_does_not_matter():
+    rng = np.random.default_rng(73)
+    rows, inf = 3, 896          # 2688 weights: the last super-block's second half is padding
+    data, _ = _stream_from_fields(rng, rows, inf)
+    other = data.copy()
+    last = other[-144:]
+    # weights 128..255 of the last block are runs 2 and 3 (code bytes
+    # 64..127) with sub-blocks 4..7, whose scale bytes 8..11 hold nothing else
+    last[16 + 64:] = rng.integers(0, 256, 64, dtype=np.uint8)
+    last[12:16] = rng.integers(0, 256, 4, dtype=np.uint8)
+    assert np.array_equal(oracle.dequantize("q4_k_stream", data, rows, inf),
+                          oracle.dequantize("q4_k_stream", other, rows, inf))
+
+
+@pytest.mark.parametrize("rows,inf", [(3, 128), (5, 384), (4, 896)])
+def test_q4_k_stream_gemv_brute_force(rows, inf):
+    rng = np.random.default_rng([74, rows, inf])
+    data, exact_w = _stream_from_fields(rng, rows, inf)
+    x = rng.standard_normal((2, inf)).astype(np.float32)
+    bias = rng.normal(0, 0.02, rows).astype(np.float32)
+    y, s = oracle.gemv_packed("q4_k_stream", data, rows, inf, x, bias)
+    ex = _exact_gemv(exact_w, x, bias)
+    for b in range(2):
+        for o in range(rows):
+            err = abs(Fraction(float(y[b, o])) - ex[b][o])
+            assert err <= Fraction(2.0 ** -50) * Fraction(float(s[b, o])) + Fraction(1, 2 ** 200), (b, o)
+
+
+def test_q4_k_stream_gemv_row_chunks_start_on_super_blocks():
+    """The oracle expands a large stream matrix in row chunks; each chunk
+    must begin on a super-block (a multiple of 2 rows at 896 columns)."""
+    rng = np.random.default_rng(75)
+    rows, inf = 37, 896
+    data, _ = _stream_from_fields(rng, rows, inf)
+    x = rng.standard_normal((1, inf)).astype(np.float32)
+    whole, s = oracle.gemv(oracle.dequantize("q4_k_stream", data, rows, inf), x)
+    for chunk in (1, 2, 3, 8, 1000):
+        y, _ = oracle.gemv_packed("q4_k_stream", data, rows, inf, x, row_chunk=chunk)
+        # float64 sums in another blocking differ at most by rounding
+        assert np.all(np.abs(y - whole) <= 2.0 ** -40 * s), chunk
+
+
+def test_planted_row_layout_reading_of_the_stream_is_caught():
+    """Reading a stream matrix as padded rows (896-weight rows as whole
+    super-blocks) fails the stream fixtures."""
+    fx = golden_io.load("q4_k_stream_rows.txt")
+    data, _ = golden_io.packed(fx)
+    w = oracle.dequantize("q4_k_stream", data, fx["rows"], fx["in_features"])
+    assert np.array_equal(w.reshape(-1), fx["f64"])
+    # padded rows of 384 weights are two whole super-blocks (288 bytes)
+    wrong = oracle.dequant_q4_k(data[:2 * 288], 2, fx["in_features"])
+    assert not np.array_equal(wrong.reshape(-1), fx["f64"][:2 * fx["in_features"]])
