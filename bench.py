@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "batch-1 dequant-GEMV HBM GB/s (% of peak), µs per Qwen2.5-0.5B decode step"
 CONFIG_INDEX = 2          # the decode-step workload
 NOMINAL_BYTES_PER_WEIGHT = {"q8_0": 34 / 32, "q2_k": 84 / 256, "q3_k": 110 / 256, "q4_k": 144 / 256,
+                            "q4_k_stream": 144 / 256,
                             "q5_k": 176 / 256, "q6_k": 210 / 256, "i8row": 1.0,
                             "i4row": 0.5}
 
@@ -52,6 +53,9 @@ def parse_args(argv=None):
     p.add_argument("--copies", type=int, default=2, help="weight copies alternated per step")
     p.add_argument("--grouping", choices=("stage", "none"), default="stage",
                    help="one launch per dependency stage (Q/K/V, O, gate/up, down) or per call")
+    p.add_argument("--layout", choices=("rows", "stream"), default="rows",
+                   help="Q4_K matrices of 896-weight rows in the row layout (whole super-blocks per "
+                        "row, 576 bytes) or the byte-minimal stream layout (504 bytes per row)")
     p.add_argument("--ffn", choices=("separate", "swiglu"), default="separate",
                    help="gate and up as two mat-vecs (the 169-call step) or one fused launch "
                         "writing silu(gate) * up, which the down projection then reads")
@@ -73,8 +77,9 @@ def parse_args(argv=None):
                         "fill kernels, one JSON line per case")
     p.add_argument("--suite-filter", default="",
                    help="only suite cases whose name contains this (comma-separated alternatives)")
-    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                   help="write the counter summary from two rocprofv3 --pmc runs and exit")
+    p.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                   help="write the counter summary from rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE "
+                        "and optionally the read request sizes) and exit")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="before the step, copy this many MiB device-to-device three times "
                         "(a kernel of known traffic for scaling HBM counters)")
@@ -91,7 +96,7 @@ def host_inputs(calls):
     out = []
     for layer, name, fmt, rows, inf, has_bias in calls:
         tidx = synth.TENSOR_INDEX[name]
-        packed = synth.quant_blocks(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), rows, inf)
+        packed, _ = synth.matrix(fmt, synth.rng_for(CONFIG_INDEX, layer, tidx), rows, inf)
         x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
         b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
         out.append((packed, x, b))
@@ -217,7 +222,7 @@ def kernel_name(fmt, infs, outs):
     if fmt == "q4_k" and all(inf <= 1024 for inf in infs):
         fmt = "q4_kh"
     units = max({"q8_0x2": inf // 64, "q8_0": inf // 32, "q4_k": -(-inf // 64), "q4_kh": 2 * -(-inf // 64),
-                 "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
+                 "q4_k_stream": inf // 64, "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     rows = 1
     return f"gemv_kernel<{fmt}, L={lanes}, B=1, R={rows}>"
@@ -591,11 +596,12 @@ def run_launch_floor(lib):
           flush=True)
 
 
-def summarize_pmc(fetch_csv, write_csv, calib_mib=256):
+def summarize_pmc(fetch_csv, write_csv, requests_csv=None, calib_mib=256):
     """Per-launch HBM bytes of every mat-vec kernel shape in a bench run, from
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
     same counter reads for the device-to-device copy of calib_mib MiB that
-    the run starts with (it moves calib_mib MiB each way)."""
+    the run starts with (it moves calib_mib MiB each way); with requests_csv
+    also the read bytes counted by request size (add_request_bytes)."""
     import csv
     import statistics
     known_kib = calib_mib * 1024.0
@@ -617,9 +623,44 @@ def summarize_pmc(fetch_csv, write_csv, calib_mib=256):
             d = out["kernels"].setdefault(key, {})
             d[counter.lower() + "_bytes"] = round(statistics.median(vals))
             d["dispatches"] = len(vals)
+    if requests_csv:
+        add_request_bytes(out, requests_csv, calib_mib)
     with open(PMC_SUMMARY, "w") as f:
         f.write(json.dumps(out, indent=1) + "\n")
     return out
+
+
+REQUEST_COUNTERS = (("TCC_EA0_RDREQ_32B_sum", 32), ("TCC_EA0_RDREQ_64B_sum", 64),
+                    ("TCC_EA0_RDREQ_128B_sum", 128))
+
+
+def add_request_bytes(out, path, calib_mib):
+    """Read bytes per dispatch counted by request size, 32 n32 + 64 n64 +
+    128 n128, from one counter pass over the three L2-to-fabric read request
+    counters.  Unlike a single scale factor fitted to the copy's 128-byte
+    requests, this counts a 32- or 64-byte request at its own size; the
+    copy's figure is kept to show the sum needs no scaling."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(path)))
+    per_dispatch = {}
+    for r in rows:
+        size = dict(REQUEST_COUNTERS).get(r["Counter_Name"])
+        if size is None:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"].split("(")[0], r["Grid_Size"])
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + size * float(r["Counter_Value"])
+    copies = [v for (_, name, _), v in per_dispatch.items()
+              if "copyBuffer" in name and v > calib_mib * (1 << 20) / 4]
+    out["calibration"]["read_requests"] = {
+        "copy_mib": calib_mib, "bytes": round(statistics.median(copies)) if copies else None,
+        "ratio_to_copy_size": round(statistics.median(copies) / (calib_mib * (1 << 20)), 5) if copies else None}
+    per = {}
+    for (_, name, grid), v in per_dispatch.items():
+        if "gemv_kernel" in name:
+            per.setdefault(f"{name} grid={grid}", []).append(v)
+    for key, vals in per.items():
+        out["kernels"].setdefault(key, {})["read_request_bytes"] = round(statistics.median(vals))
 
 
 def dominant_traffic(kernel_label):
@@ -636,7 +677,7 @@ def dominant_traffic(kernel_label):
     fmt = kernel_label.split("<")[1].split(",")[0]
     lanes = kernel_label.split("L=")[1].split(",")[0]
     tag = {"q8_0": "FmtQ8_0", "q8_0x2": "FmtQ8_0x2", "q4_k": "FmtQ4_K", "q4_kh": "FmtQ4_KH",
-           "q6_k": "FmtQ6_K"}[fmt]
+           "q4_k_stream": "FmtQ4_KS", "q6_k": "FmtQ6_K"}[fmt]
     # one entry per launch shape of the kernel; every shape of the decode step
     # occurs equally often (once per layer), so the per-launch average is
     # the plain mean over shapes
@@ -684,15 +725,19 @@ def parity_leg(path):
     from dequantize_mat_vec_amd import synth
     import oracle
     data = np.load(path)
-    calls = synth.decode_step_calls()
+    calls = synth.decode_step_calls(layout=str(data["layout"]) if "layout" in data.files else "rows")
     n_out, worst, failures = 0, 0.0, []
     for i in data["calls"]:
         i = int(i)
         layer, name, fmt, out, inf, _ = calls[i]
         rows, y = data[f"rows_{i}"], data[f"y_{i}"]
         packed, x, b = host_inputs([calls[i]])[0]
-        sub = packed.reshape(out, -1)[rows]
-        y_ref, s_ref = oracle.gemv_packed(fmt, sub, len(rows), inf, x, None if b is None else b[rows])
+        if fmt == "q4_k_stream":   # rows have no fixed stride: the whole (small) matrix
+            y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, b)
+            y_ref, s_ref = y_ref[:, rows], s_ref[:, rows]
+        else:
+            sub = packed.reshape(out, -1)[rows]
+            y_ref, s_ref = oracle.gemv_packed(fmt, sub, len(rows), inf, x, None if b is None else b[rows])
         ratio = np.abs(y.astype(np.float64) - y_ref[0]) / (GEMV_REL * s_ref[0] + 1e-6)
         bad = ~(ratio <= 1.0)
         n_out += len(rows)
@@ -704,7 +749,7 @@ def parity_leg(path):
             "worst_err_over_bound": round(worst, 4), "failures": failures[:8]}
 
 
-def run_parity(calls, ys, skip_names=()):
+def run_parity(calls, ys, skip_names=(), layout="rows"):
     """parity_sample() in this process, the check in a child process (the
     oracle runs only in the CPU leg)."""
     import tempfile
@@ -713,7 +758,7 @@ def run_parity(calls, ys, skip_names=()):
     fd, path = tempfile.mkstemp(suffix=".npz")
     os.close(fd)
     try:
-        arrays = {"calls": np.array(sorted(sample), dtype=np.int64)}
+        arrays = {"calls": np.array(sorted(sample), dtype=np.int64), "layout": np.array(layout)}
         for i, (rows, y) in sample.items():
             arrays[f"rows_{i}"] = rows
             arrays[f"y_{i}"] = y
@@ -822,6 +867,9 @@ def main(argv=None):
         suite_oracle_leg(args.suite_filter)
         return 0
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (2, 3):
+            print("--summarize-pmc takes FETCH_CSV WRITE_CSV [REQUESTS_CSV]", file=sys.stderr)
+            return 2
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
         return 0
     if args.gpus != 1:
@@ -839,11 +887,13 @@ def main(argv=None):
     if args.launch_floor:
         run_launch_floor(lib)
         return 0
-    calls, weights, xs, ys, biases = build_inputs(args.copies)
-    launches = plan_launches(calls, args.grouping)
-    if args.ffn == "swiglu" and args.grouping != "stage":
-        print("--ffn swiglu fuses the gate/up stage: it needs --grouping stage", file=sys.stderr)
+    if args.ffn == "swiglu" and (args.grouping != "stage" or args.layout != "rows"):
+        print("--ffn swiglu fuses the gate/up stage: it needs --grouping stage and --layout rows",
+              file=sys.stderr)
         return 2
+    from dequantize_mat_vec_amd import synth
+    calls, weights, xs, ys, biases = build_inputs(args.copies, synth.decode_step_calls(layout=args.layout))
+    launches = plan_launches(calls, args.grouping)
     step = make_step(lib, calls, launches, weights, xs, ys, biases, args.ffn)
     bytes_per_step = sum(call_bytes(fmt, out, inf, 1, hb) for _, _, fmt, out, inf, hb in calls)
     stream = torch.cuda.Stream()
@@ -892,7 +942,7 @@ def main(argv=None):
             torch.cuda.synchronize()
             # with the fused SwiGLU the gate buffer holds h and the down
             # projection reads it: those calls are checked by the test suite
-            parity = run_parity(calls, ys, ("gate", "up", "down") if args.ffn == "swiglu" else ())
+            parity = run_parity(calls, ys, ("gate", "up", "down") if args.ffn == "swiglu" else (), args.layout)
         t0 = time.perf_counter()
         for i in range(args.steps):
             run(i)
@@ -964,7 +1014,8 @@ def main(argv=None):
                                "{Q,K,V,O,gate,up Q4_K; down Q4_K/Q6_K} + 151936x896 Q8_0 LM head "
                                "= 169 mat-vecs", "bytes_per_step": bytes_per_step,
                    "launch": args.mode, "launches_per_step": len(launches),
-                   "grouping": args.grouping, "ffn": args.ffn, "weight_copies": args.copies},
+                   "grouping": args.grouping, "ffn": args.ffn, "q4_k_layout": args.layout,
+                   "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (None if traffic is None else int(traffic)),

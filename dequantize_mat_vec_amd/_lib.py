@@ -23,7 +23,8 @@ PESTI_ERR_ALIGN = -4
 PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
 
-FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7}
+FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7,
+              "q4_k_stream": 8}
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
@@ -31,6 +32,7 @@ _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
 _SIGNATURES = {
     "pesti_gemv_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pesti_gemv_q4_k_stream": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q2_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q3_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pesti_gemv_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp, _i32, _vp]),
@@ -48,6 +50,7 @@ _SIGNATURES = {
     "pesti_gemm_q5_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
+    "pesti_dequant_q4_k_stream": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q2_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q3_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q5_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -56,6 +59,7 @@ _SIGNATURES = {
     "pesti_dequant_i4row": (_c_int, [_i64, _i64, _vp, _vp, _vp, _vp]),
     "pesti_stream_read": (_c_int, [_vp, _i64, _vp, _vp]),
     "pesti_row_bytes": (_i64, [_i32, _i64]),
+    "pesti_matrix_bytes": (_i64, [_i32, _i64, _i64]),
     "pesti_strerror": (_c_char_p, [_c_int]),
     "pesti_abi_version": (_i32, []),
 }
@@ -146,6 +150,11 @@ def pesti_row_bytes(fmt, in_features: int) -> int:
     return load().pesti_row_bytes(fid, in_features)
 
 
+def pesti_matrix_bytes(fmt, rows: int, in_features: int) -> int:
+    fid = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
+    return load().pesti_matrix_bytes(fid, rows, in_features)
+
+
 def _gemv(name, out_features, in_features, blocks, x, y, bias, batch, stream):
     fn = getattr(load(), name)
     return _check(name, fn(out_features, in_features, _ptr(blocks), _ptr(x), _ptr(y),
@@ -158,6 +167,10 @@ def pesti_gemv_q8_0(out_features, in_features, blocks, x, y, bias=None, batch=1,
 
 def pesti_gemv_q4_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
     return _gemv("pesti_gemv_q4_k", out_features, in_features, blocks, x, y, bias, batch, stream)
+
+
+def pesti_gemv_q4_k_stream(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
+    return _gemv("pesti_gemv_q4_k_stream", out_features, in_features, blocks, x, y, bias, batch, stream)
 
 
 def pesti_gemv_q2_k(out_features, in_features, blocks, x, y, bias=None, batch=1, stream=None):
@@ -266,6 +279,10 @@ def pesti_dequant_q8_0(rows, in_features, blocks, w_out, stream=None):
 
 def pesti_dequant_q4_k(rows, in_features, blocks, w_out, stream=None):
     return _dequant("pesti_dequant_q4_k", rows, in_features, blocks, w_out, stream)
+
+
+def pesti_dequant_q4_k_stream(rows, in_features, blocks, w_out, stream=None):
+    return _dequant("pesti_dequant_q4_k_stream", rows, in_features, blocks, w_out, stream)
 
 
 def pesti_dequant_q2_k(rows, in_features, blocks, w_out, stream=None):

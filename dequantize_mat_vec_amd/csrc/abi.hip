@@ -48,8 +48,18 @@ int64_t pesti_row_bytes(int32_t format, int64_t in_features) {
     case PESTI_FMT_Q6_K: return ((in_features + 255) / 256) * 210;
     case PESTI_FMT_I8ROW: return in_features;
     case PESTI_FMT_I4ROW: return ((in_features + 63) / 64) * 32;
-    default: return -1;
+    default: return -1;   // PESTI_FMT_Q4_K_STREAM rows have no fixed size
   }
+}
+
+int64_t pesti_matrix_bytes(int32_t format, int64_t rows, int64_t in_features) {
+  if (rows < 0) return -1;
+  if (format == PESTI_FMT_Q4_K_STREAM) {
+    if (in_features < 0 || in_features % 64 != 0) return -1;
+    return (rows * in_features + 255) / 256 * 144;
+  }
+  const int64_t rb = pesti_row_bytes(format, in_features);
+  return rb < 0 ? -1 : rows * rb;
 }
 
 const char* pesti_strerror(int status) {

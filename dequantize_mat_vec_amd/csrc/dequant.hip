@@ -237,6 +237,29 @@ int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks, fl
                         ((in_features + 255) / 256) * 144, false);
 }
 
+// The stream layout is one long Q4_K row of ceil(rows * in / 256)
+// super-blocks; its first rows * in weights, in order, are w_out [rows][in].
+int pesti_dequant_q4_k_stream(int64_t rows, int64_t in_features, const void* blocks, float* w_out,
+                              void* stream) {
+  if (rows < 0 || in_features < 0 || in_features % 64 != 0 || in_features > PESTI_MAX_IN_FEATURES)
+    return PESTI_ERR_SHAPE;
+  if (rows == 0 || in_features == 0) return PESTI_OK;
+  if (!blocks || !w_out) return PESTI_ERR_NULL;
+  if (!pesti_host::aligned(blocks, 16) || !pesti_host::aligned(w_out, 16)) return PESTI_ERR_ALIGN;
+  int dev = 0;
+  size_t lds = 0;
+  const int st = pesti_host::current_device(&dev, &lds);
+  if (st != PESTI_OK) return st;
+  const int64_t n = rows * in_features;
+  pesti::DequantArgs a{static_cast<const uint8_t*>(blocks), nullptr, w_out, 1, n, (n + 255) / 256 * 144};
+  const int64_t threads = n / 32;
+  void* params[] = {&a};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::dequant_q4_k_kernel),
+                                       dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), params,
+                                       0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+}
+
 int pesti_dequant_q2_k(int64_t rows, int64_t in_features, const void* blocks, float* w_out,
                        void* stream) {
   return dequant_launch(pesti::dequant_q2_k_kernel, rows, in_features, blocks, nullptr, w_out, stream,

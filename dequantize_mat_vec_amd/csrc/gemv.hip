@@ -41,6 +41,7 @@ int pesti_gemv_group(int32_t format, int32_t n_ops, const pesti_gemv_op* ops, in
   switch (format) {
     case PESTI_FMT_Q8_0: return pesti_gemv::group_q8_0(n_ops, ops, batch, stream);
     case PESTI_FMT_Q4_K: return pesti_gemv::group_q4_k(n_ops, ops, batch, stream);
+    case PESTI_FMT_Q4_K_STREAM: return pesti_gemv::group_q4_k_stream(n_ops, ops, batch, stream);
     case PESTI_FMT_Q5_K: return pesti_gemv::group_q5_k(n_ops, ops, batch, stream);
     case PESTI_FMT_Q2_K: return pesti_gemv::group_q2_k(n_ops, ops, batch, stream);
     case PESTI_FMT_Q3_K: return pesti_gemv::group_q3_k(n_ops, ops, batch, stream);
@@ -93,6 +94,12 @@ int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* block
                     float* y, const float* bias, int32_t batch, void* stream) {
   const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);
   return pesti_gemv::group_q4_k(1, &o, batch, stream);
+}
+
+int pesti_gemv_q4_k_stream(int64_t out_features, int64_t in_features, const void* blocks, const float* x,
+                    float* y, const float* bias, int32_t batch, void* stream) {
+  const pesti_gemv_op o = pesti_gemv::make_op(out_features, in_features, blocks, nullptr, x, y, bias);
+  return pesti_gemv::group_q4_k_stream(1, &o, batch, stream);
 }
 
 int pesti_gemv_q2_k(int64_t out_features, int64_t in_features, const void* blocks, const float* x,

@@ -404,6 +404,46 @@ struct FmtQ4_KH {
 };
 
 // ---------------------------------------------------------------------------
+// Q4_K stream layout: the matrix's weights in row-major order cut into
+// 256-weight super-blocks in order (only the last one padded), so a row of
+// `in` weights (in % 64 == 0) starts at run R0 = row * in / 64 of the
+// stream - super-block R0 / 4, run R0 % 4 - and a 896-weight row takes 504
+// bytes instead of the row layout's 576.  Unit u of a row is stream run
+// R0 + u: FmtQ4_K's unit, addressed from the row's first super-block with
+// the row's phase R0 % 4 added (the lane's run, and so its scale gather, is
+// (sub + phase) % 4).  Rows are handled one per lane group (all units of a
+// lane group's rows then share one phase).
+// ---------------------------------------------------------------------------
+struct FmtQ4_KS {
+  static constexpr bool kRowScales = false;
+  static constexpr int kPad = 64;
+  using Raw = FmtQ4_K::Raw;
+  struct Lane {
+    FmtQ4_K::Lane k;
+    int phase;
+  };
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+  __device__ static Lane lane_state(int sub, const GemvArgs& a, int64_t row) {
+    const int phase = static_cast<int>((row * (a.in >> 6)) & 3);
+    return Lane{FmtQ4_K::lane_state((sub + phase) & 3), phase};
+  }
+  __device__ static const uint8_t* row_ptr(const GemvArgs& a, int64_t row) {
+    return a.w + ((row * (a.in >> 6)) >> 2) * 144;
+  }
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, const Lane& L, Raw& r) {
+    FmtQ4_K::issue(rp, u + L.phase, r);
+  }
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const Lane& L, float* acc) {
+    FmtQ4_K::compute<B, R>(a, r, u, xs, L.k, acc);
+  }
+};
+
+template <class F>
+constexpr bool kStreamLayout = std::is_same<F, FmtQ4_KS>::value;
+
+// ---------------------------------------------------------------------------
 // Q2_K and Q3_K share a unit: half h and column c of super-block u / 4
 // (h = (u >> 1) & 1, c = u & 1), i.e. code bytes 32h + 16c .. +15 of the
 // super-block, whose bits 2j, 2j+1 hold weights 128h + 32j + 16c + [0, 16)
@@ -896,9 +936,11 @@ struct AccScale<F, std::void_t<decltype(F::kAccScale)>> { static constexpr float
 
 template <class F>
 __device__ __forceinline__ void issue_unit(const GemvArgs& a, const uint8_t* rp, int u,
-                                           typename F::Raw& r) {
+                                           const typename F::Lane& ls, typename F::Raw& r) {
   if constexpr (std::is_same<F, FmtI8Row>::value) {
     F::issue_n(rp, u, a.in, r);
+  } else if constexpr (kStreamLayout<F>) {
+    F::issue(rp, u, ls, r);
   } else {
     F::issue(rp, u, r);
   }
@@ -1019,6 +1061,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   constexpr int kRowsPerTile = kTileRows<L, R, P>;
   static_assert(R == 1 || L < 64 || U == 1, "several rows per lane group need short rows");
   static_assert(!P || (R == 1 && L < 64) || R == 2, "paired rows: lane-group pairs or two rows per group");
+  static_assert(!kStreamLayout<F> || (R == 1 && !P), "stream rows: one row per lane group, unpaired");
 
   // blockIdx.y picks the op, so the op's arguments are read without first
   // scanning the group.  All of its fields are loaded before the first
@@ -1039,16 +1082,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   const int sub = lane & (L - 1);
   const int rofs = wave * kRowsPerWave + lane / L;   // row within a slab
   const int ipt = static_cast<int>((a.units + L - 1) / L);
-  const typename F::Lane ls = F::lane_state(sub);
   // Row k of the lane sits rofs + k * kRowsPerSlab rows past the tile's
   // first row; rows past the end read the first row instead.  Offsets
   // within a tile fit 24 bits (at most 256 rows of at most 34816 bytes).
   const uint8_t* tile_base = a.w + first * a.row_bytes;
   const int64_t left = a.out - first;
+  const typename F::Lane ls = [&]() {
+    if constexpr (kStreamLayout<F>) return F::lane_state(sub, a, first + (rofs < left ? rofs : 0));
+    else return F::lane_state(sub);
+  }();
   const uint8_t* rp[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    if constexpr (P && R == 1) {   // even lane groups: gate row rofs / 2; odd: up row
+    if constexpr (kStreamLayout<F>) {   // one row per lane group (R = 1)
+      rp[k] = F::row_ptr(a, first + (rofs < left ? rofs : 0));
+    } else if constexpr (P && R == 1) {   // even lane groups: gate row rofs / 2; odd: up row
       const int pr = rofs >> 1;
       const uint8_t* base = ((rofs & 1) ? a.w2 : a.w) + first * a.row_bytes;
       rp[k] = base + (pr < left ? __umul24(static_cast<uint32_t>(pr),
@@ -1119,11 +1167,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
       // the x stores below wait for x alone.
       have[j] = j < ipt && live(j);
 #pragma unroll
-      for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), r[j][k]);
+      for (int k = 0; k < R; ++k) issue_unit<F>(a, rp[k], unit(j), ls, r[j][k]);
     }
   } else if constexpr (kWalk) {
-    issue_unit<F>(a, rp[0], unit(0), r[0][0]);
-    issue_unit<F>(a, rp[0], unit(1), rb[0]);
+    issue_unit<F>(a, rp[0], unit(0), ls, r[0][0]);
+    issue_unit<F>(a, rp[0], unit(1), ls, rb[0]);
   }
   epilogue_loads();
   if constexpr (kEarly) stage_store<B, XS>(a, xs, 0, xc);
@@ -1140,9 +1188,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
     for (int j = 0; j < ipt; j += 2) {
       if (live(j)) F::template compute<B, 1>(a, r[0], sub + L * j, xs, ls, acc);
       if (j + 1 >= ipt) break;
-      issue_unit<F>(a, rp[0], unit(j + 2), r[0][0]);
+      issue_unit<F>(a, rp[0], unit(j + 2), ls, r[0][0]);
       if (live(j + 1)) F::template compute<B, 1>(a, rb, sub + L * (j + 1), xs, ls, acc);
-      issue_unit<F>(a, rp[0], unit(j + 3), rb[0]);
+      issue_unit<F>(a, rp[0], unit(j + 3), ls, rb[0]);
     }
   }
 #pragma unroll
@@ -1252,7 +1300,9 @@ constexpr int64_t kMinTiles = PESTI_MIN_TILES;
 template <class F, int L>
 int launch_r(const GroupArgs& g, int64_t max_out, int batch, size_t lds, hipStream_t st) {
   const int64_t tiles1 = (max_out + 4 * (64 / L) - 1) / (4 * (64 / L));
-  if (batch >= 2 && tiles1 >= 2 * kMinTiles) return launch_b<F, L, 1, 2>(g, batch, lds, st);
+  if constexpr (!pesti::kStreamLayout<F>) {
+    if (batch >= 2 && tiles1 >= 2 * kMinTiles) return launch_b<F, L, 1, 2>(g, batch, lds, st);
+  }
   return launch_b<F, L, 1, 1>(g, batch, lds, st);
 }
 
@@ -1287,6 +1337,9 @@ template <> inline void shape_of<pesti::FmtQ4_K>(int64_t in, int64_t* rb, int64_
 template <> inline void shape_of<pesti::FmtQ4_KH>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 144; *u = 2 * ((in + 63) / 64);
 }
+template <> inline void shape_of<pesti::FmtQ4_KS>(int64_t in, int64_t* rb, int64_t* u) {
+  *rb = 0; *u = in / 64;   // rows have no fixed stride: FmtQ4_KS::row_ptr
+}
 template <> inline void shape_of<pesti::FmtQ2_K>(int64_t in, int64_t* rb, int64_t* u) {
   *rb = ((in + 255) / 256) * 84; *u = ((in + 127) / 128) * 2;
 }
@@ -1316,6 +1369,7 @@ int check_op(const pesti_gemv_op& o, int32_t batch) {
   if (o.out_features < 0 || o.in_features < 0) return PESTI_ERR_SHAPE;
   if (o.out_features == 0 || batch == 0) return 1;
   if (o.in_features % 32 != 0 || o.in_features > PESTI_MAX_IN_FEATURES) return PESTI_ERR_SHAPE;
+  if (pesti::kStreamLayout<F> && o.in_features % 64 != 0) return PESTI_ERR_SHAPE;   // rows of whole runs
   const bool has_in = o.in_features > 0;
   if (!o.y || (has_in && (!o.w || !o.x))) return PESTI_ERR_NULL;
   if (F::kRowScales && has_in && !o.row_scales) return PESTI_ERR_NULL;
@@ -1584,6 +1638,7 @@ namespace pesti_gemv {
 // (gemv_<format>.hip) so the kernels of the four formats compile in parallel.
 int group_q8_0(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q4_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
+int group_q4_k_stream(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q2_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q3_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);
 int group_q5_k(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void* stream);

@@ -186,15 +186,21 @@ GPT2_LINEARS = (
 )
 
 
-def decode_step_calls(layers: int = QWEN_LAYERS):
+def decode_step_calls(layers: int = QWEN_LAYERS, layout: str = "rows"):
     """The decode step's mat-vec calls in stream order:
     [(layer, name, fmt, out, in, has_bias)].  Every layer's projections are
     Q4_K, except that the FFN down projection is Q6_K on even layers
-    (0, 2, ..., 22); the step ends with the tied Q8_0 LM head."""
+    (0, 2, ..., 22); the step ends with the tied Q8_0 LM head.  With layout
+    "stream" the Q4_K matrices of rows that are not whole super-blocks (the
+    896-column Q, K, V, O, gate and up) are in the Q4_K stream layout."""
+    if layout not in ("rows", "stream"):
+        raise ValueError(f"unknown layout {layout!r}")
     calls = []
     for layer in range(layers):
         for name, out, inp, has_bias in QWEN_LAYER_CALLS:
             fmt = "q6_k" if (name == "down" and layer % 2 == 0) else "q4_k"
+            if fmt == "q4_k" and layout == "stream" and inp % 256:
+                fmt = "q4_k_stream"
             calls.append((layer, name, fmt, out, inp, has_bias))
     calls.append((layers, "lm_head", "q8_0", QWEN_VOCAB, QWEN_HIDDEN, False))
     return calls

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PESTI_ABI_VERSION 1
+#define PESTI_ABI_VERSION 2
 
 #define PESTI_OK 0
 #define PESTI_ERR_NULL (-1)   /* a required pointer is NULL                 */
@@ -95,6 +95,7 @@ extern "C" {
 #define PESTI_FMT_Q2_K 5
 #define PESTI_FMT_Q3_K 6
 #define PESTI_FMT_I4ROW 7
+#define PESTI_FMT_Q4_K_STREAM 8
 
 #define PESTI_MAX_BATCH 8
 #define PESTI_MAX_IN_FEATURES 32768
@@ -122,6 +123,22 @@ int pesti_gemv_q8_0(int64_t out_features, int64_t in_features, const void* block
 int pesti_gemv_q4_k(int64_t out_features, int64_t in_features, const void* blocks,
                     const float* x, float* y, const float* bias, int32_t batch,
                     void* stream);
+
+/* Q4_K in the stream layout: the byte-minimal layout of rows that are not a
+ * whole number of super-blocks (the 896-weight rows of "PESTI ..." README,
+ * "Conformance": hidden size 896 is 3.5 super-blocks).  The matrix's
+ * weights in row-major order, weight (r, c) at position r * in + c of one
+ * stream, are cut into 144-byte Q4_K super-blocks in stream order; only the
+ * last super-block holds padding.  `blocks` is pesti_matrix_bytes(
+ * PESTI_FMT_Q4_K_STREAM, out_features, in_features) bytes: a 896-weight row
+ * takes 504 bytes instead of 576, and rows start at weight 0 or 128 of a
+ * super-block.  in_features must be a multiple of 64 (rows of whole 64-weight
+ * runs), else PESTI_ERR_SHAPE; for multiples of 256 the layout is the row
+ * layout of pesti_gemv_q4_k byte for byte.  Same arguments and bound as
+ * pesti_gemv_q4_k; every batch runs on the vector ALUs. */
+int pesti_gemv_q4_k_stream(int64_t out_features, int64_t in_features, const void* blocks,
+                           const float* x, float* y, const float* bias, int32_t batch,
+                           void* stream);
 
 /* Q2_K (84-byte) and Q3_K (110-byte) super-blocks of 256 weights, rows
  * padded to whole super-blocks ("PESTI ..." README, "What This Is": all
@@ -279,6 +296,8 @@ int pesti_dequant_q8_0(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q4_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
+int pesti_dequant_q4_k_stream(int64_t rows, int64_t in_features, const void* blocks,
+                              float* w_out, void* stream);
 int pesti_dequant_q2_k(int64_t rows, int64_t in_features, const void* blocks,
                        float* w_out, void* stream);
 int pesti_dequant_q3_k(int64_t rows, int64_t in_features, const void* blocks,
@@ -305,9 +324,16 @@ int pesti_stream_read(const void* buf, int64_t bytes, uint32_t* partial, void* s
 /* --- host-only helpers (no device work) --------------------------------- */
 
 /* Packed bytes per row for a PESTI_FMT_* format (code bytes only for
- * i8row); -1 for an unknown format or a negative / non-multiple-of-32
- * in_features. */
+ * i8row); -1 for an unknown format, a negative / non-multiple-of-32
+ * in_features, or PESTI_FMT_Q4_K_STREAM (whose rows have no fixed size:
+ * see pesti_matrix_bytes). */
 int64_t pesti_row_bytes(int32_t format, int64_t in_features);
+
+/* Packed bytes of a whole matrix of `rows` rows: rows * pesti_row_bytes for
+ * the row layouts, the super-blocks holding rows * in_features weights for
+ * PESTI_FMT_Q4_K_STREAM (in_features a multiple of 64); -1 for an unknown
+ * format or an invalid size. */
+int64_t pesti_matrix_bytes(int32_t format, int64_t rows, int64_t in_features);
 
 /* Static text for a status code. */
 const char* pesti_strerror(int status);

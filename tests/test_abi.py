@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version():
-    assert dmv.pesti_abi_version() == 1
+    assert dmv.pesti_abi_version() == 2
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row"])
@@ -189,7 +189,9 @@ def test_group_argument_checks():
     ops = _lib.gemv_ops([(8, 64, FAKE, FAKE, FAKE, None, None)] * 2)
     ptr = ctypes.cast(ops, ctypes.c_void_p)
     assert lib.pesti_gemv_group(0, 9, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
-    assert lib.pesti_gemv_group(8, 2, ptr, 1, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_gemv_group(9, 2, ptr, 1, None) == _lib.PESTI_ERR_SHAPE   # unknown format
+    half_run = _lib.gemv_ops([(8, 96, FAKE, FAKE, FAKE, None, None)])       # 96 % 64 != 0
+    assert lib.pesti_gemv_group(8, 1, ctypes.cast(half_run, ctypes.c_void_p), 1, None) == _lib.PESTI_ERR_SHAPE
     assert lib.pesti_gemv_group(7, 2, ptr, 1, None) == _lib.PESTI_ERR_NULL   # i4row without row scales
     assert lib.pesti_gemv_group(1, 2, None, 1, None) == _lib.PESTI_ERR_NULL
     assert lib.pesti_gemv_group(1, 2, ptr, 9, None) == _lib.PESTI_ERR_BATCH
@@ -246,3 +248,31 @@ def test_stream_read_argument_checks():
     assert lib.pesti_stream_read(FAKE, 64, part + 2, None) == _lib.PESTI_ERR_ALIGN
     m = re.search(r"#define PESTI_READ_GROUPS (\d+)", HEADER.read_text())
     assert int(m.group(1)) == _lib.READ_GROUPS
+
+
+def test_matrix_bytes():
+    """Whole-matrix sizes: rows * row bytes for the row layouts; the stream
+    layout holds rows * in weights in whole 144-byte super-blocks (896-weight
+    rows: 504 bytes each, the last super-block padded)."""
+    assert dmv.pesti_matrix_bytes("q4_k", 3, 896) == 3 * 576
+    assert dmv.pesti_matrix_bytes("q4_k_stream", 2, 896) == 1008
+    assert dmv.pesti_matrix_bytes("q4_k_stream", 3, 896) == 11 * 144
+    assert dmv.pesti_matrix_bytes("q4_k_stream", 4864, 896) == 4864 * 504
+    assert dmv.pesti_matrix_bytes("q4_k_stream", 5, 4864) == 5 * oracle_row_bytes_q4_k(4864)
+    assert dmv.pesti_matrix_bytes("q4_k_stream", 3, 96) == -1
+    assert dmv.pesti_row_bytes("q4_k_stream", 896) == -1
+    assert dmv.pesti_matrix_bytes("i8row", 4, 64) == 256
+    assert dmv.pesti_matrix_bytes(99, 4, 64) == -1
+
+
+def oracle_row_bytes_q4_k(inf):
+    return -(-inf // 256) * 144
+
+
+def test_stream_dequant_argument_checks():
+    lib = _raw()
+    assert lib.pesti_dequant_q4_k_stream(2, 96, FAKE, FAKE, None) == _lib.PESTI_ERR_SHAPE
+    assert lib.pesti_dequant_q4_k_stream(0, 896, FAKE, FAKE, None) == _lib.PESTI_OK
+    assert lib.pesti_dequant_q4_k_stream(2, 896, None, FAKE, None) == _lib.PESTI_ERR_NULL
+    assert lib.pesti_dequant_q4_k_stream(2, 896, FAKE + 4, FAKE, None) == _lib.PESTI_ERR_ALIGN
+    assert lib.pesti_gemv_q4_k_stream(4, 96, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE

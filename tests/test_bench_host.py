@@ -110,6 +110,41 @@ def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
     assert json.load(open(tmp_path / "pmc.txt"))["source_sha256"] == bench.source_digest()
 
 
+def test_read_request_bytes_count_each_size(tmp_path, monkeypatch):
+    """The request-size pass sums 32 n32 + 64 n64 + 128 n128 per dispatch
+    (three counter rows of one dispatch), median per kernel shape, with no
+    scaling; the copy's sum is reported against its size."""
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(tmp_path / "pmc.txt"))
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    simple = tmp_path / "s.csv"
+    with open(simple, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": "512",
+                    "Counter_Name": "FETCH_SIZE", "Counter_Value": 262144.0})
+    req = tmp_path / "r.csv"
+    copy_n128 = 256 * (1 << 20) // 128
+    kernel = "void pesti::gemv_kernel<pesti::FmtQ4_KS, 16, 1, 1, 1, false>(x)"
+    with open(req, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for name, val in (("TCC_EA0_RDREQ_32B_sum", 0), ("TCC_EA0_RDREQ_64B_sum", 0),
+                          ("TCC_EA0_RDREQ_128B_sum", copy_n128)):
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": "512",
+                        "Counter_Name": name, "Counter_Value": val})
+        for disp, (n32, n64, n128) in ((2, (1, 2, 10)), (3, (3, 0, 20)), (4, (0, 0, 1))):
+            for name, val in (("TCC_EA0_RDREQ_32B_sum", n32), ("TCC_EA0_RDREQ_64B_sum", n64),
+                              ("TCC_EA0_RDREQ_128B_sum", n128)):
+                w.writerow({"Dispatch_Id": disp, "Kernel_Name": kernel, "Grid_Size": "14336",
+                            "Counter_Name": name, "Counter_Value": val})
+    out = bench.summarize_pmc(str(simple), str(simple), str(req), calib_mib=256)
+    assert out["calibration"]["read_requests"]["ratio_to_copy_size"] == 1.0
+    (key, d), = out["kernels"].items()
+    assert key.endswith("grid=14336")
+    # dispatch sums 32 + 128 + 1280 = 1440, 96 + 2560 = 2656, 128: median 1440
+    assert d["read_request_bytes"] == 1440
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
@@ -158,7 +193,7 @@ def test_parity_leg_accepts_rounded_oracle_and_rejects_a_planted_error(tmp_path,
     # and the head
     sample_calls = list(range(len(calls)))
     ys = _oracle_outputs(calls, sample_calls)
-    monkeypatch.setattr(synth, "decode_step_calls", lambda layers=2: calls)
+    monkeypatch.setattr(synth, "decode_step_calls", lambda layers=2, layout="rows": calls)
     sample = bench.parity_sample(calls, ys)
     assert sorted(sample) == sample_calls
     head_rows = sample[len(calls) - 1][0]
@@ -189,3 +224,20 @@ def test_parity_sample_skips_the_fused_calls():
     ys = [_HostY(np.zeros(c[3], np.float32)) for c in calls]
     sample = bench.parity_sample(calls, ys, ("gate", "up", "down"))
     assert all(calls[i][1] not in ("gate", "up", "down") for i in sample)
+
+
+def test_stream_layout_step_keeps_the_plan_and_the_nominal_bytes():
+    """With the stream layout the 896-column Q4_K calls change format only:
+    same launches, same nominal bytes per step (the stored bytes shrink)."""
+    rows = synth.decode_step_calls()
+    stream = synth.decode_step_calls(layout="stream")
+    assert [c[:2] + c[3:] for c in rows] == [c[:2] + c[3:] for c in stream]
+    changed = [c for c in stream if c[2] == "q4_k_stream"]
+    assert {c[1] for c in changed} == {"q", "k", "v", "o", "gate", "up"} and len(changed) == 24 * 6
+    assert len(bench.plan_launches(stream, "stage")) == 97
+    assert (sum(bench.call_bytes(f, o, i, 1, b) for _, _, f, o, i, b in rows)
+            == sum(bench.call_bytes(f, o, i, 1, b) for _, _, f, o, i, b in stream))
+
+
+def test_stream_kernel_label():
+    assert bench.kernel_name("q4_k_stream", [896], [896]) == "gemv_kernel<q4_k_stream, L=16, B=1, R=1>"

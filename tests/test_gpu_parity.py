@@ -1129,3 +1129,103 @@ def test_tall_q4_k_batch_1_full_lm_head_sampled_rows():
     rows = np.unique(np.concatenate([rng.integers(0, out, 2048), [0, out - 1]]))
     y_ref, s_ref = oracle.gemv_packed("q4_k", packed.reshape(out, -1)[rows], len(rows), inf, x, bias[rows])
     assert_within(y[:, rows], y_ref, s_ref, GEMV_REL, "q4_k lm head b1")
+
+
+# ---------------------------------------------------------------------------
+# Q4_K stream layout (the byte-minimal layout of 896-weight rows)
+# ---------------------------------------------------------------------------
+STREAM_DEQUANT = [(2, 128), (3, 384), (7, 896), (33, 896), (5, 4864), (1, 64), (9, 192)]
+
+
+@pytest.mark.parametrize("rows,inf", STREAM_DEQUANT)
+def test_stream_dequant_bit_exact(rows, inf):
+    rng = np.random.default_rng([160, rows, inf])
+    packed = synth.stream_blocks(rng, rows, inf)
+    got = run_dequant("q4_k_stream", packed, None, rows, inf)
+    assert np.array_equal(got, oracle.dequantize_f32("q4_k_stream", packed, rows, inf))
+
+
+STREAM_GEMV = [(67, 896, 1), (67, 896, 3), (67, 896, 8), (1152, 896, 1), (4864, 896, 1), (300, 64, 1),
+               (37, 192, 2), (130, 4864, 2), (11, 20480, 1), (MFMA_ROWS + 37, 896, 1), (MFMA_ROWS + 37, 896, 4)]
+
+
+@pytest.mark.parametrize("out,inf,batch", STREAM_GEMV)
+def test_stream_gemv_parity(out, inf, batch):
+    rng = np.random.default_rng([161, out, inf, batch])
+    packed = synth.stream_blocks(rng, out, inf)
+    x = synth.activations(rng, batch, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"q4_k_stream {out}x{inf} b{batch}")
+
+
+def test_stream_one_hot_x_gives_dequantized_column():
+    out, inf = 129, 896
+    rng = np.random.default_rng(162)
+    packed = synth.stream_blocks(rng, out, inf)
+    w32 = oracle.dequantize_f32("q4_k_stream", packed, out, inf)
+    cols = [0, 1, 127, 128, 255, 256, 640, 895]
+    x = np.zeros((8, inf), np.float32)
+    for b, j in enumerate(cols):
+        x[b, j] = 1.0
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x)
+    for b, j in enumerate(cols):
+        assert np.array_equal(y[b], w32[:, j]), j
+
+
+def test_stream_padding_at_the_end_does_not_matter():
+    out, inf = 45, 896           # 40320 weights: 157.5 super-blocks, the last half padding
+    rng = np.random.default_rng(163)
+    packed = synth.stream_blocks(rng, out, inf)
+    other = packed.copy()
+    other[-64:] = rng.integers(0, 256, 64, dtype=np.uint8)     # runs 2-3 of the last block
+    other[-144 + 12:-144 + 16] = rng.integers(0, 256, 4, dtype=np.uint8)   # sub-blocks 4-7's scale bytes
+    x = synth.activations(rng, 2, inf)
+    assert np.array_equal(run_gemv("q4_k_stream", packed, None, out, inf, x),
+                          run_gemv("q4_k_stream", other, None, out, inf, x))
+
+
+def test_stream_forced_scales():
+    for d_bits in (0x0000, 0x0001, 0x0400, 0x7BFF):
+        rng = np.random.default_rng([164, d_bits])
+        out, inf = 23, 896
+        packed = synth.stream_blocks(rng, out, inf, force_d=d_bits)
+        x = synth.activations(rng, 1, inf)
+        y = run_gemv("q4_k_stream", packed, None, out, inf, x)
+        y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x)
+        assert_within(y, y_ref, s_ref, GEMV_REL, f"stream d={d_bits:#x}")
+
+
+def test_stream_group_equals_single_calls_bitwise():
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for n, (out, inf) in enumerate([(896, 896), (128, 896), (128, 896), (33, 4864)]):
+        rng = np.random.default_rng([165, n])
+        packed = synth.stream_blocks(rng, out, inf)
+        x, bias = synth.activations(rng, 1, inf), synth.bias(rng, out)
+        singles.append(run_gemv("q4_k_stream", packed, None, out, inf, x, bias))
+        w, xd, bd = to_dev(packed), to_dev(x), to_dev(bias)
+        yd = torch.zeros(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w, xd, yd, bd, None))
+    dmv.pesti_gemv_group("q4_k_stream", ops, 1)
+    torch.cuda.synchronize()
+    for (out, inf, w, xd, yd, bd, _), y1 in zip(ops, singles):
+        assert np.array_equal(yd.cpu().numpy(), y1[0])
+
+
+def test_stream_exact_cancellation_gives_bias():
+    """Stream rows whose weights are all exactly zero (every sub-block's
+    codes one constant c with d sc c = dmin m)."""
+    out, inf = 40, 896
+    rng = np.random.default_rng(166)
+    nsb = -(-out * inf // 256)
+    packed = _cancelling_row("q4_k", rng, nsb)
+    assert not np.any(oracle.dequantize("q4_k_stream", packed, out, inf))
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, "stream cancelling")

@@ -167,3 +167,41 @@ def test_decode_step_fused_swiglu_matches_oracle(step_setup):
             torch.cuda.synchronize()
             check(f"fused SwiGLU graph replay {rep}")
     del g
+
+
+def test_decode_step_stream_layout_matches_oracle():
+    """The step with the 896-column Q4_K matrices in the byte-minimal stream
+    layout (504 bytes per row): eager, then two graph replays, all 169
+    outputs against the oracle."""
+    import torch
+    import bench
+    import dequantize_mat_vec_amd as dmv
+    from dequantize_mat_vec_amd import synth
+    announce("decode step (stream layout): inputs and the oracle's outputs")
+    calls = synth.decode_step_calls(layout="stream")
+    host = bench.host_inputs(calls)
+    with ThreadPoolExecutor(8) as ex:
+        refs = list(ex.map(lambda i: _oracle_call(calls[i], host[i]), range(len(calls))))
+    lib = dmv.load()
+    calls, weights, xs, ys, biases = bench.build_inputs(1, calls, host)
+    st = dict(calls=calls, ys=ys, refs=refs)
+    launches = bench.plan_launches(calls, "stage")
+    step = bench.make_step(lib, calls, launches, weights, xs, ys, biases)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        announce("decode step (stream layout): eager")
+        _poison(ys)
+        step(0, stream.cuda_stream)
+        torch.cuda.synchronize()
+        _check_all(st, "stream layout eager")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            announce(f"decode step (stream layout): graph replay {rep}")
+            _poison(ys)
+            g.replay()
+            torch.cuda.synchronize()
+            _check_all(st, f"stream layout graph replay {rep}")
+    del g
