@@ -270,6 +270,12 @@ def suite_cases():
             for fmt in ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k"):
                 cases.append((f"{fmt} gemm {label} {n}x{k} m{m}", "qgemm", (fmt, m, n, k)))
             cases.append((f"f16 gemm {label} {n}x{k} m{m}", "gemm", (m, k, n)))
+    # the Q4_K shapes of 896-weight rows again in the stream layout (504
+    # bytes per row, no padding); appended so that earlier cases keep their
+    # seeds
+    cases += [("q4_k_stream lm-head 151936x896 b1", "gemv", ("q4_k_stream", synth.QWEN_VOCAB, 896, 1)),
+              ("q4_k_stream 4864x896 b1 (gate/up)", "gemv", ("q4_k_stream", 4864, 896, 1)),
+              ("q4_k_stream 4864x896 b1 (gate/up) x8 grouped", "group", ("q4_k_stream", 4864, 896, 8))]
     return cases
 
 

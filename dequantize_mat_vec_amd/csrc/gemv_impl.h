@@ -1431,19 +1431,23 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
          a.in > 0 && a.in <= 1024;
 }
 // Tall Q4_K matrices with rows of at most 1024 weights at batch 1 take the
-// batch-1 kernel of gemv_tall.hip (128-weight units, a row per U lanes).
+// batch-1 kernel of gemv_tall.hip (128-weight units, a row per U lanes); in
+// the stream layout only rows of a whole number of 128-weight units, so
+// that no unit straddles two super-blocks.
 #ifndef PESTI_TALL_MIN_ROWS
 #define PESTI_TALL_MIN_ROWS 16384
 #endif
 constexpr int64_t kTallMinRows = PESTI_TALL_MIN_ROWS;
 template <class F>
+constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || pesti::kStreamLayout<F>;
+template <class F>
 inline bool tall_op(const GemvArgs& a, int batch) {
-  return std::is_same<F, pesti::FmtQ4_K>::value && batch == 1 && a.out >= kTallMinRows && a.in > 0 &&
-         a.in <= 1024;
+  return kHasTall<F> && batch == 1 && a.out >= kTallMinRows && a.in > 0 && a.in <= 1024 &&
+         (!pesti::kStreamLayout<F> || a.in % 128 == 0);
 }
 // One launch of ops that all pass tall_op and share one row length in
 // 128-weight units; x and y of every op set.
-int launch_tall_q4_k(const GroupArgs& g, hipStream_t st);
+int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st);
 
 // One launch of ops that all pass mfma_op and share one row length in
 // super-blocks; x and y of every op set.
@@ -1524,7 +1528,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     if (r != PESTI_OK) return r;
   }
   if (n_mv == 0) return PESTI_OK;
-  if constexpr (std::is_same<F, pesti::FmtQ4_K>::value) {
+  if constexpr (kHasTall<F>) {
     // Tall batch-1 ops leave the group: one launch per row length in
     // 128-weight units.
     GroupArgs rest{};
@@ -1542,7 +1546,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
         t.op[t.n_ops].y = ops[live[j]].y;
         ++t.n_ops;
       }
-      const int r = launch_tall_q4_k(t, stream_h);
+      const int r = launch_tall_q4_k(t, pesti::kStreamLayout<F>, stream_h);
       if (r != PESTI_OK) return r;
     }
     max_units = 0;

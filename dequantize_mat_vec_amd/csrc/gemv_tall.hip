@@ -32,14 +32,19 @@ constexpr int kTallWaves = PESTI_TALL_WAVES;
 constexpr int kTallThreads = kTallWaves * kWave;
 constexpr int kTallMaxIn = 1024;
 
-// One lane's unit u of a row: runs 2(u % 2) and 2(u % 2) + 1 of super-block
-// u / 2 (sub-blocks 4(u % 2) .. +3), weights 128u .. 128u + 127.
+// One lane's 128-weight unit: runs 2h and 2h + 1 (sub-blocks 4h .. 4h + 3)
+// of one super-block.  In the row layout unit u of a row is half h = u % 2
+// of the row's super-block u / 2, weights 128u .. 128u + 127; in the stream
+// layout (rows of a whole number of units) it is stream unit g = row U + u,
+// half g % 2 of stream super-block g / 2, again weights 128u .. of the row.
 struct TallQ4K {
   struct Raw { u32x4 hdr, c0, c1, c2, c3; };
 
-  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, Raw& r) {
-    const uint8_t* sb = rp + (u >> 1) * 144;
-    const uint8_t* cp = sb + 16 + 64 * (u & 1);
+  // g: the unit's index in 128-weight units from `base` (a row's start in
+  // the row layout, the matrix's in the stream layout).
+  __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
+    const uint8_t* sb = base + (g >> 1) * 144;
+    const uint8_t* cp = sb + 16 + 64 * (g & 1);
     r.hdr = load_u32x4_a16(sb);
     r.c0 = load_u32x4_a16(cp);
     r.c1 = load_u32x4_a16(cp + 16);
@@ -58,13 +63,13 @@ struct TallQ4K {
     }
   }
 
-  // acc += sum over the unit's 128 weights of w * x.  Sub-block 4h + t
-  // (h = u % 2): t = 0..3 for h = 0 take sc = S[t] & 63, m = S[t + 4] & 63;
-  // for h = 1 sc = (S[t + 8] & 15) | (S[t] >> 6) << 4, m = (S[t + 8] >> 4) |
-  // (S[t + 4] >> 6) << 4 (S = header bytes 4..15, dwords y, z, w).
-  __device__ __forceinline__ static float compute(const Raw& r, int u, const float* xs) {
+  // acc += sum over the unit's 128 weights of w * x (x from logical
+  // column 128u of the row).  Sub-block 4h + t: t = 0..3 for h = 0 take
+  // sc = S[t] & 63, m = S[t + 4] & 63; for h = 1 sc = (S[t + 8] & 15) |
+  // (S[t] >> 6) << 4, m = (S[t + 8] >> 4) | (S[t + 4] >> 6) << 4 (S = header
+  // bytes 4..15, dwords y, z, w).
+  __device__ __forceinline__ static float compute(const Raw& r, int u, bool h1, const float* xs) {
     const uint32_t y = r.hdr.y, z = r.hdr.z, w = r.hdr.w;
-    const bool h1 = (u & 1) != 0;
     const uint32_t scv = h1 ? ((w & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u)) : (y & 0x3F3F3F3Fu);
     const uint32_t mv = h1 ? (((w >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u)) : (z & 0x3F3F3F3Fu);
     const float d512 = f16_lo(r.hdr.x) * 512.0f, dmin = f16_hi(r.hdr.x);
@@ -97,12 +102,16 @@ struct TallQ4K {
   }
 };
 
-// U = 128-weight units per row (rows of up to 128 U weights, padded to
-// whole super-blocks); a wave serves 64 / U rows, a workgroup kTallWaves
-// times that.  Measured and not taken: two or four row groups per wave with
-// all their loads in flight at once (24.2 / 36.0 us), and register caps of
-// 80 or 64 VGPRs for more waves per SIMD (26.8 us; 46.6 us with spills).
-template <int U>
+// U = 128-weight units per row (row layout: rows of up to 128 U weights,
+// padded to whole super-blocks; stream layout, S: rows of exactly 128 U);
+// a wave serves 64 / U rows, a workgroup kTallWaves times that.  Measured
+// and not taken: two or four row groups per wave with all their loads in
+// flight at once (24.2 / 36.0 us), register caps of 80 or 64 VGPRs for
+// more waves per SIMD (26.8 us; 46.6 us with spills), and workgroups that
+// take 2, 4 or 8 row blocks in turn with the next block's loads issued
+// before the current block's arithmetic (in one run: 23.2 us for one block against
+// 24.0 / 26.5 / 33.2: fewer workgroups keep fewer loads in flight).
+template <int U, bool S>
 __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g) {
   __shared__ float xs[xs_phys(kTallMaxIn)];
   constexpr int kRowsPerWave = kWave / U;
@@ -130,17 +139,19 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
     const int s = tid + k * kTallThreads;
     xv[k] = reinterpret_cast<const f32x4*>(a.x)[s < in4 ? s : 0];
   }
-  const uint8_t* rp = a.w + (live ? row : first_wg) * a.row_bytes;
+  const int64_t lrow = live ? row : first_wg;
+  const int lu = live ? u : 0;
+  const int64_t gu = S ? lrow * U + lu : lu;
   TallQ4K::Raw r;
-  TallQ4K::issue(rp, live ? u : 0, r);
-  const float bv = *(a.bias ? a.bias + (live ? row : first_wg) : reinterpret_cast<const float*>(rp));
+  TallQ4K::issue(S ? a.w : a.w + lrow * a.row_bytes, gu, r);
+  const float bv = *(a.bias ? a.bias + lrow : reinterpret_cast<const float*>(a.w));
 #pragma unroll
   for (int k = 0; k < kXPer; ++k) {
     const int s = tid + k * kTallThreads;
     if (s < kX4) *reinterpret_cast<f32x4*>(xs + xs_phys(4 * s)) = s < in4 ? xv[k] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
-  const float part = live ? TallQ4K::compute(r, u, xs) : 0.f;
+  const float part = live ? TallQ4K::compute(r, u, (gu & 1) != 0, xs) : 0.f;
   // the row's U partial sums, added in lane order (reads past the wave take
   // the lane's own value; only the row's first lane stores)
   float sum = part;
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
 
 namespace pesti_gemv {
 
-template <int U>
+template <int U, bool S>
 int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   constexpr int64_t kRows = (pesti::kWave / U) * pesti::kTallWaves;
   int64_t max_out = 0;
@@ -161,26 +172,35 @@ int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   const int64_t groups = (max_out + kRows - 1) / kRows;
   GroupArgs args = g;
   void* params[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_q4k_kernel<U>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_q4k_kernel<U, S>),
                                        dim3(static_cast<unsigned>(groups), static_cast<unsigned>(g.n_ops)),
                                        dim3(pesti::kTallThreads), params, 0, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-// One launch of tall batch-1 Q4_K ops that share one row length.
-int launch_tall_q4_k(const GroupArgs& g, hipStream_t st) {
-  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+template <bool S>
+int launch_tall_s(const GroupArgs& g, hipStream_t st) {
   switch ((g.op[0].in + 127) / 128) {
-    case 1: return launch_tall_u<1>(g, st);
-    case 2: return launch_tall_u<2>(g, st);
-    case 3: return launch_tall_u<3>(g, st);
-    case 4: return launch_tall_u<4>(g, st);
-    case 5: return launch_tall_u<5>(g, st);
-    case 6: return launch_tall_u<6>(g, st);
-    case 7: return launch_tall_u<7>(g, st);
-    case 8: return launch_tall_u<8>(g, st);
+    case 1: return launch_tall_u<1, S>(g, st);
+    case 2: return launch_tall_u<2, S>(g, st);
+    case 3: return launch_tall_u<3, S>(g, st);
+    case 4: return launch_tall_u<4, S>(g, st);
+    case 5: return launch_tall_u<5, S>(g, st);
+    case 6: return launch_tall_u<6, S>(g, st);
+    case 7: return launch_tall_u<7, S>(g, st);
+    case 8: return launch_tall_u<8, S>(g, st);
     default: return PESTI_ERR_SHAPE;
   }
+}
+
+// One launch of tall batch-1 Q4_K ops that share one row length; in the
+// stream layout every row is a whole number of 128-weight units.
+int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  if (!stream_layout) return launch_tall_s<false>(g, st);
+  for (int i = 0; i < g.n_ops; ++i)
+    if (g.op[i].in % 128 != 0 || g.op[i].in != g.op[0].in) return PESTI_ERR_SHAPE;
+  return launch_tall_s<true>(g, st);
 }
 
 }  // namespace pesti_gemv

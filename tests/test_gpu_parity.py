@@ -1229,3 +1229,96 @@ def test_stream_exact_cancellation_gives_bias():
     y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
     y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x, bias)
     assert_within(y, y_ref, s_ref, GEMV_REL, "stream cancelling")
+
+
+# ---------------------------------------------------------------------------
+# tall Q4_K matrices in the stream layout at batch 1: the 128-weight-unit
+# kernel when rows are a whole number of units (a unit is then half of one
+# stream super-block), the general stream kernel otherwise
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("inf", [128, 256, 384, 640, 896, 1024, 960, 192])
+def test_tall_stream_batch_1_every_row(inf):
+    out = TALL_ROWS + 37            # odd row count: with 896 the stream ends on a half super-block
+    rng = np.random.default_rng([170, inf])
+    packed = synth.stream_blocks(rng, out, inf)
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall q4_k_stream b1 in={inf}")
+
+
+def test_tall_stream_batch_1_one_hot_gives_dequantized_column():
+    out, inf = TALL_ROWS + 5, 896
+    rng = np.random.default_rng(171)
+    packed = synth.stream_blocks(rng, out, inf)
+    w32 = oracle.dequantize_f32("q4_k_stream", packed, out, inf)
+    for j in (0, 31, 32, 127, 128, 255, 256, 895):
+        x = np.zeros((1, inf), np.float32)
+        x[0, j] = 1.0
+        y = run_gemv("q4_k_stream", packed, None, out, inf, x)
+        assert np.array_equal(y[0], w32[:, j]), j
+
+
+def test_tall_stream_batch_1_padding_at_the_end_does_not_matter():
+    out, inf = TALL_ROWS + 1, 896   # 14681 stream units: the last super-block's second half is padding
+    rng = np.random.default_rng(172)
+    packed = synth.stream_blocks(rng, out, inf)
+    other = packed.copy()
+    other[-64:] = rng.integers(0, 256, 64, dtype=np.uint8)
+    other[-144 + 12:-144 + 16] = rng.integers(0, 256, 4, dtype=np.uint8)
+    x = synth.activations(rng, 1, inf)
+    assert np.array_equal(run_gemv("q4_k_stream", packed, None, out, inf, x),
+                          run_gemv("q4_k_stream", other, None, out, inf, x))
+
+
+def test_tall_stream_batch_1_exact_cancellation_gives_bias():
+    out, inf = TALL_ROWS + 3, 896
+    rng = np.random.default_rng(173)
+    packed = _cancelling_row("q4_k", rng, -(-out * inf // 256))
+    assert not np.any(oracle.dequantize("q4_k_stream", packed, out, inf))
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("q4_k_stream", packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, "tall stream cancelling")
+
+
+def test_tall_stream_batch_1_group_equals_single_calls_bitwise():
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    cases = [(TALL_ROWS + 7, 896), (TALL_ROWS + 100, 896), (TALL_ROWS + 1, 512), (TALL_ROWS + 2, 960),
+             (300, 896)]
+    ops, singles = [], []
+    for n, (out, inf) in enumerate(cases):
+        rng = np.random.default_rng([174, n])
+        packed = synth.stream_blocks(rng, out, inf)
+        x, bias = synth.activations(rng, 1, inf), synth.bias(rng, out)
+        singles.append(run_gemv("q4_k_stream", packed, None, out, inf, x, bias))
+        w, xd, bd = to_dev(packed), to_dev(x), to_dev(bias)
+        yd = torch.zeros(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w, xd, yd, bd, None))
+    dmv.pesti_gemv_group("q4_k_stream", ops, 1)
+    torch.cuda.synchronize()
+    for (out, inf, w, xd, yd, bd, _), y1 in zip(ops, singles):
+        assert np.array_equal(yd.cpu().numpy(), y1[0])
+
+
+def test_tall_stream_batch_1_full_lm_head_sampled_rows():
+    out, inf = synth.QWEN_VOCAB, 896
+    rng = np.random.default_rng([175, out, inf])
+    packed = synth.stream_blocks(rng, out, inf)
+    x = synth.activations(rng, 1, inf)
+    bias = synth.bias(rng, out)
+    y = run_gemv("q4_k_stream", packed, None, out, inf, x, bias)
+    # rows 2k and 2k + 1 share their middle super-block: check sampled pairs
+    # through the oracle on the slice of the stream that holds them
+    # (7 units of 128 weights per row, 2 units per 144-byte super-block)
+    starts = np.unique(np.concatenate([rng.integers(0, out // 2, 512) * 2, [0, out - 2]]))
+    for r0 in starts:
+        sb0 = (r0 * 7) // 2
+        sb1 = -(-((r0 + 2) * 7) // 2)
+        sub = packed[sb0 * 144: sb1 * 144]
+        y_ref, s_ref = oracle.gemv_packed("q4_k_stream", sub, 2, inf, x, bias[r0:r0 + 2])
+        assert_within(y[:, r0:r0 + 2], y_ref, s_ref, GEMV_REL, f"stream lm head rows {r0}, {r0 + 1}")
