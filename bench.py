@@ -53,7 +53,7 @@ def parse_args(argv=None):
     p.add_argument("--copies", type=int, default=2, help="weight copies alternated per step")
     p.add_argument("--grouping", choices=("stage", "none"), default="stage",
                    help="one launch per dependency stage (Q/K/V, O, gate/up, down) or per call")
-    p.add_argument("--layout", choices=("rows", "stream"), default="rows",
+    p.add_argument("--layout", choices=("rows", "stream"), default="stream",
                    help="Q4_K matrices of 896-weight rows in the row layout (whole super-blocks per "
                         "row, 576 bytes) or the byte-minimal stream layout (504 bytes per row)")
     p.add_argument("--ffn", choices=("separate", "swiglu"), default="separate",
@@ -513,13 +513,20 @@ def run_suite_oracle(args):
         env["HIP_VISIBLE_DEVICES"] = ""
         cmd = [sys.executable, os.path.abspath(__file__), "--suite-oracle-leg", "--suite-filter",
                args.suite_filter]
-        out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=1800)
-        if out.returncode != 0:
-            raise RuntimeError(f"suite oracle leg failed: {out.stderr[-2000:]}")
-        for line in out.stdout.splitlines():
-            if line.startswith("{"):
-                r = json.loads(line)
-                res.setdefault(r["case"], []).append(r)
+        # each case's line is echoed to stderr as it arrives (progress of a
+        # leg that can take minutes)
+        with subprocess.Popen(cmd, env=env, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                              text=True) as proc:
+            for line in proc.stdout:
+                if line.startswith("{"):
+                    r = json.loads(line)
+                    res.setdefault(r["case"], []).append(r)
+                    print(f"oracle, {threads} thread(s): {r['case']}: {r['us_per_call']} us", file=sys.stderr,
+                          flush=True)
+            err = proc.stderr.read()
+            rc = proc.wait(timeout=60)
+        if rc != 0:
+            raise RuntimeError(f"suite oracle leg failed: {err[-2000:]}")
     print(json.dumps({"suite_oracle_host": host}), flush=True)
     return {k: tuple(v) for k, v in res.items() if len(v) == 2}
 
@@ -669,9 +676,10 @@ def add_request_bytes(out, path, calib_mib):
         out["kernels"].setdefault(key, {})["read_request_bytes"] = round(statistics.median(vals))
 
 
-def dominant_traffic(kernel_label):
+def dominant_traffic(kernel_label, read_key="fetch_size_bytes"):
     """Average HBM bytes per launch of the dominant kernel from the committed
-    counter summary, or None if it is missing or was taken on other sources."""
+    counter summary (reads by read_key, plus writes), or None if it is
+    missing, lacks that figure or was taken on other sources."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     try:
@@ -687,9 +695,11 @@ def dominant_traffic(kernel_label):
     # one entry per launch shape of the kernel; every shape of the decode step
     # occurs equally often (once per layer), so the per-launch average is
     # the plain mean over shapes
-    vals = [d.get("fetch_size_bytes", 0) + d.get("write_size_bytes", 0)
-            for key, d in summ["kernels"].items() if f"{tag}, {lanes}, 1," in key]
-    return sum(vals) / len(vals) if vals else None
+    shapes = [d for key, d in summ["kernels"].items() if f"{tag}, {lanes}, 1," in key]
+    if not shapes or any(read_key not in d for d in shapes):
+        return None
+    vals = [d[read_key] + d.get("write_size_bytes", 0) for d in shapes]
+    return sum(vals) / len(vals)
 
 
 # ---------------------------------------------------------------------------
@@ -783,14 +793,14 @@ def run_parity(calls, ys, skip_names=(), layout="rows"):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same step
 # ---------------------------------------------------------------------------
-def cpu_leg(seconds):
+def cpu_leg(seconds, layout):
     """Runs in a child process (BLAS/OpenMP threads set by the parent): times
     the oracle (float64 dequantize + dot) on whole calls of the step in
-    stream order (the LM head as a 16384-row slice), passing over the step
-    again until `seconds` of work is done."""
+    stream order (the LM head as a 16384-row slice), with the step's Q4_K
+    layout, passing over the step again until `seconds` of work is done."""
     from dequantize_mat_vec_amd import synth
     import oracle
-    calls = synth.decode_step_calls()
+    calls = synth.decode_step_calls(layout=layout)
     done_bytes, spent, ncalls, passes = 0, 0.0, 0, 0
     first = last = None
     while spent < seconds:
@@ -801,7 +811,7 @@ def cpu_leg(seconds):
             tidx = synth.TENSOR_INDEX[name]
             rng = synth.rng_for(CONFIG_INDEX, layer, tidx)
             rows = min(out, 16384) if name == "lm_head" else out
-            packed = synth.quant_blocks(fmt, rng, rows, inf)
+            packed, _ = synth.matrix(fmt, rng, rows, inf)
             x = synth.activations(synth.rng_for(CONFIG_INDEX, layer, 100 + tidx), 1, inf)
             b = synth.bias(synth.rng_for(CONFIG_INDEX, layer, 200 + tidx), rows) if has_bias else None
             t0 = time.perf_counter()
@@ -828,31 +838,31 @@ def host_cpu():
             "affinity": len(os.sched_getaffinity(0))}
 
 
-def run_cpu_leg(seconds, threads):
+def run_cpu_leg(seconds, threads, layout):
     env = dict(os.environ)
     for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
         env[k] = str(threads)
     env["HIP_VISIBLE_DEVICES"] = ""
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg",
-           "--cpu-sample-seconds", str(seconds)]
+           "--cpu-sample-seconds", str(seconds), "--layout", layout]
     res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
     if res.returncode != 0:
         raise RuntimeError(f"cpu baseline failed: {res.stderr[-2000:]}")
     return json.loads(res.stdout.strip().splitlines()[-1])
 
 
-def run_cpu_baseline(seconds):
+def run_cpu_baseline(seconds, layout):
     """The oracle on the host cores, twice: one BLAS/OpenMP thread (the
     reported value) and the process's whole CPU share (OMP_NUM_THREADS if
     set, else the affinity mask)."""
     host = host_cpu()
     share = int(os.environ.get("OMP_NUM_THREADS") or host["affinity"])
-    one = run_cpu_leg(seconds, 1)
-    many = run_cpu_leg(seconds / 2, share)
+    one = run_cpu_leg(seconds, 1, layout)
+    many = run_cpu_leg(seconds / 2, share, layout)
 
     def sample(r, threads):
         return (f"float64 oracle, {threads} thread(s), {r['calls']} calls of the decode step in "
-                f"stream order ({r['first']} .. {r['last']}, {r['passes']} pass(es)), "
+                f"stream order ({r['first']} .. {r['last']}, {r['passes']} pass(es), Q4_K {layout} layout), "
                 f"{r['bytes']} nominal bytes in {r['seconds']:.1f} s")
     return {"value": round(one["value"], 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": sample(one, 1), "host": host,
@@ -864,7 +874,7 @@ def run_cpu_baseline(seconds):
 def main(argv=None):
     args = parse_args(argv)
     if args.cpu_leg:
-        print(json.dumps(cpu_leg(args.cpu_sample_seconds)))
+        print(json.dumps(cpu_leg(args.cpu_sample_seconds, args.layout)))
         return 0
     if args.parity_leg:
         print(json.dumps(parity_leg(args.parity_leg)))
@@ -999,6 +1009,7 @@ def main(argv=None):
     achieved = bytes_per_launch / avg_s / 1e9
 
     traffic = dominant_traffic(dom_name)
+    traffic_req = dominant_traffic(dom_name, "read_request_bytes")
     ms_per_step = elapsed / args.steps * 1e3
     value = bytes_per_step / (ms_per_step / 1e3) / 1e9
     result = {
@@ -1025,6 +1036,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (None if traffic is None else int(traffic)),
+                     "traffic_by_request_size": (None if traffic_req is None else int(traffic_req)),
                      "bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_us": round(avg_s * 1e6, 3)},
         "kernels": {k: {"launches_per_step": v["launches"] // args.kernel_steps,
@@ -1033,7 +1045,7 @@ def main(argv=None):
                     for k, v in sorted(per_name.items(), key=lambda kv: -kv[1]["ms"])},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = run_cpu_baseline(args.cpu_sample_seconds)
+        result["cpu_baseline"] = run_cpu_baseline(args.cpu_sample_seconds, args.layout)
     else:
         result["cpu_baseline"] = None
     result["parity"] = None if parity is None else parity["ok"]
