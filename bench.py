@@ -553,10 +553,10 @@ def source_digest():
 def run_launch_floor(lib):
     """Per-launch cost of the decode step's dependent launches against their
     floor: a graph of 96 dependent batch-1 Q4_K mat-vecs (896 columns, each
-    launch its own x; weight copies rotated so that one replay touches 96
-    of them - at 896 rows and fewer the copies stay in the last-level cache,
-    at 4864 rows 229 copies exceed it), and a graph of 96 dependent fills
-    of one float (torch's fill kernel: launch and completion only)."""
+    launch its own x; launch i reads weight copy i mod C - at 896 rows and
+    fewer C = 64 copies that stay in the last-level cache, at 4864 rows
+    C = 229 copies that exceed it), and a graph of 96 dependent fills of one
+    float (torch's fill kernel: launch and completion only)."""
     import numpy as np
     import torch
     import dequantize_mat_vec_amd as dmv
