@@ -216,13 +216,17 @@ def kernel_name(fmt, infs, outs):
     """Label of the mat-vec kernel instance one batch-1 launch uses: lanes
     per row L by the longest row (one row per lane group at batch 1); Q8_0
     rows of an even block count take two blocks per unit (q8_0x2), Q4_K rows
-    of at most 1024 weights half units (q4_kh)."""
+    of at most 1024 weights half units (q4_kh; q4_ksh in the stream
+    layout)."""
     if fmt == "q8_0" and all(inf % 64 == 0 for inf in infs):
         fmt = "q8_0x2"
     if fmt == "q4_k" and all(inf <= 1024 for inf in infs):
         fmt = "q4_kh"
+    if fmt == "q4_k_stream" and all(inf <= 1024 for inf in infs):
+        fmt = "q4_ksh"
     units = max({"q8_0x2": inf // 64, "q8_0": inf // 32, "q4_k": -(-inf // 64), "q4_kh": 2 * -(-inf // 64),
-                 "q4_k_stream": inf // 64, "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
+                 "q4_k_stream": inf // 64, "q4_ksh": 2 * (inf // 64),
+                 "q6_k": 4 * -(-inf // 256)}[fmt] for inf in infs)
     lanes = 16 if units <= 16 else (32 if units <= 32 else 64)
     rows = 1
     return f"gemv_kernel<{fmt}, L={lanes}, B=1, R={rows}>"
@@ -691,7 +695,7 @@ def dominant_traffic(kernel_label, read_key="fetch_size_bytes"):
     fmt = kernel_label.split("<")[1].split(",")[0]
     lanes = kernel_label.split("L=")[1].split(",")[0]
     tag = {"q8_0": "FmtQ8_0", "q8_0x2": "FmtQ8_0x2", "q4_k": "FmtQ4_K", "q4_kh": "FmtQ4_KH",
-           "q4_k_stream": "FmtQ4_KS", "q6_k": "FmtQ6_K"}[fmt]
+           "q4_k_stream": "FmtQ4_KS", "q4_ksh": "FmtQ4_KSH", "q6_k": "FmtQ6_K"}[fmt]
     # one entry per launch shape of the kernel; every shape of the decode step
     # occurs equally often (once per layer), so the per-launch average is
     # the plain mean over shapes

@@ -151,6 +151,30 @@ __device__ __forceinline__ float nearest_code(float dm, float ds, float cmax) {
   return (r >= 0.f && r <= cmax) ? r : 0.f;   // false for NaN and infinity
 }
 
+// Row tile of workgroup b of a grid of n along x.  Workgroups go to the 8
+// XCDs in turn (b % 8), and each XCD has its own L2: with tile = b,
+// neighbouring tiles sit on different XCDs and a 128-byte line that two
+// tiles share is fetched by both L2s.  With PESTI_XCD_TILES each XCD takes
+// one contiguous run of tiles instead (XCD j: [start_j, start_j +
+// count_j), the first n % 8 XCDs one more than the others; a bijection for
+// every n).  Measured on the decode step, it cut the Q/K/V launch's reads
+// from 730 to 665 KB and gate/up's from 5.07 to 5.00 MB, and made every
+// mat-vec slower (step 371 -> 397 us, the down projections 3.9 -> 4.1 and
+// 4.7 -> 4.9 us): the tiles stay in launch order by default.
+#ifndef PESTI_XCD_TILES
+#define PESTI_XCD_TILES 0
+#endif
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
+  if constexpr (PESTI_XCD_TILES == 0) {
+    return b;
+  } else {
+    const int64_t xcd = b % kXcds, slot = b / kXcds;
+    const int64_t per = n / kXcds, rem = n % kXcds;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  }
+}
+
 // Read 4 consecutive logical floats starting at logical index i (i % 4 == 0).
 __device__ __forceinline__ f32x4 xs4(const float* xs, int64_t i) {
   return *reinterpret_cast<const f32x4*>(xs + xs_phys(i));

@@ -1,6 +1,6 @@
 // Small-M prefill GEMM with block-quantized weights: Y = X W^T + b with W in
-// Q8_0 or Q4_K (packed rows, the layouts of the mat-vec), X binary16 [m][K],
-// Y float32 [m][N].  This is the prompt-width case of the decode step's
+// Q8_0 or a K-family format, Q2_K .. Q6_K (packed rows, the layouts of the
+// mat-vec), X binary16 [m][K], Y float32 [m][N].  This is the prompt-width case of the decode step's
 // linear layer ("inferno" README, "Benchmarks": linear = x @ w + b at prompt
 // width, the products that page finds dominate prefill) with the weights kept
 // in the quantized form of the mat-vec ("Project scaffold ...", quant.rs:
@@ -9,7 +9,8 @@
 // The product runs on the matrix cores on exact operands.  Every code is an
 // integer that binary16 represents exactly (Q8_0 int8 through a float32 and
 // a round-to-zero pack; Q4_K nibbles through v_cvt_scalef32_pk_f16_fp8 of
-// the nibble read as an e4m3 byte, exactly q * 2^-9), and X is binary16, so
+// the nibble read as an e4m3 byte, exactly q * 2^-9; the other K-family
+// codes through binary16 1024 + q built by a byte permute), and X is binary16, so
 // every product is exact in the float32 accumulator of
 // v_mfma_f32_16x16x32_f16.  One MFMA k-step is one 32-weight sub-block
 // (a Q8_0 block, a Q4_K sub-block), so its scales are applied to the

@@ -440,8 +440,33 @@ struct FmtQ4_KS {
   }
 };
 
+// The stream layout in half units, for rows of at most 1024 weights at
+// batch 1 (as FmtQ4_KH for the row layout): half unit u of a row is stream
+// half unit u + 2 * phase from the row's first super-block, and its scale
+// gather is FmtQ4_K's for run ((sub / 2) + phase) % 4.
+struct FmtQ4_KSH {
+  static constexpr bool kRowScales = false;
+  static constexpr int kPad = 64;
+  using Raw = FmtQ4_KH::Raw;
+  using Lane = FmtQ4_KS::Lane;
+  __device__ static bool valid(const GemvArgs&, int) { return true; }
+  __device__ static Lane lane_state(int sub, const GemvArgs& a, int64_t row) {
+    const int phase = static_cast<int>((row * (a.in >> 6)) & 3);
+    return Lane{FmtQ4_K::lane_state(((sub >> 1) + phase) & 3), phase};
+  }
+  __device__ static const uint8_t* row_ptr(const GemvArgs& a, int64_t row) { return FmtQ4_KS::row_ptr(a, row); }
+  __device__ __forceinline__ static void issue(const uint8_t* rp, int u, const Lane& L, Raw& r) {
+    FmtQ4_KH::issue(rp, u + 2 * L.phase, r);
+  }
+  template <int B, int R>
+  __device__ __forceinline__ static void compute(const GemvArgs& a, const Raw* r, int u,
+                                                 const float* xs, const Lane& L, float* acc) {
+    FmtQ4_KH::compute<B, R>(a, r, u, xs, L.k, acc);
+  }
+};
+
 template <class F>
-constexpr bool kStreamLayout = std::is_same<F, FmtQ4_KS>::value;
+constexpr bool kStreamLayout = std::is_same<F, FmtQ4_KS>::value || std::is_same<F, FmtQ4_KSH>::value;
 
 // ---------------------------------------------------------------------------
 // Q2_K and Q3_K share a unit: half h and column c of super-block u / 4
@@ -1072,7 +1097,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GroupArgs g) {
   asm volatile("" ::"s"(a.w), "s"(a.scales), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in),
                "s"(a.row_bytes), "s"(a.units), "s"(a.xpad), "s"(a.xstride));
   if constexpr (P) asm volatile("" ::"s"(a.w2), "s"(a.scales2));
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int64_t first = tile * kRowsPerTile;
   if (first >= a.out) return;   // this op has fewer tiles (uniform)
   float* xs = lds;
@@ -1607,12 +1632,38 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     }
     const size_t lds = row_lds * nb;
     int r = 1;
-    if constexpr (std::is_same<F, pesti::FmtQ4_K>::value && pesti::kQ4KHalfUnits) {
-      if (nb == 1 && max_units <= 16) {
-        // rows of at most 1024 weights at batch 1: half units (FmtQ4_KH)
-        for (int i = 0; i < n_mv; ++i) c.op[i].units = 2 * c.op[i].units;
-        r = max_units <= 8 ? launch_one<pesti::FmtQ4_KH, 16, 1, 1, 1>(c, lds, stream_h)
-                           : launch_one<pesti::FmtQ4_KH, 32, 1, 1, 1>(c, lds, stream_h);
+    if constexpr ((std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ4_KS>::value) &&
+                  pesti::kQ4KHalfUnits) {
+      if (nb == 1) {
+        // Rows of at most 1024 weights at batch 1 take half units (FmtQ4_KH,
+        // FmtQ4_KSH in the stream layout).  The choice is made per op, so a
+        // group of short and long rows is two launches and every op gives
+        // the bits of its own single call.
+        using H = typename std::conditional<std::is_same<F, pesti::FmtQ4_K>::value, pesti::FmtQ4_KH,
+                                            pesti::FmtQ4_KSH>::type;
+        GroupArgs sh{}, lg{};
+        int64_t sh_units = 0, lg_units = 0, lg_out = 0;
+        size_t sh_lds = 0, lg_lds = 0;
+        for (int i = 0; i < n_mv; ++i) {
+          const size_t op_lds = sizeof(float) * static_cast<size_t>(c.op[i].xstride);
+          if (c.op[i].units <= 16) {
+            sh.op[sh.n_ops] = c.op[i];
+            sh.op[sh.n_ops].units = 2 * c.op[i].units;
+            ++sh.n_ops;
+            if (c.op[i].units > sh_units) sh_units = c.op[i].units;
+            if (op_lds > sh_lds) sh_lds = op_lds;
+          } else {
+            lg.op[lg.n_ops++] = c.op[i];
+            if (c.op[i].units > lg_units) lg_units = c.op[i].units;
+            if (c.op[i].out > lg_out) lg_out = c.op[i].out;
+            if (op_lds > lg_lds) lg_lds = op_lds;
+          }
+        }
+        r = PESTI_OK;
+        if (sh.n_ops > 0)
+          r = sh_units <= 8 ? launch_one<H, 16, 1, 1, 1>(sh, sh_lds, stream_h)
+                            : launch_one<H, 32, 1, 1, 1>(sh, sh_lds, stream_h);
+        if (r == PESTI_OK && lg.n_ops > 0) r = launch_lu<F>(lg, lg_units, lg_out, nb, lg_lds, stream_h);
       }
     }
     if (r == 1) r = launch_lu<F>(c, max_units, max_out, nb, lds, stream_h);

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
   constexpr int kRowsPerGroup = kRowsPerWave * kTallWaves;
   const GemvArgs a = g.op[blockIdx.y];
   asm volatile("" ::"s"(a.w), "s"(a.x), "s"(a.y), "s"(a.bias), "s"(a.out), "s"(a.in), "s"(a.row_bytes));
-  const int64_t first_wg = static_cast<int64_t>(blockIdx.x) * kRowsPerGroup;
+  const int64_t first_wg = xcd_tile(blockIdx.x, gridDim.x) * kRowsPerGroup;
   if (first_wg >= a.out) return;   // this op has fewer row groups (uniform)
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);

@@ -240,4 +240,8 @@ def test_stream_layout_step_keeps_the_plan_and_the_nominal_bytes():
 
 
 def test_stream_kernel_label():
-    assert bench.kernel_name("q4_k_stream", [896], [896]) == "gemv_kernel<q4_k_stream, L=16, B=1, R=1>"
+    """Stream-layout rows of at most 1024 weights run in half units at batch
+    1, longer ones in whole runs."""
+    assert bench.kernel_name("q4_k_stream", [896], [896]) == "gemv_kernel<q4_ksh, L=32, B=1, R=1>"
+    assert bench.kernel_name("q4_k_stream", [512], [896]) == "gemv_kernel<q4_ksh, L=16, B=1, R=1>"
+    assert bench.kernel_name("q4_k_stream", [4864], [896]) == "gemv_kernel<q4_k_stream, L=64, B=1, R=1>"

@@ -571,6 +571,29 @@ def test_group_equals_single_calls_bitwise():
         assert torch.equal(yg, ys)
 
 
+def test_group_of_short_and_long_rows_equals_single_calls_bitwise():
+    """At batch 1, rows of at most 1024 weights run in half units and longer
+    ones in whole runs; the choice is made per op (a mixed group is two
+    launches), so every op gives the bits of its own single call."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for i, (out, inf) in enumerate([(896, 896), (896, 4864), (128, 512), (37, 2048), (300, 1024)]):
+        packed, _, x, bias = make("q4_k", out, inf, 70 + i, 1)
+        w_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yg = torch.empty(out, dtype=torch.float32, device="cuda")
+        ys = torch.empty(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, None))
+        singles.append((out, inf, w_d, x_d, ys, b_d))
+    dmv.pesti_gemv_group("q4_k", ops, 1)
+    for out, inf, w_d, x_d, ys, b_d in singles:
+        dmv.pesti_gemv_q4_k(out, inf, w_d, x_d, ys, b_d, 1)
+    torch.cuda.synchronize()
+    for (o, _, _, _, yg, _, _), (_, _, _, _, ys, _) in zip(ops, singles):
+        assert torch.equal(yg, ys), o
+
+
 # ---------------------------------------------------------------------------
 # tall matrices: launches where a lane group serves 2 or 4 rows, with a
 # ragged last tile, checked on every row
@@ -1146,7 +1169,8 @@ def test_stream_dequant_bit_exact(rows, inf):
 
 
 STREAM_GEMV = [(67, 896, 1), (67, 896, 3), (67, 896, 8), (1152, 896, 1), (4864, 896, 1), (300, 64, 1),
-               (37, 192, 2), (130, 4864, 2), (11, 20480, 1), (MFMA_ROWS + 37, 896, 1), (MFMA_ROWS + 37, 896, 4)]
+               (37, 192, 2), (130, 4864, 2), (11, 20480, 1), (MFMA_ROWS + 37, 896, 1), (MFMA_ROWS + 37, 896, 4),
+               (77, 192, 1), (65, 1024, 1), (3, 960, 1), (130, 4864, 1), (5, 1088, 1)]
 
 
 @pytest.mark.parametrize("out,inf,batch", STREAM_GEMV)
@@ -1172,6 +1196,54 @@ def test_stream_one_hot_x_gives_dequantized_column():
     y = run_gemv("q4_k_stream", packed, None, out, inf, x)
     for b, j in enumerate(cols):
         assert np.array_equal(y[b], w32[:, j]), j
+
+
+@pytest.mark.parametrize("out,inf", [(129, 896), (37, 512), (21, 1024), (9, 960)])
+def test_stream_batch_1_one_hot_gives_dequantized_column(out, inf):
+    """Batch 1 takes the half-unit stream kernel for rows of at most 1024
+    weights: every sampled column comes back bit for bit."""
+    rng = np.random.default_rng([167, out, inf])
+    packed = synth.stream_blocks(rng, out, inf)
+    w32 = oracle.dequantize_f32("q4_k_stream", packed, out, inf)
+    for j in sorted({0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 255, 256, inf - 1}):
+        if j >= inf:
+            continue
+        x = np.zeros((1, inf), np.float32)
+        x[0, j] = 1.0
+        y = run_gemv("q4_k_stream", packed, None, out, inf, x)
+        assert np.array_equal(y[0], w32[:, j]), j
+
+
+def test_stream_batch_1_padding_at_the_end_does_not_matter():
+    out, inf = 45, 896
+    rng = np.random.default_rng(168)
+    packed = synth.stream_blocks(rng, out, inf)
+    other = packed.copy()
+    other[-64:] = rng.integers(0, 256, 64, dtype=np.uint8)
+    other[-144 + 12:-144 + 16] = rng.integers(0, 256, 4, dtype=np.uint8)
+    x = synth.activations(rng, 1, inf)
+    assert np.array_equal(run_gemv("q4_k_stream", packed, None, out, inf, x),
+                          run_gemv("q4_k_stream", other, None, out, inf, x))
+
+
+def test_stream_batch_1_group_of_short_rows_equals_single_calls_bitwise():
+    """The step's Q/K/V and gate/up shapes in one grouped launch (half units)."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles = [], []
+    for n, (out, inf) in enumerate([(896, 896), (128, 896), (128, 896), (4864, 896), (35, 512)]):
+        rng = np.random.default_rng([169, n])
+        packed = synth.stream_blocks(rng, out, inf)
+        x, bias = synth.activations(rng, 1, inf), synth.bias(rng, out)
+        singles.append(run_gemv("q4_k_stream", packed, None, out, inf, x, bias))
+        w, xd, bd = to_dev(packed), to_dev(x), to_dev(bias)
+        yd = torch.zeros(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w, xd, yd, bd, None))
+    dmv.pesti_gemv_group("q4_k_stream", ops, 1)
+    torch.cuda.synchronize()
+    for (out, inf, w, xd, yd, bd, _), y1 in zip(ops, singles):
+        assert np.array_equal(yd.cpu().numpy(), y1[0])
 
 
 def test_stream_padding_at_the_end_does_not_matter():
