@@ -212,17 +212,21 @@ def make_step(lib, calls, launches, weights, xs, ys, biases, ffn="separate"):
     return step
 
 
+HALF_UNIT_MAX_ROWS = 2048   # the library's PESTI_HALF_UNIT_MAX_ROWS
+
+
 def kernel_name(fmt, infs, outs):
     """Label of the mat-vec kernel instance one batch-1 launch uses: lanes
     per row L by the longest row (one row per lane group at batch 1); Q8_0
-    rows of an even block count take two blocks per unit (q8_0x2), Q4_K rows
-    of at most 1024 weights half units (q4_kh; q4_ksh in the stream
-    layout)."""
+    rows of an even block count take two blocks per unit (q8_0x2), Q4_K ops
+    of at most 2048 rows of at most 1024 weights half units (q4_kh; q4_ksh in
+    the stream layout)."""
     if fmt == "q8_0" and all(inf % 64 == 0 for inf in infs):
         fmt = "q8_0x2"
-    if fmt == "q4_k" and all(inf <= 1024 for inf in infs):
+    half = all(inf <= 1024 for inf in infs) and all(out <= HALF_UNIT_MAX_ROWS for out in outs)
+    if fmt == "q4_k" and half:
         fmt = "q4_kh"
-    if fmt == "q4_k_stream" and all(inf <= 1024 for inf in infs):
+    if fmt == "q4_k_stream" and half:
         fmt = "q4_ksh"
     units = max({"q8_0x2": inf // 64, "q8_0": inf // 32, "q4_k": -(-inf // 64), "q4_kh": 2 * -(-inf // 64),
                  "q4_k_stream": inf // 64, "q4_ksh": 2 * (inf // 64),

@@ -445,9 +445,17 @@ struct WPolQ8_0 {
 // Q6_K unit: one super-block - per lane its 8-byte pieces of ql (four) and
 // qh (two), the 16 scale bytes and d; a unit feeds eight k-steps of two
 // scaled parts each.
+// The wide kernel's threshold per format (layer width in 16-column tiles).
+// At the 4864-column gate/up layers (304 tiles) the K-split kernel is
+// faster for Q2_K, Q4_K, Q5_K and Q6_K, whose operands need the most
+// decoding per k-step (m 16: 7.1 / 6.7 / 7.5 / 9.0 us against 9.2 / 8.8 /
+// 9.0 / 11.6 on the wide kernel), so they take the wide kernel from 1024
+// tiles, as binary16 and Q8_0 do; Q3_K keeps it from 256 (7.9 against
+// 10.0 us).  At the 151936-column LM head (9496 tiles) every format is
+// faster on the wide kernel.
 struct WPolQ6_K {
   static constexpr int kSumWidth = 32;
-  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr bool kChained = false;
@@ -487,7 +495,7 @@ struct WPolQ6_K {
 
 struct WPolQ4_K {
   static constexpr int kSumWidth = 32;
-  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr bool kChained = true;
@@ -542,7 +550,7 @@ struct WPolQ4_K {
 // each run and its 8 fifth-bit bytes; chained like Q4_K with (q - c_j) *
 // sc_j (q <= 31) in the operand.
 struct WPolQ5_K {
-  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr int kSumWidth = 32;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
@@ -641,7 +649,7 @@ struct WPolQ3_K {
 // its nearest_code); the 16 remainders d sc c - dmin m (one per 16 weights)
 // take 16-weight sums of X, four per product.
 struct WPolQ2_K {
-  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr int kSumWidth = 16;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;

@@ -344,6 +344,10 @@ struct FmtQ4_K {
 #define PESTI_Q4K_HALF_UNITS 1
 #endif
 constexpr bool kQ4KHalfUnits = PESTI_Q4K_HALF_UNITS != 0;
+#ifndef PESTI_HALF_UNIT_MAX_ROWS
+#define PESTI_HALF_UNIT_MAX_ROWS 2048
+#endif
+constexpr int64_t kHalfUnitMaxRows = PESTI_HALF_UNIT_MAX_ROWS;
 
 struct FmtQ4_KH {
   static constexpr bool kRowScales = false;
@@ -1635,10 +1639,13 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
     if constexpr ((std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ4_KS>::value) &&
                   pesti::kQ4KHalfUnits) {
       if (nb == 1) {
-        // Rows of at most 1024 weights at batch 1 take half units (FmtQ4_KH,
-        // FmtQ4_KSH in the stream layout).  The choice is made per op, so a
-        // group of short and long rows is two launches and every op gives
-        // the bits of its own single call.
+        // Ops of at most kHalfUnitMaxRows rows of at most 1024 weights take
+        // half units at batch 1 (FmtQ4_KH, FmtQ4_KSH in the stream layout):
+        // they halve each lane's arithmetic after a short launch's one memory
+        // round trip, while on larger ops the extra workgroups and header
+        // reads cost more than that saves.  The choice is made per op, so a
+        // group of both kinds is two launches and every op gives the bits
+        // of its own single call.
         using H = typename std::conditional<std::is_same<F, pesti::FmtQ4_K>::value, pesti::FmtQ4_KH,
                                             pesti::FmtQ4_KSH>::type;
         GroupArgs sh{}, lg{};
@@ -1646,7 +1653,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
         size_t sh_lds = 0, lg_lds = 0;
         for (int i = 0; i < n_mv; ++i) {
           const size_t op_lds = sizeof(float) * static_cast<size_t>(c.op[i].xstride);
-          if (c.op[i].units <= 16) {
+          if (c.op[i].units <= 16 && c.op[i].out <= pesti::kHalfUnitMaxRows) {
             sh.op[sh.n_ops] = c.op[i];
             sh.op[sh.n_ops].units = 2 * c.op[i].units;
             ++sh.n_ops;

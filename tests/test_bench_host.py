@@ -81,6 +81,15 @@ def test_kernel_label_lanes(fmt, inf, lanes, label):
     assert bench.kernel_name(fmt, [inf], [896]) == f"gemv_kernel<{label}, L={lanes}, B=1, R=1>"
 
 
+def test_half_units_only_for_ops_of_at_most_2048_rows():
+    """The step's Q/K/V and O launches run in half units, its 4864-row
+    gate/up launch in whole runs."""
+    assert bench.kernel_name("q4_k", [896, 896, 896], [896, 128, 128]) == "gemv_kernel<q4_kh, L=32, B=1, R=1>"
+    assert bench.kernel_name("q4_k", [896, 896], [4864, 4864]) == "gemv_kernel<q4_k, L=16, B=1, R=1>"
+    assert bench.kernel_name("q4_k_stream", [896], [2048]) == "gemv_kernel<q4_ksh, L=32, B=1, R=1>"
+    assert bench.kernel_name("q4_k_stream", [896], [2049]) == "gemv_kernel<q4_k_stream, L=16, B=1, R=1>"
+
+
 def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the
     same counter reads for a copy of known size; medians per kernel shape."""
