@@ -112,14 +112,18 @@ struct QPolQ4_K {
   static constexpr int kParts = 1;
   struct Step { uint32_t c[2]; u32x4 hdr; uint32_t j; };
 
-  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+  // Steps s and s + 1 (s even: sub-blocks 2g and 2g + 1, the low and high
+  // nibbles of the same code bytes) share all their bytes: 3 loads for the
+  // pair instead of 6.
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
     const uint8_t* sb = row + 144 * (s >> 3);
-    const int j = s & 7;
+    const int j = s & 6;
     const uint8_t* p = sb + 16 + 32 * (j >> 1) + 8 * kg;
-    st.c[0] = load_u32(p);
-    st.c[1] = load_u32(p + 4);
-    st.hdr = load_u32x4_a16(sb);
-    st.j = static_cast<uint32_t>(j);
+    a.c[0] = b.c[0] = load_u32(p);
+    a.c[1] = b.c[1] = load_u32(p + 4);
+    a.hdr = b.hdr = load_u32x4_a16(sb);
+    a.j = static_cast<uint32_t>(j);
+    b.j = static_cast<uint32_t>(j + 1);
   }
 
   // The codes less c, (q - c) 2^-9: a nibble in an otherwise zero e4m3 byte
@@ -193,6 +197,7 @@ struct QPolQ4_K {
 // ---------------------------------------------------------------------------
 typedef uint32_t q6u2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef uint32_t q6u4 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t q6u1 __attribute__((aligned(2)));
 
 __device__ __forceinline__ qhalf8 q6_k_codes(uint32_t l0, uint32_t l1, uint32_t h0, uint32_t h1, int g) {
   const uint32_t ls = 4u * static_cast<uint32_t>(g >> 1);
@@ -221,16 +226,26 @@ struct QPolQ6_K {
   static constexpr int kParts = 2;
   struct Step { uint32_t l[2]; uint32_t h[2]; uint32_t sc; uint32_t d; uint32_t g; };
 
-  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+  // Steps s and s + 1 (s even: groups g and g + 1 of one half h, one
+  // super-block) share the high-part bytes, d and one dword of scales:
+  // 5 loads for the pair instead of 8.
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
     const uint8_t* sb = row + 210 * (s >> 3);
-    const int t = s & 7, h = t >> 2, g = t & 3;
-    const q6u2 lv = *reinterpret_cast<const q6u2*>(sb + 64 * h + 32 * (g & 1) + 8 * kg);
+    const int t = s & 6, h = t >> 2, g = t & 3;   // g = 0 or 2
+    const q6u2 l0 = *reinterpret_cast<const q6u2*>(sb + 64 * h + 8 * kg);
+    const q6u2 l1 = *reinterpret_cast<const q6u2*>(sb + 64 * h + 32 + 8 * kg);
     const q6u2 hv = *reinterpret_cast<const q6u2*>(sb + 128 + 32 * h + 8 * kg);
-    st.l[0] = lv.x; st.l[1] = lv.y;
-    st.h[0] = hv.x; st.h[1] = hv.y;
-    st.sc = load_u16(sb + 192 + 2 * t);   // scales of sub-blocks 2t, 2t + 1
-    st.d = load_u16(sb + 208);
-    st.g = static_cast<uint32_t>(g);
+    const uint32_t sc = *reinterpret_cast<const q6u1*>(sb + 192 + 2 * t);   // scales 2t .. 2t + 3
+    const uint32_t d = load_u16(sb + 208);
+    a.l[0] = l0.x; a.l[1] = l0.y;
+    b.l[0] = l1.x; b.l[1] = l1.y;
+    a.h[0] = b.h[0] = hv.x;
+    a.h[1] = b.h[1] = hv.y;
+    a.sc = sc & 0xFFFFu;
+    b.sc = sc >> 16;
+    a.d = b.d = d;
+    a.g = static_cast<uint32_t>(g);
+    b.g = static_cast<uint32_t>(g + 1);
   }
   __device__ __forceinline__ static qhalf8 codes(const Step& st, int part, int kg) {
     return q6_k_part(q6_k_codes(st.l[0], st.l[1], st.h[0], st.h[1], static_cast<int>(st.g)), part, kg);
@@ -298,16 +313,19 @@ struct QPolQ5_K {
   static constexpr int kParts = 1;
   struct Step { uint32_t c[2]; uint32_t h[2]; u32x4 hdr; uint32_t j; };
 
-  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+  // Steps s and s + 1 (s even) share all their bytes: 5 loads for the pair
+  // instead of 10.
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
     const uint8_t* sb = row + 176 * (s >> 3);
-    const int j = s & 7;
+    const int j = s & 6;
     const uint8_t* p = sb + 48 + 32 * (j >> 1) + 8 * kg;
-    st.c[0] = load_u32(p);
-    st.c[1] = load_u32(p + 4);
-    st.h[0] = load_u32(sb + 16 + 8 * kg);
-    st.h[1] = load_u32(sb + 20 + 8 * kg);
-    st.hdr = load_u32x4_a16(sb);
-    st.j = static_cast<uint32_t>(j);
+    a.c[0] = b.c[0] = load_u32(p);
+    a.c[1] = b.c[1] = load_u32(p + 4);
+    a.h[0] = b.h[0] = load_u32(sb + 16 + 8 * kg);
+    a.h[1] = b.h[1] = load_u32(sb + 20 + 8 * kg);
+    a.hdr = b.hdr = load_u32x4_a16(sb);
+    a.j = static_cast<uint32_t>(j);
+    b.j = static_cast<uint32_t>(j + 1);
   }
   __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) {
     const uint32_t sh = 4u * (st.j & 1u);
@@ -341,20 +359,31 @@ struct QPolQ3_K {
   static constexpr int kParts = 1;
   struct Step { uint32_t q[2]; uint32_t hm[2]; uint32_t s01, s2; uint32_t d; uint32_t t; };
 
-  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+  // Steps s and s + 1 (s even: j and j + 1 of one half h, one
+  // super-block) share the code bytes, the high-bit bytes, d and one dword
+  // of each scale run: 5 loads for the pair instead of 10.  The lane's scale
+  // k = 8h + 2j + c has its low bits in byte k % 8 = 2j + c (nibble h) and
+  // its high bits in byte 8 + k % 4 (bits 4h + 2(j / 2)).
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
     const uint8_t* sb = row + 110 * (s >> 3);
-    const int t = s & 7, h = t >> 2, c = kg >> 1, l = 8 * (kg & 1);
+    const int t = s & 6, h = t >> 2, c = kg >> 1, l = 8 * (kg & 1);
+    const int j = t & 3;   // 0 or 2
     const q6u2 qv = *reinterpret_cast<const q6u2*>(sb + 32 + 32 * h + 16 * c + l);
     const q6u2 hv = *reinterpret_cast<const q6u2*>(sb + 16 * c + l);
-    st.q[0] = qv.x; st.q[1] = qv.y;
-    st.hm[0] = hv.x; st.hm[1] = hv.y;
-    // the lane's scale k = 8h + 2j + c: low bits in byte k % 8 = 2j + c
-    // (nibble h), high bits in byte 8 + k % 4 (bits 4h + 2(j / 2))
-    const int j = t & 3;
-    st.s01 = load_u16(sb + 96 + 2 * j);        // bytes 2j, 2j + 1
-    st.s2 = load_u16(sb + 104 + 2 * (j & 1));  // bytes 8 + 2(j % 2), +1
-    st.d = load_u16(sb + 108);
-    st.t = static_cast<uint32_t>(t | (kg << 3));
+    const uint32_t s01 = *reinterpret_cast<const q6u1*>(sb + 96 + 2 * j);   // bytes 2j .. 2j + 3
+    const uint32_t s2 = *reinterpret_cast<const q6u1*>(sb + 104);           // bytes 8 .. 11
+    const uint32_t d = load_u16(sb + 108);
+    a.q[0] = b.q[0] = qv.x;
+    a.q[1] = b.q[1] = qv.y;
+    a.hm[0] = b.hm[0] = hv.x;
+    a.hm[1] = b.hm[1] = hv.y;
+    a.s01 = s01 & 0xFFFFu;
+    b.s01 = s01 >> 16;
+    a.s2 = s2 & 0xFFFFu;   // j even: bytes 8, 9
+    b.s2 = s2 >> 16;       // j + 1 odd: bytes 10, 11
+    a.d = b.d = d;
+    a.t = static_cast<uint32_t>(t | (kg << 3));
+    b.t = static_cast<uint32_t>((t + 1) | (kg << 3));
   }
   __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int kg) {
     const uint32_t t = st.t & 7u, h = t >> 2, j = t & 3u, c = static_cast<uint32_t>(kg >> 1);
@@ -386,15 +415,21 @@ struct QPolQ2_K {
   static constexpr int kParts = 1;
   struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
 
-  __device__ __forceinline__ static void load(const uint8_t* row, int s, int kg, Step& st) {
+  // Steps s and s + 1 (s even: j and j + 1 of one half h) share their code
+  // bytes, d and dmin and one dword of scale/min bytes: 4 loads for the
+  // pair instead of 8.
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
     const uint8_t* sb = row + 84 * (s >> 3);
-    const int t = s & 7, h = t >> 2, j = t & 3, c = kg >> 1, l = 8 * (kg & 1);
+    const int t = s & 6, h = t >> 2, j = t & 3, c = kg >> 1, l = 8 * (kg & 1);   // j = 0 or 2
     const uint8_t* p = sb + 16 + 32 * h + 16 * c + l;
-    st.q[0] = load_u32(p);
-    st.q[1] = load_u32(p + 4);
-    st.scb = load_u16(sb + 8 * h + 2 * j) >> (8 * c);   // byte k = 8h + 2j + c in bits 0-7
-    st.dd = load_u32(sb + 80);
-    st.j = static_cast<uint32_t>(j);
+    a.q[0] = b.q[0] = load_u32(p);
+    a.q[1] = b.q[1] = load_u32(p + 4);
+    const uint32_t sw = load_u32(sb + 8 * h + 2 * j);   // bytes 8h + 2j .. + 3
+    a.scb = sw >> (8 * c);                              // byte k = 8h + 2j + c in bits 0-7
+    b.scb = sw >> (16 + 8 * c);                         // byte 8h + 2(j + 1) + c
+    a.dd = b.dd = load_u32(sb + 80);
+    a.j = static_cast<uint32_t>(j);
+    b.j = static_cast<uint32_t>(j + 1);
   }
   // d * sc, dmin * m and nearest_code of the lane's sub-block
   __device__ __forceinline__ static void sub_block(const Step& st, float& ds, float& dm, float& c) {
@@ -445,14 +480,11 @@ struct WPolQ8_0 {
 // Q6_K unit: one super-block - per lane its 8-byte pieces of ql (four) and
 // qh (two), the 16 scale bytes and d; a unit feeds eight k-steps of two
 // scaled parts each.
-// The wide kernel's threshold per format (layer width in 16-column tiles).
-// At the 4864-column gate/up layers (304 tiles) the K-split kernel is
-// faster for Q2_K, Q4_K, Q5_K and Q6_K, whose operands need the most
-// decoding per k-step (m 16: 7.1 / 6.7 / 7.5 / 9.0 us against 9.2 / 8.8 /
-// 9.0 / 11.6 on the wide kernel), so they take the wide kernel from 1024
-// tiles, as binary16 and Q8_0 do; Q3_K keeps it from 256 (7.9 against
-// 10.0 us).  At the 151936-column LM head (9496 tiles) every format is
-// faster on the wide kernel.
+// The wide kernel takes layers from 1024 16-column tiles in every format:
+// at the 4864-column gate/up layers (304 tiles) the K-split kernel, with
+// its pair loads, is faster (m 16, Q2_K .. Q6_K: 5.9 / 6.6 / 5.7 / 6.1 /
+// 6.9 us against 9.2 / 7.9 / 8.8 / 9.0 / 11.6 on the wide kernel), and at
+// the 151936-column LM head (9496 tiles) the wide kernel is.
 struct WPolQ6_K {
   static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 1024;
@@ -597,7 +629,7 @@ struct WPolQ5_K {
 // scale bytes and d; step j = 4h + jj carries (q) * (scale - 32) of the
 // lane's sub-block 8h + 2jj + c in the operand.
 struct WPolQ3_K {
-  static constexpr int64_t kWideMinTiles = 256;
+  static constexpr int64_t kWideMinTiles = 1024;
   static constexpr int kSumWidth = 32;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
@@ -708,6 +740,11 @@ struct QBuf {
   qhalf8 x[2][MT];
 };
 
+template <class Q, class = void>
+struct PairLoad : std::false_type {};
+template <class Q>
+struct PairLoad<Q, std::void_t<decltype(&Q::load_pair)>> : std::true_type {};
+
 template <class Q, int NW, int MT>
 __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   __shared__ qfloat4 part[NW][MT][kWave];
@@ -739,11 +776,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
     xrow[t] = a.x + xm * a.k + 8 * kg;
   }
 
+  // Steps past the slice read in-bounds stand-ins (the slice's first step)
+  // and are skipped.  Formats with a pair load read steps s and s + 1 (s is
+  // even, so both lie in one super-block, and s + 1 is inside the row's
+  // padded blocks even past the last step) in one go.
   auto load = [&](int s, QBuf<Q, MT>& b) {
+    if constexpr (PairLoad<Q>::value) {
+      const int s0 = s < s_end ? s : (s_begin < ksteps ? s_begin : 0);
+      Q::load_pair(wrow, s0, kg, b.w[0], b.w[1]);
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int sc = s + c < s_end ? s + c : (s_begin < ksteps ? s_begin : 0);
-      Q::load(wrow, sc, kg, b.w[c]);
+      if constexpr (!PairLoad<Q>::value) Q::load(wrow, sc, kg, b.w[c]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const qhalf8*>(xrow[t] + 32 * sc);
     }
