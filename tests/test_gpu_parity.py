@@ -1394,3 +1394,29 @@ def test_tall_stream_batch_1_full_lm_head_sampled_rows():
         sub = packed[sb0 * 144: sb1 * 144]
         y_ref, s_ref = oracle.gemv_packed("q4_k_stream", sub, 2, inf, x, bias[r0:r0 + 2])
         assert_within(y[:, r0:r0 + 2], y_ref, s_ref, GEMV_REL, f"stream lm head rows {r0}, {r0 + 1}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_k_stream"])
+def test_half_unit_row_limit_group_equals_single_calls_bitwise(fmt):
+    """Ops of 2048 rows take half units at batch 1 and ops of 2049 rows
+    whole runs; in one group each keeps the bits of its own single call,
+    and every output meets the oracle's bound."""
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, singles, cases = [], [], []
+    for n, (out, inf) in enumerate([(2048, 896), (2049, 896), (2048, 512), (7, 1024)]):
+        rng = np.random.default_rng([176, n])
+        packed, _ = synth.matrix(fmt, rng, out, inf)
+        x, bias = synth.activations(rng, 1, inf), synth.bias(rng, out)
+        y1 = run_gemv(fmt, packed, None, out, inf, x, bias)
+        y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+        assert_within(y1, y_ref, s_ref, GEMV_REL, f"{fmt} {out}x{inf}")
+        singles.append(y1)
+        w, xd, bd = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
+        yd = torch.zeros(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w, xd, yd, bd, None))
+    dmv.pesti_gemv_group(fmt, ops, 1)
+    torch.cuda.synchronize()
+    for (out, inf, w, xd, yd, bd, _), y1 in zip(ops, singles):
+        assert np.array_equal(yd.cpu().numpy(), y1[0]), (out, inf)
