@@ -302,6 +302,34 @@ __device__ __forceinline__ void k4_scale_min(uint32_t y, uint32_t z, uint32_t w,
   }
 }
 
+// The wide kernel's per-unit preparation for Q4_K and Q5_K: the scale sc_j
+// and nearest code c_j of all eight sub-blocks of the row's super-block,
+// which every lane of the row needs.  Lane kg decodes sub-blocks 2kg and
+// 2kg + 1 (sc | c << 6, 16 bits each, in one dword) and the row's four
+// lanes (i + 16 kg') exchange their dwords: 2 decodes and 4 shuffles per
+// lane instead of 8 decodes.
+struct K4Prep {
+  uint32_t w[4];   // w[k]: sub-block 2k in bits 0-15, 2k + 1 in bits 16-31
+  __device__ __forceinline__ uint32_t sc(int j) const { return (w[j >> 1] >> (16 * (j & 1))) & 63u; }
+  __device__ __forceinline__ float c(int j) const { return static_cast<float>((w[j >> 1] >> (16 * (j & 1) + 6)) & 63u); }
+};
+__device__ __forceinline__ K4Prep k4_prep(const u32x4& hdr, int kg, float cmax) {
+  const float d = f16_lo(hdr.x), dmin = f16_hi(hdr.x);
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint32_t sc, mn;
+    k4_scale_min(hdr.y, hdr.z, hdr.w, 2 * kg + e, sc, mn);
+    const float c = nearest_code(dmin * static_cast<float>(mn), d * static_cast<float>(sc), cmax);
+    mine |= (sc | (static_cast<uint32_t>(c) << 6)) << (16 * e);
+  }
+  K4Prep p;
+  const int i = static_cast<int>(__lane_id()) & 15;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) p.w[k] = static_cast<uint32_t>(__shfl(static_cast<int>(mine), i + 16 * k, kWave));
+  return p;
+}
+
 // Q5_K step s (sub-block j = s % 8 of super-block s / 8, 176 bytes): the
 // lane's 8 low nibbles (bytes 48 + 32(j / 2) + 8kg) and their fifth bits
 // (bit j of bytes 16 + 8kg); operand (q - c) * sc_j with c the sub-block's
@@ -553,14 +581,14 @@ struct WPolQ4_K {
   // applied once.  A code byte q becomes binary16 1024 + q by placing 0x64
   // above it (v_perm_b32); an exact packed subtraction of 1024 + c_j and an
   // exact packed product by sc_j follow.
-  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int) {
+  using Prep = K4Prep;
+  __device__ __forceinline__ static Prep prep(const Unit& un, int kg) { return k4_prep(un.hdr, kg, 15.f); }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, const Prep& pr, int j, int) {
     const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
     const uint32_t a = (un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu;
     const uint32_t b = (un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu;
-    uint32_t sc, mn;
-    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, j, sc, mn);
-    const float c = nearest_code(f16_hi(un.hdr.x) * static_cast<float>(mn), d(un) * static_cast<float>(sc), 15.f);
-    return offset_codes(a, b, half_pair(sc), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
+    const float c = pr.c(j);
+    return offset_codes(a, b, half_pair(pr.sc(j)), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
   }
 
   __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
@@ -604,14 +632,14 @@ struct WPolQ5_K {
     un.h[0] = load_u32(sb + 16 + 8 * kg);
     un.h[1] = load_u32(sb + 20 + 8 * kg);
   }
-  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int) {
+  using Prep = K4Prep;
+  __device__ __forceinline__ static Prep prep(const Unit& un, int kg) { return k4_prep(un.hdr, kg, 31.f); }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, const Prep& pr, int j, int) {
     const uint32_t sh = 4u * static_cast<uint32_t>(j & 1);
     const uint32_t lo = ((un.c[j >> 1][0] >> sh) & 0x0F0F0F0Fu) | (((un.h[0] >> j) & 0x01010101u) << 4);
     const uint32_t hi = ((un.c[j >> 1][1] >> sh) & 0x0F0F0F0Fu) | (((un.h[1] >> j) & 0x01010101u) << 4);
-    uint32_t sc, mn;
-    k4_scale_min(un.hdr.y, un.hdr.z, un.hdr.w, j, sc, mn);
-    const float c = nearest_code(f16_hi(un.hdr.x) * static_cast<float>(mn), d(un) * static_cast<float>(sc), 31.f);
-    return offset_codes(lo, hi, half_pair(sc), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
+    const float c = pr.c(j);
+    return offset_codes(lo, hi, half_pair(pr.sc(j)), __builtin_bit_cast(qhalf2, pack_f16(1024.0f + c, 1024.0f + c)));
   }
   __device__ __forceinline__ static float d(const Unit& un) { return f16_lo(un.hdr.x); }
   __device__ __forceinline__ static float neg_min(const Unit& un, int half, int kg) {

@@ -35,12 +35,27 @@
 // k = 8kg..8kg+7 of the step; B = W row i (output column i), the same k;
 // C = column i, rows 4kg..4kg+3.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace pesti {
 
 typedef _Float16 whalf8 __attribute__((ext_vector_type(8)));
 typedef float wfloat4 __attribute__((ext_vector_type(4)));
+
+// Chained policies may decode per-unit data once for the wave (Q::Prep,
+// Q::prep(unit, kg)); codes(unit, prep, j, kg) then reads it.
+template <class Q, class = void>
+struct HasPrep : std::false_type {};
+template <class Q>
+struct HasPrep<Q, std::void_t<typename Q::Prep>> : std::true_type {};
+struct NoPrep {};
+template <class Q>
+__device__ __forceinline__ auto prep_of(const typename Q::Unit& un, int kg) {
+  if constexpr (HasPrep<Q>::value) return Q::prep(un, kg);
+  else return NoPrep{};
+}
 
 struct WideArgs {
   const uint8_t* w;    // N rows of row_bytes
@@ -200,11 +215,14 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(WideArgs a) {
           wfloat4 pc[MT];
 #pragma unroll
           for (int t = 0; t < MT; ++t) pc[t] = wfloat4{0.f, 0.f, 0.f, 0.f};
+          [[maybe_unused]] const auto pr = prep_of<Q>(ring[u].un, kg);
 #pragma unroll
           for (int j = 0; j < KS; ++j) {
             const int s = c_u * KS + j;
             if (s >= S) break;   // wave-uniform: the row's last, partial unit
-            const whalf8 wv = Q::codes(ring[u].un, j, kg);
+            whalf8 wv;
+            if constexpr (HasPrep<Q>::value) wv = Q::codes(ring[u].un, pr, j, kg);
+            else wv = Q::codes(ring[u].un, j, kg);
 #pragma unroll
             for (int t = 0; t < MT; ++t)
               pc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[(t * S + s) * 64 + lane], wv, pc[t], 0, 0, 0);
