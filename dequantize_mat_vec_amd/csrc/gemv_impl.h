@@ -1459,16 +1459,17 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
          a.in > 0 && a.in <= 1024;
 }
-// Tall Q4_K matrices with rows of at most 1024 weights at batch 1 take the
-// batch-1 kernel of gemv_tall.hip (128-weight units, a row per U lanes); in
-// the stream layout only rows of a whole number of 128-weight units, so
-// that no unit straddles two super-blocks.
+// Tall Q4_K and Q5_K matrices with rows of at most 1024 weights at batch 1
+// take the batch-1 kernel of gemv_tall.hip (128-weight units, a row per U
+// lanes); in the Q4_K stream layout only rows of a whole number of
+// 128-weight units, so that no unit straddles two super-blocks.
 #ifndef PESTI_TALL_MIN_ROWS
 #define PESTI_TALL_MIN_ROWS 16384
 #endif
 constexpr int64_t kTallMinRows = PESTI_TALL_MIN_ROWS;
 template <class F>
-constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || pesti::kStreamLayout<F>;
+constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ5_K>::value ||
+                          pesti::kStreamLayout<F>;
 template <class F>
 inline bool tall_op(const GemvArgs& a, int batch) {
   return kHasTall<F> && batch == 1 && a.out >= kTallMinRows && a.in > 0 && a.in <= 1024 &&
@@ -1477,6 +1478,12 @@ inline bool tall_op(const GemvArgs& a, int batch) {
 // One launch of ops that all pass tall_op and share one row length in
 // 128-weight units; x and y of every op set.
 int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st);
+int launch_tall_q5_k(const GroupArgs& g, hipStream_t st);
+template <class F>
+inline int launch_tall(const GroupArgs& g, hipStream_t st) {
+  if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_tall_q5_k(g, st);
+  else return launch_tall_q4_k(g, pesti::kStreamLayout<F>, st);
+}
 
 // One launch of ops that all pass mfma_op and share one row length in
 // super-blocks; x and y of every op set.
@@ -1575,7 +1582,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
         t.op[t.n_ops].y = ops[live[j]].y;
         ++t.n_ops;
       }
-      const int r = launch_tall_q4_k(t, pesti::kStreamLayout<F>, stream_h);
+      const int r = launch_tall<F>(t, stream_h);
       if (r != PESTI_OK) return r;
     }
     max_units = 0;

@@ -1,19 +1,20 @@
-// Batch-1 mat-vec for tall Q4_K matrices with short rows (the LM head,
-// 151936 x 896): y = W x + b.
+// Batch-1 mat-vec for tall Q4_K and Q5_K matrices with short rows (the LM
+// head, 151936 x 896): y = W x + b.
 //
 // The operation is the decode step's row-major matrix-vector product with
-// the weights kept in GGUF Q4_K blocks ("Project scaffold: modules, CLI, and
-// correctness harness", file summaries of tensor.rs and quant.rs; "PESTI -
-// Portable Execution Substrate for Transformer Inference", "What This Is"):
-// w = d sc q - dmin m per 32-weight sub-block.
+// the weights kept in GGUF Q4_K or Q5_K blocks ("Project scaffold: modules,
+// CLI, and correctness harness", file summaries of tensor.rs and quant.rs;
+// "PESTI - Portable Execution Substrate for Transformer Inference", "What
+// This Is"): w = d sc q - dmin m per 32-weight sub-block.
 //
 // At batch 1 the general kernel (gemv_impl.h) spends most of a lane's
 // instructions on work that does not scale with the weights it reads - x
 // staging, address set-up, scale decode, the reduction - for one 64-weight
 // unit per lane, and 2 of each 16-lane row group stay idle on 896-weight
 // rows (14 units).  Here a lane takes a 128-weight unit (two runs of one
-// super-block: its 16-byte header and 64 code bytes, five 16-byte loads)
-// and a row takes U = in / 128 consecutive lanes, so a wave holds
+// super-block: for Q4_K its 16-byte header and 64 code bytes, five 16-byte
+// loads; TallQ5K below for Q5_K) and a row takes U = in / 128 consecutive
+// lanes, so a wave holds
 // floor(64 / U) rows (9 rows of 7 lanes at 896 columns, one lane idle), and
 // a workgroup of 4 waves stages x once for 36 rows (measured on the
 // 151936 x 896 head: 2 / 4 / 8 / 16 waves 21.5 / 20.0 / 22.6 / 26.8 us).  Each weight is
@@ -38,12 +39,13 @@ constexpr int kTallMaxIn = 1024;
 // layout (rows of a whole number of units) it is stream unit g = row U + u,
 // half g % 2 of stream super-block g / 2, again weights 128u .. of the row.
 struct TallQ4K {
+  static constexpr int kBytes = 144;
   struct Raw { u32x4 hdr, c0, c1, c2, c3; };
 
   // g: the unit's index in 128-weight units from `base` (a row's start in
   // the row layout, the matrix's in the stream layout).
   __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
-    const uint8_t* sb = base + (g >> 1) * 144;
+    const uint8_t* sb = base + (g >> 1) * kBytes;
     const uint8_t* cp = sb + 16 + 64 * (g & 1);
     r.hdr = load_u32x4_a16(sb);
     r.c0 = load_u32x4_a16(cp);
@@ -102,6 +104,76 @@ struct TallQ4K {
   }
 };
 
+// Q5_K (176-byte super-blocks): Q4_K's 16-byte header, 32 fifth-bit
+// bytes at 16, the 128 low-nibble bytes at 48.  Weight 64r + 32c + l of a
+// super-block (run r, nibble c, l = 0..31) has its low 4 bits in nibble c
+// of byte 48 + 32r + l and its fifth bit at bit 2r + c of byte 16 + l.  A
+// lane's 128-weight unit is runs 2h and 2h + 1 (h = g % 2): the header, all
+// 32 fifth-bit bytes and 64 low-nibble bytes, seven 16-byte loads.  The
+// 5-bit codes convert exactly with one unsigned-byte convert each, and
+// w = d sc q - dmin m is one rounding of the exact value, as for Q4_K.
+struct TallQ5K {
+  static constexpr int kBytes = 176;
+  struct Raw { u32x4 hdr, h0, h1, c0, c1, c2, c3; };
+
+  __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
+    const uint8_t* sb = base + (g >> 1) * kBytes;
+    const uint8_t* cp = sb + 48 + 64 * (g & 1);
+    r.hdr = load_u32x4_a16(sb);
+    r.h0 = load_u32x4_a16(sb + 16);
+    r.h1 = load_u32x4_a16(sb + 32);
+    r.c0 = load_u32x4_a16(cp);
+    r.c1 = load_u32x4_a16(cp + 16);
+    r.c2 = load_u32x4_a16(cp + 32);
+    r.c3 = load_u32x4_a16(cp + 48);
+  }
+
+  __device__ __forceinline__ static uint32_t pick(const u32x4& v, int i) {
+    switch (i & 3) {
+      case 0: return v.x;
+      case 1: return v.y;
+      case 2: return v.z;
+      default: return v.w;
+    }
+  }
+
+  // acc += sum over the unit's 128 weights of w * x; scales and mins of
+  // sub-blocks 4h + t as TallQ4K::compute.
+  __device__ __forceinline__ static float compute(const Raw& r, int u, bool h1, const float* xs) {
+    const uint32_t y = r.hdr.y, z = r.hdr.z, w = r.hdr.w;
+    const uint32_t scv = h1 ? ((w & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u)) : (y & 0x3F3F3F3Fu);
+    const uint32_t mv = h1 ? (((w >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u)) : (z & 0x3F3F3F3Fu);
+    const float d = f16_lo(r.hdr.x), dmin = f16_hi(r.hdr.x);
+    const float ds[4] = {d * ubyte<0>(scv), d * ubyte<1>(scv), d * ubyte<2>(scv), d * ubyte<3>(scv)};
+    const float ndm[4] = {-(dmin * ubyte<0>(mv)), -(dmin * ubyte<1>(mv)), -(dmin * ubyte<2>(mv)),
+                          -(dmin * ubyte<3>(mv))};
+    const uint32_t hshift = h1 ? 4u : 0u;   // fifth bits of runs 2h, 2h + 1: bits 4h .. 4h + 3
+    float acc = 0.f;
+    const int x0 = 128 * u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t hb = (i < 4 ? pick(r.h0, i) : pick(r.h1, i)) >> hshift;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {   // run 2h + k: low nibbles sub-block 2k, high 2k + 1
+        const uint32_t q = k == 0 ? (i < 4 ? pick(r.c0, i) : pick(r.c1, i)) : (i < 4 ? pick(r.c2, i) : pick(r.c3, i));
+        const uint32_t lo = (q & 0x0F0F0F0Fu) | (((hb >> (2 * k)) & 0x01010101u) << 4);
+        const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (((hb >> (2 * k + 1)) & 0x01010101u) << 4);
+        const f32x4 xl = xs4(xs, x0 + 64 * k + 4 * i);
+        const f32x4 xh = xs4(xs, x0 + 64 * k + 32 + 4 * i);
+        acc = fmaf(fmaf(ds[2 * k], ubyte<0>(lo), ndm[2 * k]), xl.x, acc);
+        acc = fmaf(fmaf(ds[2 * k], ubyte<1>(lo), ndm[2 * k]), xl.y, acc);
+        acc = fmaf(fmaf(ds[2 * k], ubyte<2>(lo), ndm[2 * k]), xl.z, acc);
+        acc = fmaf(fmaf(ds[2 * k], ubyte<3>(lo), ndm[2 * k]), xl.w, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<0>(hi), ndm[2 * k + 1]), xh.x, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<1>(hi), ndm[2 * k + 1]), xh.y, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<2>(hi), ndm[2 * k + 1]), xh.z, acc);
+        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<3>(hi), ndm[2 * k + 1]), xh.w, acc);
+      }
+    }
+    return acc;
+  }
+};
+
 // U = 128-weight units per row (row layout: rows of up to 128 U weights,
 // padded to whole super-blocks; stream layout, S: rows of exactly 128 U);
 // a wave serves 64 / U rows, a workgroup kTallWaves times that.  Measured
@@ -111,8 +183,9 @@ struct TallQ4K {
 // take 2, 4 or 8 row blocks in turn with the next block's loads issued
 // before the current block's arithmetic (in one run: 23.2 us for one block against
 // 24.0 / 26.5 / 33.2: fewer workgroups keep fewer loads in flight).
-template <int U, bool S>
-__global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g) {
+template <class T, int U, bool S>
+__global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
+  static_assert(!S || std::is_same<T, TallQ4K>::value, "the stream layout is Q4_K's");
   __shared__ float xs[xs_phys(kTallMaxIn)];
   constexpr int kRowsPerWave = kWave / U;
   constexpr int kRowsPerGroup = kRowsPerWave * kTallWaves;
@@ -142,8 +215,8 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
   const int64_t lrow = live ? row : first_wg;
   const int lu = live ? u : 0;
   const int64_t gu = S ? lrow * U + lu : lu;
-  TallQ4K::Raw r;
-  TallQ4K::issue(S ? a.w : a.w + lrow * a.row_bytes, gu, r);
+  typename T::Raw r;
+  T::issue(S ? a.w : a.w + lrow * a.row_bytes, gu, r);
   const float bv = *(a.bias ? a.bias + lrow : reinterpret_cast<const float*>(a.w));
 #pragma unroll
   for (int k = 0; k < kXPer; ++k) {
@@ -151,7 +224,7 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
     if (s < kX4) *reinterpret_cast<f32x4*>(xs + xs_phys(4 * s)) = s < in4 ? xv[k] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
-  const float part = live ? TallQ4K::compute(r, u, (gu & 1) != 0, xs) : 0.f;
+  const float part = live ? T::compute(r, u, (gu & 1) != 0, xs) : 0.f;
   // the row's U partial sums, added in lane order (reads past the wave take
   // the lane's own value; only the row's first lane stores)
   float sum = part;
@@ -164,7 +237,7 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_q4k_kernel(GroupArgs g
 
 namespace pesti_gemv {
 
-template <int U, bool S>
+template <class T, int U, bool S>
 int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   constexpr int64_t kRows = (pesti::kWave / U) * pesti::kTallWaves;
   int64_t max_out = 0;
@@ -172,23 +245,23 @@ int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   const int64_t groups = (max_out + kRows - 1) / kRows;
   GroupArgs args = g;
   void* params[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_q4k_kernel<U, S>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_kernel<T, U, S>),
                                        dim3(static_cast<unsigned>(groups), static_cast<unsigned>(g.n_ops)),
                                        dim3(pesti::kTallThreads), params, 0, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-template <bool S>
+template <class T, bool S>
 int launch_tall_s(const GroupArgs& g, hipStream_t st) {
   switch ((g.op[0].in + 127) / 128) {
-    case 1: return launch_tall_u<1, S>(g, st);
-    case 2: return launch_tall_u<2, S>(g, st);
-    case 3: return launch_tall_u<3, S>(g, st);
-    case 4: return launch_tall_u<4, S>(g, st);
-    case 5: return launch_tall_u<5, S>(g, st);
-    case 6: return launch_tall_u<6, S>(g, st);
-    case 7: return launch_tall_u<7, S>(g, st);
-    case 8: return launch_tall_u<8, S>(g, st);
+    case 1: return launch_tall_u<T, 1, S>(g, st);
+    case 2: return launch_tall_u<T, 2, S>(g, st);
+    case 3: return launch_tall_u<T, 3, S>(g, st);
+    case 4: return launch_tall_u<T, 4, S>(g, st);
+    case 5: return launch_tall_u<T, 5, S>(g, st);
+    case 6: return launch_tall_u<T, 6, S>(g, st);
+    case 7: return launch_tall_u<T, 7, S>(g, st);
+    case 8: return launch_tall_u<T, 8, S>(g, st);
     default: return PESTI_ERR_SHAPE;
   }
 }
@@ -197,10 +270,16 @@ int launch_tall_s(const GroupArgs& g, hipStream_t st) {
 // stream layout every row is a whole number of 128-weight units.
 int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
-  if (!stream_layout) return launch_tall_s<false>(g, st);
+  if (!stream_layout) return launch_tall_s<pesti::TallQ4K, false>(g, st);
   for (int i = 0; i < g.n_ops; ++i)
     if (g.op[i].in % 128 != 0 || g.op[i].in != g.op[0].in) return PESTI_ERR_SHAPE;
-  return launch_tall_s<true>(g, st);
+  return launch_tall_s<pesti::TallQ4K, true>(g, st);
+}
+
+// The same for Q5_K (row layout).
+int launch_tall_q5_k(const GroupArgs& g, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  return launch_tall_s<pesti::TallQ5K, false>(g, st);
 }
 
 }  // namespace pesti_gemv

@@ -1072,41 +1072,45 @@ def test_gemm_quant_exact_cancellation_gives_bias(fmt, m, k, n):
 
 
 # ---------------------------------------------------------------------------
-# tall Q4_K matrices at batch 1: the 128-weight-unit kernel (rows of at most
-# 1024 weights, at least 16384 rows)
+# tall Q4_K and Q5_K matrices at batch 1: the 128-weight-unit kernel (rows
+# of at most 1024 weights, at least 16384 rows)
 # ---------------------------------------------------------------------------
 TALL_ROWS = 16384
+TALL_FORMATS = ("q4_k", "q5_k")
 
 
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
 @pytest.mark.parametrize("inf", [128, 256, 384, 512, 640, 768, 800, 896, 1024])
-def test_tall_q4_k_batch_1_every_row(inf):
+def test_tall_batch_1_every_row(fmt, inf):
     out = TALL_ROWS + 37
-    packed, scales, x, bias = make("q4_k", out, inf, 140, 1)
-    y = run_gemv("q4_k", packed, scales, out, inf, x, bias)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x, bias)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall q4_k b1 in={inf}")
+    packed, scales, x, bias = make(fmt, out, inf, 140, 1)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall {fmt} b1 in={inf}")
 
 
-def test_tall_q4_k_batch_1_one_hot_gives_dequantized_column():
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
+def test_tall_batch_1_one_hot_gives_dequantized_column(fmt):
     out, inf = TALL_ROWS + 5, 896
-    packed, _, _, _ = make("q4_k", out, inf, 141)
-    w32 = oracle.dequantize_f32("q4_k", packed, out, inf)
-    for j in (0, 31, 32, 127, 128, 895):
+    packed, _, _, _ = make(fmt, out, inf, 141)
+    w32 = oracle.dequantize_f32(fmt, packed, out, inf)
+    for j in (0, 31, 32, 63, 64, 127, 128, 255, 256, 895):
         x = np.zeros((1, inf), np.float32)
         x[0, j] = 1.0
-        y = run_gemv("q4_k", packed, None, out, inf, x)
+        y = run_gemv(fmt, packed, None, out, inf, x)
         assert np.array_equal(y[0], w32[:, j]), j
 
 
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
 @pytest.mark.parametrize("d_bits", [0x0000, 0x0001, 0x0400, 0x7BFF])
-def test_tall_q4_k_batch_1_forced_scales(d_bits):
+def test_tall_batch_1_forced_scales(fmt, d_bits):
     rng = np.random.default_rng([142, d_bits])
     out, inf = TALL_ROWS + 11, 768
-    packed = synth.quant_blocks("q4_k", rng, out, inf, force_d=d_bits)
+    packed = synth.quant_blocks(fmt, rng, out, inf, force_d=d_bits)
     x = synth.activations(rng, 1, inf)
-    y = run_gemv("q4_k", packed, None, out, inf, x)
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed, out, inf, x)
-    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall q4_k b1 d={d_bits:#x}")
+    y = run_gemv(fmt, packed, None, out, inf, x)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall {fmt} b1 d={d_bits:#x}")
 
 
 def test_tall_q4_k_batch_1_padding_bytes_do_not_matter():
@@ -1124,34 +1128,52 @@ def test_tall_q4_k_batch_1_padding_bytes_do_not_matter():
     assert np.array_equal(y1, y2)
 
 
-def test_tall_q4_k_batch_1_group_equals_single_calls_bitwise():
+def test_tall_q5_k_batch_1_padding_bytes_do_not_matter():
+    out, inf = TALL_ROWS + 3, 800
+    packed, _, x, bias = make("q5_k", out, inf, 146, 1)
+    other = packed.copy().reshape(out, 4, 176)
+    rng = np.random.default_rng(147)
+    # super-block 3 holds weights 768..1023: 768..799 are real (run 0, low
+    # nibbles of bytes 48..79, fifth bit 0 of bytes 16..47); every other
+    # code bit of it is padding
+    other[:, 3, 80:] = rng.integers(0, 256, (out, 96), dtype=np.uint8)
+    other[:, 3, 48:80] = (other[:, 3, 48:80] & 0x0F) | (rng.integers(0, 16, (out, 32), dtype=np.uint8) << 4)
+    other[:, 3, 16:48] = (other[:, 3, 16:48] & 0x01) | (rng.integers(0, 128, (out, 32), dtype=np.uint8) << 1)
+    y1 = run_gemv("q5_k", packed, None, out, inf, x, bias)
+    y2 = run_gemv("q5_k", other.reshape(out, -1), None, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
+def test_tall_batch_1_group_equals_single_calls_bitwise(fmt):
     import torch
     import dequantize_mat_vec_amd as dmv
     from gpu_util import to_dev
     cases = [(TALL_ROWS + 7, 896), (TALL_ROWS + 100, 896), (TALL_ROWS + 1, 512), (300, 896)]
     ops, singles = [], []
     for n, (out, inf) in enumerate(cases):
-        packed, _, x, bias = make("q4_k", out, inf, 150 + n, 1)
-        singles.append(run_gemv("q4_k", packed, None, out, inf, x, bias))
+        packed, _, x, bias = make(fmt, out, inf, 150 + n, 1)
+        singles.append(run_gemv(fmt, packed, None, out, inf, x, bias))
         w, xd, bd = to_dev(packed.reshape(-1)), to_dev(x), to_dev(bias)
         yd = torch.zeros(out, dtype=torch.float32, device="cuda")
         ops.append((out, inf, w, xd, yd, bd, None))
-    dmv.pesti_gemv_group("q4_k", ops, 1)
+    dmv.pesti_gemv_group(fmt, ops, 1)
     torch.cuda.synchronize()
     for (out, inf, w, xd, yd, bd, _), y1 in zip(ops, singles):
         assert np.array_equal(yd.cpu().numpy(), y1[0])
 
 
-def test_tall_q4_k_batch_1_full_lm_head_sampled_rows():
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
+def test_tall_batch_1_full_lm_head_sampled_rows(fmt):
     out, inf = synth.QWEN_VOCAB, 896
     rng = np.random.default_rng([145, out, inf])
-    packed, _ = synth.matrix("q4_k", rng, out, inf)
+    packed, _ = synth.matrix(fmt, rng, out, inf)
     x = synth.activations(rng, 1, inf)
     bias = synth.bias(rng, out)
-    y = run_gemv("q4_k", packed, None, out, inf, x, bias)
+    y = run_gemv(fmt, packed, None, out, inf, x, bias)
     rows = np.unique(np.concatenate([rng.integers(0, out, 2048), [0, out - 1]]))
-    y_ref, s_ref = oracle.gemv_packed("q4_k", packed.reshape(out, -1)[rows], len(rows), inf, x, bias[rows])
-    assert_within(y[:, rows], y_ref, s_ref, GEMV_REL, "q4_k lm head b1")
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed.reshape(out, -1)[rows], len(rows), inf, x, bias[rows])
+    assert_within(y[:, rows], y_ref, s_ref, GEMV_REL, f"{fmt} lm head b1")
 
 
 # ---------------------------------------------------------------------------
