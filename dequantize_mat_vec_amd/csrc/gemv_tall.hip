@@ -1,11 +1,12 @@
-// Batch-1 mat-vec for tall Q4_K and Q5_K matrices with short rows (the LM
-// head, 151936 x 896): y = W x + b.
+// Batch-1 mat-vec for tall Q4_K, Q5_K and Q2_K matrices with short rows
+// (the LM head, 151936 x 896): y = W x + b.
 //
 // The operation is the decode step's row-major matrix-vector product with
-// the weights kept in GGUF Q4_K or Q5_K blocks ("Project scaffold: modules,
-// CLI, and correctness harness", file summaries of tensor.rs and quant.rs;
-// "PESTI - Portable Execution Substrate for Transformer Inference", "What
-// This Is"): w = d sc q - dmin m per 32-weight sub-block.
+// the weights kept in GGUF Q4_K, Q5_K or Q2_K blocks ("Project scaffold:
+// modules, CLI, and correctness harness", file summaries of tensor.rs and
+// quant.rs; "PESTI - Portable Execution Substrate for Transformer
+// Inference", "What This Is"): w = d sc q - dmin m per sub-block (32
+// weights; 16 for Q2_K).
 //
 // At batch 1 the general kernel (gemv_impl.h) spends most of a lane's
 // instructions on work that does not scale with the weights it reads - x
@@ -13,15 +14,15 @@
 // unit per lane, and 2 of each 16-lane row group stay idle on 896-weight
 // rows (14 units).  Here a lane takes a 128-weight unit (two runs of one
 // super-block: for Q4_K its 16-byte header and 64 code bytes, five 16-byte
-// loads; TallQ5K below for Q5_K) and a row takes U = in / 128 consecutive
-// lanes, so a wave holds
-// floor(64 / U) rows (9 rows of 7 lanes at 896 columns, one lane idle), and
-// a workgroup of 4 waves stages x once for 36 rows (measured on the
-// 151936 x 896 head: 2 / 4 / 8 / 16 waves 21.5 / 20.0 / 22.6 / 26.8 us).  Each weight is
-// dequantized on its own, w = (d sc 2^9)(q 2^-9) - dmin m, one rounding of
-// the exact value (the float32 weight, bit for bit), then multiplied into
-// the lane's sum; the U partial sums of a row are added in lane order by
-// cross-lane reads (a fixed order: results do not depend on timing).
+// loads; TallQ5K and TallQ2K below for Q5_K and Q2_K) and a row takes U =
+// in / 128 consecutive lanes, so a wave holds floor(64 / U) rows (9 rows of 7
+// lanes at 896 columns, one lane idle), and a workgroup of 4 waves stages x
+// once for 36 rows (measured on the 151936 x 896 head: 2 / 4 / 8 / 16 waves
+// 21.5 / 20.0 / 22.6 / 26.8 us).  Each weight is dequantized on its own, w =
+// (d sc 2^9)(q 2^-9) - dmin m, one rounding of the exact value (the float32
+// weight, bit for bit), then multiplied into the lane's sum; the U partial
+// sums of a row are added in lane order by cross-lane reads (a fixed order:
+// results do not depend on timing).
 #include "gemv_impl.h"
 
 namespace pesti {
@@ -174,6 +175,58 @@ struct TallQ5K {
   }
 };
 
+// Q2_K (84-byte super-blocks: 16 scale bytes, scale in the low nibble and
+// min in the high nibble of byte k for 16-weight sub-block k; 64 code
+// bytes from 16; d, dmin at 80).  Weight 128h + 32j + 16c + l has its
+// 2-bit code at bit 2j of code byte 32h + 16c + l, sub-block 8h + 2j + c.
+// A lane's 128-weight unit is half h = g % 2: its 32 code bytes, its 8
+// scale bytes and d, dmin (four loads).  Codes convert as q 2^-9 (the fp8
+// nibble trick) and w = (d sc 2^9)(q 2^-9) - dmin m is one rounding of the
+// exact value, as for Q4_K.
+struct TallQ2K {
+  static constexpr int kBytes = 84;
+  struct Raw { u32x4 q0, q1; uint32_t s0, s1, dd; };
+
+  __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
+    const uint8_t* sb = base + (g >> 1) * kBytes;
+    const int h = static_cast<int>(g & 1);
+    r.q0 = load_u32x4(sb + 16 + 32 * h);
+    r.q1 = load_u32x4(sb + 32 + 32 * h);
+    r.s0 = load_u32(sb + 8 * h);
+    r.s1 = load_u32(sb + 8 * h + 4);
+    r.dd = load_u32(sb + 80);
+  }
+
+  __device__ __forceinline__ static float compute(const Raw& r, int u, bool, const float* xs) {
+    const float d512 = f16_lo(r.dd) * 512.0f, dmin = f16_hi(r.dd);
+    float acc = 0.f;
+    const int x0 = 128 * u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const u32x4& qv = c ? r.q1 : r.q0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 2 * j + c;   // sub-block within the unit (scale byte k)
+        const uint32_t sbyte_v = ((k < 4 ? r.s0 : r.s1) >> (8 * (k & 3))) & 0xFFu;
+        const float ds = d512 * static_cast<float>(sbyte_v & 15u);
+        const float ndm = -(dmin * static_cast<float>(sbyte_v >> 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = t == 0 ? qv.x : (t == 1 ? qv.y : (t == 2 ? qv.z : qv.w));
+          float q0, q1, q2, q3;
+          nibbles_x512((w >> (2 * j)) & 0x03030303u, q0, q1, q2, q3);
+          const f32x4 xv = xs4(xs, x0 + 32 * j + 16 * c + 4 * t);
+          acc = fmaf(fmaf(ds, q0, ndm), xv.x, acc);
+          acc = fmaf(fmaf(ds, q1, ndm), xv.y, acc);
+          acc = fmaf(fmaf(ds, q2, ndm), xv.z, acc);
+          acc = fmaf(fmaf(ds, q3, ndm), xv.w, acc);
+        }
+      }
+    }
+    return acc;
+  }
+};
+
 // U = 128-weight units per row (row layout: rows of up to 128 U weights,
 // padded to whole super-blocks; stream layout, S: rows of exactly 128 U);
 // a wave serves 64 / U rows, a workgroup kTallWaves times that.  Measured
@@ -276,10 +329,15 @@ int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st) {
   return launch_tall_s<pesti::TallQ4K, true>(g, st);
 }
 
-// The same for Q5_K (row layout).
+// The same for Q5_K and Q2_K (row layout).
 int launch_tall_q5_k(const GroupArgs& g, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
   return launch_tall_s<pesti::TallQ5K, false>(g, st);
+}
+
+int launch_tall_q2_k(const GroupArgs& g, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  return launch_tall_s<pesti::TallQ2K, false>(g, st);
 }
 
 }  // namespace pesti_gemv

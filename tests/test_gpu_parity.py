@@ -1072,11 +1072,11 @@ def test_gemm_quant_exact_cancellation_gives_bias(fmt, m, k, n):
 
 
 # ---------------------------------------------------------------------------
-# tall Q4_K and Q5_K matrices at batch 1: the 128-weight-unit kernel (rows
-# of at most 1024 weights, at least 16384 rows)
+# tall Q4_K, Q5_K and Q2_K matrices at batch 1: the 128-weight-unit kernel
+# (rows of at most 1024 weights, at least 16384 rows)
 # ---------------------------------------------------------------------------
 TALL_ROWS = 16384
-TALL_FORMATS = ("q4_k", "q5_k")
+TALL_FORMATS = ("q4_k", "q5_k", "q2_k")
 
 
 @pytest.mark.parametrize("fmt", TALL_FORMATS)
@@ -1141,6 +1141,22 @@ def test_tall_q5_k_batch_1_padding_bytes_do_not_matter():
     other[:, 3, 16:48] = (other[:, 3, 16:48] & 0x01) | (rng.integers(0, 128, (out, 32), dtype=np.uint8) << 1)
     y1 = run_gemv("q5_k", packed, None, out, inf, x, bias)
     y2 = run_gemv("q5_k", other.reshape(out, -1), None, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+
+
+def test_tall_q2_k_batch_1_padding_bytes_do_not_matter():
+    out, inf = TALL_ROWS + 3, 800
+    packed, _, x, bias = make("q2_k", out, inf, 148, 1)
+    other = packed.copy().reshape(out, 4, 84)
+    rng = np.random.default_rng(149)
+    # super-block 3 holds weights 768..1023: 768..799 are real (half 0, bits
+    # 0-1 of code bytes 16..47, scale bytes 0 and 1); every other code bit
+    # and scale byte of it is padding (d, dmin at 80..83 are shared)
+    other[:, 3, 48:80] = rng.integers(0, 256, (out, 32), dtype=np.uint8)
+    other[:, 3, 16:48] = (other[:, 3, 16:48] & 0x03) | (rng.integers(0, 64, (out, 32), dtype=np.uint8) << 2)
+    other[:, 3, 2:16] = rng.integers(0, 256, (out, 14), dtype=np.uint8)
+    y1 = run_gemv("q2_k", packed, None, out, inf, x, bias)
+    y2 = run_gemv("q2_k", other.reshape(out, -1), None, out, inf, x, bias)
     assert np.array_equal(y1, y2)
 
 
