@@ -38,7 +38,16 @@ struct GemmArgs {
 // kg = l / 16): A row i, k = 8kg..8kg+7; B column i, the same k; C column i,
 // rows 4kg..4kg+3.  Only the pairing of A and B k-slots matters for the sum,
 // so both read the same 8 consecutive k of their row.
-constexpr int kGemmC = 2;   // k-steps per buffer
+//
+// A k-step reads 64 bytes of each of 16 rows.  When the row stride is a
+// whole number of 128-byte lines (K a multiple of 64), those 16 pieces sit
+// at the same offset in their lines and one load instruction crowds one half
+// of the memory path (K = 768 and 3072 ran 10-20% slower than K = 800 or
+// 3040).  Odd rows of W and X therefore load the two k-steps of a buffer in
+// the opposite order, so each instruction reads both halves, and pick their
+// operands back in step order: the matrix cores see the same operands in the
+// same order, so the sums are unchanged bit for bit.
+constexpr int kGemmC = 2;   // k-steps per buffer (even: swapped in pairs)
 
 template <int NW, int MT, int C>
 struct GemmBuf {
@@ -46,7 +55,7 @@ struct GemmBuf {
   half8 x[C][MT];
 };
 
-template <int NW, int MT, int C>
+template <int NW, int MT, int C, bool SW>
 __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
   __shared__ floatx4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
@@ -69,10 +78,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
     xrow[t] = a.x + xm * a.k + 8 * kg;
   }
 
+  // With SW (K a multiple of 64) slot c of a buffer holds k-step
+  // s + (c ^ swap); W row i and X rows 16t + i share the parity of i.
+  static_assert(C % 2 == 0, "k-steps are swapped in pairs");
+  const int swap = SW ? (i & 1) : 0;
   auto load = [&](int s, GemmBuf<NW, MT, C>& b) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int sc = s + c < s_end ? s + c : (s_begin < ksteps ? s_begin : 0);
+      const int sl = s + (c ^ swap);
+      const int sc = sl < s_end ? sl : (s_begin < ksteps ? s_begin : 0);
       b.w[c] = *reinterpret_cast<const half8*>(wrow + 32 * sc);
 #pragma unroll
       for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const half8*>(xrow[t] + 32 * sc);
@@ -84,10 +98,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
   auto mma = [&](int s, const GemmBuf<NW, MT, C>& b) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const half8 wv = s + c < s_end ? b.w[c] : half8{};
+      const half8 wsel = swap ? b.w[c ^ 1] : b.w[c];
+      const half8 wv = s + c < s_end ? wsel : half8{};
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, acc[t], 0, 0, 0);
+      for (int t = 0; t < MT; ++t) {
+        const half8 xv = swap ? b.x[c ^ 1][t] : b.x[c][t];
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, acc[t], 0, 0, 0);
+      }
     }
   };
 
@@ -251,9 +268,10 @@ int launch_mfma_t(const GemmArgs& a, hipStream_t st) {
   dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
   GemmArgs args = a;
   void* params[] = {&args};
-  hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC>), grid,
-      dim3(NW * 64), params, 0, st);
+  const void* fn = a.k % 64 == 0
+                       ? reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC, true>)
+                       : reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC, false>);
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(NW * 64), params, 0, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 

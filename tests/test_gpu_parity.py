@@ -337,6 +337,10 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               (20, 0, 37), (5, 0, 9), (8, 8192, 40), (3, 16384, 24), (48, 16384, 20),
               # a ragged K split: 3 k-steps over the workgroup's wavefronts
               (33, 96, 17),
+              # K a multiple of 64 (odd rows load each pair of k-steps in
+              # swapped order): odd step counts per wavefront, one step per
+              # wavefront, and the 8- and 16-wavefront launch shapes
+              (33, 192, 40), (16, 576, 40), (17, 64, 70), (16, 576, 1600), (40, 1344, 1540),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
               (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
