@@ -277,10 +277,16 @@ int launch_mfma_t(const GemmArgs& a, hipStream_t st) {
 
 // Launch shape by how many 16-column tiles the layer has: narrow layers
 // (under 96 tiles, e.g. N = 768) give every 16-row tile of X its own
-// workgroup of 8 K slices, so that enough workgroups stream W; wider ones
-// let a workgroup of 16 K slices reuse each W load for 2 or 4 tiles of X.
+// workgroup, so that enough workgroups stream W; wider ones let a
+// workgroup of 16 K slices reuse each W load for 2 or 4 tiles of X.  A
+// narrow layer's workgroup takes 16 K slices when K is short (at most 32
+// k-steps: one buffer round per wavefront instead of two) or long (over 128
+// k-steps), else 8 (measured at N = 768 and 896, m = 16..64: K = 768 4.05 ->
+// 3.43 us, K = 4864 11.3 -> 10.6 us, K = 1536..3072 0.3-1.1 us slower).
 int launch_mfma(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
+  const int64_t ksteps = a.k / 32;
+  if (tiles_n < 96 && (ksteps <= 32 || ksteps > 128)) return launch_mfma_t<16, 1>(a, st);
   if (tiles_n < 96) return launch_mfma_t<8, 1>(a, st);
   if (tiles_m <= 1) return launch_mfma_t<16, 1>(a, st);
   if (tiles_m <= 2) return launch_mfma_t<16, 2>(a, st);

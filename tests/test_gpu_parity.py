@@ -341,6 +341,8 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               # swapped order): odd step counts per wavefront, one step per
               # wavefront, and the 8- and 16-wavefront launch shapes
               (33, 192, 40), (16, 576, 40), (17, 64, 70), (16, 576, 1600), (40, 1344, 1540),
+              # narrow layers over 128 k-steps (16 K slices): the Qwen down shape
+              (16, 4864, 896), (33, 4128, 70),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
               (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
