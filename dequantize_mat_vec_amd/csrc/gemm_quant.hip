@@ -110,6 +110,7 @@ struct QPolQ4_K {
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
+  static constexpr int kNarrowLongNW = 16;
   struct Step { uint32_t c[2]; u32x4 hdr; uint32_t j; };
 
   // Steps s and s + 1 (s even: sub-blocks 2g and 2g + 1, the low and high
@@ -339,6 +340,7 @@ struct QPolQ5_K {
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
+  static constexpr int kNarrowLongNW = 16;
   struct Step { uint32_t c[2]; uint32_t h[2]; u32x4 hdr; uint32_t j; };
 
   // Steps s and s + 1 (s even) share all their bytes: 5 loads for the pair
@@ -768,12 +770,19 @@ struct QBuf {
   qhalf8 x[2][MT];
 };
 
+// Wavefronts per workgroup on narrow layers of over 128 k-steps (8 unless
+// the policy says otherwise).
+template <class Q, class = void>
+struct NarrowLongNW { static constexpr int value = 8; };
+template <class Q>
+struct NarrowLongNW<Q, std::void_t<decltype(Q::kNarrowLongNW)>> { static constexpr int value = Q::kNarrowLongNW; };
+
 template <class Q, class = void>
 struct PairLoad : std::false_type {};
 template <class Q>
 struct PairLoad<Q, std::void_t<decltype(&Q::load_pair)>> : std::true_type {};
 
-template <class Q, int NW, int MT>
+template <class Q, int NW, int MT, bool SW>
 __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   __shared__ qfloat4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
@@ -808,6 +817,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   // and are skipped.  Formats with a pair load read steps s and s + 1 (s is
   // even, so both lie in one super-block, and s + 1 is inside the row's
   // padded blocks even past the last step) in one go.
+  // X rows of whole 128-byte lines (SW: K a multiple of 64, at most 1024):
+  // odd rows load the two steps of a buffer in the opposite order (x slot
+  // c holds step s + (c ^ swap)) and pick them back, as in the binary16
+  // GEMM.  Same operands, same order: the sums are unchanged bit for bit.
+  const int swap = SW ? (i & 1) : 0;
   auto load = [&](int s, QBuf<Q, MT>& b) {
     if constexpr (PairLoad<Q>::value) {
       const int s0 = s < s_end ? s : (s_begin < ksteps ? s_begin : 0);
@@ -816,9 +830,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int sc = s + c < s_end ? s + c : (s_begin < ksteps ? s_begin : 0);
+      const int sl = s + (c ^ swap);
+      const int sx = sl < s_end ? sl : (s_begin < ksteps ? s_begin : 0);
       if constexpr (!PairLoad<Q>::value) Q::load(wrow, sc, kg, b.w[c]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const qhalf8*>(xrow[t] + 32 * sc);
+      for (int t = 0; t < MT; ++t) b.x[c][t] = *reinterpret_cast<const qhalf8*>(xrow[t] + 32 * sx);
     }
   };
   qfloat4 acc[MT];
@@ -836,7 +852,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
         const qhalf8 wv = Q::codes(b.w[c], pt, kg);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], wv, qfloat4{0.f, 0.f, 0.f, 0.f},
+          const qhalf8 xv = swap ? b.x[c ^ 1][t] : b.x[c][t];
+          const qfloat4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, qfloat4{0.f, 0.f, 0.f, 0.f},
                                                                    0, 0, 0);
           acc[t] += ds * p;
           if constexpr (HalfMins<Q>::value) {
@@ -846,15 +863,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
             const float dm_other = __shfl_xor(dm, 32, kWave);
             const bool first = kg < 2;
             const qhalf8 zeros = {0, 0, 0, 0, 0, 0, 0, 0};
-            const qfloat4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], first ? ones : zeros,
+            const qfloat4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, first ? ones : zeros,
                                                                       qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            const qfloat4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], first ? zeros : ones,
+            const qfloat4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, first ? zeros : ones,
                                                                       qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             acc[t] -= (first ? dm : dm_other) * s0;
             acc[t] -= (first ? dm_other : dm) * s1;
           } else if constexpr (Q::kMin) {
             // the step's sum of x (ones)
-            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.x[c][t], ones,
+            const qfloat4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, ones,
                                                                       qfloat4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             acc[t] -= dm * sx;
           }
@@ -912,23 +929,30 @@ __global__ __launch_bounds__(256) void gemm_quant_bias_kernel(QGemmArgs a) {
 namespace {
 
 using pesti::QGemmArgs;
+using pesti::NarrowLongNW;
 
 template <class Q, int NW, int MT>
 int launch_q(const QGemmArgs& a, hipStream_t st) {
   dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
   QGemmArgs args = a;
   void* params[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT>),
-                                       grid, dim3(NW * 64), params, 0, st);
+  const bool sw = a.k % 64 == 0 && a.k <= 1024;
+  const void* fn = sw ? reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>)
+                      : reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, false>);
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(NW * 64), params, 0, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
 // Launch shape as for the binary16 GEMM: narrow layers give every 16-row
-// tile of X its own workgroup of 8 K slices; wider ones share each W load
-// across 2 or 4 row tiles in workgroups of 16 K slices.
+// tile of X its own workgroup of 8 K slices (16 for Q4_K and Q5_K over 128
+// k-steps: Qwen down m16 10.4 -> 8.9 and 11.3 -> 10.9 us; the other formats
+// measured the same or slower with 16); wider ones share each W load across
+// 2 or 4 row tiles in workgroups of 16 K slices.
 template <class Q>
 int launch_quant(const QGemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
+  constexpr int kLongNW = NarrowLongNW<Q>::value;
+  if (tiles_n < 96 && a.k / 32 > 128) return launch_q<Q, kLongNW, 1>(a, st);
   if (tiles_n < 96) return launch_q<Q, 8, 1>(a, st);
   if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, st);
   if (tiles_m <= 2) return launch_q<Q, 16, 2>(a, st);
