@@ -370,6 +370,12 @@ def run_suite(lib, args):
             x16 = torch.from_numpy(inp["x16"].view(np.uint16)).to(dev)
             b = torch.from_numpy(inp["bias"]).to(dev)
             y = torch.empty(m * n, dtype=torch.float32, device=dev)
+            # the GEMMs run with a workspace (split K where the shape asks for it)
+            gfid = _lib.GEMM_FORMAT_IDS[fmt if kind == "qgemm" else "f16"]
+            ws_bytes = lib.pesti_gemm_workspace_bytes(gfid, m, n, k)
+            if ws_bytes < 0:
+                raise RuntimeError(f"{name}: workspace query status {ws_bytes}")
+            gws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         copies = max(2, int(np.ceil(640e6 / nbytes)))
         host = torch.from_numpy(np.ascontiguousarray(packed).reshape(-1))
         ws = [host.to(dev) for _ in range(copies)]
@@ -394,12 +400,9 @@ def run_suite(lib, args):
                       if fmt in ("i8row", "i4row") else
                       getattr(lib, f"pesti_gemv_{fmt}")(out, inf, ws[i % copies].data_ptr(),
                                                        x.data_ptr(), y.data_ptr(), None, batch, sh))
-            elif kind == "qgemm":
-                st = getattr(lib, f"pesti_gemm_{fmt}_smallm")(m, n, k, ws[i % copies].data_ptr(),
-                                                              x16.data_ptr(), y.data_ptr(), b.data_ptr(), sh)
             else:
-                st = lib.pesti_gemm_f16_smallm(m, n, k, ws[i % copies].data_ptr(), x16.data_ptr(),
-                                               y.data_ptr(), b.data_ptr(), sh)
+                st = lib.pesti_gemm_smallm_ws(gfid, m, n, k, ws[i % copies].data_ptr(), x16.data_ptr(),
+                                              y.data_ptr(), b.data_ptr(), gws.data_ptr(), ws_bytes, sh)
             if st != 0:
                 raise RuntimeError(f"{name}: status {st}")
 

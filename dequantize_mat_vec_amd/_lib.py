@@ -22,9 +22,12 @@ PESTI_ERR_BATCH = -3
 PESTI_ERR_ALIGN = -4
 PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
+PESTI_ERR_WORKSPACE = -7
 
 FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7,
               "q4_k_stream": 8}
+# formats of the small-M GEMM calls that take a format id
+GEMM_FORMAT_IDS = {"f16": 16, "q8_0": 0, "q2_k": 5, "q3_k": 6, "q4_k": 1, "q5_k": 4, "q6_k": 2}
 
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _c_int, _c_char_p = ctypes.c_int, ctypes.c_char_p
@@ -48,6 +51,8 @@ _SIGNATURES = {
     "pesti_gemm_q2_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q3_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_q5_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "pesti_gemm_workspace_bytes": (_i64, [_i32, _i64, _i64, _i64]),
+    "pesti_gemm_smallm_ws": (_c_int, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k_stream": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -235,6 +240,26 @@ def pesti_gemm_q4_k_smallm(m, out_features, in_features, blocks, x, y, bias=None
 def pesti_gemm_q6_k_smallm(m, out_features, in_features, blocks, x, y, bias=None, stream=None):
     return _gemm_q("pesti_gemm_q6_k_smallm", m, out_features, in_features, blocks, x, y, bias,
                    stream)
+
+
+def _gemm_fid(fmt):
+    return GEMM_FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def pesti_gemm_workspace_bytes(fmt, m, out_features, in_features):
+    """Workspace bytes the split-K form needs (0: none); negative status on bad input."""
+    return int(load().pesti_gemm_workspace_bytes(_gemm_fid(fmt), m, out_features, in_features))
+
+
+def pesti_gemm_smallm_ws(fmt, m, out_features, in_features, w, x, y, bias=None, workspace=None,
+                         workspace_bytes=None, stream=None):
+    """Small-M GEMM of format `fmt` ("f16" or a block format) with a caller's
+    workspace (a device tensor, or a pointer with workspace_bytes)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return _check("pesti_gemm_smallm_ws", load().pesti_gemm_smallm_ws(
+        _gemm_fid(fmt), m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def gemv_ops(ops):

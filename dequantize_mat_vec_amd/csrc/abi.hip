@@ -71,6 +71,7 @@ const char* pesti_strerror(int status) {
     case PESTI_ERR_ALIGN: return "pointer not aligned (16 bytes for data, 4 for bias/scales)";
     case PESTI_ERR_LAUNCH: return "HIP kernel launch failed";
     case PESTI_ERR_DEVICE: return "current HIP device is missing or not gfx950";
+    case PESTI_ERR_WORKSPACE: return "GEMM workspace missing or smaller than pesti_gemm_workspace_bytes";
     default: return "unknown status";
   }
 }

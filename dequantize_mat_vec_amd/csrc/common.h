@@ -193,6 +193,32 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 // LDS limit.  Returns PESTI_OK or PESTI_ERR_DEVICE.
 int current_device(int* device, size_t* lds_per_group);
 
+// Small-M GEMMs on narrow layers (under 96 16-column tiles) with long rows
+// (over 128 k-steps) leave most compute units idle: a workgroup per column
+// tile and row tile of X.  There the K range is split over `splits`
+// workgroups per tile, each writing its partial tile to a float32 workspace
+// [splits][m][n], and a second launch sums the partials in split order and
+// adds the bias.  At most 4 splits, so that about 256 workgroups run; the
+// binary16 GEMM splits only single row tiles of X (it measured slower at
+// two), and below m = 16 it runs on the vector ALUs, unsplit.
+inline int gemm_splits(bool f16, int64_t m, int64_t n, int64_t k) {
+  const int64_t tiles_n = (n + 15) / 16, tiles_m = (m + 15) / 16;
+  if (m <= 0 || n <= 0 || tiles_n >= 96 || k / 32 <= 128) return 1;
+  if (f16 && (m < 16 || tiles_m > 1)) return 1;
+  const int64_t s = 256 / (tiles_n * tiles_m);
+  return s >= 4 ? 4 : (s >= 2 ? static_cast<int>(s) : 1);
+}
+
+// The GEMM entry points behind the C ABI.  ws: nullptr, or a device buffer
+// of gemm_splits(...) * m * n floats (16-byte aligned) for the split form.
+int gemm_f16_run(int64_t m, int64_t n, int64_t k, const uint16_t* w, const uint16_t* x, float* y,
+                 const float* bias, float* ws, hipStream_t st);
+int gemm_quant_run(int32_t format, int64_t m, int64_t n, int64_t k, const void* blocks, const uint16_t* x,
+                   float* y, const float* bias, float* ws, hipStream_t st);
+// y[e] = sum over s < splits of part[s][e] (in order) + bias[e % n].
+int launch_split_sum(int64_t m, int64_t n, const float* part, int splits, const float* bias, float* y,
+                     hipStream_t st);
+
 // Largest batch that fits LDS when one staged row takes `bytes_per_row`.
 inline int batch_per_launch(size_t lds_limit, size_t bytes_per_row, size_t fixed_bytes, int batch) {
   if (bytes_per_row == 0) return batch;

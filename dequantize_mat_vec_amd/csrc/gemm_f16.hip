@@ -55,8 +55,11 @@ struct GemmBuf {
   half8 x[C][MT];
 };
 
+// Split form (kpart non-null, gridDim.z = splits > 1): workgroup z takes
+// the z-th run of whole k-step pairs and writes its partial tile, without
+// bias, to kpart[z][m][n]; a second launch sums them.
 template <int NW, int MT, int C, bool SW>
-__global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a, float* kpart) {
   __shared__ floatx4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
@@ -65,9 +68,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
   const int ksteps = static_cast<int>(a.k / 32);
-  const int per_wave = (ksteps + NW - 1) / NW;
-  const int s_begin = wave * per_wave;
-  const int s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
+  const int split = static_cast<int>(blockIdx.z);
+  const int per_split = 2 * ((ksteps + 2 * static_cast<int>(gridDim.z) - 1) / (2 * static_cast<int>(gridDim.z)));
+  const int g_begin = per_split * split < ksteps ? per_split * split : ksteps;
+  const int g_end = g_begin + per_split < ksteps ? g_begin + per_split : ksteps;
+  const int per_wave = (g_end - g_begin + NW - 1) / NW;
+  const int s_begin = g_begin + wave * per_wave;
+  const int s_end = s_begin + per_wave < g_end ? s_begin + per_wave : g_end;
 
   const int64_t wn = n0 + i < a.n ? n0 + i : a.n - 1;
   const uint16_t* wrow = a.w + wn * a.k + 8 * kg;
@@ -133,12 +140,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_f16_mfma_kernel(GemmArgs a) {
     }
     const int64_t col = n0 + (l & 15);
     if (col < a.n) {
-      const float bv = a.bias ? a.bias[col] : 0.f;
+      const float bv = kpart ? 0.f : (a.bias ? a.bias[col] : 0.f);
+      float* dst = kpart ? kpart + split * a.m * a.n : a.y;
       const float v[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = m0 + 16 * t + 4 * (l >> 4) + q;
-        if (row < a.m) a.y[row * a.n + col] = v[q] + bv;
+        if (row < a.m) dst[row * a.n + col] = v[q] + bv;
       }
     }
   }
@@ -264,15 +272,19 @@ int launch_valu_b(const GemmArgs& a, int b, hipStream_t st) {
 }
 
 template <int NW, int MT>
-int launch_mfma_t(const GemmArgs& a, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
+int launch_mfma_t(const GemmArgs& a, float* ws, hipStream_t st) {
+  const int splits = ws ? pesti_host::gemm_splits(true, a.m, a.n, a.k) : 1;
+  float* kpart = splits > 1 ? ws : nullptr;
+  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)),
+            static_cast<unsigned>(splits));
   GemmArgs args = a;
-  void* params[] = {&args};
+  void* params[] = {&args, &kpart};
   const void* fn = a.k % 64 == 0
                        ? reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC, true>)
                        : reinterpret_cast<const void*>(&pesti::gemm_f16_mfma_kernel<NW, MT, pesti::kGemmC, false>);
   hipError_t e = hipLaunchKernel(fn, grid, dim3(NW * 64), params, 0, st);
-  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+  if (e != hipSuccess) return PESTI_ERR_LAUNCH;
+  return splits > 1 ? pesti_host::launch_split_sum(a.m, a.n, kpart, splits, a.bias, a.y, st) : PESTI_OK;
 }
 
 // Launch shape by how many 16-column tiles the layer has: narrow layers
@@ -283,14 +295,14 @@ int launch_mfma_t(const GemmArgs& a, hipStream_t st) {
 // k-steps: one buffer round per wavefront instead of two) or long (over 128
 // k-steps), else 8 (measured at N = 768 and 896, m = 16..64: K = 768 4.05 ->
 // 3.43 us, K = 4864 11.3 -> 10.6 us, K = 1536..3072 0.3-1.1 us slower).
-int launch_mfma(const GemmArgs& a, hipStream_t st) {
+int launch_mfma(const GemmArgs& a, float* ws, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
   const int64_t ksteps = a.k / 32;
-  if (tiles_n < 96 && (ksteps <= 32 || ksteps > 128)) return launch_mfma_t<16, 1>(a, st);
-  if (tiles_n < 96) return launch_mfma_t<8, 1>(a, st);
-  if (tiles_m <= 1) return launch_mfma_t<16, 1>(a, st);
-  if (tiles_m <= 2) return launch_mfma_t<16, 2>(a, st);
-  return launch_mfma_t<16, 4>(a, st);
+  if (tiles_n < 96 && (ksteps <= 32 || ksteps > 128)) return launch_mfma_t<16, 1>(a, ws, st);
+  if (tiles_n < 96) return launch_mfma_t<8, 1>(a, ws, st);
+  if (tiles_m <= 1) return launch_mfma_t<16, 1>(a, nullptr, st);
+  if (tiles_m <= 2) return launch_mfma_t<16, 2>(a, nullptr, st);
+  return launch_mfma_t<16, 4>(a, nullptr, st);
 }
 
 // binary16 weights for the wide-layer kernel: a unit is one k-step, 32
@@ -315,9 +327,8 @@ struct WPolF16 {
 
 }  // namespace
 
-extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
-                                     const uint16_t* w, const uint16_t* x, float* y,
-                                     const float* bias, void* stream) {
+int pesti_host::gemm_f16_run(int64_t m, int64_t out_features, int64_t in_features, const uint16_t* w,
+                             const uint16_t* x, float* y, const float* bias, float* ws, hipStream_t sh) {
   if (out_features < 0 || in_features < 0) return PESTI_ERR_SHAPE;
   if (m < 0 || m > PESTI_MAX_GEMM_M) return PESTI_ERR_BATCH;
   if (m == 0 || out_features == 0) return PESTI_OK;
@@ -330,7 +341,6 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
   size_t lds_limit = 0;
   int st = pesti_host::current_device(&dev, &lds_limit);
   if (st != PESTI_OK) return st;
-  hipStream_t sh = static_cast<hipStream_t>(stream);
   GemmArgs a{w, x, y, bias, m, out_features, in_features};
   if (in_features == 0) {
     void* params[] = {&a};
@@ -345,7 +355,7 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
                         2 * in_features},
         lds_limit, sh);
     if (wide != 1) return wide;
-    return launch_mfma(a, sh);
+    return launch_mfma(a, ws, sh);
   }
   // m < 16: rows of X in chunks of up to 8 as a batch of binary16 mat-vecs;
   // 32 lanes per W row holding up to 2 units each (rows of up to 2048
@@ -370,4 +380,11 @@ extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in
     if (r != PESTI_OK) return r;
   }
   return PESTI_OK;
+}
+
+extern "C" int pesti_gemm_f16_smallm(int64_t m, int64_t out_features, int64_t in_features,
+                                     const uint16_t* w, const uint16_t* x, float* y,
+                                     const float* bias, void* stream) {
+  return pesti_host::gemm_f16_run(m, out_features, in_features, w, x, y, bias, nullptr,
+                                  static_cast<hipStream_t>(stream));
 }

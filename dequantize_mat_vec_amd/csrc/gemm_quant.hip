@@ -443,6 +443,9 @@ struct QPolQ2_K {
   static constexpr bool kHalfMins = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
+  // The X pair swap takes this kernel from 63 to 70 VGPRs, past the 64 at
+  // which two 16-wavefront workgroups fit a compute unit.
+  static constexpr bool kXSwap = false;
   struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
 
   // Steps s and s + 1 (s even: j and j + 1 of one half h) share their code
@@ -770,6 +773,12 @@ struct QBuf {
   qhalf8 x[2][MT];
 };
 
+// Whether the X pair swap is taken (unless the policy says otherwise).
+template <class Q, class = void>
+struct XSwap { static constexpr bool value = true; };
+template <class Q>
+struct XSwap<Q, std::void_t<decltype(Q::kXSwap)>> { static constexpr bool value = Q::kXSwap; };
+
 // Wavefronts per workgroup on narrow layers of over 128 k-steps (8 unless
 // the policy says otherwise).
 template <class Q, class = void>
@@ -782,8 +791,11 @@ struct PairLoad : std::false_type {};
 template <class Q>
 struct PairLoad<Q, std::void_t<decltype(&Q::load_pair)>> : std::true_type {};
 
+// Split form (kpart non-null, gridDim.z = splits > 1): workgroup z takes
+// the z-th run of whole k-step pairs and writes its partial tile, without
+// bias, to kpart[z][m][n]; a second launch sums them.
 template <class Q, int NW, int MT, bool SW>
-__global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
+__global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a, float* kpart) {
   __shared__ qfloat4 part[NW][MT][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
@@ -792,11 +804,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
   const int ksteps = static_cast<int>(a.k / 32);
-  // Slices of whole k-step pairs.
-  const int pairs = (ksteps + 1) / 2;
+  // Slices of whole k-step pairs (of the workgroup's split of K).
+  const int split = static_cast<int>(blockIdx.z);
+  const int split_pairs = ((ksteps + 1) / 2 + static_cast<int>(gridDim.z) - 1) / static_cast<int>(gridDim.z);
+  const int g_begin = 2 * split_pairs * split < ksteps ? 2 * split_pairs * split : ksteps;
+  const int g_end = g_begin + 2 * split_pairs < ksteps ? g_begin + 2 * split_pairs : ksteps;
+  const int pairs = (g_end - g_begin + 1) / 2;
   const int per_wave = 2 * ((pairs + NW - 1) / NW);
-  const int s_begin = wave * per_wave;
-  const int s_end = s_begin + per_wave < ksteps ? s_begin + per_wave : ksteps;
+  const int s_begin = g_begin + wave * per_wave;
+  const int s_end = s_begin + per_wave < g_end ? s_begin + per_wave : g_end;
 
   const int64_t wn = n0 + i < a.n ? n0 + i : a.n - 1;
   // The bias of the lane's output column, loaded first (branch-free: without
@@ -906,12 +922,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_quant_kernel(QGemmArgs a) {
     for (int w = 1; w < NW; ++w) r += part[w][t][l];
     const int64_t col = n0 + (l & 15);
     if (col < a.n) {
-      const float bv = bias_v;   // e = threadIdx.x: column n0 + i
+      const float bv = kpart ? 0.f : bias_v;   // e = threadIdx.x: column n0 + i
+      float* dst = kpart ? kpart + split * a.m * a.n : a.y;
       const float v[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = m0 + 16 * t + 4 * (l >> 4) + q;
-        if (row < a.m) a.y[row * a.n + col] = v[q] + bv;
+        if (row < a.m) dst[row * a.n + col] = v[q] + bv;
       }
     }
   }
@@ -932,15 +949,21 @@ using pesti::QGemmArgs;
 using pesti::NarrowLongNW;
 
 template <class Q, int NW, int MT>
-int launch_q(const QGemmArgs& a, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)));
+int launch_q(const QGemmArgs& a, float* ws, hipStream_t st) {
+  const int splits = ws ? pesti_host::gemm_splits(false, a.m, a.n, a.k) : 1;
+  float* kpart = splits > 1 ? ws : nullptr;
+  dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)),
+            static_cast<unsigned>(splits));
   QGemmArgs args = a;
-  void* params[] = {&args};
-  const bool sw = a.k % 64 == 0 && a.k <= 1024;
-  const void* fn = sw ? reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>)
-                      : reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, false>);
+  void* params[] = {&args, &kpart};
+  const void* fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, false>);
+  if constexpr (pesti::XSwap<Q>::value) {
+    if (a.k % 64 == 0 && a.k <= 1024)
+      fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>);
+  }
   const hipError_t e = hipLaunchKernel(fn, grid, dim3(NW * 64), params, 0, st);
-  return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
+  if (e != hipSuccess) return PESTI_ERR_LAUNCH;
+  return splits > 1 ? pesti_host::launch_split_sum(a.m, a.n, kpart, splits, a.bias, a.y, st) : PESTI_OK;
 }
 
 // Launch shape as for the binary16 GEMM: narrow layers give every 16-row
@@ -949,19 +972,19 @@ int launch_q(const QGemmArgs& a, hipStream_t st) {
 // measured the same or slower with 16); wider ones share each W load across
 // 2 or 4 row tiles in workgroups of 16 K slices.
 template <class Q>
-int launch_quant(const QGemmArgs& a, hipStream_t st) {
+int launch_quant(const QGemmArgs& a, float* ws, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
   constexpr int kLongNW = NarrowLongNW<Q>::value;
-  if (tiles_n < 96 && a.k / 32 > 128) return launch_q<Q, kLongNW, 1>(a, st);
-  if (tiles_n < 96) return launch_q<Q, 8, 1>(a, st);
-  if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, st);
-  if (tiles_m <= 2) return launch_q<Q, 16, 2>(a, st);
-  return launch_q<Q, 16, 4>(a, st);
+  if (tiles_n < 96 && a.k / 32 > 128) return launch_q<Q, kLongNW, 1>(a, ws, st);
+  if (tiles_n < 96) return launch_q<Q, 8, 1>(a, nullptr, st);
+  if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, nullptr, st);
+  if (tiles_m <= 2) return launch_q<Q, 16, 2>(a, nullptr, st);
+  return launch_q<Q, 16, 4>(a, nullptr, st);
 }
 
 template <class Q, class W>
 int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
-               const uint16_t* x, float* y, const float* bias, int64_t row_bytes, void* stream) {
+               const uint16_t* x, float* y, const float* bias, int64_t row_bytes, float* ws, hipStream_t sh) {
   if (out_features < 0 || in_features < 0) return PESTI_ERR_SHAPE;
   if (m < 0 || m > PESTI_MAX_GEMM_M) return PESTI_ERR_BATCH;
   if (m == 0 || out_features == 0) return PESTI_OK;
@@ -974,7 +997,6 @@ int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void*
   size_t lds_limit = 0;
   const int st = pesti_host::current_device(&dev, &lds_limit);
   if (st != PESTI_OK) return st;
-  hipStream_t sh = static_cast<hipStream_t>(stream);
   QGemmArgs a{static_cast<const uint8_t*>(blocks), x, y, bias, m, out_features, in_features, row_bytes};
   const int wide = pesti_host::launch_wide<W>(
       pesti::WideArgs{a.w, x, y, bias, m, out_features, in_features, row_bytes}, lds_limit, sh);
@@ -986,47 +1008,68 @@ int gemm_quant(int64_t m, int64_t out_features, int64_t in_features, const void*
                                          dim3(256), params, 0, sh);
     return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
   }
-  return launch_quant<Q>(a, sh);
+  return launch_quant<Q>(a, ws, sh);
 }
 
 }  // namespace
+
+int pesti_host::gemm_quant_run(int32_t format, int64_t m, int64_t n, int64_t k, const void* blocks,
+                               const uint16_t* x, float* y, const float* bias, float* ws, hipStream_t st) {
+  using namespace pesti;
+  switch (format) {
+    case PESTI_FMT_Q8_0:
+      return gemm_quant<QPolQ8_0, WPolQ8_0>(m, n, k, blocks, x, y, bias, (k / 32) * 34, ws, st);
+    case PESTI_FMT_Q4_K:
+      return gemm_quant<QPolQ4_K, WPolQ4_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 144, ws, st);
+    case PESTI_FMT_Q2_K:
+      return gemm_quant<QPolQ2_K, WPolQ2_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 84, ws, st);
+    case PESTI_FMT_Q3_K:
+      return gemm_quant<QPolQ3_K, WPolQ3_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 110, ws, st);
+    case PESTI_FMT_Q5_K:
+      return gemm_quant<QPolQ5_K, WPolQ5_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 176, ws, st);
+    case PESTI_FMT_Q6_K:
+      return gemm_quant<QPolQ6_K, WPolQ6_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 210, ws, st);
+    default:
+      return PESTI_ERR_SHAPE;
+  }
+}
 
 extern "C" {
 
 int pesti_gemm_q8_0_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ8_0, pesti::WPolQ8_0>(m, out_features, in_features, blocks, x, y, bias,
-                                     (in_features / 32) * 34, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q8_0, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int pesti_gemm_q4_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ4_K, pesti::WPolQ4_K>(m, out_features, in_features, blocks, x, y, bias,
-                                     ((in_features + 255) / 256) * 144, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q4_K, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int pesti_gemm_q2_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ2_K, pesti::WPolQ2_K>(m, out_features, in_features, blocks, x, y, bias,
-                                     ((in_features + 255) / 256) * 84, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q2_K, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int pesti_gemm_q3_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ3_K, pesti::WPolQ3_K>(m, out_features, in_features, blocks, x, y, bias,
-                                     ((in_features + 255) / 256) * 110, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q3_K, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int pesti_gemm_q5_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ5_K, pesti::WPolQ5_K>(m, out_features, in_features, blocks, x, y, bias,
-                                     ((in_features + 255) / 256) * 176, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q5_K, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features, const void* blocks,
                            const uint16_t* x, float* y, const float* bias, void* stream) {
-  return gemm_quant<pesti::QPolQ6_K, pesti::WPolQ6_K>(m, out_features, in_features, blocks, x, y, bias,
-                                     ((in_features + 255) / 256) * 210, stream);
+  return pesti_host::gemm_quant_run(PESTI_FMT_Q6_K, m, out_features, in_features, blocks, x, y, bias, nullptr,
+                                    static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

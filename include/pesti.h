@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PESTI_ABI_VERSION 2
+#define PESTI_ABI_VERSION 3
 
 #define PESTI_OK 0
 #define PESTI_ERR_NULL (-1)   /* a required pointer is NULL                 */
@@ -86,6 +86,7 @@ extern "C" {
 #define PESTI_ERR_ALIGN (-4)  /* a pointer breaks the alignment rule above  */
 #define PESTI_ERR_LAUNCH (-5) /* the HIP launch reported an error           */
 #define PESTI_ERR_DEVICE (-6) /* current device is not gfx950, or no device */
+#define PESTI_ERR_WORKSPACE (-7) /* GEMM workspace missing or too small     */
 
 #define PESTI_FMT_Q8_0 0
 #define PESTI_FMT_Q4_K 1
@@ -96,6 +97,8 @@ extern "C" {
 #define PESTI_FMT_Q3_K 6
 #define PESTI_FMT_I4ROW 7
 #define PESTI_FMT_Q4_K_STREAM 8
+/* binary16 weights [out][in]: for the small-M GEMM calls that take a format */
+#define PESTI_FMT_F16 16
 
 #define PESTI_MAX_BATCH 8
 #define PESTI_MAX_IN_FEATURES 32768
@@ -286,6 +289,33 @@ int pesti_gemm_q5_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
 int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
                            const void* blocks, const uint16_t* x, float* y,
                            const float* bias, void* stream);
+
+/* --- the same GEMMs with a caller's workspace (split K) -------------------
+ * Narrow layers (fewer than 96 16-column tiles, e.g. the 896-wide down
+ * projection) with long rows (in_features over 4096) run one workgroup per
+ * output tile and leave most compute units idle.  With a workspace, K is
+ * split over 2..4 workgroups per tile (more workgroups for fewer row tiles
+ * of X; binary16 only at m 16), each writing its partial tile to the
+ * workspace, and a second launch on the same stream sums the partials in a
+ * fixed order and adds the bias: results do not depend on timing, but the
+ * summation order differs from the call without workspace (same bound).
+ *
+ * pesti_gemm_workspace_bytes returns the bytes the split needs for this
+ * format (PESTI_FMT_F16 or one of the six block formats) and shape: 0 when
+ * the shape does not split, at most 384 KiB; negative PESTI_ERR_* for an
+ * unknown format or a bad shape.  Host-only, no device needed.
+ *
+ * pesti_gemm_smallm_ws: arguments as for pesti_gemm_<format>_smallm (w is
+ * the binary16 W or the packed blocks), plus `workspace`, device memory of
+ * at least that many bytes, 16-byte aligned, owned by the caller and used
+ * only by the work this call enqueues (calls that run concurrently need
+ * their own); ignored when the shape needs none.  Errors as for the
+ * format's call, PESTI_ERR_SHAPE for an unknown format, and
+ * PESTI_ERR_WORKSPACE if a needed workspace is NULL or smaller. */
+int64_t pesti_gemm_workspace_bytes(int32_t format, int64_t m, int64_t out_features, int64_t in_features);
+int pesti_gemm_smallm_ws(int32_t format, int64_t m, int64_t out_features, int64_t in_features,
+                         const void* w, const uint16_t* x, float* y, const float* bias,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* --- dequantization to float32 (bit-exact; checks the unpacking) --------
  * w_out float32 [rows][in_features]: each weight rounded once from its

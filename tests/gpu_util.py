@@ -109,6 +109,27 @@ def run_gemm_quant(fmt, packed, m, n, k, x16, bias=None):
     return y_d.cpu().numpy().reshape(m, n)
 
 
+def run_gemm_ws(fmt, w, m, n, k, x16, bias=None, workspace_bytes=None):
+    """Y from pesti_gemm_smallm_ws (w: binary16 [n][k] for "f16", else packed
+    rows) with a workspace of pesti_gemm_workspace_bytes(...) bytes (or
+    `workspace_bytes`) between canaries; Y and workspace guards checked."""
+    import dequantize_mat_vec_amd as dmv
+    torch, _ = torch_dev()
+    w_d = to_dev(np.asarray(w).reshape(-1).view(np.uint8))
+    x_d = to_dev(np.ascontiguousarray(x16).view(np.uint16))
+    b_d = to_dev(bias.astype(np.float32)) if bias is not None else None
+    need = dmv.pesti_gemm_workspace_bytes(fmt, m, n, k)
+    assert need >= 0 and need % 4 == 0
+    nbytes = need if workspace_bytes is None else workspace_bytes
+    wbuf, ws = guarded_y(nbytes // 4)
+    fbuf, y_d = guarded_y(m * n)
+    dmv.pesti_gemm_smallm_ws(fmt, m, n, k, w_d, x_d, y_d, b_d, ws if nbytes else None, nbytes)
+    torch.cuda.synchronize()
+    assert guards_intact(fbuf, m * n), "GEMM wrote outside Y"
+    assert guards_intact(wbuf, nbytes // 4), "GEMM wrote outside its workspace"
+    return y_d.cpu().numpy().reshape(m, n)
+
+
 def run_swiglu(fmt, w_gate, w_up, gate_scales, up_scales, out, inf, x):
     import dequantize_mat_vec_amd as dmv
     torch, _ = torch_dev()

@@ -34,16 +34,16 @@ def test_library_exports_every_declared_symbol():
 def test_header_constants_match_binding():
     text = HEADER.read_text()
     for name in ("PESTI_OK", "PESTI_ERR_NULL", "PESTI_ERR_SHAPE", "PESTI_ERR_BATCH",
-                 "PESTI_ERR_ALIGN", "PESTI_ERR_LAUNCH", "PESTI_ERR_DEVICE"):
+                 "PESTI_ERR_ALIGN", "PESTI_ERR_LAUNCH", "PESTI_ERR_DEVICE", "PESTI_ERR_WORKSPACE"):
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
-    for fmt, fid in _lib.FORMAT_IDS.items():
+    for fmt, fid in list(_lib.FORMAT_IDS.items()) + list(_lib.GEMM_FORMAT_IDS.items()):
         m = re.search(rf"#define PESTI_FMT_{fmt.upper()} (\d+)", text)
         assert m and int(m.group(1)) == fid
 
 
 def test_abi_version():
-    assert dmv.pesti_abi_version() == 2
+    assert dmv.pesti_abi_version() == 3
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k", "i8row", "i4row"])
@@ -60,7 +60,7 @@ def test_row_bytes_rejects_bad_input():
 
 
 def test_strerror_covers_every_status():
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert dmv.strerror(st) and dmv.strerror(st) != "unknown status"
     assert dmv.strerror(-99) == "unknown status"
 
@@ -276,3 +276,45 @@ def test_stream_dequant_argument_checks():
     assert lib.pesti_dequant_q4_k_stream(2, 896, None, FAKE, None) == _lib.PESTI_ERR_NULL
     assert lib.pesti_dequant_q4_k_stream(2, 896, FAKE + 4, FAKE, None) == _lib.PESTI_ERR_ALIGN
     assert lib.pesti_gemv_q4_k_stream(4, 96, FAKE, FAKE, FAKE, None, 1, None) == _lib.PESTI_ERR_SHAPE
+
+
+def test_gemm_workspace_bytes_rule():
+    """Host-only: the split-K workspace of the small-M GEMMs (splits * m * n
+    float32 partials), by format and shape."""
+    ws = dmv.pesti_gemm_workspace_bytes
+    # Qwen down projection 896x4864: 56 column tiles, 4 splits at one row
+    # tile of X, 2 at two, none at three
+    for fmt in ("q8_0", "q2_k", "q3_k", "q4_k", "q5_k", "q6_k"):
+        assert ws(fmt, 16, 896, 4864) == 4 * 16 * 896 * 4
+        assert ws(fmt, 1, 896, 4864) == 4 * 1 * 896 * 4
+        assert ws(fmt, 32, 896, 4864) == 2 * 32 * 896 * 4
+        assert ws(fmt, 48, 896, 4864) == 0
+    # binary16: only m = 16 row tiles (below 16 the vector-ALU path)
+    assert ws("f16", 16, 896, 4864) == 4 * 16 * 896 * 4
+    assert ws("f16", 32, 896, 4864) == 0
+    assert ws("f16", 8, 896, 4864) == 0
+    # rows of at most 128 k-steps, 96+ column tiles, empty shapes: no split
+    assert ws("q6_k", 16, 896, 4096) == 0
+    assert ws("q6_k", 16, 1536, 8192) == 0
+    assert ws("q6_k", 16, 1520, 8192) == 2 * 16 * 1520 * 4
+    assert ws("q6_k", 0, 896, 4864) == 0
+    assert ws("q6_k", 16, 0, 4864) == 0
+    # bad input
+    assert ws("q6_k", 16, 896, 4865) == dmv.PESTI_ERR_SHAPE
+    assert ws("q6_k", 4097, 896, 4864) == dmv.PESTI_ERR_BATCH
+    assert ws(3, 16, 896, 4864) == dmv.PESTI_ERR_SHAPE   # i8row has no GEMM
+    # the largest workspace any shape asks for stays under 384 KiB
+    worst = max(ws(f, m, n, 8192) for f in ("f16", "q8_0") for m in range(1, 80, 3) for n in range(16, 1537, 16))
+    assert 0 < worst <= 384 * 1024
+
+
+def test_gemm_ws_argument_checks():
+    """Rejected before any device work: unknown format, missing workspace."""
+    lib = _lib.load()
+    f = lib.pesti_gemm_smallm_ws
+    assert f(3, 16, 896, 4864, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == dmv.PESTI_ERR_SHAPE
+    assert f(16, 16, 896, 4864, FAKE, FAKE, FAKE, None, None, 0, None) == dmv.PESTI_ERR_WORKSPACE
+    assert f(1, 16, 896, 4864, FAKE, FAKE, FAKE, None, FAKE, 4 * 16 * 896 * 4 - 16, None) == dmv.PESTI_ERR_WORKSPACE
+    assert f(1, 16, 896, 4864, FAKE, FAKE, FAKE, None, FAKE + 4, 1 << 20, None) == dmv.PESTI_ERR_ALIGN
+    assert f(1, 16, 896, 4865, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == dmv.PESTI_ERR_SHAPE
+

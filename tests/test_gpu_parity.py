@@ -12,8 +12,9 @@ import numpy as np
 import pytest
 
 import oracle
+import dequantize_mat_vec_amd as dmv
 from dequantize_mat_vec_amd import synth
-from gpu_util import (announce, assert_within, run_dequant, run_gemm, run_gemm_quant, run_gemv,
+from gpu_util import (announce, assert_within, run_dequant, run_gemm, run_gemm_quant, run_gemm_ws, run_gemv,
                       run_swiglu)
 
 pytestmark = pytest.mark.gpu
@@ -441,6 +442,66 @@ def test_gemm_quant_full_size_sampled_columns(fmt, m, n, k):
     sub = packed.reshape(n, -1)[cols]
     y_ref, s_ref = oracle.gemm_packed(fmt, sub, len(cols), k, x, bias[cols])
     assert_within(y[:, cols], y_ref, s_ref, QGEMM_REL, f"{fmt} gemm m{m} {n}x{k}")
+
+
+# ---------------------------------------------------------------------------
+# the same GEMMs with a caller's workspace: K split over workgroups on narrow
+# layers with long rows, partial tiles summed by a second launch
+# ---------------------------------------------------------------------------
+WS_FORMATS = ("f16",) + QGEMM_FORMATS
+# (m, k, n): 4 splits at m 16 on the down shape; one and eight rows of X
+# (binary16 below 16 rows: vector ALUs, unsplit); ragged K (129 k-steps);
+# 2 and 3 row tiles of X; 95 column tiles (2 splits); very long rows
+WS_SPLIT_CASES = [(16, 4864, 896), (1, 4864, 896), (8, 4864, 896), (16, 4128, 70), (33, 8192, 40),
+                  (32, 4864, 896), (16, 4160, 1520), (5, 16384, 24), (16, 32768, 20)]
+# shapes that do not split in any format: the workspace call equals the
+# plain call
+WS_PLAIN_CASES = [(64, 4864, 896), (16, 896, 4864), (48, 4864, 896), (16, 4096, 896)]
+
+
+def _ws_inputs(fmt, m, k, n, seed):
+    rng = np.random.default_rng([seed, m, k, n, len(fmt)])
+    w = synth.f16_weights(rng, n, k) if fmt == "f16" else synth.quant_blocks(fmt, rng, n, k)
+    return w, synth.f16_activations(rng, m, k), synth.bias(rng, n)
+
+
+def _ws_oracle(fmt, w, m, n, k, x, bias):
+    return oracle.gemm_f16(x, w, bias) if fmt == "f16" else oracle.gemm_packed(fmt, w, n, k, x, bias)
+
+
+@pytest.mark.parametrize("fmt", WS_FORMATS)
+@pytest.mark.parametrize("m,k,n", WS_SPLIT_CASES)
+def test_gemm_ws_split_parity(fmt, m, k, n):
+    w, x, bias = _ws_inputs(fmt, m, k, n, 31)
+    need = dmv.pesti_gemm_workspace_bytes(fmt, m, n, k)
+    if fmt != "f16" or (m == 16 and (n + 15) // 16 < 96):
+        assert need > 0, (fmt, m, k, n)
+    y = run_gemm_ws(fmt, w, m, n, k, x, bias)
+    y_ref, s_ref = _ws_oracle(fmt, w, m, n, k, x, bias)
+    assert_within(y, y_ref, s_ref, QGEMM_REL if fmt != "f16" else GEMM_REL, f"{fmt} ws gemm m{m} k{k} n{n}")
+    # the partials are summed in a fixed order: a second call gives the same bits
+    assert np.array_equal(run_gemm_ws(fmt, w, m, n, k, x, bias), y)
+
+
+@pytest.mark.parametrize("fmt", WS_FORMATS)
+@pytest.mark.parametrize("m,k,n", WS_PLAIN_CASES)
+def test_gemm_ws_without_split_equals_plain_call(fmt, m, k, n):
+    w, x, bias = _ws_inputs(fmt, m, k, n, 32)
+    assert dmv.pesti_gemm_workspace_bytes(fmt, m, n, k) == 0
+    y = run_gemm_ws(fmt, w, m, n, k, x, bias)
+    plain = run_gemm(x, w, bias) if fmt == "f16" else run_gemm_quant(fmt, w, m, n, k, x, bias)
+    assert np.array_equal(y, plain)
+
+
+@pytest.mark.parametrize("fmt", ("f16", "q6_k"))
+def test_gemm_ws_rejects_missing_or_short_workspace(fmt):
+    m, k, n = 16, 4864, 896
+    w, x, bias = _ws_inputs(fmt, m, k, n, 33)
+    need = dmv.pesti_gemm_workspace_bytes(fmt, m, n, k)
+    for nbytes in (0, need - 16):
+        with pytest.raises(dmv.PestiError) as ei:
+            run_gemm_ws(fmt, w, m, n, k, x, bias, workspace_bytes=nbytes)
+        assert ei.value.status == dmv.PESTI_ERR_WORKSPACE
 
 
 # ---------------------------------------------------------------------------
