@@ -18,7 +18,8 @@ from ._lib import (FORMAT_IDS, LIB_PATH, PESTI_ERR_ALIGN, PESTI_ERR_BATCH,  # no
                    pesti_gemv_q2_k, pesti_gemv_q3_k, pesti_dequant_q2_k, pesti_dequant_q3_k,
                    pesti_gemv_i4row, pesti_dequant_i4row, pesti_gemv_q4_k_stream,
                    pesti_dequant_q4_k_stream, pesti_matrix_bytes, strerror,
-                   PESTI_ERR_WORKSPACE, GEMM_FORMAT_IDS, pesti_gemm_workspace_bytes, pesti_gemm_smallm_ws)
+                   PESTI_ERR_WORKSPACE, GEMM_FORMAT_IDS, GEMM_SCRATCH_BYTES, pesti_gemm_workspace_bytes,
+                   pesti_gemm_smallm_ws, pesti_gemm_smallm_noalloc)
 
 __all__ = [n for n in dir() if n.startswith("pesti_")] + [
     "PestiError", "GemvOp", "MAX_GROUP", "gemv", "gemv_ops", "gemm_quant", "dequant", "load", "strerror",

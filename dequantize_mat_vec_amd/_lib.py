@@ -24,6 +24,8 @@ PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
 PESTI_ERR_WORKSPACE = -7
 
+GEMM_SCRATCH_BYTES = 256 * 1024   # PESTI_GEMM_SCRATCH_BYTES
+
 FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7,
               "q4_k_stream": 8}
 # formats of the small-M GEMM calls that take a format id
@@ -53,6 +55,7 @@ _SIGNATURES = {
     "pesti_gemm_q5_k_smallm": (_c_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_gemm_workspace_bytes": (_i64, [_i32, _i64, _i64, _i64]),
     "pesti_gemm_smallm_ws": (_c_int, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "pesti_gemm_smallm_noalloc": (_c_int, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pesti_dequant_q8_0": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
     "pesti_dequant_q4_k_stream": (_c_int, [_i64, _i64, _vp, _vp, _vp]),
@@ -260,6 +263,13 @@ def pesti_gemm_smallm_ws(fmt, m, out_features, in_features, w, x, y, bias=None, 
     return _check("pesti_gemm_smallm_ws", load().pesti_gemm_smallm_ws(
         _gemm_fid(fmt), m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias),
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def pesti_gemm_smallm_noalloc(fmt, m, out_features, in_features, w, x, y, bias=None, stream=None):
+    """pesti_gemm_smallm_ws with the library's own scratch (allocates nothing;
+    calls that overlap on one GPU race)."""
+    return _check("pesti_gemm_smallm_noalloc", load().pesti_gemm_smallm_noalloc(
+        _gemm_fid(fmt), m, out_features, in_features, _ptr(w), _ptr(x), _ptr(y), _ptr(bias), _stream(stream)))
 
 
 def gemv_ops(ops):

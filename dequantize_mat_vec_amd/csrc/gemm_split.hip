@@ -3,7 +3,10 @@
 // narrow layers with long rows, where one workgroup per output tile leaves
 // most compute units idle.  The partial tiles of the splits go to the
 // workspace; a second launch sums them in split order and adds the bias, so
-// results do not depend on timing.
+// results do not depend on timing.  An allocation-free variant takes the
+// partials to a static device array of the library instead.
+#include <atomic>
+
 #include "common.h"
 
 namespace pesti {
@@ -57,7 +60,29 @@ int pesti_host::launch_split_sum(int64_t m, int64_t n, const float* part, int sp
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
+// The allocation-free variant's scratch: this array per GPU, held until the
+// process ends.  In host code its name is only a stand-in; kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[PESTI_GEMM_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up once per device (every
+// thread that races here stores the same address).
+int scratch_on(int dev, float** out) {
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return PESTI_ERR_DEVICE;
+    p = static_cast<float*>(a);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PESTI_OK;
+}
 
 bool gemm_format(int32_t format) {
   switch (format) {
@@ -77,6 +102,13 @@ bool gemm_format(int32_t format) {
 int64_t workspace_bytes(int32_t format, int64_t m, int64_t out_features, int64_t in_features) {
   const int s = pesti_host::gemm_splits(format == PESTI_FMT_F16, m, out_features, in_features);
   return s > 1 ? static_cast<int64_t>(s) * m * out_features * static_cast<int64_t>(sizeof(float)) : 0;
+}
+
+int run(int32_t format, int64_t m, int64_t n, int64_t k, const void* w, const uint16_t* x, float* y,
+        const float* bias, float* ws, hipStream_t st) {
+  if (format == PESTI_FMT_F16)
+    return pesti_host::gemm_f16_run(m, n, k, static_cast<const uint16_t*>(w), x, y, bias, ws, st);
+  return pesti_host::gemm_quant_run(format, m, n, k, w, x, y, bias, ws, st);
 }
 
 }  // namespace
@@ -102,11 +134,24 @@ int pesti_gemm_smallm_ws(int32_t format, int64_t m, int64_t out_features, int64_
     if (!pesti_host::aligned(workspace, 16)) return PESTI_ERR_ALIGN;
     ws = static_cast<float*>(workspace);
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (format == PESTI_FMT_F16)
-    return pesti_host::gemm_f16_run(m, out_features, in_features, static_cast<const uint16_t*>(w), x, y, bias, ws,
-                                    st);
-  return pesti_host::gemm_quant_run(format, m, out_features, in_features, w, x, y, bias, ws, st);
+  return run(format, m, out_features, in_features, w, x, y, bias, ws, static_cast<hipStream_t>(stream));
+}
+
+int pesti_gemm_smallm_noalloc(int32_t format, int64_t m, int64_t out_features, int64_t in_features,
+                              const void* w, const uint16_t* x, float* y, const float* bias, void* stream) {
+  const int64_t need = pesti_gemm_workspace_bytes(format, m, out_features, in_features);
+  if (need < 0) return static_cast<int>(need);
+  if (need > PESTI_GEMM_SCRATCH_BYTES) return PESTI_ERR_WORKSPACE;
+  float* ws = nullptr;
+  if (need > 0) {
+    int dev = 0;
+    size_t lds = 0;
+    int st = pesti_host::current_device(&dev, &lds);
+    if (st != PESTI_OK) return st;
+    st = scratch_on(dev, &ws);
+    if (st != PESTI_OK) return st;
+  }
+  return run(format, m, out_features, in_features, w, x, y, bias, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

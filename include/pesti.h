@@ -302,8 +302,9 @@ int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
  *
  * pesti_gemm_workspace_bytes returns the bytes the split needs for this
  * format (PESTI_FMT_F16 or one of the six block formats) and shape: 0 when
- * the shape does not split, at most 384 KiB; negative PESTI_ERR_* for an
- * unknown format or a bad shape.  Host-only, no device needed.
+ * the shape does not split, at most PESTI_GEMM_SCRATCH_BYTES (256 KiB);
+ * negative PESTI_ERR_* for an unknown format or a bad shape.  Host-only,
+ * no device needed.
  *
  * pesti_gemm_smallm_ws: arguments as for pesti_gemm_<format>_smallm (w is
  * the binary16 W or the packed blocks), plus `workspace`, device memory of
@@ -316,6 +317,23 @@ int64_t pesti_gemm_workspace_bytes(int32_t format, int64_t m, int64_t out_featur
 int pesti_gemm_smallm_ws(int32_t format, int64_t m, int64_t out_features, int64_t in_features,
                          const void* w, const uint16_t* x, float* y, const float* bias,
                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* --- allocation-free form of pesti_gemm_smallm_ws --------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * GEMM with the split partials in the library's own scratch, a static device
+ * array of PESTI_GEMM_SCRATCH_BYTES on each GPU the library runs on, held
+ * until the process ends.  Nothing is allocated; every shape's workspace
+ * fits.  All calls on one GPU share that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or graphs replayed concurrently)
+ * race and may return wrong results; calls ordered on one stream are safe.
+ * Nothing in the array needs to start at zero.  Results equal
+ * pesti_gemm_smallm_ws bit for bit.  Errors as for pesti_gemm_smallm_ws;
+ * PESTI_ERR_WORKSPACE if a shape ever needed more than the array. */
+#define PESTI_GEMM_SCRATCH_BYTES (256 * 1024)
+int pesti_gemm_smallm_noalloc(int32_t format, int64_t m, int64_t out_features, int64_t in_features,
+                              const void* w, const uint16_t* x, float* y, const float* bias,
+                              void* stream);
 
 /* --- dequantization to float32 (bit-exact; checks the unpacking) --------
  * w_out float32 [rows][in_features]: each weight rounded once from its

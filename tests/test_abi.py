@@ -303,9 +303,12 @@ def test_gemm_workspace_bytes_rule():
     assert ws("q6_k", 16, 896, 4865) == dmv.PESTI_ERR_SHAPE
     assert ws("q6_k", 4097, 896, 4864) == dmv.PESTI_ERR_BATCH
     assert ws(3, 16, 896, 4864) == dmv.PESTI_ERR_SHAPE   # i8row has no GEMM
-    # the largest workspace any shape asks for stays under 384 KiB
+    # the largest workspace any shape asks for is the allocation-free
+    # variant's scratch (reached at 64 tiles of 16x16 outputs with 4 splits)
     worst = max(ws(f, m, n, 8192) for f in ("f16", "q8_0") for m in range(1, 80, 3) for n in range(16, 1537, 16))
-    assert 0 < worst <= 384 * 1024
+    assert worst == dmv.GEMM_SCRATCH_BYTES
+    text = HEADER.read_text()
+    assert re.search(r"#define PESTI_GEMM_SCRATCH_BYTES \(256 \* 1024\)", text)
 
 
 def test_gemm_ws_argument_checks():
@@ -317,4 +320,7 @@ def test_gemm_ws_argument_checks():
     assert f(1, 16, 896, 4864, FAKE, FAKE, FAKE, None, FAKE, 4 * 16 * 896 * 4 - 16, None) == dmv.PESTI_ERR_WORKSPACE
     assert f(1, 16, 896, 4864, FAKE, FAKE, FAKE, None, FAKE + 4, 1 << 20, None) == dmv.PESTI_ERR_ALIGN
     assert f(1, 16, 896, 4865, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == dmv.PESTI_ERR_SHAPE
-
+    g = lib.pesti_gemm_smallm_noalloc
+    assert g(3, 16, 896, 4864, FAKE, FAKE, FAKE, None, None) == dmv.PESTI_ERR_SHAPE
+    assert g(1, 4097, 896, 4864, FAKE, FAKE, FAKE, None, None) == dmv.PESTI_ERR_BATCH
+    assert g(1, 16, 896, 4865, FAKE, FAKE, FAKE, None, None) == dmv.PESTI_ERR_SHAPE
