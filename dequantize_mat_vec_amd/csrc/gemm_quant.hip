@@ -443,9 +443,10 @@ struct QPolQ2_K {
   static constexpr bool kHalfMins = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
-  // The X pair swap takes this kernel from 63 to 70 VGPRs, past the 64 at
-  // which two 16-wavefront workgroups fit a compute unit.
-  static constexpr bool kXSwap = false;
+  // With one row tile of X the pair swap takes this kernel from 63 to 70
+  // VGPRs, past the 64 at which two 16-wavefront workgroups fit a compute
+  // unit; with 2 or 4 (over 64 either way) it is taken.
+  static constexpr int kXSwapMinMT = 2;
   struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
 
   // Steps s and s + 1 (s even: j and j + 1 of one half h) share their code
@@ -773,11 +774,12 @@ struct QBuf {
   qhalf8 x[2][MT];
 };
 
-// Whether the X pair swap is taken (unless the policy says otherwise).
+// Fewest row tiles of X per workgroup at which the X pair swap is taken (1
+// unless the policy says otherwise).
 template <class Q, class = void>
-struct XSwap { static constexpr bool value = true; };
+struct XSwapMinMT { static constexpr int value = 1; };
 template <class Q>
-struct XSwap<Q, std::void_t<decltype(Q::kXSwap)>> { static constexpr bool value = Q::kXSwap; };
+struct XSwapMinMT<Q, std::void_t<decltype(Q::kXSwapMinMT)>> { static constexpr int value = Q::kXSwapMinMT; };
 
 // Wavefronts per workgroup on narrow layers of over 128 k-steps (8 unless
 // the policy says otherwise).
@@ -957,7 +959,7 @@ int launch_q(const QGemmArgs& a, float* ws, hipStream_t st) {
   QGemmArgs args = a;
   void* params[] = {&args, &kpart};
   const void* fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, false>);
-  if constexpr (pesti::XSwap<Q>::value) {
+  if constexpr (MT >= pesti::XSwapMinMT<Q>::value) {
     if (a.k % 64 == 0 && a.k <= 1024)
       fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>);
   }
