@@ -1,6 +1,7 @@
 // Dequantization to float32 ("PESTI - Portable Execution Substrate for
-// Transformer Inference", "What This Is": K-family dequantization verified
-// byte-exact).  One thread expands one 32-weight sub-block of one row and
+// Transformer Inference", "What This Is": the page checks its unpacking of
+// the K-family formats against a reference, to the byte).  One thread
+// expands one 32-weight sub-block of one row and
 // writes its float32 values; the mat-vec kernels never do this, the entry
 // points exist so the unpacking itself can be checked bit for bit.
 //
