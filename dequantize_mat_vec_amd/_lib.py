@@ -24,7 +24,7 @@ PESTI_ERR_LAUNCH = -5
 PESTI_ERR_DEVICE = -6
 PESTI_ERR_WORKSPACE = -7
 
-GEMM_SCRATCH_BYTES = 256 * 1024   # PESTI_GEMM_SCRATCH_BYTES
+GEMM_SCRATCH_BYTES = 512 * 1024   # PESTI_GEMM_SCRATCH_BYTES
 
 FORMAT_IDS = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "i8row": 3, "q5_k": 4, "q2_k": 5, "q3_k": 6, "i4row": 7,
               "q4_k_stream": 8}

@@ -201,11 +201,21 @@ int current_device(int* device, size_t* lds_per_group);
 // adds the bias.  At most 4 splits, so that about 256 workgroups run; the
 // binary16 GEMM splits only single row tiles of X (it measured slower at
 // two), and below m = 16 it runs on the vector ALUs, unsplit.
-inline int gemm_splits(bool f16, int64_t m, int64_t n, int64_t k) {
+//
+// Q8_0, Q3_K and Q6_K, whose K-split kernels are bound by their count of
+// small W loads per workgroup, take two row tiles of X per workgroup when
+// split (gemm_split_row_tiles), which halves the W loads at the same
+// workgroup count; the other formats measured slower that way.
+inline int gemm_split_row_tiles(int32_t format, int64_t m) {
+  const bool pairs = format == PESTI_FMT_Q8_0 || format == PESTI_FMT_Q3_K || format == PESTI_FMT_Q6_K;
+  return pairs && m > 16 ? 2 : 1;
+}
+inline int gemm_splits(int32_t format, int64_t m, int64_t n, int64_t k) {
   const int64_t tiles_n = (n + 15) / 16, tiles_m = (m + 15) / 16;
   if (m <= 0 || n <= 0 || tiles_n >= 96 || k / 32 <= 128) return 1;
-  if (f16 && (m < 16 || tiles_m > 1)) return 1;
-  const int64_t s = 256 / (tiles_n * tiles_m);
+  if (format == PESTI_FMT_F16 && (m < 16 || tiles_m > 1)) return 1;
+  const int mt = gemm_split_row_tiles(format, m);
+  const int64_t s = 256 / (tiles_n * ((tiles_m + mt - 1) / mt));
   return s >= 4 ? 4 : (s >= 2 ? static_cast<int>(s) : 1);
 }
 

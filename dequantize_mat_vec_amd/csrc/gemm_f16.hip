@@ -273,7 +273,7 @@ int launch_valu_b(const GemmArgs& a, int b, hipStream_t st) {
 
 template <int NW, int MT>
 int launch_mfma_t(const GemmArgs& a, float* ws, hipStream_t st) {
-  const int splits = ws ? pesti_host::gemm_splits(true, a.m, a.n, a.k) : 1;
+  const int splits = ws ? pesti_host::gemm_splits(PESTI_FMT_F16, a.m, a.n, a.k) : 1;
   float* kpart = splits > 1 ? ws : nullptr;
   dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)),
             static_cast<unsigned>(splits));

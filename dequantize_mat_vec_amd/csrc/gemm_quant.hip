@@ -61,6 +61,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // in-bounds re-read), never a byte outside the block, and realigns them.
 // ---------------------------------------------------------------------------
 struct QPolQ8_0 {
+  static constexpr int32_t kFormat = PESTI_FMT_Q8_0;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -107,6 +108,7 @@ struct QPolQ8_0 {
 // super-blocks).
 // ---------------------------------------------------------------------------
 struct QPolQ4_K {
+  static constexpr int32_t kFormat = PESTI_FMT_Q4_K;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -222,6 +224,7 @@ __device__ __forceinline__ qhalf8 q6_k_part(qhalf8 v, int part, int kg) {
 }
 
 struct QPolQ6_K {
+  static constexpr int32_t kFormat = PESTI_FMT_Q6_K;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 2;
@@ -337,6 +340,7 @@ __device__ __forceinline__ K4Prep k4_prep(const u32x4& hdr, int kg, float cmax) 
 // nearest_code, scaled by d; the remainder dmin * m_j - d sc_j c times the
 // step's sum of x (product against ones).
 struct QPolQ5_K {
+  static constexpr int32_t kFormat = PESTI_FMT_Q5_K;
   static constexpr bool kMin = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -384,6 +388,7 @@ struct QPolQ5_K {
 // 32 + 32h + 16c + l, high bit at bit 4h + j of bytes 16c + l.  Operand
 // (low | high << 2) - 4 = q times the lane's own scale - 32, scaled by d.
 struct QPolQ3_K {
+  static constexpr int32_t kFormat = PESTI_FMT_Q3_K;
   static constexpr bool kMin = false;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
@@ -439,6 +444,7 @@ struct QPolQ3_K {
 // remainders dmin m - d sc c_k of the step's two sub-blocks multiply sums
 // of x over its two 16-weight halves (products against ones on one half).
 struct QPolQ2_K {
+  static constexpr int32_t kFormat = PESTI_FMT_Q2_K;
   static constexpr bool kMin = true;
   static constexpr bool kHalfMins = true;
   static constexpr bool kScaled = true;
@@ -952,7 +958,7 @@ using pesti::NarrowLongNW;
 
 template <class Q, int NW, int MT>
 int launch_q(const QGemmArgs& a, float* ws, hipStream_t st) {
-  const int splits = ws ? pesti_host::gemm_splits(false, a.m, a.n, a.k) : 1;
+  const int splits = ws ? pesti_host::gemm_splits(Q::kFormat, a.m, a.n, a.k) : 1;
   float* kpart = splits > 1 ? ws : nullptr;
   dim3 grid(static_cast<unsigned>((a.n + 15) / 16), static_cast<unsigned>((a.m + 16 * MT - 1) / (16 * MT)),
             static_cast<unsigned>(splits));
@@ -977,6 +983,8 @@ template <class Q>
 int launch_quant(const QGemmArgs& a, float* ws, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
   constexpr int kLongNW = NarrowLongNW<Q>::value;
+  if (tiles_n < 96 && a.k / 32 > 128 && ws && pesti_host::gemm_split_row_tiles(Q::kFormat, a.m) == 2)
+    return launch_q<Q, kLongNW, 2>(a, ws, st);
   if (tiles_n < 96 && a.k / 32 > 128) return launch_q<Q, kLongNW, 1>(a, ws, st);
   if (tiles_n < 96) return launch_q<Q, 8, 1>(a, nullptr, st);
   if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, nullptr, st);

@@ -100,7 +100,7 @@ bool gemm_format(int32_t format) {
 }
 
 int64_t workspace_bytes(int32_t format, int64_t m, int64_t out_features, int64_t in_features) {
-  const int s = pesti_host::gemm_splits(format == PESTI_FMT_F16, m, out_features, in_features);
+  const int s = pesti_host::gemm_splits(format, m, out_features, in_features);
   return s > 1 ? static_cast<int64_t>(s) * m * out_features * static_cast<int64_t>(sizeof(float)) : 0;
 }
 

@@ -295,14 +295,15 @@ int pesti_gemm_q6_k_smallm(int64_t m, int64_t out_features, int64_t in_features,
  * projection) with long rows (in_features over 4096) run one workgroup per
  * output tile and leave most compute units idle.  With a workspace, K is
  * split over 2..4 workgroups per tile (more workgroups for fewer row tiles
- * of X; binary16 only at m 16), each writing its partial tile to the
+ * of X; binary16 only at m 16; Q8_0, Q3_K and Q6_K take two row tiles of X
+ * per workgroup), each writing its partial tile to the
  * workspace, and a second launch on the same stream sums the partials in a
  * fixed order and adds the bias: results do not depend on timing, but the
  * summation order differs from the call without workspace (same bound).
  *
  * pesti_gemm_workspace_bytes returns the bytes the split needs for this
  * format (PESTI_FMT_F16 or one of the six block formats) and shape: 0 when
- * the shape does not split, at most PESTI_GEMM_SCRATCH_BYTES (256 KiB);
+ * the shape does not split, at most PESTI_GEMM_SCRATCH_BYTES (512 KiB);
  * negative PESTI_ERR_* for an unknown format or a bad shape.  Host-only,
  * no device needed.
  *
@@ -330,7 +331,7 @@ int pesti_gemm_smallm_ws(int32_t format, int64_t m, int64_t out_features, int64_
  * Nothing in the array needs to start at zero.  Results equal
  * pesti_gemm_smallm_ws bit for bit.  Errors as for pesti_gemm_smallm_ws;
  * PESTI_ERR_WORKSPACE if a shape ever needed more than the array. */
-#define PESTI_GEMM_SCRATCH_BYTES (256 * 1024)
+#define PESTI_GEMM_SCRATCH_BYTES (512 * 1024)
 int pesti_gemm_smallm_noalloc(int32_t format, int64_t m, int64_t out_features, int64_t in_features,
                               const void* w, const uint16_t* x, float* y, const float* bias,
                               void* stream);
