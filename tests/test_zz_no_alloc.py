@@ -60,3 +60,32 @@ def test_noalloc_shape_without_split_equals_plain_call():
     w, x, bias = _inputs("q4_k", m, k, n, 43)
     assert dmv.pesti_gemm_workspace_bytes("q4_k", m, n, k) == 0
     assert np.array_equal(_noalloc("q4_k", w, m, n, k, x, bias), run_gemm_ws("q4_k", w, m, n, k, x, bias))
+
+
+def test_noalloc_in_a_captured_graph():
+    """The call it exists for: captured in a graph (no allocation inside the
+    capture), replayed with new X written eagerly between replays; every
+    replay equals the eager workspace call on the same X bit for bit."""
+    torch, _ = torch_dev()
+    fmt, m, k, n = "q6_k", 32, 4864, 896
+    w, x, bias = _inputs(fmt, m, k, n, 44)
+    w_d = to_dev(np.asarray(w).reshape(-1).view(np.uint8))
+    x_d = to_dev(np.ascontiguousarray(x).view(np.uint16))
+    b_d = to_dev(bias.astype(np.float32))
+    y_d = torch.empty(m * n, dtype=torch.float32, device=x_d.device)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dmv.pesti_gemm_smallm_noalloc(fmt, m, n, k, w_d, x_d, y_d, b_d)   # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            dmv.pesti_gemm_smallm_noalloc(fmt, m, n, k, w_d, x_d, y_d, b_d)
+    for r in range(3):
+        announce(f"noalloc graph replay {r}")
+        xr = synth.f16_activations(np.random.default_rng([45, r]), m, k)
+        x_d.copy_(to_dev(np.ascontiguousarray(xr).view(np.uint16)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y = y_d.cpu().numpy().reshape(m, n).copy()
+        assert np.array_equal(y, run_gemm_ws(fmt, w, m, n, k, xr, bias)), r
