@@ -1459,7 +1459,7 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
          a.in > 0 && a.in <= 1024;
 }
-// Tall Q4_K, Q5_K and Q2_K matrices with rows of at most 1024 weights at batch 1
+// Tall Q4_K, Q5_K, Q2_K and Q3_K matrices with rows of at most 1024 weights at batch 1
 // take the batch-1 kernel of gemv_tall.hip (128-weight units, a row per U
 // lanes); in the Q4_K stream layout only rows of a whole number of
 // 128-weight units, so that no unit straddles two super-blocks.
@@ -1469,7 +1469,8 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
 constexpr int64_t kTallMinRows = PESTI_TALL_MIN_ROWS;
 template <class F>
 constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ5_K>::value ||
-                          std::is_same<F, pesti::FmtQ2_K>::value || pesti::kStreamLayout<F>;
+                          std::is_same<F, pesti::FmtQ2_K>::value || std::is_same<F, pesti::FmtQ3_K>::value ||
+                          pesti::kStreamLayout<F>;
 template <class F>
 inline bool tall_op(const GemvArgs& a, int batch) {
   return kHasTall<F> && batch == 1 && a.out >= kTallMinRows && a.in > 0 && a.in <= 1024 &&
@@ -1480,10 +1481,12 @@ inline bool tall_op(const GemvArgs& a, int batch) {
 int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st);
 int launch_tall_q5_k(const GroupArgs& g, hipStream_t st);
 int launch_tall_q2_k(const GroupArgs& g, hipStream_t st);
+int launch_tall_q3_k(const GroupArgs& g, hipStream_t st);
 template <class F>
 inline int launch_tall(const GroupArgs& g, hipStream_t st) {
   if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_tall_q5_k(g, st);
   else if constexpr (std::is_same<F, pesti::FmtQ2_K>::value) return launch_tall_q2_k(g, st);
+  else if constexpr (std::is_same<F, pesti::FmtQ3_K>::value) return launch_tall_q3_k(g, st);
   else return launch_tall_q4_k(g, pesti::kStreamLayout<F>, st);
 }
 

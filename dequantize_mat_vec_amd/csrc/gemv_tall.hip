@@ -1,12 +1,12 @@
-// Batch-1 mat-vec for tall Q4_K, Q5_K and Q2_K matrices with short rows
-// (the LM head, 151936 x 896): y = W x + b.
+// Batch-1 mat-vec for tall Q4_K, Q5_K, Q2_K and Q3_K matrices with short
+// rows (the LM head, 151936 x 896): y = W x + b.
 //
 // The operation is the decode step's row-major matrix-vector product with
-// the weights kept in GGUF Q4_K, Q5_K or Q2_K blocks ("Project scaffold:
+// the weights kept in GGUF Q4_K, Q5_K, Q2_K or Q3_K blocks ("Project scaffold:
 // modules, CLI, and correctness harness", file summaries of tensor.rs and
 // quant.rs; "PESTI - Portable Execution Substrate for Transformer
 // Inference", "What This Is"): w = d sc q - dmin m per sub-block (32
-// weights; 16 for Q2_K).
+// weights; 16 for Q2_K), w = d (sc - 32) q for Q3_K (16).
 //
 // At batch 1 the general kernel (gemv_impl.h) spends most of a lane's
 // instructions on work that does not scale with the weights it reads - x
@@ -14,7 +14,7 @@
 // unit per lane, and 2 of each 16-lane row group stay idle on 896-weight
 // rows (14 units).  Here a lane takes a 128-weight unit (two runs of one
 // super-block: for Q4_K its 16-byte header and 64 code bytes, five 16-byte
-// loads; TallQ5K and TallQ2K below for Q5_K and Q2_K) and a row takes U =
+// loads; TallQ5K, TallQ2K and TallQ3K below) and a row takes U =
 // in / 128 consecutive lanes, so a wave holds floor(64 / U) rows (9 rows of 7
 // lanes at 896 columns, one lane idle), and a workgroup of 4 waves stages x
 // once for 36 rows (measured on the 151936 x 896 head: 2 / 4 / 8 / 16 waves
@@ -227,6 +227,80 @@ struct TallQ2K {
   }
 };
 
+// Q3_K (110-byte super-blocks: hmask[32], qs[64], 12 scale bytes, d): unit
+// g is half h = g & 1 of super-block g / 2, weights 128h + 32j + l (j, l =
+// 0..3, 0..31): the low two bits at bit 2j of qs byte 32h + l, the high bit
+// at bit 4h + j of hmask byte l (clear: the code is 4 less), 16-weight
+// sub-block 8h + 2j + (l >= 16) with a 6-bit scale less 32 (low 4 bits in
+// nibble h of scale byte 2j + (l >= 16), high 2 bits in byte 8 + (2j + (l >=
+// 16)) % 4 at bit 4h + 2(j / 2)).  Super-blocks are only 2-byte aligned; the
+// unit takes five 16-byte loads (hmask, its half of qs, and bytes 94..109
+// for the scale bytes and d), the scale dwords realigned in registers.
+// Codes are exact signed bytes (-4..3); with no mins, a sub-block's sum of
+// code times x scaled once by d (sc - 32) is its weights times x, rounding
+// aside, with nothing to cancel.
+struct TallQ3K {
+  static constexpr int kBytes = 110;
+  struct Raw { u32x4 h0, h1, q0, q1, sd; };
+
+  __device__ __forceinline__ static u32x4 load2(const uint8_t* p) {
+    const u32x4u2 v = *reinterpret_cast<const u32x4u2*>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
+  }
+  __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
+    const uint8_t* sb = base + (g >> 1) * kBytes;
+    const int h = static_cast<int>(g & 1);
+    r.h0 = load2(sb);
+    r.h1 = load2(sb + 16);
+    r.q0 = load2(sb + 32 + 32 * h);
+    r.q1 = load2(sb + 48 + 32 * h);
+    r.sd = load2(sb + 94);
+  }
+
+  __device__ __forceinline__ static float compute(const Raw& r, int u, bool half, const float* xs) {
+    // scale bytes 0..3, 4..7, 8..11 (super-block bytes 96..107) and d (108)
+    const uint32_t s0 = __builtin_amdgcn_alignbyte(r.sd.y, r.sd.x, 2);
+    const uint32_t s1 = __builtin_amdgcn_alignbyte(r.sd.z, r.sd.y, 2);
+    const uint32_t s2 = __builtin_amdgcn_alignbyte(r.sd.w, r.sd.z, 2);
+    const float d = f16_hi(r.sd.w);
+    const uint32_t h4 = half ? 4u : 0u;
+    float acc = 0.f;
+    const int x0 = 128 * u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hs = h4 + static_cast<uint32_t>(j);   // high-bit position
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4& qv = c ? r.q1 : r.q0;
+        const u32x4& hv = c ? r.h1 : r.h0;
+        const int k = 2 * j + c;   // sub-block within the unit
+        const uint32_t lo4 = ((k < 4 ? s0 : s1) >> (8 * (k & 3) + h4)) & 15u;
+        const uint32_t hi2 = (s2 >> (8 * (k & 3) + h4 + 2 * (j >> 1))) & 3u;
+        const float ds = d * static_cast<float>(static_cast<int>(lo4 | (hi2 << 4)) - 32);
+        float p = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = t == 0 ? qv.x : (t == 1 ? qv.y : (t == 2 ? qv.z : qv.w));
+          const uint32_t hw = t == 0 ? hv.x : (t == 1 ? hv.y : (t == 2 ? hv.z : hv.w));
+          const uint32_t low2 = (w >> (2 * j)) & 0x03030303u;
+          const uint32_t hb = (hw >> hs) & 0x01010101u;   // 1 where the high bit is set
+          // 0xFF in the bytes whose high bit is clear: byte selector 13 of
+          // v_perm gives 0xFF, 12 gives 0 (no multiply)
+          const uint32_t neg = __builtin_amdgcn_perm(0u, 0u, 0x0D0D0D0Du - hb);
+          const uint32_t qb = low2 | (neg & 0xFCFCFCFCu);   // signed bytes -4..3
+          const f32x4 xv = xs4(xs, x0 + 32 * j + 16 * c + 4 * t);
+          p = fmaf(sbyte<0>(qb), xv.x, p);
+          p = fmaf(sbyte<1>(qb), xv.y, p);
+          p = fmaf(sbyte<2>(qb), xv.z, p);
+          p = fmaf(sbyte<3>(qb), xv.w, p);
+        }
+        acc = fmaf(ds, p, acc);
+      }
+    }
+    return acc;
+  }
+};
+
 // U = 128-weight units per row (row layout: rows of up to 128 U weights,
 // padded to whole super-blocks; stream layout, S: rows of exactly 128 U);
 // a wave serves 64 / U rows, a workgroup kTallWaves times that.  Measured
@@ -329,7 +403,7 @@ int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st) {
   return launch_tall_s<pesti::TallQ4K, true>(g, st);
 }
 
-// The same for Q5_K and Q2_K (row layout).
+// The same for Q5_K, Q2_K and Q3_K (row layout).
 int launch_tall_q5_k(const GroupArgs& g, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
   return launch_tall_s<pesti::TallQ5K, false>(g, st);
@@ -338,6 +412,11 @@ int launch_tall_q5_k(const GroupArgs& g, hipStream_t st) {
 int launch_tall_q2_k(const GroupArgs& g, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
   return launch_tall_s<pesti::TallQ2K, false>(g, st);
+}
+
+int launch_tall_q3_k(const GroupArgs& g, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  return launch_tall_s<pesti::TallQ3K, false>(g, st);
 }
 
 }  // namespace pesti_gemv

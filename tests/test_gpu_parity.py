@@ -1148,7 +1148,7 @@ def test_gemm_quant_exact_cancellation_gives_bias(fmt, m, k, n):
 # (rows of at most 1024 weights, at least 16384 rows)
 # ---------------------------------------------------------------------------
 TALL_ROWS = 16384
-TALL_FORMATS = ("q4_k", "q5_k", "q2_k")
+TALL_FORMATS = ("q4_k", "q5_k", "q2_k", "q3_k")
 
 
 @pytest.mark.parametrize("fmt", TALL_FORMATS)
@@ -1229,6 +1229,29 @@ def test_tall_q2_k_batch_1_padding_bytes_do_not_matter():
     other[:, 3, 2:16] = rng.integers(0, 256, (out, 14), dtype=np.uint8)
     y1 = run_gemv("q2_k", packed, None, out, inf, x, bias)
     y2 = run_gemv("q2_k", other.reshape(out, -1), None, out, inf, x, bias)
+    assert np.array_equal(y1, y2)
+
+
+def test_tall_q3_k_batch_1_padding_bytes_do_not_matter():
+    out, inf = TALL_ROWS + 3, 800
+    packed, _, x, bias = make("q3_k", out, inf, 160, 1)
+    other = packed.copy().reshape(out, 4, 110)
+    rng = np.random.default_rng(161)
+    # super-block 3 holds weights 768..1023: 768..799 are real (half 0, field
+    # j = 0: bits 0-1 of qs bytes 32..63, bit 0 of hmask bytes 0..31, the
+    # scales of sub-blocks 0 and 1: low nibbles of scale bytes 0 and 1, bits
+    # 0-1 of scale bytes 8 and 9); every other code and scale bit is padding
+    # (d at 108..109 is shared)
+    r = lambda hi, n: rng.integers(0, hi, (out, n), dtype=np.uint8)
+    other[:, 3, 64:96] = r(256, 32)
+    other[:, 3, 32:64] = (other[:, 3, 32:64] & 0x03) | (r(64, 32) << 2)
+    other[:, 3, 0:32] = (other[:, 3, 0:32] & 0x01) | (r(128, 32) << 1)
+    other[:, 3, 96:98] = (other[:, 3, 96:98] & 0x0F) | (r(16, 2) << 4)
+    other[:, 3, 98:104] = r(256, 6)
+    other[:, 3, 104:106] = (other[:, 3, 104:106] & 0x03) | (r(64, 2) << 2)
+    other[:, 3, 106:108] = r(256, 2)
+    y1 = run_gemv("q3_k", packed, None, out, inf, x, bias)
+    y2 = run_gemv("q3_k", other.reshape(out, -1), None, out, inf, x, bias)
     assert np.array_equal(y1, y2)
 
 
