@@ -1459,10 +1459,11 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
          a.in > 0 && a.in <= 1024;
 }
-// Tall Q4_K, Q5_K, Q2_K and Q3_K matrices with rows of at most 1024 weights at batch 1
+// Tall Q4_K, Q5_K, Q2_K, Q3_K and per-row INT4 matrices with rows of at most 1024 weights at batch 1
 // take the batch-1 kernel of gemv_tall.hip (128-weight units, a row per U
-// lanes); in the Q4_K stream layout only rows of a whole number of
-// 128-weight units, so that no unit straddles two super-blocks.
+// lanes); in the Q4_K stream layout and for per-row INT4 only rows of a
+// whole number of 128-weight units, so that no unit straddles two
+// super-blocks or reads past its row.
 #ifndef PESTI_TALL_MIN_ROWS
 #define PESTI_TALL_MIN_ROWS 16384
 #endif
@@ -1470,11 +1471,12 @@ constexpr int64_t kTallMinRows = PESTI_TALL_MIN_ROWS;
 template <class F>
 constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ5_K>::value ||
                           std::is_same<F, pesti::FmtQ2_K>::value || std::is_same<F, pesti::FmtQ3_K>::value ||
-                          pesti::kStreamLayout<F>;
+                          std::is_same<F, pesti::FmtI4Row>::value || pesti::kStreamLayout<F>;
 template <class F>
 inline bool tall_op(const GemvArgs& a, int batch) {
+  constexpr bool kWholeUnits = pesti::kStreamLayout<F> || std::is_same<F, pesti::FmtI4Row>::value;
   return kHasTall<F> && batch == 1 && a.out >= kTallMinRows && a.in > 0 && a.in <= 1024 &&
-         (!pesti::kStreamLayout<F> || a.in % 128 == 0);
+         (!kWholeUnits || a.in % 128 == 0);
 }
 // One launch of ops that all pass tall_op and share one row length in
 // 128-weight units; x and y of every op set.
@@ -1482,11 +1484,13 @@ int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st);
 int launch_tall_q5_k(const GroupArgs& g, hipStream_t st);
 int launch_tall_q2_k(const GroupArgs& g, hipStream_t st);
 int launch_tall_q3_k(const GroupArgs& g, hipStream_t st);
+int launch_tall_i4row(const GroupArgs& g, hipStream_t st);
 template <class F>
 inline int launch_tall(const GroupArgs& g, hipStream_t st) {
   if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_tall_q5_k(g, st);
   else if constexpr (std::is_same<F, pesti::FmtQ2_K>::value) return launch_tall_q2_k(g, st);
   else if constexpr (std::is_same<F, pesti::FmtQ3_K>::value) return launch_tall_q3_k(g, st);
+  else if constexpr (std::is_same<F, pesti::FmtI4Row>::value) return launch_tall_i4row(g, st);
   else return launch_tall_q4_k(g, pesti::kStreamLayout<F>, st);
 }
 

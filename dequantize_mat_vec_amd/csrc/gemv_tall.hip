@@ -1,12 +1,13 @@
-// Batch-1 mat-vec for tall Q4_K, Q5_K, Q2_K and Q3_K matrices with short
-// rows (the LM head, 151936 x 896): y = W x + b.
+// Batch-1 mat-vec for tall Q4_K, Q5_K, Q2_K, Q3_K and per-row INT4 matrices
+// with short rows (the LM head, 151936 x 896): y = W x + b.
 //
 // The operation is the decode step's row-major matrix-vector product with
 // the weights kept in GGUF Q4_K, Q5_K, Q2_K or Q3_K blocks ("Project scaffold:
 // modules, CLI, and correctness harness", file summaries of tensor.rs and
 // quant.rs; "PESTI - Portable Execution Substrate for Transformer
 // Inference", "What This Is"): w = d sc q - dmin m per sub-block (32
-// weights; 16 for Q2_K), w = d (sc - 32) q for Q3_K (16).
+// weights; 16 for Q2_K), w = d (sc - 32) q for Q3_K (16), w = s q for
+// per-row INT4 (s per row).
 //
 // At batch 1 the general kernel (gemv_impl.h) spends most of a lane's
 // instructions on work that does not scale with the weights it reads - x
@@ -14,7 +15,7 @@
 // unit per lane, and 2 of each 16-lane row group stay idle on 896-weight
 // rows (14 units).  Here a lane takes a 128-weight unit (two runs of one
 // super-block: for Q4_K its 16-byte header and 64 code bytes, five 16-byte
-// loads; TallQ5K, TallQ2K and TallQ3K below) and a row takes U =
+// loads; TallQ5K, TallQ2K, TallQ3K and TallI4 below) and a row takes U =
 // in / 128 consecutive lanes, so a wave holds floor(64 / U) rows (9 rows of 7
 // lanes at 896 columns, one lane idle), and a workgroup of 4 waves stages x
 // once for 36 rows (measured on the 151936 x 896 head: 2 / 4 / 8 / 16 waves
@@ -301,6 +302,56 @@ struct TallQ3K {
   }
 };
 
+// Per-row INT4 (rows of in / 2 code bytes, weights 2i and 2i + 1 in the low
+// and high nibble of byte i, two's complement; w = s q with the row's scale
+// s): a unit is 64 code bytes, four 16-byte loads, and rows must be a whole
+// number of units (in % 128 == 0) so that no unit reads past its row.  A
+// nibble moved to the top of a byte is the exact signed byte 16 q,
+// converted with one sign-extending convert; the 1/16 and the row scale
+// multiply the row's sum (kRowScales).
+struct TallI4 {
+  static constexpr bool kRowScales = true;
+  static constexpr float kAccScale = 0.0625f;
+  struct Raw { u32x4 c0, c1, c2, c3; };
+
+  __device__ __forceinline__ static void issue(const uint8_t* base, int64_t g, Raw& r) {
+    const uint8_t* p = base + 64 * g;
+    r.c0 = load_u32x4_a16(p);
+    r.c1 = load_u32x4_a16(p + 16);
+    r.c2 = load_u32x4_a16(p + 32);
+    r.c3 = load_u32x4_a16(p + 48);
+  }
+
+  __device__ __forceinline__ static float compute(const Raw& r, int u, bool, const float* xs) {
+    float acc = 0.f;
+    const int x0 = 128 * u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4& cv = i < 4 ? r.c0 : (i < 8 ? r.c1 : (i < 12 ? r.c2 : r.c3));
+      const uint32_t v = (i & 3) == 0 ? cv.x : ((i & 3) == 1 ? cv.y : ((i & 3) == 2 ? cv.z : cv.w));
+      const uint32_t ev = (v << 4) & 0xF0F0F0F0u;   // even weights, 16 q each
+      const uint32_t od = v & 0xF0F0F0F0u;          // odd weights
+      const f32x4 xa = xs4(xs, x0 + 8 * i);
+      const f32x4 xb = xs4(xs, x0 + 8 * i + 4);
+      acc = fmaf(sbyte<0>(ev), xa.x, acc);
+      acc = fmaf(sbyte<0>(od), xa.y, acc);
+      acc = fmaf(sbyte<1>(ev), xa.z, acc);
+      acc = fmaf(sbyte<1>(od), xa.w, acc);
+      acc = fmaf(sbyte<2>(ev), xb.x, acc);
+      acc = fmaf(sbyte<2>(od), xb.y, acc);
+      acc = fmaf(sbyte<3>(ev), xb.z, acc);
+      acc = fmaf(sbyte<3>(od), xb.w, acc);
+    }
+    return acc;
+  }
+};
+
+// Whether a unit policy scales each row's sum (T::kRowScales, per-row INT4).
+template <class T, class = void>
+struct TallRowScales { static constexpr bool value = false; };
+template <class T>
+struct TallRowScales<T, std::void_t<decltype(T::kRowScales)>> { static constexpr bool value = T::kRowScales; };
+
 // U = 128-weight units per row (row layout: rows of up to 128 U weights,
 // padded to whole super-blocks; stream layout, S: rows of exactly 128 U);
 // a wave serves 64 / U rows, a workgroup kTallWaves times that.  Measured
@@ -345,6 +396,8 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
   typename T::Raw r;
   T::issue(S ? a.w : a.w + lrow * a.row_bytes, gu, r);
   const float bv = *(a.bias ? a.bias + lrow : reinterpret_cast<const float*>(a.w));
+  float rs = 1.f;
+  if constexpr (TallRowScales<T>::value) rs = a.scales[lrow];
 #pragma unroll
   for (int k = 0; k < kXPer; ++k) {
     const int s = tid + k * kTallThreads;
@@ -357,7 +410,11 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
   float sum = part;
 #pragma unroll
   for (int k = 1; k < U; ++k) sum += __shfl(part, lane + k < kWave ? lane + k : lane, kWave);
-  if (u == 0 && live) a.y[row] = sum + (a.bias ? bv : 0.f);
+  if constexpr (TallRowScales<T>::value) {
+    if (u == 0 && live) a.y[row] = fmaf(sum * T::kAccScale, rs, a.bias ? bv : 0.f);
+  } else {
+    if (u == 0 && live) a.y[row] = sum + (a.bias ? bv : 0.f);
+  }
 }
 
 }  // namespace pesti
@@ -417,6 +474,14 @@ int launch_tall_q2_k(const GroupArgs& g, hipStream_t st) {
 int launch_tall_q3_k(const GroupArgs& g, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
   return launch_tall_s<pesti::TallQ3K, false>(g, st);
+}
+
+// Per-row INT4: rows of a whole number of 128-weight units only.
+int launch_tall_i4row(const GroupArgs& g, hipStream_t st) {
+  if (g.n_ops < 1) return PESTI_ERR_SHAPE;
+  for (int i = 0; i < g.n_ops; ++i)
+    if (g.op[i].in % 128 != 0 || !g.op[i].scales) return PESTI_ERR_SHAPE;
+  return launch_tall_s<pesti::TallI4, false>(g, st);
 }
 
 }  // namespace pesti_gemv

@@ -946,6 +946,52 @@ def test_tall_i4row_every_row(out, inf, batch):
     assert_within(y, y_ref, s_ref, GEMV_REL, f"tall i4row {out}x{inf} b{batch}")
 
 
+# batch 1 on the 128-weight-unit kernel (rows of whole 128-weight units;
+# 800 and 192 stay on the general kernel)
+@pytest.mark.parametrize("inf", [128, 256, 384, 512, 640, 768, 896, 1024, 800, 192])
+def test_tall_i4row_batch_1_every_row(inf):
+    out = MFMA_ROWS + 37
+    packed, scales, x, bias = make("i4row", out, inf, 136, 1)
+    y = run_gemv("i4row", packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("i4row", packed, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall i4row b1 in={inf}")
+
+
+def test_tall_i4row_batch_1_one_hot_and_sparse_codes():
+    out, inf = MFMA_ROWS + 5, 896
+    packed, scales, x, bias = make("i4row", out, inf, 137, 1)
+    w32 = oracle.dequantize_f32("i4row", packed, out, inf, scales)
+    for j in (0, 1, 127, 128, 129, 255, 256, 895):
+        xo = np.zeros((1, inf), np.float32)
+        xo[0, j] = 1.0
+        assert np.array_equal(run_gemv("i4row", packed, scales, out, inf, xo)[0], w32[:, j]), j
+    rng = np.random.default_rng(138)
+    p = packed.reshape(out, -1).copy()
+    p[rng.random(p.shape) < 0.98] = 0
+    y = run_gemv("i4row", p, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed("i4row", p, out, inf, x, bias, scales)
+    assert_within(y, y_ref, s_ref, GEMV_REL, "tall i4row sparse b1")
+
+
+def test_tall_i4row_batch_1_group_equals_single_calls_bitwise():
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    ops, cases = [], []
+    for i, (out, inf) in enumerate([(MFMA_ROWS + 7, 896), (300, 896), (MFMA_ROWS + 100, 800), (MFMA_ROWS + 3, 896)]):
+        packed, scales, x, bias = make("i4row", out, inf, 145 + i, 1)
+        w_d, s_d, x_d, b_d = to_dev(packed.reshape(-1)), to_dev(scales), to_dev(x), to_dev(bias)
+        yg = torch.empty(out, dtype=torch.float32, device="cuda")
+        ops.append((out, inf, w_d, x_d, yg, b_d, s_d))
+        cases.append((out, inf, w_d, s_d, x_d, b_d, yg))
+    dmv.pesti_gemv_group("i4row", ops, 1)
+    for out, inf, w_d, s_d, x_d, b_d, yg in cases:
+        ys = torch.empty(out, dtype=torch.float32, device="cuda")
+        dmv.pesti_gemv_i4row(out, inf, w_d, s_d, x_d, ys, b_d, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ys), (out, inf)
+
+
 def test_tall_i4row_one_hot_and_scaling():
     out, inf = MFMA_ROWS + 21, 800
     packed, scales, x, _ = make("i4row", out, inf, 131, 8)
