@@ -1459,8 +1459,8 @@ inline bool mfma_op(const GemvArgs& a, int batch) {
   return kHasMfma<F> && batch >= kMfmaMinBatch<F> && batch <= PESTI_MAX_BATCH && a.out >= kMfmaMinRows &&
          a.in > 0 && a.in <= 1024;
 }
-// Tall Q4_K, Q5_K, Q2_K, Q3_K and per-row INT4 matrices with rows of at most 1024 weights at batch 1
-// take the batch-1 kernel of gemv_tall.hip (128-weight units, a row per U
+// Tall Q4_K, Q5_K, Q2_K, Q3_K and per-row INT4 matrices with rows of at most 1024 weights at
+// batch 1 (2 but for INT4) take the kernel of gemv_tall.hip (128-weight units, a row per U
 // lanes); in the Q4_K stream layout and for per-row INT4 only rows of a
 // whole number of 128-weight units, so that no unit straddles two
 // super-blocks or reads past its row.
@@ -1472,26 +1472,34 @@ template <class F>
 constexpr bool kHasTall = std::is_same<F, pesti::FmtQ4_K>::value || std::is_same<F, pesti::FmtQ5_K>::value ||
                           std::is_same<F, pesti::FmtQ2_K>::value || std::is_same<F, pesti::FmtQ3_K>::value ||
                           std::is_same<F, pesti::FmtI4Row>::value || pesti::kStreamLayout<F>;
+// Largest batch the tall kernel takes: 2 (one dequantized weight feeds both
+// columns), below the batch at which the matrix cores take over.
+#ifndef PESTI_TALL_MAX_BATCH
+#define PESTI_TALL_MAX_BATCH 2
+#endif
+template <class F>
+constexpr int kTallMaxBatch = PESTI_TALL_MAX_BATCH < kMfmaMinBatch<F> - 1 ? PESTI_TALL_MAX_BATCH
+                                                                           : kMfmaMinBatch<F> - 1;
 template <class F>
 inline bool tall_op(const GemvArgs& a, int batch) {
   constexpr bool kWholeUnits = pesti::kStreamLayout<F> || std::is_same<F, pesti::FmtI4Row>::value;
-  return kHasTall<F> && batch == 1 && a.out >= kTallMinRows && a.in > 0 && a.in <= 1024 &&
-         (!kWholeUnits || a.in % 128 == 0);
+  return kHasTall<F> && batch >= 1 && batch <= kTallMaxBatch<F> && a.out >= kTallMinRows && a.in > 0 &&
+         a.in <= 1024 && (!kWholeUnits || a.in % 128 == 0);
 }
 // One launch of ops that all pass tall_op and share one row length in
 // 128-weight units; x and y of every op set.
-int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st);
-int launch_tall_q5_k(const GroupArgs& g, hipStream_t st);
-int launch_tall_q2_k(const GroupArgs& g, hipStream_t st);
-int launch_tall_q3_k(const GroupArgs& g, hipStream_t st);
-int launch_tall_i4row(const GroupArgs& g, hipStream_t st);
+int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, int batch, hipStream_t st);
+int launch_tall_q5_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_tall_q2_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_tall_q3_k(const GroupArgs& g, int batch, hipStream_t st);
+int launch_tall_i4row(const GroupArgs& g, int batch, hipStream_t st);
 template <class F>
-inline int launch_tall(const GroupArgs& g, hipStream_t st) {
-  if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_tall_q5_k(g, st);
-  else if constexpr (std::is_same<F, pesti::FmtQ2_K>::value) return launch_tall_q2_k(g, st);
-  else if constexpr (std::is_same<F, pesti::FmtQ3_K>::value) return launch_tall_q3_k(g, st);
-  else if constexpr (std::is_same<F, pesti::FmtI4Row>::value) return launch_tall_i4row(g, st);
-  else return launch_tall_q4_k(g, pesti::kStreamLayout<F>, st);
+inline int launch_tall(const GroupArgs& g, int batch, hipStream_t st) {
+  if constexpr (std::is_same<F, pesti::FmtQ5_K>::value) return launch_tall_q5_k(g, batch, st);
+  else if constexpr (std::is_same<F, pesti::FmtQ2_K>::value) return launch_tall_q2_k(g, batch, st);
+  else if constexpr (std::is_same<F, pesti::FmtQ3_K>::value) return launch_tall_q3_k(g, batch, st);
+  else if constexpr (std::is_same<F, pesti::FmtI4Row>::value) return launch_tall_i4row(g, batch, st);
+  else return launch_tall_q4_k(g, pesti::kStreamLayout<F>, batch, st);
 }
 
 // One launch of ops that all pass mfma_op and share one row length in
@@ -1591,7 +1599,7 @@ int group_dispatch(int32_t n_ops, const pesti_gemv_op* ops, int32_t batch, void*
         t.op[t.n_ops].y = ops[live[j]].y;
         ++t.n_ops;
       }
-      const int r = launch_tall<F>(t, stream_h);
+      const int r = launch_tall<F>(t, batch, stream_h);
       if (r != PESTI_OK) return r;
     }
     max_units = 0;

@@ -1,5 +1,5 @@
-// Batch-1 mat-vec for tall Q4_K, Q5_K, Q2_K, Q3_K and per-row INT4 matrices
-// with short rows (the LM head, 151936 x 896): y = W x + b.
+// Batch-1 and batch-2 mat-vec for tall Q4_K, Q5_K, Q2_K, Q3_K and per-row
+// INT4 matrices with short rows (the LM head, 151936 x 896): y = W x + b.
 //
 // The operation is the decode step's row-major matrix-vector product with
 // the weights kept in GGUF Q4_K, Q5_K, Q2_K or Q3_K blocks ("Project scaffold:
@@ -21,9 +21,10 @@
 // once for 36 rows (measured on the 151936 x 896 head: 2 / 4 / 8 / 16 waves
 // 21.5 / 20.0 / 22.6 / 26.8 us).  Each weight is dequantized on its own, w =
 // (d sc 2^9)(q 2^-9) - dmin m, one rounding of the exact value (the float32
-// weight, bit for bit), then multiplied into the lane's sum; the U partial
-// sums of a row are added in lane order by cross-lane reads (a fixed order:
-// results do not depend on timing).
+// weight, bit for bit), then multiplied into the lane's sum (at batch 2
+// into both columns' sums: the decode is paid once for two products); the U
+// partial sums of a row are added in lane order by cross-lane reads (a fixed
+// order: results do not depend on timing).
 #include "gemv_impl.h"
 
 namespace pesti {
@@ -72,7 +73,9 @@ struct TallQ4K {
   // sc = S[t] & 63, m = S[t + 4] & 63; for h = 1 sc = (S[t + 8] & 15) |
   // (S[t] >> 6) << 4, m = (S[t + 8] >> 4) | (S[t + 4] >> 6) << 4 (S = header
   // bytes 4..15, dwords y, z, w).
-  __device__ __forceinline__ static float compute(const Raw& r, int u, bool h1, const float* xs) {
+  template <int B>
+  __device__ __forceinline__ static void compute(const Raw& r, int u, bool h1, const float* xs, int xst,
+                                                 float (&acc)[B]) {
     const uint32_t y = r.hdr.y, z = r.hdr.z, w = r.hdr.w;
     const uint32_t scv = h1 ? ((w & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u)) : (y & 0x3F3F3F3Fu);
     const uint32_t mv = h1 ? (((w >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u)) : (z & 0x3F3F3F3Fu);
@@ -80,29 +83,36 @@ struct TallQ4K {
     const float ds[4] = {d512 * ubyte<0>(scv), d512 * ubyte<1>(scv), d512 * ubyte<2>(scv), d512 * ubyte<3>(scv)};
     const float ndm[4] = {-(dmin * ubyte<0>(mv)), -(dmin * ubyte<1>(mv)), -(dmin * ubyte<2>(mv)),
                           -(dmin * ubyte<3>(mv))};
-    float acc = 0.f;
     const int x0 = 128 * u;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {   // run 2h + k: low nibbles sub-block 4h + 2k, high 4h + 2k + 1
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t q = word(r, 8 * k + i);
-        const f32x4 xl = xs4(xs, x0 + 64 * k + 4 * i);
-        const f32x4 xh = xs4(xs, x0 + 64 * k + 32 + 4 * i);
-        float l0, l1, l2, l3, g0, g1, g2, g3;
-        nibbles_x512(q & 0x0F0F0F0Fu, l0, l1, l2, l3);
-        nibbles_x512((q >> 4) & 0x0F0F0F0Fu, g0, g1, g2, g3);
-        acc = fmaf(fmaf(ds[2 * k], l0, ndm[2 * k]), xl.x, acc);
-        acc = fmaf(fmaf(ds[2 * k], l1, ndm[2 * k]), xl.y, acc);
-        acc = fmaf(fmaf(ds[2 * k], l2, ndm[2 * k]), xl.z, acc);
-        acc = fmaf(fmaf(ds[2 * k], l3, ndm[2 * k]), xl.w, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], g0, ndm[2 * k + 1]), xh.x, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], g1, ndm[2 * k + 1]), xh.y, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], g2, ndm[2 * k + 1]), xh.z, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], g3, ndm[2 * k + 1]), xh.w, acc);
+        float l[4], g[4];
+        nibbles_x512(q & 0x0F0F0F0Fu, l[0], l[1], l[2], l[3]);
+        nibbles_x512((q >> 4) & 0x0F0F0F0Fu, g[0], g[1], g[2], g[3]);
+        float wl[4], wg[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wl[e] = fmaf(ds[2 * k], l[e], ndm[2 * k]);
+          wg[e] = fmaf(ds[2 * k + 1], g[e], ndm[2 * k + 1]);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const f32x4 xl = xs4(xs + b * xst, x0 + 64 * k + 4 * i);
+          const f32x4 xh = xs4(xs + b * xst, x0 + 64 * k + 32 + 4 * i);
+          acc[b] = fmaf(wl[0], xl.x, acc[b]);
+          acc[b] = fmaf(wl[1], xl.y, acc[b]);
+          acc[b] = fmaf(wl[2], xl.z, acc[b]);
+          acc[b] = fmaf(wl[3], xl.w, acc[b]);
+          acc[b] = fmaf(wg[0], xh.x, acc[b]);
+          acc[b] = fmaf(wg[1], xh.y, acc[b]);
+          acc[b] = fmaf(wg[2], xh.z, acc[b]);
+          acc[b] = fmaf(wg[3], xh.w, acc[b]);
+        }
       }
     }
-    return acc;
   }
 };
 
@@ -141,7 +151,9 @@ struct TallQ5K {
 
   // acc += sum over the unit's 128 weights of w * x; scales and mins of
   // sub-blocks 4h + t as TallQ4K::compute.
-  __device__ __forceinline__ static float compute(const Raw& r, int u, bool h1, const float* xs) {
+  template <int B>
+  __device__ __forceinline__ static void compute(const Raw& r, int u, bool h1, const float* xs, int xst,
+                                                 float (&acc)[B]) {
     const uint32_t y = r.hdr.y, z = r.hdr.z, w = r.hdr.w;
     const uint32_t scv = h1 ? ((w & 0x0F0F0F0Fu) | ((y >> 2) & 0x30303030u)) : (y & 0x3F3F3F3Fu);
     const uint32_t mv = h1 ? (((w >> 4) & 0x0F0F0F0Fu) | ((z >> 2) & 0x30303030u)) : (z & 0x3F3F3F3Fu);
@@ -150,7 +162,6 @@ struct TallQ5K {
     const float ndm[4] = {-(dmin * ubyte<0>(mv)), -(dmin * ubyte<1>(mv)), -(dmin * ubyte<2>(mv)),
                           -(dmin * ubyte<3>(mv))};
     const uint32_t hshift = h1 ? 4u : 0u;   // fifth bits of runs 2h, 2h + 1: bits 4h .. 4h + 3
-    float acc = 0.f;
     const int x0 = 128 * u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -160,19 +171,27 @@ struct TallQ5K {
         const uint32_t q = k == 0 ? (i < 4 ? pick(r.c0, i) : pick(r.c1, i)) : (i < 4 ? pick(r.c2, i) : pick(r.c3, i));
         const uint32_t lo = (q & 0x0F0F0F0Fu) | (((hb >> (2 * k)) & 0x01010101u) << 4);
         const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (((hb >> (2 * k + 1)) & 0x01010101u) << 4);
-        const f32x4 xl = xs4(xs, x0 + 64 * k + 4 * i);
-        const f32x4 xh = xs4(xs, x0 + 64 * k + 32 + 4 * i);
-        acc = fmaf(fmaf(ds[2 * k], ubyte<0>(lo), ndm[2 * k]), xl.x, acc);
-        acc = fmaf(fmaf(ds[2 * k], ubyte<1>(lo), ndm[2 * k]), xl.y, acc);
-        acc = fmaf(fmaf(ds[2 * k], ubyte<2>(lo), ndm[2 * k]), xl.z, acc);
-        acc = fmaf(fmaf(ds[2 * k], ubyte<3>(lo), ndm[2 * k]), xl.w, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<0>(hi), ndm[2 * k + 1]), xh.x, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<1>(hi), ndm[2 * k + 1]), xh.y, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<2>(hi), ndm[2 * k + 1]), xh.z, acc);
-        acc = fmaf(fmaf(ds[2 * k + 1], ubyte<3>(hi), ndm[2 * k + 1]), xh.w, acc);
+        const float wl[4] = {fmaf(ds[2 * k], ubyte<0>(lo), ndm[2 * k]), fmaf(ds[2 * k], ubyte<1>(lo), ndm[2 * k]),
+                             fmaf(ds[2 * k], ubyte<2>(lo), ndm[2 * k]), fmaf(ds[2 * k], ubyte<3>(lo), ndm[2 * k])};
+        const float wg[4] = {fmaf(ds[2 * k + 1], ubyte<0>(hi), ndm[2 * k + 1]),
+                             fmaf(ds[2 * k + 1], ubyte<1>(hi), ndm[2 * k + 1]),
+                             fmaf(ds[2 * k + 1], ubyte<2>(hi), ndm[2 * k + 1]),
+                             fmaf(ds[2 * k + 1], ubyte<3>(hi), ndm[2 * k + 1])};
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const f32x4 xl = xs4(xs + b * xst, x0 + 64 * k + 4 * i);
+          const f32x4 xh = xs4(xs + b * xst, x0 + 64 * k + 32 + 4 * i);
+          acc[b] = fmaf(wl[0], xl.x, acc[b]);
+          acc[b] = fmaf(wl[1], xl.y, acc[b]);
+          acc[b] = fmaf(wl[2], xl.z, acc[b]);
+          acc[b] = fmaf(wl[3], xl.w, acc[b]);
+          acc[b] = fmaf(wg[0], xh.x, acc[b]);
+          acc[b] = fmaf(wg[1], xh.y, acc[b]);
+          acc[b] = fmaf(wg[2], xh.z, acc[b]);
+          acc[b] = fmaf(wg[3], xh.w, acc[b]);
+        }
       }
     }
-    return acc;
   }
 };
 
@@ -198,9 +217,10 @@ struct TallQ2K {
     r.dd = load_u32(sb + 80);
   }
 
-  __device__ __forceinline__ static float compute(const Raw& r, int u, bool, const float* xs) {
+  template <int B>
+  __device__ __forceinline__ static void compute(const Raw& r, int u, bool, const float* xs, int xst,
+                                                 float (&acc)[B]) {
     const float d512 = f16_lo(r.dd) * 512.0f, dmin = f16_hi(r.dd);
-    float acc = 0.f;
     const int x0 = 128 * u;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -216,15 +236,18 @@ struct TallQ2K {
           const uint32_t w = t == 0 ? qv.x : (t == 1 ? qv.y : (t == 2 ? qv.z : qv.w));
           float q0, q1, q2, q3;
           nibbles_x512((w >> (2 * j)) & 0x03030303u, q0, q1, q2, q3);
-          const f32x4 xv = xs4(xs, x0 + 32 * j + 16 * c + 4 * t);
-          acc = fmaf(fmaf(ds, q0, ndm), xv.x, acc);
-          acc = fmaf(fmaf(ds, q1, ndm), xv.y, acc);
-          acc = fmaf(fmaf(ds, q2, ndm), xv.z, acc);
-          acc = fmaf(fmaf(ds, q3, ndm), xv.w, acc);
+          const float w0 = fmaf(ds, q0, ndm), w1 = fmaf(ds, q1, ndm), w2 = fmaf(ds, q2, ndm), w3 = fmaf(ds, q3, ndm);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const f32x4 xv = xs4(xs + b * xst, x0 + 32 * j + 16 * c + 4 * t);
+            acc[b] = fmaf(w0, xv.x, acc[b]);
+            acc[b] = fmaf(w1, xv.y, acc[b]);
+            acc[b] = fmaf(w2, xv.z, acc[b]);
+            acc[b] = fmaf(w3, xv.w, acc[b]);
+          }
         }
       }
     }
-    return acc;
   }
 };
 
@@ -258,14 +281,15 @@ struct TallQ3K {
     r.sd = load2(sb + 94);
   }
 
-  __device__ __forceinline__ static float compute(const Raw& r, int u, bool half, const float* xs) {
+  template <int B>
+  __device__ __forceinline__ static void compute(const Raw& r, int u, bool half, const float* xs, int xst,
+                                                 float (&acc)[B]) {
     // scale bytes 0..3, 4..7, 8..11 (super-block bytes 96..107) and d (108)
     const uint32_t s0 = __builtin_amdgcn_alignbyte(r.sd.y, r.sd.x, 2);
     const uint32_t s1 = __builtin_amdgcn_alignbyte(r.sd.z, r.sd.y, 2);
     const uint32_t s2 = __builtin_amdgcn_alignbyte(r.sd.w, r.sd.z, 2);
     const float d = f16_hi(r.sd.w);
     const uint32_t h4 = half ? 4u : 0u;
-    float acc = 0.f;
     const int x0 = 128 * u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -278,7 +302,9 @@ struct TallQ3K {
         const uint32_t lo4 = ((k < 4 ? s0 : s1) >> (8 * (k & 3) + h4)) & 15u;
         const uint32_t hi2 = (s2 >> (8 * (k & 3) + h4 + 2 * (j >> 1))) & 3u;
         const float ds = d * static_cast<float>(static_cast<int>(lo4 | (hi2 << 4)) - 32);
-        float p = 0.f;
+        float p[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) p[b] = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const uint32_t w = t == 0 ? qv.x : (t == 1 ? qv.y : (t == 2 ? qv.z : qv.w));
@@ -289,16 +315,20 @@ struct TallQ3K {
           // v_perm gives 0xFF, 12 gives 0 (no multiply)
           const uint32_t neg = __builtin_amdgcn_perm(0u, 0u, 0x0D0D0D0Du - hb);
           const uint32_t qb = low2 | (neg & 0xFCFCFCFCu);   // signed bytes -4..3
-          const f32x4 xv = xs4(xs, x0 + 32 * j + 16 * c + 4 * t);
-          p = fmaf(sbyte<0>(qb), xv.x, p);
-          p = fmaf(sbyte<1>(qb), xv.y, p);
-          p = fmaf(sbyte<2>(qb), xv.z, p);
-          p = fmaf(sbyte<3>(qb), xv.w, p);
+          const float c0 = sbyte<0>(qb), c1 = sbyte<1>(qb), c2 = sbyte<2>(qb), c3 = sbyte<3>(qb);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const f32x4 xv = xs4(xs + b * xst, x0 + 32 * j + 16 * c + 4 * t);
+            p[b] = fmaf(c0, xv.x, p[b]);
+            p[b] = fmaf(c1, xv.y, p[b]);
+            p[b] = fmaf(c2, xv.z, p[b]);
+            p[b] = fmaf(c3, xv.w, p[b]);
+          }
         }
-        acc = fmaf(ds, p, acc);
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = fmaf(ds, p[b], acc[b]);
       }
     }
-    return acc;
   }
 };
 
@@ -322,8 +352,9 @@ struct TallI4 {
     r.c3 = load_u32x4_a16(p + 48);
   }
 
-  __device__ __forceinline__ static float compute(const Raw& r, int u, bool, const float* xs) {
-    float acc = 0.f;
+  template <int B>
+  __device__ __forceinline__ static void compute(const Raw& r, int u, bool, const float* xs, int xst,
+                                                 float (&acc)[B]) {
     const int x0 = 128 * u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -331,18 +362,22 @@ struct TallI4 {
       const uint32_t v = (i & 3) == 0 ? cv.x : ((i & 3) == 1 ? cv.y : ((i & 3) == 2 ? cv.z : cv.w));
       const uint32_t ev = (v << 4) & 0xF0F0F0F0u;   // even weights, 16 q each
       const uint32_t od = v & 0xF0F0F0F0u;          // odd weights
-      const f32x4 xa = xs4(xs, x0 + 8 * i);
-      const f32x4 xb = xs4(xs, x0 + 8 * i + 4);
-      acc = fmaf(sbyte<0>(ev), xa.x, acc);
-      acc = fmaf(sbyte<0>(od), xa.y, acc);
-      acc = fmaf(sbyte<1>(ev), xa.z, acc);
-      acc = fmaf(sbyte<1>(od), xa.w, acc);
-      acc = fmaf(sbyte<2>(ev), xb.x, acc);
-      acc = fmaf(sbyte<2>(od), xb.y, acc);
-      acc = fmaf(sbyte<3>(ev), xb.z, acc);
-      acc = fmaf(sbyte<3>(od), xb.w, acc);
+      const float q[8] = {sbyte<0>(ev), sbyte<0>(od), sbyte<1>(ev), sbyte<1>(od),
+                          sbyte<2>(ev), sbyte<2>(od), sbyte<3>(ev), sbyte<3>(od)};
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const f32x4 xa = xs4(xs + b * xst, x0 + 8 * i);
+        const f32x4 xb = xs4(xs + b * xst, x0 + 8 * i + 4);
+        acc[b] = fmaf(q[0], xa.x, acc[b]);
+        acc[b] = fmaf(q[1], xa.y, acc[b]);
+        acc[b] = fmaf(q[2], xa.z, acc[b]);
+        acc[b] = fmaf(q[3], xa.w, acc[b]);
+        acc[b] = fmaf(q[4], xb.x, acc[b]);
+        acc[b] = fmaf(q[5], xb.y, acc[b]);
+        acc[b] = fmaf(q[6], xb.z, acc[b]);
+        acc[b] = fmaf(q[7], xb.w, acc[b]);
+      }
     }
-    return acc;
   }
 };
 
@@ -361,10 +396,11 @@ struct TallRowScales<T, std::void_t<decltype(T::kRowScales)>> { static constexpr
 // take 2, 4 or 8 row blocks in turn with the next block's loads issued
 // before the current block's arithmetic (in one run: 23.2 us for one block against
 // 24.0 / 26.5 / 33.2: fewer workgroups keep fewer loads in flight).
-template <class T, int U, bool S>
+template <class T, int U, bool S, int B>
 __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
   static_assert(!S || std::is_same<T, TallQ4K>::value, "the stream layout is Q4_K's");
-  __shared__ float xs[xs_phys(kTallMaxIn)];
+  constexpr int kXS = static_cast<int>(xs_phys(kTallMaxIn));   // LDS floats per batch column
+  __shared__ float xs[B * kXS];
   constexpr int kRowsPerWave = kWave / U;
   constexpr int kRowsPerGroup = kRowsPerWave * kTallWaves;
   const GemvArgs a = g.op[blockIdx.y];
@@ -384,12 +420,14 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
   constexpr int kX4 = 32 * U;   // float4 slots of the padded row
   constexpr int kXPer = (kX4 + kTallThreads - 1) / kTallThreads;
   const int in4 = static_cast<int>(a.in >> 2);
-  f32x4 xv[kXPer];
+  f32x4 xv[B][kXPer];
 #pragma unroll
-  for (int k = 0; k < kXPer; ++k) {
-    const int s = tid + k * kTallThreads;
-    xv[k] = reinterpret_cast<const f32x4*>(a.x)[s < in4 ? s : 0];
-  }
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+      const int s = tid + k * kTallThreads;
+      xv[b][k] = reinterpret_cast<const f32x4*>(a.x + b * a.in)[s < in4 ? s : 0];
+    }
   const int64_t lrow = live ? row : first_wg;
   const int lu = live ? u : 0;
   const int64_t gu = S ? lrow * U + lu : lu;
@@ -399,21 +437,30 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
   float rs = 1.f;
   if constexpr (TallRowScales<T>::value) rs = a.scales[lrow];
 #pragma unroll
-  for (int k = 0; k < kXPer; ++k) {
-    const int s = tid + k * kTallThreads;
-    if (s < kX4) *reinterpret_cast<f32x4*>(xs + xs_phys(4 * s)) = s < in4 ? xv[k] : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-  const float part = live ? T::compute(r, u, (gu & 1) != 0, xs) : 0.f;
-  // the row's U partial sums, added in lane order (reads past the wave take
-  // the lane's own value; only the row's first lane stores)
-  float sum = part;
+  for (int b = 0; b < B; ++b)
 #pragma unroll
-  for (int k = 1; k < U; ++k) sum += __shfl(part, lane + k < kWave ? lane + k : lane, kWave);
-  if constexpr (TallRowScales<T>::value) {
-    if (u == 0 && live) a.y[row] = fmaf(sum * T::kAccScale, rs, a.bias ? bv : 0.f);
-  } else {
-    if (u == 0 && live) a.y[row] = sum + (a.bias ? bv : 0.f);
+    for (int k = 0; k < kXPer; ++k) {
+      const int s = tid + k * kTallThreads;
+      if (s < kX4)
+        *reinterpret_cast<f32x4*>(xs + b * kXS + xs_phys(4 * s)) = s < in4 ? xv[b][k] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  __syncthreads();
+  float part[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) part[b] = 0.f;
+  if (live) T::template compute<B>(r, u, (gu & 1) != 0, xs, kXS, part);
+  // each column's U partial sums of the row, added in lane order (reads past
+  // the wave take the lane's own value; only the row's first lane stores)
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    float sum = part[b];
+#pragma unroll
+    for (int k = 1; k < U; ++k) sum += __shfl(part[b], lane + k < kWave ? lane + k : lane, kWave);
+    if constexpr (TallRowScales<T>::value) {
+      if (u == 0 && live) a.y[b * a.out + row] = fmaf(sum * T::kAccScale, rs, a.bias ? bv : 0.f);
+    } else {
+      if (u == 0 && live) a.y[b * a.out + row] = sum + (a.bias ? bv : 0.f);
+    }
   }
 }
 
@@ -421,7 +468,7 @@ __global__ __launch_bounds__(kTallThreads) void gemv_tall_kernel(GroupArgs g) {
 
 namespace pesti_gemv {
 
-template <class T, int U, bool S>
+template <class T, int U, bool S, int B>
 int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   constexpr int64_t kRows = (pesti::kWave / U) * pesti::kTallWaves;
   int64_t max_out = 0;
@@ -429,59 +476,66 @@ int launch_tall_u(const GroupArgs& g, hipStream_t st) {
   const int64_t groups = (max_out + kRows - 1) / kRows;
   GroupArgs args = g;
   void* params[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_kernel<T, U, S>),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pesti::gemv_tall_kernel<T, U, S, B>),
                                        dim3(static_cast<unsigned>(groups), static_cast<unsigned>(g.n_ops)),
                                        dim3(pesti::kTallThreads), params, 0, st);
   return e == hipSuccess ? PESTI_OK : PESTI_ERR_LAUNCH;
 }
 
-template <class T, bool S>
-int launch_tall_s(const GroupArgs& g, hipStream_t st) {
+template <class T, bool S, int B>
+int launch_tall_b(const GroupArgs& g, hipStream_t st) {
   switch ((g.op[0].in + 127) / 128) {
-    case 1: return launch_tall_u<T, 1, S>(g, st);
-    case 2: return launch_tall_u<T, 2, S>(g, st);
-    case 3: return launch_tall_u<T, 3, S>(g, st);
-    case 4: return launch_tall_u<T, 4, S>(g, st);
-    case 5: return launch_tall_u<T, 5, S>(g, st);
-    case 6: return launch_tall_u<T, 6, S>(g, st);
-    case 7: return launch_tall_u<T, 7, S>(g, st);
-    case 8: return launch_tall_u<T, 8, S>(g, st);
+    case 1: return launch_tall_u<T, 1, S, B>(g, st);
+    case 2: return launch_tall_u<T, 2, S, B>(g, st);
+    case 3: return launch_tall_u<T, 3, S, B>(g, st);
+    case 4: return launch_tall_u<T, 4, S, B>(g, st);
+    case 5: return launch_tall_u<T, 5, S, B>(g, st);
+    case 6: return launch_tall_u<T, 6, S, B>(g, st);
+    case 7: return launch_tall_u<T, 7, S, B>(g, st);
+    case 8: return launch_tall_u<T, 8, S, B>(g, st);
     default: return PESTI_ERR_SHAPE;
   }
 }
 
-// One launch of tall batch-1 Q4_K ops that share one row length; in the
+template <class T, bool S>
+int launch_tall_s(const GroupArgs& g, int batch, hipStream_t st) {
+  if (batch == 1) return launch_tall_b<T, S, 1>(g, st);
+  if (batch == 2 && !pesti::TallRowScales<T>::value) return launch_tall_b<T, S, 2>(g, st);
+  return PESTI_ERR_BATCH;
+}
+
+// One launch of tall Q4_K ops that share one row length; in the
 // stream layout every row is a whole number of 128-weight units.
-int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, hipStream_t st) {
+int launch_tall_q4_k(const GroupArgs& g, bool stream_layout, int batch, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
-  if (!stream_layout) return launch_tall_s<pesti::TallQ4K, false>(g, st);
+  if (!stream_layout) return launch_tall_s<pesti::TallQ4K, false>(g, batch, st);
   for (int i = 0; i < g.n_ops; ++i)
     if (g.op[i].in % 128 != 0 || g.op[i].in != g.op[0].in) return PESTI_ERR_SHAPE;
-  return launch_tall_s<pesti::TallQ4K, true>(g, st);
+  return launch_tall_s<pesti::TallQ4K, true>(g, batch, st);
 }
 
 // The same for Q5_K, Q2_K and Q3_K (row layout).
-int launch_tall_q5_k(const GroupArgs& g, hipStream_t st) {
+int launch_tall_q5_k(const GroupArgs& g, int batch, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
-  return launch_tall_s<pesti::TallQ5K, false>(g, st);
+  return launch_tall_s<pesti::TallQ5K, false>(g, batch, st);
 }
 
-int launch_tall_q2_k(const GroupArgs& g, hipStream_t st) {
+int launch_tall_q2_k(const GroupArgs& g, int batch, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
-  return launch_tall_s<pesti::TallQ2K, false>(g, st);
+  return launch_tall_s<pesti::TallQ2K, false>(g, batch, st);
 }
 
-int launch_tall_q3_k(const GroupArgs& g, hipStream_t st) {
+int launch_tall_q3_k(const GroupArgs& g, int batch, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
-  return launch_tall_s<pesti::TallQ3K, false>(g, st);
+  return launch_tall_s<pesti::TallQ3K, false>(g, batch, st);
 }
 
 // Per-row INT4: rows of a whole number of 128-weight units only.
-int launch_tall_i4row(const GroupArgs& g, hipStream_t st) {
+int launch_tall_i4row(const GroupArgs& g, int batch, hipStream_t st) {
   if (g.n_ops < 1) return PESTI_ERR_SHAPE;
   for (int i = 0; i < g.n_ops; ++i)
     if (g.op[i].in % 128 != 0 || !g.op[i].scales) return PESTI_ERR_SHAPE;
-  return launch_tall_s<pesti::TallI4, false>(g, st);
+  return launch_tall_s<pesti::TallI4, false>(g, batch, st);
 }
 
 }  // namespace pesti_gemv

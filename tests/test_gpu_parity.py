@@ -1320,6 +1320,46 @@ def test_tall_batch_1_group_equals_single_calls_bitwise(fmt):
         assert np.array_equal(yd.cpu().numpy(), y1[0])
 
 
+# batch 2 on the same kernel: each dequantized weight feeds both columns
+@pytest.mark.parametrize("fmt", TALL_FORMATS + ("q4_k_stream",))
+@pytest.mark.parametrize("inf", [128, 384, 896, 1024, 800])
+def test_tall_batch_2_every_row(fmt, inf):
+    if fmt == "q4_k_stream" and inf % 128:
+        pytest.skip("the stream layout's tall rows are whole 128-weight units")
+    out = TALL_ROWS + 29
+    packed, scales, x, bias = make(fmt, out, inf, 170, 2)
+    y = run_gemv(fmt, packed, scales, out, inf, x, bias)
+    y_ref, s_ref = oracle.gemv_packed(fmt, packed, out, inf, x, bias)
+    assert_within(y, y_ref, s_ref, GEMV_REL, f"tall {fmt} b2 in={inf}")
+
+
+@pytest.mark.parametrize("fmt", TALL_FORMATS)
+def test_tall_batch_2_one_hot_columns_and_group_bitwise(fmt):
+    import torch
+    import dequantize_mat_vec_amd as dmv
+    from gpu_util import to_dev
+    out, inf = TALL_ROWS + 5, 896
+    packed, _, _, _ = make(fmt, out, inf, 171)
+    w32 = oracle.dequantize_f32(fmt, packed, out, inf)
+    for j0, j1 in ((0, 895), (127, 128), (255, 256)):
+        x = np.zeros((2, inf), np.float32)
+        x[0, j0] = 1.0
+        x[1, j1] = 1.0
+        y = run_gemv(fmt, packed, None, out, inf, x)
+        assert np.array_equal(y[0], w32[:, j0]) and np.array_equal(y[1], w32[:, j1]), (j0, j1)
+    ops, singles = [], []
+    for n, (o, i) in enumerate([(TALL_ROWS + 7, 896), (300, 896), (TALL_ROWS + 1, 512)]):
+        pk, _, x, bias = make(fmt, o, i, 172 + n, 2)
+        w, xd, bd = to_dev(pk.reshape(-1)), to_dev(x), to_dev(bias)
+        yd = torch.zeros(2 * o, dtype=torch.float32, device="cuda")
+        ops.append((o, i, w, xd, yd, bd, None))
+        singles.append(run_gemv(fmt, pk, None, o, i, x, bias))
+    dmv.pesti_gemv_group(fmt, ops, 2)
+    torch.cuda.synchronize()
+    for (o, _, _, _, yd, _, _), ys in zip(ops, singles):
+        assert np.array_equal(yd.cpu().numpy().reshape(2, o), ys), o
+
+
 @pytest.mark.parametrize("fmt", TALL_FORMATS)
 def test_tall_batch_1_full_lm_head_sampled_rows(fmt):
     out, inf = synth.QWEN_VOCAB, 896
