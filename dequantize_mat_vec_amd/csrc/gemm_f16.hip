@@ -201,12 +201,39 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_valu_kernel(GemmArgs a) {
       for (int c = 0; c < 4; ++c) wv[j][c] = load_u32x4_a16(p + 8 * c);
     }
     if (j0 == 0) {
-      // X (B rows of K halves) into LDS, 16 bytes per thread and step.
+      // X (B rows of K halves) into LDS, 16 bytes per thread and step.  With
+      // more than four steps per thread (long rows), four steps' loads are
+      // issued before their stores (slots past the end re-read the thread's
+      // first chunk and are not stored) so that they overlap instead of
+      // paying one round trip each: 3072-deep rows at m = 8 6.56 -> 6.04 us;
+      // shorter rows keep one step at a time (batching them measured 2-5%
+      // slower: the stand-in loads cost more than they hide).
       const int chunks = B * (units * 4);
-      for (int e = threadIdx.x; e < chunks; e += kThreads) {
-        const int b = e / (units * 4), q = e % (units * 4);
-        const u32x4 v = load_u32x4_a16(a.x + b * a.k + 8 * q);
-        *reinterpret_cast<u32x4*>(xh + b * stride + xh_phys(8 * q)) = v;
+      if (chunks > 4 * kThreads) {
+        constexpr int kBatch = 4;
+        for (int e0 = threadIdx.x; e0 < chunks; e0 += kBatch * kThreads) {
+          u32x4 v[kBatch];
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int e = e0 + i * kThreads < chunks ? e0 + i * kThreads : e0;
+            const int b = e / (units * 4), q = e % (units * 4);
+            v[i] = load_u32x4_a16(a.x + b * a.k + 8 * q);
+          }
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int e = e0 + i * kThreads;
+            if (e < chunks) {
+              const int b = e / (units * 4), q = e % (units * 4);
+              *reinterpret_cast<u32x4*>(xh + b * stride + xh_phys(8 * q)) = v[i];
+            }
+          }
+        }
+      } else {
+        for (int e = threadIdx.x; e < chunks; e += kThreads) {
+          const int b = e / (units * 4), q = e % (units * 4);
+          const u32x4 v = load_u32x4_a16(a.x + b * a.k + 8 * q);
+          *reinterpret_cast<u32x4*>(xh + b * stride + xh_phys(8 * q)) = v;
+        }
       }
       __syncthreads();
     }
