@@ -202,12 +202,13 @@ int current_device(int* device, size_t* lds_per_group);
 // binary16 GEMM splits only single row tiles of X (it measured slower at
 // two), and below m = 16 it runs on the vector ALUs, unsplit.
 //
-// Q8_0, Q3_K and Q6_K, whose K-split kernels are bound by their count of
-// small W loads per workgroup, take two row tiles of X per workgroup when
-// split (gemm_split_row_tiles), which halves the W loads at the same
-// workgroup count; the other formats measured slower that way.
+// Q3_K and Q6_K, whose K-split kernels are bound by their count of small W
+// loads per workgroup, take two row tiles of X per workgroup when split
+// (gemm_split_row_tiles), which halves the W loads at the same workgroup
+// count; the other formats measured slower that way (Q8_0 too, once it read
+// its blocks in pairs).
 inline int gemm_split_row_tiles(int32_t format, int64_t m) {
-  const bool pairs = format == PESTI_FMT_Q8_0 || format == PESTI_FMT_Q3_K || format == PESTI_FMT_Q6_K;
+  const bool pairs = format == PESTI_FMT_Q3_K || format == PESTI_FMT_Q6_K;
   return pairs && m > 16 ? 2 : 1;
 }
 inline int gemm_splits(int32_t format, int64_t m, int64_t n, int64_t k) {

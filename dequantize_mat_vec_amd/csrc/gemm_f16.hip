@@ -332,6 +332,10 @@ int launch_mfma(const GemmArgs& a, float* ws, hipStream_t st) {
   return launch_mfma_t<16, 4>(a, nullptr, st);
 }
 
+#ifndef PESTI_WIDE_F16_RING
+#define PESTI_WIDE_F16_RING 8
+#endif
+
 // binary16 weights for the wide-layer kernel: a unit is one k-step, 32
 // consecutive weights of the row, the lane's 8 of them one 16-byte load.
 struct WPolF16 {
@@ -341,7 +345,7 @@ struct WPolF16 {
   static constexpr bool kScaled = false;
   static constexpr bool kChained = false;
   static constexpr int kSteps = 1;
-  static constexpr int kRing = 12;
+  static constexpr int kRing = PESTI_WIDE_F16_RING;
   struct Unit { pesti::u32x4 v; };
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
     un.v = pesti::load_u32x4_a16(row + 64 * u + 16 * kg);

@@ -100,6 +100,64 @@ struct QPolQ8_0 {
   }
 };
 
+// Eight int8 codes (two dwords) as exact binary16 operands: q + 128 (the
+// sign bit flipped) becomes 1152 + q by writing 0x64 above each byte, and
+// an exact packed subtraction of 1152 leaves q.
+__device__ __forceinline__ qhalf8 q8_codes(uint32_t lo, uint32_t hi) {
+  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+  uint32_t h[4];
+  h[0] = __builtin_amdgcn_perm(0x64646464u, a, 0x04010400u);
+  h[1] = __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u);
+  h[2] = __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u);
+  h[3] = __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u);
+  const qhalf2 base{static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(qhalf2, h[e]) - base);
+  return __builtin_bit_cast(qhalf8, h);
+}
+
+// Q8_0 block pairs, for rows of an even number of blocks (rows then start
+// on a dword boundary): steps s and s + 1 (s even) are blocks s and s + 1,
+// 68 bytes from byte 34s.  A lane reads bytes 8kg..8kg+11 of the pair (its
+// 8 codes of the first block, 2 bytes in, and for kg = 0 that block's d)
+// and bytes 36 + 8kg..+7 (its 8 codes of the second block); the second
+// block's d is the top half of the last dword lane kg = 3 reads.  Two
+// loads per pair instead of eight; each d reaches the other lanes of its
+// column by a cross-lane read when the step is used (all lanes active).
+struct QPolQ8_0P {
+  static constexpr int32_t kFormat = PESTI_FMT_Q8_0;
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr int kParts = 1;
+  // w: first block (odd 0) the three dwords at 8kg; second block (odd 1)
+  // its two code dwords and the first block's third dword (for its d).
+  struct Step { uint32_t w[3]; uint32_t odd; };
+
+  __device__ __forceinline__ static void load_pair(const uint8_t* row, int s, int kg, Step& a, Step& b) {
+    const uint8_t* pp = row + 34 * s;
+    const uint32_t* ev = reinterpret_cast<const uint32_t*>(pp + 8 * kg);
+    const uint32_t* ov = reinterpret_cast<const uint32_t*>(pp + 36 + 8 * kg);
+    a.w[0] = ev[0];
+    a.w[1] = ev[1];
+    a.w[2] = ev[2];
+    a.odd = 0;
+    b.w[0] = ov[0];
+    b.w[1] = ov[1];
+    b.w[2] = a.w[2];
+    b.odd = 1;
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Step& st, int, int) {
+    if (st.odd) return q8_codes(st.w[0], st.w[1]);
+    return q8_codes(__builtin_amdgcn_alignbyte(st.w[1], st.w[0], 2), __builtin_amdgcn_alignbyte(st.w[2], st.w[1], 2));
+  }
+  __device__ __forceinline__ static void scales(const Step& st, int, float& ds, float& dm) {
+    const int i = static_cast<int>(__lane_id()) & 15;
+    ds = st.odd ? f16_hi(static_cast<uint32_t>(__shfl(static_cast<int>(st.w[2]), i + 48, kWave)))
+                : f16_lo(static_cast<uint32_t>(__shfl(static_cast<int>(st.w[0]), i, kWave)));
+    dm = 0.f;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Q4_K: k-step s = sub-block j = s % 8 of super-block s / 8 (144 bytes:
 // d, dmin, 12 bytes of 6-bit scales/mins, 128 code bytes).  Sub-blocks 2g
@@ -500,6 +558,10 @@ struct QPolQ2_K {
 // super-block per unit - the 16-byte header once, and each lane's 8 code
 // bytes of the four sub-block pairs - so a unit feeds eight k-steps.
 // ---------------------------------------------------------------------------
+#ifndef PESTI_WIDE_Q8P_RING
+#define PESTI_WIDE_Q8P_RING 4
+#endif
+
 struct WPolQ8_0 {
   static constexpr int kSumWidth = 32;
   static constexpr int64_t kWideMinTiles = 1024;
@@ -515,6 +577,49 @@ struct WPolQ8_0 {
   }
   __device__ __forceinline__ static qhalf8 codes(const Unit& un, int, int, int) { return QPolQ8_0::codes(un); }
   __device__ __forceinline__ static float scale(const Unit& un, int, int) { return f16_lo(un.d); }
+};
+
+// Q8_0 pair unit, for rows of an even number of blocks: blocks 2u and
+// 2u + 1, 68 bytes that start on a dword boundary.  A lane reads bytes
+// 8kg..8kg+11 of the pair (its 8 codes of the first block, 2 bytes in, and
+// for kg = 0 that block's d) and bytes 36 + 8kg..+7 (its 8 codes of the
+// second block); the second block's d is the top half of the last dword
+// that lane kg = 3 reads.  Two loads for two k-steps instead of eight; the
+// d of each block reaches the other lanes of its column by a cross-lane
+// read.  Codes as in q8_codes.
+struct WPolQ8_0P {
+  static constexpr int kSumWidth = 32;
+  static constexpr int64_t kWideMinTiles = 1024;
+  static constexpr bool kMin = false;
+  static constexpr bool kScaled = true;
+  static constexpr bool kChained = false;
+  static constexpr int kSteps = 2;
+  static constexpr int kRing = PESTI_WIDE_Q8P_RING;
+  static constexpr int kParts = 1;
+  struct Unit { uint32_t e[3]; uint32_t o[2]; };
+
+  __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
+    const uint32_t* ev = reinterpret_cast<const uint32_t*>(row + 68 * u + 8 * kg);
+    const uint32_t* ov = reinterpret_cast<const uint32_t*>(row + 68 * u + 36 + 8 * kg);
+    un.e[0] = ev[0];
+    un.e[1] = ev[1];
+    un.e[2] = ev[2];
+    un.o[0] = ov[0];
+    un.o[1] = ov[1];
+  }
+  __device__ __forceinline__ static qhalf8 codes(const Unit& un, int j, int, int) {
+    if (j == 0)
+      return q8_codes(__builtin_amdgcn_alignbyte(un.e[1], un.e[0], 2), __builtin_amdgcn_alignbyte(un.e[2], un.e[1], 2));
+    return q8_codes(un.o[0], un.o[1]);
+  }
+  // d of block j of the pair, for the lane's column i: from lane i (kg 0)
+  // for the first block, lane i + 48 (kg 3) for the second.  Every lane of
+  // the wavefront takes part (the kernel calls this on wave-uniform paths).
+  __device__ __forceinline__ static float scale(const Unit& un, int j, int) {
+    const int i = static_cast<int>(__lane_id()) & 15;
+    if (j == 0) return f16_lo(static_cast<uint32_t>(__shfl(static_cast<int>(un.e[0]), i, kWave)));
+    return f16_hi(static_cast<uint32_t>(__shfl(static_cast<int>(un.e[2]), i + 48, kWave)));
+  }
 };
 
 // Q6_K unit: one super-block - per lane its 8-byte pieces of ql (four) and
@@ -1028,6 +1133,8 @@ int pesti_host::gemm_quant_run(int32_t format, int64_t m, int64_t n, int64_t k, 
   using namespace pesti;
   switch (format) {
     case PESTI_FMT_Q8_0:
+      if ((k / 32) % 2 == 0)
+        return gemm_quant<QPolQ8_0P, WPolQ8_0P>(m, n, k, blocks, x, y, bias, (k / 32) * 34, ws, st);
       return gemm_quant<QPolQ8_0, WPolQ8_0>(m, n, k, blocks, x, y, bias, (k / 32) * 34, ws, st);
     case PESTI_FMT_Q4_K:
       return gemm_quant<QPolQ4_K, WPolQ4_K>(m, n, k, blocks, x, y, bias, ((k + 255) / 256) * 144, ws, st);
