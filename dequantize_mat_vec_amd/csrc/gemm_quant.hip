@@ -557,6 +557,10 @@ struct QPolQ2_K {
 // Q8_0: one block per unit, the step's loads as above.  Q4_K: one
 // super-block per unit - the 16-byte header once, and each lane's 8 code
 // bytes of the four sub-block pairs - so a unit feeds eight k-steps.
+// The super-block formats keep two units in flight per wavefront: deeper
+// rings measured slower at the 151936x896 LM head (m 16, Q4_K 32.2 / 32.7 /
+// 33.4 / 40.4 us for 2 / 3 / 4 / 6 units, Q6_K 47.5 / 51.4 / 53.5 / 68.5;
+// m 64 within 1-3%).
 // ---------------------------------------------------------------------------
 #ifndef PESTI_WIDE_Q8P_RING
 #define PESTI_WIDE_Q8P_RING 4
@@ -638,7 +642,7 @@ struct WPolQ6_K {
   static constexpr bool kChained = false;
   static constexpr int kParts = 2;
   static constexpr int kSteps = 8;
-  static constexpr int kRing = 3;
+  static constexpr int kRing = 2;
   struct Unit { uint32_t l[4][2]; uint32_t h[2][2]; q6u4 sc; uint32_t d; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
@@ -678,7 +682,7 @@ struct WPolQ4_K {
   static constexpr bool kChained = true;
   static constexpr int kParts = 1;
   static constexpr int kSteps = 8;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 2;
   struct Unit { u32x4 hdr; uint32_t c[4][2]; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
@@ -734,7 +738,7 @@ struct WPolQ5_K {
   static constexpr bool kChained = true;
   static constexpr int kParts = 1;
   static constexpr int kSteps = 8;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 2;
   struct Unit { u32x4 hdr; uint32_t c[4][2]; uint32_t h[2]; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
@@ -781,7 +785,7 @@ struct WPolQ3_K {
   static constexpr bool kChained = true;
   static constexpr int kParts = 1;
   static constexpr int kSteps = 8;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 2;
   struct Unit { uint32_t q[2][2]; uint32_t hm[2]; uint32_t s0, s1, s2; uint32_t d; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
@@ -833,7 +837,7 @@ struct WPolQ2_K {
   static constexpr bool kChained = true;
   static constexpr int kParts = 1;
   static constexpr int kSteps = 8;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 2;
   struct Unit { uint32_t q[2][2]; u32x4 sc; uint32_t dd; };
 
   __device__ __forceinline__ static void load(const uint8_t* row, int u, int kg, Unit& un) {
