@@ -347,6 +347,9 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
               (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
+              # 256+ workgroups at 2 and 4 row tiles of X (8 K slices),
+              # ragged in M and N, K a multiple of 64 or not
+              (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
               # wide layers (1024+ column tiles): X rows staged in LDS once
               # per workgroup
               (17, 96, 16385), (65, 1024, 16400), (130, 256, 16500), (16, 4096, 16384),
@@ -381,6 +384,8 @@ QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
                (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
                # wide layers: 1, 2 and 4 row tiles per workgroup
                (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536),
+               # 256+ workgroups at 2 and 4 row tiles of X (8 K slices)
+               (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
                # the largest m the entry points take (PESTI_MAX_GEMM_M)
                (4096, 96, 40)]
 # Wide layers (1024+ column tiles, 256+ for Q4_K; X rows staged in LDS):
@@ -454,7 +459,7 @@ WS_FORMATS = ("f16",) + QGEMM_FORMATS
 # 2 and 3 row tiles of X; 95 column tiles (2 splits); very long rows
 WS_SPLIT_CASES = [(16, 4864, 896), (1, 4864, 896), (8, 4864, 896), (16, 4128, 70), (33, 8192, 40),
                   (32, 4864, 896), (16, 4160, 1520), (5, 16384, 24), (16, 32768, 20),
-                  # Q8_0, Q3_K, Q6_K: two row tiles of X per workgroup (the
+                  # Q3_K, Q6_K: two row tiles of X per workgroup (the
                   # second ragged at 48 and 47 rows); the others do not split
                   (48, 4864, 896), (64, 4864, 896), (47, 4128, 70)]
 # shapes that do not split in any format: the workspace call equals the
@@ -479,7 +484,7 @@ def test_gemm_ws_split_parity(fmt, m, k, n):
     need = dmv.pesti_gemm_workspace_bytes(fmt, m, n, k)
     if m <= 33 and (fmt != "f16" or (m == 16 and (n + 15) // 16 < 96)):
         assert need > 0, (fmt, m, k, n)
-    if m >= 47 and fmt in ("q8_0", "q3_k", "q6_k"):
+    if m >= 47 and fmt in ("q3_k", "q6_k"):
         assert need > 0, (fmt, m, k, n)
     y = run_gemm_ws(fmt, w, m, n, k, x, bias)
     y_ref, s_ref = _ws_oracle(fmt, w, m, n, k, x, bias)
