@@ -327,10 +327,10 @@ int launch_mfma(const GemmArgs& a, float* ws, hipStream_t st) {
   const int64_t ksteps = a.k / 32;
   if (tiles_n < 96 && (ksteps <= 32 || ksteps > 128)) return launch_mfma_t<16, 1>(a, ws, st);
   if (tiles_n < 96) return launch_mfma_t<8, 1>(a, ws, st);
-  if (tiles_m <= 1) return launch_mfma_t<16, 1>(a, nullptr, st);
-  // 8 K slices once there are at least 256 workgroups (4864x896: m 32 7.7
-  // -> 7.2 us, m 64 10.3 -> 9.2), else 16 (GPT-2 c_attn m 32: 4.2 against
-  // 5.1 with 8)
+  // 8 K slices once there are at least 256 workgroups (4864x896: m 16 6.3
+  // -> 5.6 us, m 32 7.7 -> 7.2, m 64 10.3 -> 9.2), else 16 (GPT-2 c_attn
+  // m 32: 4.2 against 5.1 with 8)
+  if (tiles_m <= 1) return tiles_n >= 256 ? launch_mfma_t<8, 1>(a, nullptr, st) : launch_mfma_t<16, 1>(a, nullptr, st);
   if (tiles_m <= 2) return tiles_n >= 256 ? launch_mfma_t<8, 2>(a, nullptr, st) : launch_mfma_t<16, 2>(a, nullptr, st);
   return tiles_n * ((tiles_m + 3) / 4) >= 256 ? launch_mfma_t<8, 4>(a, nullptr, st)
                                               : launch_mfma_t<16, 4>(a, nullptr, st);

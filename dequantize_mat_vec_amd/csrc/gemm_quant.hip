@@ -1087,9 +1087,10 @@ int launch_q(const QGemmArgs& a, float* ws, hipStream_t st) {
 // tile of X its own workgroup of 8 K slices (16 for Q4_K and Q5_K over 128
 // k-steps: Qwen down m16 10.4 -> 8.9 and 11.3 -> 10.9 us; the other formats
 // measured the same or slower with 16); wider ones share each W load across
-// 2 or 4 row tiles, in workgroups of 8 K slices when there are at least 256
-// workgroups (gate/up 4864x896, us for 16 -> 8 slices: m 32 Q4_K 7.7 ->
-// 6.6, Q8_0 7.1 -> 5.9; m 64 Q4_K 11.1 -> 8.7, Q6_K 12.4 -> 10.4), else 16.
+// 1, 2 or 4 row tiles, in workgroups of 8 K slices when there are at least
+// 256 workgroups (gate/up 4864x896, us for 16 -> 8 slices: m 16 Q6_K 7.3
+// -> 7.0, Q3_K 7.0 -> 6.6; m 32 Q4_K 7.7 -> 6.6, Q8_0 7.1 -> 5.9; m 64 Q4_K
+// 11.1 -> 8.7, Q6_K 12.4 -> 10.4), else 16.
 template <class Q>
 int launch_quant(const QGemmArgs& a, float* ws, hipStream_t st) {
   const int64_t tiles_n = (a.n + 15) / 16, tiles_m = (a.m + 15) / 16;
@@ -1098,7 +1099,7 @@ int launch_quant(const QGemmArgs& a, float* ws, hipStream_t st) {
     return launch_q<Q, kLongNW, 2>(a, ws, st);
   if (tiles_n < 96 && a.k / 32 > 128) return launch_q<Q, kLongNW, 1>(a, ws, st);
   if (tiles_n < 96) return launch_q<Q, 8, 1>(a, nullptr, st);
-  if (tiles_m <= 1) return launch_q<Q, 16, 1>(a, nullptr, st);
+  if (tiles_m <= 1) return tiles_n >= 256 ? launch_q<Q, 8, 1>(a, nullptr, st) : launch_q<Q, 16, 1>(a, nullptr, st);
   if (tiles_m <= 2) return tiles_n >= 256 ? launch_q<Q, 8, 2>(a, nullptr, st) : launch_q<Q, 16, 2>(a, nullptr, st);
   return tiles_n * ((tiles_m + 3) / 4) >= 256 ? launch_q<Q, 8, 4>(a, nullptr, st)
                                               : launch_q<Q, 16, 4>(a, nullptr, st);

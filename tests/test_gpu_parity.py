@@ -347,9 +347,9 @@ GEMM_CASES = [(8, 768, 2304), (32, 768, 768), (64, 768, 3072), (64, 3072, 768),
               # wide layers (96+ column tiles): 1, 2 and 4 row tiles per
               # workgroup, ragged in M and N
               (16, 64, 1600), (20, 128, 2000), (40, 96, 1540),
-              # 256+ workgroups at 2 and 4 row tiles of X (8 K slices),
+              # 256+ workgroups at 1, 2 and 4 row tiles of X (8 K slices),
               # ragged in M and N, K a multiple of 64 or not
-              (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
+              (16, 896, 4100), (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
               # wide layers (1024+ column tiles): X rows staged in LDS once
               # per workgroup
               (17, 96, 16385), (65, 1024, 16400), (130, 256, 16500), (16, 4096, 16384),
@@ -384,8 +384,8 @@ QGEMM_CASES = [(16, 896, 4864), (32, 4864, 896), (64, 896, 128), (17, 896, 70),
                (20, 0, 37), (8, 8192, 40), (48, 16384, 20), (3, 32768, 9),
                # wide layers: 1, 2 and 4 row tiles per workgroup
                (16, 64, 1600), (20, 256, 2000), (40, 96, 1540), (64, 128, 1536),
-               # 256+ workgroups at 2 and 4 row tiles of X (8 K slices)
-               (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
+               # 256+ workgroups at 1, 2 and 4 row tiles of X (8 K slices)
+               (16, 896, 4100), (5, 96, 4864), (24, 896, 4100), (50, 256, 4864), (100, 160, 4100),
                # the largest m the entry points take (PESTI_MAX_GEMM_M)
                (4096, 96, 40)]
 # Wide layers (1024+ column tiles, 256+ for Q4_K; X rows staged in LDS):
