@@ -507,10 +507,6 @@ struct QPolQ2_K {
   static constexpr bool kHalfMins = true;
   static constexpr bool kScaled = true;
   static constexpr int kParts = 1;
-  // With one row tile of X the pair swap takes this kernel from 63 to 70
-  // VGPRs, past the 64 at which two 16-wavefront workgroups fit a compute
-  // unit; with 2 or 4 (over 64 either way) it is taken.
-  static constexpr int kXSwapMinMT = 2;
   struct Step { uint32_t q[2]; uint32_t scb; uint32_t dd; uint32_t j; };
 
   // Steps s and s + 1 (s even: j and j + 1 of one half h) share their code
@@ -889,13 +885,6 @@ struct QBuf {
   qhalf8 x[2][MT];
 };
 
-// Fewest row tiles of X per workgroup at which the X pair swap is taken (1
-// unless the policy says otherwise).
-template <class Q, class = void>
-struct XSwapMinMT { static constexpr int value = 1; };
-template <class Q>
-struct XSwapMinMT<Q, std::void_t<decltype(Q::kXSwapMinMT)>> { static constexpr int value = Q::kXSwapMinMT; };
-
 // Wavefronts per workgroup on narrow layers of over 128 k-steps (8 unless
 // the policy says otherwise).
 template <class Q, class = void>
@@ -1074,10 +1063,7 @@ int launch_q(const QGemmArgs& a, float* ws, hipStream_t st) {
   QGemmArgs args = a;
   void* params[] = {&args, &kpart};
   const void* fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, false>);
-  if constexpr (MT >= pesti::XSwapMinMT<Q>::value) {
-    if (a.k % 64 == 0 && a.k <= 1024)
-      fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>);
-  }
+  if (a.k % 64 == 0 && a.k <= 1024) fn = reinterpret_cast<const void*>(&pesti::gemm_quant_kernel<Q, NW, MT, true>);
   const hipError_t e = hipLaunchKernel(fn, grid, dim3(NW * 64), params, 0, st);
   if (e != hipSuccess) return PESTI_ERR_LAUNCH;
   return splits > 1 ? pesti_host::launch_split_sum(a.m, a.n, kpart, splits, a.bias, a.y, st) : PESTI_OK;
